@@ -1,0 +1,148 @@
+"""Python access to the float64 SRWM oracle (oracle/srwm_oracle.c).
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  The product path
+(``self_referential_weight_amd``) never imports it and has no CPU fallback.
+
+The C file holds every formula and cites the pages for each step; this module
+only marshals numpy arrays in and out, and builds the shared library with gcc
+(``-O2 -ffp-contract=off``, no fast-math, no BLAS).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+_HERE = Path(__file__).resolve().parent
+_SRC = _HERE / "srwm_oracle.c"
+_LIB = _HERE / "libsrwm_oracle.so"
+
+_CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-std=c11", "-Wall"]
+
+
+def build(force: bool = False) -> Path:
+    """Compile the oracle (float64 and the float32 study variant) with gcc."""
+    if not force and _LIB.exists() and _LIB.stat().st_mtime >= _SRC.stat().st_mtime:
+        return _LIB
+    tmp = _LIB.with_suffix(".so.tmp")
+    objs = []
+    for tag, extra in (("f64", []), ("f32", ["-DORACLE_FLOAT"])):
+        obj = _HERE / f"_srwm_oracle_{tag}.o"
+        subprocess.check_call(["gcc", *_CFLAGS, *extra, "-c", str(_SRC), "-o", str(obj)])
+        objs.append(str(obj))
+    subprocess.check_call(["gcc", "-shared", "-o", str(tmp), *objs, "-lm", "-lpthread"])
+    os.replace(tmp, _LIB)
+    for o in objs:
+        os.unlink(o)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(str(_LIB))
+        dp = ctypes.POINTER(ctypes.c_double)
+        fp = ctypes.POINTER(ctypes.c_float)
+        for prefix, p in (("srwm_oracle_", dp), ("srwm_oracle_f32_", fp)):
+            f = getattr(lib, prefix + "delta_update")
+            f.argtypes = [p, ctypes.c_int, ctypes.c_int, p, p, p, p, p]
+            f.restype = None
+            f = getattr(lib, prefix + "step")
+            f.argtypes = [p, ctypes.c_int, ctypes.c_int, p, ctypes.c_int] + [p] * 8
+            f.restype = None
+            f = getattr(lib, prefix + "forward")
+            f.argtypes = [p, p, p, p, ctypes.c_long, ctypes.c_long, ctypes.c_long,
+                          ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray | None, ctype):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def m_rows(d_in: int, d_out: int) -> int:
+    return d_out + 2 * d_in + 4
+
+
+def delta_update(W, kh, qh, eta):
+    """Given-address delta update.  Returns (W_new, v, vb)."""
+    lib = _load()
+    W = np.array(W, dtype=np.float64, order="C", copy=True)
+    rows, d_in = W.shape
+    kh = np.ascontiguousarray(kh, dtype=np.float64)
+    qh = np.ascontiguousarray(qh, dtype=np.float64)
+    eta = np.ascontiguousarray(np.broadcast_to(np.asarray(eta, np.float64), (rows,)))
+    v = np.empty(rows)
+    vb = np.empty(rows)
+    d = ctypes.c_double
+    lib.srwm_oracle_delta_update(_ptr(W, d), rows, d_in, _ptr(kh, d), _ptr(qh, d),
+                                 _ptr(eta, d), _ptr(v, d), _ptr(vb, d))
+    return W, v, vb
+
+
+def step(W, x_t, d_out: int, apply_input_softmax: bool):
+    """One step on one unit.  Returns a dict with W (= W_t), y, u, z, kh, qh, g, v, vb."""
+    lib = _load()
+    W = np.array(W, dtype=np.float64, order="C", copy=True)
+    m, d_in = W.shape
+    assert m == m_rows(d_in, d_out)
+    x_t = np.ascontiguousarray(x_t, dtype=np.float64)
+    out = {k: np.empty(n) for k, n in (("y", d_out), ("u", d_in), ("z", m), ("kh", d_in),
+                                       ("qh", d_in), ("g", 4), ("v", m), ("vb", m))}
+    d = ctypes.c_double
+    lib.srwm_oracle_step(_ptr(W, d), d_in, d_out, _ptr(x_t, d), int(bool(apply_input_softmax)),
+                         *[_ptr(out[k], d) for k in ("y", "u", "z", "kh", "qh", "g", "v", "vb")])
+    out["W"] = W
+    return out
+
+
+def _forward(prefix, npdtype, ctype, x, W0, apply_input_softmax, return_state, nthreads):
+    lib = _load()
+    x = np.ascontiguousarray(x, dtype=npdtype)
+    W0 = np.ascontiguousarray(W0, dtype=npdtype)
+    B, T, H, d_in = x.shape
+    H2, m, d_in2 = W0.shape
+    assert H2 == H and d_in2 == d_in
+    d_out = m - 2 * d_in - 4
+    assert d_out >= 1
+    y = np.empty((B, T, H, d_out), dtype=npdtype)
+    WT = np.empty((B, H, m, d_in), dtype=npdtype) if return_state else None
+    n = default_threads() if nthreads is None else int(nthreads)
+    rc = getattr(lib, prefix + "forward")(_ptr(x, ctype), _ptr(W0, ctype), _ptr(y, ctype),
+                                          _ptr(WT, ctype), B, T, H, d_in, d_out,
+                                          int(bool(apply_input_softmax)), n)
+    if rc != 0:
+        raise ValueError(f"oracle forward rejected its arguments (code {rc})")
+    return y, WT
+
+
+def forward(x, W0, apply_input_softmax=False, return_state=True, nthreads=None):
+    """float64 oracle: x[B,T,H,d_in], W0[H,m,d_in] -> (y[B,T,H,d_out], W_T[B,H,m,d_in])."""
+    return _forward("srwm_oracle_", np.float64, ctypes.c_double, x, W0,
+                    apply_input_softmax, return_state, nthreads)
+
+
+def forward_f32(x, W0, apply_input_softmax=False, return_state=True, nthreads=None):
+    """The same definition evaluated in float32 (drift study only)."""
+    return _forward("srwm_oracle_f32_", np.float32, ctypes.c_float, x, W0,
+                    apply_input_softmax, return_state, nthreads)

@@ -1,0 +1,257 @@
+/*
+ * srwm_oracle.c -- plain CPU oracle of the SRWM forward recurrence.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the independent checker of the GPU
+ * library; it shares no code, header, table or helper with it.  Only tests/,
+ * __graft_entry__.smoke() and bench.py's cpu_baseline leg may load it.  The
+ * product path never calls it and has no CPU fallback.
+ *
+ * What it computes (the plain definition, evaluated with one scalar loop per
+ * formula, in float64):
+ *
+ *   Self-referential weight matrix, 4-learning-rate, multi-head.
+ *   Source pages:
+ *   [ACL]  "Metalearning Continual Learning Algorithms -- part 2/5",
+ *          Sec. 2.3 SRWM dynamics, Eq. (1)-(3), and the paragraph
+ *          "4-learning-rate version", Eq. (4)-(5).
+ *   [SRWM] review page "SRWM: 让权重矩阵学习修改自身" of Irie et al.,
+ *          "A Modern Self-Referential Weight Matrix That Learns to Modify
+ *          Itself" (ICML 2022): Sec. 2.2 (symbol table, output timing),
+ *          Sec. 2.3 (delta-rule intuition, worked example),
+ *          Sec. 2.4 (four row blocks, multi-head, input activation),
+ *          Sec. 2.5 (W0 is the trained initial program).
+ *
+ *   Per (sequence b, head h) the state W is an m x d_in matrix,
+ *   m = d_out + 2*d_in + 4, with row blocks [W^y; W^k; W^q; W^beta]
+ *   ([ACL] 4-lr paragraph; [SRWM] Sec. 2.4).  Every unit starts from the
+ *   shared W0[h] ([ACL] after Eq. (3); [SRWM] Sec. 2.5).  For t = 1..T:
+ *
+ *     u      = x_t, or softmax(x_t) when the input activation is on
+ *              ([ACL] after Eq. (3); [SRWM] Sec. 2.4 last paragraph)
+ *     z      = W u = [y_t, k_t, q_t, beta_t]          [ACL] Eq. (1)
+ *     y_t    = z[0:d_out], taken from W_{t-1}         [SRWM] Sec. 2.2
+ *     kh, qh = softmax(k_t), softmax(q_t)             [ACL] Eq. (2), phi
+ *     g      = sigmoid(beta_t), beta_t in R^4          [ACL] Eq. (4)-(5)
+ *     v      = W qh,  vb = W kh  (both with W_{t-1})  [ACL] Eq. (2), (4)
+ *     W     += eta_i (v_i - vb_i) kh^T, eta_i = g[block(i)]
+ *                                                     [ACL] Eq. (3), (5)
+ *
+ *   The block order of the gate vector is (y, k, q, beta) as the 4-lr
+ *   paragraph lists the sub-blocks.  Eq. (3) as extracted has its bracket
+ *   pair swapped ("sigma( CLOSE ... OPEN beta_t )"); it is read as
+ *   sigma(beta_t) (v_t - vb_t) outer phi(k_t), the only reading whose
+ *   shapes agree, and the one the [SRWM] Sec. 2.1 prose spells out.
+ *
+ * softmax(s)_j = exp(s_j - max s) / sum_l exp(s_l - max s);
+ * sigmoid(z)   = 1/(1+exp(-z)) for z >= 0, exp(z)/(1+exp(z)) otherwise.
+ * Neither page fixes a temperature or scale; none is applied.
+ *
+ * Pins (tests/test_oracle_pins.py): the worked example of [SRWM] Sec. 2.3,
+ * the W0 = 0 fixed point of [SRWM] Sec. 2.5, the reread identity of
+ * [SRWM] Sec. 2.3, the address-norm bounds of [SRWM] Sec. 2.3, an
+ * independent d = 2 closed-form expansion, and derived invariants.  No
+ * function here is "parity unpinned".
+ *
+ * Built twice from this one source: REAL = double (the oracle, symbols
+ * srwm_oracle_*) and REAL = float (symbols srwm_oracle_f32_*), the latter
+ * only to measure how far any float32 evaluation drifts from float64.
+ * Compile with -ffp-contract=off so that no multiply-add is fused.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef ORACLE_FLOAT
+typedef float real;
+#define FN(name) srwm_oracle_f32_##name
+#define EXP expf
+#else
+typedef double real;
+#define FN(name) srwm_oracle_##name
+#define EXP exp
+#endif
+
+/* softmax over n entries: exp(s_j - max) / sum exp(s_l - max). */
+static void softmax(const real* s, int n, real* out)
+{
+    real mx = s[0];
+    for (int j = 1; j < n; ++j)
+        if (s[j] > mx) mx = s[j];
+    real sum = 0;
+    for (int j = 0; j < n; ++j) {
+        out[j] = EXP(s[j] - mx);
+        sum += out[j];
+    }
+    for (int j = 0; j < n; ++j) out[j] = out[j] / sum;
+}
+
+static real sigmoid(real z)
+{
+    if (z >= 0) return (real)1 / ((real)1 + EXP(-z));
+    real e = EXP(z);
+    return e / ((real)1 + e);
+}
+
+/* Block of row i in the 4-lr split [y | k | q | beta]: 0, 1, 2 or 3. */
+static int row_block(int i, int d_in, int d_out)
+{
+    if (i < d_out) return 0;
+    if (i < d_out + d_in) return 1;
+    if (i < d_out + 2 * d_in) return 2;
+    return 3;
+}
+
+/*
+ * Delta-rule self-update with the addresses given ([ACL] Eq. (2)-(3) and
+ * (4)-(5); [SRWM] Sec. 2.3):
+ *   v  = W qh,  vb = W kh       (reads of the current W)
+ *   W  = W + eta_i (v_i - vb_i) kh_j    for every row i and column j
+ * W is rows x d_in, row-major.  eta holds one learning rate per row.
+ * v_out / vb_out (length rows) receive the two reads when non-NULL.
+ */
+void FN(delta_update)(real* W, int rows, int d_in, const real* kh,
+                      const real* qh, const real* eta, real* v_out,
+                      real* vb_out)
+{
+    for (int i = 0; i < rows; ++i) {
+        real* w = W + (size_t)i * d_in;
+        real v = 0, vb = 0;
+        for (int j = 0; j < d_in; ++j) v += w[j] * qh[j];
+        for (int j = 0; j < d_in; ++j) vb += w[j] * kh[j];
+        if (v_out) v_out[i] = v;
+        if (vb_out) vb_out[i] = vb;
+        real a = eta[i] * (v - vb);
+        for (int j = 0; j < d_in; ++j) w[j] = w[j] + a * kh[j];
+    }
+}
+
+/*
+ * One step of the recurrence on one unit.  W (m x d_in) is updated in place
+ * from W_{t-1} to W_t.  x_t has d_in entries; y_t receives d_out entries.
+ * Every other pointer may be NULL; when given it receives the step's
+ * intermediate: u (d_in), z (m), kh, qh (d_in), g (4), v, vb (m).
+ */
+void FN(step)(real* W, int d_in, int d_out, const real* x_t,
+              int apply_input_softmax, real* y_t, real* u_out, real* z_out,
+              real* kh_out, real* qh_out, real* g_out, real* v_out,
+              real* vb_out)
+{
+    const int m = d_out + 2 * d_in + 4;
+    real* buf = (real*)malloc(sizeof(real) * (size_t)(3 * d_in + 2 * m + 4));
+    real* u = buf;
+    real* kh = u + d_in;
+    real* qh = kh + d_in;
+    real* z = qh + d_in;
+    real* eta = z + m;
+    real* g = eta + m;
+
+    /* Input of Eq. (1): x_t itself, or softmax(x_t) in the RL variant. */
+    if (apply_input_softmax)
+        softmax(x_t, d_in, u);
+    else
+        for (int j = 0; j < d_in; ++j) u[j] = x_t[j];
+
+    /* Eq. (1): [y_t, k_t, q_t, beta_t] = W_{t-1} u. */
+    for (int i = 0; i < m; ++i) {
+        real s = 0;
+        for (int j = 0; j < d_in; ++j) s += W[(size_t)i * d_in + j] * u[j];
+        z[i] = s;
+    }
+    /* The output comes from W_{t-1}, before the self-update. */
+    for (int i = 0; i < d_out; ++i) y_t[i] = z[i];
+
+    /* phi = softmax on key and query; sigma on the four rate logits. */
+    softmax(z + d_out, d_in, kh);
+    softmax(z + d_out + d_in, d_in, qh);
+    for (int c = 0; c < 4; ++c) g[c] = sigmoid(z[m - 4 + c]);
+
+    /* Eq. (5): every row block uses its own learning rate. */
+    for (int i = 0; i < m; ++i) eta[i] = g[row_block(i, d_in, d_out)];
+
+    /* Eq. (2) reads and Eq. (3) rank-one delta update. */
+    FN(delta_update)(W, m, d_in, kh, qh, eta, v_out, vb_out);
+
+    if (u_out) memcpy(u_out, u, sizeof(real) * (size_t)d_in);
+    if (z_out) memcpy(z_out, z, sizeof(real) * (size_t)m);
+    if (kh_out) memcpy(kh_out, kh, sizeof(real) * (size_t)d_in);
+    if (qh_out) memcpy(qh_out, qh, sizeof(real) * (size_t)d_in);
+    if (g_out) memcpy(g_out, g, sizeof(real) * 4);
+    free(buf);
+}
+
+/*
+ * Whole sequence for one unit.  x: T rows of d_in at row stride x_ld;
+ * y: T rows of d_out at row stride y_ld; W0 and W_T: m x d_in (W_T may be
+ * NULL).  T = 0 leaves y untouched and copies W0 to W_T.
+ */
+void FN(unit)(const real* x, ptrdiff_t x_ld, const real* W0, real* y,
+              ptrdiff_t y_ld, real* W_T, long T, int d_in, int d_out,
+              int apply_input_softmax)
+{
+    const int m = d_out + 2 * d_in + 4;
+    const size_t n = (size_t)m * d_in;
+    real* W = (real*)malloc(sizeof(real) * n);
+    memcpy(W, W0, sizeof(real) * n);
+    for (long t = 0; t < T; ++t)
+        FN(step)(W, d_in, d_out, x + t * x_ld, apply_input_softmax,
+                 y + t * y_ld, NULL, NULL, NULL, NULL, NULL, NULL, NULL);
+    if (W_T) memcpy(W_T, W, sizeof(real) * n);
+    free(W);
+}
+
+/* Batched forward: x[B][T][H][d_in], W0[H][m][d_in], y[B][T][H][d_out],
+ * W_T[B][H][m][d_in] (or NULL).  The (b, h) units are independent
+ * ([SRWM] Sec. 2.4: each head runs on its own); they are spread over
+ * nthreads POSIX threads, each unit evaluated sequentially in t. */
+typedef struct {
+    const real* x;
+    const real* W0;
+    real* y;
+    real* W_T;
+    long B, T, H;
+    int d_in, d_out, flag;
+    long first, stride;
+} job_t;
+
+static void* run_job(void* p)
+{
+    const job_t* jb = (const job_t*)p;
+    const long m = jb->d_out + 2L * jb->d_in + 4;
+    for (long u = jb->first; u < jb->B * jb->H; u += jb->stride) {
+        const long b = u / jb->H, h = u % jb->H;
+        const real* x = jb->x + (b * jb->T * jb->H + h) * jb->d_in;
+        real* y = jb->y + (b * jb->T * jb->H + h) * jb->d_out;
+        real* wt = jb->W_T ? jb->W_T + (b * jb->H + h) * m * jb->d_in : NULL;
+        FN(unit)(x, jb->H * jb->d_in, jb->W0 + h * m * jb->d_in, y,
+                 jb->H * jb->d_out, wt, jb->T, jb->d_in, jb->d_out, jb->flag);
+    }
+    return NULL;
+}
+
+int FN(forward)(const real* x, const real* W0, real* y, real* W_T, long B,
+                long T, long H, int d_in, int d_out, int apply_input_softmax,
+                int nthreads)
+{
+    if (B < 0 || T < 0 || H < 0 || d_in < 1 || d_out < 1) return -1;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    pthread_t th[256];
+    job_t jobs[256];
+    for (int i = 0; i < nthreads; ++i) {
+        jobs[i] = (job_t){x, W0, y, W_T, B, T, H, d_in, d_out,
+                          apply_input_softmax, i, nthreads};
+    }
+    int started = 0;
+    for (int i = 1; i < nthreads; ++i) {
+        if (pthread_create(&th[i], NULL, run_job, &jobs[i]) != 0) break;
+        started = i;
+    }
+    run_job(&jobs[0]);
+    for (int i = 1; i <= started; ++i) pthread_join(th[i], NULL);
+    /* Threads that could not start: run their share here. */
+    for (int i = started + 1; i < nthreads; ++i) run_job(&jobs[i]);
+    return 0;
+}

@@ -1,0 +1,114 @@
+"""The five synthetic SRWM workloads and their seeded input generator.
+
+This module holds no arithmetic of the method: it only names shapes and draws
+seeded random inputs.  It is the one piece of code that both the GPU path's
+tests/bench and the float64 oracle consume.
+
+Input recipe (identical for every consumer):
+  * x[b] (shape [T, H, d_in]) is drawn from ``numpy.random.default_rng([seed, 1, b])``
+    as float32 standard normals, one independent stream per sequence b, so any
+    sampled sequence can be regenerated on its own;
+  * W0 (shape [H, m, d_in]) is drawn from ``numpy.random.default_rng([seed, 2])``
+    as float64 standard normals scaled by ``w0_std`` and rounded to float32;
+  * for bf16 I/O, x is rounded to bfloat16 with round-to-nearest-even; the
+    float32 array returned then holds exactly the bf16 values the GPU reads.
+
+Shapes follow the pages' workloads where they give them: 16 heads of width 16
+in the sequential multi-task model, input softmax in the RL model (review page
+"SRWM: 让权重矩阵学习修改自身", Sec. 2.4 and 3.2-3.3); the larger d and T stress the GPU.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    d_in: int
+    d_out: int
+    T: int
+    io_dtype: str            # "f32" or "bf16"
+    apply_input_softmax: bool
+    return_state: bool
+    w0_std: float
+    seed: int = 0
+
+    @property
+    def m(self) -> int:
+        return self.d_out + 2 * self.d_in + 4
+
+    @property
+    def units(self) -> int:
+        return self.B * self.H
+
+    @property
+    def head_steps(self) -> int:
+        return self.B * self.H * self.T
+
+    @property
+    def flop_per_head_step(self) -> int:
+        """Algorithmic work of one head-step: 8*m*d_in (2md projection,
+        4md for the two reads, 2md for the rank-one update)."""
+        return 8 * self.m * self.d_in
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+WORKLOADS = {
+    "tiny_d8": Workload("tiny_d8", B=1, H=1, d_in=8, d_out=8, T=16, io_dtype="f32",
+                        apply_input_softmax=False, return_state=True, w0_std=0.1),
+    "multitask_d16": Workload("multitask_d16", B=4, H=4, d_in=16, d_out=16, T=256,
+                              io_dtype="f32", apply_input_softmax=False, return_state=True,
+                              w0_std=16 ** -0.5),
+    "fewshot_d64": Workload("fewshot_d64", B=32, H=8, d_in=64, d_out=64, T=1024,
+                            io_dtype="f32", apply_input_softmax=False, return_state=False,
+                            w0_std=64 ** -0.5),
+    "rl_d64_bf16": Workload("rl_d64_bf16", B=128, H=16, d_in=64, d_out=64, T=4096,
+                            io_dtype="bf16", apply_input_softmax=True, return_state=False,
+                            w0_std=64 ** -0.5),
+    "wide_d128": Workload("wide_d128", B=8, H=4, d_in=128, d_out=128, T=8192,
+                          io_dtype="f32", apply_input_softmax=False, return_state=True,
+                          w0_std=128 ** -0.5),
+}
+
+#: The workload the headline throughput is quoted on (RL-shaped, d = 64).
+HEADLINE = "rl_d64_bf16"
+
+
+def round_to_bf16(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even); returns
+    float32 holding the rounded values.  Inputs are finite normals."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32)
+
+
+def gen_x_seq(w: Workload, b: int, T: int | None = None) -> np.ndarray:
+    """x[b] of shape [T, H, d_in] as float32 (bf16-representable for bf16 I/O)."""
+    T = w.T if T is None else T
+    rng = np.random.default_rng([w.seed, 1, b])
+    xb = rng.standard_normal((T, w.H, w.d_in), dtype=np.float32)
+    if w.io_dtype == "bf16":
+        xb = round_to_bf16(xb)
+    return xb
+
+
+def gen_W0(w: Workload) -> np.ndarray:
+    rng = np.random.default_rng([w.seed, 2])
+    return (rng.standard_normal((w.H, w.m, w.d_in)) * w.w0_std).astype(np.float32)
+
+
+def gen_x(w: Workload, batch=None) -> np.ndarray:
+    """x[B', T, H, d_in] for the sequences in ``batch`` (default: all B)."""
+    bs = range(w.B) if batch is None else list(batch)
+    out = np.empty((len(bs), w.T, w.H, w.d_in), dtype=np.float32)
+    for i, b in enumerate(bs):
+        out[i] = gen_x_seq(w, b)
+    return out
