@@ -1,0 +1,103 @@
+"""The C ABI of libsrwm without a GPU: every symbol include/srwm.h declares is
+exported, and invalid calls are rejected by validation before any HIP call."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+from self_referential_weight_amd import _lib
+
+HEADER = Path(__file__).resolve().parents[1] / "include" / "srwm.h"
+
+OK, E_NULL, E_SHAPE, E_UNSUP, E_ALIAS, E_HIP, E_ARG = 0, -1, -2, -3, -4, -5, -6
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(srwm_\w+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    lib = _lib.load()
+    names = declared_functions()
+    assert {"srwm_forward", "srwm_strerror", "srwm_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strerror():
+    lib = _lib.load()
+    assert lib.srwm_version() == 100
+    for code in (OK, E_NULL, E_SHAPE, E_UNSUP, E_ALIAS, E_HIP, E_ARG):
+        assert _lib.strerror(code).startswith("SRWM_")
+    assert "unknown" in _lib.strerror(-99)
+
+
+def test_variant_table_covers_workloads():
+    from self_referential_weight_amd.workloads import WORKLOADS
+    vs = _lib.variants()
+    assert len(vs) == _lib.load().srwm_variant_count()
+    for w in WORKLOADS.values():
+        io = _lib.SRWM_IO_BF16 if w.io_dtype == "bf16" else _lib.SRWM_IO_F32
+        assert _lib.load().srwm_supported(w.d_in, w.d_out, io) == 1, w.name
+    # exactly one default per (d_in, d_out, io)
+    keys = [(v["d_in"], v["d_out"], v["io_dtype"]) for v in vs if v["default"]]
+    assert len(keys) == len(set(keys))
+    assert _lib.load().srwm_variant_info(len(vs), None, None, None, None, None, None) == E_ARG
+
+
+FAKE_X, FAKE_W0, FAKE_Y, FAKE_WT = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+
+
+def call(x=FAKE_X, W0=FAKE_W0, y=FAKE_Y, WT=FAKE_WT, B=2, T=3, H=2, d_in=16, d_out=16,
+         m=None, io=0, flag=0, variant=None):
+    lib = _lib.load()
+    m = d_out + 2 * d_in + 4 if m is None else m
+    args = (x, W0, y, WT, B, T, H, d_in, d_out, m, io, flag, None)
+    if variant is None:
+        return lib.srwm_forward(*args)
+    return lib.srwm_forward_variant(*args, variant)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(m=51), E_SHAPE),
+    (dict(B=-1), E_SHAPE),
+    (dict(T=-5), E_SHAPE),
+    (dict(H=-1), E_SHAPE),
+    (dict(d_in=0), E_SHAPE),
+    (dict(d_out=0, m=36), E_SHAPE),
+    (dict(d_in=7, d_out=7), E_UNSUP),
+    (dict(d_in=64, d_out=32), E_UNSUP),
+    (dict(io=2), E_ARG),
+    (dict(flag=2), E_ARG),
+    (dict(variant=-2), E_ARG),
+    (dict(variant=10 ** 6), E_ARG),
+    (dict(x=None), E_NULL),
+    (dict(y=None), E_NULL),
+    (dict(W0=None), E_NULL),
+    (dict(y=FAKE_X), E_ALIAS),
+    (dict(y=FAKE_X + 64), E_ALIAS),
+    (dict(WT=FAKE_W0), E_ALIAS),
+    (dict(WT=FAKE_Y + 16), E_ALIAS),
+    (dict(B=2 ** 40, T=2 ** 40), E_SHAPE),
+    (dict(x=FAKE_X + 4), E_ARG),
+    (dict(WT=FAKE_WT + 8), E_ARG),
+])
+def test_validation_rejects(kw, code):
+    assert call(**kw) == code
+
+
+def test_variant_must_match_shape():
+    vs = _lib.variants()
+    v64 = next(v for v in vs if v["d_in"] == 64 and v["io_dtype"] == "f32")
+    assert call(d_in=16, d_out=16, variant=v64["index"]) == E_ARG
+
+
+def test_empty_problems_are_noops_without_gpu():
+    # B*H == 0: nothing to do, no HIP call is made.
+    assert call(B=0, x=None, y=None, WT=None) == OK
+    assert call(H=0, x=None, y=None, W0=None, WT=None) == OK
+    # T == 0 with no state requested: nothing to write.
+    assert call(T=0, x=None, y=None, WT=None) == OK
