@@ -1,0 +1,208 @@
+"""Throughput of the SRWM forward recurrence on one MI355X.
+
+One "step" is one srwm_forward call over a whole synthetic batch (every
+(sequence, head) unit through all T time steps).  The default workload is the
+RL-shaped one: B=128, H=16, d_in=d_out=64 (m=196), T=4096, bf16 x/y, fp32
+state, softmax on x_t.  Inputs are seeded, generated on the host and resident
+in HBM before timing starts.
+
+Prints ONE JSON line with the headline metric (head-steps/s = B*H*T/s), the
+roofline of the kernel (algorithmic FP32 FLOP per launch / average launch time
+from HIP events on the launch stream, against the FP32 vector peak) and the
+float64 CPU oracle timed on a bounded sample of the same workload.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--variant I] [--no-cpu] [--copy-calibration BYTES]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "SRWM head-steps/sec (B·H·T/s) and % of FP32 VALU peak, 1×MI355X"
+# MI355X FP32 vector peak: 256 CUs x 256 FLOP/clk/CU x 2.4 GHz.
+PEAK_FP32_TFLOPS = 157.3
+KERNEL_SRC = ROOT / "self_referential_weight_amd" / "csrc" / "srwm_fwd.hip"
+TRAFFIC_FILE = ROOT / "profiles" / "srwm_fwd_rl_d64_bf16_hbm_traffic.json"
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(KERNEL_SRC.read_bytes()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str, variant: int):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    runs, if they were taken on the current kernel source; else None."""
+    if not TRAFFIC_FILE.exists():
+        return None
+    try:
+        rec = json.loads(TRAFFIC_FILE.read_text())
+    except ValueError:
+        return None
+    if (rec.get("kernel_source_sha256_16") != kernel_source_hash()
+            or rec.get("workload") != workload or rec.get("variant", -1) != variant):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, x_host, W0_host, budget_s: float):
+    """Time the float64 oracle on the first n sequences (all heads, all T
+    steps) of the workload, n sized so the run takes about budget_s."""
+    import numpy as np
+
+    from oracle import oracle
+
+    cores = oracle.default_threads()
+    env_cap = os.environ.get("OMP_NUM_THREADS")
+    if env_cap and env_cap.isdigit():
+        cores = max(1, min(cores, int(env_cap)))
+    # calibration: one sequence
+    t0 = time.perf_counter()
+    oracle.forward(np.ascontiguousarray(x_host[:1], dtype=np.float64), W0_host,
+                   w.apply_input_softmax, return_state=False, nthreads=cores)
+    t1 = time.perf_counter() - t0
+    # one thread takes tau seconds per unit; n sequences spread n*H units over the cores
+    tau = t1 * min(w.H, cores) / w.H
+    n = max(1, min(w.B, int(budget_s * cores / (max(tau, 1e-9) * w.H))))
+    xs = np.ascontiguousarray(x_host[:n], dtype=np.float64)
+    t0 = time.perf_counter()
+    oracle.forward(xs, W0_host, w.apply_input_softmax, return_state=False, nthreads=cores)
+    dt = time.perf_counter() - t0
+    units = n * w.H
+    return {
+        "value": units * w.T / dt,
+        "unit": "head-steps/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"first {n} of {w.B} sequences x {w.H} heads ({units} units) x T={w.T} "
+                   f"of {w.name}, float64, {dt:.1f} s wall"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--variant", type=int, default=-1)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle wall time")
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="also run a plain device copy of this many bytes (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
+              "the (sequence, head) units shard across GPUs with no communication, "
+              "so one GPU's share is what is measured", file=sys.stderr)
+        return 2
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: multi-rank launch is not supported", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import self_referential_weight_amd as srwm
+    from self_referential_weight_amd.workloads import HEADLINE, WORKLOADS, gen_W0, gen_x
+
+    name = args.workload or HEADLINE
+    w = WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    log(f"[bench] generating {name}: B={w.B} H={w.H} d_in={w.d_in} d_out={w.d_out} T={w.T} "
+        f"io={w.io_dtype} input_softmax={w.apply_input_softmax}")
+    x_host = gen_x(w)
+    W0_host = gen_W0(w)
+    x = torch.from_numpy(x_host).to(dev)
+    if w.io_dtype == "bf16":
+        x = x.to(torch.bfloat16)
+    W0 = torch.from_numpy(W0_host).to(dev)
+    y = torch.empty((w.B, w.T, w.H, w.d_out), dtype=x.dtype, device=dev)
+    W_T = torch.empty((w.B, w.H, w.m, w.d_in), dtype=torch.float32, device=dev) if w.return_state else None
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        srwm.forward(x, W0, apply_input_softmax=w.apply_input_softmax, return_state=w.return_state,
+                     variant=args.variant, y=y, W_T=W_T, stream=stream)
+
+    if args.copy_calibration:
+        nbytes = int(args.copy_calibration)
+        a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        bcopy = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            bcopy.copy_(a)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: 3 copies of {nbytes} bytes done")
+        del a, bcopy
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1) / args.steps  # one kernel launch per step
+    ms_per_step = wall * 1e3 / args.steps
+    log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step wall, {gpu_ms:.3f} ms/launch (HIP events)")
+
+    head_steps = w.B * w.H * w.T
+    flop = w.flop_per_head_step * head_steps
+    achieved = flop / (gpu_ms * 1e-3) / 1e12
+    io_bytes = head_steps * (w.d_in + w.d_out) * (2 if w.io_dtype == "bf16" else 4)
+    traffic = measured_traffic(name, args.variant)
+
+    rec = {
+        "metric": METRIC,
+        "value": head_steps / (ms_per_step * 1e-3),
+        "unit": "head-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded normal x, W0 ~ N(0, 1/d_in); no dataset)",
+        "config": {"workload": name, "B": w.B, "H": w.H, "d_in": w.d_in, "d_out": w.d_out,
+                   "T": w.T, "io_dtype": w.io_dtype, "apply_input_softmax": w.apply_input_softmax,
+                   "return_state": w.return_state, "variant": args.variant},
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_TFLOPS, "traffic": traffic},
+        "kernel_ms": gpu_ms,
+        "io_stream_GBps": io_bytes / (gpu_ms * 1e-3) / 1e9,
+    }
+    if not args.no_cpu:
+        log("[bench] timing the float64 CPU oracle on a bounded sample")
+        rec["cpu_baseline"] = cpu_baseline(w, x_host, W0_host, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

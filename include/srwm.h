@@ -90,9 +90,13 @@ int srwm_forward(const void* x, const float* W0, void* y, float* W_T,
 /*
  * srwm_forward_variant -- srwm_forward with an explicit kernel variant, for
  * tuning and for testing every variant against the same definition.
- * variant = -1 picks the default (identical to srwm_forward); otherwise it
- * indexes the list reported by srwm_variant_info().  A variant whose
- * (d_in, d_out, io_dtype) does not match the call gives SRWM_ERR_ARG.
+ * variant = -1 makes the automatic choice (identical to srwm_forward): among
+ * the eligible variants of (d_in, d_out, io_dtype), the fewest waves per
+ * unit for which B*H*waves fills every SIMD of the chip (>= 1024 waves), or
+ * else the most waves per unit.  Otherwise `variant` indexes the list that
+ * srwm_variant_info() reports; a variant whose (d_in, d_out, io_dtype) does
+ * not match the call gives SRWM_ERR_ARG.  Every variant computes the same
+ * function; they differ in how a unit's state is spread over lanes.
  */
 int srwm_forward_variant(const void* x, const float* W0, void* y, float* W_T,
                          int64_t B, int64_t T, int64_t H, int64_t d_in,
@@ -103,13 +107,14 @@ int srwm_forward_variant(const void* x, const float* W0, void* y, float* W_T,
 int srwm_variant_count(void);
 
 /*
- * srwm_variant_info -- describe variant `i` (0 <= i < srwm_variant_count()).
- * Writes d_in, d_out, io_dtype, waves per workgroup (one workgroup per unit),
- * lanes sharing one row of W, and whether it is the default for its shape.
- * Any output pointer may be NULL.  Returns SRWM_OK or SRWM_ERR_ARG.
+ * srwm_variant_info -- describe variant `i` (0 <= i < srwm_variant_count()):
+ * d_in, d_out, io_dtype, waves per workgroup (one workgroup per unit), lanes
+ * sharing one row of W, waves per SIMD its register use allows, and whether
+ * the automatic choice may pick it.  Any output pointer may be NULL.
+ * Returns SRWM_OK or SRWM_ERR_ARG.
  */
 int srwm_variant_info(int i, int* d_in, int* d_out, int* io_dtype, int* waves,
-                      int* lanes_per_row, int* is_default);
+                      int* lanes_per_row, int* waves_per_simd, int* is_auto);
 
 /* 1 if a kernel exists for (d_in, d_out, io_dtype), else 0. */
 int srwm_supported(int64_t d_in, int64_t d_out, int io_dtype);

@@ -193,9 +193,10 @@ struct Geom {
     static constexpr bool ALIGNED = (D_IN % G == 0) && (D_OUT % G == 0);
     static constexpr int LB = BETA_SEP ? D_IN / 16 : 0; // beta columns per lane
     // x staging: E consecutive elements per lane, LR lanes per step row.
-    // Aim for 32 step rows per chunk with every lane loading, at most 16 and
-    // at least d_in/16 elements per lane (so a row spans <= 16 lanes).
-    static constexpr int E_TARGET = (32 * D_IN) / NT;
+    // Aim for 32 step rows per chunk (8 for one-wave units, whose registers
+    // are scarcer) with every lane loading, at most 16 and at least d_in/16
+    // elements per lane (so a row spans <= 16 lanes).
+    static constexpr int E_TARGET = ((NW == 1 ? 8 : 32) * D_IN) / NT;
     static constexpr int E_LO = D_IN / 16 > E_TARGET ? D_IN / 16 : E_TARGET;
     static constexpr int E = D_IN < 16 ? D_IN : (E_LO < 16 ? (E_LO < 1 ? 1 : E_LO) : 16);
     static constexpr int LR = D_IN / E;
@@ -218,86 +219,89 @@ __device__ __forceinline__ int block_of_row(int row, int d_in, int d_out)
     return row < d_out ? 0 : row < d_out + d_in ? 1 : row < d_out + 2 * d_in ? 2 : 3;
 }
 
-// Softmax of one d-vector by one wave: src/dst in LDS, lanes take entries
-// lane, lane+64, ...
+// phi(k) and phi(q) by one wave: k and q are d-vectors in LDS; lanes take
+// entries lane, lane+64, ...  Writes kh = softmax(k) and e = softmax(q) - kh,
+// the difference the fused read of Eq. (2) needs.  The two reductions are
+// interleaved for ILP.
 template <int D>
-__device__ __forceinline__ void wave_softmax(const float* __restrict__ src, float* __restrict__ dst,
-                                             int lane)
-{
-    constexpr int EPL = (D + 63) / 64;
-    float v[EPL];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-        const int j = lane + 64 * e;
-        v[e] = (j < D) ? src[j] : -INFINITY;
-        mx = fmax2(mx, v[e]);
-    }
-    mx = wave_max(mx);
-    float s = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-        const int j = lane + 64 * e;
-        v[e] = (j < D) ? exp_f32(v[e] - mx) : 0.f;
-        s += v[e];
-    }
-    const float inv = 1.0f / wave_sum(s);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-        const int j = lane + 64 * e;
-        if (j < D) dst[j] = v[e] * inv;
-    }
-}
-
-// Two independent softmaxes by one wave, interleaved for ILP.
-template <int D>
-__device__ __forceinline__ void wave_softmax2(const float* __restrict__ srcA, float* __restrict__ dstA,
-                                              const float* __restrict__ srcB, float* __restrict__ dstB,
-                                              int lane)
+__device__ __forceinline__ void wave_addresses(const float* __restrict__ k, const float* __restrict__ q,
+                                               float* __restrict__ kh_out, float* __restrict__ e_out,
+                                               int lane)
 {
     constexpr int EPL = (D + 63) / 64;
     float a[EPL], b[EPL];
     float ma = -INFINITY, mb = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-        const int j = lane + 64 * e;
-        a[e] = (j < D) ? srcA[j] : -INFINITY;
-        b[e] = (j < D) ? srcB[j] : -INFINITY;
-        ma = fmax2(ma, a[e]);
-        mb = fmax2(mb, b[e]);
+    for (int i = 0; i < EPL; ++i) {
+        const int j = lane + 64 * i;
+        a[i] = (j < D) ? k[j] : -INFINITY;
+        b[i] = (j < D) ? q[j] : -INFINITY;
+        ma = fmax2(ma, a[i]);
+        mb = fmax2(mb, b[i]);
     }
     ma = wave_max(ma);
     mb = wave_max(mb);
     float sa = 0.f, sb = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-        const int j = lane + 64 * e;
-        a[e] = (j < D) ? exp_f32(a[e] - ma) : 0.f;
-        b[e] = (j < D) ? exp_f32(b[e] - mb) : 0.f;
-        sa += a[e];
-        sb += b[e];
+    for (int i = 0; i < EPL; ++i) {
+        const int j = lane + 64 * i;
+        a[i] = (j < D) ? exp_f32(a[i] - ma) : 0.f;
+        b[i] = (j < D) ? exp_f32(b[i] - mb) : 0.f;
+        sa += a[i];
+        sb += b[i];
     }
     const float ia = 1.0f / wave_sum(sa);
     const float ib = 1.0f / wave_sum(sb);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-        const int j = lane + 64 * e;
+    for (int i = 0; i < EPL; ++i) {
+        const int j = lane + 64 * i;
         if (j < D) {
-            dstA[j] = a[e] * ia;
-            dstB[j] = b[e] * ib;
+            // Both probabilities are rounded before the difference (no fused
+            // multiply-subtract), so k_t == q_t gives e == 0 exactly.
+#pragma clang fp contract(off)
+            const float kh = a[i] * ia;
+            const float qh = b[i] * ib;
+            kh_out[j] = kh;
+            e_out[j] = qh - kh;
         }
     }
 }
-
-// Compiler-level fence: LDS values read before it are re-read after it, so
-// short vector pieces are streamed from LDS instead of held in VGPRs.
-__device__ __forceinline__ void reload_fence() { asm volatile("" ::: "memory"); }
 
 // Width of the LDS vector pieces streamed through the FMA loops.
 template <int N>
 struct Piece {
     static constexpr int W = N % 4 == 0 ? 4 : N % 2 == 0 ? 2 : 1;
 };
+
+// Stream src[0..N) from LDS in pieces of Piece<N>::W floats through
+// body(c, value), double-buffered: piece k+1 is requested before piece k is
+// consumed, and a scheduling barrier after each piece keeps the compiler from
+// hoisting later pieces (which would hold the whole vector in VGPRs).
+template <int N, class F>
+__device__ __forceinline__ void stream_lds(const float* __restrict__ src, F&& body)
+{
+    constexpr int VW = Piece<N>::W;
+    constexpr int NPC = N / VW;
+    float cur[VW];
+    load_f32<VW>(src, cur);
+#pragma unroll
+    for (int k = 0; k < NPC; ++k) {
+        float nxt[VW];
+        if (k + 1 < NPC) load_f32<VW>(src + (k + 1) * VW, nxt);
+#pragma unroll
+        for (int c = 0; c < VW; ++c) body(k * VW + c, cur[c]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (k + 1 < NPC) {
+#pragma unroll
+            for (int c = 0; c < VW; ++c) cur[c] = nxt[c];
+        }
+    }
+}
+
+__device__ __forceinline__ float uniform(float v)
+{
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
 
 // ----------------------------------------------------------------------------
 // The kernel: grid = B*H workgroups (unit = b*H + h), NW*64 threads each.
@@ -313,14 +317,12 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
     constexpr int L = Gm::L, G = Gm::G, R = Gm::R, LB = Gm::LB;
     constexpr int E = Gm::E, LR = Gm::LR, S = Gm::S;
     constexpr bool BETA_SEP = Gm::BETA_SEP;
-    constexpr int VW = Piece<L>::W;
-    constexpr int VWB = BETA_SEP ? Piece<LB>::W : 1;
 
     __shared__ __attribute__((aligned(16))) float s_x[2][S][D_IN];
     __shared__ __attribute__((aligned(16))) float s_z[R * G + 4];
-    __shared__ __attribute__((aligned(16))) float s_kh[D_IN];
-    __shared__ __attribute__((aligned(16))) float s_qh[D_IN];
-    __shared__ __attribute__((aligned(16))) float s_g[4];
+    __shared__ __attribute__((aligned(16))) float s_kh[D_IN]; // phi(k_t)
+    __shared__ __attribute__((aligned(16))) float s_e[D_IN];  // phi(q_t) - phi(k_t)
+    __shared__ __attribute__((aligned(16))) float s_g[4];     // sigma(beta_t)
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -428,10 +430,8 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
         if (xs_active) store_f32<E>(&dst[xs_row][xs_col], v);
     };
 
-    // Phase B roles.
-    constexpr int WAVE_K = 0;
-    constexpr int WAVE_Q = NW >= 2 ? 1 : 0;
-    constexpr int WAVE_Y = NW >= 3 ? 2 : 0;
+    // Phase B roles: wave 0 forms the addresses; WAVE_AUX the gates and y_t.
+    constexpr int WAVE_AUX = NW >= 2 ? 1 : 0;
 
     if (T > 0) {
         load_chunk(0);
@@ -450,15 +450,10 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
                 float acc[R];
 #pragma unroll
                 for (int r = 0; r < R; ++r) acc[r] = 0.f;
+                stream_lds<L>(urow + p * L, [&](int c, float uc) {
 #pragma unroll
-                for (int c0v = 0; c0v < L; c0v += VW) {
-                    float u[VW];
-                    load_f32<VW>(urow + p * L + c0v, u);
-#pragma unroll
-                    for (int c = 0; c < VW; ++c)
-#pragma unroll
-                        for (int r = 0; r < R; ++r) acc[r] = fmaf(w[r][c0v + c], u[c], acc[r]);
-                }
+                    for (int r = 0; r < R; ++r) acc[r] = fmaf(w[r][c], uc, acc[r]);
+                });
 #pragma unroll
                 for (int r = 0; r < R; ++r) acc[r] = group_sum<P>(acc[r]);
                 // All P lanes of a row group hold the same sums; lane p stores
@@ -474,13 +469,7 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
                 if constexpr (BETA_SEP) {
                     if (wave == 0) {
                         float accb = 0.f;
-#pragma unroll
-                        for (int c0v = 0; c0v < LB; c0v += VWB) {
-                            float u[VWB];
-                            load_f32<VWB>(urow + bcol + c0v, u);
-#pragma unroll
-                            for (int c = 0; c < VWB; ++c) accb = fmaf(wb[c0v + c], u[c], accb);
-                        }
+                        stream_lds<LB>(urow + bcol, [&](int c, float uc) { accb = fmaf(wb[c], uc, accb); });
                         accb = group_sum<16>(accb);
                         if ((lane & 15) == 0) s_z[MAIN + brow] = accb;
                     }
@@ -488,14 +477,9 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
                 __syncthreads();
 
                 // ---- (B) phi(k), phi(q), sigma(beta); y_t from W_{t-1}.
-                if constexpr (NW == 1) {
-                    wave_softmax2<D_IN>(s_z + D_OUT, s_kh, s_z + D_OUT + D_IN, s_qh, lane);
-                } else {
-                    if (wave == WAVE_K) wave_softmax<D_IN>(s_z + D_OUT, s_kh, lane);
-                    if (wave == WAVE_Q) wave_softmax<D_IN>(s_z + D_OUT + D_IN, s_qh, lane);
-                }
-                if (wave == WAVE_Q && lane < 4) s_g[lane] = sigmoid_f32(s_z[MAIN + lane]);
-                if (wave == WAVE_Y) {
+                if (wave == 0) wave_addresses<D_IN>(s_z + D_OUT, s_z + D_OUT + D_IN, s_kh, s_e, lane);
+                if (wave == WAVE_AUX) {
+                    if (lane < 4) s_g[lane] = sigmoid_f32(s_z[MAIN + lane]);
 #pragma unroll
                     for (int j0 = 0; j0 < D_OUT; j0 += kWave) {
                         const int j = j0 + lane;
@@ -511,21 +495,14 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
                 __syncthreads();
 
                 // ---- (C) Eq. (2)/(4) fused: W (qh - kh) = v - vb, times the gate.
-                const float g0 = s_g[0], g1 = s_g[1], g2 = s_g[2], g3 = s_g[3];
+                const float g0 = uniform(s_g[0]), g1 = uniform(s_g[1]);
+                const float g2 = uniform(s_g[2]), g3 = uniform(s_g[3]);
 #pragma unroll
                 for (int r = 0; r < R; ++r) acc[r] = 0.f;
+                stream_lds<L>(s_e + p * L, [&](int c, float ec) {
 #pragma unroll
-                for (int c0v = 0; c0v < L; c0v += VW) {
-                    float kq[VW], qq[VW];
-                    load_f32<VW>(s_kh + p * L + c0v, kq);
-                    load_f32<VW>(s_qh + p * L + c0v, qq);
-#pragma unroll
-                    for (int c = 0; c < VW; ++c) {
-                        const float e = qq[c] - kq[c];
-#pragma unroll
-                        for (int r = 0; r < R; ++r) acc[r] = fmaf(w[r][c0v + c], e, acc[r]);
-                    }
-                }
+                    for (int r = 0; r < R; ++r) acc[r] = fmaf(w[r][c], ec, acc[r]);
+                });
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     float gate;
@@ -541,38 +518,18 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
                 float accb = 0.f;
                 if constexpr (BETA_SEP) {
                     if (wave == 0) {
-#pragma unroll
-                        for (int c0v = 0; c0v < LB; c0v += VWB) {
-                            float kq[VWB], qq[VWB];
-                            load_f32<VWB>(s_kh + bcol + c0v, kq);
-                            load_f32<VWB>(s_qh + bcol + c0v, qq);
-#pragma unroll
-                            for (int c = 0; c < VWB; ++c) accb = fmaf(wb[c0v + c], qq[c] - kq[c], accb);
-                        }
+                        stream_lds<LB>(s_e + bcol, [&](int c, float ec) { accb = fmaf(wb[c], ec, accb); });
                         accb = g3 * group_sum<16>(accb);
                     }
                 }
-                reload_fence();
                 // ---- (D) Eq. (3)/(5): W += a kh^T, in place.
+                stream_lds<L>(s_kh + p * L, [&](int c, float kc) {
 #pragma unroll
-                for (int c0v = 0; c0v < L; c0v += VW) {
-                    float kq[VW];
-                    load_f32<VW>(s_kh + p * L + c0v, kq);
-#pragma unroll
-                    for (int c = 0; c < VW; ++c)
-#pragma unroll
-                        for (int r = 0; r < R; ++r) w[r][c0v + c] = fmaf(acc[r], kq[c], w[r][c0v + c]);
-                }
+                    for (int r = 0; r < R; ++r) w[r][c] = fmaf(acc[r], kc, w[r][c]);
+                });
                 if constexpr (BETA_SEP) {
-                    if (wave == 0) {
-#pragma unroll
-                        for (int c0v = 0; c0v < LB; c0v += VWB) {
-                            float kq[VWB];
-                            load_f32<VWB>(s_kh + bcol + c0v, kq);
-#pragma unroll
-                            for (int c = 0; c < VWB; ++c) wb[c0v + c] = fmaf(accb, kq[c], wb[c0v + c]);
-                        }
-                    }
+                    if (wave == 0)
+                        stream_lds<LB>(s_kh + bcol, [&](int c, float kc) { wb[c] = fmaf(accb, kc, wb[c]); });
                 }
             }
             if (c0 + S < T) {
@@ -602,20 +559,22 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
 using KernelFn = void (*)(const void*, const float*, void*, float*, int, int, int);
 
 struct Variant {
-    int d_in, d_out, io, nw, p, is_default;
+    int d_in, d_out, io, nw, p, wpe, is_auto;
     KernelFn fn;
 };
 
 template <int D_IN, int D_OUT, int NW, int P, int WPE, bool BF16>
-constexpr Variant make_variant(int is_default)
+constexpr Variant make_variant(int is_auto)
 {
-    return Variant{D_IN, D_OUT, BF16 ? SRWM_IO_BF16 : SRWM_IO_F32, NW, P, is_default,
+    return Variant{D_IN, D_OUT, BF16 ? SRWM_IO_BF16 : SRWM_IO_F32, NW, P, WPE, is_auto,
                    &srwm_fwd_kernel<D_IN, D_OUT, NW, P, WPE, BF16>};
 }
 
-#define SRWM_BOTH_IO(DI, DO, NW, P, WPE, DEF) \
-    make_variant<DI, DO, NW, P, WPE, false>(DEF), make_variant<DI, DO, NW, P, WPE, true>(DEF)
+#define SRWM_BOTH_IO(DI, DO, NW, P, WPE, AUTO) \
+    make_variant<DI, DO, NW, P, WPE, false>(AUTO), make_variant<DI, DO, NW, P, WPE, true>(AUTO)
 
+// (d_in, d_out, waves per unit, lanes per row, waves per SIMD the registers
+// allow, eligible for the automatic choice).
 const Variant kVariants[] = {
     SRWM_BOTH_IO(2, 2, 1, 2, 1, 1),
     SRWM_BOTH_IO(3, 5, 1, 1, 1, 1),
@@ -624,15 +583,18 @@ const Variant kVariants[] = {
     SRWM_BOTH_IO(16, 8, 1, 8, 1, 1),
     SRWM_BOTH_IO(16, 16, 1, 4, 1, 1),
     SRWM_BOTH_IO(32, 32, 1, 4, 1, 1),
-    SRWM_BOTH_IO(64, 64, 1, 4, 1, 1),
-    SRWM_BOTH_IO(64, 64, 1, 4, 2, 0),
-    SRWM_BOTH_IO(64, 64, 2, 8, 2, 0),
+    SRWM_BOTH_IO(64, 64, 1, 4, 2, 1),
+    SRWM_BOTH_IO(64, 64, 2, 8, 2, 1),
+    SRWM_BOTH_IO(64, 64, 4, 8, 1, 1),
+    SRWM_BOTH_IO(64, 64, 1, 4, 1, 0),
     SRWM_BOTH_IO(64, 64, 4, 16, 1, 0),
-    SRWM_BOTH_IO(64, 64, 4, 8, 1, 0),
+    SRWM_BOTH_IO(128, 128, 8, 16, 1, 1),
     SRWM_BOTH_IO(128, 128, 16, 16, 1, 1),
-    SRWM_BOTH_IO(128, 128, 8, 16, 1, 0),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
+
+// One wave per SIMD of the chip (256 CUs x 4 SIMDs).
+constexpr int64_t kChipSimds = 1024;
 
 bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb)
 {
@@ -649,18 +611,24 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out)
     return true;
 }
 
-int find_variant(int64_t d_in, int64_t d_out, int io, int requested)
+// Automatic choice among the eligible variants of (d_in, d_out, io): the
+// fewest waves per unit that still give every SIMD of the chip a wave
+// (units * waves >= 1024); if none does, the most waves per unit.
+int find_variant(int64_t d_in, int64_t d_out, int io, int requested, int64_t units)
 {
     if (requested >= 0) {
         if (requested >= kNumVariants) return -1;
         const Variant& v = kVariants[requested];
         return (v.d_in == d_in && v.d_out == d_out && v.io == io) ? requested : -1;
     }
+    int best_fill = -1, best_any = -1;
     for (int i = 0; i < kNumVariants; ++i) {
         const Variant& v = kVariants[i];
-        if (v.d_in == d_in && v.d_out == d_out && v.io == io && v.is_default) return i;
+        if (v.d_in != d_in || v.d_out != d_out || v.io != io || !v.is_auto) continue;
+        if (units * v.nw >= kChipSimds && (best_fill < 0 || v.nw < kVariants[best_fill].nw)) best_fill = i;
+        if (best_any < 0 || v.nw > kVariants[best_any].nw) best_any = i;
     }
-    return -1;
+    return best_fill >= 0 ? best_fill : best_any;
 }
 
 int forward_impl(const void* x, const float* W0, void* y, float* W_T, int64_t B, int64_t T,
@@ -672,7 +640,8 @@ int forward_impl(const void* x, const float* W0, void* y, float* W_T, int64_t B,
     if (io_dtype != SRWM_IO_F32 && io_dtype != SRWM_IO_BF16) return SRWM_ERR_ARG;
     if (apply_input_softmax != 0 && apply_input_softmax != 1) return SRWM_ERR_ARG;
     if (variant < -1) return SRWM_ERR_ARG;
-    const int vi = find_variant(d_in, d_out, io_dtype, variant);
+    const int64_t units_hint = (B > 0 && H > INT64_MAX / B) ? INT64_MAX : B * H;
+    const int vi = find_variant(d_in, d_out, io_dtype, variant, units_hint);
     if (vi < 0) return variant >= 0 ? SRWM_ERR_ARG : SRWM_ERR_UNSUPPORTED;
     const int64_t es = io_dtype == SRWM_IO_BF16 ? 2 : 4;
     int64_t units, steps, nx, ny, nw0, nwt;
@@ -727,7 +696,7 @@ int srwm_forward_variant(const void* x, const float* W0, void* y, float* W_T, in
 int srwm_variant_count(void) { return kNumVariants; }
 
 int srwm_variant_info(int i, int* d_in, int* d_out, int* io_dtype, int* waves, int* lanes_per_row,
-                      int* is_default)
+                      int* waves_per_simd, int* is_auto)
 {
     if (i < 0 || i >= kNumVariants) return SRWM_ERR_ARG;
     const Variant& v = kVariants[i];
@@ -736,13 +705,14 @@ int srwm_variant_info(int i, int* d_in, int* d_out, int* io_dtype, int* waves, i
     if (io_dtype) *io_dtype = v.io;
     if (waves) *waves = v.nw;
     if (lanes_per_row) *lanes_per_row = v.p;
-    if (is_default) *is_default = v.is_default;
+    if (waves_per_simd) *waves_per_simd = v.wpe;
+    if (is_auto) *is_auto = v.is_auto;
     return SRWM_OK;
 }
 
 int srwm_supported(int64_t d_in, int64_t d_out, int io_dtype)
 {
-    return find_variant(d_in, d_out, io_dtype, -1) >= 0 ? 1 : 0;
+    return find_variant(d_in, d_out, io_dtype, -1, 1) >= 0 ? 1 : 0;
 }
 
 const char* srwm_strerror(int code)

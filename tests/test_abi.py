@@ -42,10 +42,11 @@ def test_variant_table_covers_workloads():
     for w in WORKLOADS.values():
         io = _lib.SRWM_IO_BF16 if w.io_dtype == "bf16" else _lib.SRWM_IO_F32
         assert _lib.load().srwm_supported(w.d_in, w.d_out, io) == 1, w.name
-    # exactly one default per (d_in, d_out, io)
-    keys = [(v["d_in"], v["d_out"], v["io_dtype"]) for v in vs if v["default"]]
-    assert len(keys) == len(set(keys))
-    assert _lib.load().srwm_variant_info(len(vs), None, None, None, None, None, None) == E_ARG
+    # every supported shape has at least one automatically eligible variant
+    shapes = {(v["d_in"], v["d_out"], v["io_dtype"]) for v in vs}
+    auto = {(v["d_in"], v["d_out"], v["io_dtype"]) for v in vs if v["auto"]}
+    assert shapes == auto
+    assert _lib.load().srwm_variant_info(len(vs), None, None, None, None, None, None, None) == E_ARG
 
 
 FAKE_X, FAKE_W0, FAKE_Y, FAKE_WT = 0x10000000, 0x20000000, 0x30000000, 0x40000000
