@@ -175,6 +175,8 @@ def main() -> int:
     achieved = flop / (gpu_ms * 1e-3) / 1e12
     io_bytes = head_steps * (w.d_in + w.d_out) * (2 if w.io_dtype == "bf16" else 4)
     traffic = measured_traffic(name, args.variant)
+    kernel = (srwm.variants()[args.variant] if args.variant >= 0
+              else srwm.select_variant(w.d_in, w.d_out, w.io_dtype, w.units))
 
     rec = {
         "metric": METRIC,
@@ -194,6 +196,7 @@ def main() -> int:
                    "return_state": w.return_state, "variant": args.variant},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_TFLOPS, "traffic": traffic},
+        "kernel": {k: kernel[k] for k in ("index", "waves", "lanes_per_row", "waves_per_simd", "schedule")},
         "kernel_ms": gpu_ms,
         "io_stream_GBps": io_bytes / (gpu_ms * 1e-3) / 1e9,
     }

@@ -92,8 +92,8 @@ int srwm_forward(const void* x, const float* W0, void* y, float* W_T,
  * tuning and for testing every variant against the same definition.
  * variant = -1 makes the automatic choice (identical to srwm_forward): among
  * the eligible variants of (d_in, d_out, io_dtype), the fewest waves per
- * unit for which B*H*waves fills every SIMD of the chip (>= 1024 waves), or
- * else the most waves per unit.  Otherwise `variant` indexes the list that
+ * unit for which B*H*waves gives every SIMD of the chip two waves (>= 2048
+ * waves), or else the most waves per unit.  Otherwise `variant` indexes the list that
  * srwm_variant_info() reports; a variant whose (d_in, d_out, io_dtype) does
  * not match the call gives SRWM_ERR_ARG.  Every variant computes the same
  * function; they differ in how a unit's state is spread over lanes.
@@ -109,12 +109,23 @@ int srwm_variant_count(void);
 /*
  * srwm_variant_info -- describe variant `i` (0 <= i < srwm_variant_count()):
  * d_in, d_out, io_dtype, waves per workgroup (one workgroup per unit), lanes
- * sharing one row of W, waves per SIMD its register use allows, and whether
- * the automatic choice may pick it.  Any output pointer may be NULL.
+ * sharing one row of W, waves per SIMD its register use allows, its step
+ * schedule (0: projection, addresses, read, update in turn; 1: the read of
+ * step t and the projection of step t+1 share one pass over W, with the
+ * rank-one correction of Eq. (3) applied to the projection), and whether the
+ * automatic choice may pick it.  Any output pointer may be NULL.
  * Returns SRWM_OK or SRWM_ERR_ARG.
  */
 int srwm_variant_info(int i, int* d_in, int* d_out, int* io_dtype, int* waves,
-                      int* lanes_per_row, int* waves_per_simd, int* is_auto);
+                      int* lanes_per_row, int* waves_per_simd, int* schedule,
+                      int* is_auto);
+
+/*
+ * srwm_select_variant -- the variant index srwm_forward would use for
+ * (d_in, d_out, io_dtype) and `units` = B*H (>= 0), or a negative error code
+ * (SRWM_ERR_SHAPE, SRWM_ERR_ARG, SRWM_ERR_UNSUPPORTED).
+ */
+int srwm_select_variant(int64_t d_in, int64_t d_out, int io_dtype, int64_t units);
 
 /* 1 if a kernel exists for (d_in, d_out, io_dtype), else 0. */
 int srwm_supported(int64_t d_in, int64_t d_out, int io_dtype);

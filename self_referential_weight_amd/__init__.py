@@ -12,7 +12,7 @@ from __future__ import annotations
 from . import _lib
 from .workloads import HEADLINE, WORKLOADS, Workload
 
-__all__ = ["forward", "supported", "variants", "m_rows", "WORKLOADS", "HEADLINE", "Workload"]
+__all__ = ["forward", "supported", "variants", "select_variant", "m_rows", "WORKLOADS", "HEADLINE", "Workload"]
 
 
 def m_rows(d_in: int, d_out: int) -> int:
@@ -27,6 +27,15 @@ def supported(d_in: int, d_out: int, io_dtype: str = "f32") -> bool:
 
 def variants() -> list[dict]:
     return _lib.variants()
+
+
+def select_variant(d_in: int, d_out: int, io_dtype: str, units: int) -> dict:
+    """The kernel variant the automatic choice uses for B*H = units."""
+    io = _lib.SRWM_IO_BF16 if io_dtype == "bf16" else _lib.SRWM_IO_F32
+    i = _lib.load().srwm_select_variant(d_in, d_out, io, units)
+    if i < 0:
+        raise RuntimeError(_lib.strerror(i))
+    return _lib.variants()[i]
 
 
 def forward(x, W0, apply_input_softmax: bool = False, return_state: bool = False,

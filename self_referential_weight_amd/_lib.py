@@ -31,8 +31,10 @@ def load() -> ctypes.CDLL:
     lib.srwm_variant_count.argtypes = []
     lib.srwm_variant_count.restype = ci
     ip = ctypes.POINTER(ci)
-    lib.srwm_variant_info.argtypes = [ci, ip, ip, ip, ip, ip, ip, ip]
+    lib.srwm_variant_info.argtypes = [ci, ip, ip, ip, ip, ip, ip, ip, ip]
     lib.srwm_variant_info.restype = ci
+    lib.srwm_select_variant.argtypes = [i64, i64, ci, i64]
+    lib.srwm_select_variant.restype = ci
     lib.srwm_supported.argtypes = [i64, i64, ci]
     lib.srwm_supported.restype = ci
     lib.srwm_strerror.argtypes = [ci]
@@ -51,11 +53,12 @@ def variants() -> list[dict]:
     lib = load()
     out = []
     for i in range(lib.srwm_variant_count()):
-        vals = [ctypes.c_int() for _ in range(7)]
+        vals = [ctypes.c_int() for _ in range(8)]
         rc = lib.srwm_variant_info(i, *[ctypes.byref(v) for v in vals])
         assert rc == 0
-        d_in, d_out, io, nw, p, wpe, auto = (v.value for v in vals)
+        d_in, d_out, io, nw, p, wpe, sched, auto = (v.value for v in vals)
         out.append(dict(index=i, d_in=d_in, d_out=d_out,
                         io_dtype="bf16" if io == SRWM_IO_BF16 else "f32",
-                        waves=nw, lanes_per_row=p, waves_per_simd=wpe, auto=bool(auto)))
+                        waves=nw, lanes_per_row=p, waves_per_simd=wpe,
+                        schedule="fused" if sched else "phased", auto=bool(auto)))
     return out

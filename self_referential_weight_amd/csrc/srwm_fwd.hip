@@ -71,14 +71,36 @@ __device__ __forceinline__ float group_sum(float v)
 // max(a, b) for finite or infinite operands (no NaN canonicalisation).
 __device__ __forceinline__ float fmax2(float a, float b) { return a > b ? a : b; }
 
+// Order-preserving map of a float to a signed int (an involution): positive
+// floats keep their bits, negative ones flip their magnitude bits, so signed
+// integer max equals float max (integer max fuses with DPP; float max would
+// need NaN canonicalisation of both operands).
+__device__ __forceinline__ int order_key(float f)
+{
+    const int b = __float_as_int(f);
+    return b ^ static_cast<int>(static_cast<unsigned>(b >> 31) >> 1);
+}
+
+__device__ __forceinline__ float from_order_key(int k)
+{
+    return __int_as_float(k ^ static_cast<int>(static_cast<unsigned>(k >> 31) >> 1));
+}
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
 template <int P>
 __device__ __forceinline__ float group_max(float v)
 {
-    if constexpr (P >= 2) v = fmax2(v, dpp<kDppXor1>(v));
-    if constexpr (P >= 4) v = fmax2(v, dpp<kDppXor2>(v));
-    if constexpr (P >= 8) v = fmax2(v, dpp<kDppHalfMirror>(v));
-    if constexpr (P >= 16) v = fmax2(v, dpp<kDppMirror>(v));
-    return v;
+    int k = order_key(v);
+    if constexpr (P >= 2) k = max(k, dpp_i<kDppXor1>(k));
+    if constexpr (P >= 4) k = max(k, dpp_i<kDppXor2>(k));
+    if constexpr (P >= 8) k = max(k, dpp_i<kDppHalfMirror>(k));
+    if constexpr (P >= 16) k = max(k, dpp_i<kDppMirror>(k));
+    return from_order_key(k);
 }
 
 __device__ __forceinline__ float readlane(float v, int l)
@@ -86,11 +108,18 @@ __device__ __forceinline__ float readlane(float v, int l)
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
-// Wave-uniform max / sum over all 64 lanes.
+// Wave-uniform max / sum over all 64 lanes (the cross-row step runs on the
+// scalar unit for the max).
 __device__ __forceinline__ float wave_max(float v)
 {
-    v = group_max<16>(v);
-    return fmax2(fmax2(readlane(v, 0), readlane(v, 16)), fmax2(readlane(v, 32), readlane(v, 48)));
+    int k = order_key(v);
+    k = max(k, dpp_i<kDppXor1>(k));
+    k = max(k, dpp_i<kDppXor2>(k));
+    k = max(k, dpp_i<kDppHalfMirror>(k));
+    k = max(k, dpp_i<kDppMirror>(k));
+    const int m = max(max(__builtin_amdgcn_readlane(k, 0), __builtin_amdgcn_readlane(k, 16)),
+                      max(__builtin_amdgcn_readlane(k, 32), __builtin_amdgcn_readlane(k, 48)));
+    return from_order_key(m);
 }
 
 __device__ __forceinline__ float wave_sum(float v)
@@ -105,9 +134,12 @@ __device__ __forceinline__ float exp_f32(float x)
     return __builtin_amdgcn_exp2f(x * 1.44269504088896340736f);
 }
 
+// 1/x on the hardware reciprocal (v_rcp_f32, 1 ulp).
+__device__ __forceinline__ float rcp_f32(float x) { return __builtin_amdgcn_rcpf(x); }
+
 __device__ __forceinline__ float sigmoid_f32(float z)
 {
-    return 1.0f / (1.0f + exp_f32(-z));
+    return rcp_f32(1.0f + exp_f32(-z));
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h)
@@ -115,13 +147,10 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h)
     return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// float32 -> bfloat16, round to nearest, ties to even; NaN stays NaN.
+// float32 -> bfloat16, round to nearest, ties to even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 // Load N consecutive floats (16-byte aligned when N % 4 == 0).
@@ -250,8 +279,8 @@ __device__ __forceinline__ void wave_addresses(const float* __restrict__ k, cons
         sa += a[i];
         sb += b[i];
     }
-    const float ia = 1.0f / wave_sum(sa);
-    const float ib = 1.0f / wave_sum(sb);
+    const float ia = rcp_f32(wave_sum(sa));
+    const float ib = rcp_f32(wave_sum(sb));
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int j = lane + 64 * i;
@@ -298,9 +327,123 @@ __device__ __forceinline__ void stream_lds(const float* __restrict__ src, F&& bo
     }
 }
 
+// Make this wave's LDS stores visible to its own later LDS loads from other
+// lanes (DS operations of one wave complete in order; this orders them in the
+// compiler and waits for the stores).
+__device__ __forceinline__ void wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ float uniform(float v)
 {
     return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+
+// x staging.  S step rows of x for one unit are loaded one chunk ahead into
+// registers (lane tid < S*LR takes E consecutive elements of row tid/LR), then
+// widened (bf16 -> f32 is exact), optionally softmax-ed per row, and written
+// to an LDS tile.
+template <int D_IN, int D_OUT, int NW, int P, bool BF16>
+struct XStage {
+    using Gm = Geom<D_IN, D_OUT, NW, P>;
+    static constexpr int E = Gm::E, LR = Gm::LR, S = Gm::S;
+    static constexpr int XR = BF16 ? (E + 1) / 2 : E; // registers held per lane
+    uint32_t xr[XR];
+    int row, col;
+    bool active;
+    const void* __restrict__ xv;
+    int64_t x0, x_step;
+    int T;
+
+    __device__ __forceinline__ XStage(int tid, const void* __restrict__ xv_, int64_t x0_, int64_t x_step_, int T_)
+        : row(tid / LR), col((tid % LR) * E), active(tid < S * LR), xv(xv_), x0(x0_), x_step(x_step_), T(T_)
+    {
+    }
+
+    // Issue the global loads of the chunk that starts at step c0.
+    __device__ __forceinline__ void load(int c0)
+    {
+        const int t = c0 + row;
+        if (active && t < T) {
+            if constexpr (BF16) {
+                const uint16_t* src = reinterpret_cast<const uint16_t*>(xv) + x0 + (int64_t)t * x_step + col;
+                if constexpr (E % 8 == 0) {
+#pragma unroll
+                    for (int i = 0; i < E / 8; ++i) {
+                        const uint4 v = reinterpret_cast<const uint4*>(src)[i];
+                        xr[4 * i + 0] = v.x;
+                        xr[4 * i + 1] = v.y;
+                        xr[4 * i + 2] = v.z;
+                        xr[4 * i + 3] = v.w;
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < XR; ++i) {
+                        const uint32_t lo = src[2 * i];
+                        const uint32_t hi = (2 * i + 1 < E) ? src[2 * i + 1] : 0u;
+                        xr[i] = lo | (hi << 16);
+                    }
+                }
+            } else {
+                const float* src = reinterpret_cast<const float*>(xv) + x0 + (int64_t)t * x_step + col;
+                float tmp[E];
+                load_f32<E>(src, tmp);
+#pragma unroll
+                for (int i = 0; i < E; ++i) xr[i] = __float_as_uint(tmp[i]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < XR; ++i) xr[i] = 0u;
+        }
+    }
+
+    // Widen, apply the optional input softmax per step row, write to LDS.
+    __device__ __forceinline__ void stage(float (*dst)[D_IN], int in_softmax)
+    {
+        float v[E];
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+            if constexpr (BF16)
+                v[i] = __uint_as_float((i & 1) ? (xr[i >> 1] & 0xffff0000u) : (xr[i >> 1] << 16));
+            else
+                v[i] = __uint_as_float(xr[i]);
+        }
+        if (in_softmax) {
+            float mx = v[0];
+#pragma unroll
+            for (int i = 1; i < E; ++i) mx = fmax2(mx, v[i]);
+            mx = group_max<LR>(mx);
+            float sum = 0.f;
+#pragma unroll
+            for (int i = 0; i < E; ++i) {
+                v[i] = exp_f32(v[i] - mx);
+                sum += v[i];
+            }
+            const float inv = rcp_f32(group_sum<LR>(sum));
+#pragma unroll
+            for (int i = 0; i < E; ++i) v[i] *= inv;
+        }
+        if (active) store_f32<E>(&dst[row][col], v);
+    }
+};
+
+// Store y_t = z[0:d_out] (one wave; lanes take consecutive entries).
+template <int D_OUT, bool BF16>
+__device__ __forceinline__ void store_y(void* __restrict__ yv, int64_t off, const float* __restrict__ z, int lane)
+{
+#pragma unroll
+    for (int j0 = 0; j0 < D_OUT; j0 += kWave) {
+        const int j = j0 + lane;
+        if (j < D_OUT) {
+            if constexpr (BF16)
+                reinterpret_cast<uint16_t*>(yv)[off + j] = f32_to_bf16(z[j]);
+            else
+                reinterpret_cast<float*>(yv)[off + j] = z[j];
+        }
+    }
 }
 
 // ----------------------------------------------------------------------------
@@ -315,14 +458,15 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
     using Gm = Geom<D_IN, D_OUT, NW, P>;
     constexpr int M = Gm::M, MAIN = Gm::MAIN, ROWS = Gm::ROWS;
     constexpr int L = Gm::L, G = Gm::G, R = Gm::R, LB = Gm::LB;
-    constexpr int E = Gm::E, LR = Gm::LR, S = Gm::S;
+    constexpr int S = Gm::S;
     constexpr bool BETA_SEP = Gm::BETA_SEP;
 
     __shared__ __attribute__((aligned(16))) float s_x[2][S][D_IN];
-    __shared__ __attribute__((aligned(16))) float s_z[R * G + 4];
-    __shared__ __attribute__((aligned(16))) float s_kh[D_IN]; // phi(k_t)
-    __shared__ __attribute__((aligned(16))) float s_e[D_IN];  // phi(q_t) - phi(k_t)
-    __shared__ __attribute__((aligned(16))) float s_g[4];     // sigma(beta_t)
+    // z_t, double-buffered by step parity so one barrier per step suffices.
+    __shared__ __attribute__((aligned(16))) float s_z[2][R * G + 4];
+    // Each wave forms phi(k_t) and phi(q_t) - phi(k_t) itself, in its own slice.
+    __shared__ __attribute__((aligned(16))) float s_kh[NW][D_IN];
+    __shared__ __attribute__((aligned(16))) float s_e[NW][D_IN];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -360,83 +504,15 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
         if (wave == 0) load_f32<LB>(w0h + (int64_t)(MAIN + brow) * D_IN + bcol, wb);
     }
 
-    // ---- x staging: lane tid < S*LR loads E elements of step row tid/LR.
-    const int xs_row = tid / LR;
-    const int xs_col = (tid % LR) * E;
-    const bool xs_active = tid < S * LR;
-    constexpr int XR = BF16 ? (E + 1) / 2 : E; // registers held per lane
-    uint32_t xr[XR];
+    XStage<D_IN, D_OUT, NW, P, BF16> xs(tid, xv, x0, x_step, T);
 
-    auto load_chunk = [&](int c0) {
-        const int t = c0 + xs_row;
-        if (xs_active && t < T) {
-            if constexpr (BF16) {
-                const uint16_t* src = reinterpret_cast<const uint16_t*>(xv) + x0 + (int64_t)t * x_step + xs_col;
-                if constexpr (E % 8 == 0) {
-#pragma unroll
-                    for (int i = 0; i < E / 8; ++i) {
-                        const uint4 v = reinterpret_cast<const uint4*>(src)[i];
-                        xr[4 * i + 0] = v.x;
-                        xr[4 * i + 1] = v.y;
-                        xr[4 * i + 2] = v.z;
-                        xr[4 * i + 3] = v.w;
-                    }
-                } else {
-#pragma unroll
-                    for (int i = 0; i < XR; ++i) {
-                        const uint32_t lo = src[2 * i];
-                        const uint32_t hi = (2 * i + 1 < E) ? src[2 * i + 1] : 0u;
-                        xr[i] = lo | (hi << 16);
-                    }
-                }
-            } else {
-                const float* src = reinterpret_cast<const float*>(xv) + x0 + (int64_t)t * x_step + xs_col;
-                float tmp[E];
-                load_f32<E>(src, tmp);
-#pragma unroll
-                for (int i = 0; i < E; ++i) xr[i] = __float_as_uint(tmp[i]);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < XR; ++i) xr[i] = 0u;
-        }
-    };
-
-    // Widen, apply the optional input softmax per step row, write to LDS.
-    auto stage_chunk = [&](float (*dst)[D_IN]) {
-        float v[E];
-#pragma unroll
-        for (int i = 0; i < E; ++i) {
-            if constexpr (BF16)
-                v[i] = __uint_as_float((i & 1) ? (xr[i >> 1] & 0xffff0000u) : (xr[i >> 1] << 16));
-            else
-                v[i] = __uint_as_float(xr[i]);
-        }
-        if (in_softmax) {
-            float mx = v[0];
-#pragma unroll
-            for (int i = 1; i < E; ++i) mx = fmax2(mx, v[i]);
-            mx = group_max<LR>(mx);
-            float s = 0.f;
-#pragma unroll
-            for (int i = 0; i < E; ++i) {
-                v[i] = exp_f32(v[i] - mx);
-                s += v[i];
-            }
-            const float inv = 1.0f / group_sum<LR>(s);
-#pragma unroll
-            for (int i = 0; i < E; ++i) v[i] *= inv;
-        }
-        if (xs_active) store_f32<E>(&dst[xs_row][xs_col], v);
-    };
-
-    // Phase B roles: wave 0 forms the addresses; WAVE_AUX the gates and y_t.
+    // The wave that stores y_t.
     constexpr int WAVE_AUX = NW >= 2 ? 1 : 0;
 
     if (T > 0) {
-        load_chunk(0);
-        stage_chunk(s_x[0]);
-        if (T > S) load_chunk(S);
+        xs.load(0);
+        xs.stage(s_x[0], in_softmax);
+        if (T > S) xs.load(S);
         __syncthreads();
 
         int chunk = 0;
@@ -447,6 +523,7 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
                 const int t = c0 + s;
                 const float* __restrict__ urow = sxc + s * D_IN;
                 // ---- (A) Eq. (1): z = W u.
+                float* __restrict__ zt = s_z[t & 1];
                 float acc[R];
 #pragma unroll
                 for (int r = 0; r < R; ++r) acc[r] = 0.f;
@@ -464,42 +541,32 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
 #pragma unroll
                     for (int q = 1; q < P && r0 + q < R; ++q) v = (p == q) ? acc[r0 + q] : v;
                     const int row = rg + G * (r0 + p);
-                    if ((r0 + P <= R || r0 + p < R) && (Gm::ALIGNED || row < ROWS)) s_z[row] = v;
+                    if ((r0 + P <= R || r0 + p < R) && (Gm::ALIGNED || row < ROWS)) zt[row] = v;
                 }
                 if constexpr (BETA_SEP) {
                     if (wave == 0) {
                         float accb = 0.f;
                         stream_lds<LB>(urow + bcol, [&](int c, float uc) { accb = fmaf(wb[c], uc, accb); });
                         accb = group_sum<16>(accb);
-                        if ((lane & 15) == 0) s_z[MAIN + brow] = accb;
+                        if ((lane & 15) == 0) zt[MAIN + brow] = accb;
                     }
                 }
                 __syncthreads();
 
-                // ---- (B) phi(k), phi(q), sigma(beta); y_t from W_{t-1}.
-                if (wave == 0) wave_addresses<D_IN>(s_z + D_OUT, s_z + D_OUT + D_IN, s_kh, s_e, lane);
-                if (wave == WAVE_AUX) {
-                    if (lane < 4) s_g[lane] = sigmoid_f32(s_z[MAIN + lane]);
-#pragma unroll
-                    for (int j0 = 0; j0 < D_OUT; j0 += kWave) {
-                        const int j = j0 + lane;
-                        if (j < D_OUT) {
-                            const float zy = s_z[j];
-                            if constexpr (BF16)
-                                reinterpret_cast<uint16_t*>(yv)[y0 + (int64_t)t * y_step + j] = f32_to_bf16(zy);
-                            else
-                                reinterpret_cast<float*>(yv)[y0 + (int64_t)t * y_step + j] = zy;
-                        }
-                    }
-                }
-                __syncthreads();
+                // ---- (B) phi(k), phi(q), sigma(beta), computed by every wave for
+                // itself (identical bits in every wave); y_t from W_{t-1}.
+                wave_addresses<D_IN>(zt + D_OUT, zt + D_OUT + D_IN, s_kh[wave], s_e[wave], lane);
+                const float gl = sigmoid_f32(zt[MAIN + (lane & 3)]);
+                const float g0 = readlane(gl, 0), g1 = readlane(gl, 1), g2 = readlane(gl, 2), g3 = readlane(gl, 3);
+                if (wave == WAVE_AUX) store_y<D_OUT, BF16>(yv, y0 + (int64_t)t * y_step, zt, lane);
+                wave_sync();
+                const float* __restrict__ khw = s_kh[wave];
+                const float* __restrict__ ew = s_e[wave];
 
                 // ---- (C) Eq. (2)/(4) fused: W (qh - kh) = v - vb, times the gate.
-                const float g0 = uniform(s_g[0]), g1 = uniform(s_g[1]);
-                const float g2 = uniform(s_g[2]), g3 = uniform(s_g[3]);
 #pragma unroll
                 for (int r = 0; r < R; ++r) acc[r] = 0.f;
-                stream_lds<L>(s_e + p * L, [&](int c, float ec) {
+                stream_lds<L>(ew + p * L, [&](int c, float ec) {
 #pragma unroll
                     for (int r = 0; r < R; ++r) acc[r] = fmaf(w[r][c], ec, acc[r]);
                 });
@@ -518,24 +585,266 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
                 float accb = 0.f;
                 if constexpr (BETA_SEP) {
                     if (wave == 0) {
-                        stream_lds<LB>(s_e + bcol, [&](int c, float ec) { accb = fmaf(wb[c], ec, accb); });
+                        stream_lds<LB>(ew + bcol, [&](int c, float ec) { accb = fmaf(wb[c], ec, accb); });
                         accb = g3 * group_sum<16>(accb);
                     }
                 }
                 // ---- (D) Eq. (3)/(5): W += a kh^T, in place.
-                stream_lds<L>(s_kh + p * L, [&](int c, float kc) {
+                stream_lds<L>(khw + p * L, [&](int c, float kc) {
 #pragma unroll
                     for (int r = 0; r < R; ++r) w[r][c] = fmaf(acc[r], kc, w[r][c]);
                 });
                 if constexpr (BETA_SEP) {
                     if (wave == 0)
-                        stream_lds<LB>(s_kh + bcol, [&](int c, float kc) { wb[c] = fmaf(accb, kc, wb[c]); });
+                        stream_lds<LB>(khw + bcol, [&](int c, float kc) { wb[c] = fmaf(accb, kc, wb[c]); });
                 }
             }
             if (c0 + S < T) {
-                stage_chunk(s_x[(chunk + 1) & 1]);
-                if (c0 + 2 * S < T) load_chunk(c0 + 2 * S);
+                xs.stage(s_x[(chunk + 1) & 1], in_softmax);
+                if (c0 + 2 * S < T) xs.load(c0 + 2 * S);
                 __syncthreads();
+            }
+        }
+    }
+
+    // ---- a7: W_T[b,h] <- W.
+    if (WT != nullptr) {
+        float* __restrict__ wdst = WT + (int64_t)unit * M * D_IN;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = rg + G * r;
+            if (row < ROWS) store_f32<L>(wdst + (int64_t)row * D_IN + p * L, w[r]);
+        }
+        if constexpr (BETA_SEP) {
+            if (wave == 0) store_f32<LB>(wdst + (int64_t)(MAIN + brow) * D_IN + bcol, wb);
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Fused-schedule kernel for units spread over several waves (latency-bound
+// shapes).  It computes the same recurrence with a shorter serial chain per
+// step.  The projection of step t+1 is formed from W_{t-1}, in the same pass
+// over W as the read of step t, and corrected by the rank-one update of step t:
+//     W_t u_{t+1} = W_{t-1} u_{t+1} + a_t (kh_t . u_{t+1}),   a_t = g (W_{t-1}(qh_t - kh_t)),
+// which is Eq. (3) applied to the vector u_{t+1}.  The update of W itself is
+// deferred to the next iteration, where it runs between the barrier and the
+// fused pass and fills the latency of the softmax chain.  One workgroup
+// barrier per step.
+template <int D_IN, int D_OUT, int NW, int P, int WPE, bool BF16>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * kWave, NW * kWave),
+                          amdgpu_waves_per_eu(WPE)))
+void srwm_fwd_fused_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
+                           void* __restrict__ yv, float* __restrict__ WT, int T, int H, int in_softmax)
+{
+    using Gm = Geom<D_IN, D_OUT, NW, P>;
+    constexpr int M = Gm::M, MAIN = Gm::MAIN, ROWS = Gm::ROWS;
+    constexpr int L = Gm::L, G = Gm::G, R = Gm::R, LB = Gm::LB;
+    constexpr int S = Gm::S;
+    constexpr bool BETA_SEP = Gm::BETA_SEP;
+    static_assert(NW >= 2, "fused schedule is for multi-wave units");
+
+    __shared__ __attribute__((aligned(16))) float s_x[2][S][D_IN];
+    __shared__ __attribute__((aligned(16))) float s_z[2][R * G + 4];
+    // phi(k_t) and phi(q_t) - phi(k_t), per wave and by step parity (the
+    // update of step t-1 still reads phi(k_{t-1}) while step t's are written).
+    __shared__ __attribute__((aligned(16))) float s_kh[2][NW][D_IN];
+    __shared__ __attribute__((aligned(16))) float s_e[NW][D_IN];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int p = tid % P;
+    const int rg = tid / P;
+    const int unit = blockIdx.x;
+    const int b = unit / H;
+    const int h = unit - b * H;
+    const int64_t x_step = (int64_t)H * D_IN;
+    const int64_t y_step = (int64_t)H * D_OUT;
+    const int64_t x0 = ((int64_t)b * T * H + h) * D_IN;
+    const int64_t y0 = ((int64_t)b * T * H + h) * D_OUT;
+    const float* __restrict__ w0h = W0 + (int64_t)h * M * D_IN;
+
+    // ---- a0: W <- W0[h].
+    float w[R][L];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int row = rg + G * r;
+        if (row < ROWS) {
+            load_f32<L>(w0h + (int64_t)row * D_IN + p * L, w[r]);
+        } else {
+#pragma unroll
+            for (int c = 0; c < L; ++c) w[r][c] = 0.f;
+        }
+    }
+    const int bcol = (lane & 15) * (LB > 0 ? LB : 1);
+    const int brow = lane >> 4;
+    float wb[LB > 0 ? LB : 1];
+    if constexpr (BETA_SEP) {
+        if (wave == 0) load_f32<LB>(w0h + (int64_t)(MAIN + brow) * D_IN + bcol, wb);
+    }
+    float gate_of[R];  // filled per step: the learning rate of register r
+
+    if (T > 0) {
+        XStage<D_IN, D_OUT, NW, P, BF16> xs(tid, xv, x0, x_step, T);
+        xs.load(0);
+        xs.stage(s_x[0], in_softmax);
+        if (T > S) xs.load(S);
+        __syncthreads();
+
+        // ---- prologue: z_0 = W_0 u_0.
+        {
+            const float* __restrict__ u0 = &s_x[0][0][0];
+            float acc[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[r] = 0.f;
+            stream_lds<L>(u0 + p * L, [&](int c, float uc) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) acc[r] = fmaf(w[r][c], uc, acc[r]);
+            });
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                acc[r] = group_sum<P>(acc[r]);
+                const int row = rg + G * r;
+                if (p == 0 && (Gm::ALIGNED || row < ROWS)) s_z[0][row] = acc[r];
+            }
+            if constexpr (BETA_SEP) {
+                if (wave == 0) {
+                    float accb = 0.f;
+                    stream_lds<LB>(u0 + bcol, [&](int c, float uc) { accb = fmaf(wb[c], uc, accb); });
+                    accb = group_sum<16>(accb);
+                    if ((lane & 15) == 0) s_z[0][MAIN + brow] = accb;
+                }
+            }
+        }
+
+        float a_prev[R];   // a_{t-1}, applied at the start of iteration t
+        float ab_prev = 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) a_prev[r] = 0.f;
+
+        for (int t = 0; t < T; ++t) {
+            const bool has_next = t + 1 < T;
+            // chunk holding step t+1 must be in LDS before this barrier
+            if (has_next && ((t + 1) % S) == 0) {
+                xs.stage(s_x[((t + 1) / S) & 1], in_softmax);
+                if (t + 1 + S < T) xs.load(t + 1 + S);
+            }
+            __syncthreads();
+            const float* __restrict__ zt = s_z[t & 1];
+
+            // ---- (B) addresses and gates of step t (every wave), y_t.
+            float* __restrict__ khw = s_kh[t & 1][wave];
+            float* __restrict__ ew = s_e[wave];
+            wave_addresses<D_IN>(zt + D_OUT, zt + D_OUT + D_IN, khw, ew, lane);
+            const float gl = sigmoid_f32(zt[MAIN + (lane & 3)]);
+            const float g0 = readlane(gl, 0), g1 = readlane(gl, 1), g2 = readlane(gl, 2), g3 = readlane(gl, 3);
+            if (wave == 1) store_y<D_OUT, BF16>(yv, y0 + (int64_t)t * y_step, zt, lane);
+
+            // ---- (D) of step t-1: W_{t-2} -> W_{t-1} (overlaps the chain above).
+            if (t > 0) {
+                const float* __restrict__ khp = s_kh[(t - 1) & 1][wave];
+                float kv[L];
+                load_f32<L>(khp + p * L, kv);
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int c = 0; c < L; ++c) w[r][c] = fmaf(a_prev[r], kv[c], w[r][c]);
+                if constexpr (BETA_SEP) {
+                    if (wave == 0) {
+                        float kb[LB];
+                        load_f32<LB>(khp + bcol, kb);
+#pragma unroll
+                        for (int c = 0; c < LB; ++c) wb[c] = fmaf(ab_prev, kb[c], wb[c]);
+                    }
+                }
+            }
+            wave_sync();
+
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                if constexpr (Gm::ALIGNED) {
+                    const int bk = Gm::block_of_reg(r);
+                    gate_of[r] = bk == 0 ? g0 : bk == 1 ? g1 : bk == 2 ? g2 : g3;
+                } else {
+                    const int bk = block_of_row(rg + G * r, D_IN, D_OUT);
+                    gate_of[r] = bk == 0 ? g0 : bk == 1 ? g1 : bk == 2 ? g2 : g3;
+                }
+            }
+
+            // ---- fused pass over W_{t-1}: read (e_t) and next projection (u_{t+1}).
+            const int tn = has_next ? t + 1 : t;
+            const float* __restrict__ un = &s_x[(tn / S) & 1][tn % S][0];
+            float accr[R], accz[R];
+            float cpart = 0.f;  // kh_t . u_{t+1}, this lane's columns
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                accr[r] = 0.f;
+                accz[r] = 0.f;
+            }
+            {
+                float ev[L], uv[L], kv[L];
+                load_f32<L>(ew + p * L, ev);
+                load_f32<L>(un + p * L, uv);
+                load_f32<L>(khw + p * L, kv);
+#pragma unroll
+                for (int c = 0; c < L; ++c) {
+                    cpart = fmaf(kv[c], uv[c], cpart);
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        accr[r] = fmaf(w[r][c], ev[c], accr[r]);
+                        accz[r] = fmaf(w[r][c], uv[c], accz[r]);
+                    }
+                }
+            }
+            const float ct = group_sum<P>(cpart);
+            float* __restrict__ zn = s_z[(t + 1) & 1];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float a = gate_of[r] * group_sum<P>(accr[r]);
+                a_prev[r] = a;
+                if (has_next) {
+                    const float z = fmaf(a, ct, group_sum<P>(accz[r]));
+                    const int row = rg + G * r;
+                    if (p == 0 && (Gm::ALIGNED || row < ROWS)) zn[row] = z;
+                }
+            }
+            if constexpr (BETA_SEP) {
+                if (wave == 0) {
+                    float eb[LB], ub[LB];
+                    load_f32<LB>(ew + bcol, eb);
+                    load_f32<LB>(un + bcol, ub);
+                    float br = 0.f, bz = 0.f;
+#pragma unroll
+                    for (int c = 0; c < LB; ++c) {
+                        br = fmaf(wb[c], eb[c], br);
+                        bz = fmaf(wb[c], ub[c], bz);
+                    }
+                    ab_prev = g3 * group_sum<16>(br);
+                    if (has_next) {
+                        const float z = fmaf(ab_prev, ct, group_sum<16>(bz));
+                        if ((lane & 15) == 0) zn[MAIN + brow] = z;
+                    }
+                }
+            }
+        }
+
+        // ---- (D) of the last step.
+        {
+            const float* __restrict__ khp = s_kh[(T - 1) & 1][wave];
+            float kv[L];
+            load_f32<L>(khp + p * L, kv);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int c = 0; c < L; ++c) w[r][c] = fmaf(a_prev[r], kv[c], w[r][c]);
+            if constexpr (BETA_SEP) {
+                if (wave == 0) {
+                    float kb[LB];
+                    load_f32<LB>(khp + bcol, kb);
+#pragma unroll
+                    for (int c = 0; c < LB; ++c) wb[c] = fmaf(ab_prev, kb[c], wb[c]);
+                }
             }
         }
     }
@@ -559,42 +868,64 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
 using KernelFn = void (*)(const void*, const float*, void*, float*, int, int, int);
 
 struct Variant {
-    int d_in, d_out, io, nw, p, wpe, is_auto;
+    int d_in, d_out, io, nw, p, wpe, fused, is_auto;
     KernelFn fn;
 };
 
-template <int D_IN, int D_OUT, int NW, int P, int WPE, bool BF16>
+template <int D_IN, int D_OUT, int NW, int P, int WPE, bool FUSED, bool BF16>
 constexpr Variant make_variant(int is_auto)
 {
-    return Variant{D_IN, D_OUT, BF16 ? SRWM_IO_BF16 : SRWM_IO_F32, NW, P, WPE, is_auto,
-                   &srwm_fwd_kernel<D_IN, D_OUT, NW, P, WPE, BF16>};
+    if constexpr (FUSED)
+        return Variant{D_IN, D_OUT, BF16 ? SRWM_IO_BF16 : SRWM_IO_F32, NW, P, WPE, 1, is_auto,
+                       &srwm_fwd_fused_kernel<D_IN, D_OUT, NW, P, WPE, BF16>};
+    else
+        return Variant{D_IN, D_OUT, BF16 ? SRWM_IO_BF16 : SRWM_IO_F32, NW, P, WPE, 0, is_auto,
+                       &srwm_fwd_kernel<D_IN, D_OUT, NW, P, WPE, BF16>};
 }
 
 #define SRWM_BOTH_IO(DI, DO, NW, P, WPE, AUTO) \
-    make_variant<DI, DO, NW, P, WPE, false>(AUTO), make_variant<DI, DO, NW, P, WPE, true>(AUTO)
+    make_variant<DI, DO, NW, P, WPE, false, false>(AUTO), make_variant<DI, DO, NW, P, WPE, false, true>(AUTO)
+#define SRWM_BOTH_IO_FUSED(DI, DO, NW, P, WPE, AUTO) \
+    make_variant<DI, DO, NW, P, WPE, true, false>(AUTO), make_variant<DI, DO, NW, P, WPE, true, true>(AUTO)
 
 // (d_in, d_out, waves per unit, lanes per row, waves per SIMD the registers
 // allow, eligible for the automatic choice).
 const Variant kVariants[] = {
+    // small shapes (tests, latency-bound workloads)
     SRWM_BOTH_IO(2, 2, 1, 2, 1, 1),
     SRWM_BOTH_IO(3, 5, 1, 1, 1, 1),
     SRWM_BOTH_IO(8, 8, 1, 8, 1, 1),
     SRWM_BOTH_IO(8, 16, 1, 8, 1, 1),
     SRWM_BOTH_IO(16, 8, 1, 8, 1, 1),
     SRWM_BOTH_IO(16, 16, 1, 4, 1, 1),
+    SRWM_BOTH_IO_FUSED(16, 16, 2, 4, 1, 0),
     SRWM_BOTH_IO(32, 32, 1, 4, 1, 1),
-    SRWM_BOTH_IO(64, 64, 1, 4, 2, 1),
+    // d = 64: one wave per unit for many units, up to eight for few
+    SRWM_BOTH_IO(64, 64, 1, 2, 2, 1),
     SRWM_BOTH_IO(64, 64, 2, 8, 2, 1),
-    SRWM_BOTH_IO(64, 64, 4, 8, 1, 1),
+    SRWM_BOTH_IO_FUSED(64, 64, 4, 8, 1, 1),
+    SRWM_BOTH_IO_FUSED(64, 64, 8, 8, 1, 1),
+    SRWM_BOTH_IO(64, 64, 1, 4, 2, 0),
     SRWM_BOTH_IO(64, 64, 1, 4, 1, 0),
+    SRWM_BOTH_IO(64, 64, 4, 8, 1, 0),
     SRWM_BOTH_IO(64, 64, 4, 16, 1, 0),
-    SRWM_BOTH_IO(128, 128, 8, 16, 1, 1),
-    SRWM_BOTH_IO(128, 128, 16, 16, 1, 1),
+    SRWM_BOTH_IO(64, 64, 4, 4, 1, 0),
+    SRWM_BOTH_IO(64, 64, 8, 8, 1, 0),
+    SRWM_BOTH_IO_FUSED(64, 64, 4, 4, 1, 0),
+    // d = 128
+    SRWM_BOTH_IO_FUSED(128, 128, 8, 8, 1, 1),
+    SRWM_BOTH_IO_FUSED(128, 128, 8, 16, 1, 0),
+    SRWM_BOTH_IO_FUSED(128, 128, 16, 16, 1, 0),
+    SRWM_BOTH_IO(128, 128, 8, 16, 1, 0),
+    SRWM_BOTH_IO(128, 128, 16, 16, 1, 0),
+    SRWM_BOTH_IO(128, 128, 16, 8, 1, 0),
+    SRWM_BOTH_IO(128, 128, 8, 8, 1, 0),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-// One wave per SIMD of the chip (256 CUs x 4 SIMDs).
-constexpr int64_t kChipSimds = 1024;
+// Two waves per SIMD of the chip (256 CUs x 4 SIMDs x 2): enough waves to
+// hide one wave's latency behind another's arithmetic.
+constexpr int64_t kChipWaveSlots = 2048;
 
 bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb)
 {
@@ -612,8 +943,8 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out)
 }
 
 // Automatic choice among the eligible variants of (d_in, d_out, io): the
-// fewest waves per unit that still give every SIMD of the chip a wave
-// (units * waves >= 1024); if none does, the most waves per unit.
+// fewest waves per unit that still give every SIMD of the chip two waves
+// (units * waves >= 2048); if none does, the most waves per unit.
 int find_variant(int64_t d_in, int64_t d_out, int io, int requested, int64_t units)
 {
     if (requested >= 0) {
@@ -625,7 +956,7 @@ int find_variant(int64_t d_in, int64_t d_out, int io, int requested, int64_t uni
     for (int i = 0; i < kNumVariants; ++i) {
         const Variant& v = kVariants[i];
         if (v.d_in != d_in || v.d_out != d_out || v.io != io || !v.is_auto) continue;
-        if (units * v.nw >= kChipSimds && (best_fill < 0 || v.nw < kVariants[best_fill].nw)) best_fill = i;
+        if (units * v.nw >= kChipWaveSlots && (best_fill < 0 || v.nw < kVariants[best_fill].nw)) best_fill = i;
         if (best_any < 0 || v.nw > kVariants[best_any].nw) best_any = i;
     }
     return best_fill >= 0 ? best_fill : best_any;
@@ -696,7 +1027,7 @@ int srwm_forward_variant(const void* x, const float* W0, void* y, float* W_T, in
 int srwm_variant_count(void) { return kNumVariants; }
 
 int srwm_variant_info(int i, int* d_in, int* d_out, int* io_dtype, int* waves, int* lanes_per_row,
-                      int* waves_per_simd, int* is_auto)
+                      int* waves_per_simd, int* schedule, int* is_auto)
 {
     if (i < 0 || i >= kNumVariants) return SRWM_ERR_ARG;
     const Variant& v = kVariants[i];
@@ -706,8 +1037,17 @@ int srwm_variant_info(int i, int* d_in, int* d_out, int* io_dtype, int* waves, i
     if (waves) *waves = v.nw;
     if (lanes_per_row) *lanes_per_row = v.p;
     if (waves_per_simd) *waves_per_simd = v.wpe;
+    if (schedule) *schedule = v.fused;
     if (is_auto) *is_auto = v.is_auto;
     return SRWM_OK;
+}
+
+int srwm_select_variant(int64_t d_in, int64_t d_out, int io_dtype, int64_t units)
+{
+    if (d_in < 1 || d_out < 1 || units < 0) return SRWM_ERR_SHAPE;
+    if (io_dtype != SRWM_IO_F32 && io_dtype != SRWM_IO_BF16) return SRWM_ERR_ARG;
+    const int vi = find_variant(d_in, d_out, io_dtype, -1, units);
+    return vi >= 0 ? vi : SRWM_ERR_UNSUPPORTED;
 }
 
 int srwm_supported(int64_t d_in, int64_t d_out, int io_dtype)

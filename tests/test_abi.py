@@ -46,7 +46,7 @@ def test_variant_table_covers_workloads():
     shapes = {(v["d_in"], v["d_out"], v["io_dtype"]) for v in vs}
     auto = {(v["d_in"], v["d_out"], v["io_dtype"]) for v in vs if v["auto"]}
     assert shapes == auto
-    assert _lib.load().srwm_variant_info(len(vs), None, None, None, None, None, None, None) == E_ARG
+    assert _lib.load().srwm_variant_info(len(vs), None, None, None, None, None, None, None, None) == E_ARG
 
 
 FAKE_X, FAKE_W0, FAKE_Y, FAKE_WT = 0x10000000, 0x20000000, 0x30000000, 0x40000000
@@ -88,6 +88,22 @@ def call(x=FAKE_X, W0=FAKE_W0, y=FAKE_Y, WT=FAKE_WT, B=2, T=3, H=2, d_in=16, d_o
 ])
 def test_validation_rejects(kw, code):
     assert call(**kw) == code
+
+
+def test_select_variant():
+    lib = _lib.load()
+    vs = _lib.variants()
+    for d, io, units in [(64, 1, 2048), (64, 0, 256), (128, 0, 32), (16, 0, 16), (8, 0, 1)]:
+        i = lib.srwm_select_variant(d, d, io, units)
+        assert 0 <= i < len(vs)
+        v = vs[i]
+        assert (v["d_in"], v["d_out"], v["io_dtype"]) == (d, d, "bf16" if io else "f32") and v["auto"]
+    # many units: the fewest waves per unit; few units: more waves per unit
+    assert vs[lib.srwm_select_variant(64, 64, 1, 2048)]["waves"] == 1
+    assert vs[lib.srwm_select_variant(64, 64, 0, 256)]["waves"] > 1
+    assert lib.srwm_select_variant(7, 7, 0, 4) == E_UNSUP
+    assert lib.srwm_select_variant(64, 64, 3, 4) == E_ARG
+    assert lib.srwm_select_variant(0, 64, 0, 4) == E_SHAPE
 
 
 def test_variant_must_match_shape():

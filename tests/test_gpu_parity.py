@@ -183,8 +183,18 @@ def test_continuation_from_state(name):
     ya, WA = run_gpu(np.ascontiguousarray(x[:, :T1]), W0, w.io_dtype, w.apply_input_softmax)
     yb, WB = run_gpu(np.ascontiguousarray(x[:, T1:]), np.ascontiguousarray(WA[0]), w.io_dtype,
                      w.apply_input_softmax)
-    np.testing.assert_array_equal(np.concatenate([ya, yb], 1), y)
-    np.testing.assert_array_equal(WB, WT)
+    v = _srwm().select_variant(w.d_in, w.d_out, w.io_dtype, w.units)
+    if v["schedule"] == "phased":
+        # the restarted run performs exactly the same operations
+        np.testing.assert_array_equal(np.concatenate([ya, yb], 1), y)
+        np.testing.assert_array_equal(WB, WT)
+    else:
+        # the fused schedule forms the first projection after the restart
+        # directly instead of through the rank-one correction: same value,
+        # different rounding
+        from tests._parity import rel_l2
+        assert rel_l2(np.concatenate([ya, yb], 1), y) < 1e-5
+        assert rel_l2(WB, WT) < 1e-5
 
 
 @pytest.mark.parametrize("gate", [0, 1, 2, 3])
@@ -202,3 +212,26 @@ def test_gate_to_block_assignment(gate):
             assert change <= 1e-6 * np.abs(W0[:, blk]).max(), (X, change)
         elif X < 3:
             assert change > 1e-4, (X, change)
+
+
+@pytest.mark.parametrize("name,flag", [("fewshot_d64", False), ("rl_d64_bf16", True), ("multitask_d16", False)])
+def test_bf16_output_is_rne_of_f32_path(name, flag):
+    # The same kernel geometry with fp32 and with bf16 I/O on the same
+    # bf16-representable x computes the same fp32 values; the bf16 path must
+    # store exactly their round-to-nearest-even bf16.
+    srwm = _srwm()
+    w = WORKLOADS[name].with_(B=2, T=77, io_dtype="bf16", apply_input_softmax=flag)
+    x = gen_x(w)
+    W0 = gen_W0(w)
+    vs = srwm.variants()
+    picked = 0
+    for vf in vs:
+        if vf["d_in"] != w.d_in or vf["d_out"] != w.d_out or vf["io_dtype"] != "f32":
+            continue
+        vb = next(v for v in vs if v["io_dtype"] == "bf16" and all(
+            v[k] == vf[k] for k in ("d_in", "d_out", "waves", "lanes_per_row", "waves_per_simd", "schedule")))
+        yf, _ = run_gpu(x, W0, "f32", flag, return_state=False, variant=vf["index"])
+        yb, _ = run_gpu(x, W0, "bf16", flag, return_state=False, variant=vb["index"])
+        np.testing.assert_array_equal(yb, round_to_bf16(yf))
+        picked += 1
+    assert picked >= 1
