@@ -56,11 +56,12 @@ def _load():
             f.argtypes = [p, ctypes.c_int, ctypes.c_int, p, p, p, p, p]
             f.restype = None
             f = getattr(lib, prefix + "step")
-            f.argtypes = [p, ctypes.c_int, ctypes.c_int, p, ctypes.c_int] + [p] * 8
+            f.argtypes = [p, ctypes.c_int, ctypes.c_int, ctypes.c_int, p, ctypes.c_int] + [p] * 8
             f.restype = None
             f = getattr(lib, prefix + "forward")
             f.argtypes = [p, p, p, p, ctypes.c_long, ctypes.c_long, ctypes.c_long,
-                          ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+                          ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                          ctypes.c_long, ctypes.c_int]
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -80,8 +81,8 @@ def default_threads() -> int:
         return os.cpu_count() or 1
 
 
-def m_rows(d_in: int, d_out: int) -> int:
-    return d_out + 2 * d_in + 4
+def m_rows(d_in: int, d_out: int, n_lr: int = 4) -> int:
+    return d_out + 2 * d_in + n_lr
 
 
 def delta_update(W, kh, qh, eta):
@@ -100,49 +101,60 @@ def delta_update(W, kh, qh, eta):
     return W, v, vb
 
 
-def step(W, x_t, d_out: int, apply_input_softmax: bool):
+def step(W, x_t, d_out: int, apply_input_softmax: bool, n_lr: int = 4):
     """One step on one unit.  Returns a dict with W (= W_t), y, u, z, kh, qh, g, v, vb."""
     lib = _load()
     W = np.array(W, dtype=np.float64, order="C", copy=True)
     m, d_in = W.shape
-    assert m == m_rows(d_in, d_out)
+    assert m == m_rows(d_in, d_out, n_lr)
     x_t = np.ascontiguousarray(x_t, dtype=np.float64)
     out = {k: np.empty(n) for k, n in (("y", d_out), ("u", d_in), ("z", m), ("kh", d_in),
-                                       ("qh", d_in), ("g", 4), ("v", m), ("vb", m))}
+                                       ("qh", d_in), ("g", n_lr), ("v", m), ("vb", m))}
     d = ctypes.c_double
-    lib.srwm_oracle_step(_ptr(W, d), d_in, d_out, _ptr(x_t, d), int(bool(apply_input_softmax)),
+    lib.srwm_oracle_step(_ptr(W, d), d_in, d_out, n_lr, _ptr(x_t, d), int(bool(apply_input_softmax)),
                          *[_ptr(out[k], d) for k in ("y", "u", "z", "kh", "qh", "g", "v", "vb")])
     out["W"] = W
     return out
 
 
-def _forward(prefix, npdtype, ctype, x, W0, apply_input_softmax, return_state, nthreads):
+def _forward(prefix, npdtype, ctype, x, W0, apply_input_softmax, return_state, nthreads,
+             n_lr, reset_interval):
     lib = _load()
     x = np.ascontiguousarray(x, dtype=npdtype)
     W0 = np.ascontiguousarray(W0, dtype=npdtype)
     B, T, H, d_in = x.shape
-    H2, m, d_in2 = W0.shape
+    per_seq = W0.ndim == 4
+    if per_seq:
+        B2, H2, m, d_in2 = W0.shape
+        assert B2 == B
+    else:
+        H2, m, d_in2 = W0.shape
     assert H2 == H and d_in2 == d_in
-    d_out = m - 2 * d_in - 4
+    d_out = m - 2 * d_in - n_lr
     assert d_out >= 1
     y = np.empty((B, T, H, d_out), dtype=npdtype)
     WT = np.empty((B, H, m, d_in), dtype=npdtype) if return_state else None
     n = default_threads() if nthreads is None else int(nthreads)
     rc = getattr(lib, prefix + "forward")(_ptr(x, ctype), _ptr(W0, ctype), _ptr(y, ctype),
-                                          _ptr(WT, ctype), B, T, H, d_in, d_out,
-                                          int(bool(apply_input_softmax)), n)
+                                          _ptr(WT, ctype), B, T, H, d_in, d_out, int(n_lr),
+                                          int(bool(apply_input_softmax)), int(per_seq),
+                                          int(reset_interval), n)
     if rc != 0:
         raise ValueError(f"oracle forward rejected its arguments (code {rc})")
     return y, WT
 
 
-def forward(x, W0, apply_input_softmax=False, return_state=True, nthreads=None):
-    """float64 oracle: x[B,T,H,d_in], W0[H,m,d_in] -> (y[B,T,H,d_out], W_T[B,H,m,d_in])."""
+def forward(x, W0, apply_input_softmax=False, return_state=True, nthreads=None, n_lr=4,
+            reset_interval=0):
+    """float64 oracle: x[B,T,H,d_in], W0[H,m,d_in] (shared) or W0[B,H,m,d_in]
+    (per sequence) -> (y[B,T,H,d_out], W_T[B,H,m,d_in]).  m = d_out+2*d_in+n_lr;
+    reset_interval R > 0 returns the state to W0 before every step t>0, t%R==0."""
     return _forward("srwm_oracle_", np.float64, ctypes.c_double, x, W0,
-                    apply_input_softmax, return_state, nthreads)
+                    apply_input_softmax, return_state, nthreads, n_lr, reset_interval)
 
 
-def forward_f32(x, W0, apply_input_softmax=False, return_state=True, nthreads=None):
+def forward_f32(x, W0, apply_input_softmax=False, return_state=True, nthreads=None, n_lr=4,
+                reset_interval=0):
     """The same definition evaluated in float32 (drift study only)."""
     return _forward("srwm_oracle_f32_", np.float32, ctypes.c_float, x, W0,
-                    apply_input_softmax, return_state, nthreads)
+                    apply_input_softmax, return_state, nthreads, n_lr, reset_interval)

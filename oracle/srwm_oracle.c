@@ -22,7 +22,7 @@
  *          Sec. 2.5 (W0 is the trained initial program).
  *
  *   Per (sequence b, head h) the state W is an m x d_in matrix,
- *   m = d_out + 2*d_in + 4, with row blocks [W^y; W^k; W^q; W^beta]
+ *   m = d_out + 2*d_in + 4 (4 learning rates), with row blocks [W^y; W^k; W^q; W^beta]
  *   ([ACL] 4-lr paragraph; [SRWM] Sec. 2.4).  Every unit starts from the
  *   shared W0[h] ([ACL] after Eq. (3); [SRWM] Sec. 2.5).  For t = 1..T:
  *
@@ -41,6 +41,16 @@
  *   pair swapped ("sigma( CLOSE ... OPEN beta_t )"); it is read as
  *   sigma(beta_t) (v_t - vb_t) outer phi(k_t), the only reading whose
  *   shapes agree, and the one the [SRWM] Sec. 2.1 prose spells out.
+ *
+ *   With one learning rate ([ACL] Eq. (1)-(3) as first written,
+ *   m = d_out + 2*d_in + 1) the single sigmoid(beta_t) gates every row.
+ *
+ *   Options beyond the shared-W0 forward ([SRWM] Sec. 3.3 and 4.5: the RL
+ *   state persists across truncation windows, and resetting it every 50
+ *   steps is the ablation that loses the benefit):
+ *     - a per-sequence initial state W0[b][h] instead of the shared W0[h];
+ *     - reset_interval R > 0: at every step t > 0 with t % R == 0 the state
+ *       returns to the initial matrix before the step is taken.
  *
  * softmax(s)_j = exp(s_j - max s) / sum_l exp(s_l - max s);
  * sigmoid(z)   = 1/(1+exp(-z)) for z >= 0, exp(z)/(1+exp(z)) otherwise.
@@ -104,6 +114,12 @@ static int row_block(int i, int d_in, int d_out)
     return 3;
 }
 
+/* Learning-rate index of row i: its block with four rates, 0 with one. */
+static int rate_of_row(int i, int d_in, int d_out, int n_lr)
+{
+    return n_lr == 1 ? 0 : row_block(i, d_in, d_out);
+}
+
 /*
  * Delta-rule self-update with the addresses given ([ACL] Eq. (2)-(3) and
  * (4)-(5); [SRWM] Sec. 2.3):
@@ -129,17 +145,18 @@ void FN(delta_update)(real* W, int rows, int d_in, const real* kh,
 }
 
 /*
- * One step of the recurrence on one unit.  W (m x d_in) is updated in place
- * from W_{t-1} to W_t.  x_t has d_in entries; y_t receives d_out entries.
- * Every other pointer may be NULL; when given it receives the step's
- * intermediate: u (d_in), z (m), kh, qh (d_in), g (4), v, vb (m).
+ * One step of the recurrence on one unit.  W (m x d_in, m = d_out + 2*d_in +
+ * n_lr, n_lr = 4 or 1) is updated in place from W_{t-1} to W_t.  x_t has d_in
+ * entries; y_t receives d_out entries.  Every other pointer may be NULL; when
+ * given it receives the step's intermediate: u (d_in), z (m), kh, qh (d_in),
+ * g (n_lr), v, vb (m).
  */
-void FN(step)(real* W, int d_in, int d_out, const real* x_t,
+void FN(step)(real* W, int d_in, int d_out, int n_lr, const real* x_t,
               int apply_input_softmax, real* y_t, real* u_out, real* z_out,
               real* kh_out, real* qh_out, real* g_out, real* v_out,
               real* vb_out)
 {
-    const int m = d_out + 2 * d_in + 4;
+    const int m = d_out + 2 * d_in + n_lr;
     real* buf = (real*)malloc(sizeof(real) * (size_t)(3 * d_in + 2 * m + 4));
     real* u = buf;
     real* kh = u + d_in;
@@ -163,13 +180,13 @@ void FN(step)(real* W, int d_in, int d_out, const real* x_t,
     /* The output comes from W_{t-1}, before the self-update. */
     for (int i = 0; i < d_out; ++i) y_t[i] = z[i];
 
-    /* phi = softmax on key and query; sigma on the four rate logits. */
+    /* phi = softmax on key and query; sigma on the rate logit(s). */
     softmax(z + d_out, d_in, kh);
     softmax(z + d_out + d_in, d_in, qh);
-    for (int c = 0; c < 4; ++c) g[c] = sigmoid(z[m - 4 + c]);
+    for (int c = 0; c < n_lr; ++c) g[c] = sigmoid(z[m - n_lr + c]);
 
-    /* Eq. (5): every row block uses its own learning rate. */
-    for (int i = 0; i < m; ++i) eta[i] = g[row_block(i, d_in, d_out)];
+    /* Eq. (5): every row block uses its own learning rate (Eq. (3): one). */
+    for (int i = 0; i < m; ++i) eta[i] = g[rate_of_row(i, d_in, d_out, n_lr)];
 
     /* Eq. (2) reads and Eq. (3) rank-one delta update. */
     FN(delta_update)(W, m, d_in, kh, qh, eta, v_out, vb_out);
@@ -178,71 +195,82 @@ void FN(step)(real* W, int d_in, int d_out, const real* x_t,
     if (z_out) memcpy(z_out, z, sizeof(real) * (size_t)m);
     if (kh_out) memcpy(kh_out, kh, sizeof(real) * (size_t)d_in);
     if (qh_out) memcpy(qh_out, qh, sizeof(real) * (size_t)d_in);
-    if (g_out) memcpy(g_out, g, sizeof(real) * 4);
+    if (g_out) memcpy(g_out, g, sizeof(real) * (size_t)n_lr);
     free(buf);
 }
 
 /*
  * Whole sequence for one unit.  x: T rows of d_in at row stride x_ld;
  * y: T rows of d_out at row stride y_ld; W0 and W_T: m x d_in (W_T may be
- * NULL).  T = 0 leaves y untouched and copies W0 to W_T.
+ * NULL).  T = 0 leaves y untouched and copies W0 to W_T.  reset_interval
+ * R > 0 returns the state to W0 before every step t > 0 with t % R == 0.
  */
 void FN(unit)(const real* x, ptrdiff_t x_ld, const real* W0, real* y,
               ptrdiff_t y_ld, real* W_T, long T, int d_in, int d_out,
-              int apply_input_softmax)
+              int n_lr, int apply_input_softmax, long reset_interval)
 {
-    const int m = d_out + 2 * d_in + 4;
+    const int m = d_out + 2 * d_in + n_lr;
     const size_t n = (size_t)m * d_in;
     real* W = (real*)malloc(sizeof(real) * n);
     memcpy(W, W0, sizeof(real) * n);
-    for (long t = 0; t < T; ++t)
-        FN(step)(W, d_in, d_out, x + t * x_ld, apply_input_softmax,
+    for (long t = 0; t < T; ++t) {
+        if (reset_interval > 0 && t > 0 && t % reset_interval == 0)
+            memcpy(W, W0, sizeof(real) * n);
+        FN(step)(W, d_in, d_out, n_lr, x + t * x_ld, apply_input_softmax,
                  y + t * y_ld, NULL, NULL, NULL, NULL, NULL, NULL, NULL);
+    }
     if (W_T) memcpy(W_T, W, sizeof(real) * n);
     free(W);
 }
 
-/* Batched forward: x[B][T][H][d_in], W0[H][m][d_in], y[B][T][H][d_out],
- * W_T[B][H][m][d_in] (or NULL).  The (b, h) units are independent
- * ([SRWM] Sec. 2.4: each head runs on its own); they are spread over
- * nthreads POSIX threads, each unit evaluated sequentially in t. */
+/* Batched forward: x[B][T][H][d_in], W0[H][m][d_in] (or W0[B][H][m][d_in]
+ * with w0_per_sequence), y[B][T][H][d_out], W_T[B][H][m][d_in] (or NULL).
+ * The (b, h) units are independent ([SRWM] Sec. 2.4: each head runs on its
+ * own); they are spread over nthreads POSIX threads, each unit evaluated
+ * sequentially in t. */
 typedef struct {
     const real* x;
     const real* W0;
     real* y;
     real* W_T;
     long B, T, H;
-    int d_in, d_out, flag;
+    int d_in, d_out, n_lr, flag, w0_per_seq;
+    long reset_interval;
     long first, stride;
 } job_t;
 
 static void* run_job(void* p)
 {
     const job_t* jb = (const job_t*)p;
-    const long m = jb->d_out + 2L * jb->d_in + 4;
+    const long m = jb->d_out + 2L * jb->d_in + jb->n_lr;
     for (long u = jb->first; u < jb->B * jb->H; u += jb->stride) {
         const long b = u / jb->H, h = u % jb->H;
         const real* x = jb->x + (b * jb->T * jb->H + h) * jb->d_in;
         real* y = jb->y + (b * jb->T * jb->H + h) * jb->d_out;
         real* wt = jb->W_T ? jb->W_T + (b * jb->H + h) * m * jb->d_in : NULL;
-        FN(unit)(x, jb->H * jb->d_in, jb->W0 + h * m * jb->d_in, y,
-                 jb->H * jb->d_out, wt, jb->T, jb->d_in, jb->d_out, jb->flag);
+        const real* w0 = jb->W0 + (jb->w0_per_seq ? u : h) * m * jb->d_in;
+        FN(unit)(x, jb->H * jb->d_in, w0, y, jb->H * jb->d_out, wt, jb->T,
+                 jb->d_in, jb->d_out, jb->n_lr, jb->flag, jb->reset_interval);
     }
     return NULL;
 }
 
 int FN(forward)(const real* x, const real* W0, real* y, real* W_T, long B,
-                long T, long H, int d_in, int d_out, int apply_input_softmax,
-                int nthreads)
+                long T, long H, int d_in, int d_out, int n_lr,
+                int apply_input_softmax, int w0_per_sequence,
+                long reset_interval, int nthreads)
 {
     if (B < 0 || T < 0 || H < 0 || d_in < 1 || d_out < 1) return -1;
+    if (n_lr != 1 && n_lr != 4) return -1;
+    if (reset_interval < 0) return -1;
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 256) nthreads = 256;
     pthread_t th[256];
     job_t jobs[256];
     for (int i = 0; i < nthreads; ++i) {
-        jobs[i] = (job_t){x, W0, y, W_T, B, T, H, d_in, d_out,
-                          apply_input_softmax, i, nthreads};
+        jobs[i] = (job_t){x, W0, y, W_T, B, T, H, d_in, d_out, n_lr,
+                          apply_input_softmax, w0_per_sequence,
+                          reset_interval, i, nthreads};
     }
     int started = 0;
     for (int i = 1; i < nthreads; ++i) {

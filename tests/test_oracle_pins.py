@@ -304,3 +304,92 @@ def test_zero_length_sequence():
     y, WT = oracle.forward(x, W0, False)
     assert y.shape == (3, 0, 2, 4)
     np.testing.assert_array_equal(WT, np.broadcast_to(W0, WT.shape))
+
+
+# ---------------------------------------------------------------------------
+# One learning rate ([ACL] Eq. (1)-(3) as first written, m = d_out+2*d_in+1).
+def _brute_force_d2_one_rate(x, W0, flag):
+    # Same (sum, difference) expansion as above with one gate for all 7 rows.
+    mpmath.mp.dps = 50
+    s = [mpmath.mpf(float(r[0])) + mpmath.mpf(float(r[1])) for r in W0]
+    dl = [mpmath.mpf(float(r[0])) - mpmath.mpf(float(r[1])) for r in W0]
+    ys = []
+    for x1, x2 in x:
+        x1, x2 = mpmath.mpf(float(x1)), mpmath.mpf(float(x2))
+        u1, u2 = (_sig(x1 - x2), _sig(x2 - x1)) if flag else (x1, x2)
+        z = [s[i] * (u1 + u2) / 2 + dl[i] * (u1 - u2) / 2 for i in range(7)]
+        ys.append([z[0], z[1]])
+        kh1, qh1, g = _sig(z[2] - z[3]), _sig(z[4] - z[5]), _sig(z[6])
+        for i in range(7):
+            c = g * dl[i] * (qh1 - kh1)
+            s[i], dl[i] = s[i] + c, dl[i] + c * (2 * kh1 - 1)
+    W = [[(s[i] + dl[i]) / 2, (s[i] - dl[i]) / 2] for i in range(7)]
+    return (np.array([[float(v) for v in r] for r in ys]),
+            np.array([[float(v) for v in r] for r in W]))
+
+
+@pytest.mark.parametrize("flag", [False, True])
+def test_one_rate_brute_force_d2(flag):
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((3, 2)) * 1.5
+    W0 = rng.standard_normal((7, 2)) * 1.2
+    y_bf, W_bf = _brute_force_d2_one_rate(x, W0, flag)
+    y, WT = oracle.forward(x.reshape(1, 3, 1, 2), W0.reshape(1, 7, 2), flag, n_lr=1)
+    np.testing.assert_allclose(y[0, :, 0], y_bf, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(WT[0, 0], W_bf, rtol=1e-12, atol=1e-13)
+
+
+# Four identical rate rows make the four rates equal at every step (identical
+# rows read identical values and get identical updates), which is exactly the
+# one-rate recurrence with that row.
+@pytest.mark.parametrize("flag", [False, True])
+def test_one_rate_equals_four_equal_rates(flag):
+    rng = np.random.default_rng(22)
+    d_in, d_out = 5, 3
+    x, W4 = _rand_problem(rng, 2, 15, 2, d_in, d_out)
+    W4[:, -4:] = W4[:, -1:]
+    W1 = np.ascontiguousarray(W4[:, :-3])
+    y4, T4 = oracle.forward(x, W4, flag)
+    y1, T1 = oracle.forward(x, W1, flag, n_lr=1)
+    np.testing.assert_array_equal(y4, y1)
+    np.testing.assert_array_equal(T4[..., :-3, :], T1)
+    for i in range(3):
+        np.testing.assert_array_equal(T4[..., -4 + i, :], T4[..., -1, :])
+
+
+# ---------------------------------------------------------------------------
+# Per-sequence initial state and state carry ([SRWM] Sec. 3.3: the state
+# persists to the end of the episode across truncation windows).
+def test_per_sequence_initial_state():
+    rng = np.random.default_rng(23)
+    x, W0 = _rand_problem(rng, 3, 10, 2, 6, 4)
+    y, WT = oracle.forward(x, W0, False)
+    yb, WTb = oracle.forward(x, np.ascontiguousarray(np.broadcast_to(W0, (3,) + W0.shape)), False)
+    np.testing.assert_array_equal(yb, y)
+    np.testing.assert_array_equal(WTb, WT)
+    # continuation of a whole batch from its own final states
+    ya, WA = oracle.forward(x[:, :4], W0, False)
+    yc, WC = oracle.forward(x[:, 4:], WA, False)
+    np.testing.assert_array_equal(np.concatenate([ya, yc], 1), y)
+    np.testing.assert_array_equal(WC, WT)
+    # different initial states per sequence give different outputs
+    W0s = np.ascontiguousarray(np.stack([W0, W0 * 0.5, W0 * 2.0]))
+    ys, _ = oracle.forward(x, W0s, False)
+    np.testing.assert_array_equal(ys[0], y[0])
+    assert np.abs(ys[1] - y[1]).max() > 1e-6
+
+
+# Reset ablation ([SRWM] Sec. 4.5): resetting every R steps equals independent
+# runs of the windows [0,R), [R,2R), ... each from W0.
+@pytest.mark.parametrize("flag", [False, True])
+def test_reset_interval_is_independent_windows(flag):
+    rng = np.random.default_rng(24)
+    x, W0 = _rand_problem(rng, 2, 23, 2, 6, 4)
+    R = 7
+    y, WT = oracle.forward(x, W0, flag, reset_interval=R)
+    parts = [oracle.forward(np.ascontiguousarray(x[:, a:a + R]), W0, flag) for a in range(0, 23, R)]
+    np.testing.assert_array_equal(y, np.concatenate([p[0] for p in parts], 1))
+    np.testing.assert_array_equal(WT, parts[-1][1])
+    y0, _ = oracle.forward(x, W0, flag)
+    np.testing.assert_array_equal(y[:, :R], y0[:, :R])
+    assert np.abs(y[:, R:] - y0[:, R:]).max() > 1e-6
