@@ -9,6 +9,37 @@ LIB_PATH = Path(__file__).resolve().parent / "libsrwm.so"
 SRWM_IO_F32 = 0
 SRWM_IO_BF16 = 1
 
+
+class ForwardArgs(ctypes.Structure):
+    """srwm_forward_args_t."""
+    _fields_ = [
+        ("x", ctypes.c_void_p),
+        ("W0", ctypes.c_void_p),
+        ("y", ctypes.c_void_p),
+        ("W_T", ctypes.c_void_p),
+        ("B", ctypes.c_int64),
+        ("T", ctypes.c_int64),
+        ("H", ctypes.c_int64),
+        ("d_in", ctypes.c_int64),
+        ("d_out", ctypes.c_int64),
+        ("m", ctypes.c_int64),
+        ("io_dtype", ctypes.c_int),
+        ("apply_input_softmax", ctypes.c_int),
+        ("n_lr", ctypes.c_int),
+        ("w0_per_sequence", ctypes.c_int),
+        ("reset_interval", ctypes.c_int64),
+        ("variant", ctypes.c_int),
+        ("stream", ctypes.c_void_p),
+    ]
+
+
+class VariantInfo(ctypes.Structure):
+    """srwm_variant_info_t."""
+    _fields_ = [(name, ctypes.c_int) for name in (
+        "d_in", "d_out", "io_dtype", "n_lr", "waves", "lanes_per_row", "waves_per_simd",
+        "schedule", "supports_reset", "is_auto")]
+
+
 _lib = None
 
 
@@ -28,14 +59,15 @@ def load() -> ctypes.CDLL:
     lib.srwm_forward.restype = ci
     lib.srwm_forward_variant.argtypes = fwd_args + [ci]
     lib.srwm_forward_variant.restype = ci
+    lib.srwm_forward_ex.argtypes = [ctypes.POINTER(ForwardArgs)]
+    lib.srwm_forward_ex.restype = ci
     lib.srwm_variant_count.argtypes = []
     lib.srwm_variant_count.restype = ci
-    ip = ctypes.POINTER(ci)
-    lib.srwm_variant_info.argtypes = [ci, ip, ip, ip, ip, ip, ip, ip, ip]
+    lib.srwm_variant_info.argtypes = [ci, ctypes.POINTER(VariantInfo)]
     lib.srwm_variant_info.restype = ci
-    lib.srwm_select_variant.argtypes = [i64, i64, ci, i64]
+    lib.srwm_select_variant.argtypes = [i64, i64, ci, ci, i64, i64]
     lib.srwm_select_variant.restype = ci
-    lib.srwm_supported.argtypes = [i64, i64, ci]
+    lib.srwm_supported.argtypes = [i64, i64, ci, ci]
     lib.srwm_supported.restype = ci
     lib.srwm_strerror.argtypes = [ci]
     lib.srwm_strerror.restype = ctypes.c_char_p
@@ -53,12 +85,13 @@ def variants() -> list[dict]:
     lib = load()
     out = []
     for i in range(lib.srwm_variant_count()):
-        vals = [ctypes.c_int() for _ in range(8)]
-        rc = lib.srwm_variant_info(i, *[ctypes.byref(v) for v in vals])
+        info = VariantInfo()
+        rc = lib.srwm_variant_info(i, ctypes.byref(info))
         assert rc == 0
-        d_in, d_out, io, nw, p, wpe, sched, auto = (v.value for v in vals)
-        out.append(dict(index=i, d_in=d_in, d_out=d_out,
-                        io_dtype="bf16" if io == SRWM_IO_BF16 else "f32",
-                        waves=nw, lanes_per_row=p, waves_per_simd=wpe,
-                        schedule="fused" if sched else "phased", auto=bool(auto)))
+        out.append(dict(index=i, d_in=info.d_in, d_out=info.d_out,
+                        io_dtype="bf16" if info.io_dtype == SRWM_IO_BF16 else "f32",
+                        n_lr=info.n_lr, waves=info.waves, lanes_per_row=info.lanes_per_row,
+                        waves_per_simd=info.waves_per_simd,
+                        schedule="fused" if info.schedule else "phased",
+                        supports_reset=bool(info.supports_reset), auto=bool(info.is_auto)))
     return out

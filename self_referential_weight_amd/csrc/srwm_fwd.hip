@@ -201,18 +201,20 @@ __device__ __forceinline__ void store_f32(float* __restrict__ dst, const float (
 // Compile-time geometry of one kernel variant.
 //
 // Main rows (the y, k and q blocks, MAIN = d_out + 2*d_in rows) use the
-// strided lane layout described at the top of the file.  The four beta rows
-// use one of two layouts:
+// strided lane layout described at the top of the file.  The NLR rate rows
+// (four, or one in the one-rate form) use one of two layouts:
 //   BETA_SEP (d_in % 16 == 0): wave 0 holds them, DPP row i (lanes 16i..16i+15)
-//     holding beta row i, LB = d_in/16 consecutive columns per lane; a beta
+//     holding rate row i, LB = d_in/16 consecutive columns per lane; a rate
 //     row's dot product is then a 16-lane DPP sum inside one DPP row, and the
 //     lanes that need its learning-rate term are the ones that computed it.
+//     With one rate, DPP rows 1-3 hold zeros and store nothing.
 //   otherwise: they are appended to the main rows (one extra register row,
 //     zero padded), which only the small test shapes use.
-template <int D_IN, int D_OUT, int NW, int P>
+template <int D_IN, int D_OUT, int NW, int P, int NLR = 4>
 struct Geom {
-    static constexpr int NT = NW * kWave;          // threads per unit
-    static constexpr int M = D_OUT + 2 * D_IN + 4; // rows of W
+    static_assert(NLR == 1 || NLR == 4, "one or four learning rates");
+    static constexpr int NT = NW * kWave;            // threads per unit
+    static constexpr int M = D_OUT + 2 * D_IN + NLR; // rows of W
     static constexpr int MAIN = D_OUT + 2 * D_IN;  // y, k, q rows
     static constexpr bool BETA_SEP = (D_IN % 16 == 0);
     static constexpr int ROWS = BETA_SEP ? MAIN : M; // rows in the strided layout
@@ -235,16 +237,20 @@ struct Geom {
     static_assert(D_IN % E == 0, "E must divide d_in");
     static_assert(LR <= 16 && (LR & (LR - 1)) == 0, "row lanes");
     static_assert(G >= 4, "need at least four row groups");
-    // Row block (0 y, 1 k, 2 q, 3 beta) of register r when ALIGNED.
-    static constexpr int block_of_reg(int r)
+    // Learning-rate index of register r when ALIGNED: the row block (0 y,
+    // 1 k, 2 q, 3 beta) with four rates, 0 with one.
+    static constexpr int rate_of_reg(int r)
     {
         const int row = G * r;
+        if (NLR == 1) return 0;
         return row < D_OUT ? 0 : row < D_OUT + D_IN ? 1 : row < D_OUT + 2 * D_IN ? 2 : 3;
     }
 };
 
-__device__ __forceinline__ int block_of_row(int row, int d_in, int d_out)
+template <int NLR>
+__device__ __forceinline__ int rate_of_row(int row, int d_in, int d_out)
 {
+    if (NLR == 1) return 0;
     return row < d_out ? 0 : row < d_out + d_in ? 1 : row < d_out + 2 * d_in ? 2 : 3;
 }
 
@@ -351,16 +357,20 @@ struct XStage {
     using Gm = Geom<D_IN, D_OUT, NW, P>;
     static constexpr int E = Gm::E, LR = Gm::LR, S = Gm::S;
     static constexpr int XR = BF16 ? (E + 1) / 2 : E; // registers held per lane
+    using XT = typename std::conditional<BF16, uint16_t, float>::type;
     uint32_t xr[XR];
     int row, col;
+    uint32_t lane_off;  // element offset of this lane's piece within a chunk
     bool active;
-    const void* __restrict__ xv;
-    int64_t x0, x_step;
+    const XT* __restrict__ xu;  // x[b][0][h][0] (wave-uniform)
+    int64_t x_step;
     int T;
 
     __device__ __forceinline__ XStage(int tid, const void* __restrict__ xv_, int64_t x0_, int64_t x_step_, int T_)
-        : row(tid / LR), col((tid % LR) * E), active(tid < S * LR), xv(xv_), x0(x0_), x_step(x_step_), T(T_)
+        : row(tid / LR), col((tid % LR) * E), active(tid < S * LR),
+          xu(reinterpret_cast<const XT*>(xv_) + x0_), x_step(x_step_), T(T_)
     {
+        lane_off = static_cast<uint32_t>(row * x_step + col);
     }
 
     // Issue the global loads of the chunk that starts at step c0.
@@ -368,8 +378,8 @@ struct XStage {
     {
         const int t = c0 + row;
         if (active && t < T) {
+            const XT* src = xu + (int64_t)c0 * x_step + lane_off;
             if constexpr (BF16) {
-                const uint16_t* src = reinterpret_cast<const uint16_t*>(xv) + x0 + (int64_t)t * x_step + col;
                 if constexpr (E % 8 == 0) {
 #pragma unroll
                     for (int i = 0; i < E / 8; ++i) {
@@ -388,7 +398,6 @@ struct XStage {
                     }
                 }
             } else {
-                const float* src = reinterpret_cast<const float*>(xv) + x0 + (int64_t)t * x_step + col;
                 float tmp[E];
                 load_f32<E>(src, tmp);
 #pragma unroll
@@ -449,13 +458,14 @@ __device__ __forceinline__ void store_y(void* __restrict__ yv, int64_t off, cons
 // ----------------------------------------------------------------------------
 // The kernel: grid = B*H workgroups (unit = b*H + h), NW*64 threads each.
 // WPE is the occupancy (waves per SIMD) the register allocation must allow.
-template <int D_IN, int D_OUT, int NW, int P, int WPE, bool BF16>
+template <int D_IN, int D_OUT, int NW, int P, int WPE, int NLR, bool RESET, bool BF16>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * kWave, NW * kWave),
                           amdgpu_waves_per_eu(WPE)))
 void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
-                     void* __restrict__ yv, float* __restrict__ WT, int T, int H, int in_softmax)
+                     void* __restrict__ yv, float* __restrict__ WT, int T, int H, int in_softmax,
+                     int w0_per_seq, int reset_interval)
 {
-    using Gm = Geom<D_IN, D_OUT, NW, P>;
+    using Gm = Geom<D_IN, D_OUT, NW, P, NLR>;
     constexpr int M = Gm::M, MAIN = Gm::MAIN, ROWS = Gm::ROWS;
     constexpr int L = Gm::L, G = Gm::G, R = Gm::R, LB = Gm::LB;
     constexpr int S = Gm::S;
@@ -482,27 +492,36 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
     const int64_t y_step = (int64_t)H * D_OUT;
     const int64_t x0 = ((int64_t)b * T * H + h) * D_IN;
     const int64_t y0 = ((int64_t)b * T * H + h) * D_OUT;
-    const float* __restrict__ w0h = W0 + (int64_t)h * M * D_IN;
+    const float* __restrict__ w0h = W0 + (int64_t)(w0_per_seq ? unit : h) * M * D_IN;
 
-    // ---- a0: W <- W0[h] into registers.
+    // ---- a0: W <- W0 into registers (again at each reset of the ablation).
     float w[R][L];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int row = rg + G * r;
-        if (row < ROWS) {
-            load_f32<L>(w0h + (int64_t)row * D_IN + p * L, w[r]);
-        } else {
-#pragma unroll
-            for (int c = 0; c < L; ++c) w[r][c] = 0.f;
-        }
-    }
-    // beta rows (BETA_SEP): wave 0, lane -> row MAIN + lane/16, cols bcol..bcol+LB
     const int bcol = (lane & 15) * (LB > 0 ? LB : 1);
     const int brow = lane >> 4;
     float wb[LB > 0 ? LB : 1];
-    if constexpr (BETA_SEP) {
-        if (wave == 0) load_f32<LB>(w0h + (int64_t)(MAIN + brow) * D_IN + bcol, wb);
-    }
+    auto load_w0 = [&]() {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = rg + G * r;
+            if (row < ROWS) {
+                load_f32<L>(w0h + (int64_t)row * D_IN + p * L, w[r]);
+            } else {
+#pragma unroll
+                for (int c = 0; c < L; ++c) w[r][c] = 0.f;
+            }
+        }
+        if constexpr (BETA_SEP) {
+            if (wave == 0) {
+                if (brow < NLR) {
+                    load_f32<LB>(w0h + (int64_t)(MAIN + brow) * D_IN + bcol, wb);
+                } else {
+#pragma unroll
+                    for (int c = 0; c < LB; ++c) wb[c] = 0.f;
+                }
+            }
+        }
+    };
+    load_w0();
 
     XStage<D_IN, D_OUT, NW, P, BF16> xs(tid, xv, x0, x_step, T);
 
@@ -516,12 +535,25 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
         __syncthreads();
 
         int chunk = 0;
+        int until_reset = reset_interval;  // steps left before the next reset
+        (void)until_reset;
         for (int c0 = 0; c0 < T; c0 += S, ++chunk) {
             const int n = (T - c0) < S ? (T - c0) : S;
             const float* sxc = &s_x[chunk & 1][0][0];
             for (int s = 0; s < n; ++s) {
                 const int t = c0 + s;
                 const float* __restrict__ urow = sxc + s * D_IN;
+                if constexpr (RESET) {
+                    // Reset ablation of the review page (Sec. 4.5): before every
+                    // step t > 0 with t % R == 0 the state returns to W0.
+                    if (reset_interval > 0) {
+                        if (until_reset == 0) {
+                            load_w0();
+                            until_reset = reset_interval;
+                        }
+                        --until_reset;
+                    }
+                }
                 // ---- (A) Eq. (1): z = W u.
                 float* __restrict__ zt = s_z[t & 1];
                 float acc[R];
@@ -548,7 +580,7 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
                         float accb = 0.f;
                         stream_lds<LB>(urow + bcol, [&](int c, float uc) { accb = fmaf(wb[c], uc, accb); });
                         accb = group_sum<16>(accb);
-                        if ((lane & 15) == 0) zt[MAIN + brow] = accb;
+                        if ((lane & 15) == 0 && brow < NLR) zt[MAIN + brow] = accb;
                     }
                 }
                 __syncthreads();
@@ -556,7 +588,7 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
                 // ---- (B) phi(k), phi(q), sigma(beta), computed by every wave for
                 // itself (identical bits in every wave); y_t from W_{t-1}.
                 wave_addresses<D_IN>(zt + D_OUT, zt + D_OUT + D_IN, s_kh[wave], s_e[wave], lane);
-                const float gl = sigmoid_f32(zt[MAIN + (lane & 3)]);
+                const float gl = sigmoid_f32(zt[MAIN + (NLR == 4 ? (lane & 3) : 0)]);
                 const float g0 = readlane(gl, 0), g1 = readlane(gl, 1), g2 = readlane(gl, 2), g3 = readlane(gl, 3);
                 if (wave == WAVE_AUX) store_y<D_OUT, BF16>(yv, y0 + (int64_t)t * y_step, zt, lane);
                 wave_sync();
@@ -574,10 +606,10 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
                 for (int r = 0; r < R; ++r) {
                     float gate;
                     if constexpr (Gm::ALIGNED) {
-                        const int bk = Gm::block_of_reg(r);
+                        const int bk = Gm::rate_of_reg(r);
                         gate = bk == 0 ? g0 : bk == 1 ? g1 : bk == 2 ? g2 : g3;
                     } else {
-                        const int bk = block_of_row(rg + G * r, D_IN, D_OUT);
+                        const int bk = rate_of_row<NLR>(rg + G * r, D_IN, D_OUT);
                         gate = bk == 0 ? g0 : bk == 1 ? g1 : bk == 2 ? g2 : g3;
                     }
                     acc[r] = gate * group_sum<P>(acc[r]);
@@ -616,7 +648,7 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
             if (row < ROWS) store_f32<L>(wdst + (int64_t)row * D_IN + p * L, w[r]);
         }
         if constexpr (BETA_SEP) {
-            if (wave == 0) store_f32<LB>(wdst + (int64_t)(MAIN + brow) * D_IN + bcol, wb);
+            if (wave == 0 && brow < NLR) store_f32<LB>(wdst + (int64_t)(MAIN + brow) * D_IN + bcol, wb);
         }
     }
 }
@@ -631,13 +663,14 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
 // deferred to the next iteration, where it runs between the barrier and the
 // fused pass and fills the latency of the softmax chain.  One workgroup
 // barrier per step.
-template <int D_IN, int D_OUT, int NW, int P, int WPE, bool BF16>
+template <int D_IN, int D_OUT, int NW, int P, int WPE, int NLR, bool BF16>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * kWave, NW * kWave),
                           amdgpu_waves_per_eu(WPE)))
 void srwm_fwd_fused_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
-                           void* __restrict__ yv, float* __restrict__ WT, int T, int H, int in_softmax)
+                           void* __restrict__ yv, float* __restrict__ WT, int T, int H, int in_softmax,
+                           int w0_per_seq, int /*reset_interval: not supported by this schedule*/)
 {
-    using Gm = Geom<D_IN, D_OUT, NW, P>;
+    using Gm = Geom<D_IN, D_OUT, NW, P, NLR>;
     constexpr int M = Gm::M, MAIN = Gm::MAIN, ROWS = Gm::ROWS;
     constexpr int L = Gm::L, G = Gm::G, R = Gm::R, LB = Gm::LB;
     constexpr int S = Gm::S;
@@ -663,7 +696,7 @@ void srwm_fwd_fused_kernel(const void* __restrict__ xv, const float* __restrict_
     const int64_t y_step = (int64_t)H * D_OUT;
     const int64_t x0 = ((int64_t)b * T * H + h) * D_IN;
     const int64_t y0 = ((int64_t)b * T * H + h) * D_OUT;
-    const float* __restrict__ w0h = W0 + (int64_t)h * M * D_IN;
+    const float* __restrict__ w0h = W0 + (int64_t)(w0_per_seq ? unit : h) * M * D_IN;
 
     // ---- a0: W <- W0[h].
     float w[R][L];
@@ -681,7 +714,14 @@ void srwm_fwd_fused_kernel(const void* __restrict__ xv, const float* __restrict_
     const int brow = lane >> 4;
     float wb[LB > 0 ? LB : 1];
     if constexpr (BETA_SEP) {
-        if (wave == 0) load_f32<LB>(w0h + (int64_t)(MAIN + brow) * D_IN + bcol, wb);
+        if (wave == 0) {
+            if (brow < NLR) {
+                load_f32<LB>(w0h + (int64_t)(MAIN + brow) * D_IN + bcol, wb);
+            } else {
+#pragma unroll
+                for (int c = 0; c < LB; ++c) wb[c] = 0.f;
+            }
+        }
     }
     float gate_of[R];  // filled per step: the learning rate of register r
 
@@ -713,7 +753,7 @@ void srwm_fwd_fused_kernel(const void* __restrict__ xv, const float* __restrict_
                     float accb = 0.f;
                     stream_lds<LB>(u0 + bcol, [&](int c, float uc) { accb = fmaf(wb[c], uc, accb); });
                     accb = group_sum<16>(accb);
-                    if ((lane & 15) == 0) s_z[0][MAIN + brow] = accb;
+                    if ((lane & 15) == 0 && brow < NLR) s_z[0][MAIN + brow] = accb;
                 }
             }
         }
@@ -737,7 +777,7 @@ void srwm_fwd_fused_kernel(const void* __restrict__ xv, const float* __restrict_
             float* __restrict__ khw = s_kh[t & 1][wave];
             float* __restrict__ ew = s_e[wave];
             wave_addresses<D_IN>(zt + D_OUT, zt + D_OUT + D_IN, khw, ew, lane);
-            const float gl = sigmoid_f32(zt[MAIN + (lane & 3)]);
+            const float gl = sigmoid_f32(zt[MAIN + (NLR == 4 ? (lane & 3) : 0)]);
             const float g0 = readlane(gl, 0), g1 = readlane(gl, 1), g2 = readlane(gl, 2), g3 = readlane(gl, 3);
             if (wave == 1) store_y<D_OUT, BF16>(yv, y0 + (int64_t)t * y_step, zt, lane);
 
@@ -764,10 +804,10 @@ void srwm_fwd_fused_kernel(const void* __restrict__ xv, const float* __restrict_
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 if constexpr (Gm::ALIGNED) {
-                    const int bk = Gm::block_of_reg(r);
+                    const int bk = Gm::rate_of_reg(r);
                     gate_of[r] = bk == 0 ? g0 : bk == 1 ? g1 : bk == 2 ? g2 : g3;
                 } else {
-                    const int bk = block_of_row(rg + G * r, D_IN, D_OUT);
+                    const int bk = rate_of_row<NLR>(rg + G * r, D_IN, D_OUT);
                     gate_of[r] = bk == 0 ? g0 : bk == 1 ? g1 : bk == 2 ? g2 : g3;
                 }
             }
@@ -823,7 +863,7 @@ void srwm_fwd_fused_kernel(const void* __restrict__ xv, const float* __restrict_
                     ab_prev = g3 * group_sum<16>(br);
                     if (has_next) {
                         const float z = fmaf(ab_prev, ct, group_sum<16>(bz));
-                        if ((lane & 15) == 0) zn[MAIN + brow] = z;
+                        if ((lane & 15) == 0 && brow < NLR) zn[MAIN + brow] = z;
                     }
                 }
             }
@@ -858,68 +898,87 @@ void srwm_fwd_fused_kernel(const void* __restrict__ xv, const float* __restrict_
             if (row < ROWS) store_f32<L>(wdst + (int64_t)row * D_IN + p * L, w[r]);
         }
         if constexpr (BETA_SEP) {
-            if (wave == 0) store_f32<LB>(wdst + (int64_t)(MAIN + brow) * D_IN + bcol, wb);
+            if (wave == 0 && brow < NLR) store_f32<LB>(wdst + (int64_t)(MAIN + brow) * D_IN + bcol, wb);
         }
     }
 }
 
 // ----------------------------------------------------------------------------
 // Variant table.
-using KernelFn = void (*)(const void*, const float*, void*, float*, int, int, int);
+using KernelFn = void (*)(const void*, const float*, void*, float*, int, int, int, int, int);
 
 struct Variant {
-    int d_in, d_out, io, nw, p, wpe, fused, is_auto;
+    int d_in, d_out, io, nw, p, wpe, nlr, fused, reset, is_auto;
     KernelFn fn;
 };
 
-template <int D_IN, int D_OUT, int NW, int P, int WPE, bool FUSED, bool BF16>
+// SCHED: 0 phased, 1 phased with the reset ablation, 2 fused.
+template <int D_IN, int D_OUT, int NW, int P, int WPE, int NLR, int SCHED, bool BF16>
 constexpr Variant make_variant(int is_auto)
 {
-    if constexpr (FUSED)
-        return Variant{D_IN, D_OUT, BF16 ? SRWM_IO_BF16 : SRWM_IO_F32, NW, P, WPE, 1, is_auto,
-                       &srwm_fwd_fused_kernel<D_IN, D_OUT, NW, P, WPE, BF16>};
+    constexpr int io = BF16 ? SRWM_IO_BF16 : SRWM_IO_F32;
+    if constexpr (SCHED == 2)
+        return Variant{D_IN, D_OUT, io, NW, P, WPE, NLR, 1, 0, is_auto,
+                       &srwm_fwd_fused_kernel<D_IN, D_OUT, NW, P, WPE, NLR, BF16>};
     else
-        return Variant{D_IN, D_OUT, BF16 ? SRWM_IO_BF16 : SRWM_IO_F32, NW, P, WPE, 0, is_auto,
-                       &srwm_fwd_kernel<D_IN, D_OUT, NW, P, WPE, BF16>};
+        return Variant{D_IN, D_OUT, io, NW, P, WPE, NLR, 0, SCHED == 1, is_auto,
+                       &srwm_fwd_kernel<D_IN, D_OUT, NW, P, WPE, NLR, SCHED == 1, BF16>};
 }
 
-#define SRWM_BOTH_IO(DI, DO, NW, P, WPE, AUTO) \
-    make_variant<DI, DO, NW, P, WPE, false, false>(AUTO), make_variant<DI, DO, NW, P, WPE, false, true>(AUTO)
-#define SRWM_BOTH_IO_FUSED(DI, DO, NW, P, WPE, AUTO) \
-    make_variant<DI, DO, NW, P, WPE, true, false>(AUTO), make_variant<DI, DO, NW, P, WPE, true, true>(AUTO)
+// Both I/O dtypes of one geometry: (d_in, d_out, waves per unit, lanes per
+// row, waves per SIMD the registers allow, learning rates, eligible for the
+// automatic choice).  _RESET variants also implement the reset ablation.
+#define SRWM_BOTH_IO(DI, DO, NW, P, WPE, NLR, AUTO)                   \
+    make_variant<DI, DO, NW, P, WPE, NLR, 0, false>(AUTO),             \
+        make_variant<DI, DO, NW, P, WPE, NLR, 0, true>(AUTO)
+#define SRWM_BOTH_IO_RESET(DI, DO, NW, P, WPE, NLR, AUTO)             \
+    make_variant<DI, DO, NW, P, WPE, NLR, 1, false>(AUTO),             \
+        make_variant<DI, DO, NW, P, WPE, NLR, 1, true>(AUTO)
+#define SRWM_BOTH_IO_FUSED(DI, DO, NW, P, WPE, NLR, AUTO)             \
+    make_variant<DI, DO, NW, P, WPE, NLR, 2, false>(AUTO),             \
+        make_variant<DI, DO, NW, P, WPE, NLR, 2, true>(AUTO)
 
-// (d_in, d_out, waves per unit, lanes per row, waves per SIMD the registers
-// allow, eligible for the automatic choice).
 const Variant kVariants[] = {
     // small shapes (tests, latency-bound workloads)
-    SRWM_BOTH_IO(2, 2, 1, 2, 1, 1),
-    SRWM_BOTH_IO(3, 5, 1, 1, 1, 1),
-    SRWM_BOTH_IO(8, 8, 1, 8, 1, 1),
-    SRWM_BOTH_IO(8, 16, 1, 8, 1, 1),
-    SRWM_BOTH_IO(16, 8, 1, 8, 1, 1),
-    SRWM_BOTH_IO(16, 16, 1, 4, 1, 1),
-    SRWM_BOTH_IO_FUSED(16, 16, 2, 4, 1, 0),
-    SRWM_BOTH_IO(32, 32, 1, 4, 1, 1),
+    SRWM_BOTH_IO_RESET(2, 2, 1, 2, 1, 4, 1),
+    SRWM_BOTH_IO_RESET(3, 5, 1, 1, 1, 4, 1),
+    SRWM_BOTH_IO_RESET(8, 8, 1, 8, 1, 4, 1),
+    SRWM_BOTH_IO_RESET(8, 16, 1, 8, 1, 4, 1),
+    SRWM_BOTH_IO_RESET(16, 8, 1, 8, 1, 4, 1),
+    SRWM_BOTH_IO_RESET(16, 16, 1, 4, 1, 4, 1),
+    SRWM_BOTH_IO_FUSED(16, 16, 2, 4, 1, 4, 0),
+    SRWM_BOTH_IO_RESET(32, 32, 1, 4, 1, 4, 1),
     // d = 64: one wave per unit for many units, up to eight for few
-    SRWM_BOTH_IO(64, 64, 1, 2, 2, 1),
-    SRWM_BOTH_IO(64, 64, 2, 8, 2, 1),
-    SRWM_BOTH_IO_FUSED(64, 64, 4, 8, 1, 1),
-    SRWM_BOTH_IO_FUSED(64, 64, 8, 8, 1, 1),
-    SRWM_BOTH_IO(64, 64, 1, 4, 2, 0),
-    SRWM_BOTH_IO(64, 64, 1, 4, 1, 0),
-    SRWM_BOTH_IO(64, 64, 4, 8, 1, 0),
-    SRWM_BOTH_IO(64, 64, 4, 16, 1, 0),
-    SRWM_BOTH_IO(64, 64, 4, 4, 1, 0),
-    SRWM_BOTH_IO(64, 64, 8, 8, 1, 0),
-    SRWM_BOTH_IO_FUSED(64, 64, 4, 4, 1, 0),
+    SRWM_BOTH_IO(64, 64, 1, 2, 2, 4, 1),
+    SRWM_BOTH_IO(64, 64, 2, 8, 2, 4, 1),
+    SRWM_BOTH_IO_FUSED(64, 64, 4, 8, 1, 4, 1),
+    SRWM_BOTH_IO_FUSED(64, 64, 8, 8, 1, 4, 1),
+    SRWM_BOTH_IO(64, 64, 1, 4, 2, 4, 0),
+    SRWM_BOTH_IO(64, 64, 1, 4, 1, 4, 0),
+    SRWM_BOTH_IO(64, 64, 4, 8, 1, 4, 0),
+    SRWM_BOTH_IO(64, 64, 4, 16, 1, 4, 0),
+    SRWM_BOTH_IO(64, 64, 4, 4, 1, 4, 0),
+    SRWM_BOTH_IO(64, 64, 8, 8, 1, 4, 0),
+    SRWM_BOTH_IO_FUSED(64, 64, 4, 4, 1, 4, 0),
+    SRWM_BOTH_IO_RESET(64, 64, 2, 8, 2, 4, 1),
     // d = 128
-    SRWM_BOTH_IO_FUSED(128, 128, 8, 8, 1, 1),
-    SRWM_BOTH_IO_FUSED(128, 128, 8, 16, 1, 0),
-    SRWM_BOTH_IO_FUSED(128, 128, 16, 16, 1, 0),
-    SRWM_BOTH_IO(128, 128, 8, 16, 1, 0),
-    SRWM_BOTH_IO(128, 128, 16, 16, 1, 0),
-    SRWM_BOTH_IO(128, 128, 16, 8, 1, 0),
-    SRWM_BOTH_IO(128, 128, 8, 8, 1, 0),
+    SRWM_BOTH_IO_FUSED(128, 128, 8, 8, 1, 4, 1),
+    SRWM_BOTH_IO(128, 128, 8, 8, 1, 4, 0),
+    SRWM_BOTH_IO_FUSED(128, 128, 8, 16, 1, 4, 0),
+    SRWM_BOTH_IO_FUSED(128, 128, 16, 16, 1, 4, 0),
+    SRWM_BOTH_IO(128, 128, 8, 16, 1, 4, 0),
+    SRWM_BOTH_IO(128, 128, 16, 16, 1, 4, 0),
+    SRWM_BOTH_IO(128, 128, 16, 8, 1, 4, 0),
+    SRWM_BOTH_IO_RESET(128, 128, 8, 8, 1, 4, 1),
+    // one learning rate
+    SRWM_BOTH_IO_RESET(2, 2, 1, 2, 1, 1, 1),
+    SRWM_BOTH_IO_RESET(8, 8, 1, 8, 1, 1, 1),
+    SRWM_BOTH_IO_RESET(16, 16, 1, 4, 1, 1, 1),
+    SRWM_BOTH_IO(64, 64, 1, 2, 2, 1, 1),
+    SRWM_BOTH_IO_RESET(64, 64, 2, 8, 2, 1, 1),
+    SRWM_BOTH_IO_FUSED(64, 64, 8, 8, 1, 1, 1),
+    SRWM_BOTH_IO_FUSED(128, 128, 8, 8, 1, 1, 1),
+    SRWM_BOTH_IO_RESET(128, 128, 8, 8, 1, 1, 1),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -942,45 +1001,62 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out)
     return true;
 }
 
-// Automatic choice among the eligible variants of (d_in, d_out, io): the
-// fewest waves per unit that still give every SIMD of the chip two waves
-// (units * waves >= 2048); if none does, the most waves per unit.
-int find_variant(int64_t d_in, int64_t d_out, int io, int requested, int64_t units)
+bool variant_matches(const Variant& v, int64_t d_in, int64_t d_out, int io, int nlr, bool reset)
+{
+    return v.d_in == d_in && v.d_out == d_out && v.io == io && v.nlr == nlr && (!reset || v.reset);
+}
+
+// Automatic choice among the eligible variants: the fewest waves per unit
+// that still give every SIMD of the chip two waves (units * waves >= 2048);
+// if none does, the most waves per unit.  With a reset interval only the
+// variants built with the reset ablation qualify.
+int find_variant(int64_t d_in, int64_t d_out, int io, int nlr, bool reset, int requested, int64_t units)
 {
     if (requested >= 0) {
         if (requested >= kNumVariants) return -1;
-        const Variant& v = kVariants[requested];
-        return (v.d_in == d_in && v.d_out == d_out && v.io == io) ? requested : -1;
+        return variant_matches(kVariants[requested], d_in, d_out, io, nlr, reset) ? requested : -1;
     }
     int best_fill = -1, best_any = -1;
     for (int i = 0; i < kNumVariants; ++i) {
         const Variant& v = kVariants[i];
-        if (v.d_in != d_in || v.d_out != d_out || v.io != io || !v.is_auto) continue;
+        if (!variant_matches(v, d_in, d_out, io, nlr, reset) || !v.is_auto) continue;
         if (units * v.nw >= kChipWaveSlots && (best_fill < 0 || v.nw < kVariants[best_fill].nw)) best_fill = i;
         if (best_any < 0 || v.nw > kVariants[best_any].nw) best_any = i;
     }
-    return best_fill >= 0 ? best_fill : best_any;
+    if (best_fill >= 0 || best_any >= 0) return best_fill >= 0 ? best_fill : best_any;
+    // a shape whose only variants are not marked eligible (or all fused, with reset)
+    for (int i = 0; i < kNumVariants; ++i)
+        if (variant_matches(kVariants[i], d_in, d_out, io, nlr, reset)) return i;
+    return -1;
 }
 
-int forward_impl(const void* x, const float* W0, void* y, float* W_T, int64_t B, int64_t T,
-                 int64_t H, int64_t d_in, int64_t d_out, int64_t m, int io_dtype,
-                 int apply_input_softmax, void* stream, int variant)
+int forward_impl(const srwm_forward_args_t* a)
 {
+    if (a == nullptr) return SRWM_ERR_NULL;
+    const int64_t B = a->B, T = a->T, H = a->H, d_in = a->d_in, d_out = a->d_out, m = a->m;
     if (B < 0 || T < 0 || H < 0 || d_in < 1 || d_out < 1) return SRWM_ERR_SHAPE;
-    if (m != d_out + 2 * d_in + 4) return SRWM_ERR_SHAPE;
-    if (io_dtype != SRWM_IO_F32 && io_dtype != SRWM_IO_BF16) return SRWM_ERR_ARG;
-    if (apply_input_softmax != 0 && apply_input_softmax != 1) return SRWM_ERR_ARG;
-    if (variant < -1) return SRWM_ERR_ARG;
+    if (a->n_lr != 1 && a->n_lr != 4) return SRWM_ERR_ARG;
+    if (m != d_out + 2 * d_in + a->n_lr) return SRWM_ERR_SHAPE;
+    if (a->io_dtype != SRWM_IO_F32 && a->io_dtype != SRWM_IO_BF16) return SRWM_ERR_ARG;
+    if (a->apply_input_softmax != 0 && a->apply_input_softmax != 1) return SRWM_ERR_ARG;
+    if (a->w0_per_sequence != 0 && a->w0_per_sequence != 1) return SRWM_ERR_ARG;
+    if (a->reset_interval < 0 || a->reset_interval > INT32_MAX) return SRWM_ERR_ARG;
+    if (a->variant < -1) return SRWM_ERR_ARG;
+    const bool reset = a->reset_interval > 0;
     const int64_t units_hint = (B > 0 && H > INT64_MAX / B) ? INT64_MAX : B * H;
-    const int vi = find_variant(d_in, d_out, io_dtype, variant, units_hint);
-    if (vi < 0) return variant >= 0 ? SRWM_ERR_ARG : SRWM_ERR_UNSUPPORTED;
-    const int64_t es = io_dtype == SRWM_IO_BF16 ? 2 : 4;
+    const int vi = find_variant(d_in, d_out, a->io_dtype, a->n_lr, reset, a->variant, units_hint);
+    if (vi < 0) return a->variant >= 0 ? SRWM_ERR_ARG : SRWM_ERR_UNSUPPORTED;
+    const int64_t es = a->io_dtype == SRWM_IO_BF16 ? 2 : 4;
     int64_t units, steps, nx, ny, nw0, nwt;
     if (!mul_ok(B, H, &units) || !mul_ok(units, T, &steps) || !mul_ok(steps, d_in * es, &nx) ||
-        !mul_ok(steps, d_out * es, &ny) || !mul_ok(H, m * d_in * 4, &nw0) ||
+        !mul_ok(steps, d_out * es, &ny) || !mul_ok(a->w0_per_sequence ? units : H, m * d_in * 4, &nw0) ||
         !mul_ok(units, m * d_in * 4, &nwt))
         return SRWM_ERR_SHAPE;
     if (units > INT32_MAX || T > INT32_MAX || H > INT32_MAX) return SRWM_ERR_SHAPE;
+    const void* x = a->x;
+    const float* W0 = a->W0;
+    void* y = a->y;
+    float* W_T = a->W_T;
     if ((nx > 0 && x == nullptr) || (ny > 0 && y == nullptr) || (nw0 > 0 && units > 0 && W0 == nullptr))
         return SRWM_ERR_NULL;
     // The kernels move 16-byte pieces: every buffer must be 16-byte aligned.
@@ -996,12 +1072,38 @@ int forward_impl(const void* x, const float* W0, void* y, float* W_T, int64_t B,
     if (T == 0 && W_T == nullptr) return SRWM_OK;
 
     const Variant& v = kVariants[vi];
-    int Ti = static_cast<int>(T), Hi = static_cast<int>(H), fl = apply_input_softmax;
-    void* args[] = {&x, &W0, &y, &W_T, &Ti, &Hi, &fl};
+    int Ti = static_cast<int>(T), Hi = static_cast<int>(H), fl = a->apply_input_softmax;
+    int per_seq = a->w0_per_sequence, rst = static_cast<int>(a->reset_interval);
+    void* args[] = {const_cast<void**>(&x), const_cast<float**>(&W0), &y, &W_T, &Ti, &Hi, &fl, &per_seq, &rst};
     const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(v.fn),
                                            dim3(static_cast<unsigned>(units)), dim3(v.nw * kWave),
-                                           args, 0, static_cast<hipStream_t>(stream));
+                                           args, 0, static_cast<hipStream_t>(a->stream));
     return err == hipSuccess ? SRWM_OK : SRWM_ERR_HIP;
+}
+
+srwm_forward_args_t basic_args(const void* x, const float* W0, void* y, float* W_T, int64_t B, int64_t T,
+                               int64_t H, int64_t d_in, int64_t d_out, int64_t m, int io_dtype,
+                               int apply_input_softmax, void* stream, int variant)
+{
+    srwm_forward_args_t a;
+    a.x = x;
+    a.W0 = W0;
+    a.y = y;
+    a.W_T = W_T;
+    a.B = B;
+    a.T = T;
+    a.H = H;
+    a.d_in = d_in;
+    a.d_out = d_out;
+    a.m = m;
+    a.io_dtype = io_dtype;
+    a.apply_input_softmax = apply_input_softmax;
+    a.n_lr = 4;
+    a.w0_per_sequence = 0;
+    a.reset_interval = 0;
+    a.variant = variant;
+    a.stream = stream;
+    return a;
 }
 
 }  // namespace
@@ -1012,47 +1114,55 @@ int srwm_forward(const void* x, const float* W0, void* y, float* W_T, int64_t B,
                  int64_t H, int64_t d_in, int64_t d_out, int64_t m, int io_dtype,
                  int apply_input_softmax, void* stream)
 {
-    return forward_impl(x, W0, y, W_T, B, T, H, d_in, d_out, m, io_dtype, apply_input_softmax,
-                        stream, -1);
+    const srwm_forward_args_t a =
+        basic_args(x, W0, y, W_T, B, T, H, d_in, d_out, m, io_dtype, apply_input_softmax, stream, -1);
+    return forward_impl(&a);
 }
 
 int srwm_forward_variant(const void* x, const float* W0, void* y, float* W_T, int64_t B,
                          int64_t T, int64_t H, int64_t d_in, int64_t d_out, int64_t m,
                          int io_dtype, int apply_input_softmax, void* stream, int variant)
 {
-    return forward_impl(x, W0, y, W_T, B, T, H, d_in, d_out, m, io_dtype, apply_input_softmax,
-                        stream, variant);
+    const srwm_forward_args_t a =
+        basic_args(x, W0, y, W_T, B, T, H, d_in, d_out, m, io_dtype, apply_input_softmax, stream, variant);
+    return forward_impl(&a);
 }
+
+int srwm_forward_ex(const srwm_forward_args_t* args) { return forward_impl(args); }
 
 int srwm_variant_count(void) { return kNumVariants; }
 
-int srwm_variant_info(int i, int* d_in, int* d_out, int* io_dtype, int* waves, int* lanes_per_row,
-                      int* waves_per_simd, int* schedule, int* is_auto)
+int srwm_variant_info(int i, srwm_variant_info_t* info)
 {
     if (i < 0 || i >= kNumVariants) return SRWM_ERR_ARG;
+    if (info == nullptr) return SRWM_ERR_NULL;
     const Variant& v = kVariants[i];
-    if (d_in) *d_in = v.d_in;
-    if (d_out) *d_out = v.d_out;
-    if (io_dtype) *io_dtype = v.io;
-    if (waves) *waves = v.nw;
-    if (lanes_per_row) *lanes_per_row = v.p;
-    if (waves_per_simd) *waves_per_simd = v.wpe;
-    if (schedule) *schedule = v.fused;
-    if (is_auto) *is_auto = v.is_auto;
+    info->d_in = v.d_in;
+    info->d_out = v.d_out;
+    info->io_dtype = v.io;
+    info->n_lr = v.nlr;
+    info->waves = v.nw;
+    info->lanes_per_row = v.p;
+    info->waves_per_simd = v.wpe;
+    info->schedule = v.fused;
+    info->supports_reset = v.reset;
+    info->is_auto = v.is_auto;
     return SRWM_OK;
 }
 
-int srwm_select_variant(int64_t d_in, int64_t d_out, int io_dtype, int64_t units)
+int srwm_select_variant(int64_t d_in, int64_t d_out, int io_dtype, int n_lr, int64_t reset_interval,
+                        int64_t units)
 {
-    if (d_in < 1 || d_out < 1 || units < 0) return SRWM_ERR_SHAPE;
+    if (d_in < 1 || d_out < 1 || units < 0 || reset_interval < 0) return SRWM_ERR_SHAPE;
     if (io_dtype != SRWM_IO_F32 && io_dtype != SRWM_IO_BF16) return SRWM_ERR_ARG;
-    const int vi = find_variant(d_in, d_out, io_dtype, -1, units);
+    if (n_lr != 1 && n_lr != 4) return SRWM_ERR_ARG;
+    const int vi = find_variant(d_in, d_out, io_dtype, n_lr, reset_interval > 0, -1, units);
     return vi >= 0 ? vi : SRWM_ERR_UNSUPPORTED;
 }
 
-int srwm_supported(int64_t d_in, int64_t d_out, int io_dtype)
+int srwm_supported(int64_t d_in, int64_t d_out, int io_dtype, int n_lr)
 {
-    return find_variant(d_in, d_out, io_dtype, -1, 1) >= 0 ? 1 : 0;
+    return find_variant(d_in, d_out, io_dtype, n_lr, false, -1, 1) >= 0 ? 1 : 0;
 }
 
 const char* srwm_strerror(int code)
@@ -1060,11 +1170,11 @@ const char* srwm_strerror(int code)
     switch (code) {
     case SRWM_OK: return "SRWM_OK: success";
     case SRWM_ERR_NULL: return "SRWM_ERR_NULL: a required pointer is NULL";
-    case SRWM_ERR_SHAPE: return "SRWM_ERR_SHAPE: invalid sizes (negative, m != d_out+2*d_in+4, or overflow)";
-    case SRWM_ERR_UNSUPPORTED: return "SRWM_ERR_UNSUPPORTED: no kernel built for this (d_in, d_out, io_dtype)";
+    case SRWM_ERR_SHAPE: return "SRWM_ERR_SHAPE: invalid sizes (negative, m != d_out+2*d_in+n_lr, or overflow)";
+    case SRWM_ERR_UNSUPPORTED: return "SRWM_ERR_UNSUPPORTED: no kernel built for this (d_in, d_out, io_dtype, n_lr)";
     case SRWM_ERR_ALIAS: return "SRWM_ERR_ALIAS: an output buffer overlaps another buffer";
     case SRWM_ERR_HIP: return "SRWM_ERR_HIP: the HIP runtime rejected the launch";
-    case SRWM_ERR_ARG: return "SRWM_ERR_ARG: invalid io_dtype, flag or variant";
+    case SRWM_ERR_ARG: return "SRWM_ERR_ARG: invalid io_dtype, flag, n_lr, reset interval, variant or alignment";
     default: return "unknown srwm error code";
     }
 }

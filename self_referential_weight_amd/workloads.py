@@ -37,10 +37,11 @@ class Workload:
     return_state: bool
     w0_std: float
     seed: int = 0
+    n_lr: int = 4            # learning rates: 4 (one per row block) or 1
 
     @property
     def m(self) -> int:
-        return self.d_out + 2 * self.d_in + 4
+        return self.d_out + 2 * self.d_in + self.n_lr
 
     @property
     def units(self) -> int:

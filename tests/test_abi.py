@@ -29,7 +29,7 @@ def test_header_symbols_exported():
 
 def test_version_and_strerror():
     lib = _lib.load()
-    assert lib.srwm_version() == 100
+    assert lib.srwm_version() == 200
     for code in (OK, E_NULL, E_SHAPE, E_UNSUP, E_ALIAS, E_HIP, E_ARG):
         assert _lib.strerror(code).startswith("SRWM_")
     assert "unknown" in _lib.strerror(-99)
@@ -41,12 +41,17 @@ def test_variant_table_covers_workloads():
     assert len(vs) == _lib.load().srwm_variant_count()
     for w in WORKLOADS.values():
         io = _lib.SRWM_IO_BF16 if w.io_dtype == "bf16" else _lib.SRWM_IO_F32
-        assert _lib.load().srwm_supported(w.d_in, w.d_out, io) == 1, w.name
-    # every supported shape has at least one automatically eligible variant
-    shapes = {(v["d_in"], v["d_out"], v["io_dtype"]) for v in vs}
-    auto = {(v["d_in"], v["d_out"], v["io_dtype"]) for v in vs if v["auto"]}
-    assert shapes == auto
-    assert _lib.load().srwm_variant_info(len(vs), None, None, None, None, None, None, None, None) == E_ARG
+        assert _lib.load().srwm_supported(w.d_in, w.d_out, io, 4) == 1, w.name
+        assert _lib.load().srwm_supported(w.d_in, w.d_out, io, 1) == 1, w.name
+    # every supported shape has an automatically eligible variant, and one that
+    # implements the reset ablation
+    shapes = {(v["d_in"], v["d_out"], v["io_dtype"], v["n_lr"]) for v in vs}
+    auto = {(v["d_in"], v["d_out"], v["io_dtype"], v["n_lr"]) for v in vs if v["auto"]}
+    reset = {(v["d_in"], v["d_out"], v["io_dtype"], v["n_lr"]) for v in vs if v["supports_reset"]}
+    assert shapes == auto == reset
+    info = _lib.VariantInfo()
+    assert _lib.load().srwm_variant_info(len(vs), ctypes.byref(info)) == E_ARG
+    assert _lib.load().srwm_variant_info(0, None) == E_NULL
 
 
 FAKE_X, FAKE_W0, FAKE_Y, FAKE_WT = 0x10000000, 0x20000000, 0x30000000, 0x40000000
@@ -94,22 +99,63 @@ def test_select_variant():
     lib = _lib.load()
     vs = _lib.variants()
     for d, io, units in [(64, 1, 2048), (64, 0, 256), (128, 0, 32), (16, 0, 16), (8, 0, 1)]:
-        i = lib.srwm_select_variant(d, d, io, units)
-        assert 0 <= i < len(vs)
-        v = vs[i]
-        assert (v["d_in"], v["d_out"], v["io_dtype"]) == (d, d, "bf16" if io else "f32") and v["auto"]
+        for n_lr in (4, 1):
+            for reset in (0, 50):
+                i = lib.srwm_select_variant(d, d, io, n_lr, reset, units)
+                assert 0 <= i < len(vs)
+                v = vs[i]
+                assert (v["d_in"], v["d_out"], v["io_dtype"], v["n_lr"]) == (d, d, "bf16" if io else "f32", n_lr)
+                assert v["auto"] and (v["supports_reset"] or reset == 0)
     # many units: the fewest waves per unit; few units: more waves per unit
-    assert vs[lib.srwm_select_variant(64, 64, 1, 2048)]["waves"] == 1
-    assert vs[lib.srwm_select_variant(64, 64, 0, 256)]["waves"] > 1
-    assert lib.srwm_select_variant(7, 7, 0, 4) == E_UNSUP
-    assert lib.srwm_select_variant(64, 64, 3, 4) == E_ARG
-    assert lib.srwm_select_variant(0, 64, 0, 4) == E_SHAPE
+    assert vs[lib.srwm_select_variant(64, 64, 1, 4, 0, 2048)]["waves"] == 1
+    assert vs[lib.srwm_select_variant(64, 64, 0, 4, 0, 256)]["waves"] > 1
+    assert lib.srwm_select_variant(7, 7, 0, 4, 0, 4) == E_UNSUP
+    assert lib.srwm_select_variant(64, 64, 3, 4, 0, 4) == E_ARG
+    assert lib.srwm_select_variant(64, 64, 0, 2, 0, 4) == E_ARG
+    assert lib.srwm_select_variant(0, 64, 0, 4, 0, 4) == E_SHAPE
 
 
 def test_variant_must_match_shape():
     vs = _lib.variants()
     v64 = next(v for v in vs if v["d_in"] == 64 and v["io_dtype"] == "f32")
     assert call(d_in=16, d_out=16, variant=v64["index"]) == E_ARG
+
+
+def call_ex(**kw):
+    base = dict(x=FAKE_X, W0=FAKE_W0, y=FAKE_Y, W_T=FAKE_WT, B=2, T=3, H=2, d_in=16, d_out=16,
+                m=None, io_dtype=0, apply_input_softmax=0, n_lr=4, w0_per_sequence=0,
+                reset_interval=0, variant=-1, stream=None)
+    base.update(kw)
+    if base["m"] is None:
+        base["m"] = base["d_out"] + 2 * base["d_in"] + base["n_lr"]
+    return _lib.load().srwm_forward_ex(ctypes.byref(_lib.ForwardArgs(**base)))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_lr=2), E_ARG),
+    (dict(n_lr=1, m=52), E_SHAPE),
+    (dict(n_lr=4, m=49), E_SHAPE),
+    (dict(w0_per_sequence=2), E_ARG),
+    (dict(reset_interval=-1), E_ARG),
+    (dict(reset_interval=2 ** 40), E_ARG),
+    (dict(W0=None, w0_per_sequence=1), E_NULL),
+    (dict(W_T=FAKE_W0 + 8192, w0_per_sequence=1), E_ALIAS),  # inside the [B,H,m,d] W0 only
+    (dict(d_in=7, d_out=7, n_lr=1), E_UNSUP),
+])
+def test_forward_ex_validation(kw, code):
+    assert call_ex(**kw) == code
+
+
+def test_forward_ex_null_args():
+    assert _lib.load().srwm_forward_ex(None) == E_NULL
+
+
+def test_fused_variant_rejects_reset():
+    vs = _lib.variants()
+    fused = next(v for v in vs if v["schedule"] == "fused" and v["d_in"] == 64 and v["io_dtype"] == "f32"
+                 and v["n_lr"] == 4)
+    assert not fused["supports_reset"]
+    assert call_ex(d_in=64, d_out=64, variant=fused["index"], reset_interval=5) == E_ARG
 
 
 def test_empty_problems_are_noops_without_gpu():

@@ -26,10 +26,11 @@ def to_dev(x_np, io_dtype):
     return t.to(torch.bfloat16) if io_dtype == "bf16" else t
 
 
-def run_gpu(x_np, W0_np, io_dtype, flag, return_state=True, variant=-1):
+def run_gpu(x_np, W0_np, io_dtype, flag, return_state=True, variant=-1, n_lr=4, reset_interval=0):
     srwm = _srwm()
-    y, WT = srwm.forward(to_dev(x_np, io_dtype), torch.from_numpy(W0_np).to(dev()),
-                         apply_input_softmax=flag, return_state=return_state, variant=variant)
+    y, WT = srwm.forward(to_dev(x_np, io_dtype), torch.from_numpy(np.ascontiguousarray(W0_np)).to(dev()),
+                         apply_input_softmax=flag, return_state=return_state, variant=variant,
+                         n_lr=n_lr, reset_interval=reset_interval)
     torch.cuda.synchronize()
     y = y.float().cpu().numpy()
     WT = WT.cpu().numpy() if WT is not None else None
@@ -84,12 +85,14 @@ def _variant_ids():
 def test_variant_small(vi, T, flag):
     v = _srwm().variants()[vi]
     w = Workload("sweep", B=3, H=2, d_in=v["d_in"], d_out=v["d_out"], T=T, io_dtype=v["io_dtype"],
-                 apply_input_softmax=flag, return_state=True, w0_std=v["d_in"] ** -0.5, seed=vi)
-    say(f"[parity] variant {v} T={T} flag={flag}")
+                 apply_input_softmax=flag, return_state=True, w0_std=v["d_in"] ** -0.5, seed=vi,
+                 n_lr=v["n_lr"])
+    reset = 13 if (v["supports_reset"] and T > 13) else 0
+    say(f"[parity] variant {v} T={T} flag={flag} reset={reset}")
     x = gen_x(w)
     W0 = gen_W0(w)
-    y, WT = run_gpu(x, W0, w.io_dtype, flag, variant=vi)
-    y_ref, WT_ref = oracle.forward(x, W0, flag)
+    y, WT = run_gpu(x, W0, w.io_dtype, flag, variant=vi, n_lr=w.n_lr, reset_interval=reset)
+    y_ref, WT_ref = oracle.forward(x, W0, flag, n_lr=w.n_lr, reset_interval=reset)
     check_y(y, y_ref, w.io_dtype, f"variant {vi}")
     check_state(WT, WT_ref, f"variant {vi}")
 
@@ -226,12 +229,79 @@ def test_bf16_output_is_rne_of_f32_path(name, flag):
     vs = srwm.variants()
     picked = 0
     for vf in vs:
-        if vf["d_in"] != w.d_in or vf["d_out"] != w.d_out or vf["io_dtype"] != "f32":
+        if (vf["d_in"] != w.d_in or vf["d_out"] != w.d_out or vf["io_dtype"] != "f32"
+                or vf["n_lr"] != w.n_lr):
             continue
         vb = next(v for v in vs if v["io_dtype"] == "bf16" and all(
-            v[k] == vf[k] for k in ("d_in", "d_out", "waves", "lanes_per_row", "waves_per_simd", "schedule")))
+            v[k] == vf[k] for k in ("d_in", "d_out", "n_lr", "waves", "lanes_per_row", "waves_per_simd",
+                                    "schedule", "supports_reset")))
         yf, _ = run_gpu(x, W0, "f32", flag, return_state=False, variant=vf["index"])
         yb, _ = run_gpu(x, W0, "bf16", flag, return_state=False, variant=vb["index"])
         np.testing.assert_array_equal(yb, round_to_bf16(yf))
         picked += 1
     assert picked >= 1
+
+
+
+# ---------------------------------------------------------------------------
+# One learning rate, per-sequence initial state, state carry, reset ablation.
+@pytest.mark.parametrize("name", ["multitask_d16", "fewshot_d64", "rl_d64_bf16", "wide_d128"])
+def test_one_rate_parity(name):
+    w = WORKLOADS[name].with_(B=4, T=300, n_lr=1)
+    say(f"[parity] one rate {name}")
+    x = gen_x(w)
+    W0 = gen_W0(w)
+    y, WT = run_gpu(x, W0, w.io_dtype, w.apply_input_softmax, n_lr=1)
+    y_ref, WT_ref = oracle.forward(x, W0, w.apply_input_softmax, n_lr=1)
+    check_y(y, y_ref, w.io_dtype, name)
+    check_state(WT, WT_ref, name)
+
+
+@pytest.mark.parametrize("name", ["fewshot_d64", "rl_d64_bf16"])
+def test_one_rate_equals_four_equal_rates_gpu(name):
+    w = WORKLOADS[name].with_(B=3, T=120)
+    x = gen_x(w)
+    W4 = gen_W0(w)
+    W4[:, -4:] = W4[:, -1:]
+    W1 = np.ascontiguousarray(W4[:, :-3])
+    y4, T4 = run_gpu(x, W4, w.io_dtype, w.apply_input_softmax)
+    y1, T1 = run_gpu(x, W1, w.io_dtype, w.apply_input_softmax, n_lr=1)
+    from tests._parity import rel_l2
+    assert rel_l2(y1, y4) < 1e-6
+    assert rel_l2(T1, T4[..., :-3, :]) < 1e-6
+
+
+@pytest.mark.parametrize("name", ["multitask_d16", "fewshot_d64", "rl_d64_bf16", "wide_d128"])
+def test_per_sequence_initial_state_and_carry(name):
+    # State carry across two calls for a whole batch: the second call starts
+    # every unit from its own W_T of the first ([SRWM] Sec. 3.3).
+    w = WORKLOADS[name].with_(B=4, T=160)
+    say(f"[parity] per-sequence state {name}")
+    x = gen_x(w)
+    W0 = gen_W0(w)
+    T1 = 57
+    ya, WA = run_gpu(np.ascontiguousarray(x[:, :T1]), W0, w.io_dtype, w.apply_input_softmax)
+    yb, WB = run_gpu(np.ascontiguousarray(x[:, T1:]), WA, w.io_dtype, w.apply_input_softmax)
+    y_ref, WT_ref = oracle.forward(x, W0, w.apply_input_softmax)
+    check_y(np.concatenate([ya, yb], 1), y_ref, w.io_dtype, name)
+    check_state(WB, WT_ref, name)
+    # distinct initial states per sequence
+    rng = np.random.default_rng(31)
+    W0s = (W0[None] * rng.uniform(0.5, 1.5, size=(w.B, 1, 1, 1))).astype(np.float32)
+    y, WT = run_gpu(x, W0s, w.io_dtype, w.apply_input_softmax)
+    y_ref, WT_ref = oracle.forward(x, W0s, w.apply_input_softmax)
+    check_y(y, y_ref, w.io_dtype, name)
+    check_state(WT, WT_ref, name)
+
+
+@pytest.mark.parametrize("name", ["multitask_d16", "fewshot_d64", "rl_d64_bf16", "wide_d128"])
+def test_reset_ablation(name):
+    # Reset every 50 steps, as in the ablation of [SRWM] Sec. 4.5.
+    w = WORKLOADS[name].with_(B=4, T=173)
+    say(f"[parity] reset every 50 {name}")
+    x = gen_x(w)
+    W0 = gen_W0(w)
+    y, WT = run_gpu(x, W0, w.io_dtype, w.apply_input_softmax, reset_interval=50)
+    y_ref, WT_ref = oracle.forward(x, W0, w.apply_input_softmax, reset_interval=50)
+    check_y(y, y_ref, w.io_dtype, name)
+    check_state(WT, WT_ref, name)
