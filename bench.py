@@ -11,8 +11,13 @@ roofline of the kernel (algorithmic FP32 FLOP per launch / average launch time
 from HIP events on the launch stream, against the FP32 vector peak) and the
 float64 CPU oracle timed on a bounded sample of the same workload.
 
+With --backward a step is one training pass instead: the forward pass that
+records the tape, then the backward pass (dx and the batch-summed dW0 for a
+seeded output cotangent); the roofline then describes the backward kernel and
+the CPU baseline is the float64 gradient oracle.
+
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                  [--variant I] [--no-cpu] [--copy-calibration BYTES]
+                  [--variant I] [--no-cpu] [--copy-calibration BYTES] [--backward]
 """
 from __future__ import annotations
 
@@ -91,6 +96,38 @@ def cpu_baseline(w, x_host, W0_host, budget_s: float):
     }
 
 
+def cpu_baseline_backward(w, x_host, W0_host, gy_host, budget_s: float):
+    """Time the float64 gradient oracle on the first n sequences, n sized from
+    a calibration run on a prefix of one sequence so the run takes about budget_s."""
+    import numpy as np
+    import torch
+
+    from oracle import backward as oracle_bwd
+
+    cores = torch.get_num_threads()
+    Tc = min(w.T, 64)
+    t0 = time.perf_counter()
+    oracle_bwd.grads(x_host[:1, :Tc], W0_host, w.apply_input_softmax, gy_host[:1, :Tc], n_lr=w.n_lr)
+    per_step = (time.perf_counter() - t0) / Tc          # seconds per step of one sequence
+    n = max(1, min(w.B, int(budget_s / (per_step * w.T))))
+    T = w.T
+    if n == 1 and per_step * w.T > budget_s:
+        T = max(1, int(budget_s / per_step))
+    t0 = time.perf_counter()
+    oracle_bwd.grads(np.ascontiguousarray(x_host[:n, :T]), W0_host, w.apply_input_softmax,
+                     np.ascontiguousarray(gy_host[:n, :T]), n_lr=w.n_lr)
+    dt = time.perf_counter() - t0
+    units = n * w.H
+    return {
+        "value": units * T / dt,
+        "unit": "head-steps/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"forward+backward of the first {n} of {w.B} sequences x {w.H} heads ({units} units) "
+                   f"x T={T} of {w.name}, float64 autograd, {dt:.1f} s wall"),
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,6 +139,8 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle wall time")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also run a plain device copy of this many bytes (counter calibration)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the training step (taped forward + backward) instead of the forward")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -135,6 +174,9 @@ def main() -> int:
     y = torch.empty((w.B, w.T, w.H, w.d_out), dtype=x.dtype, device=dev)
     W_T = torch.empty((w.B, w.H, w.m, w.d_in), dtype=torch.float32, device=dev) if w.return_state else None
     stream = torch.cuda.current_stream(dev)
+
+    if args.backward:
+        return bench_backward(args, w, name, x, x_host, W0, W0_host, dev)
 
     def step():
         srwm.forward(x, W0, apply_input_softmax=w.apply_input_softmax, return_state=w.return_state,
@@ -203,6 +245,81 @@ def main() -> int:
     if not args.no_cpu:
         log("[bench] timing the float64 CPU oracle on a bounded sample")
         rec["cpu_baseline"] = cpu_baseline(w, x_host, W0_host, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def bench_backward(args, w, name, x, x_host, W0, W0_host, dev) -> int:
+    import torch
+
+    import self_referential_weight_amd as srwm
+    from self_referential_weight_amd.workloads import gen_gy
+
+    gy_host = gen_gy(w)
+    gy = torch.from_numpy(gy_host).to(dev)
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    fwd_ms, bwd_ms = [], []
+
+    def step(timed: bool):
+        if timed:
+            ev[0].record(stream)
+        y, W_T, tape = srwm.forward(x, W0, apply_input_softmax=w.apply_input_softmax, n_lr=w.n_lr,
+                                    save_tape=True, stream=stream)
+        if timed:
+            ev[1].record(stream)
+        srwm.backward(x, W_T, tape, gy, None, apply_input_softmax=w.apply_input_softmax, n_lr=w.n_lr,
+                      shared_W0=True, stream=stream)
+        if timed:
+            ev[2].record(stream)
+            torch.cuda.synchronize()
+            fwd_ms.append(ev[0].elapsed_time(ev[1]))
+            bwd_ms.append(ev[1].elapsed_time(ev[2]))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done; timing {args.steps} training steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    f_ms = sum(fwd_ms) / len(fwd_ms)
+    b_ms = sum(bwd_ms) / len(bwd_ms)
+    log(f"[bench] {args.steps} training steps: {ms_per_step:.3f} ms/step wall; "
+        f"forward {f_ms:.3f} ms, backward {b_ms:.3f} ms (HIP events)")
+    head_steps = w.B * w.H * w.T
+    # Algorithmic work of the backward per head-step, counted like the
+    # forward's 8 m d_in: each of the three matrix-vector products (W u, W qh,
+    # W kh) has two adjoint products (the vector's and the matrix's, 4 m d_in
+    # FLOP), the rank-one update two more (Wh kh and Wh^T a, 4 m d_in): 16 m d_in.
+    flop_bwd = 16 * w.m * w.d_in * head_steps
+    achieved = flop_bwd / (b_ms * 1e-3) / 1e12
+    rec = {
+        "metric": "SRWM training head-steps/sec (taped forward + backward), 1×MI355X",
+        "value": head_steps / (ms_per_step * 1e-3),
+        "unit": "head-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded normal x, W0 ~ N(0, 1/d_in), normal output cotangent; no dataset)",
+        "config": {"workload": name + "+backward", "B": w.B, "H": w.H, "d_in": w.d_in, "d_out": w.d_out,
+                   "T": w.T, "io_dtype": w.io_dtype, "apply_input_softmax": w.apply_input_softmax},
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_TFLOPS, "traffic": None},
+        "forward_ms": f_ms,
+        "backward_ms": b_ms,
+    }
+    if not args.no_cpu:
+        log("[bench] timing the float64 gradient oracle on a bounded sample")
+        rec["cpu_baseline"] = cpu_baseline_backward(w, x_host, W0_host, gy_host, args.cpu_budget)
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -133,6 +133,8 @@ typedef struct srwm_forward_args {
     int64_t reset_interval;
     int variant;
     void* stream;
+    float* tape;   /* NULL, or [B][H][T][srwm_tape_row()] float32 (out): the
+                      record srwm_backward needs (see there); not with resets */
 } srwm_forward_args_t;
 
 /* srwm_forward_ex -- the forward pass with every option.  Same edge cases,
@@ -154,6 +156,7 @@ typedef struct srwm_variant_info {
                               share one pass over W, the projection corrected by
                               the rank-one update of Eq. (3)                   */
     int supports_reset; /* built with the reset ablation (reset_interval > 0)  */
+    int writes_tape;    /* writes the backward tape (used when args.tape != NULL) */
     int is_auto;        /* may the automatic choice pick it                     */
 } srwm_variant_info_t;
 
@@ -172,6 +175,54 @@ int srwm_variant_info(int i, srwm_variant_info_t* info);
  */
 int srwm_select_variant(int64_t d_in, int64_t d_out, int io_dtype, int n_lr,
                         int64_t reset_interval, int64_t units);
+
+/*
+ * Backward pass (memory-efficient backpropagation through time: the pages
+ * train W0 by backpropagating through the unrolled self-modification,
+ * "Metalearning Continual Learning Algorithms" after Eq. (6) and the review
+ * page Sec. 2.5).
+ *
+ * The forward pass run with args.tape != NULL records, per unit and step,
+ * a_t (m floats, the rank-one update's row factor) and phi(k_t) (d_in
+ * floats) at [b][h][t][0, m) and [b][h][t][srwm_tape_row - d_in, ...).  From
+ * the final state W_T, srwm_backward walks t = T-1..0, undoes each update
+ * (W_{t-1} = W_t - a_t phi(k_t)^T), recomputes the step and accumulates the
+ * adjoint.  With L = sum_t <gy[t], y_t> + <gW_T, W_T> it writes
+ *   dx       [B][T][H][d_in]   dL/dx, float32 (also for bf16 x)
+ *   dW_init  [B][H][m][d_in]   dL/d(initial state of each unit)
+ *   dW0      [H][m][d_in]      sum over b of dW_init (the gradient of an
+ *                              initial matrix shared over the batch), or NULL
+ * Inputs: x and W_T as the forward pass saw and wrote them, the tape, gy
+ * [B][T][H][d_out] float32, gW_T [B][H][m][d_in] float32 or NULL (zero).
+ * With B == 0 a given dW0 is filled with zeros (one kernel launch); with
+ * H == 0 nothing is launched.  Not covered: the reset ablation.  Same
+ * conventions as the forward: device pointers, 16-byte aligned, nothing
+ * allocated, asynchronous on `stream`; errors as there (SRWM_ERR_UNSUPPORTED
+ * when srwm_backward_supported() is 0).
+ */
+typedef struct srwm_backward_args {
+    const void* x;
+    const float* W_T;
+    const float* tape;
+    const float* gy;
+    const float* gW_T;
+    float* dx;
+    float* dW_init;
+    float* dW0;
+    int64_t B, T, H, d_in, d_out, m;
+    int io_dtype;
+    int apply_input_softmax;
+    int n_lr;
+    void* stream;
+} srwm_backward_args_t;
+
+int srwm_backward(const srwm_backward_args_t* args);
+
+/* Floats per step in the tape: round_up(m, 4) + d_in, or SRWM_ERR_SHAPE. */
+int64_t srwm_tape_row(int64_t d_in, int64_t d_out, int n_lr);
+
+/* 1 if srwm_backward has a kernel for (d_in, d_out, io_dtype, n_lr), else 0. */
+int srwm_backward_supported(int64_t d_in, int64_t d_out, int io_dtype, int n_lr);
 
 /* 1 if a kernel exists for (d_in, d_out, io_dtype, n_lr), else 0. */
 int srwm_supported(int64_t d_in, int64_t d_out, int io_dtype, int n_lr);

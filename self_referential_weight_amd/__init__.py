@@ -12,7 +12,7 @@ from __future__ import annotations
 from . import _lib
 from .workloads import HEADLINE, WORKLOADS, Workload
 
-__all__ = ["forward", "supported", "variants", "select_variant", "m_rows", "WORKLOADS", "HEADLINE", "Workload"]
+__all__ = ["forward", "backward", "srwm", "tape_row", "supported", "backward_supported", "variants", "select_variant", "m_rows", "WORKLOADS", "HEADLINE", "Workload"]
 
 
 def m_rows(d_in: int, d_out: int, n_lr: int = 4) -> int:
@@ -28,6 +28,10 @@ def supported(d_in: int, d_out: int, io_dtype: str = "f32", n_lr: int = 4) -> bo
     return bool(_lib.load().srwm_supported(d_in, d_out, _io(io_dtype), n_lr))
 
 
+def backward_supported(d_in: int, d_out: int, io_dtype: str = "f32", n_lr: int = 4) -> bool:
+    return bool(_lib.load().srwm_backward_supported(d_in, d_out, _io(io_dtype), n_lr))
+
+
 def variants() -> list[dict]:
     return _lib.variants()
 
@@ -41,9 +45,14 @@ def select_variant(d_in: int, d_out: int, io_dtype: str, units: int, n_lr: int =
     return _lib.variants()[i]
 
 
+def tape_row(d_in: int, d_out: int, n_lr: int = 4) -> int:
+    """Floats per step and unit in the backward tape."""
+    return int(_lib.load().srwm_tape_row(d_in, d_out, n_lr))
+
+
 def forward(x, W0, apply_input_softmax: bool = False, return_state: bool = False,
             variant: int = -1, y=None, W_T=None, stream=None, n_lr: int = 4,
-            reset_interval: int = 0):
+            reset_interval: int = 0, save_tape: bool = False):
     """Run the SRWM recurrence on the GPU.
 
     x   : torch tensor [B, T, H, d_in], float32 or bfloat16, on a ROCm device
@@ -53,6 +62,8 @@ def forward(x, W0, apply_input_softmax: bool = False, return_state: bool = False
     n_lr: 4 (a learning rate per row block) or 1 (one for every row)
     reset_interval: 0, or R > 0 to return every state to W0 before each step
           t > 0 with t % R == 0 (the reset ablation)
+    save_tape: also record what ``backward`` needs (implies return_state);
+          the return value is then (y, W_T, tape).
     Returns (y [B, T, H, d_out] in x's dtype, W_T [B, H, m, d_in] float32 or None).
     ``y`` / ``W_T`` may be passed preallocated; the call is asynchronous on
     ``stream`` (default: torch's current stream).
@@ -94,6 +105,8 @@ def forward(x, W0, apply_input_softmax: bool = False, return_state: bool = False
     elif (tuple(y.shape) != (B, T, H, d_out) or y.dtype != x.dtype or y.device != x.device
           or not y.is_contiguous()):
         raise ValueError("preallocated y has the wrong shape/dtype/device/layout")
+    if save_tape:
+        return_state = True
     if return_state:
         if W_T is None:
             W_T = torch.empty((B, H, m, d_in), dtype=torch.float32, device=x.device)
@@ -102,6 +115,9 @@ def forward(x, W0, apply_input_softmax: bool = False, return_state: bool = False
             raise ValueError("preallocated W_T has the wrong shape/dtype/device/layout")
     else:
         W_T = None
+    tape = None
+    if save_tape:
+        tape = torch.empty((B, H, T, tape_row(d_in, d_out, n_lr)), dtype=torch.float32, device=x.device)
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
@@ -112,9 +128,102 @@ def forward(x, W0, apply_input_softmax: bool = False, return_state: bool = False
         B=B, T=T, H=H, d_in=d_in, d_out=d_out, m=m, io_dtype=io,
         apply_input_softmax=int(bool(apply_input_softmax)), n_lr=int(n_lr),
         w0_per_sequence=int(per_seq), reset_interval=int(reset_interval), variant=int(variant),
-        stream=handle)
+        stream=handle, tape=tape.data_ptr() if tape is not None and tape.numel() else None)
     with torch.cuda.device(x.device):
         rc = lib.srwm_forward_ex(a)
     if rc != 0:
         raise RuntimeError(_lib.strerror(rc))
+    if save_tape:
+        return y, W_T, tape
     return y, W_T
+
+
+def backward(x, W_T, tape, gy, gW_T=None, apply_input_softmax: bool = False, n_lr: int = 4,
+             shared_W0: bool = True, stream=None):
+    """Gradients of L = sum_t <gy[t], y_t> + <gW_T, W_T> through the recurrence.
+
+    x, W_T, tape: the forward pass's input, final state and tape
+    (``forward(..., save_tape=True)``); gy [B, T, H, d_out] and gW_T
+    [B, H, m, d_in] (or None) float32.  Returns (dx [B, T, H, d_in] float32,
+    dW0): dW0 is [H, m, d_in] (summed over the batch) when shared_W0, else the
+    per-unit gradient [B, H, m, d_in].
+    """
+    import torch
+
+    lib = _lib.load()
+    B, T, H, d_in = x.shape
+    m = W_T.shape[-2]
+    d_out = m - 2 * d_in - n_lr
+    if x.device.type != "cuda":
+        raise ValueError("x must live on a ROCm GPU")
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
+    io = _lib.SRWM_IO_BF16 if x.dtype == torch.bfloat16 else _lib.SRWM_IO_F32
+    if gW_T is not None and (gW_T.dtype != torch.float32 or tuple(gW_T.shape) != (B, H, m, d_in)):
+        raise ValueError("gW_T must be float32 [B, H, m, d_in]")
+    for name, t_ in (("x", x), ("W_T", W_T), ("tape", tape), ("gy", gy)) + ((("gW_T", gW_T),) if gW_T is not None else ()):
+        if t_.device != x.device or not t_.is_contiguous():
+            raise ValueError(f"{name} must be contiguous on x's device")
+    if gy.dtype != torch.float32 or W_T.dtype != torch.float32 or tape.dtype != torch.float32:
+        raise TypeError("gy, W_T and tape must be float32")
+    if tuple(gy.shape) != (B, T, H, d_out) or tuple(W_T.shape) != (B, H, m, d_in):
+        raise ValueError("gy / W_T shapes do not match x")
+    if tuple(tape.shape) != (B, H, T, tape_row(d_in, d_out, n_lr)):
+        raise ValueError("tape shape does not match x")
+    dx = torch.empty((B, T, H, d_in), dtype=torch.float32, device=x.device)
+    dWi = torch.empty((B, H, m, d_in), dtype=torch.float32, device=x.device)
+    dW0 = torch.empty((H, m, d_in), dtype=torch.float32, device=x.device) if shared_W0 else None
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+    def ptr(t_):
+        return t_.data_ptr() if t_ is not None and t_.numel() else None
+
+    a = _lib.BackwardArgs(x=ptr(x), W_T=ptr(W_T), tape=ptr(tape), gy=ptr(gy), gW_T=ptr(gW_T),
+                          dx=ptr(dx), dW_init=ptr(dWi), dW0=ptr(dW0), B=B, T=T, H=H, d_in=d_in,
+                          d_out=d_out, m=m, io_dtype=io,
+                          apply_input_softmax=int(bool(apply_input_softmax)), n_lr=int(n_lr),
+                          stream=handle)
+    with torch.cuda.device(x.device):
+        rc = lib.srwm_backward(a)
+    if rc != 0:
+        raise RuntimeError(_lib.strerror(rc))
+    return dx, (dW0 if shared_W0 else dWi)
+
+
+def _autograd_function():
+    import torch
+
+    class SRWMFunction(torch.autograd.Function):
+        """y, W_T = srwm(x, W0) with gradients for x and W0 from ``backward``."""
+
+        @staticmethod
+        def forward(ctx, x, W0, apply_input_softmax, n_lr):
+            y, W_T, tape = forward(x, W0, apply_input_softmax=apply_input_softmax, n_lr=n_lr,
+                                   save_tape=True)
+            ctx.save_for_backward(x, W_T, tape)
+            ctx.flags = (bool(apply_input_softmax), int(n_lr), W0.dim() == 3)
+            ctx.set_materialize_grads(False)
+            return y, W_T
+
+        @staticmethod
+        def backward(ctx, gy, gW_T):
+            x, W_T, tape = ctx.saved_tensors
+            flag, n_lr, shared = ctx.flags
+            if gy is None:
+                d_out = W_T.shape[-2] - 2 * x.shape[-1] - n_lr
+                gy = torch.zeros((*x.shape[:3], d_out), dtype=torch.float32, device=x.device)
+            else:
+                gy = gy.float().contiguous()
+            gW_T = None if gW_T is None else gW_T.contiguous()
+            dx, dW0 = backward(x, W_T, tape, gy, gW_T, apply_input_softmax=flag, n_lr=n_lr,
+                               shared_W0=shared)
+            return dx.to(x.dtype), dW0, None, None
+
+    return SRWMFunction
+
+
+def srwm(x, W0, apply_input_softmax: bool = False, n_lr: int = 4):
+    """Differentiable forward: returns (y, W_T); gradients flow to x and W0."""
+    return _autograd_function().apply(x, W0, apply_input_softmax, n_lr)

@@ -30,6 +30,31 @@ class ForwardArgs(ctypes.Structure):
         ("reset_interval", ctypes.c_int64),
         ("variant", ctypes.c_int),
         ("stream", ctypes.c_void_p),
+        ("tape", ctypes.c_void_p),
+    ]
+
+
+class BackwardArgs(ctypes.Structure):
+    """srwm_backward_args_t."""
+    _fields_ = [
+        ("x", ctypes.c_void_p),
+        ("W_T", ctypes.c_void_p),
+        ("tape", ctypes.c_void_p),
+        ("gy", ctypes.c_void_p),
+        ("gW_T", ctypes.c_void_p),
+        ("dx", ctypes.c_void_p),
+        ("dW_init", ctypes.c_void_p),
+        ("dW0", ctypes.c_void_p),
+        ("B", ctypes.c_int64),
+        ("T", ctypes.c_int64),
+        ("H", ctypes.c_int64),
+        ("d_in", ctypes.c_int64),
+        ("d_out", ctypes.c_int64),
+        ("m", ctypes.c_int64),
+        ("io_dtype", ctypes.c_int),
+        ("apply_input_softmax", ctypes.c_int),
+        ("n_lr", ctypes.c_int),
+        ("stream", ctypes.c_void_p),
     ]
 
 
@@ -37,7 +62,7 @@ class VariantInfo(ctypes.Structure):
     """srwm_variant_info_t."""
     _fields_ = [(name, ctypes.c_int) for name in (
         "d_in", "d_out", "io_dtype", "n_lr", "waves", "lanes_per_row", "waves_per_simd",
-        "schedule", "supports_reset", "is_auto")]
+        "schedule", "supports_reset", "writes_tape", "is_auto")]
 
 
 _lib = None
@@ -61,6 +86,12 @@ def load() -> ctypes.CDLL:
     lib.srwm_forward_variant.restype = ci
     lib.srwm_forward_ex.argtypes = [ctypes.POINTER(ForwardArgs)]
     lib.srwm_forward_ex.restype = ci
+    lib.srwm_backward.argtypes = [ctypes.POINTER(BackwardArgs)]
+    lib.srwm_backward.restype = ci
+    lib.srwm_tape_row.argtypes = [i64, i64, ci]
+    lib.srwm_tape_row.restype = i64
+    lib.srwm_backward_supported.argtypes = [i64, i64, ci, ci]
+    lib.srwm_backward_supported.restype = ci
     lib.srwm_variant_count.argtypes = []
     lib.srwm_variant_count.restype = ci
     lib.srwm_variant_info.argtypes = [ci, ctypes.POINTER(VariantInfo)]
@@ -93,5 +124,6 @@ def variants() -> list[dict]:
                         n_lr=info.n_lr, waves=info.waves, lanes_per_row=info.lanes_per_row,
                         waves_per_simd=info.waves_per_simd,
                         schedule="fused" if info.schedule else "phased",
-                        supports_reset=bool(info.supports_reset), auto=bool(info.is_auto)))
+                        supports_reset=bool(info.supports_reset),
+                        writes_tape=bool(info.writes_tape), auto=bool(info.is_auto)))
     return out

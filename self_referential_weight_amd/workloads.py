@@ -113,3 +113,23 @@ def gen_x(w: Workload, batch=None) -> np.ndarray:
     for i, b in enumerate(bs):
         out[i] = gen_x_seq(w, b)
     return out
+
+
+def gen_gy(w: Workload, batch=None) -> np.ndarray:
+    """Seeded output cotangent gy[B', T, H, d_out] (float32 standard normals),
+    one stream per sequence: ``default_rng([seed, 3, b])``."""
+    bs = range(w.B) if batch is None else list(batch)
+    out = np.empty((len(bs), w.T, w.H, w.d_out), dtype=np.float32)
+    for i, b in enumerate(bs):
+        out[i] = np.random.default_rng([w.seed, 3, b]).standard_normal((w.T, w.H, w.d_out), dtype=np.float32)
+    return out
+
+
+def gen_gW(w: Workload, batch=None) -> np.ndarray:
+    """Seeded final-state cotangent gW_T[B', H, m, d_in] (float32 standard
+    normals): ``default_rng([seed, 4, b])``."""
+    bs = range(w.B) if batch is None else list(batch)
+    out = np.empty((len(bs), w.H, w.m, w.d_in), dtype=np.float32)
+    for i, b in enumerate(bs):
+        out[i] = np.random.default_rng([w.seed, 4, b]).standard_normal((w.H, w.m, w.d_in), dtype=np.float32)
+    return out

@@ -2,6 +2,12 @@
 
 Tolerances (fp32 state in every case):
   * fp32 I/O: relative L2 <= 2e-4 on y and on W_T, and max|dy| <= 1e-3 * max|y|.
+  * gradients (float32 backward against the float64 gradient oracle):
+    relative L2 <= 1e-4 on dx and dW0, and max|d| <= 1e-3 * max|ref|.  The
+    same recurrence differentiated by autograd in float32 instead of float64
+    drifts by 5e-7 .. 1e-6 (relative L2, T = 512); 1e-4 leaves two orders of
+    magnitude for the backward's different summation order and for undoing
+    each update by subtraction.
   * bf16 I/O: relative L2 <= 1e-2 on y.  The max-abs clause is applied against
     the oracle's y rounded to bf16 with one bf16 ulp of headroom per element,
     |dy_i| <= 1e-3 * max|y| + ulp_bf16(y_i): bf16 output rounding alone can err
@@ -16,6 +22,7 @@ from self_referential_weight_amd.workloads import round_to_bf16
 RTOL_L2_F32 = 2e-4
 RTOL_L2_BF16 = 1e-2
 MAXABS_FRAC = 1e-3
+RTOL_L2_GRAD = 1e-4
 
 
 def rel_l2(a, ref):
@@ -55,4 +62,17 @@ def check_state(W_gpu, W_ref, what=""):
     assert r <= RTOL_L2_F32, f"{what} W_T relL2 {r:.3e}"
     d = float(np.abs(np.asarray(W_gpu, np.float64) - W_ref).max())
     assert d <= MAXABS_FRAC * float(np.abs(W_ref).max()), f"{what} W_T max-abs {d:.3e}"
+    return r
+
+
+def check_grad(g_gpu, g_ref, what="", rtol=RTOL_L2_GRAD):
+    g_gpu = np.asarray(g_gpu, np.float64)
+    g_ref = np.asarray(g_ref, np.float64)
+    if g_ref.size == 0:
+        assert g_gpu.size == 0
+        return 0.0
+    r = rel_l2(g_gpu, g_ref)
+    assert r <= rtol, f"{what} relL2 {r:.3e}"
+    d = float(np.abs(g_gpu - g_ref).max())
+    assert d <= MAXABS_FRAC * float(np.abs(g_ref).max()), f"{what} max-abs {d:.3e}"
     return r

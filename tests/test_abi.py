@@ -164,3 +164,85 @@ def test_empty_problems_are_noops_without_gpu():
     assert call(H=0, x=None, y=None, W0=None, WT=None) == OK
     # T == 0 with no state requested: nothing to write.
     assert call(T=0, x=None, y=None, WT=None) == OK
+
+
+# ---------------------------------------------------------------------------
+# Backward pass and the forward tape.
+FAKE_TAPE, FAKE_GY, FAKE_DX, FAKE_DWI, FAKE_DW0 = 0x50000000, 0x60000000, 0x70000000, 0x80000000, 0x90000000
+
+
+def test_tape_row_and_backward_support():
+    lib = _lib.load()
+    for d_in, d_out, n_lr in [(8, 8, 4), (16, 16, 1), (64, 64, 4), (64, 64, 1), (3, 5, 1)]:
+        m = d_out + 2 * d_in + n_lr
+        assert lib.srwm_tape_row(d_in, d_out, n_lr) == (m + 3) // 4 * 4 + d_in
+    assert lib.srwm_tape_row(0, 8, 4) == E_SHAPE
+    assert lib.srwm_tape_row(8, 8, 2) == E_SHAPE
+    for d in (8, 16, 64):
+        for io in (0, 1):
+            for n_lr in (4, 1):
+                assert lib.srwm_backward_supported(d, d, io, n_lr) == 1
+    assert lib.srwm_backward_supported(128, 128, 0, 4) == 0
+    assert lib.srwm_backward_supported(64, 64, 2, 4) == 0
+    # every shape with a backward kernel has forward variants that write the tape
+    vs = _lib.variants()
+    tape = {(v["d_in"], v["d_out"], v["io_dtype"], v["n_lr"]) for v in vs if v["writes_tape"]}
+    for d in (8, 16, 64):
+        for io in ("f32", "bf16"):
+            for n_lr in (4, 1):
+                assert (d, d, io, n_lr) in tape
+    assert not any(v["writes_tape"] and v["supports_reset"] for v in vs)
+
+
+def test_forward_tape_validation():
+    assert call_ex(tape=FAKE_TAPE, reset_interval=5) == E_ARG       # backward does not cover resets
+    assert call_ex(tape=FAKE_TAPE + 4) == E_ARG                     # misaligned
+    assert call_ex(tape=FAKE_X + 16) == E_ALIAS                     # overlaps x
+    assert call_ex(tape=FAKE_TAPE, d_in=128, d_out=128) == E_UNSUP  # no tape variant at d=128
+    vs = _lib.variants()
+    plain = next(v for v in vs if v["d_in"] == 16 and v["io_dtype"] == "f32" and v["n_lr"] == 4
+                 and not v["writes_tape"])
+    taped = next(v for v in vs if v["d_in"] == 16 and v["io_dtype"] == "f32" and v["n_lr"] == 4
+                 and v["writes_tape"])
+    assert call_ex(tape=FAKE_TAPE, variant=plain["index"]) == E_ARG
+    assert call_ex(variant=taped["index"]) == E_ARG
+
+
+def call_bwd(**kw):
+    base = dict(x=FAKE_X, W_T=FAKE_WT, tape=FAKE_TAPE, gy=FAKE_GY, gW_T=None, dx=FAKE_DX,
+                dW_init=FAKE_DWI, dW0=FAKE_DW0, B=2, T=3, H=2, d_in=16, d_out=16, m=None,
+                io_dtype=0, apply_input_softmax=0, n_lr=4, stream=None)
+    base.update(kw)
+    if base["m"] is None:
+        base["m"] = base["d_out"] + 2 * base["d_in"] + base["n_lr"]
+    return _lib.load().srwm_backward(ctypes.byref(_lib.BackwardArgs(**base)))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_lr=2), E_ARG),
+    (dict(m=51), E_SHAPE),
+    (dict(B=-1), E_SHAPE),
+    (dict(d_in=0), E_SHAPE),
+    (dict(io_dtype=2), E_ARG),
+    (dict(apply_input_softmax=3), E_ARG),
+    (dict(d_in=128, d_out=128), E_UNSUP),
+    (dict(W_T=None), E_NULL),
+    (dict(dW_init=None), E_NULL),
+    (dict(tape=None), E_NULL),
+    (dict(gy=None), E_NULL),
+    (dict(dx=None), E_NULL),
+    (dict(dx=FAKE_DX + 8), E_ARG),
+    (dict(dx=FAKE_X), E_ALIAS),
+    (dict(dW0=FAKE_DWI + 16), E_ALIAS),
+    (dict(gW_T=FAKE_DWI), E_ALIAS),
+    (dict(dW_init=FAKE_TAPE + 64), E_ALIAS),
+])
+def test_backward_validation(kw, code):
+    assert call_bwd(**kw) == code
+
+
+def test_backward_null_and_empty():
+    lib = _lib.load()
+    assert lib.srwm_backward(None) == E_NULL
+    assert call_bwd(B=0, x=None, W_T=None, tape=None, gy=None, dx=None, dW_init=None, dW0=None) == OK
+    assert call_bwd(H=0, x=None, W_T=None, tape=None, gy=None, dx=None, dW_init=None, dW0=None) == OK

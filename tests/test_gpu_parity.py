@@ -5,7 +5,7 @@ import pytest
 
 from oracle import oracle
 from self_referential_weight_amd.workloads import WORKLOADS, Workload, gen_W0, gen_x, round_to_bf16
-from tests._parity import check_state, check_y
+from tests._parity import check_state, check_y, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -26,15 +26,42 @@ def to_dev(x_np, io_dtype):
     return t.to(torch.bfloat16) if io_dtype == "bf16" else t
 
 
-def run_gpu(x_np, W0_np, io_dtype, flag, return_state=True, variant=-1, n_lr=4, reset_interval=0):
+def run_gpu(x_np, W0_np, io_dtype, flag, return_state=True, variant=-1, n_lr=4, reset_interval=0,
+            save_tape=False):
     srwm = _srwm()
-    y, WT = srwm.forward(to_dev(x_np, io_dtype), torch.from_numpy(np.ascontiguousarray(W0_np)).to(dev()),
-                         apply_input_softmax=flag, return_state=return_state, variant=variant,
-                         n_lr=n_lr, reset_interval=reset_interval)
+    out = srwm.forward(to_dev(x_np, io_dtype), torch.from_numpy(np.ascontiguousarray(W0_np)).to(dev()),
+                       apply_input_softmax=flag, return_state=return_state, variant=variant,
+                       n_lr=n_lr, reset_interval=reset_interval, save_tape=save_tape)
     torch.cuda.synchronize()
-    y = y.float().cpu().numpy()
-    WT = WT.cpu().numpy() if WT is not None else None
+    y = out[0].float().cpu().numpy()
+    WT = out[1].cpu().numpy() if out[1] is not None else None
+    if save_tape:
+        return y, WT, out[2].cpu().numpy()
     return y, WT
+
+
+def check_tape(tape, x, W0, d_out, flag, n_lr, units):
+    # The tape of unit (b, h) holds, per step, the update's row factor
+    # a_t = g_rate(row) * (v_t - vbar_t) and phi(k_t); both from the oracle's
+    # step-by-step quantities.
+    d_in = x.shape[-1]
+    m = W0.shape[-2]
+    kh_off = (m + 3) // 4 * 4
+    if n_lr == 4:
+        rate = np.array([0] * d_out + [1] * d_in + [2] * d_in + [3] * 4)
+    else:
+        rate = np.zeros(m, dtype=int)
+    for b, h in units:
+        W = W0[h].astype(np.float64)
+        a_ref, kh_ref = [], []
+        for t in range(x.shape[1]):
+            s = oracle.step(W, x[b, t, h], d_out, flag, n_lr)
+            a_ref.append(s["g"][rate] * (s["v"] - s["vb"]))
+            kh_ref.append(s["kh"])
+            W = s["W"]
+        tp = tape[b, h]
+        assert rel_l2(tp[:, :m], np.array(a_ref)) <= 2e-4
+        assert rel_l2(tp[:, kh_off:kh_off + d_in], np.array(kh_ref)) <= 2e-4
 
 
 def say(msg):
@@ -91,10 +118,14 @@ def test_variant_small(vi, T, flag):
     say(f"[parity] variant {v} T={T} flag={flag} reset={reset}")
     x = gen_x(w)
     W0 = gen_W0(w)
-    y, WT = run_gpu(x, W0, w.io_dtype, flag, variant=vi, n_lr=w.n_lr, reset_interval=reset)
+    out = run_gpu(x, W0, w.io_dtype, flag, variant=vi, n_lr=w.n_lr, reset_interval=reset,
+                  save_tape=v["writes_tape"])
+    y, WT = out[0], out[1]
     y_ref, WT_ref = oracle.forward(x, W0, flag, n_lr=w.n_lr, reset_interval=reset)
     check_y(y, y_ref, w.io_dtype, f"variant {vi}")
     check_state(WT, WT_ref, f"variant {vi}")
+    if v["writes_tape"]:
+        check_tape(out[2], x, W0, w.d_out, flag, w.n_lr, [(0, 0), (2, 1)])
 
 
 # ---------------------------------------------------------------------------
@@ -234,9 +265,10 @@ def test_bf16_output_is_rne_of_f32_path(name, flag):
             continue
         vb = next(v for v in vs if v["io_dtype"] == "bf16" and all(
             v[k] == vf[k] for k in ("d_in", "d_out", "n_lr", "waves", "lanes_per_row", "waves_per_simd",
-                                    "schedule", "supports_reset")))
-        yf, _ = run_gpu(x, W0, "f32", flag, return_state=False, variant=vf["index"])
-        yb, _ = run_gpu(x, W0, "bf16", flag, return_state=False, variant=vb["index"])
+                                    "schedule", "supports_reset", "writes_tape")))
+        tp = vf["writes_tape"]
+        yf = run_gpu(x, W0, "f32", flag, return_state=tp, variant=vf["index"], save_tape=tp)[0]
+        yb = run_gpu(x, W0, "bf16", flag, return_state=tp, variant=vb["index"], save_tape=tp)[0]
         np.testing.assert_array_equal(yb, round_to_bf16(yf))
         picked += 1
     assert picked >= 1
