@@ -35,7 +35,8 @@ sys.path.insert(0, str(ROOT))
 METRIC = "SRWM head-steps/sec (B·H·T/s) and % of FP32 VALU peak, 1×MI355X"
 # MI355X FP32 vector peak: 256 CUs x 256 FLOP/clk/CU x 2.4 GHz.
 PEAK_FP32_TFLOPS = 157.3
-KERNEL_SRC = ROOT / "self_referential_weight_amd" / "csrc" / "srwm_fwd.hip"
+# The forward kernels and the device helpers they include.
+KERNEL_SRCS = [ROOT / "self_referential_weight_amd" / "csrc" / f for f in ("srwm_fwd.hip", "srwm_device.h")]
 TRAFFIC_FILE = ROOT / "profiles" / "srwm_fwd_rl_d64_bf16_hbm_traffic.json"
 
 
@@ -44,7 +45,10 @@ def log(msg: str) -> None:
 
 
 def kernel_source_hash() -> str:
-    return hashlib.sha256(KERNEL_SRC.read_bytes()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(f.read_bytes())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str, variant: int):

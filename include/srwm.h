@@ -182,12 +182,17 @@ int srwm_select_variant(int64_t d_in, int64_t d_out, int io_dtype, int n_lr,
  * "Metalearning Continual Learning Algorithms" after Eq. (6) and the review
  * page Sec. 2.5).
  *
- * The forward pass run with args.tape != NULL records, per unit and step,
- * a_t (m floats, the rank-one update's row factor) and phi(k_t) (d_in
- * floats) at [b][h][t][0, m) and [b][h][t][srwm_tape_row - d_in, ...).  From
- * the final state W_T, srwm_backward walks t = T-1..0, undoes each update
- * (W_{t-1} = W_t - a_t phi(k_t)^T), recomputes the step and accumulates the
- * adjoint.  With L = sum_t <gy[t], y_t> + <gW_T, W_T> it writes
+ * The forward pass run with args.tape != NULL records, per unit and step, a
+ * row of srwm_tape_row() floats at tape[b][h][t][...]: with
+ * K = round_up(m, 4),
+ *   [0, m)            a_t, the row factor of the step's rank-one update
+ *   [K, K+d_in)       phi(k_t)
+ *   [K+d_in, K+2d_in) phi(q_t) - phi(k_t), rounded as the forward pass used it
+ *   [K+2d_in, +4)     the learning rates sigma(beta_t) (n_lr of them)
+ * ([m, K) is padding and is not written).  From the final state W_T,
+ * srwm_backward walks t = T-1..0, undoes each update (W_{t-1} = W_t -
+ * a_t phi(k_t)^T) and accumulates the adjoint; no projection is recomputed.
+ * With L = sum_t <gy[t], y_t> + <gW_T, W_T> it writes
  *   dx       [B][T][H][d_in]   dL/dx, float32 (also for bf16 x)
  *   dW_init  [B][H][m][d_in]   dL/d(initial state of each unit)
  *   dW0      [H][m][d_in]      sum over b of dW_init (the gradient of an
@@ -218,7 +223,7 @@ typedef struct srwm_backward_args {
 
 int srwm_backward(const srwm_backward_args_t* args);
 
-/* Floats per step in the tape: round_up(m, 4) + d_in, or SRWM_ERR_SHAPE. */
+/* Floats per step in the tape: round_up(m, 4) + 2*d_in + 4, or SRWM_ERR_SHAPE. */
 int64_t srwm_tape_row(int64_t d_in, int64_t d_out, int n_lr);
 
 /* 1 if srwm_backward has a kernel for (d_in, d_out, io_dtype, n_lr), else 0. */

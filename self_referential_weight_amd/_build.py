@@ -8,7 +8,7 @@ from pathlib import Path
 
 PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
-SRC = PKG / "csrc" / "srwm_fwd.hip"
+SRCS = [PKG / "csrc" / "srwm_fwd.hip", PKG / "csrc" / "srwm_bwd.hip"]
 LIB = PKG / "libsrwm.so"
 
 HIPCC_FLAGS = [
@@ -32,7 +32,7 @@ def hipcc() -> str:
 def build(verbose: bool = False) -> Path:
     """Compile the kernels and the C ABI into self_referential_weight_amd/libsrwm.so."""
     tmp = LIB.with_name(LIB.name + ".tmp")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", str(ROOT / "include"), "-o", str(tmp), str(SRC)]
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", str(ROOT / "include"), "-o", str(tmp), *[str(f) for f in SRCS]]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)

@@ -1,0 +1,226 @@
+// srwm_device.h -- device helpers shared by the forward and backward kernels
+// of libsrwm (gfx950): cross-lane reductions on DPP, the hardware exp2 and
+// reciprocal, bf16 conversion, 16-byte vector moves; and the host-side
+// argument checks both entry points use.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace srwm {
+
+constexpr int kWave = 64;
+
+// ----------------------------------------------------------------------------
+// Cross-lane helpers (GFX9 DPP encodings).
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within 8
+constexpr int kDppMirror = 0x140;     // lane i <- lane 15-i within 16
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of P adjacent lanes (P | 16); every lane of the
+// group gets the same bits (fp addition is commutative).
+template <int P>
+__device__ __forceinline__ float group_sum(float v)
+{
+    static_assert(P == 1 || P == 2 || P == 4 || P == 8 || P == 16, "P");
+    if constexpr (P >= 2) v += dpp<kDppXor1>(v);
+    if constexpr (P >= 4) v += dpp<kDppXor2>(v);
+    if constexpr (P >= 8) v += dpp<kDppHalfMirror>(v);
+    if constexpr (P >= 16) v += dpp<kDppMirror>(v);
+    return v;
+}
+
+// max(a, b) for finite or infinite operands (no NaN canonicalisation).
+__device__ __forceinline__ float fmax2(float a, float b) { return a > b ? a : b; }
+
+// Order-preserving map of a float to a signed int (an involution): positive
+// floats keep their bits, negative ones flip their magnitude bits, so signed
+// integer max equals float max (integer max fuses with DPP; float max would
+// need NaN canonicalisation of both operands).
+__device__ __forceinline__ int order_key(float f)
+{
+    const int b = __float_as_int(f);
+    return b ^ static_cast<int>(static_cast<unsigned>(b >> 31) >> 1);
+}
+
+__device__ __forceinline__ float from_order_key(int k)
+{
+    return __int_as_float(k ^ static_cast<int>(static_cast<unsigned>(k >> 31) >> 1));
+}
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+template <int P>
+__device__ __forceinline__ float group_max(float v)
+{
+    int k = order_key(v);
+    if constexpr (P >= 2) k = max(k, dpp_i<kDppXor1>(k));
+    if constexpr (P >= 4) k = max(k, dpp_i<kDppXor2>(k));
+    if constexpr (P >= 8) k = max(k, dpp_i<kDppHalfMirror>(k));
+    if constexpr (P >= 16) k = max(k, dpp_i<kDppMirror>(k));
+    return from_order_key(k);
+}
+
+__device__ __forceinline__ float readlane(float v, int l)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Wave-uniform max / sum over all 64 lanes (the cross-row step runs on the
+// scalar unit for the max).
+__device__ __forceinline__ float wave_max(float v)
+{
+    int k = order_key(v);
+    k = max(k, dpp_i<kDppXor1>(k));
+    k = max(k, dpp_i<kDppXor2>(k));
+    k = max(k, dpp_i<kDppHalfMirror>(k));
+    k = max(k, dpp_i<kDppMirror>(k));
+    const int m = max(max(__builtin_amdgcn_readlane(k, 0), __builtin_amdgcn_readlane(k, 16)),
+                      max(__builtin_amdgcn_readlane(k, 32), __builtin_amdgcn_readlane(k, 48)));
+    return from_order_key(m);
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v = group_sum<16>(v);
+    return (readlane(v, 0) + readlane(v, 16)) + (readlane(v, 32) + readlane(v, 48));
+}
+
+// e^x as 2^(x log2 e) on the hardware exp2 (v_exp_f32).
+__device__ __forceinline__ float exp_f32(float x)
+{
+    return __builtin_amdgcn_exp2f(x * 1.44269504088896340736f);
+}
+
+// 1/x on the hardware reciprocal (v_rcp_f32, 1 ulp).
+__device__ __forceinline__ float rcp_f32(float x) { return __builtin_amdgcn_rcpf(x); }
+
+__device__ __forceinline__ float sigmoid_f32(float z)
+{
+    return rcp_f32(1.0f + exp_f32(-z));
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h)
+{
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// float32 -> bfloat16, round to nearest, ties to even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f)
+{
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// Load N consecutive floats (16-byte aligned when N % 4 == 0).
+template <int N>
+__device__ __forceinline__ void load_f32(const float* __restrict__ src, float (&dst)[N])
+{
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < N / 4; ++i) {
+            const float4 v = reinterpret_cast<const float4*>(src)[i];
+            dst[4 * i + 0] = v.x;
+            dst[4 * i + 1] = v.y;
+            dst[4 * i + 2] = v.z;
+            dst[4 * i + 3] = v.w;
+        }
+    } else if constexpr (N % 2 == 0) {
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) {
+            const float2 v = reinterpret_cast<const float2*>(src)[i];
+            dst[2 * i + 0] = v.x;
+            dst[2 * i + 1] = v.y;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) dst[i] = src[i];
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void store_f32(float* __restrict__ dst, const float (&src)[N])
+{
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < N / 4; ++i)
+            reinterpret_cast<float4*>(dst)[i] =
+                make_float4(src[4 * i], src[4 * i + 1], src[4 * i + 2], src[4 * i + 3]);
+    } else if constexpr (N % 2 == 0) {
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i)
+            reinterpret_cast<float2*>(dst)[i] = make_float2(src[2 * i], src[2 * i + 1]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) dst[i] = src[i];
+    }
+}
+
+
+// Make this wave's LDS stores visible to its own later LDS loads from other
+// lanes (DS operations of one wave complete in order; this orders them in the
+// compiler and waits for the stores).
+__device__ __forceinline__ void wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float uniform(float v)
+{
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+
+// ----------------------------------------------------------------------------
+// The backward tape: one float32 row per (unit, step), written by the forward
+// pass and read by the backward pass.
+//   [0, m)                a_t, the row factor of the step's rank-one update
+//   [m, KH_OFF)           padding to a 16-byte boundary (not written)
+//   [KH_OFF, E_OFF)       phi(k_t)
+//   [E_OFF, G_OFF)        phi(q_t) - phi(k_t), as the forward pass rounded it
+//   [G_OFF, G_OFF + 4)    the learning rates sigma(beta_t) (n_lr of them, rest zero)
+template <int M, int D_IN>
+struct TapeLayout {
+    static constexpr int KH_OFF = (M + 3) & ~3;
+    static constexpr int E_OFF = KH_OFF + D_IN;
+    static constexpr int G_OFF = E_OFF + D_IN;
+    static constexpr int ROW = G_OFF + 4;
+};
+
+inline int64_t tape_row(int64_t d_in, int64_t d_out, int64_t n_lr)
+{
+    return ((d_out + 2 * d_in + n_lr + 3) & ~int64_t(3)) + 2 * d_in + 4;
+}
+
+// ----------------------------------------------------------------------------
+// Host-side helpers.
+
+inline bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb)
+{
+    if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+inline bool mul_ok(int64_t a, int64_t b, int64_t* out)
+{
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > INT64_MAX / a) return false;
+    *out = a * b;
+    return true;
+}
+
+}  // namespace srwm

@@ -37,165 +37,11 @@
 #include <type_traits>
 
 #include "srwm.h"
+#include "srwm_device.h"
 
 namespace {
 
-constexpr int kWave = 64;
-
-// ----------------------------------------------------------------------------
-// Cross-lane helpers (GFX9 DPP encodings).
-constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
-constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
-constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within 8
-constexpr int kDppMirror = 0x140;     // lane i <- lane 15-i within 16
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
-// Sum over aligned groups of P adjacent lanes (P | 16); every lane of the
-// group gets the same bits (fp addition is commutative).
-template <int P>
-__device__ __forceinline__ float group_sum(float v)
-{
-    static_assert(P == 1 || P == 2 || P == 4 || P == 8 || P == 16, "P");
-    if constexpr (P >= 2) v += dpp<kDppXor1>(v);
-    if constexpr (P >= 4) v += dpp<kDppXor2>(v);
-    if constexpr (P >= 8) v += dpp<kDppHalfMirror>(v);
-    if constexpr (P >= 16) v += dpp<kDppMirror>(v);
-    return v;
-}
-
-// max(a, b) for finite or infinite operands (no NaN canonicalisation).
-__device__ __forceinline__ float fmax2(float a, float b) { return a > b ? a : b; }
-
-// Order-preserving map of a float to a signed int (an involution): positive
-// floats keep their bits, negative ones flip their magnitude bits, so signed
-// integer max equals float max (integer max fuses with DPP; float max would
-// need NaN canonicalisation of both operands).
-__device__ __forceinline__ int order_key(float f)
-{
-    const int b = __float_as_int(f);
-    return b ^ static_cast<int>(static_cast<unsigned>(b >> 31) >> 1);
-}
-
-__device__ __forceinline__ float from_order_key(int k)
-{
-    return __int_as_float(k ^ static_cast<int>(static_cast<unsigned>(k >> 31) >> 1));
-}
-
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int v)
-{
-    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
-}
-
-template <int P>
-__device__ __forceinline__ float group_max(float v)
-{
-    int k = order_key(v);
-    if constexpr (P >= 2) k = max(k, dpp_i<kDppXor1>(k));
-    if constexpr (P >= 4) k = max(k, dpp_i<kDppXor2>(k));
-    if constexpr (P >= 8) k = max(k, dpp_i<kDppHalfMirror>(k));
-    if constexpr (P >= 16) k = max(k, dpp_i<kDppMirror>(k));
-    return from_order_key(k);
-}
-
-__device__ __forceinline__ float readlane(float v, int l)
-{
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
-
-// Wave-uniform max / sum over all 64 lanes (the cross-row step runs on the
-// scalar unit for the max).
-__device__ __forceinline__ float wave_max(float v)
-{
-    int k = order_key(v);
-    k = max(k, dpp_i<kDppXor1>(k));
-    k = max(k, dpp_i<kDppXor2>(k));
-    k = max(k, dpp_i<kDppHalfMirror>(k));
-    k = max(k, dpp_i<kDppMirror>(k));
-    const int m = max(max(__builtin_amdgcn_readlane(k, 0), __builtin_amdgcn_readlane(k, 16)),
-                      max(__builtin_amdgcn_readlane(k, 32), __builtin_amdgcn_readlane(k, 48)));
-    return from_order_key(m);
-}
-
-__device__ __forceinline__ float wave_sum(float v)
-{
-    v = group_sum<16>(v);
-    return (readlane(v, 0) + readlane(v, 16)) + (readlane(v, 32) + readlane(v, 48));
-}
-
-// e^x as 2^(x log2 e) on the hardware exp2 (v_exp_f32).
-__device__ __forceinline__ float exp_f32(float x)
-{
-    return __builtin_amdgcn_exp2f(x * 1.44269504088896340736f);
-}
-
-// 1/x on the hardware reciprocal (v_rcp_f32, 1 ulp).
-__device__ __forceinline__ float rcp_f32(float x) { return __builtin_amdgcn_rcpf(x); }
-
-__device__ __forceinline__ float sigmoid_f32(float z)
-{
-    return rcp_f32(1.0f + exp_f32(-z));
-}
-
-__device__ __forceinline__ float bf16_to_f32(uint16_t h)
-{
-    return __uint_as_float(static_cast<uint32_t>(h) << 16);
-}
-
-// float32 -> bfloat16, round to nearest, ties to even (v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f)
-{
-    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
-}
-
-// Load N consecutive floats (16-byte aligned when N % 4 == 0).
-template <int N>
-__device__ __forceinline__ void load_f32(const float* __restrict__ src, float (&dst)[N])
-{
-    if constexpr (N % 4 == 0) {
-#pragma unroll
-        for (int i = 0; i < N / 4; ++i) {
-            const float4 v = reinterpret_cast<const float4*>(src)[i];
-            dst[4 * i + 0] = v.x;
-            dst[4 * i + 1] = v.y;
-            dst[4 * i + 2] = v.z;
-            dst[4 * i + 3] = v.w;
-        }
-    } else if constexpr (N % 2 == 0) {
-#pragma unroll
-        for (int i = 0; i < N / 2; ++i) {
-            const float2 v = reinterpret_cast<const float2*>(src)[i];
-            dst[2 * i + 0] = v.x;
-            dst[2 * i + 1] = v.y;
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < N; ++i) dst[i] = src[i];
-    }
-}
-
-template <int N>
-__device__ __forceinline__ void store_f32(float* __restrict__ dst, const float (&src)[N])
-{
-    if constexpr (N % 4 == 0) {
-#pragma unroll
-        for (int i = 0; i < N / 4; ++i)
-            reinterpret_cast<float4*>(dst)[i] =
-                make_float4(src[4 * i], src[4 * i + 1], src[4 * i + 2], src[4 * i + 3]);
-    } else if constexpr (N % 2 == 0) {
-#pragma unroll
-        for (int i = 0; i < N / 2; ++i)
-            reinterpret_cast<float2*>(dst)[i] = make_float2(src[2 * i], src[2 * i + 1]);
-    } else {
-#pragma unroll
-        for (int i = 0; i < N; ++i) dst[i] = src[i];
-    }
-}
+using namespace srwm;
 
 // ----------------------------------------------------------------------------
 // Compile-time geometry of one kernel variant.
@@ -331,21 +177,6 @@ __device__ __forceinline__ void stream_lds(const float* __restrict__ src, F&& bo
             for (int c = 0; c < VW; ++c) cur[c] = nxt[c];
         }
     }
-}
-
-// Make this wave's LDS stores visible to its own later LDS loads from other
-// lanes (DS operations of one wave complete in order; this orders them in the
-// compiler and waits for the stores).
-__device__ __forceinline__ void wave_sync()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-__device__ __forceinline__ float uniform(float v)
-{
-    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
 }
 
 // x staging.  S step rows of x for one unit are loaded one chunk ahead into
@@ -622,10 +453,11 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
                     }
                 }
                 if constexpr (TAPE) {
-                    // Tape for the backward pass: a_t (m) and phi(k_t) (d_in) of this
-                    // step, enough to undo its update (W_{t-1} = W_t - a_t phi(k_t)^T).
-                    constexpr int KH_OFF = (M + 3) & ~3;  // phi(k_t) at a 16-byte boundary
-                    float* __restrict__ tp = tape + ((int64_t)unit * T + t) * (KH_OFF + D_IN);
+                    // Tape for the backward pass: a_t, phi(k_t) (enough to undo the
+                    // update, W_{t-1} = W_t - a_t phi(k_t)^T), phi(q_t) - phi(k_t) and
+                    // the learning rates (so the backward needs no projection).
+                    using TL = TapeLayout<M, D_IN>;
+                    float* __restrict__ tp = tape + ((int64_t)unit * T + t) * TL::ROW;
 #pragma unroll
                     for (int r0 = 0; r0 < R; r0 += P) {
                         float v = acc[r0];
@@ -639,8 +471,13 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
                     }
                     if (wave == 0) {
 #pragma unroll
-                        for (int j0 = 0; j0 < D_IN; j0 += kWave)
-                            if (j0 + lane < D_IN) tp[KH_OFF + j0 + lane] = khw[j0 + lane];
+                        for (int j0 = 0; j0 < D_IN; j0 += kWave) {
+                            if (j0 + lane < D_IN) {
+                                tp[TL::KH_OFF + j0 + lane] = khw[j0 + lane];
+                                tp[TL::E_OFF + j0 + lane] = ew[j0 + lane];
+                            }
+                        }
+                        if (lane < 4) tp[TL::G_OFF + lane] = lane < NLR ? gl : 0.f;
                     }
                 }
                 // ---- (D) Eq. (3)/(5): W += a kh^T, in place.
@@ -927,418 +764,6 @@ void srwm_fwd_fused_kernel(const void* __restrict__ xv, const float* __restrict_
 }
 
 // ----------------------------------------------------------------------------
-// Backward pass (memory-efficient BPTT).
-//
-// The pages train W0 by backpropagation through the unrolled self-modification
-// ("Metalearning Continual Learning Algorithms", after Eq. (6): memory-efficient
-// BPTT; review page Sec. 2.5).  The forward pass run with a tape stores, per
-// step, a_t = g (.) W_{t-1}(qh_t - kh_t) and kh_t: exactly what undoes its
-// update, W_{t-1} = W_t - a_t kh_t^T.  Walking t backwards from W_T, the kernel
-// reconstructs W_{t-1}, recomputes the step (z_t, kh, qh, e, g), and carries
-// the adjoint Wh = dL/dW in registers:
-//     ah    = Wh kh_t                 khh  = Wh^T a_t
-//     rh    = g (.) ah                betah_c = (1 - g_c) sum_{rate(i)=c} ah_i a_i
-//     eh    = W^T rh                  (khh -= eh, qhh = eh)
-//     kbar  = kh (.) (khh - <khh,kh>) qbar = qh (.) (qhh - <qhh,qh>)
-//     zh    = [gy_t; kbar; qbar; betah]
-//     uh    = W^T zh                  xh = uh, or softmax backward of it
-//     Wh   += rh e^T + zh u^T
-// after which Wh is dL/dW_{t-1}.  Layout: one wave per unit; lane (rg, p)
-// holds rows rg + G*r and columns [p*L, p*L + L) of both W and Wh (rate rows
-// in the strided layout, zero padded).  Row sums reduce over the P lanes of a
-// row group (DPP), column sums over the G row groups (DPP rotations inside a
-// 16-lane row, then lane exchanges across rows).
-constexpr int kDppRor4 = 0x124;  // lane i <- lane (i+4) mod 16 within a row
-constexpr int kDppRor8 = 0x128;  // lane i <- lane (i+8) mod 16 within a row
-
-// Sum over the lanes of a wave that share p = lane % P (the G row groups).
-template <int P>
-__device__ __forceinline__ float colgroup_sum(float v)
-{
-    static_assert(P == 1 || P == 2 || P == 4 || P == 8 || P == 16, "P");
-    if constexpr (P <= 1) v += dpp<0x121>(v);  // ror 1
-    if constexpr (P <= 2) v += dpp<0x122>(v);  // ror 2
-    if constexpr (P <= 4) v += dpp<kDppRor4>(v);
-    if constexpr (P <= 8) v += dpp<kDppRor8>(v);
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    return v;
-}
-
-template <int D_IN, int D_OUT, int NW, int P, int NLR, bool BF16>
-__global__ __attribute__((amdgpu_flat_work_group_size(NW * kWave, NW * kWave), amdgpu_waves_per_eu(1)))
-void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin,
-                     const float* __restrict__ tape, const float* __restrict__ gy,
-                     const float* __restrict__ gWT, float* __restrict__ dx,
-                     float* __restrict__ dWinit, int T, int H, int in_softmax)
-{
-    constexpr int NT = NW * kWave;
-    constexpr int M = D_OUT + 2 * D_IN + NLR;
-    constexpr int MAIN = D_OUT + 2 * D_IN;
-    constexpr int L = D_IN / P;
-    constexpr int G = NT / P;
-    constexpr int GW = kWave / P;  // row groups per wave
-    constexpr int R = (M + G - 1) / G;
-    constexpr int KH_OFF = (M + 3) & ~3;  // tape row: a_t, pad, kh_t
-    constexpr int TW = KH_OFF + D_IN;
-    constexpr int EPL = (D_IN + kWave - 1) / kWave;
-    static_assert(D_IN % P == 0 && D_IN % G == 0 && D_OUT % G == 0, "layout must align with blocks");
-    static_assert(D_OUT <= NT, "one lane per output entry");
-
-    __shared__ __attribute__((aligned(16))) float s_tape[2][TW];
-    __shared__ __attribute__((aligned(16))) float s_u[2][D_IN];
-    __shared__ __attribute__((aligned(16))) float s_gy[2][D_OUT];
-    __shared__ __attribute__((aligned(16))) float s_z[R * G];
-    __shared__ __attribute__((aligned(16))) float s_zh[R * G];
-    __shared__ __attribute__((aligned(16))) float s_kh[NW][D_IN];
-    __shared__ __attribute__((aligned(16))) float s_qh[NW][D_IN];
-    __shared__ __attribute__((aligned(16))) float s_e[NW][D_IN];
-    // per-wave partial column sums: khh, eh (then uh), and the betah partials
-    __shared__ __attribute__((aligned(16))) float s_red[NW][2][D_IN];
-    __shared__ __attribute__((aligned(16))) float s_bred[NW][4];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = NW == 1 ? 0 : tid / kWave;
-    const int p = tid % P;
-    const int rg = tid / P;
-    const bool wave_lead = (lane / P) == 0;  // row group 0 of this wave: lanes 0..P-1
-    const int unit = blockIdx.x;
-    const int b = unit / H;
-    const int h = unit - b * H;
-    const int64_t x_step = (int64_t)H * D_IN;
-    const int64_t y_step = (int64_t)H * D_OUT;
-    const int64_t x0 = ((int64_t)b * T * H + h) * D_IN;
-    const int64_t y0 = ((int64_t)b * T * H + h) * D_OUT;
-    const float* __restrict__ tp0 = tape + (int64_t)unit * T * TW;
-
-    // W <- W_T, Wh <- dL/dW_T (or 0)
-    float w[R][L], wh[R][L];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int row = rg + G * r;
-        if (row < M) {
-            load_f32<L>(WTin + ((int64_t)unit * M + row) * D_IN + p * L, w[r]);
-            if (gWT != nullptr) {
-                load_f32<L>(gWT + ((int64_t)unit * M + row) * D_IN + p * L, wh[r]);
-            } else {
-#pragma unroll
-                for (int c = 0; c < L; ++c) wh[r][c] = 0.f;
-            }
-        } else {
-#pragma unroll
-            for (int c = 0; c < L; ++c) w[r][c] = wh[r][c] = 0.f;
-        }
-    }
-
-    // Step inputs are fetched one step ahead into registers and staged into a
-    // double-buffered LDS slot: tape row (threads < TW), x_t (wave 0), gy_t.
-    constexpr int TPL = (TW + NT - 1) / NT;
-    float tnext[TPL];
-    float xnext[EPL];
-    float gnext = 0.f;
-    auto fetch = [&](int t) {
-        const float* __restrict__ tp = tp0 + (int64_t)t * TW;
-#pragma unroll
-        for (int i = 0; i < TPL; ++i) {
-            const int j = tid + NT * i;
-            tnext[i] = (j < TW) ? tp[j] : 0.f;
-        }
-        if (wave == 0) {
-#pragma unroll
-            for (int i = 0; i < EPL; ++i) {
-                const int j = lane + kWave * i;
-                if (j < D_IN) {
-                    if constexpr (BF16)
-                        xnext[i] = bf16_to_f32(reinterpret_cast<const uint16_t*>(xv)[x0 + (int64_t)t * x_step + j]);
-                    else
-                        xnext[i] = reinterpret_cast<const float*>(xv)[x0 + (int64_t)t * x_step + j];
-                } else {
-                    xnext[i] = 0.f;
-                }
-            }
-        }
-        if (tid < D_OUT) gnext = gy[y0 + (int64_t)t * y_step + tid];
-    };
-    auto stage = [&](int slot) {
-#pragma unroll
-        for (int i = 0; i < TPL; ++i) {
-            const int j = tid + NT * i;
-            if (j < TW) s_tape[slot][j] = tnext[i];
-        }
-        if (wave == 0) {
-            float uv[EPL];
-            if (in_softmax) {
-                float mx = -INFINITY;
-#pragma unroll
-                for (int i = 0; i < EPL; ++i) mx = fmax2(mx, (lane + kWave * i < D_IN) ? xnext[i] : -INFINITY);
-                mx = wave_max(mx);
-                float sum = 0.f;
-#pragma unroll
-                for (int i = 0; i < EPL; ++i) {
-                    uv[i] = (lane + kWave * i < D_IN) ? exp_f32(xnext[i] - mx) : 0.f;
-                    sum += uv[i];
-                }
-                const float inv = rcp_f32(wave_sum(sum));
-#pragma unroll
-                for (int i = 0; i < EPL; ++i) uv[i] *= inv;
-            } else {
-#pragma unroll
-                for (int i = 0; i < EPL; ++i) uv[i] = xnext[i];
-            }
-#pragma unroll
-            for (int i = 0; i < EPL; ++i)
-                if (lane + kWave * i < D_IN) s_u[slot][lane + kWave * i] = uv[i];
-        }
-        if (tid < D_OUT) s_gy[slot][tid] = gnext;
-    };
-    // Sum of this lane's L column partials over every row group of the unit:
-    // in-wave lane exchange, then the NW wave partials through LDS (fixed
-    // order, so every lane ends with the same bits).
-    auto colsum2 = [&](float (&va)[L], float (&vb)[L]) {
-#pragma unroll
-        for (int c = 0; c < L; ++c) {
-            va[c] = colgroup_sum<P>(va[c]);
-            vb[c] = colgroup_sum<P>(vb[c]);
-        }
-        if constexpr (NW > 1) {
-            if (wave_lead) {
-                store_f32<L>(&s_red[wave][0][p * L], va);
-                store_f32<L>(&s_red[wave][1][p * L], vb);
-            }
-            __syncthreads();
-#pragma unroll
-            for (int c = 0; c < L; ++c) {
-                float sa = 0.f, sb = 0.f;
-#pragma unroll
-                for (int wv = 0; wv < NW; ++wv) {
-                    sa += s_red[wv][0][p * L + c];
-                    sb += s_red[wv][1][p * L + c];
-                }
-                va[c] = sa;
-                vb[c] = sb;
-            }
-        }
-    };
-
-    if (T > 0) {
-        fetch(T - 1);
-        stage((T - 1) & 1);
-        if (T > 1) fetch(T - 2);
-        __syncthreads();
-    }
-
-    for (int t = T - 1; t >= 0; --t) {
-        const int slot = t & 1;
-        const float* __restrict__ tt = s_tape[slot];
-        const float* __restrict__ us = s_u[slot];
-
-        // ---- undo the update of step t: W_{t-1} = W_t - a_t kh_t^T
-        float a[R], kt[L], u[L];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int row = rg + G * r;
-            a[r] = row < M ? tt[row] : 0.f;
-        }
-        load_f32<L>(tt + KH_OFF + p * L, kt);
-        load_f32<L>(us + p * L, u);
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int c = 0; c < L; ++c) w[r][c] = fmaf(-a[r], kt[c], w[r][c]);
-
-        // ---- z = W u (rows); ah = Wh kh_t (rows); khh = Wh^T a_t (column partials)
-        float ah[R], khh[L];
-#pragma unroll
-        for (int c = 0; c < L; ++c) khh[c] = 0.f;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            float zs = 0.f, as = 0.f;
-#pragma unroll
-            for (int c = 0; c < L; ++c) {
-                zs = fmaf(w[r][c], u[c], zs);
-                as = fmaf(wh[r][c], kt[c], as);
-                khh[c] = fmaf(wh[r][c], a[r], khh[c]);
-            }
-            zs = group_sum<P>(zs);
-            ah[r] = group_sum<P>(as);
-            const int row = rg + G * r;
-            if (p == 0) s_z[row] = zs;
-        }
-        __syncthreads();
-
-        // ---- recompute phi(k_t), phi(q_t), e_t (every wave, own slice) and the rates
-        {
-            float kv[EPL], qv[EPL];
-            float mk = -INFINITY, mq = -INFINITY;
-#pragma unroll
-            for (int i = 0; i < EPL; ++i) {
-                const int j = lane + kWave * i;
-                kv[i] = j < D_IN ? s_z[D_OUT + j] : -INFINITY;
-                qv[i] = j < D_IN ? s_z[D_OUT + D_IN + j] : -INFINITY;
-                mk = fmax2(mk, kv[i]);
-                mq = fmax2(mq, qv[i]);
-            }
-            mk = wave_max(mk);
-            mq = wave_max(mq);
-            float sk = 0.f, sq = 0.f;
-#pragma unroll
-            for (int i = 0; i < EPL; ++i) {
-                const int j = lane + kWave * i;
-                kv[i] = j < D_IN ? exp_f32(kv[i] - mk) : 0.f;
-                qv[i] = j < D_IN ? exp_f32(qv[i] - mq) : 0.f;
-                sk += kv[i];
-                sq += qv[i];
-            }
-            const float ik = rcp_f32(wave_sum(sk)), iq = rcp_f32(wave_sum(sq));
-#pragma unroll
-            for (int i = 0; i < EPL; ++i) {
-                const int j = lane + kWave * i;
-                if (j < D_IN) {
-#pragma clang fp contract(off)
-                    const float khv = kv[i] * ik, qhv = qv[i] * iq;
-                    s_kh[wave][j] = khv;
-                    s_qh[wave][j] = qhv;
-                    s_e[wave][j] = qhv - khv;
-                }
-            }
-        }
-        const float gl = sigmoid_f32(s_z[MAIN + (NLR == 4 ? (lane & 3) : 0)]);
-        const float g0 = readlane(gl, 0), g1 = readlane(gl, 1), g2 = readlane(gl, 2), g3 = readlane(gl, 3);
-
-        // ---- rh = g (.) ah ; eh = W^T rh (column partials); betah partials
-        float rh[R], eh[L];
-        float bp0 = 0.f, bp1 = 0.f, bp2 = 0.f, bp3 = 0.f;
-#pragma unroll
-        for (int c = 0; c < L; ++c) eh[c] = 0.f;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int row = rg + G * r;
-            const int rt = NLR == 1 ? 0 : (G * r < D_OUT ? 0 : G * r < D_OUT + D_IN ? 1 : G * r < MAIN ? 2 : 3);
-            const float bv = (p == 0 && row < M) ? ah[r] * a[r] : 0.f;  // each row once
-            if (rt == 0) bp0 += bv;
-            else if (rt == 1) bp1 += bv;
-            else if (rt == 2) bp2 += bv;
-            else bp3 += bv;
-            rh[r] = (rt == 0 ? g0 : rt == 1 ? g1 : rt == 2 ? g2 : g3) * ah[r];
-#pragma unroll
-            for (int c = 0; c < L; ++c) eh[c] = fmaf(w[r][c], rh[r], eh[c]);
-        }
-        bp0 = wave_sum(bp0);
-        if constexpr (NLR == 4) {
-            bp1 = wave_sum(bp1);
-            bp2 = wave_sum(bp2);
-            bp3 = wave_sum(bp3);
-        }
-        if constexpr (NW > 1) {
-            if (lane == 0) {
-                s_bred[wave][0] = bp0;
-                s_bred[wave][1] = bp1;
-                s_bred[wave][2] = bp2;
-                s_bred[wave][3] = bp3;
-            }
-        }
-        colsum2(khh, eh);  // (the barrier inside also publishes s_bred)
-        if constexpr (NW > 1) {
-            bp0 = bp1 = bp2 = bp3 = 0.f;
-#pragma unroll
-            for (int wv = 0; wv < NW; ++wv) {
-                bp0 += s_bred[wv][0];
-                bp1 += s_bred[wv][1];
-                bp2 += s_bred[wv][2];
-                bp3 += s_bred[wv][3];
-            }
-        }
-
-        // ---- softmax backward: kh (adjoint khh - eh), qh (adjoint eh)
-        float khv[L], qhv[L], ev[L];
-        load_f32<L>(&s_kh[wave][p * L], khv);
-        load_f32<L>(&s_qh[wave][p * L], qhv);
-        load_f32<L>(&s_e[wave][p * L], ev);
-        float dk = 0.f, dq = 0.f;
-#pragma unroll
-        for (int c = 0; c < L; ++c) {
-            khh[c] -= eh[c];
-            dk = fmaf(khh[c], khv[c], dk);
-            dq = fmaf(eh[c], qhv[c], dq);
-        }
-        dk = group_sum<P>(dk);
-        dq = group_sum<P>(dq);
-        if (rg == 0) {
-#pragma unroll
-            for (int c = 0; c < L; ++c) {
-                s_zh[D_OUT + p * L + c] = khv[c] * (khh[c] - dk);
-                s_zh[D_OUT + D_IN + p * L + c] = qhv[c] * (eh[c] - dq);
-            }
-        }
-        if (tid < D_OUT) s_zh[tid] = s_gy[slot][tid];
-        if (tid == 0) {
-            s_zh[MAIN] = (1.f - g0) * bp0;
-            if (NLR == 4) {
-                s_zh[MAIN + 1] = (1.f - g1) * bp1;
-                s_zh[MAIN + 2] = (1.f - g2) * bp2;
-                s_zh[MAIN + 3] = (1.f - g3) * bp3;
-            }
-        }
-        __syncthreads();
-
-        // ---- uh = W^T zh (column partials); Wh += rh e^T + zh u^T
-        float uh[L], unused[L];
-#pragma unroll
-        for (int c = 0; c < L; ++c) uh[c] = unused[c] = 0.f;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int row = rg + G * r;
-            const float zhr = row < M ? s_zh[row] : 0.f;
-#pragma unroll
-            for (int c = 0; c < L; ++c) {
-                uh[c] = fmaf(w[r][c], zhr, uh[c]);
-                wh[r][c] = fmaf(rh[r], ev[c], fmaf(zhr, u[c], wh[r][c]));
-            }
-        }
-        // stage the inputs of step t-1 (read after the barriers below)
-        if (t > 0) {
-            stage((t - 1) & 1);
-            if (t > 1) fetch(t - 2);
-        }
-        if constexpr (NW > 1) __syncthreads();  // s_red of the previous exchange is free again
-        colsum2(uh, unused);
-
-        // ---- xh: uh, or the softmax backward of it
-        if (in_softmax) {
-            float du = 0.f;
-#pragma unroll
-            for (int c = 0; c < L; ++c) du = fmaf(uh[c], u[c], du);
-            du = group_sum<P>(du);
-#pragma unroll
-            for (int c = 0; c < L; ++c) uh[c] = u[c] * (uh[c] - du);
-        }
-        if (rg == 0) store_f32<L>(dx + x0 + (int64_t)t * x_step + p * L, uh);
-        __syncthreads();
-    }
-
-    // dL/d(initial state of this unit)
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int row = rg + G * r;
-        if (row < M) store_f32<L>(dWinit + ((int64_t)unit * M + row) * D_IN + p * L, wh[r]);
-    }
-}
-
-// dW0[h] = sum_b dWinit[b][h] (the gradient of the initial matrix shared over
-// the batch), summed in a fixed order b = 0, 1, ...
-__global__ __launch_bounds__(256) void srwm_sum_over_batch_kernel(const float* __restrict__ dWinit,
-                                                                  float* __restrict__ dW0, int64_t B,
-                                                                  int64_t per_b)
-{
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= per_b) return;
-    float s = 0.f;
-    for (int64_t b = 0; b < B; ++b) s += dWinit[b * per_b + i];
-    dW0[i] = s;
-}
-
-// ----------------------------------------------------------------------------
 // Variant table.
 using KernelFn = void (*)(const void*, const float*, void*, float*, float*, int, int, int, int, int);
 
@@ -1427,47 +852,11 @@ const Variant kVariants[] = {
     SRWM_BOTH_IO_TAPE(64, 64, 2, 8, 2, 1, 1),
 };
 
-// Backward kernels: (d_in, d_out, waves per unit, lanes per row, learning
-// rates), both I/O dtypes.
-using BwdFn = void (*)(const void*, const float*, const float*, const float*, const float*, float*,
-                       float*, int, int, int);
-struct BwdVariant {
-    int d_in, d_out, io, nlr, nw;
-    BwdFn fn;
-};
-#define SRWM_BWD(DI, DO, NW, P, NLR)                                                            \
-    BwdVariant{DI, DO, SRWM_IO_F32, NLR, NW, &srwm_bwd_kernel<DI, DO, NW, P, NLR, false>},      \
-        BwdVariant{DI, DO, SRWM_IO_BF16, NLR, NW, &srwm_bwd_kernel<DI, DO, NW, P, NLR, true>}
-const BwdVariant kBwdVariants[] = {
-    SRWM_BWD(8, 8, 1, 8, 4), SRWM_BWD(16, 16, 1, 8, 4), SRWM_BWD(64, 64, 4, 8, 4),
-    SRWM_BWD(8, 8, 1, 8, 1), SRWM_BWD(16, 16, 1, 8, 1), SRWM_BWD(64, 64, 4, 8, 1),
-};
-constexpr int kNumBwdVariants = sizeof(kBwdVariants) / sizeof(kBwdVariants[0]);
-
-int64_t tape_row(int64_t d_in, int64_t d_out, int64_t n_lr)
-{
-    return ((d_out + 2 * d_in + n_lr + 3) & ~int64_t(3)) + d_in;
-}
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 // Two waves per SIMD of the chip (256 CUs x 4 SIMDs x 2): enough waves to
 // hide one wave's latency behind another's arithmetic.
 constexpr int64_t kChipWaveSlots = 2048;
-
-bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb)
-{
-    if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
-    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
-    return a0 < b0 + nb && b0 < a0 + na;
-}
-
-bool mul_ok(int64_t a, int64_t b, int64_t* out)
-{
-    if (a < 0 || b < 0) return false;
-    if (a != 0 && b > INT64_MAX / a) return false;
-    *out = a * b;
-    return true;
-}
 
 bool variant_matches(const Variant& v, int64_t d_in, int64_t d_out, int io, int nlr, bool reset, bool tape)
 {
@@ -1584,79 +973,6 @@ srwm_forward_args_t basic_args(const void* x, const float* W0, void* y, float* W
     return a;
 }
 
-int backward_impl(const srwm_backward_args_t* a)
-{
-    if (a == nullptr) return SRWM_ERR_NULL;
-    const int64_t B = a->B, T = a->T, H = a->H, d_in = a->d_in, d_out = a->d_out, m = a->m;
-    if (B < 0 || T < 0 || H < 0 || d_in < 1 || d_out < 1) return SRWM_ERR_SHAPE;
-    if (a->n_lr != 1 && a->n_lr != 4) return SRWM_ERR_ARG;
-    if (m != d_out + 2 * d_in + a->n_lr) return SRWM_ERR_SHAPE;
-    if (a->io_dtype != SRWM_IO_F32 && a->io_dtype != SRWM_IO_BF16) return SRWM_ERR_ARG;
-    if (a->apply_input_softmax != 0 && a->apply_input_softmax != 1) return SRWM_ERR_ARG;
-    int vi = -1;
-    for (int i = 0; i < kNumBwdVariants; ++i) {
-        const BwdVariant& v = kBwdVariants[i];
-        if (v.d_in == d_in && v.d_out == d_out && v.io == a->io_dtype && v.nlr == a->n_lr) vi = i;
-    }
-    if (vi < 0) return SRWM_ERR_UNSUPPORTED;
-    const int64_t es = a->io_dtype == SRWM_IO_BF16 ? 2 : 4;
-    int64_t units, steps, nx, ndx, ngy, nst, ntape, nw0;
-    if (!mul_ok(B, H, &units) || !mul_ok(units, T, &steps) || !mul_ok(steps, d_in * es, &nx) ||
-        !mul_ok(steps, d_in * 4, &ndx) || !mul_ok(steps, d_out * 4, &ngy) ||
-        !mul_ok(units, m * d_in * 4, &nst) || !mul_ok(steps, tape_row(d_in, d_out, a->n_lr) * 4, &ntape) ||
-        !mul_ok(H, m * d_in * 4, &nw0))
-        return SRWM_ERR_SHAPE;
-    if (units > INT32_MAX || T > INT32_MAX || H > INT32_MAX) return SRWM_ERR_SHAPE;
-    if ((nst > 0 && (a->W_T == nullptr || a->dW_init == nullptr)) || (ntape > 0 && a->tape == nullptr) ||
-        (nx > 0 && (a->x == nullptr || a->dx == nullptr)) || (ngy > 0 && a->gy == nullptr))
-        return SRWM_ERR_NULL;
-    if ((reinterpret_cast<uintptr_t>(a->x) | reinterpret_cast<uintptr_t>(a->W_T) |
-         reinterpret_cast<uintptr_t>(a->tape) | reinterpret_cast<uintptr_t>(a->gy) |
-         reinterpret_cast<uintptr_t>(a->gW_T) | reinterpret_cast<uintptr_t>(a->dx) |
-         reinterpret_cast<uintptr_t>(a->dW_init) | reinterpret_cast<uintptr_t>(a->dW0)) & 15u)
-        return SRWM_ERR_ARG;
-    hipStream_t st = static_cast<hipStream_t>(a->stream);
-    auto sum_over_batch = [&]() -> int {
-        // dW0 = sum over b of dW_init (zero when B == 0)
-        const int64_t per_b = H * m * d_in;
-        if (a->dW0 == nullptr || per_b == 0) return SRWM_OK;
-        const float* dWi = a->dW_init;
-        float* dW0 = a->dW0;
-        int64_t Bv = B, pb = per_b;
-        void* args2[] = {const_cast<float**>(&dWi), &dW0, &Bv, &pb};
-        const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&srwm_sum_over_batch_kernel),
-                                             dim3(static_cast<unsigned>((per_b + 255) / 256)), dim3(256),
-                                             args2, 0, st);
-        return e == hipSuccess ? SRWM_OK : SRWM_ERR_HIP;
-    };
-    if (units == 0) return sum_over_batch();
-    const void* ins[] = {a->x, a->W_T, a->tape, a->gy, a->gW_T};
-    const int64_t nins[] = {nx, nst, ntape, ngy, a->gW_T ? nst : 0};
-    void* outs[] = {a->dx, a->dW_init, a->dW0};
-    const int64_t nouts[] = {ndx, nst, a->dW0 ? nw0 : 0};
-    for (int o = 0; o < 3; ++o) {
-        for (int i = 0; i < 5; ++i)
-            if (ranges_overlap(outs[o], nouts[o], ins[i], nins[i])) return SRWM_ERR_ALIAS;
-        for (int o2 = o + 1; o2 < 3; ++o2)
-            if (ranges_overlap(outs[o], nouts[o], outs[o2], nouts[o2])) return SRWM_ERR_ALIAS;
-    }
-    const BwdVariant& v = kBwdVariants[vi];
-    const void* x = a->x;
-    const float* WTp = a->W_T;
-    const float* tape = a->tape;
-    const float* gy = a->gy;
-    const float* gWT = a->gW_T;
-    float* dx = a->dx;
-    float* dWi = a->dW_init;
-    int Ti = static_cast<int>(T), Hi = static_cast<int>(H), fl = a->apply_input_softmax;
-    void* args[] = {const_cast<void**>(&x), const_cast<float**>(&WTp), const_cast<float**>(&tape),
-                    const_cast<float**>(&gy), const_cast<float**>(&gWT), &dx, &dWi, &Ti, &Hi, &fl};
-    const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(v.fn),
-                                           dim3(static_cast<unsigned>(units)), dim3(v.nw * kWave), args, 0, st);
-    if (err != hipSuccess) return SRWM_ERR_HIP;
-    return sum_over_batch();
-}
-
 }  // namespace
 
 extern "C" {
@@ -1681,21 +997,10 @@ int srwm_forward_variant(const void* x, const float* W0, void* y, float* W_T, in
 
 int srwm_forward_ex(const srwm_forward_args_t* args) { return forward_impl(args); }
 
-int srwm_backward(const srwm_backward_args_t* args) { return backward_impl(args); }
-
 int64_t srwm_tape_row(int64_t d_in, int64_t d_out, int n_lr)
 {
     if (d_in < 1 || d_out < 1 || (n_lr != 1 && n_lr != 4)) return SRWM_ERR_SHAPE;
     return tape_row(d_in, d_out, n_lr);
-}
-
-int srwm_backward_supported(int64_t d_in, int64_t d_out, int io_dtype, int n_lr)
-{
-    for (int i = 0; i < kNumBwdVariants; ++i) {
-        const BwdVariant& v = kBwdVariants[i];
-        if (v.d_in == d_in && v.d_out == d_out && v.io == io_dtype && v.nlr == n_lr) return 1;
-    }
-    return 0;
 }
 
 int srwm_variant_count(void) { return kNumVariants; }

@@ -175,7 +175,7 @@ def test_tape_row_and_backward_support():
     lib = _lib.load()
     for d_in, d_out, n_lr in [(8, 8, 4), (16, 16, 1), (64, 64, 4), (64, 64, 1), (3, 5, 1)]:
         m = d_out + 2 * d_in + n_lr
-        assert lib.srwm_tape_row(d_in, d_out, n_lr) == (m + 3) // 4 * 4 + d_in
+        assert lib.srwm_tape_row(d_in, d_out, n_lr) == (m + 3) // 4 * 4 + 2 * d_in + 4
     assert lib.srwm_tape_row(0, 8, 4) == E_SHAPE
     assert lib.srwm_tape_row(8, 8, 2) == E_SHAPE
     for d in (8, 16, 64):
