@@ -38,29 +38,32 @@ PEAK_FP32_TFLOPS = 157.3
 # The forward kernels and the device helpers they include.
 KERNEL_SRCS = [ROOT / "self_referential_weight_amd" / "csrc" / f for f in ("srwm_fwd.hip", "srwm_device.h")]
 TRAFFIC_FILE = ROOT / "profiles" / "srwm_fwd_rl_d64_bf16_hbm_traffic.json"
+# The backward kernel and the device helpers it includes.
+BWD_SRCS = [ROOT / "self_referential_weight_amd" / "csrc" / f for f in ("srwm_bwd.hip", "srwm_device.h")]
+BWD_TRAFFIC_FILE = ROOT / "profiles" / "srwm_bwd_rl_d64_bf16_hbm_traffic.json"
 
 
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(srcs=None) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SRCS:
+    for f in (KERNEL_SRCS if srcs is None else srcs):
         h.update(f.read_bytes())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, variant: int):
+def measured_traffic(workload: str, variant: int, path=TRAFFIC_FILE, srcs=None):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
     runs, if they were taken on the current kernel source; else None."""
-    if not TRAFFIC_FILE.exists():
+    if not path.exists():
         return None
     try:
-        rec = json.loads(TRAFFIC_FILE.read_text())
+        rec = json.loads(path.read_text())
     except ValueError:
         return None
-    if (rec.get("kernel_source_sha256_16") != kernel_source_hash()
+    if (rec.get("kernel_source_sha256_16") != kernel_source_hash(srcs)
             or rec.get("workload") != workload or rec.get("variant", -1) != variant):
         return None
     return rec.get("hbm_bytes_per_launch")
@@ -100,6 +103,20 @@ def cpu_baseline(w, x_host, W0_host, budget_s: float):
     }
 
 
+def copy_calibration(nbytes: int, dev) -> None:
+    """Three plain device-to-device copies of nbytes (scale reference for the
+    HBM byte counters)."""
+    import torch
+
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    bcopy = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        bcopy.copy_(a)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: 3 copies of {nbytes} bytes done")
+
+
 def cpu_baseline_backward(w, x_host, W0_host, gy_host, budget_s: float):
     """Time the float64 gradient oracle on the first n sequences, n sized from
     a calibration run on a prefix of one sequence so the run takes about budget_s."""
@@ -113,10 +130,11 @@ def cpu_baseline_backward(w, x_host, W0_host, gy_host, budget_s: float):
     t0 = time.perf_counter()
     oracle_bwd.grads(x_host[:1, :Tc], W0_host, w.apply_input_softmax, gy_host[:1, :Tc], n_lr=w.n_lr)
     per_step = (time.perf_counter() - t0) / Tc          # seconds per step of one sequence
-    n = max(1, min(w.B, int(budget_s / (per_step * w.T))))
+    # autograd over a longer, batched run costs about twice the prefix's rate per step
+    n = max(1, min(w.B, int(budget_s / (2.0 * per_step * w.T))))
     T = w.T
-    if n == 1 and per_step * w.T > budget_s:
-        T = max(1, int(budget_s / per_step))
+    if n == 1 and 2.0 * per_step * w.T > budget_s:
+        T = max(1, int(budget_s / (2.0 * per_step)))
     t0 = time.perf_counter()
     oracle_bwd.grads(np.ascontiguousarray(x_host[:n, :T]), W0_host, w.apply_input_softmax,
                      np.ascontiguousarray(gy_host[:n, :T]), n_lr=w.n_lr)
@@ -179,23 +197,15 @@ def main() -> int:
     W_T = torch.empty((w.B, w.H, w.m, w.d_in), dtype=torch.float32, device=dev) if w.return_state else None
     stream = torch.cuda.current_stream(dev)
 
+    if args.copy_calibration:
+        copy_calibration(int(args.copy_calibration), dev)
+
     if args.backward:
         return bench_backward(args, w, name, x, x_host, W0, W0_host, dev)
 
     def step():
         srwm.forward(x, W0, apply_input_softmax=w.apply_input_softmax, return_state=w.return_state,
                      variant=args.variant, y=y, W_T=W_T, stream=stream)
-
-    if args.copy_calibration:
-        nbytes = int(args.copy_calibration)
-        a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
-        bcopy = torch.empty_like(a)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            bcopy.copy_(a)
-        torch.cuda.synchronize()
-        log(f"[bench] copy calibration: 3 copies of {nbytes} bytes done")
-        del a, bcopy
 
     for _ in range(args.warmup):
         step()
@@ -317,7 +327,8 @@ def bench_backward(args, w, name, x, x_host, W0, W0_host, dev) -> int:
         "config": {"workload": name + "+backward", "B": w.B, "H": w.H, "d_in": w.d_in, "d_out": w.d_out,
                    "T": w.T, "io_dtype": w.io_dtype, "apply_input_softmax": w.apply_input_softmax},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_TFLOPS, "traffic": None},
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_TFLOPS,
+                     "traffic": measured_traffic(name + "+backward", -1, BWD_TRAFFIC_FILE, BWD_SRCS)},
         "forward_ms": f_ms,
         "backward_ms": b_ms,
     }

@@ -846,10 +846,14 @@ const Variant kVariants[] = {
     // forward passes that also write the backward tape
     SRWM_BOTH_IO_TAPE(8, 8, 1, 8, 1, 4, 1),
     SRWM_BOTH_IO_TAPE(16, 16, 1, 4, 1, 4, 1),
+    SRWM_BOTH_IO_TAPE(64, 64, 1, 4, 2, 4, 1),
     SRWM_BOTH_IO_TAPE(64, 64, 2, 8, 2, 4, 1),
+    SRWM_BOTH_IO_TAPE(64, 64, 4, 8, 1, 4, 1),
     SRWM_BOTH_IO_TAPE(8, 8, 1, 8, 1, 1, 1),
     SRWM_BOTH_IO_TAPE(16, 16, 1, 4, 1, 1, 1),
+    SRWM_BOTH_IO_TAPE(64, 64, 1, 4, 2, 1, 1),
     SRWM_BOTH_IO_TAPE(64, 64, 2, 8, 2, 1, 1),
+    SRWM_BOTH_IO_TAPE(64, 64, 4, 8, 1, 1, 1),
 };
 
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
