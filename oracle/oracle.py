@@ -63,6 +63,16 @@ def _load():
                           ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                           ctypes.c_long, ctypes.c_int]
             f.restype = ctypes.c_int
+            f = getattr(lib, prefix + "fast_step")
+            f.argtypes = [p, ctypes.c_int, ctypes.c_int, p, p, p, p, p, p]
+            f.restype = None
+            L = ctypes.c_long
+            f = getattr(lib, prefix + "deltanet_forward")
+            f.argtypes = [p, p, p, p, p, L, L, L, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+            f.restype = ctypes.c_int
+            f = getattr(lib, prefix + "srdeltanet_forward")
+            f.argtypes = [p, p, p, p, p, p, L, L, L] + [ctypes.c_int] * 6
+            f.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -158,3 +168,76 @@ def forward_f32(x, W0, apply_input_softmax=False, return_state=True, nthreads=No
     """The same definition evaluated in float32 (drift study only)."""
     return _forward("srwm_oracle_f32_", np.float32, ctypes.c_float, x, W0,
                     apply_input_softmax, return_state, nthreads, n_lr, reset_interval)
+
+
+# ---------------------------------------------------------------------------
+# DeltaNet / SR-DeltaNet (the C file states the definitions and their sources).
+def proj_rows(d_key: int, d_v: int) -> int:
+    """Rows of one head's projection [k; v; q; beta]: d_v + 2*d_key + 1."""
+    return d_v + 2 * d_key + 1
+
+
+def fast_step(F, p, d_key: int, d_v: int):
+    """One fast-matrix step.  Returns a dict with F (updated), y, kh, qh, g, vb."""
+    lib = _load()
+    F = np.array(F, dtype=np.float64, order="C", copy=True)
+    assert F.shape == (d_v, d_key)
+    p = np.ascontiguousarray(p, dtype=np.float64)
+    assert p.shape == (proj_rows(d_key, d_v),)
+    out = {k: np.empty(n) for k, n in (("y", d_v), ("kh", d_key), ("qh", d_key), ("g", 1), ("vb", d_v))}
+    d = ctypes.c_double
+    lib.srwm_oracle_fast_step(_ptr(F, d), d_key, d_v, _ptr(p, d),
+                              *[_ptr(out[k], d) for k in ("y", "kh", "qh", "g", "vb")])
+    out["F"] = F
+    return out
+
+
+def deltanet_forward(x, Wslow, d_key: int, d_v: int, F0=None, nthreads=None, f32=False):
+    """x[B,T,H,d_in], Wslow[H*P, H*d_in] -> (y[B,T,H,d_v], F_T[B,H,d_v,d_key]);
+    F0: None (zero) or [B,H,d_v,d_key].  f32=True evaluates the same definition
+    in float32 (drift study only)."""
+    lib = _load()
+    dt, d, fn = ((np.float32, ctypes.c_float, lib.srwm_oracle_f32_deltanet_forward) if f32 else
+                 (np.float64, ctypes.c_double, lib.srwm_oracle_deltanet_forward))
+    x = np.ascontiguousarray(x, dtype=dt)
+    B, T, H, d_in = x.shape
+    P = proj_rows(d_key, d_v)
+    Wslow = np.ascontiguousarray(Wslow, dtype=dt)
+    assert Wslow.shape == (H * P, H * d_in)
+    if F0 is not None:
+        F0 = np.ascontiguousarray(F0, dtype=dt)
+        assert F0.shape == (B, H, d_v, d_key)
+    y = np.empty((B, T, H, d_v), dtype=dt)
+    FT = np.empty((B, H, d_v, d_key), dtype=dt)
+    n = default_threads() if nthreads is None else int(nthreads)
+    rc = fn(_ptr(x, d), _ptr(Wslow, d), _ptr(F0, d), _ptr(y, d), _ptr(FT, d), B, T, H, d_in, d_key, d_v, n)
+    if rc != 0:
+        raise ValueError(f"oracle deltanet_forward rejected its arguments (code {rc})")
+    return y, FT
+
+
+def srdeltanet_forward(x, W0, d_key: int, d_v: int, F0=None, apply_input_softmax=False, n_lr=4,
+                       nthreads=None):
+    """x[B,T,H,d_in], SRWM W0[H,m,d_in] (m = P + 2*d_in + n_lr) ->
+    (y[B,T,H,d_v], W_T[B,H,m,d_in], F_T[B,H,d_v,d_key])."""
+    lib = _load()
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    B, T, H, d_in = x.shape
+    P = proj_rows(d_key, d_v)
+    W0 = np.ascontiguousarray(W0, dtype=np.float64)
+    m = P + 2 * d_in + n_lr
+    assert W0.shape == (H, m, d_in)
+    if F0 is not None:
+        F0 = np.ascontiguousarray(F0, dtype=np.float64)
+        assert F0.shape == (B, H, d_v, d_key)
+    y = np.empty((B, T, H, d_v))
+    WT = np.empty((B, H, m, d_in))
+    FT = np.empty((B, H, d_v, d_key))
+    n = default_threads() if nthreads is None else int(nthreads)
+    d = ctypes.c_double
+    rc = lib.srwm_oracle_srdeltanet_forward(_ptr(x, d), _ptr(W0, d), _ptr(F0, d), _ptr(y, d), _ptr(WT, d),
+                                            _ptr(FT, d), B, T, H, d_in, d_key, d_v, int(n_lr),
+                                            int(bool(apply_input_softmax)), n)
+    if rc != 0:
+        raise ValueError(f"oracle srdeltanet_forward rejected its arguments (code {rc})")
+    return y, WT, FT

@@ -52,6 +52,9 @@
  *     - reset_interval R > 0: at every step t > 0 with t % R == 0 the state
  *       returns to the initial matrix before the step is taken.
  *
+ * Also here: DeltaNet and SR-DeltaNet ([SRWM] Sec. 2.1 and Appendix C.1),
+ * stated with their readings at the end of the file.
+ *
  * softmax(s)_j = exp(s_j - max s) / sum_l exp(s_l - max s);
  * sigmoid(z)   = 1/(1+exp(-z)) for z >= 0, exp(z)/(1+exp(z)) otherwise.
  * Neither page fixes a temperature or scale; none is applied.
@@ -282,4 +285,171 @@ int FN(forward)(const real* x, const real* W0, real* y, real* W_T, long B,
     /* Threads that could not start: run their share here. */
     for (int i = started + 1; i < nthreads; ++i) run_job(&jobs[i]);
     return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * DeltaNet and SR-DeltaNet.
+ *
+ * DeltaNet ([SRWM] Sec. 2.1, the page's Eq. (1)-(4)): a slow matrix maps the
+ * input to a key, a value, a query and a rate logit; a separate fast matrix
+ * F (d_v x d_key per head, usually starting from zero) gets a delta write at
+ * the key and is then queried.  Per step, with the projection
+ * p = [k (d_key); v (d_v); q (d_key); beta (1)] (the order the page names
+ * them in):
+ *   kh = softmax(k), qh = softmax(q), g = sigmoid(beta)
+ *   vb = F kh                       what the key address holds now
+ *   F  = F + g (v - vb) kh^T        the delta write
+ *   y  = F qh                       the query reads the matrix AFTER the write
+ * (the page stresses that DeltaNet queries the updated matrix, while the
+ * SRWM's output comes from the matrix before its update).  The slow
+ * projection is full width: p for head h is rows [h*P, (h+1)*P) of
+ * Wslow[H*P][D] times the whole input x_t (D = H*d_in), P = d_v + 2*d_key + 1
+ * (the page contrasts DeltaNet's (D, D) key projection with the SRWM's
+ * per-head (H, d, d)).
+ *
+ * SR-DeltaNet ([SRWM] Appendix C.1): the slow projection is replaced by an
+ * SRWM (per head, d_out = P output rows, its own self-modification as
+ * above), and the fast matrix is kept: the SRWM's output y^SR_t, taken from
+ * its matrix before its update, is the projection p of the fast step.
+ * ------------------------------------------------------------------------ */
+
+/* One fast-matrix step.  F (d_v x d_key, row-major) is updated in place; y
+ * (d_v) receives the query after the write.  kh_out, qh_out (d_key), g_out
+ * (1) and vb_out (d_v) receive the step's intermediates when non-NULL. */
+void FN(fast_step)(real* F, int d_key, int d_v, const real* p, real* y,
+                   real* kh_out, real* qh_out, real* g_out, real* vb_out)
+{
+    real* buf = (real*)malloc(sizeof(real) * (size_t)(2 * d_key + d_v));
+    real* kh = buf;
+    real* qh = kh + d_key;
+    real* vb = qh + d_key;
+    const real* k = p;
+    const real* v = p + d_key;
+    const real* q = p + d_key + d_v;
+    softmax(k, d_key, kh);
+    softmax(q, d_key, qh);
+    const real g = sigmoid(p[2 * d_key + d_v]);
+    /* read at the key address */
+    for (int i = 0; i < d_v; ++i) {
+        real s = 0;
+        for (int j = 0; j < d_key; ++j) s += F[(size_t)i * d_key + j] * kh[j];
+        vb[i] = s;
+    }
+    /* delta write */
+    for (int i = 0; i < d_v; ++i) {
+        const real a = g * (v[i] - vb[i]);
+        for (int j = 0; j < d_key; ++j) F[(size_t)i * d_key + j] = F[(size_t)i * d_key + j] + a * kh[j];
+    }
+    /* query the updated matrix */
+    for (int i = 0; i < d_v; ++i) {
+        real s = 0;
+        for (int j = 0; j < d_key; ++j) s += F[(size_t)i * d_key + j] * qh[j];
+        y[i] = s;
+    }
+    if (kh_out) memcpy(kh_out, kh, sizeof(real) * (size_t)d_key);
+    if (qh_out) memcpy(qh_out, qh, sizeof(real) * (size_t)d_key);
+    if (g_out) g_out[0] = g;
+    if (vb_out) memcpy(vb_out, vb, sizeof(real) * (size_t)d_v);
+    free(buf);
+}
+
+typedef struct {
+    int kind; /* 0 DeltaNet, 1 SR-DeltaNet */
+    const real* x;
+    const real* Wp; /* DeltaNet: Wslow[H*P][D]; SR-DeltaNet: W0[H][m][d_in] */
+    const real* F0; /* NULL (zero) or [B][H][d_v][d_key] */
+    real* y;
+    real* W_T; /* SR-DeltaNet only, or NULL */
+    real* F_T;
+    long B, T, H;
+    int d_in, d_key, d_v, n_lr, flag;
+    long first, stride;
+} fjob_t;
+
+static void* run_fjob(void* pv)
+{
+    const fjob_t* jb = (const fjob_t*)pv;
+    const int P = jb->d_v + 2 * jb->d_key + 1;
+    const long D = jb->H * jb->d_in;
+    const size_t nf = (size_t)jb->d_v * jb->d_key;
+    const int m = P + 2 * jb->d_in + jb->n_lr;
+    real* F = (real*)malloc(sizeof(real) * nf);
+    real* p = (real*)malloc(sizeof(real) * (size_t)P);
+    real* W = jb->kind == 1 ? (real*)malloc(sizeof(real) * (size_t)m * jb->d_in) : NULL;
+    for (long u = jb->first; u < jb->B * jb->H; u += jb->stride) {
+        const long b = u / jb->H, h = u % jb->H;
+        if (jb->F0)
+            memcpy(F, jb->F0 + u * nf, sizeof(real) * nf);
+        else
+            memset(F, 0, sizeof(real) * nf);
+        if (W) memcpy(W, jb->Wp + h * (long)m * jb->d_in, sizeof(real) * (size_t)m * jb->d_in);
+        for (long t = 0; t < jb->T; ++t) {
+            const real* xt = jb->x + (b * jb->T + t) * D; /* x[b][t][:][:] */
+            if (jb->kind == 0) {
+                /* slow projection of the whole input onto head h's rows */
+                const real* ws = jb->Wp + h * (long)P * D;
+                for (int i = 0; i < P; ++i) {
+                    real s = 0;
+                    for (long j = 0; j < D; ++j) s += ws[i * D + j] * xt[j];
+                    p[i] = s;
+                }
+            } else {
+                /* the SRWM of head h produces the projection and modifies itself */
+                FN(step)(W, jb->d_in, P, jb->n_lr, xt + h * jb->d_in, jb->flag, p,
+                         NULL, NULL, NULL, NULL, NULL, NULL, NULL);
+            }
+            FN(fast_step)(F, jb->d_key, jb->d_v, p, jb->y + ((b * jb->T + t) * jb->H + h) * jb->d_v,
+                          NULL, NULL, NULL, NULL);
+        }
+        if (jb->F_T) memcpy(jb->F_T + u * nf, F, sizeof(real) * nf);
+        if (W && jb->W_T) memcpy(jb->W_T + u * (long)m * jb->d_in, W, sizeof(real) * (size_t)m * jb->d_in);
+    }
+    free(F);
+    free(p);
+    free(W);
+    return NULL;
+}
+
+static int run_fjobs(fjob_t base, int nthreads)
+{
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    pthread_t th[256];
+    fjob_t jobs[256];
+    for (int i = 0; i < nthreads; ++i) {
+        jobs[i] = base;
+        jobs[i].first = i;
+        jobs[i].stride = nthreads;
+    }
+    int started = 0;
+    for (int i = 1; i < nthreads; ++i) {
+        if (pthread_create(&th[i], NULL, run_fjob, &jobs[i]) != 0) break;
+        started = i;
+    }
+    run_fjob(&jobs[0]);
+    for (int i = 1; i <= started; ++i) pthread_join(th[i], NULL);
+    for (int i = started + 1; i < nthreads; ++i) run_fjob(&jobs[i]);
+    return 0;
+}
+
+/* DeltaNet forward: x[B][T][H][d_in], Wslow[H*P][H*d_in], F0 NULL or
+ * [B][H][d_v][d_key], y[B][T][H][d_v], F_T NULL or [B][H][d_v][d_key]. */
+int FN(deltanet_forward)(const real* x, const real* Wslow, const real* F0, real* y, real* F_T,
+                         long B, long T, long H, int d_in, int d_key, int d_v, int nthreads)
+{
+    if (B < 0 || T < 0 || H < 0 || d_in < 1 || d_key < 1 || d_v < 1) return -1;
+    fjob_t base = {0, x, Wslow, F0, y, NULL, F_T, B, T, H, d_in, d_key, d_v, 4, 0, 0, 1};
+    return run_fjobs(base, nthreads);
+}
+
+/* SR-DeltaNet forward: the SRWM W0[H][m][d_in], m = P + 2*d_in + n_lr,
+ * P = d_v + 2*d_key + 1; W_T NULL or [B][H][m][d_in]; the rest as DeltaNet. */
+int FN(srdeltanet_forward)(const real* x, const real* W0, const real* F0, real* y, real* W_T,
+                           real* F_T, long B, long T, long H, int d_in, int d_key, int d_v,
+                           int n_lr, int apply_input_softmax, int nthreads)
+{
+    if (B < 0 || T < 0 || H < 0 || d_in < 1 || d_key < 1 || d_v < 1) return -1;
+    if (n_lr != 1 && n_lr != 4) return -1;
+    fjob_t base = {1, x, W0, F0, y, W_T, F_T, B, T, H, d_in, d_key, d_v, n_lr, apply_input_softmax, 0, 1};
+    return run_fjobs(base, nthreads);
 }
