@@ -229,6 +229,65 @@ int64_t srwm_tape_row(int64_t d_in, int64_t d_out, int n_lr);
 /* 1 if srwm_backward has a kernel for (d_in, d_out, io_dtype, n_lr), else 0. */
 int srwm_backward_supported(int64_t d_in, int64_t d_out, int io_dtype, int n_lr);
 
+/*
+ * DeltaNet and SR-DeltaNet forward (review page Sec. 2.1 and Appendix C.1):
+ * fast-weight programmers with a separate fast matrix F (d_v x d_key per
+ * (sequence, head) unit).  Per step, with the projection
+ * p_t = [k (d_key); v (d_v); q (d_key); beta (1)], P = d_v + 2*d_key + 1:
+ *   kh = softmax(k), qh = softmax(q), g = sigmoid(beta)
+ *   F += g (v - F kh) kh^T;   y_t = F qh   (queried after the write)
+ * DeltaNet: p_t for head h = rows [h*P, (h+1)*P) of W_slow times the whole
+ * input x_t (all heads, D = H*d_in: a full-width slow projection).
+ * SR-DeltaNet: p_t is the output of an SRWM per head (d_out = P, its own
+ * self-modification, as srwm_forward_ex with that W0, n_lr and input flag).
+ *
+ * All buffers are float32 device pointers, 16-byte aligned, caller-owned:
+ *   x      [B][T][H][d_in]
+ *   W_slow [H*P][H*d_in]          (DeltaNet; H*d_in must be a multiple of 4)
+ *   W0     [H][m][d_in], m = P + 2*d_in + n_lr   (SR-DeltaNet's SRWM)
+ *   F0     [B][H][d_v][d_key] or NULL (the fast matrix starts at zero)
+ *   z      [B][T][H][P] (out): the projections of every step (work space the
+ *          caller provides; it holds p_t afterwards)
+ *   y      [B][T][H][d_v] (out)
+ *   W_T    [B][H][m][d_in] or NULL (out, SR-DeltaNet: the SRWM's final state)
+ *   F_T    [B][H][d_v][d_key] or NULL (out)
+ * Nothing is allocated; asynchronous on `stream`; SRWM_ERR_UNSUPPORTED when
+ * no kernel exists for (d_key, d_v) (srwm_fwp_supported) or, for SR-DeltaNet,
+ * for the SRWM shape (srwm_supported(d_in, P, SRWM_IO_F32, n_lr)); other
+ * errors as for srwm_forward (outputs overlapping any buffer: SRWM_ERR_ALIAS).
+ */
+typedef struct srwm_deltanet_args {
+    const float* x;
+    const float* W_slow;
+    const float* F0;
+    float* z;
+    float* y;
+    float* F_T;
+    int64_t B, T, H, d_in, d_key, d_v;
+    void* stream;
+} srwm_deltanet_args_t;
+
+int srwm_deltanet_forward(const srwm_deltanet_args_t* args);
+
+typedef struct srwm_srdeltanet_args {
+    const float* x;
+    const float* W0;
+    const float* F0;
+    float* z;
+    float* y;
+    float* W_T;
+    float* F_T;
+    int64_t B, T, H, d_in, d_key, d_v;
+    int n_lr;
+    int apply_input_softmax;
+    void* stream;
+} srwm_srdeltanet_args_t;
+
+int srwm_srdeltanet_forward(const srwm_srdeltanet_args_t* args);
+
+/* 1 if the fast-matrix kernel exists for (d_key, d_v), else 0. */
+int srwm_fwp_supported(int64_t d_key, int64_t d_v);
+
 /* 1 if a kernel exists for (d_in, d_out, io_dtype, n_lr), else 0. */
 int srwm_supported(int64_t d_in, int64_t d_out, int io_dtype, int n_lr);
 

@@ -12,7 +12,7 @@ from __future__ import annotations
 from . import _lib
 from .workloads import HEADLINE, WORKLOADS, Workload
 
-__all__ = ["forward", "backward", "srwm", "tape_row", "supported", "backward_supported", "variants", "select_variant", "m_rows", "WORKLOADS", "HEADLINE", "Workload"]
+__all__ = ["forward", "backward", "srwm", "tape_row", "deltanet_forward", "srdeltanet_forward", "fwp_supported", "supported", "backward_supported", "variants", "select_variant", "m_rows", "WORKLOADS", "HEADLINE", "Workload"]
 
 
 def m_rows(d_in: int, d_out: int, n_lr: int = 4) -> int:
@@ -227,3 +227,98 @@ def _autograd_function():
 def srwm(x, W0, apply_input_softmax: bool = False, n_lr: int = 4):
     """Differentiable forward: returns (y, W_T); gradients flow to x and W0."""
     return _autograd_function().apply(x, W0, apply_input_softmax, n_lr)
+
+
+def fwp_supported(d_key: int, d_v: int) -> bool:
+    """Whether the fast-matrix kernel of DeltaNet / SR-DeltaNet exists for (d_key, d_v)."""
+    return bool(_lib.load().srwm_fwp_supported(d_key, d_v))
+
+
+def _fwp_common(x, F0, d_key, d_v, return_state, z, y):
+    import torch
+
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
+        raise ValueError("x must be a torch tensor on a ROCm GPU")
+    if x.dtype != torch.float32 or x.dim() != 4 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float32 [B, T, H, d_in] tensor")
+    B, T, H, d_in = x.shape
+    P = d_v + 2 * d_key + 1
+    if F0 is not None and (tuple(F0.shape) != (B, H, d_v, d_key) or F0.dtype != torch.float32
+                           or F0.device != x.device or not F0.is_contiguous()):
+        raise ValueError("F0 must be a contiguous float32 [B, H, d_v, d_key] tensor on x's device")
+    if z is None:
+        z = torch.empty((B, T, H, P), dtype=torch.float32, device=x.device)
+    elif tuple(z.shape) != (B, T, H, P) or z.dtype != torch.float32 or not z.is_contiguous():
+        raise ValueError("z must be a contiguous float32 [B, T, H, P] tensor")
+    if y is None:
+        y = torch.empty((B, T, H, d_v), dtype=torch.float32, device=x.device)
+    elif tuple(y.shape) != (B, T, H, d_v) or y.dtype != torch.float32 or not y.is_contiguous():
+        raise ValueError("y must be a contiguous float32 [B, T, H, d_v] tensor")
+    F_T = torch.empty((B, H, d_v, d_key), dtype=torch.float32, device=x.device) if return_state else None
+    return B, T, H, d_in, P, z, y, F_T
+
+
+def _ptr(t):
+    return t.data_ptr() if t is not None and t.numel() else None
+
+
+def _stream_handle(x, stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def deltanet_forward(x, W_slow, d_key: int, d_v: int, F0=None, return_state: bool = False, z=None, y=None,
+                     stream=None):
+    """DeltaNet forward on the GPU (full-width slow projection, fast matrix
+    queried after its delta write).
+
+    x [B, T, H, d_in] float32; W_slow [H*P, H*d_in] float32 with
+    P = d_v + 2*d_key + 1 (head h's rows [h*P, (h+1)*P) give [k; v; q; beta]);
+    F0 [B, H, d_v, d_key] or None (zero).  Returns (y [B, T, H, d_v],
+    F_T [B, H, d_v, d_key] or None, z [B, T, H, P] the projections).
+    """
+    import torch
+
+    lib = _lib.load()
+    B, T, H, d_in, P, z, y, F_T = _fwp_common(x, F0, d_key, d_v, return_state, z, y)
+    if (tuple(W_slow.shape) != (H * P, H * d_in) or W_slow.dtype != torch.float32
+            or W_slow.device != x.device or not W_slow.is_contiguous()):
+        raise ValueError("W_slow must be a contiguous float32 [H*P, H*d_in] tensor on x's device")
+    a = _lib.DeltanetArgs(x=_ptr(x), W_slow=_ptr(W_slow), F0=_ptr(F0), z=_ptr(z), y=_ptr(y), F_T=_ptr(F_T),
+                          B=B, T=T, H=H, d_in=d_in, d_key=d_key, d_v=d_v, stream=_stream_handle(x, stream))
+    with torch.cuda.device(x.device):
+        rc = lib.srwm_deltanet_forward(a)
+    if rc != 0:
+        raise RuntimeError(_lib.strerror(rc))
+    return y, F_T, z
+
+
+def srdeltanet_forward(x, W0, d_key: int, d_v: int, F0=None, apply_input_softmax: bool = False,
+                       n_lr: int = 4, return_state: bool = False, z=None, y=None, stream=None):
+    """SR-DeltaNet forward on the GPU: a per-head SRWM (d_out = P) produces
+    each step's [k; v; q; beta] for a fast matrix queried after its write.
+
+    W0 [H, m, d_in] float32, m = P + 2*d_in + n_lr.  Returns (y, W_T (the
+    SRWM's final state [B, H, m, d_in]) or None, F_T or None, z).
+    """
+    import torch
+
+    lib = _lib.load()
+    B, T, H, d_in, P, z, y, F_T = _fwp_common(x, F0, d_key, d_v, return_state, z, y)
+    m = P + 2 * d_in + n_lr
+    if (tuple(W0.shape) != (H, m, d_in) or W0.dtype != torch.float32 or W0.device != x.device
+            or not W0.is_contiguous()):
+        raise ValueError(f"W0 must be a contiguous float32 [H, {m}, d_in] tensor on x's device")
+    W_T = torch.empty((B, H, m, d_in), dtype=torch.float32, device=x.device) if return_state else None
+    a = _lib.SrdeltanetArgs(x=_ptr(x), W0=_ptr(W0), F0=_ptr(F0), z=_ptr(z), y=_ptr(y), W_T=_ptr(W_T),
+                            F_T=_ptr(F_T), B=B, T=T, H=H, d_in=d_in, d_key=d_key, d_v=d_v, n_lr=int(n_lr),
+                            apply_input_softmax=int(bool(apply_input_softmax)),
+                            stream=_stream_handle(x, stream))
+    with torch.cuda.device(x.device):
+        rc = lib.srwm_srdeltanet_forward(a)
+    if rc != 0:
+        raise RuntimeError(_lib.strerror(rc))
+    return y, W_T, F_T, z

@@ -58,6 +58,47 @@ class BackwardArgs(ctypes.Structure):
     ]
 
 
+class DeltanetArgs(ctypes.Structure):
+    """srwm_deltanet_args_t."""
+    _fields_ = [
+        ("x", ctypes.c_void_p),
+        ("W_slow", ctypes.c_void_p),
+        ("F0", ctypes.c_void_p),
+        ("z", ctypes.c_void_p),
+        ("y", ctypes.c_void_p),
+        ("F_T", ctypes.c_void_p),
+        ("B", ctypes.c_int64),
+        ("T", ctypes.c_int64),
+        ("H", ctypes.c_int64),
+        ("d_in", ctypes.c_int64),
+        ("d_key", ctypes.c_int64),
+        ("d_v", ctypes.c_int64),
+        ("stream", ctypes.c_void_p),
+    ]
+
+
+class SrdeltanetArgs(ctypes.Structure):
+    """srwm_srdeltanet_args_t."""
+    _fields_ = [
+        ("x", ctypes.c_void_p),
+        ("W0", ctypes.c_void_p),
+        ("F0", ctypes.c_void_p),
+        ("z", ctypes.c_void_p),
+        ("y", ctypes.c_void_p),
+        ("W_T", ctypes.c_void_p),
+        ("F_T", ctypes.c_void_p),
+        ("B", ctypes.c_int64),
+        ("T", ctypes.c_int64),
+        ("H", ctypes.c_int64),
+        ("d_in", ctypes.c_int64),
+        ("d_key", ctypes.c_int64),
+        ("d_v", ctypes.c_int64),
+        ("n_lr", ctypes.c_int),
+        ("apply_input_softmax", ctypes.c_int),
+        ("stream", ctypes.c_void_p),
+    ]
+
+
 class VariantInfo(ctypes.Structure):
     """srwm_variant_info_t."""
     _fields_ = [(name, ctypes.c_int) for name in (
@@ -92,6 +133,12 @@ def load() -> ctypes.CDLL:
     lib.srwm_tape_row.restype = i64
     lib.srwm_backward_supported.argtypes = [i64, i64, ci, ci]
     lib.srwm_backward_supported.restype = ci
+    lib.srwm_deltanet_forward.argtypes = [ctypes.POINTER(DeltanetArgs)]
+    lib.srwm_deltanet_forward.restype = ci
+    lib.srwm_srdeltanet_forward.argtypes = [ctypes.POINTER(SrdeltanetArgs)]
+    lib.srwm_srdeltanet_forward.restype = ci
+    lib.srwm_fwp_supported.argtypes = [i64, i64]
+    lib.srwm_fwp_supported.restype = ci
     lib.srwm_variant_count.argtypes = []
     lib.srwm_variant_count.restype = ci
     lib.srwm_variant_info.argtypes = [ci, ctypes.POINTER(VariantInfo)]

@@ -843,6 +843,15 @@ const Variant kVariants[] = {
     SRWM_BOTH_IO_FUSED(64, 64, 8, 8, 1, 1, 1),
     SRWM_BOTH_IO_FUSED(128, 128, 8, 8, 1, 1, 1),
     SRWM_BOTH_IO_RESET(128, 128, 8, 8, 1, 1, 1),
+    // SR-DeltaNet's projection: d_out = d_v + 2*d_key + 1 (float32 I/O)
+    make_variant<8, 25, 1, 8, 1, 4, 1, false>(1),
+    make_variant<8, 25, 1, 8, 1, 1, 1, false>(1),
+    make_variant<16, 49, 1, 4, 1, 4, 1, false>(1),
+    make_variant<16, 49, 1, 4, 1, 1, 1, false>(1),
+    make_variant<64, 193, 4, 8, 1, 4, 1, false>(1),
+    make_variant<64, 193, 4, 8, 1, 1, 1, false>(1),
+    make_variant<64, 193, 8, 8, 1, 4, 2, false>(1),
+    make_variant<64, 193, 8, 8, 1, 1, 2, false>(1),
     // forward passes that also write the backward tape
     SRWM_BOTH_IO_TAPE(8, 8, 1, 8, 1, 4, 1),
     SRWM_BOTH_IO_TAPE(16, 16, 1, 4, 1, 4, 1),

@@ -1,0 +1,418 @@
+// srwm_fwp.hip -- gfx950 kernels and C ABI of the fast-weight programmers the
+// SRWM is compared with and built into: DeltaNet and SR-DeltaNet.
+//
+// DeltaNet (review page "SRWM: 让权重矩阵学习修改自身", Sec. 2.1): a slow
+// matrix maps the input x_t to [k; v; q; beta] (in the order the page names
+// them), and a separate fast matrix F (d_v x d_key per head, zero at the start
+// unless a state is carried in) gets a delta write at the key and is then
+// queried:
+//     kh = softmax(k), qh = softmax(q), g = sigmoid(beta)
+//     vb = F kh;   F += g (v - vb) kh^T;   y_t = F qh    (F after the write)
+// The slow projection is full width: head h's rows of W_slow[H*P][H*d_in]
+// read the whole x_t (the page contrasts DeltaNet's (D, D) projection with
+// the SRWM's per-head one).  P = d_v + 2*d_key + 1.
+//
+// SR-DeltaNet (same page, Appendix C.1): an SRWM (per head, d_out = P)
+// replaces the slow projection; its output y^SR_t, which it takes from its
+// matrix before its own update, is the fast step's projection.
+//
+// Layout of the work:
+//   * The projection of every step is independent of F, so it is computed
+//     for all (b, t) first: for DeltaNet one dense GEMM, Z = X W_slow^T, on
+//     the fp32 matrix cores (v_mfma_f32_16x16x4_f32); for SR-DeltaNet the SRWM
+//     kernel of srwm_fwd.hip with y = Z.  Z[B][T][H][P] is a caller-provided
+//     float32 buffer.
+//   * The fast-matrix recurrence: one wave per (b, h) unit, F in registers
+//     (lane (rg, p) holds rows rg + G*r and columns [p*L, p*L + L)).  The
+//     softmaxes of step t+1 depend only on Z, so they are formed while step
+//     t's matrix work runs and handed over through a double-buffered LDS
+//     slice; the serial chain per step is two row reductions and the write.
+//     y_t = F_{t-1} qh + a (kh . qh) with a = g (v - vb): the query of the
+//     written matrix without a second pass over it.
+#include <hip/hip_runtime.h>
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "srwm.h"
+#include "srwm_device.h"
+
+namespace {
+
+using namespace srwm;
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// ----------------------------------------------------------------------------
+// Z[n][c] = sum_k X[n][k] W[c][k]: n < N (= B*T rows of x), c < C (= H*P),
+// k < K (= H*d_in, K % 4 == 0).  Workgroup tile 64 x 64, four waves of 32 x 32
+// (2 x 2 MFMA tiles of 16 x 16), K staged through LDS 32 at a time.
+// MFMA 16x16x4 f32 operand layout: lane l supplies A[l % 16][l / 16] and
+// B[l / 16][l % 16]; accumulator register r of lane l is D[4 (l / 16) + r][l % 16].
+constexpr int kGM = 64, kGN = 64, kGK = 32, kGPad = 4;
+
+__global__ __launch_bounds__(256) void srwm_proj_gemm_kernel(const float* __restrict__ X,
+                                                             const float* __restrict__ W,
+                                                             float* __restrict__ Z, int64_t N, int C,
+                                                             int K)
+{
+    __shared__ __attribute__((aligned(16))) float sX[kGM][kGK + kGPad];
+    __shared__ __attribute__((aligned(16))) float sW[kGN][kGK + kGPad];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int64_t n0 = (int64_t)blockIdx.x * kGM;
+    const int c0 = blockIdx.y * kGN;
+    const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
+    const int lr = tid >> 3, lc = (tid & 7) * 4;  // loader: rows lr, lr + 32; columns lc..lc+3
+
+    v4f acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    for (int k0 = 0; k0 < K; k0 += kGK) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = lr + 32 * i;
+            const int gk = k0 + lc;
+            float4 vx = make_float4(0.f, 0.f, 0.f, 0.f), vw = vx;
+            if (n0 + r < N && gk < K) vx = *reinterpret_cast<const float4*>(X + (n0 + r) * K + gk);
+            if (c0 + r < C && gk < K) vw = *reinterpret_cast<const float4*>(W + (int64_t)(c0 + r) * K + gk);
+            *reinterpret_cast<float4*>(&sX[r][lc]) = vx;
+            *reinterpret_cast<float4*>(&sW[r][lc]) = vw;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < kGK; kk += 4) {
+            const int kr = kk + (lane >> 4);
+            const float a0 = sX[wm + (lane & 15)][kr];
+            const float a1 = sX[wm + 16 + (lane & 15)][kr];
+            const float b0 = sW[wn + (lane & 15)][kr];
+            const float b1 = sW[wn + 16 + (lane & 15)][kr];
+            acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc[0][0], 0, 0, 0);
+            acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, acc[0][1], 0, 0, 0);
+            acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b0, acc[1][0], 0, 0, 0);
+            acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc[1][1], 0, 0, 0);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int col = c0 + wn + 16 * j + (lane & 15);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t row = n0 + wm + 16 * i + 4 * (lane >> 4) + r;
+                if (row < N && col < C) Z[row * C + col] = acc[i][j][r];
+            }
+        }
+}
+
+// ----------------------------------------------------------------------------
+// The fast-matrix recurrence.  One wave per unit; Z[b][t][h][0..PR) holds the
+// projection [k; v; q; beta] of step t.
+template <int D_KEY, int D_V, int P>
+__global__ __launch_bounds__(64) void srwm_fast_kernel(const float* __restrict__ Z,
+                                                       const float* __restrict__ F0,
+                                                       float* __restrict__ y, float* __restrict__ FT,
+                                                       int T, int H)
+{
+    constexpr int PR = D_V + 2 * D_KEY + 1;
+    constexpr int L = D_KEY / P;
+    constexpr int G = kWave / P;
+    constexpr int R = (D_V + G - 1) / G;
+    constexpr int EZ = (PR + kWave - 1) / kWave;
+    constexpr int V0 = D_KEY, Q0 = D_KEY + D_V, BETA = PR - 1;
+    static_assert(D_KEY % P == 0, "P must divide d_key");
+
+    __shared__ __attribute__((aligned(16))) float s_kh[2][D_KEY];
+    __shared__ __attribute__((aligned(16))) float s_qh[2][D_KEY];
+    __shared__ __attribute__((aligned(16))) float s_v[2][R * G];
+    __shared__ float s_g[2];
+
+    const int lane = threadIdx.x;
+    const int p = lane % P;
+    const int rg = lane / P;
+    const int unit = blockIdx.x;
+    const int b = unit / H;
+    const int h = unit - b * H;
+    const int64_t z_step = (int64_t)H * PR;
+    const int64_t z0 = ((int64_t)b * T * H + h) * PR;
+    const int64_t y_step = (int64_t)H * D_V;
+    const int64_t y0 = ((int64_t)b * T * H + h) * D_V;
+
+    float F[R][L];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int row = rg + G * r;
+        if (F0 != nullptr && row < D_V) {
+            load_f32<L>(F0 + ((int64_t)unit * D_V + row) * D_KEY + p * L, F[r]);
+        } else {
+#pragma unroll
+            for (int c = 0; c < L; ++c) F[r][c] = 0.f;
+        }
+    }
+
+    auto load_z = [&](int t, float (&zr)[EZ]) {
+#pragma unroll
+        for (int i = 0; i < EZ; ++i) {
+            const int e = lane + kWave * i;
+            zr[i] = (t < T && e < PR) ? Z[z0 + (int64_t)t * z_step + e] : 0.f;
+        }
+    };
+    // The softmaxes and the gate of one step, into LDS slice `buf`.
+    auto prep = [&](const float (&zr)[EZ], int buf) {
+        float mk = -INFINITY, mq = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < EZ; ++i) {
+            const int e = lane + kWave * i;
+            if (e < V0) mk = fmax2(mk, zr[i]);
+            else if (e >= Q0 && e < BETA) mq = fmax2(mq, zr[i]);
+        }
+        mk = wave_max(mk);
+        mq = wave_max(mq);
+        float ex[EZ];
+        float sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int i = 0; i < EZ; ++i) {
+            const int e = lane + kWave * i;
+            const bool isk = e < V0, isq = e >= Q0 && e < BETA;
+            ex[i] = isk ? exp_f32(zr[i] - mk) : isq ? exp_f32(zr[i] - mq) : 0.f;
+            if (isk) sk += ex[i];
+            if (isq) sq += ex[i];
+        }
+        const float ik = rcp_f32(wave_sum(sk)), iq = rcp_f32(wave_sum(sq));
+#pragma unroll
+        for (int i = 0; i < EZ; ++i) {
+            const int e = lane + kWave * i;
+            if (e < V0) s_kh[buf][e] = ex[i] * ik;
+            else if (e < Q0) s_v[buf][e - V0] = zr[i];
+            else if (e < BETA) s_qh[buf][e - Q0] = ex[i] * iq;
+            else if (e == BETA) s_g[buf] = sigmoid_f32(zr[i]);
+        }
+        if constexpr (R * G > D_V) {
+            // padding rows read value 0 (their F rows are 0 and stay 0)
+            for (int e = D_V + lane; e < R * G; e += kWave) s_v[buf][e] = 0.f;
+        }
+    };
+
+    float zn[EZ];
+    if (T > 0) {
+        float zf[EZ];
+        load_z(0, zf);
+        prep(zf, 0);
+        load_z(1, zn);
+        wave_sync();
+    }
+    for (int t = 0; t < T; ++t) {
+        const int buf = t & 1;
+        if (t + 1 < T) {
+            prep(zn, buf ^ 1);
+            load_z(t + 2, zn);
+        }
+        float kh[L], qh[L];
+        load_f32<L>(&s_kh[buf][p * L], kh);
+        load_f32<L>(&s_qh[buf][p * L], qh);
+        const float g = s_g[buf];
+        float kq = 0.f;
+#pragma unroll
+        for (int c = 0; c < L; ++c) kq = fmaf(kh[c], qh[c], kq);
+        kq = group_sum<P>(kq);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = rg + G * r;
+            float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+            for (int c = 0; c < L; ++c) {
+                s1 = fmaf(F[r][c], kh[c], s1);
+                s2 = fmaf(F[r][c], qh[c], s2);
+            }
+            s1 = group_sum<P>(s1);  // vb: the key address's content
+            s2 = group_sum<P>(s2);  // F_{t-1} qh
+            const float a = g * (s_v[buf][row] - s1);
+#pragma unroll
+            for (int c = 0; c < L; ++c) F[r][c] = fmaf(a, kh[c], F[r][c]);
+            if (p == 0 && row < D_V) y[y0 + (int64_t)t * y_step + row] = fmaf(a, kq, s2);
+        }
+        wave_sync();
+    }
+
+    if (FT != nullptr) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = rg + G * r;
+            if (row < D_V) store_f32<L>(FT + ((int64_t)unit * D_V + row) * D_KEY + p * L, F[r]);
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Variants: (d_key, d_v, lanes per row).
+using FastFn = void (*)(const float*, const float*, float*, float*, int, int);
+struct FastVariant {
+    int d_key, d_v;
+    FastFn fn;
+};
+const FastVariant kFastVariants[] = {
+    {8, 8, &srwm_fast_kernel<8, 8, 8>},
+    {16, 16, &srwm_fast_kernel<16, 16, 4>},
+    {64, 64, &srwm_fast_kernel<64, 64, 4>},
+};
+constexpr int kNumFastVariants = sizeof(kFastVariants) / sizeof(kFastVariants[0]);
+
+int find_fast(int64_t d_key, int64_t d_v)
+{
+    for (int i = 0; i < kNumFastVariants; ++i)
+        if (kFastVariants[i].d_key == d_key && kFastVariants[i].d_v == d_v) return i;
+    return -1;
+}
+
+// Byte sizes shared by both entry points: x, z, y and one fast state per unit.
+struct FwpSizes {
+    int64_t units, steps, nx, nz, ny, nf;
+};
+
+int fwp_sizes(int64_t B, int64_t T, int64_t H, int64_t d_in, int64_t d_key, int64_t d_v, FwpSizes* s)
+{
+    if (B < 0 || T < 0 || H < 0 || d_in < 1 || d_key < 1 || d_v < 1) return SRWM_ERR_SHAPE;
+    const int64_t P = d_v + 2 * d_key + 1;
+    if (!mul_ok(B, H, &s->units) || !mul_ok(s->units, T, &s->steps) || !mul_ok(s->steps, d_in * 4, &s->nx) ||
+        !mul_ok(s->steps, P * 4, &s->nz) || !mul_ok(s->steps, d_v * 4, &s->ny) ||
+        !mul_ok(s->units, d_v * d_key * 4, &s->nf))
+        return SRWM_ERR_SHAPE;
+    if (s->units > INT32_MAX || T > INT32_MAX || H > INT32_MAX) return SRWM_ERR_SHAPE;
+    return SRWM_OK;
+}
+
+int launch_fast(int vi, const float* z, const float* F0, float* y, float* FT, int64_t units, int64_t T,
+                int64_t H, void* stream)
+{
+    int Ti = static_cast<int>(T), Hi = static_cast<int>(H);
+    void* args[] = {const_cast<float**>(&z), const_cast<float**>(&F0), &y, &FT, &Ti, &Hi};
+    const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(kFastVariants[vi].fn),
+                                           dim3(static_cast<unsigned>(units)), dim3(kWave), args, 0,
+                                           static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? SRWM_OK : SRWM_ERR_HIP;
+}
+
+int deltanet_impl(const srwm_deltanet_args_t* a)
+{
+    if (a == nullptr) return SRWM_ERR_NULL;
+    FwpSizes s;
+    int rc = fwp_sizes(a->B, a->T, a->H, a->d_in, a->d_key, a->d_v, &s);
+    if (rc != SRWM_OK) return rc;
+    const int vi = find_fast(a->d_key, a->d_v);
+    if (vi < 0) return SRWM_ERR_UNSUPPORTED;
+    const int64_t P = a->d_v + 2 * a->d_key + 1;
+    int64_t K, C, nw;
+    if (!mul_ok(a->H, a->d_in, &K) || !mul_ok(a->H, P, &C) || !mul_ok(C, K * 4, &nw)) return SRWM_ERR_SHAPE;
+    if (K % 4 != 0) return SRWM_ERR_SHAPE;  // 16-byte rows of x and W_slow
+    if (K > INT32_MAX || C > INT32_MAX) return SRWM_ERR_SHAPE;
+    if (s.units == 0) return SRWM_OK;
+    if (s.nx > 0 && (a->x == nullptr || a->W_slow == nullptr || a->z == nullptr || a->y == nullptr))
+        return SRWM_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(a->x) | reinterpret_cast<uintptr_t>(a->W_slow) |
+         reinterpret_cast<uintptr_t>(a->F0) | reinterpret_cast<uintptr_t>(a->z) |
+         reinterpret_cast<uintptr_t>(a->y) | reinterpret_cast<uintptr_t>(a->F_T)) & 15u)
+        return SRWM_ERR_ARG;
+    const void* ins[] = {a->x, a->W_slow, a->F0};
+    const int64_t nins[] = {s.nx, nw, a->F0 ? s.nf : 0};
+    void* outs[] = {a->z, a->y, a->F_T};
+    const int64_t nouts[] = {s.nz, s.ny, a->F_T ? s.nf : 0};
+    for (int o = 0; o < 3; ++o) {
+        for (int i = 0; i < 3; ++i)
+            if (ranges_overlap(outs[o], nouts[o], ins[i], nins[i])) return SRWM_ERR_ALIAS;
+        for (int o2 = o + 1; o2 < 3; ++o2)
+            if (ranges_overlap(outs[o], nouts[o], outs[o2], nouts[o2])) return SRWM_ERR_ALIAS;
+    }
+    const hipStream_t st = static_cast<hipStream_t>(a->stream);
+    const int64_t N = a->B * a->T;
+    if (N > 0) {
+        const float* X = static_cast<const float*>(a->x);
+        const float* Wp = a->W_slow;
+        float* Zp = a->z;
+        int Ci = static_cast<int>(C), Ki = static_cast<int>(K);
+        int64_t Nv = N;
+        void* args[] = {const_cast<float**>(&X), const_cast<float**>(&Wp), &Zp, &Nv, &Ci, &Ki};
+        const int64_t gx = (N + kGM - 1) / kGM;
+        if (gx > INT32_MAX) return SRWM_ERR_SHAPE;
+        const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(&srwm_proj_gemm_kernel),
+                                               dim3(static_cast<unsigned>(gx), static_cast<unsigned>((C + kGN - 1) / kGN)),
+                                               dim3(256), args, 0, st);
+        if (err != hipSuccess) return SRWM_ERR_HIP;
+    }
+    return launch_fast(vi, a->z, a->F0, a->y, a->F_T, s.units, a->T, a->H, a->stream);
+}
+
+int srdeltanet_impl(const srwm_srdeltanet_args_t* a)
+{
+    if (a == nullptr) return SRWM_ERR_NULL;
+    FwpSizes s;
+    int rc = fwp_sizes(a->B, a->T, a->H, a->d_in, a->d_key, a->d_v, &s);
+    if (rc != SRWM_OK) return rc;
+    const int vi = find_fast(a->d_key, a->d_v);
+    if (vi < 0) return SRWM_ERR_UNSUPPORTED;
+    const int64_t P = a->d_v + 2 * a->d_key + 1;
+    if (a->n_lr != 1 && a->n_lr != 4) return SRWM_ERR_ARG;
+    const int64_t m = P + 2 * a->d_in + a->n_lr;
+    int64_t nst, nw0;
+    if (!mul_ok(s.units, m * a->d_in * 4, &nst) || !mul_ok(a->H, m * a->d_in * 4, &nw0)) return SRWM_ERR_SHAPE;
+    if (srwm_supported(a->d_in, P, SRWM_IO_F32, a->n_lr) != 1) return SRWM_ERR_UNSUPPORTED;
+    if (s.units == 0) return SRWM_OK;
+    if ((reinterpret_cast<uintptr_t>(a->F0) | reinterpret_cast<uintptr_t>(a->y) |
+         reinterpret_cast<uintptr_t>(a->F_T)) & 15u)
+        return SRWM_ERR_ARG;
+    if (s.ny > 0 && a->y == nullptr) return SRWM_ERR_NULL;
+    // the fast memory's buffers against everything else
+    const void* others[] = {a->x, a->W0, a->z, a->W_T};
+    const int64_t nothers[] = {s.nx, nw0, s.nz, a->W_T ? nst : 0};
+    void* outs[] = {a->y, a->F_T};
+    const int64_t nouts[] = {s.ny, a->F_T ? s.nf : 0};
+    for (int o = 0; o < 2; ++o) {
+        for (int i = 0; i < 4; ++i)
+            if (ranges_overlap(outs[o], nouts[o], others[i], nothers[i])) return SRWM_ERR_ALIAS;
+        if (ranges_overlap(outs[o], nouts[o], a->F0, a->F0 ? s.nf : 0)) return SRWM_ERR_ALIAS;
+    }
+    if (ranges_overlap(a->y, s.ny, a->F_T, a->F_T ? s.nf : 0)) return SRWM_ERR_ALIAS;
+    // the projection: the SRWM with d_out = P writes its outputs into z
+    srwm_forward_args_t f;
+    f.x = a->x;
+    f.W0 = a->W0;
+    f.y = a->z;
+    f.W_T = a->W_T;
+    f.B = a->B;
+    f.T = a->T;
+    f.H = a->H;
+    f.d_in = a->d_in;
+    f.d_out = P;
+    f.m = m;
+    f.io_dtype = SRWM_IO_F32;
+    f.apply_input_softmax = a->apply_input_softmax;
+    f.n_lr = a->n_lr;
+    f.w0_per_sequence = 0;
+    f.reset_interval = 0;
+    f.variant = -1;
+    f.stream = a->stream;
+    f.tape = nullptr;
+    rc = srwm_forward_ex(&f);
+    if (rc != SRWM_OK) return rc;
+    if (a->T == 0) {
+        if (a->F_T == nullptr) return SRWM_OK;
+    }
+    return launch_fast(vi, a->z, a->F0, a->y, a->F_T, s.units, a->T, a->H, a->stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int srwm_deltanet_forward(const srwm_deltanet_args_t* args) { return deltanet_impl(args); }
+
+int srwm_srdeltanet_forward(const srwm_srdeltanet_args_t* args) { return srdeltanet_impl(args); }
+
+int srwm_fwp_supported(int64_t d_key, int64_t d_v) { return find_fast(d_key, d_v) >= 0 ? 1 : 0; }
+
+}  // extern "C"

@@ -133,3 +133,73 @@ def gen_gW(w: Workload, batch=None) -> np.ndarray:
     for i, b in enumerate(bs):
         out[i] = np.random.default_rng([w.seed, 4, b]).standard_normal((w.H, w.m, w.d_in), dtype=np.float32)
     return out
+
+
+# ---------------------------------------------------------------------------
+# DeltaNet / SR-DeltaNet workloads (review page Sec. 2.1 and Appendix C.1).
+# The pages' RL models use a hidden width of 128 (two heads of 64 here); the
+# input recipe is the one above (x per sequence from default_rng([seed, 1, b])),
+# DeltaNet's slow projection W_slow[H*P][H*d_in] from default_rng([seed, 5]),
+# SR-DeltaNet's SRWM W0[H][m][d_in] from default_rng([seed, 2]); the fast
+# matrix starts at zero.
+@dataclass(frozen=True)
+class FwpWorkload:
+    name: str
+    kind: str                # "deltanet" or "srdeltanet"
+    B: int
+    H: int
+    d_in: int
+    d_key: int
+    d_v: int
+    T: int
+    apply_input_softmax: bool
+    w0_std: float
+    seed: int = 0
+    n_lr: int = 4
+    io_dtype: str = "f32"
+
+    @property
+    def P(self) -> int:
+        """Rows of one head's projection [k; v; q; beta]."""
+        return self.d_v + 2 * self.d_key + 1
+
+    @property
+    def m(self) -> int:
+        """Rows of SR-DeltaNet's SRWM (d_out = P)."""
+        return self.P + 2 * self.d_in + self.n_lr
+
+    @property
+    def units(self) -> int:
+        return self.B * self.H
+
+    @property
+    def head_steps(self) -> int:
+        return self.B * self.H * self.T
+
+    @property
+    def flop_per_head_step(self) -> int:
+        """Projection (DeltaNet: 2*P*H*d_in, the full-width product; SR-DeltaNet:
+        the SRWM's 8*m*d_in) plus the fast matrix's read, write and query
+        (6*d_v*d_key)."""
+        proj = 2 * self.P * self.H * self.d_in if self.kind == "deltanet" else 8 * self.m * self.d_in
+        return proj + 6 * self.d_v * self.d_key
+
+    def with_(self, **kw) -> "FwpWorkload":
+        return replace(self, **kw)
+
+
+FWP_WORKLOADS = {
+    "deltanet_small": FwpWorkload("deltanet_small", "deltanet", B=3, H=2, d_in=16, d_key=16, d_v=16, T=75,
+                                  apply_input_softmax=False, w0_std=32 ** -0.5),
+    "deltanet_rl": FwpWorkload("deltanet_rl", "deltanet", B=128, H=2, d_in=64, d_key=64, d_v=64, T=4096,
+                               apply_input_softmax=False, w0_std=128 ** -0.5),
+    "srdeltanet_small": FwpWorkload("srdeltanet_small", "srdeltanet", B=3, H=2, d_in=16, d_key=16, d_v=16,
+                                    T=75, apply_input_softmax=True, w0_std=16 ** -0.5),
+    "srdeltanet_rl": FwpWorkload("srdeltanet_rl", "srdeltanet", B=128, H=2, d_in=64, d_key=64, d_v=64,
+                                 T=4096, apply_input_softmax=True, w0_std=64 ** -0.5),
+}
+
+
+def gen_W_slow(w: FwpWorkload) -> np.ndarray:
+    rng = np.random.default_rng([w.seed, 5])
+    return (rng.standard_normal((w.H * w.P, w.H * w.d_in)) * w.w0_std).astype(np.float32)

@@ -246,3 +246,71 @@ def test_backward_null_and_empty():
     assert lib.srwm_backward(None) == E_NULL
     assert call_bwd(B=0, x=None, W_T=None, tape=None, gy=None, dx=None, dW_init=None, dW0=None) == OK
     assert call_bwd(H=0, x=None, W_T=None, tape=None, gy=None, dx=None, dW_init=None, dW0=None) == OK
+
+
+# ---------------------------------------------------------------------------
+# DeltaNet / SR-DeltaNet entry points.
+FAKE_Z = 0xA0000000
+
+
+def call_dn(**kw):
+    base = dict(x=FAKE_X, W_slow=FAKE_W0, F0=None, z=FAKE_Z, y=FAKE_Y, F_T=None, B=2, T=3, H=2, d_in=16,
+                d_key=16, d_v=16, stream=None)
+    base.update(kw)
+    return _lib.load().srwm_deltanet_forward(ctypes.byref(_lib.DeltanetArgs(**base)))
+
+
+def call_sdn(**kw):
+    base = dict(x=FAKE_X, W0=FAKE_W0, F0=None, z=FAKE_Z, y=FAKE_Y, W_T=None, F_T=None, B=2, T=3, H=2, d_in=16,
+                d_key=16, d_v=16, n_lr=4, apply_input_softmax=0, stream=None)
+    base.update(kw)
+    return _lib.load().srwm_srdeltanet_forward(ctypes.byref(_lib.SrdeltanetArgs(**base)))
+
+
+def test_fwp_supported():
+    lib = _lib.load()
+    for d in (8, 16, 64):
+        assert lib.srwm_fwp_supported(d, d) == 1
+        P = 3 * d + 1
+        for n_lr in (4, 1):
+            assert lib.srwm_supported(d, P, 0, n_lr) == 1, (d, P, n_lr)
+    assert lib.srwm_fwp_supported(7, 7) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d_key=7, d_v=7), E_UNSUP),
+    (dict(H=1, d_in=3), E_SHAPE),            # H*d_in not a multiple of 4
+    (dict(B=-1), E_SHAPE),
+    (dict(d_v=0), E_SHAPE),
+    (dict(x=None), E_NULL),
+    (dict(W_slow=None), E_NULL),
+    (dict(z=None), E_NULL),
+    (dict(y=None), E_NULL),
+    (dict(y=FAKE_Y + 4), E_ARG),
+    (dict(z=FAKE_X + 16), E_ALIAS),
+    (dict(y=FAKE_Z + 64), E_ALIAS),
+    (dict(F_T=FAKE_Y), E_ALIAS),
+])
+def test_deltanet_validation(kw, code):
+    assert call_dn(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_lr=2), E_ARG),
+    (dict(d_in=8, d_key=16, d_v=16), E_UNSUP),   # no SRWM kernel for d_out = 49 with d_in = 8
+    (dict(d_key=7, d_v=7), E_UNSUP),
+    (dict(y=FAKE_Y + 4), E_ARG),
+    (dict(y=FAKE_Z + 64), E_ALIAS),
+    (dict(F_T=FAKE_W0 + 16), E_ALIAS),
+    (dict(y=None), E_NULL),
+])
+def test_srdeltanet_validation(kw, code):
+    assert call_sdn(**kw) == code
+
+
+def test_fwp_empty_problems_are_noops():
+    lib = _lib.load()
+    assert lib.srwm_deltanet_forward(None) == E_NULL
+    assert lib.srwm_srdeltanet_forward(None) == E_NULL
+    assert call_dn(B=0, x=None, z=None, y=None) == OK
+    assert call_sdn(H=0, x=None, z=None, y=None, W0=None) == OK
