@@ -181,6 +181,9 @@ def main() -> int:
     from self_referential_weight_amd.workloads import HEADLINE, WORKLOADS, gen_W0, gen_x
 
     name = args.workload or HEADLINE
+    from self_referential_weight_amd.workloads import FWP_WORKLOADS
+    if name in FWP_WORKLOADS:
+        return bench_fwp(args, FWP_WORKLOADS[name])
     w = WORKLOADS[name]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -335,6 +338,122 @@ def bench_backward(args, w, name, x, x_host, W0, W0_host, dev) -> int:
     if not args.no_cpu:
         log("[bench] timing the float64 gradient oracle on a bounded sample")
         rec["cpu_baseline"] = cpu_baseline_backward(w, x_host, W0_host, gy_host, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def bench_fwp(args, w) -> int:
+    """DeltaNet / SR-DeltaNet: a step is the projection of every (b, t) (the
+    MFMA GEMM, or the SRWM kernel for SR-DeltaNet) followed by the fast-matrix
+    recurrence, each launch bracketed by HIP events."""
+    import numpy as np
+    import torch
+
+    import self_referential_weight_amd as srwm
+    from self_referential_weight_amd.workloads import gen_W0, gen_W_slow, gen_x
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] generating {w.name}: {w.kind} B={w.B} H={w.H} d_in={w.d_in} d_key={w.d_key} d_v={w.d_v} T={w.T}")
+    x_host = gen_x(w)
+    x = torch.from_numpy(x_host).to(dev)
+    P = w.P
+    z = torch.empty((w.B, w.T, w.H, P), dtype=torch.float32, device=dev)
+    y = torch.empty((w.B, w.T, w.H, w.d_v), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    if w.kind == "deltanet":
+        Wp_host = gen_W_slow(w)
+        Wp = torch.from_numpy(Wp_host).to(dev)
+
+        def project():
+            srwm.deltanet_project(x, Wp, w.d_key, w.d_v, z=z, stream=stream)
+        proj_name = "srwm_proj_gemm_kernel"
+        proj_flop = 2 * P * w.H * w.d_in * w.head_steps
+        proj_bound, proj_unit = "mfma", "TFLOP/s"
+    else:
+        Wp_host = gen_W0(w)
+        Wp = torch.from_numpy(Wp_host).to(dev)
+
+        def project():
+            srwm.forward(x, Wp, apply_input_softmax=w.apply_input_softmax, n_lr=w.n_lr, y=z, stream=stream)
+        proj_name = "srwm_fwd_kernel (SRWM, d_out = P)"
+        proj_flop = 8 * w.m * w.d_in * w.head_steps
+        proj_bound, proj_unit = "alu", "TFLOP/s"
+
+    def fast():
+        srwm.fast_forward(z, w.d_key, w.d_v, y=y, stream=stream)
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    t_proj, t_fast = [], []
+    for _ in range(args.warmup):
+        project()
+        fast()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        ev[0].record(stream)
+        project()
+        ev[1].record(stream)
+        fast()
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        t_proj.append(ev[0].elapsed_time(ev[1]))
+        t_fast.append(ev[1].elapsed_time(ev[2]))
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    pm, fm = float(np.mean(t_proj)), float(np.mean(t_fast))
+    fast_flop = 6 * w.d_v * w.d_key * w.head_steps
+    kernels = {
+        proj_name: {"ms": pm, "bound": proj_bound, "achieved": proj_flop / (pm * 1e-3) / 1e12,
+                    "unit": proj_unit},
+        "srwm_fast_kernel": {"ms": fm, "bound": "alu", "achieved": fast_flop / (fm * 1e-3) / 1e12,
+                             "unit": "TFLOP/s"},
+    }
+    for k in kernels.values():
+        k["frac"] = k["achieved"] / PEAK_FP32_TFLOPS
+    dom = max(kernels, key=lambda k: kernels[k]["ms"])
+    log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step wall; projection {pm:.3f} ms, fast {fm:.3f} ms")
+    rec = {
+        "metric": f"{w.kind} head-steps/sec (B·H·T/s), 1×MI355X",
+        "value": w.head_steps / (ms_per_step * 1e-3),
+        "unit": "head-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded normal x and projection weights; no dataset)",
+        "config": {"workload": w.name, "kind": w.kind, "B": w.B, "H": w.H, "d_in": w.d_in, "d_key": w.d_key,
+                   "d_v": w.d_v, "T": w.T, "apply_input_softmax": w.apply_input_softmax},
+        "roofline": {"bound": kernels[dom]["bound"], "achieved": kernels[dom]["achieved"],
+                     "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s", "frac": kernels[dom]["frac"],
+                     "traffic": None, "kernel": dom},
+        "kernels": kernels,
+    }
+    if not args.no_cpu:
+        from oracle import oracle
+        log("[bench] timing the float64 oracle on a bounded sample")
+        n = 1
+        while True:
+            t0 = time.perf_counter()
+            xs = np.ascontiguousarray(x_host[:n], dtype=np.float64)
+            if w.kind == "deltanet":
+                oracle.deltanet_forward(xs, Wp_host, w.d_key, w.d_v)
+            else:
+                oracle.srdeltanet_forward(xs, Wp_host, w.d_key, w.d_v, apply_input_softmax=w.apply_input_softmax,
+                                          n_lr=w.n_lr)
+            dt = time.perf_counter() - t0
+            if dt * 2 > args.cpu_budget or n >= w.B:
+                break
+            n = min(w.B, max(n + 1, int(n * min(8.0, args.cpu_budget / max(dt, 1e-3) / 2))))
+        rec["cpu_baseline"] = {"value": n * w.H * w.T / dt, "unit": "head-steps/s",
+                               "cores": oracle.default_threads(), "kind": "oracle",
+                               "sample": f"first {n} of {w.B} sequences x {w.H} heads x T={w.T} of {w.name}, "
+                                         f"float64, {dt:.1f} s wall"}
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -269,6 +269,25 @@ typedef struct srwm_deltanet_args {
 
 int srwm_deltanet_forward(const srwm_deltanet_args_t* args);
 
+/* The projection alone: z = the slow projection of every step (the same
+ * arguments; F0, y and F_T are ignored and may be NULL). */
+int srwm_deltanet_project(const srwm_deltanet_args_t* args);
+
+/* The fast-matrix recurrence alone, from given projections z[B][T][H][P]
+ * (P = d_v + 2*d_key + 1, rows [k; v; q; beta]): y[B][T][H][d_v] and F_T
+ * (NULL allowed), starting from F0 (NULL: zero).  The second half of both
+ * srwm_deltanet_forward and srwm_srdeltanet_forward. */
+typedef struct srwm_fast_args {
+    const float* z;
+    const float* F0;
+    float* y;
+    float* F_T;
+    int64_t B, T, H, d_key, d_v;
+    void* stream;
+} srwm_fast_args_t;
+
+int srwm_fast_forward(const srwm_fast_args_t* args);
+
 typedef struct srwm_srdeltanet_args {
     const float* x;
     const float* W0;

@@ -85,10 +85,16 @@ def _ptr(a: np.ndarray | None, ctype):
 
 
 def default_threads() -> int:
+    """Worker threads: the CPUs this process may run on, capped by
+    OMP_NUM_THREADS when set and at 16 (one GPU's share of a host)."""
     try:
-        return max(1, len(os.sched_getaffinity(0)))
+        n = max(1, len(os.sched_getaffinity(0)))
     except AttributeError:  # pragma: no cover
-        return os.cpu_count() or 1
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return min(n, 16)
 
 
 def m_rows(d_in: int, d_out: int, n_lr: int = 4) -> int:

@@ -12,7 +12,7 @@ from __future__ import annotations
 from . import _lib
 from .workloads import HEADLINE, WORKLOADS, Workload
 
-__all__ = ["forward", "backward", "srwm", "tape_row", "deltanet_forward", "srdeltanet_forward", "fwp_supported", "supported", "backward_supported", "variants", "select_variant", "m_rows", "WORKLOADS", "HEADLINE", "Workload"]
+__all__ = ["forward", "backward", "srwm", "tape_row", "deltanet_forward", "deltanet_project", "fast_forward", "srdeltanet_forward", "fwp_supported", "supported", "backward_supported", "variants", "select_variant", "m_rows", "WORKLOADS", "HEADLINE", "Workload"]
 
 
 def m_rows(d_in: int, d_out: int, n_lr: int = 4) -> int:
@@ -322,3 +322,46 @@ def srdeltanet_forward(x, W0, d_key: int, d_v: int, F0=None, apply_input_softmax
     if rc != 0:
         raise RuntimeError(_lib.strerror(rc))
     return y, W_T, F_T, z
+
+
+def deltanet_project(x, W_slow, d_key: int, d_v: int, z=None, stream=None):
+    """DeltaNet's slow projection alone: z [B, T, H, P] for every step."""
+    import torch
+
+    lib = _lib.load()
+    B, T, H, d_in, P, z, _, _ = _fwp_common(x, None, d_key, d_v, False, z, None)
+    if (tuple(W_slow.shape) != (H * P, H * d_in) or W_slow.dtype != torch.float32
+            or W_slow.device != x.device or not W_slow.is_contiguous()):
+        raise ValueError("W_slow must be a contiguous float32 [H*P, H*d_in] tensor on x's device")
+    a = _lib.DeltanetArgs(x=_ptr(x), W_slow=_ptr(W_slow), F0=None, z=_ptr(z), y=None, F_T=None,
+                          B=B, T=T, H=H, d_in=d_in, d_key=d_key, d_v=d_v, stream=_stream_handle(x, stream))
+    with torch.cuda.device(x.device):
+        rc = lib.srwm_deltanet_project(a)
+    if rc != 0:
+        raise RuntimeError(_lib.strerror(rc))
+    return z
+
+
+def fast_forward(z, d_key: int, d_v: int, F0=None, return_state: bool = False, y=None, stream=None):
+    """The fast-matrix recurrence alone from given projections z [B, T, H, P]:
+    returns (y [B, T, H, d_v], F_T or None)."""
+    import torch
+
+    lib = _lib.load()
+    if not isinstance(z, torch.Tensor) or z.device.type != "cuda" or z.dtype != torch.float32 \
+            or z.dim() != 4 or not z.is_contiguous() or z.shape[-1] != d_v + 2 * d_key + 1:
+        raise ValueError("z must be a contiguous float32 [B, T, H, d_v + 2*d_key + 1] tensor on a ROCm GPU")
+    B, T, H, _ = z.shape
+    if F0 is not None and (tuple(F0.shape) != (B, H, d_v, d_key) or F0.dtype != torch.float32
+                           or F0.device != z.device or not F0.is_contiguous()):
+        raise ValueError("F0 must be a contiguous float32 [B, H, d_v, d_key] tensor on z's device")
+    if y is None:
+        y = torch.empty((B, T, H, d_v), dtype=torch.float32, device=z.device)
+    F_T = torch.empty((B, H, d_v, d_key), dtype=torch.float32, device=z.device) if return_state else None
+    a = _lib.FastArgs(z=_ptr(z), F0=_ptr(F0), y=_ptr(y), F_T=_ptr(F_T), B=B, T=T, H=H, d_key=d_key, d_v=d_v,
+                      stream=_stream_handle(z, stream))
+    with torch.cuda.device(z.device):
+        rc = lib.srwm_fast_forward(a)
+    if rc != 0:
+        raise RuntimeError(_lib.strerror(rc))
+    return y, F_T

@@ -99,6 +99,22 @@ class SrdeltanetArgs(ctypes.Structure):
     ]
 
 
+class FastArgs(ctypes.Structure):
+    """srwm_fast_args_t."""
+    _fields_ = [
+        ("z", ctypes.c_void_p),
+        ("F0", ctypes.c_void_p),
+        ("y", ctypes.c_void_p),
+        ("F_T", ctypes.c_void_p),
+        ("B", ctypes.c_int64),
+        ("T", ctypes.c_int64),
+        ("H", ctypes.c_int64),
+        ("d_key", ctypes.c_int64),
+        ("d_v", ctypes.c_int64),
+        ("stream", ctypes.c_void_p),
+    ]
+
+
 class VariantInfo(ctypes.Structure):
     """srwm_variant_info_t."""
     _fields_ = [(name, ctypes.c_int) for name in (
@@ -137,6 +153,10 @@ def load() -> ctypes.CDLL:
     lib.srwm_deltanet_forward.restype = ci
     lib.srwm_srdeltanet_forward.argtypes = [ctypes.POINTER(SrdeltanetArgs)]
     lib.srwm_srdeltanet_forward.restype = ci
+    lib.srwm_deltanet_project.argtypes = [ctypes.POINTER(DeltanetArgs)]
+    lib.srwm_deltanet_project.restype = ci
+    lib.srwm_fast_forward.argtypes = [ctypes.POINTER(FastArgs)]
+    lib.srwm_fast_forward.restype = ci
     lib.srwm_fwp_supported.argtypes = [i64, i64]
     lib.srwm_fwp_supported.restype = ci
     lib.srwm_variant_count.argtypes = []

@@ -22,11 +22,10 @@
 //     the fp32 matrix cores (v_mfma_f32_16x16x4_f32); for SR-DeltaNet the SRWM
 //     kernel of srwm_fwd.hip with y = Z.  Z[B][T][H][P] is a caller-provided
 //     float32 buffer.
-//   * The fast-matrix recurrence: one wave per (b, h) unit, F in registers
-//     (lane (rg, p) holds rows rg + G*r and columns [p*L, p*L + L)).  The
-//     softmaxes of step t+1 depend only on Z, so they are formed while step
-//     t's matrix work runs and handed over through a double-buffered LDS
-//     slice; the serial chain per step is two row reductions and the write.
+//   * The fast-matrix recurrence: one workgroup per (b, h) unit, the rows of
+//     F split over its waves and held in registers.  The softmaxes depend
+//     only on Z, so they are formed a chunk of steps ahead, off the serial
+//     chain; per step the chain is two row reductions and the write.
 //     y_t = F_{t-1} qh + a (kh . qh) with a = g (v - vb): the query of the
 //     written matrix without a second pass over it.
 #include <hip/hip_runtime.h>
@@ -112,30 +111,43 @@ __global__ __launch_bounds__(256) void srwm_proj_gemm_kernel(const float* __rest
 }
 
 // ----------------------------------------------------------------------------
-// The fast-matrix recurrence.  One wave per unit; Z[b][t][h][0..PR) holds the
-// projection [k; v; q; beta] of step t.
-template <int D_KEY, int D_V, int P>
-__global__ __launch_bounds__(64) void srwm_fast_kernel(const float* __restrict__ Z,
-                                                       const float* __restrict__ F0,
-                                                       float* __restrict__ y, float* __restrict__ FT,
-                                                       int T, int H)
+// The fast-matrix recurrence.  Z[b][t][h][0..PR) holds the projection
+// [k; v; q; beta] of step t.  One workgroup of NW waves per unit; the rows of
+// F are independent of each other (each row's write and query need only kh,
+// qh, g and its own value), so wave w owns rows [w*RW, (w+1)*RW), RW = d_v/NW,
+// and lane (rg, p) of the wave holds rows rg + G*r and columns [p*L, p*L+L).
+// Steps are handled S at a time: the softmaxes, values and gates of chunk c+1
+// are formed (wave w takes steps w, w+NW, ... of the chunk, from registers
+// loaded a chunk earlier) into one half of a double-buffered LDS area while
+// the matrix work of chunk c runs from the other half; one workgroup barrier
+// per chunk.
+template <int D_KEY, int D_V, int NW, int P, int S>
+__global__ __launch_bounds__(NW * 64) void srwm_fast_kernel(const float* __restrict__ Z,
+                                                            const float* __restrict__ F0,
+                                                            float* __restrict__ y, float* __restrict__ FT,
+                                                            int T, int H)
 {
     constexpr int PR = D_V + 2 * D_KEY + 1;
     constexpr int L = D_KEY / P;
     constexpr int G = kWave / P;
-    constexpr int R = (D_V + G - 1) / G;
+    constexpr int RW = D_V / NW;             // rows per wave
+    constexpr int R = (RW + G - 1) / G;      // rows per lane
     constexpr int EZ = (PR + kWave - 1) / kWave;
     constexpr int V0 = D_KEY, Q0 = D_KEY + D_V, BETA = PR - 1;
-    static_assert(D_KEY % P == 0, "P must divide d_key");
+    constexpr int SW = S / NW;               // steps each wave prepares per chunk
+    // prepared step: kh [0, D_KEY), qh [D_KEY, 2 D_KEY), v [2 D_KEY, +D_V), g
+    constexpr int KQ = 2 * D_KEY, GO = KQ + D_V, KP = (GO + 1 + 3) & ~3;
+    static_assert(D_KEY % P == 0 && D_V % NW == 0 && S % NW == 0, "shapes");
+    static_assert(D_KEY % 4 == 0 && D_V % 4 == 0, "16-byte sections");
 
-    __shared__ __attribute__((aligned(16))) float s_kh[2][D_KEY];
-    __shared__ __attribute__((aligned(16))) float s_qh[2][D_KEY];
-    __shared__ __attribute__((aligned(16))) float s_v[2][R * G];
-    __shared__ float s_g[2];
+    __shared__ __attribute__((aligned(16))) float s_p[2][S][KP];
 
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = NW == 1 ? 0 : tid / kWave;
     const int p = lane % P;
     const int rg = lane / P;
+    const int row0 = wave * RW;
     const int unit = blockIdx.x;
     const int b = unit / H;
     const int h = unit - b * H;
@@ -147,104 +159,114 @@ __global__ __launch_bounds__(64) void srwm_fast_kernel(const float* __restrict__
     float F[R][L];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const int row = rg + G * r;
-        if (F0 != nullptr && row < D_V) {
-            load_f32<L>(F0 + ((int64_t)unit * D_V + row) * D_KEY + p * L, F[r]);
+        const int lr = rg + G * r;
+        if (F0 != nullptr && lr < RW) {
+            load_f32<L>(F0 + ((int64_t)unit * D_V + row0 + lr) * D_KEY + p * L, F[r]);
         } else {
 #pragma unroll
             for (int c = 0; c < L; ++c) F[r][c] = 0.f;
         }
     }
 
-    auto load_z = [&](int t, float (&zr)[EZ]) {
+    // This wave's share of a chunk's raw projections: steps c0 + wave + NW*j.
+    float zr[SW][EZ];
+    auto load_chunk = [&](int c0) {
 #pragma unroll
-        for (int i = 0; i < EZ; ++i) {
-            const int e = lane + kWave * i;
-            zr[i] = (t < T && e < PR) ? Z[z0 + (int64_t)t * z_step + e] : 0.f;
+        for (int j = 0; j < SW; ++j) {
+            const int t = c0 + wave + NW * j;
+#pragma unroll
+            for (int i = 0; i < EZ; ++i) {
+                const int e = lane + kWave * i;
+                zr[j][i] = (t < T && e < PR) ? Z[z0 + (int64_t)t * z_step + e] : 0.f;
+            }
         }
     };
-    // The softmaxes and the gate of one step, into LDS slice `buf`.
-    auto prep = [&](const float (&zr)[EZ], int buf) {
-        float mk = -INFINITY, mq = -INFINITY;
+    // Softmaxes, values and gates of this wave's steps of a chunk.
+    auto prep_chunk = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < EZ; ++i) {
-            const int e = lane + kWave * i;
-            if (e < V0) mk = fmax2(mk, zr[i]);
-            else if (e >= Q0 && e < BETA) mq = fmax2(mq, zr[i]);
-        }
-        mk = wave_max(mk);
-        mq = wave_max(mq);
-        float ex[EZ];
-        float sk = 0.f, sq = 0.f;
+        for (int j = 0; j < SW; ++j) {
+            const int s = wave + NW * j;
+            float mk = -INFINITY, mq = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < EZ; ++i) {
-            const int e = lane + kWave * i;
-            const bool isk = e < V0, isq = e >= Q0 && e < BETA;
-            ex[i] = isk ? exp_f32(zr[i] - mk) : isq ? exp_f32(zr[i] - mq) : 0.f;
-            if (isk) sk += ex[i];
-            if (isq) sq += ex[i];
-        }
-        const float ik = rcp_f32(wave_sum(sk)), iq = rcp_f32(wave_sum(sq));
+            for (int i = 0; i < EZ; ++i) {
+                const int e = lane + kWave * i;
+                if (e < V0) mk = fmax2(mk, zr[j][i]);
+                else if (e >= Q0 && e < BETA) mq = fmax2(mq, zr[j][i]);
+            }
+            mk = wave_max(mk);
+            mq = wave_max(mq);
+            float ex[EZ];
+            float sk = 0.f, sq = 0.f;
 #pragma unroll
-        for (int i = 0; i < EZ; ++i) {
-            const int e = lane + kWave * i;
-            if (e < V0) s_kh[buf][e] = ex[i] * ik;
-            else if (e < Q0) s_v[buf][e - V0] = zr[i];
-            else if (e < BETA) s_qh[buf][e - Q0] = ex[i] * iq;
-            else if (e == BETA) s_g[buf] = sigmoid_f32(zr[i]);
-        }
-        if constexpr (R * G > D_V) {
-            // padding rows read value 0 (their F rows are 0 and stay 0)
-            for (int e = D_V + lane; e < R * G; e += kWave) s_v[buf][e] = 0.f;
+            for (int i = 0; i < EZ; ++i) {
+                const int e = lane + kWave * i;
+                const bool isk = e < V0, isq = e >= Q0 && e < BETA;
+                ex[i] = isk ? exp_f32(zr[j][i] - mk) : isq ? exp_f32(zr[j][i] - mq) : 0.f;
+                if (isk) sk += ex[i];
+                if (isq) sq += ex[i];
+            }
+            const float ik = rcp_f32(wave_sum(sk)), iq = rcp_f32(wave_sum(sq));
+#pragma unroll
+            for (int i = 0; i < EZ; ++i) {
+                const int e = lane + kWave * i;
+                if (e < V0) s_p[buf][s][e] = ex[i] * ik;
+                else if (e < Q0) s_p[buf][s][KQ + e - V0] = zr[j][i];
+                else if (e < BETA) s_p[buf][s][D_KEY + e - Q0] = ex[i] * iq;
+                else if (e == BETA) s_p[buf][s][GO] = sigmoid_f32(zr[j][i]);
+            }
         }
     };
 
-    float zn[EZ];
     if (T > 0) {
-        float zf[EZ];
-        load_z(0, zf);
-        prep(zf, 0);
-        load_z(1, zn);
-        wave_sync();
+        load_chunk(0);
+        prep_chunk(0);
+        if (T > S) load_chunk(S);
+        __syncthreads();
     }
-    for (int t = 0; t < T; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < T) {
-            prep(zn, buf ^ 1);
-            load_z(t + 2, zn);
+    for (int c0 = 0, chunk = 0; c0 < T; c0 += S, ++chunk) {
+        const int buf = chunk & 1;
+        if (c0 + S < T) {
+            prep_chunk(buf ^ 1);
+            if (c0 + 2 * S < T) load_chunk(c0 + 2 * S);
         }
-        float kh[L], qh[L];
-        load_f32<L>(&s_kh[buf][p * L], kh);
-        load_f32<L>(&s_qh[buf][p * L], qh);
-        const float g = s_g[buf];
-        float kq = 0.f;
+        const int n = (T - c0) < S ? (T - c0) : S;
+        for (int s = 0; s < n; ++s) {
+            const float* __restrict__ ps = s_p[buf][s];
+            float kh[L], qh[L];
+            load_f32<L>(ps + p * L, kh);
+            load_f32<L>(ps + D_KEY + p * L, qh);
+            const float g = ps[GO];
+            float kq = 0.f;
 #pragma unroll
-        for (int c = 0; c < L; ++c) kq = fmaf(kh[c], qh[c], kq);
-        kq = group_sum<P>(kq);
+            for (int c = 0; c < L; ++c) kq = fmaf(kh[c], qh[c], kq);
+            kq = group_sum<P>(kq);
+            const int64_t yt = y0 + (int64_t)(c0 + s) * y_step + row0;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int row = rg + G * r;
-            float s1 = 0.f, s2 = 0.f;
+            for (int r = 0; r < R; ++r) {
+                const int lr = rg + G * r;
+                float s1 = 0.f, s2 = 0.f;
 #pragma unroll
-            for (int c = 0; c < L; ++c) {
-                s1 = fmaf(F[r][c], kh[c], s1);
-                s2 = fmaf(F[r][c], qh[c], s2);
+                for (int c = 0; c < L; ++c) {
+                    s1 = fmaf(F[r][c], kh[c], s1);
+                    s2 = fmaf(F[r][c], qh[c], s2);
+                }
+                s1 = group_sum<P>(s1);  // vb: the key address's content
+                s2 = group_sum<P>(s2);  // F_{t-1} qh
+                const float v = lr < RW ? ps[KQ + row0 + lr] : 0.f;
+                const float a = g * (v - s1);
+#pragma unroll
+                for (int c = 0; c < L; ++c) F[r][c] = fmaf(a, kh[c], F[r][c]);
+                if (p == 0 && lr < RW) y[yt + lr] = fmaf(a, kq, s2);
             }
-            s1 = group_sum<P>(s1);  // vb: the key address's content
-            s2 = group_sum<P>(s2);  // F_{t-1} qh
-            const float a = g * (s_v[buf][row] - s1);
-#pragma unroll
-            for (int c = 0; c < L; ++c) F[r][c] = fmaf(a, kh[c], F[r][c]);
-            if (p == 0 && row < D_V) y[y0 + (int64_t)t * y_step + row] = fmaf(a, kq, s2);
         }
-        wave_sync();
+        __syncthreads();
     }
 
     if (FT != nullptr) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int row = rg + G * r;
-            if (row < D_V) store_f32<L>(FT + ((int64_t)unit * D_V + row) * D_KEY + p * L, F[r]);
+            const int lr = rg + G * r;
+            if (lr < RW) store_f32<L>(FT + ((int64_t)unit * D_V + row0 + lr) * D_KEY + p * L, F[r]);
         }
     }
 }
@@ -253,13 +275,14 @@ __global__ __launch_bounds__(64) void srwm_fast_kernel(const float* __restrict__
 // Variants: (d_key, d_v, lanes per row).
 using FastFn = void (*)(const float*, const float*, float*, float*, int, int);
 struct FastVariant {
-    int d_key, d_v;
+    int d_key, d_v, nw;
     FastFn fn;
 };
+// (d_key, d_v, waves per unit, lanes per row, steps per chunk)
 const FastVariant kFastVariants[] = {
-    {8, 8, &srwm_fast_kernel<8, 8, 8>},
-    {16, 16, &srwm_fast_kernel<16, 16, 4>},
-    {64, 64, &srwm_fast_kernel<64, 64, 4>},
+    {8, 8, 1, &srwm_fast_kernel<8, 8, 1, 8, 16>},
+    {16, 16, 1, &srwm_fast_kernel<16, 16, 1, 4, 16>},
+    {64, 64, 4, &srwm_fast_kernel<64, 64, 4, 4, 16>},
 };
 constexpr int kNumFastVariants = sizeof(kFastVariants) / sizeof(kFastVariants[0]);
 
@@ -293,57 +316,99 @@ int launch_fast(int vi, const float* z, const float* F0, float* y, float* FT, in
     int Ti = static_cast<int>(T), Hi = static_cast<int>(H);
     void* args[] = {const_cast<float**>(&z), const_cast<float**>(&F0), &y, &FT, &Ti, &Hi};
     const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(kFastVariants[vi].fn),
-                                           dim3(static_cast<unsigned>(units)), dim3(kWave), args, 0,
+                                           dim3(static_cast<unsigned>(units)), dim3(kFastVariants[vi].nw * kWave), args, 0,
                                            static_cast<hipStream_t>(stream));
     return err == hipSuccess ? SRWM_OK : SRWM_ERR_HIP;
 }
 
-int deltanet_impl(const srwm_deltanet_args_t* a)
+// The checks of a DeltaNet call; `project_only` skips the fast-matrix buffers.
+int deltanet_check(const srwm_deltanet_args_t* a, bool project_only, int* vi, int64_t* K, int64_t* C)
 {
     if (a == nullptr) return SRWM_ERR_NULL;
     FwpSizes s;
     int rc = fwp_sizes(a->B, a->T, a->H, a->d_in, a->d_key, a->d_v, &s);
     if (rc != SRWM_OK) return rc;
-    const int vi = find_fast(a->d_key, a->d_v);
-    if (vi < 0) return SRWM_ERR_UNSUPPORTED;
+    *vi = find_fast(a->d_key, a->d_v);
+    if (*vi < 0 && !project_only) return SRWM_ERR_UNSUPPORTED;
     const int64_t P = a->d_v + 2 * a->d_key + 1;
-    int64_t K, C, nw;
-    if (!mul_ok(a->H, a->d_in, &K) || !mul_ok(a->H, P, &C) || !mul_ok(C, K * 4, &nw)) return SRWM_ERR_SHAPE;
-    if (K % 4 != 0) return SRWM_ERR_SHAPE;  // 16-byte rows of x and W_slow
-    if (K > INT32_MAX || C > INT32_MAX) return SRWM_ERR_SHAPE;
+    int64_t nw;
+    if (!mul_ok(a->H, a->d_in, K) || !mul_ok(a->H, P, C) || !mul_ok(*C, *K * 4, &nw)) return SRWM_ERR_SHAPE;
+    if (*K % 4 != 0) return SRWM_ERR_SHAPE;  // 16-byte rows of x and W_slow
+    if (*K > INT32_MAX || *C > INT32_MAX) return SRWM_ERR_SHAPE;
     if (s.units == 0) return SRWM_OK;
-    if (s.nx > 0 && (a->x == nullptr || a->W_slow == nullptr || a->z == nullptr || a->y == nullptr))
+    if (s.nx > 0 && (a->x == nullptr || a->W_slow == nullptr || a->z == nullptr || (!project_only && a->y == nullptr)))
         return SRWM_ERR_NULL;
+    const float* F0 = project_only ? nullptr : a->F0;
+    float* y = project_only ? nullptr : a->y;
+    float* FT = project_only ? nullptr : a->F_T;
     if ((reinterpret_cast<uintptr_t>(a->x) | reinterpret_cast<uintptr_t>(a->W_slow) |
-         reinterpret_cast<uintptr_t>(a->F0) | reinterpret_cast<uintptr_t>(a->z) |
-         reinterpret_cast<uintptr_t>(a->y) | reinterpret_cast<uintptr_t>(a->F_T)) & 15u)
+         reinterpret_cast<uintptr_t>(F0) | reinterpret_cast<uintptr_t>(a->z) |
+         reinterpret_cast<uintptr_t>(y) | reinterpret_cast<uintptr_t>(FT)) & 15u)
         return SRWM_ERR_ARG;
-    const void* ins[] = {a->x, a->W_slow, a->F0};
-    const int64_t nins[] = {s.nx, nw, a->F0 ? s.nf : 0};
-    void* outs[] = {a->z, a->y, a->F_T};
-    const int64_t nouts[] = {s.nz, s.ny, a->F_T ? s.nf : 0};
+    const void* ins[] = {a->x, a->W_slow, F0};
+    const int64_t nins[] = {s.nx, nw, F0 ? s.nf : 0};
+    void* outs[] = {a->z, y, FT};
+    const int64_t nouts[] = {s.nz, y ? s.ny : 0, FT ? s.nf : 0};
     for (int o = 0; o < 3; ++o) {
         for (int i = 0; i < 3; ++i)
             if (ranges_overlap(outs[o], nouts[o], ins[i], nins[i])) return SRWM_ERR_ALIAS;
         for (int o2 = o + 1; o2 < 3; ++o2)
             if (ranges_overlap(outs[o], nouts[o], outs[o2], nouts[o2])) return SRWM_ERR_ALIAS;
     }
-    const hipStream_t st = static_cast<hipStream_t>(a->stream);
+    return SRWM_OK;
+}
+
+int launch_projection(const srwm_deltanet_args_t* a, int64_t K, int64_t C)
+{
     const int64_t N = a->B * a->T;
-    if (N > 0) {
-        const float* X = static_cast<const float*>(a->x);
-        const float* Wp = a->W_slow;
-        float* Zp = a->z;
-        int Ci = static_cast<int>(C), Ki = static_cast<int>(K);
-        int64_t Nv = N;
-        void* args[] = {const_cast<float**>(&X), const_cast<float**>(&Wp), &Zp, &Nv, &Ci, &Ki};
-        const int64_t gx = (N + kGM - 1) / kGM;
-        if (gx > INT32_MAX) return SRWM_ERR_SHAPE;
-        const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(&srwm_proj_gemm_kernel),
-                                               dim3(static_cast<unsigned>(gx), static_cast<unsigned>((C + kGN - 1) / kGN)),
-                                               dim3(256), args, 0, st);
-        if (err != hipSuccess) return SRWM_ERR_HIP;
-    }
+    if (N == 0 || a->H == 0) return SRWM_OK;
+    const float* X = a->x;
+    const float* Wp = a->W_slow;
+    float* Zp = a->z;
+    int Ci = static_cast<int>(C), Ki = static_cast<int>(K);
+    int64_t Nv = N;
+    void* args[] = {const_cast<float**>(&X), const_cast<float**>(&Wp), &Zp, &Nv, &Ci, &Ki};
+    const int64_t gx = (N + kGM - 1) / kGM;
+    if (gx > INT32_MAX) return SRWM_ERR_SHAPE;
+    const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(&srwm_proj_gemm_kernel),
+                                           dim3(static_cast<unsigned>(gx), static_cast<unsigned>((C + kGN - 1) / kGN)),
+                                           dim3(256), args, 0, static_cast<hipStream_t>(a->stream));
+    return err == hipSuccess ? SRWM_OK : SRWM_ERR_HIP;
+}
+
+int deltanet_impl(const srwm_deltanet_args_t* a, bool project_only)
+{
+    int vi;
+    int64_t K, C;
+    const int rc = deltanet_check(a, project_only, &vi, &K, &C);
+    if (rc != SRWM_OK) return rc;
+    if (a->B * a->H == 0) return SRWM_OK;
+    const int rp = launch_projection(a, K, C);
+    if (rp != SRWM_OK || project_only) return rp;
+    return launch_fast(vi, a->z, a->F0, a->y, a->F_T, a->B * a->H, a->T, a->H, a->stream);
+}
+
+int fast_impl(const srwm_fast_args_t* a)
+{
+    if (a == nullptr) return SRWM_ERR_NULL;
+    FwpSizes s;
+    int rc = fwp_sizes(a->B, a->T, a->H, 1, a->d_key, a->d_v, &s);
+    if (rc != SRWM_OK) return rc;
+    const int vi = find_fast(a->d_key, a->d_v);
+    if (vi < 0) return SRWM_ERR_UNSUPPORTED;
+    if (s.units == 0) return SRWM_OK;
+    if (s.steps > 0 && (a->z == nullptr || a->y == nullptr)) return SRWM_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(a->F0) | reinterpret_cast<uintptr_t>(a->y) |
+         reinterpret_cast<uintptr_t>(a->F_T)) & 15u)
+        return SRWM_ERR_ARG;
+    const void* ins[] = {a->z, a->F0};
+    const int64_t nins[] = {s.nz, a->F0 ? s.nf : 0};
+    void* outs[] = {a->y, a->F_T};
+    const int64_t nouts[] = {s.ny, a->F_T ? s.nf : 0};
+    for (int o = 0; o < 2; ++o)
+        for (int i = 0; i < 2; ++i)
+            if (ranges_overlap(outs[o], nouts[o], ins[i], nins[i])) return SRWM_ERR_ALIAS;
+    if (ranges_overlap(a->y, s.ny, a->F_T, a->F_T ? s.nf : 0)) return SRWM_ERR_ALIAS;
     return launch_fast(vi, a->z, a->F0, a->y, a->F_T, s.units, a->T, a->H, a->stream);
 }
 
@@ -409,7 +474,11 @@ int srdeltanet_impl(const srwm_srdeltanet_args_t* a)
 
 extern "C" {
 
-int srwm_deltanet_forward(const srwm_deltanet_args_t* args) { return deltanet_impl(args); }
+int srwm_deltanet_forward(const srwm_deltanet_args_t* args) { return deltanet_impl(args, false); }
+
+int srwm_deltanet_project(const srwm_deltanet_args_t* args) { return deltanet_impl(args, true); }
+
+int srwm_fast_forward(const srwm_fast_args_t* args) { return fast_impl(args); }
 
 int srwm_srdeltanet_forward(const srwm_srdeltanet_args_t* args) { return srdeltanet_impl(args); }
 

@@ -314,3 +314,34 @@ def test_fwp_empty_problems_are_noops():
     assert lib.srwm_srdeltanet_forward(None) == E_NULL
     assert call_dn(B=0, x=None, z=None, y=None) == OK
     assert call_sdn(H=0, x=None, z=None, y=None, W0=None) == OK
+
+
+def call_fast(**kw):
+    base = dict(z=FAKE_Z, F0=None, y=FAKE_Y, F_T=None, B=2, T=3, H=2, d_key=16, d_v=16, stream=None)
+    base.update(kw)
+    return _lib.load().srwm_fast_forward(ctypes.byref(_lib.FastArgs(**base)))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d_key=7, d_v=7), E_UNSUP),
+    (dict(T=-1), E_SHAPE),
+    (dict(z=None), E_NULL),
+    (dict(y=None), E_NULL),
+    (dict(F_T=FAKE_Y + 4), E_ARG),
+    (dict(y=FAKE_Z + 32), E_ALIAS),
+    (dict(F_T=FAKE_Y + 64), E_ALIAS),
+])
+def test_fast_forward_validation(kw, code):
+    assert call_fast(**kw) == code
+
+
+def test_deltanet_project_ignores_fast_buffers():
+    # the projection alone needs no y; its checks still reject bad shapes
+    assert call_dn(B=0, x=None, z=None, y=None) == OK
+    lib = _lib.load()
+    a = _lib.DeltanetArgs(x=FAKE_X, W_slow=FAKE_W0, F0=None, z=FAKE_Z, y=None, F_T=None, B=2, T=3, H=1,
+                          d_in=3, d_key=16, d_v=16, stream=None)
+    assert lib.srwm_deltanet_project(ctypes.byref(a)) == E_SHAPE
+    a = _lib.DeltanetArgs(x=FAKE_X, W_slow=FAKE_W0, F0=None, z=FAKE_X + 16, y=None, F_T=None, B=2, T=3, H=2,
+                          d_in=16, d_key=16, d_v=16, stream=None)
+    assert lib.srwm_deltanet_project(ctypes.byref(a)) == E_ALIAS

@@ -166,3 +166,27 @@ def test_fwp_deterministic():
     b = run_deltanet(w, x, Wslow)
     for u, v in zip(a, b):
         np.testing.assert_array_equal(u, v)
+
+
+def test_split_entry_points_equal_the_composites():
+    # projection + fast recurrence called separately give the composite's bits
+    srwm = _srwm()
+    w = DN_CASES[2]
+    x, Wslow = gen_x(w), gen_W_slow(w)
+    F0 = fast0(w, 13)
+    y, FT, z = run_deltanet(w, x, Wslow, F0)
+    z2 = srwm.deltanet_project(td(x), td(Wslow), w.d_key, w.d_v)
+    y2, F2 = srwm.fast_forward(z2, w.d_key, w.d_v, F0=td(F0), return_state=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(z2.cpu().numpy(), z)
+    np.testing.assert_array_equal(y2.cpu().numpy(), y)
+    np.testing.assert_array_equal(F2.cpu().numpy(), FT)
+    ws = SDN_CASES[2]
+    x, W0 = gen_x(ws), gen_W0(ws)
+    y, WT, FT, z = run_srdeltanet(ws, x, W0)
+    zs, _ = srwm.forward(td(x), td(W0), apply_input_softmax=ws.apply_input_softmax, n_lr=ws.n_lr)
+    y3, F3 = srwm.fast_forward(zs, ws.d_key, ws.d_v, return_state=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(zs.cpu().numpy(), z)
+    np.testing.assert_array_equal(y3.cpu().numpy(), y)
+    np.testing.assert_array_equal(F3.cpu().numpy(), FT)
