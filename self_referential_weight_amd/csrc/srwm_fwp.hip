@@ -50,6 +50,12 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 // B[l / 16][l % 16]; accumulator register r of lane l is D[4 (l / 16) + r][l % 16].
 constexpr int kGM = 64, kGN = 64, kGK = 32, kGPad = 4;
 
+// Workgroups are dispatched to the 8 XCDs round-robin (workgroup i on XCD
+// i % 8), each XCD with its own L2.  The 1-D grid is renumbered so that the
+// column tiles of one row tile are consecutive on one XCD: the x rows are
+// fetched from HBM once and re-read from that XCD's L2.
+constexpr int kXcds = 8;
+
 __global__ __launch_bounds__(256) void srwm_proj_gemm_kernel(const float* __restrict__ X,
                                                              const float* __restrict__ W,
                                                              float* __restrict__ Z, int64_t N, int C,
@@ -60,8 +66,13 @@ __global__ __launch_bounds__(256) void srwm_proj_gemm_kernel(const float* __rest
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int64_t n0 = (int64_t)blockIdx.x * kGM;
-    const int c0 = blockIdx.y * kGN;
+    const int64_t ctiles = (C + kGN - 1) / kGN;
+    const int64_t tiles = ((N + kGM - 1) / kGM) * ctiles;
+    const int64_t per_xcd = (int64_t)gridDim.x / kXcds;  // grid is a multiple of kXcds
+    const int64_t g = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    if (g >= tiles) return;  // padding workgroups (whole workgroup, before any barrier)
+    const int64_t n0 = (g / ctiles) * kGM;
+    const int c0 = static_cast<int>(g % ctiles) * kGN;
     const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
     const int lr = tid >> 3, lc = (tid & 7) * 4;  // loader: rows lr, lr + 32; columns lc..lc+3
 
@@ -283,14 +294,22 @@ const FastVariant kFastVariants[] = {
     {8, 8, 1, &srwm_fast_kernel<8, 8, 1, 8, 16>},
     {16, 16, 1, &srwm_fast_kernel<16, 16, 1, 4, 16>},
     {64, 64, 4, &srwm_fast_kernel<64, 64, 4, 4, 16>},
+    {64, 64, 8, &srwm_fast_kernel<64, 64, 8, 8, 16>},
 };
 constexpr int kNumFastVariants = sizeof(kFastVariants) / sizeof(kFastVariants[0]);
 
-int find_fast(int64_t d_key, int64_t d_v)
+// The most waves per unit that keep units * waves within four waves per SIMD
+// of the chip (4096); else the fewest.
+int find_fast(int64_t d_key, int64_t d_v, int64_t units = 1)
 {
-    for (int i = 0; i < kNumFastVariants; ++i)
-        if (kFastVariants[i].d_key == d_key && kFastVariants[i].d_v == d_v) return i;
-    return -1;
+    int best = -1, fewest = -1;
+    for (int i = 0; i < kNumFastVariants; ++i) {
+        const FastVariant& v = kFastVariants[i];
+        if (v.d_key != d_key || v.d_v != d_v) continue;
+        if (fewest < 0 || v.nw < kFastVariants[fewest].nw) fewest = i;
+        if (units * v.nw <= 4096 && (best < 0 || v.nw > kFastVariants[best].nw)) best = i;
+    }
+    return best >= 0 ? best : fewest;
 }
 
 // Byte sizes shared by both entry points: x, z, y and one fast state per unit.
@@ -328,7 +347,7 @@ int deltanet_check(const srwm_deltanet_args_t* a, bool project_only, int* vi, in
     FwpSizes s;
     int rc = fwp_sizes(a->B, a->T, a->H, a->d_in, a->d_key, a->d_v, &s);
     if (rc != SRWM_OK) return rc;
-    *vi = find_fast(a->d_key, a->d_v);
+    *vi = find_fast(a->d_key, a->d_v, s.units);
     if (*vi < 0 && !project_only) return SRWM_ERR_UNSUPPORTED;
     const int64_t P = a->d_v + 2 * a->d_key + 1;
     int64_t nw;
@@ -368,11 +387,12 @@ int launch_projection(const srwm_deltanet_args_t* a, int64_t K, int64_t C)
     int Ci = static_cast<int>(C), Ki = static_cast<int>(K);
     int64_t Nv = N;
     void* args[] = {const_cast<float**>(&X), const_cast<float**>(&Wp), &Zp, &Nv, &Ci, &Ki};
-    const int64_t gx = (N + kGM - 1) / kGM;
-    if (gx > INT32_MAX) return SRWM_ERR_SHAPE;
+    const int64_t tiles = ((N + kGM - 1) / kGM) * ((C + kGN - 1) / kGN);
+    const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
+    if (grid > INT32_MAX) return SRWM_ERR_SHAPE;
     const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(&srwm_proj_gemm_kernel),
-                                           dim3(static_cast<unsigned>(gx), static_cast<unsigned>((C + kGN - 1) / kGN)),
-                                           dim3(256), args, 0, static_cast<hipStream_t>(a->stream));
+                                           dim3(static_cast<unsigned>(grid)), dim3(256), args, 0,
+                                           static_cast<hipStream_t>(a->stream));
     return err == hipSuccess ? SRWM_OK : SRWM_ERR_HIP;
 }
 
@@ -394,7 +414,7 @@ int fast_impl(const srwm_fast_args_t* a)
     FwpSizes s;
     int rc = fwp_sizes(a->B, a->T, a->H, 1, a->d_key, a->d_v, &s);
     if (rc != SRWM_OK) return rc;
-    const int vi = find_fast(a->d_key, a->d_v);
+    const int vi = find_fast(a->d_key, a->d_v, s.units);
     if (vi < 0) return SRWM_ERR_UNSUPPORTED;
     if (s.units == 0) return SRWM_OK;
     if (s.steps > 0 && (a->z == nullptr || a->y == nullptr)) return SRWM_ERR_NULL;
@@ -418,7 +438,7 @@ int srdeltanet_impl(const srwm_srdeltanet_args_t* a)
     FwpSizes s;
     int rc = fwp_sizes(a->B, a->T, a->H, a->d_in, a->d_key, a->d_v, &s);
     if (rc != SRWM_OK) return rc;
-    const int vi = find_fast(a->d_key, a->d_v);
+    const int vi = find_fast(a->d_key, a->d_v, s.units);
     if (vi < 0) return SRWM_ERR_UNSUPPORTED;
     const int64_t P = a->d_v + 2 * a->d_key + 1;
     if (a->n_lr != 1 && a->n_lr != 4) return SRWM_ERR_ARG;
