@@ -35,11 +35,12 @@ sys.path.insert(0, str(ROOT))
 METRIC = "SRWM head-steps/sec (B·H·T/s) and % of FP32 VALU peak, 1×MI355X"
 # MI355X FP32 vector peak: 256 CUs x 256 FLOP/clk/CU x 2.4 GHz.
 PEAK_FP32_TFLOPS = 157.3
-# The forward kernels and the device helpers they include.
-KERNEL_SRCS = [ROOT / "self_referential_weight_amd" / "csrc" / f for f in ("srwm_fwd.hip", "srwm_device.h")]
+# The forward kernels' device code and the device helpers they include (the
+# variant table and host code do not change the kernel's traffic).
+KERNEL_SRCS = [ROOT / "self_referential_weight_amd" / "csrc" / f for f in ("srwm_fwd_kernels.h", "srwm_device.h")]
 TRAFFIC_FILE = ROOT / "profiles" / "srwm_fwd_rl_d64_bf16_hbm_traffic.json"
-# The backward kernel and the device helpers it includes.
-BWD_SRCS = [ROOT / "self_referential_weight_amd" / "csrc" / f for f in ("srwm_bwd.hip", "srwm_device.h")]
+# The backward kernel's device code and the device helpers it includes.
+BWD_SRCS = [ROOT / "self_referential_weight_amd" / "csrc" / f for f in ("srwm_bwd_kernels.h", "srwm_device.h")]
 BWD_TRAFFIC_FILE = ROOT / "profiles" / "srwm_bwd_rl_d64_bf16_hbm_traffic.json"
 
 

@@ -1,0 +1,456 @@
+// srwm_bwd_kernels.h -- the backward kernel of libsrwm (device code only),
+// included by srwm_bwd.hip, which holds the variant table and the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "srwm_device.h"
+
+namespace srwm {
+
+// ----------------------------------------------------------------------------
+// Backward pass (memory-efficient BPTT).
+//
+// The pages train W0 by backpropagation through the unrolled self-modification
+// ("Metalearning Continual Learning Algorithms", after Eq. (6): memory-efficient
+// BPTT; review page Sec. 2.5).  The forward pass run with a tape stores, per
+// step, a_t = g (.) W_{t-1}(qh_t - kh_t), kh_t, e_t = qh_t - kh_t and the
+// rates g_t.  From W_T the kernel walks t backwards: it undoes the update,
+// W_{t-1} = W_t - a_t kh_t^T (no projection is recomputed: the tape holds
+// everything the step's adjoint needs), and carries Wh = dL/dW_t:
+//     ah    = Wh kh_t                 khh  = Wh^T a_t
+//     rh    = g (.) ah                betah_c = (1 - g_c) sum_{rate(i)=c} ah_i a_i
+//     eh    = W^T rh                  (khh -= eh, qhh = eh)
+//     kbar  = kh (.) (khh - <khh,kh>) qbar = qh (.) (qhh - <qhh,qh>)
+//     zh    = [gy_t; kbar; qbar; betah]
+//     uh    = W^T zh                  dx_t = uh, or the softmax backward of it
+//     Wh   += rh e^T + zh u^T
+// after which Wh = dL/dW_{t-1}.
+//
+// Layout: lane (rg, p), rg = tid / P, p = tid % P, holds rows rg + G*r and
+// columns [p*L, p*L + L) of both W and Wh in registers.  Row sums (ah) are P
+// lanes joined by DPP.  Column sums (khh, eh, uh) are over all G row groups:
+// inside a wave they are reduce-scattered over the row-group lane bits (the
+// lane-row swaps v_permlane32_swap / v_permlane16_swap halve the columns a
+// lane carries, 1 swap + 1 add per pair; a DPP rotation adds the remaining
+// bit), then the NW wave partials meet in LDS, where lane j of every wave
+// reads column j.  uh of step t is reduced together with khh and eh of step
+// t-1, so each step has a single workgroup barrier: step inputs are staged in
+// a triple-buffered LDS ring and the exchange area is double-buffered.
+__device__ __forceinline__ void swap32(float& x, float& y)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    x = __uint_as_float(r[0]);
+    y = __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ void swap16(float& x, float& y)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    x = __uint_as_float(r[0]);
+    y = __uint_as_float(r[1]);
+}
+
+// Sum of v over the lane pair that differs in lane bit B (B = 3, 4 or 5).
+template <int B>
+__device__ __forceinline__ float pair_sum(float v)
+{
+    static_assert(B >= 3 && B <= 5, "lane bit");
+    if constexpr (B == 3) {
+        return v + dpp<0x128>(v);  // row_ror:8 -- lane i+8 mod 16, i.e. i ^ 8
+    } else {
+        float x = v, y = v;
+        if constexpr (B == 4) swap16(x, y);
+        else swap32(x, y);
+        return x + y;
+    }
+}
+
+// Sum over all 64 lanes, the same bits in every lane.
+__device__ __forceinline__ float wave_total(float v)
+{
+    v = group_sum<16>(v);
+    return pair_sum<5>(pair_sum<4>(v));
+}
+
+// How the column sums over the row-group lane bits are split: halving on
+// lane bit 5, then on bit 4, while the lane still carries >= 2 columns; the
+// remaining row-group bits are summed in place.  After the exchange a lane
+// carries LC consecutive columns starting at col0().
+template <int P, int L>
+struct ColExchange {
+    static constexpr int LOGP = P == 1 ? 0 : P == 2 ? 1 : P == 4 ? 2 : P == 8 ? 3 : 4;
+    static_assert(P == 4 || P == 8, "row-group bits must include bits 3..5");
+    static constexpr bool H5 = L >= 2;
+    static constexpr int L1 = H5 ? L / 2 : L;
+    static constexpr bool H4 = L1 >= 2;
+    static constexpr int LC = H4 ? L1 / 2 : L1;
+    // row-group bits summed in place: bits LOGP..3, plus 4 and 5 when not halved
+    static constexpr int KEEP_MASK = ((1 << 4) - (1 << LOGP)) | (H4 ? 0 : 16) | (H5 ? 0 : 32);
+
+    template <int N>
+    __device__ __forceinline__ static void run(float (&v)[N][L])
+    {
+        if constexpr (H5) {
+#pragma unroll
+            for (int a = 0; a < N; ++a)
+#pragma unroll
+                for (int c = 0; c < L / 2; ++c) {
+                    float x = v[a][c], y = v[a][c + L / 2];
+                    swap32(x, y);
+                    v[a][c] = x + y;
+                }
+        }
+        if constexpr (H4) {
+#pragma unroll
+            for (int a = 0; a < N; ++a)
+#pragma unroll
+                for (int c = 0; c < L1 / 2; ++c) {
+                    float x = v[a][c], y = v[a][c + L1 / 2];
+                    swap16(x, y);
+                    v[a][c] = x + y;
+                }
+        }
+#pragma unroll
+        for (int a = 0; a < N; ++a)
+#pragma unroll
+            for (int c = 0; c < LC; ++c) v[a][c] = keep_sum(v[a][c]);
+    }
+
+    __device__ __forceinline__ static float keep_sum(float x)
+    {
+        if constexpr (LOGP == 2) {
+            x += dpp<0x128>(x);  // bit 3 (row_ror:8)
+            x += dpp<0x124>(x);  // then bit 2 (row_ror:4): the four lanes i + 4k of a DPP row
+        } else {
+            x = pair_sum<3>(x);
+        }
+        if constexpr (!H4) x = pair_sum<4>(x);
+        if constexpr (!H5) x = pair_sum<5>(x);
+        return x;
+    }
+
+    __device__ __forceinline__ static int col0(int lane)
+    {
+        const int p = lane % P;
+        return p * L + (H5 ? ((lane >> 5) & 1) * (L / 2) : 0) + (H4 ? ((lane >> 4) & 1) * (L1 / 2) : 0);
+    }
+    __device__ __forceinline__ static bool writer(int lane) { return (lane & KEEP_MASK) == 0; }
+};
+
+template <int D_IN, int D_OUT, int NW, int P, int NLR, bool BF16>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * kWave, NW * kWave), amdgpu_waves_per_eu(2)))
+void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin,
+                     const float* __restrict__ tape, const float* __restrict__ gy,
+                     const float* __restrict__ gWT, float* __restrict__ dx,
+                     float* __restrict__ dWinit, int T, int H, int in_softmax)
+{
+    constexpr int NT = NW * kWave;
+    constexpr int M = D_OUT + 2 * D_IN + NLR;
+    constexpr int MAIN = D_OUT + 2 * D_IN;
+    constexpr int L = D_IN / P;
+    constexpr int G = NT / P;
+    constexpr int R = (M + G - 1) / G;
+    using TL = TapeLayout<M, D_IN>;
+    using CX = ColExchange<P, L>;
+    constexpr int TW = TL::ROW;
+    constexpr int TPL = (TW + NT - 1) / NT;
+    static_assert(D_IN % P == 0 && D_IN % G == 0 && D_OUT % G == 0, "row blocks must align with row groups");
+    static_assert(D_IN <= kWave && D_OUT <= NT, "one lane per column, one thread per output");
+    static_assert(D_IN % 4 == 0, "16-byte tape pieces");
+    static_assert((NW & (NW - 1)) == 0, "power-of-two waves");
+
+    __shared__ __attribute__((aligned(16))) float s_tape[3][TW];
+    __shared__ __attribute__((aligned(16))) float s_u[3][D_IN];
+    __shared__ __attribute__((aligned(16))) float s_gy[3][D_OUT];
+    __shared__ __attribute__((aligned(16))) float4 s_red[2][NW][D_IN];  // khh, eh, uh partials per wave
+    __shared__ __attribute__((aligned(16))) float4 s_bred[2][NW];       // betah partials per wave
+    __shared__ __attribute__((aligned(16))) float s_zh[NW][M];          // each wave's own zh rows
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = NW == 1 ? 0 : tid / kWave;
+    const int p = tid % P;
+    const int rg = tid / P;
+    const int unit = blockIdx.x;
+    const int b = unit / H;
+    const int h = unit - b * H;
+    const int64_t x_step = (int64_t)H * D_IN;
+    const int64_t y_step = (int64_t)H * D_OUT;
+    const int64_t x0 = ((int64_t)b * T * H + h) * D_IN;
+    const int64_t y0 = ((int64_t)b * T * H + h) * D_OUT;
+    const float* __restrict__ tp0 = tape + (int64_t)unit * T * TW;
+
+    // Learning-rate index of register r (the row block; 0 with one rate).
+    auto rate = [](int r) constexpr {
+        const int row = G * r;
+        return NLR == 1 ? 0 : row < D_OUT ? 0 : row < D_OUT + D_IN ? 1 : row < MAIN ? 2 : 3;
+    };
+
+    // W <- W_T, Wh <- dL/dW_T (or 0)
+    float w[R][L], wh[R][L];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int row = rg + G * r;
+        if (row < M) {
+            load_f32<L>(WTin + ((int64_t)unit * M + row) * D_IN + p * L, w[r]);
+            if (gWT != nullptr) {
+                load_f32<L>(gWT + ((int64_t)unit * M + row) * D_IN + p * L, wh[r]);
+            } else {
+#pragma unroll
+                for (int c = 0; c < L; ++c) wh[r][c] = 0.f;
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < L; ++c) w[r][c] = wh[r][c] = 0.f;
+        }
+    }
+
+    // Step inputs are fetched two steps ahead into registers and staged one
+    // step ahead into the LDS ring: tape row, u_t (x_t widened, softmax-ed
+    // when the forward pass did), gy_t.
+    float tnext[TPL];
+    float xnext = 0.f, gnext = 0.f;
+    auto fetch = [&](int t) {
+        const float* __restrict__ tp = tp0 + (int64_t)t * TW;
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) {
+            const int j = tid + NT * i;
+            tnext[i] = (j < TW) ? tp[j] : 0.f;
+        }
+        if (wave == 0 && lane < D_IN) {
+            if constexpr (BF16)
+                xnext = bf16_to_f32(reinterpret_cast<const uint16_t*>(xv)[x0 + (int64_t)t * x_step + lane]);
+            else
+                xnext = reinterpret_cast<const float*>(xv)[x0 + (int64_t)t * x_step + lane];
+        }
+        if (tid < D_OUT) gnext = gy[y0 + (int64_t)t * y_step + tid];
+    };
+    auto stage = [&](int slot) {
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) {
+            const int j = tid + NT * i;
+            if (j < TW) s_tape[slot][j] = tnext[i];
+        }
+        if (wave == 0) {
+            float uv = xnext;
+            if (in_softmax) {
+                const float mx = wave_max(lane < D_IN ? xnext : -INFINITY);
+                const float ev = lane < D_IN ? exp_f32(xnext - mx) : 0.f;
+                uv = ev * rcp_f32(wave_total(ev));
+            }
+            if (lane < D_IN) s_u[slot][lane] = uv;
+        }
+        if (tid < D_OUT) s_gy[slot][tid] = gnext;
+    };
+
+    // The exchange: this lane's column partials of khh, eh and uh (and the
+    // betah partials) -> LDS area `par`.
+    float part[3][L];
+    auto exchange = [&](int par, float (&bp)[4]) {
+        CX::run(part);
+        if (CX::writer(lane)) {
+            const int c0 = CX::col0(lane);
+#pragma unroll
+            for (int c = 0; c < CX::LC; ++c) s_red[par][wave][c0 + c] = make_float4(part[0][c], part[1][c], part[2][c], 0.f);
+        }
+#pragma unroll
+        for (int c = 0; c < NLR; ++c) {
+            // only lanes with p == 0 hold betah partials: sum over the row-group bits
+            float v = bp[c];
+            if constexpr (P == 4) {
+                v += dpp<0x128>(v);
+                v += dpp<0x124>(v);
+            } else {
+                v = pair_sum<3>(v);
+            }
+            bp[c] = pair_sum<5>(pair_sum<4>(v));
+        }
+        if (lane == 0) s_bred[par][wave] = make_float4(bp[0], bp[1], bp[2], bp[3]);
+    };
+    // Column j's totals over the unit (lane j of every wave).
+    auto gather = [&](int par, float& khh_j, float& eh_j, float& uh_j) {
+        khh_j = eh_j = uh_j = 0.f;
+        if (lane < D_IN) {
+#pragma unroll
+            for (int wv = 0; wv < NW; ++wv) {
+                const float4 v = s_red[par][wv][lane];
+                khh_j += v.x;
+                eh_j += v.y;
+                uh_j += v.z;
+            }
+        }
+    };
+    // dx of a step from its uh (column j in lane j) and u_j.
+    auto store_dx = [&](int t, float uh_j, float u_j) {
+        float d = uh_j;
+        if (in_softmax) {
+            const float du = wave_total(lane < D_IN ? uh_j * u_j : 0.f);
+            d = u_j * (uh_j - du);
+        }
+        if (lane < D_IN) dx[x0 + (int64_t)t * x_step + lane] = d;
+    };
+
+#pragma unroll
+    for (int a = 0; a < 3; ++a)
+#pragma unroll
+        for (int c = 0; c < L; ++c) part[a][c] = 0.f;
+    float u_next = 0.f;  // u_{t+1}[lane]
+
+    if (T > 0) {
+        fetch(T - 1);
+        stage((T - 1) % 3);
+        if (T > 1) fetch(T - 2);
+        __syncthreads();
+    }
+
+    int slot = (T - 1) % 3;
+    for (int t = T - 1; t >= 0; --t) {
+        const float* __restrict__ tt = s_tape[slot];
+        const float* __restrict__ us = s_u[slot];
+        const float* __restrict__ gs = s_gy[slot];
+        const int par = t & 1;
+
+        // ---- (A) undo the update of step t; ah, khh, rh, eh.
+        float a[R], kt[L];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = rg + G * r;
+            a[r] = row < M ? tt[row] : 0.f;
+        }
+        load_f32<L>(tt + TL::KH_OFF + p * L, kt);
+        const float4 gv = *reinterpret_cast<const float4*>(tt + TL::G_OFF);
+        const float gate[4] = {gv.x, gv.y, gv.z, gv.w};
+
+        float khh[L], ah[R];
+#pragma unroll
+        for (int c = 0; c < L; ++c) khh[c] = 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float as = 0.f;
+#pragma unroll
+            for (int c = 0; c < L; ++c) {
+                w[r][c] = fmaf(-a[r], kt[c], w[r][c]);
+                as = fmaf(wh[r][c], kt[c], as);
+                khh[c] = fmaf(wh[r][c], a[r], khh[c]);
+            }
+            ah[r] = group_sum<P>(as);
+        }
+        float bp[4] = {0.f, 0.f, 0.f, 0.f};
+        float rh[R], eh[L];
+#pragma unroll
+        for (int c = 0; c < L; ++c) eh[c] = 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            rh[r] = gate[rate(r)] * ah[r];
+            bp[rate(r)] += (p == 0) ? ah[r] * a[r] : 0.f;  // each row once
+#pragma unroll
+            for (int c = 0; c < L; ++c) eh[c] = fmaf(w[r][c], rh[r], eh[c]);
+        }
+        // part[2] holds uh of step t+1 (zero before the first step)
+#pragma unroll
+        for (int c = 0; c < L; ++c) {
+            part[0][c] = khh[c];
+            part[1][c] = eh[c];
+        }
+        exchange(par, bp);
+
+        // stage the inputs of step t-1 (two slots away from anything in use)
+        const int slot_prev = slot == 0 ? 2 : slot - 1;
+        if (t > 0) {
+            stage(slot_prev);
+            if (t > 1) fetch(t - 2);
+        }
+        __syncthreads();
+
+        // ---- (B) per column (lane j): totals, dx of step t+1, kbar, qbar, betah.
+        float khh_j, eh_j, uh1_j;
+        gather(par, khh_j, eh_j, uh1_j);
+        if (t + 1 < T && wave == ((t + 1) & (NW - 1))) store_dx(t + 1, uh1_j, u_next);
+        u_next = lane < D_IN ? us[lane] : 0.f;
+        {
+            float4 bt = s_bred[par][0];
+#pragma unroll
+            for (int wv = 1; wv < NW; ++wv) {
+                const float4 v = s_bred[par][wv];
+                bt.x += v.x;
+                bt.y += v.y;
+                bt.z += v.z;
+                bt.w += v.w;
+            }
+            const float kh_j = lane < D_IN ? tt[TL::KH_OFF + lane] : 0.f;
+            const float e_j = lane < D_IN ? tt[TL::E_OFF + lane] : 0.f;
+            const float qh_j = kh_j + e_j;
+            const float kb = khh_j - eh_j;
+            const float dk = wave_total(kb * kh_j);
+            const float dq = wave_total(eh_j * qh_j);
+            if (lane < D_IN) {
+                s_zh[wave][D_OUT + lane] = kh_j * (kb - dk);
+                s_zh[wave][D_OUT + D_IN + lane] = qh_j * (eh_j - dq);
+            }
+            if (lane < NLR) {
+                const float bv = lane == 0 ? bt.x : lane == 1 ? bt.y : lane == 2 ? bt.z : bt.w;
+                const float gl = lane == 0 ? gate[0] : lane == 1 ? gate[1] : lane == 2 ? gate[2] : gate[3];
+                s_zh[wave][MAIN + lane] = (1.f - gl) * bv;
+            }
+        }
+        wave_sync();
+
+        // ---- (C) uh of step t (column partials, reduced with step t-1); Wh update.
+        float ev[L], uv[L];
+        load_f32<L>(tt + TL::E_OFF + p * L, ev);
+        load_f32<L>(us + p * L, uv);
+#pragma unroll
+        for (int c = 0; c < L; ++c) part[2][c] = 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = rg + G * r;
+            float zr;
+            if (G * r < D_OUT) zr = gs[row];
+            else zr = row < M ? s_zh[wave][row] : 0.f;
+#pragma unroll
+            for (int c = 0; c < L; ++c) {
+                part[2][c] = fmaf(w[r][c], zr, part[2][c]);
+                wh[r][c] = fmaf(rh[r], ev[c], fmaf(zr, uv[c], wh[r][c]));
+            }
+        }
+        slot = slot_prev;
+    }
+
+    if (T > 0) {
+        // uh of step 0: one more exchange (no khh, eh, betah)
+        float bp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < L; ++c) part[0][c] = part[1][c] = 0.f;
+        exchange(1, bp);
+        __syncthreads();
+        float khh_j, eh_j, uh0_j;
+        gather(1, khh_j, eh_j, uh0_j);
+        if (wave == 0) store_dx(0, uh0_j, u_next);
+    }
+
+    // dL/d(initial state of this unit)
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int row = rg + G * r;
+        if (row < M) store_f32<L>(dWinit + ((int64_t)unit * M + row) * D_IN + p * L, wh[r]);
+    }
+}
+
+// dW0[h] = sum_b dWinit[b][h] (the gradient of the initial matrix shared over
+// the batch), summed in a fixed order b = 0, 1, ...
+__global__ __launch_bounds__(256) void srwm_sum_over_batch_kernel(const float* __restrict__ dWinit,
+                                                                  float* __restrict__ dW0, int64_t B,
+                                                                  int64_t per_b)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= per_b) return;
+    float s = 0.f;
+    for (int64_t b = 0; b < B; ++b) s += dWinit[b * per_b + i];
+    dW0[i] = s;
+}
+
+}  // namespace srwm

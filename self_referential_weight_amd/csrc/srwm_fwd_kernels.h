@@ -1,0 +1,739 @@
+// srwm_fwd_kernels.h -- the forward kernels of libsrwm (device code only):
+// the phased and the fused-schedule SRWM recurrence and the geometry and
+// staging helpers they use.  Included by srwm_fwd.hip, which holds the
+// variant table and the C ABI.  The design notes are at the top of that file.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "srwm_device.h"
+
+namespace srwm {
+
+// ----------------------------------------------------------------------------
+// Compile-time geometry of one kernel variant.
+//
+// Main rows (the y, k and q blocks, MAIN = d_out + 2*d_in rows) use the
+// strided lane layout described at the top of the file.  The NLR rate rows
+// (four, or one in the one-rate form) use one of two layouts:
+//   BETA_SEP (d_in % 16 == 0): wave 0 holds them, DPP row i (lanes 16i..16i+15)
+//     holding rate row i, LB = d_in/16 consecutive columns per lane; a rate
+//     row's dot product is then a 16-lane DPP sum inside one DPP row, and the
+//     lanes that need its learning-rate term are the ones that computed it.
+//     With one rate, DPP rows 1-3 hold zeros and store nothing.
+//   otherwise: they are appended to the main rows (one extra register row,
+//     zero padded), which only the small test shapes use.
+template <int D_IN, int D_OUT, int NW, int P, int NLR = 4>
+struct Geom {
+    static_assert(NLR == 1 || NLR == 4, "one or four learning rates");
+    static constexpr int NT = NW * kWave;            // threads per unit
+    static constexpr int M = D_OUT + 2 * D_IN + NLR; // rows of W
+    static constexpr int MAIN = D_OUT + 2 * D_IN;  // y, k, q rows
+    static constexpr bool BETA_SEP = (D_IN % 16 == 0);
+    static constexpr int ROWS = BETA_SEP ? MAIN : M; // rows in the strided layout
+    static constexpr int L = D_IN / P;             // columns per lane
+    static constexpr int G = NT / P;               // row groups
+    static constexpr int R = (ROWS + G - 1) / G;   // rows per lane
+    static constexpr bool ALIGNED = (D_IN % G == 0) && (D_OUT % G == 0);
+    static constexpr int LB = BETA_SEP ? D_IN / 16 : 0; // beta columns per lane
+    // x staging: E consecutive elements per lane, LR lanes per step row.
+    // Aim for 32 step rows per chunk (8 for one-wave units, whose registers
+    // are scarcer) with every lane loading, at most 16 and at least d_in/16
+    // elements per lane (so a row spans <= 16 lanes).
+    static constexpr int E_TARGET = ((NW == 1 ? 8 : 32) * D_IN) / NT;
+    static constexpr int E_LO = D_IN / 16 > E_TARGET ? D_IN / 16 : E_TARGET;
+    static constexpr int E = D_IN < 16 ? D_IN : (E_LO < 16 ? (E_LO < 1 ? 1 : E_LO) : 16);
+    static constexpr int LR = D_IN / E;
+    static constexpr int S_FULL = NT / LR;
+    static constexpr int S = S_FULL < 32 ? S_FULL : 32; // steps per chunk
+    static_assert(D_IN % P == 0, "P must divide d_in");
+    static_assert(D_IN % E == 0, "E must divide d_in");
+    static_assert(LR <= 16 && (LR & (LR - 1)) == 0, "row lanes");
+    static_assert(G >= 4, "need at least four row groups");
+    // Learning-rate index of register r when ALIGNED: the row block (0 y,
+    // 1 k, 2 q, 3 beta) with four rates, 0 with one.
+    static constexpr int rate_of_reg(int r)
+    {
+        const int row = G * r;
+        if (NLR == 1) return 0;
+        return row < D_OUT ? 0 : row < D_OUT + D_IN ? 1 : row < D_OUT + 2 * D_IN ? 2 : 3;
+    }
+};
+
+template <int NLR>
+__device__ __forceinline__ int rate_of_row(int row, int d_in, int d_out)
+{
+    if (NLR == 1) return 0;
+    return row < d_out ? 0 : row < d_out + d_in ? 1 : row < d_out + 2 * d_in ? 2 : 3;
+}
+
+// phi(k) and phi(q) by one wave: k and q are d-vectors in LDS; lanes take
+// entries lane, lane+64, ...  Writes kh = softmax(k) and e = softmax(q) - kh,
+// the difference the fused read of Eq. (2) needs.  The two reductions are
+// interleaved for ILP.
+template <int D>
+__device__ __forceinline__ void wave_addresses(const float* __restrict__ k, const float* __restrict__ q,
+                                               float* __restrict__ kh_out, float* __restrict__ e_out,
+                                               int lane)
+{
+    constexpr int EPL = (D + 63) / 64;
+    float a[EPL], b[EPL];
+    float ma = -INFINITY, mb = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int j = lane + 64 * i;
+        a[i] = (j < D) ? k[j] : -INFINITY;
+        b[i] = (j < D) ? q[j] : -INFINITY;
+        ma = fmax2(ma, a[i]);
+        mb = fmax2(mb, b[i]);
+    }
+    ma = wave_max(ma);
+    mb = wave_max(mb);
+    float sa = 0.f, sb = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int j = lane + 64 * i;
+        a[i] = (j < D) ? exp_f32(a[i] - ma) : 0.f;
+        b[i] = (j < D) ? exp_f32(b[i] - mb) : 0.f;
+        sa += a[i];
+        sb += b[i];
+    }
+    const float ia = rcp_f32(wave_sum(sa));
+    const float ib = rcp_f32(wave_sum(sb));
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int j = lane + 64 * i;
+        if (j < D) {
+            // Both probabilities are rounded before the difference (no fused
+            // multiply-subtract), so k_t == q_t gives e == 0 exactly.
+#pragma clang fp contract(off)
+            const float kh = a[i] * ia;
+            const float qh = b[i] * ib;
+            kh_out[j] = kh;
+            e_out[j] = qh - kh;
+        }
+    }
+}
+
+// Width of the LDS vector pieces streamed through the FMA loops.
+template <int N>
+struct Piece {
+    static constexpr int W = N % 4 == 0 ? 4 : N % 2 == 0 ? 2 : 1;
+};
+
+// Stream src[0..N) from LDS in pieces of Piece<N>::W floats through
+// body(c, value), double-buffered: piece k+1 is requested before piece k is
+// consumed, and a scheduling barrier after each piece keeps the compiler from
+// hoisting later pieces (which would hold the whole vector in VGPRs).
+template <int N, class F>
+__device__ __forceinline__ void stream_lds(const float* __restrict__ src, F&& body)
+{
+    constexpr int VW = Piece<N>::W;
+    constexpr int NPC = N / VW;
+    float cur[VW];
+    load_f32<VW>(src, cur);
+#pragma unroll
+    for (int k = 0; k < NPC; ++k) {
+        float nxt[VW];
+        if (k + 1 < NPC) load_f32<VW>(src + (k + 1) * VW, nxt);
+#pragma unroll
+        for (int c = 0; c < VW; ++c) body(k * VW + c, cur[c]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (k + 1 < NPC) {
+#pragma unroll
+            for (int c = 0; c < VW; ++c) cur[c] = nxt[c];
+        }
+    }
+}
+
+// x staging.  S step rows of x for one unit are loaded one chunk ahead into
+// registers (lane tid < S*LR takes E consecutive elements of row tid/LR), then
+// widened (bf16 -> f32 is exact), optionally softmax-ed per row, and written
+// to an LDS tile.
+template <int D_IN, int D_OUT, int NW, int P, bool BF16>
+struct XStage {
+    using Gm = Geom<D_IN, D_OUT, NW, P>;
+    static constexpr int E = Gm::E, LR = Gm::LR, S = Gm::S;
+    static constexpr int XR = BF16 ? (E + 1) / 2 : E; // registers held per lane
+    using XT = typename std::conditional<BF16, uint16_t, float>::type;
+    uint32_t xr[XR];
+    int row, col;
+    uint32_t lane_off;  // element offset of this lane's piece within a chunk
+    bool active;
+    const XT* __restrict__ xu;  // x[b][0][h][0] (wave-uniform)
+    int64_t x_step;
+    int T;
+
+    __device__ __forceinline__ XStage(int tid, const void* __restrict__ xv_, int64_t x0_, int64_t x_step_, int T_)
+        : row(tid / LR), col((tid % LR) * E), active(tid < S * LR),
+          xu(reinterpret_cast<const XT*>(xv_) + x0_), x_step(x_step_), T(T_)
+    {
+        lane_off = static_cast<uint32_t>(row * x_step + col);
+    }
+
+    // Issue the global loads of the chunk that starts at step c0.
+    __device__ __forceinline__ void load(int c0)
+    {
+        const int t = c0 + row;
+        if (active && t < T) {
+            const XT* src = xu + (int64_t)c0 * x_step + lane_off;
+            if constexpr (BF16) {
+                if constexpr (E % 8 == 0) {
+#pragma unroll
+                    for (int i = 0; i < E / 8; ++i) {
+                        const uint4 v = reinterpret_cast<const uint4*>(src)[i];
+                        xr[4 * i + 0] = v.x;
+                        xr[4 * i + 1] = v.y;
+                        xr[4 * i + 2] = v.z;
+                        xr[4 * i + 3] = v.w;
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < XR; ++i) {
+                        const uint32_t lo = src[2 * i];
+                        const uint32_t hi = (2 * i + 1 < E) ? src[2 * i + 1] : 0u;
+                        xr[i] = lo | (hi << 16);
+                    }
+                }
+            } else {
+                float tmp[E];
+                load_f32<E>(src, tmp);
+#pragma unroll
+                for (int i = 0; i < E; ++i) xr[i] = __float_as_uint(tmp[i]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < XR; ++i) xr[i] = 0u;
+        }
+    }
+
+    // Widen, apply the optional input softmax per step row, write to LDS.
+    __device__ __forceinline__ void stage(float (*dst)[D_IN], int in_softmax)
+    {
+        float v[E];
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+            if constexpr (BF16)
+                v[i] = __uint_as_float((i & 1) ? (xr[i >> 1] & 0xffff0000u) : (xr[i >> 1] << 16));
+            else
+                v[i] = __uint_as_float(xr[i]);
+        }
+        if (in_softmax) {
+            float mx = v[0];
+#pragma unroll
+            for (int i = 1; i < E; ++i) mx = fmax2(mx, v[i]);
+            mx = group_max<LR>(mx);
+            float sum = 0.f;
+#pragma unroll
+            for (int i = 0; i < E; ++i) {
+                v[i] = exp_f32(v[i] - mx);
+                sum += v[i];
+            }
+            const float inv = rcp_f32(group_sum<LR>(sum));
+#pragma unroll
+            for (int i = 0; i < E; ++i) v[i] *= inv;
+        }
+        if (active) store_f32<E>(&dst[row][col], v);
+    }
+};
+
+// Store y_t = z[0:d_out] (one wave; lanes take consecutive entries).
+template <int D_OUT, bool BF16>
+__device__ __forceinline__ void store_y(void* __restrict__ yv, int64_t off, const float* __restrict__ z, int lane)
+{
+#pragma unroll
+    for (int j0 = 0; j0 < D_OUT; j0 += kWave) {
+        const int j = j0 + lane;
+        if (j < D_OUT) {
+            if constexpr (BF16)
+                reinterpret_cast<uint16_t*>(yv)[off + j] = f32_to_bf16(z[j]);
+            else
+                reinterpret_cast<float*>(yv)[off + j] = z[j];
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// The kernel: grid = B*H workgroups (unit = b*H + h), NW*64 threads each.
+// WPE is the occupancy (waves per SIMD) the register allocation must allow.
+template <int D_IN, int D_OUT, int NW, int P, int WPE, int NLR, bool RESET, bool TAPE, bool BF16>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * kWave, NW * kWave),
+                          amdgpu_waves_per_eu(WPE)))
+void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
+                     void* __restrict__ yv, float* __restrict__ WT, float* __restrict__ tape,
+                     int T, int H, int in_softmax, int w0_per_seq, int reset_interval)
+{
+    using Gm = Geom<D_IN, D_OUT, NW, P, NLR>;
+    constexpr int M = Gm::M, MAIN = Gm::MAIN, ROWS = Gm::ROWS;
+    constexpr int L = Gm::L, G = Gm::G, R = Gm::R, LB = Gm::LB;
+    constexpr int S = Gm::S;
+    constexpr bool BETA_SEP = Gm::BETA_SEP;
+
+    __shared__ __attribute__((aligned(16))) float s_x[2][S][D_IN];
+    // z_t, double-buffered by step parity so one barrier per step suffices.
+    __shared__ __attribute__((aligned(16))) float s_z[2][R * G + 4];
+    // Each wave forms phi(k_t) and phi(q_t) - phi(k_t) itself, in its own slice.
+    __shared__ __attribute__((aligned(16))) float s_kh[NW][D_IN];
+    __shared__ __attribute__((aligned(16))) float s_e[NW][D_IN];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = NW == 1 ? 0 : tid / kWave;
+    const int p = tid % P;
+    const int rg = tid / P;
+    const int unit = blockIdx.x;
+    const int b = unit / H;
+    const int h = unit - b * H;
+
+    // Element offsets.  x[b][t][h][:] = x0 + t*x_step.
+    const int64_t x_step = (int64_t)H * D_IN;
+    const int64_t y_step = (int64_t)H * D_OUT;
+    const int64_t x0 = ((int64_t)b * T * H + h) * D_IN;
+    const int64_t y0 = ((int64_t)b * T * H + h) * D_OUT;
+    const float* __restrict__ w0h = W0 + (int64_t)(w0_per_seq ? unit : h) * M * D_IN;
+
+    // ---- a0: W <- W0 into registers (again at each reset of the ablation).
+    float w[R][L];
+    const int bcol = (lane & 15) * (LB > 0 ? LB : 1);
+    const int brow = lane >> 4;
+    float wb[LB > 0 ? LB : 1];
+    auto load_w0 = [&]() {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = rg + G * r;
+            if (row < ROWS) {
+                load_f32<L>(w0h + (int64_t)row * D_IN + p * L, w[r]);
+            } else {
+#pragma unroll
+                for (int c = 0; c < L; ++c) w[r][c] = 0.f;
+            }
+        }
+        if constexpr (BETA_SEP) {
+            if (wave == 0) {
+                if (brow < NLR) {
+                    load_f32<LB>(w0h + (int64_t)(MAIN + brow) * D_IN + bcol, wb);
+                } else {
+#pragma unroll
+                    for (int c = 0; c < LB; ++c) wb[c] = 0.f;
+                }
+            }
+        }
+    };
+    load_w0();
+
+    XStage<D_IN, D_OUT, NW, P, BF16> xs(tid, xv, x0, x_step, T);
+
+    // The wave that stores y_t.
+    constexpr int WAVE_AUX = NW >= 2 ? 1 : 0;
+
+    if (T > 0) {
+        xs.load(0);
+        xs.stage(s_x[0], in_softmax);
+        if (T > S) xs.load(S);
+        __syncthreads();
+
+        int chunk = 0;
+        int until_reset = reset_interval;  // steps left before the next reset
+        (void)until_reset;
+        for (int c0 = 0; c0 < T; c0 += S, ++chunk) {
+            const int n = (T - c0) < S ? (T - c0) : S;
+            const float* sxc = &s_x[chunk & 1][0][0];
+            for (int s = 0; s < n; ++s) {
+                const int t = c0 + s;
+                const float* __restrict__ urow = sxc + s * D_IN;
+                if constexpr (RESET) {
+                    // Reset ablation of the review page (Sec. 4.5): before every
+                    // step t > 0 with t % R == 0 the state returns to W0.
+                    if (reset_interval > 0) {
+                        if (until_reset == 0) {
+                            load_w0();
+                            until_reset = reset_interval;
+                        }
+                        --until_reset;
+                    }
+                }
+                // ---- (A) Eq. (1): z = W u.
+                float* __restrict__ zt = s_z[t & 1];
+                float acc[R];
+#pragma unroll
+                for (int r = 0; r < R; ++r) acc[r] = 0.f;
+                stream_lds<L>(urow + p * L, [&](int c, float uc) {
+#pragma unroll
+                    for (int r = 0; r < R; ++r) acc[r] = fmaf(w[r][c], uc, acc[r]);
+                });
+#pragma unroll
+                for (int r = 0; r < R; ++r) acc[r] = group_sum<P>(acc[r]);
+                // All P lanes of a row group hold the same sums; lane p stores
+                // registers r = p, p+P, ... (one LDS store per P registers).
+#pragma unroll
+                for (int r0 = 0; r0 < R; r0 += P) {
+                    float v = acc[r0];
+#pragma unroll
+                    for (int q = 1; q < P && r0 + q < R; ++q) v = (p == q) ? acc[r0 + q] : v;
+                    const int row = rg + G * (r0 + p);
+                    if ((r0 + P <= R || r0 + p < R) && (Gm::ALIGNED || row < ROWS)) zt[row] = v;
+                }
+                if constexpr (BETA_SEP) {
+                    if (wave == 0) {
+                        float accb = 0.f;
+                        stream_lds<LB>(urow + bcol, [&](int c, float uc) { accb = fmaf(wb[c], uc, accb); });
+                        accb = group_sum<16>(accb);
+                        if ((lane & 15) == 0 && brow < NLR) zt[MAIN + brow] = accb;
+                    }
+                }
+                __syncthreads();
+
+                // ---- (B) phi(k), phi(q), sigma(beta), computed by every wave for
+                // itself (identical bits in every wave); y_t from W_{t-1}.
+                wave_addresses<D_IN>(zt + D_OUT, zt + D_OUT + D_IN, s_kh[wave], s_e[wave], lane);
+                const float gl = sigmoid_f32(zt[MAIN + (NLR == 4 ? (lane & 3) : 0)]);
+                const float g0 = readlane(gl, 0), g1 = readlane(gl, 1), g2 = readlane(gl, 2), g3 = readlane(gl, 3);
+                if (wave == WAVE_AUX) store_y<D_OUT, BF16>(yv, y0 + (int64_t)t * y_step, zt, lane);
+                wave_sync();
+                const float* __restrict__ khw = s_kh[wave];
+                const float* __restrict__ ew = s_e[wave];
+
+                // ---- (C) Eq. (2)/(4) fused: W (qh - kh) = v - vb, times the gate.
+#pragma unroll
+                for (int r = 0; r < R; ++r) acc[r] = 0.f;
+                stream_lds<L>(ew + p * L, [&](int c, float ec) {
+#pragma unroll
+                    for (int r = 0; r < R; ++r) acc[r] = fmaf(w[r][c], ec, acc[r]);
+                });
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    float gate;
+                    if constexpr (Gm::ALIGNED) {
+                        const int bk = Gm::rate_of_reg(r);
+                        gate = bk == 0 ? g0 : bk == 1 ? g1 : bk == 2 ? g2 : g3;
+                    } else {
+                        const int bk = rate_of_row<NLR>(rg + G * r, D_IN, D_OUT);
+                        gate = bk == 0 ? g0 : bk == 1 ? g1 : bk == 2 ? g2 : g3;
+                    }
+                    acc[r] = gate * group_sum<P>(acc[r]);
+                }
+                float accb = 0.f;
+                if constexpr (BETA_SEP) {
+                    if (wave == 0) {
+                        stream_lds<LB>(ew + bcol, [&](int c, float ec) { accb = fmaf(wb[c], ec, accb); });
+                        accb = g3 * group_sum<16>(accb);
+                    }
+                }
+                if constexpr (TAPE) {
+                    // Tape for the backward pass: a_t, phi(k_t) (enough to undo the
+                    // update, W_{t-1} = W_t - a_t phi(k_t)^T), phi(q_t) - phi(k_t) and
+                    // the learning rates (so the backward needs no projection).
+                    using TL = TapeLayout<M, D_IN>;
+                    float* __restrict__ tp = tape + ((int64_t)unit * T + t) * TL::ROW;
+#pragma unroll
+                    for (int r0 = 0; r0 < R; r0 += P) {
+                        float v = acc[r0];
+#pragma unroll
+                        for (int q = 1; q < P && r0 + q < R; ++q) v = (p == q) ? acc[r0 + q] : v;
+                        const int row = rg + G * (r0 + p);
+                        if ((r0 + P <= R || r0 + p < R) && row < ROWS) tp[row] = v;
+                    }
+                    if constexpr (BETA_SEP) {
+                        if (wave == 0 && (lane & 15) == 0 && brow < NLR) tp[MAIN + brow] = accb;
+                    }
+                    if (wave == 0) {
+#pragma unroll
+                        for (int j0 = 0; j0 < D_IN; j0 += kWave) {
+                            if (j0 + lane < D_IN) {
+                                tp[TL::KH_OFF + j0 + lane] = khw[j0 + lane];
+                                tp[TL::E_OFF + j0 + lane] = ew[j0 + lane];
+                            }
+                        }
+                        if (lane < 4) tp[TL::G_OFF + lane] = lane < NLR ? gl : 0.f;
+                    }
+                }
+                // ---- (D) Eq. (3)/(5): W += a kh^T, in place.
+                stream_lds<L>(khw + p * L, [&](int c, float kc) {
+#pragma unroll
+                    for (int r = 0; r < R; ++r) w[r][c] = fmaf(acc[r], kc, w[r][c]);
+                });
+                if constexpr (BETA_SEP) {
+                    if (wave == 0)
+                        stream_lds<LB>(khw + bcol, [&](int c, float kc) { wb[c] = fmaf(accb, kc, wb[c]); });
+                }
+            }
+            if (c0 + S < T) {
+                xs.stage(s_x[(chunk + 1) & 1], in_softmax);
+                if (c0 + 2 * S < T) xs.load(c0 + 2 * S);
+                __syncthreads();
+            }
+        }
+    }
+
+    // ---- a7: W_T[b,h] <- W.
+    if (WT != nullptr) {
+        float* __restrict__ wdst = WT + (int64_t)unit * M * D_IN;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = rg + G * r;
+            if (row < ROWS) store_f32<L>(wdst + (int64_t)row * D_IN + p * L, w[r]);
+        }
+        if constexpr (BETA_SEP) {
+            if (wave == 0 && brow < NLR) store_f32<LB>(wdst + (int64_t)(MAIN + brow) * D_IN + bcol, wb);
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Fused-schedule kernel for units spread over several waves (latency-bound
+// shapes).  It computes the same recurrence with a shorter serial chain per
+// step.  The projection of step t+1 is formed from W_{t-1}, in the same pass
+// over W as the read of step t, and corrected by the rank-one update of step t:
+//     W_t u_{t+1} = W_{t-1} u_{t+1} + a_t (kh_t . u_{t+1}),   a_t = g (W_{t-1}(qh_t - kh_t)),
+// which is Eq. (3) applied to the vector u_{t+1}.  The update of W itself is
+// deferred to the next iteration, where it runs between the barrier and the
+// fused pass and fills the latency of the softmax chain.  One workgroup
+// barrier per step.
+template <int D_IN, int D_OUT, int NW, int P, int WPE, int NLR, bool BF16>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * kWave, NW * kWave),
+                          amdgpu_waves_per_eu(WPE)))
+void srwm_fwd_fused_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
+                           void* __restrict__ yv, float* __restrict__ WT, float* /*tape: not written*/,
+                           int T, int H, int in_softmax, int w0_per_seq,
+                           int /*reset_interval: not supported by this schedule*/)
+{
+    using Gm = Geom<D_IN, D_OUT, NW, P, NLR>;
+    constexpr int M = Gm::M, MAIN = Gm::MAIN, ROWS = Gm::ROWS;
+    constexpr int L = Gm::L, G = Gm::G, R = Gm::R, LB = Gm::LB;
+    constexpr int S = Gm::S;
+    constexpr bool BETA_SEP = Gm::BETA_SEP;
+    static_assert(NW >= 2, "fused schedule is for multi-wave units");
+
+    __shared__ __attribute__((aligned(16))) float s_x[2][S][D_IN];
+    __shared__ __attribute__((aligned(16))) float s_z[2][R * G + 4];
+    // phi(k_t) and phi(q_t) - phi(k_t), per wave and by step parity (the
+    // update of step t-1 still reads phi(k_{t-1}) while step t's are written).
+    __shared__ __attribute__((aligned(16))) float s_kh[2][NW][D_IN];
+    __shared__ __attribute__((aligned(16))) float s_e[NW][D_IN];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int p = tid % P;
+    const int rg = tid / P;
+    const int unit = blockIdx.x;
+    const int b = unit / H;
+    const int h = unit - b * H;
+    const int64_t x_step = (int64_t)H * D_IN;
+    const int64_t y_step = (int64_t)H * D_OUT;
+    const int64_t x0 = ((int64_t)b * T * H + h) * D_IN;
+    const int64_t y0 = ((int64_t)b * T * H + h) * D_OUT;
+    const float* __restrict__ w0h = W0 + (int64_t)(w0_per_seq ? unit : h) * M * D_IN;
+
+    // ---- a0: W <- W0[h].
+    float w[R][L];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int row = rg + G * r;
+        if (row < ROWS) {
+            load_f32<L>(w0h + (int64_t)row * D_IN + p * L, w[r]);
+        } else {
+#pragma unroll
+            for (int c = 0; c < L; ++c) w[r][c] = 0.f;
+        }
+    }
+    const int bcol = (lane & 15) * (LB > 0 ? LB : 1);
+    const int brow = lane >> 4;
+    float wb[LB > 0 ? LB : 1];
+    if constexpr (BETA_SEP) {
+        if (wave == 0) {
+            if (brow < NLR) {
+                load_f32<LB>(w0h + (int64_t)(MAIN + brow) * D_IN + bcol, wb);
+            } else {
+#pragma unroll
+                for (int c = 0; c < LB; ++c) wb[c] = 0.f;
+            }
+        }
+    }
+    float gate_of[R];  // filled per step: the learning rate of register r
+
+    if (T > 0) {
+        XStage<D_IN, D_OUT, NW, P, BF16> xs(tid, xv, x0, x_step, T);
+        xs.load(0);
+        xs.stage(s_x[0], in_softmax);
+        if (T > S) xs.load(S);
+        __syncthreads();
+
+        // ---- prologue: z_0 = W_0 u_0.
+        {
+            const float* __restrict__ u0 = &s_x[0][0][0];
+            float acc[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[r] = 0.f;
+            stream_lds<L>(u0 + p * L, [&](int c, float uc) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) acc[r] = fmaf(w[r][c], uc, acc[r]);
+            });
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                acc[r] = group_sum<P>(acc[r]);
+                const int row = rg + G * r;
+                if (p == 0 && (Gm::ALIGNED || row < ROWS)) s_z[0][row] = acc[r];
+            }
+            if constexpr (BETA_SEP) {
+                if (wave == 0) {
+                    float accb = 0.f;
+                    stream_lds<LB>(u0 + bcol, [&](int c, float uc) { accb = fmaf(wb[c], uc, accb); });
+                    accb = group_sum<16>(accb);
+                    if ((lane & 15) == 0 && brow < NLR) s_z[0][MAIN + brow] = accb;
+                }
+            }
+        }
+
+        float a_prev[R];   // a_{t-1}, applied at the start of iteration t
+        float ab_prev = 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) a_prev[r] = 0.f;
+
+        for (int t = 0; t < T; ++t) {
+            const bool has_next = t + 1 < T;
+            // chunk holding step t+1 must be in LDS before this barrier
+            if (has_next && ((t + 1) % S) == 0) {
+                xs.stage(s_x[((t + 1) / S) & 1], in_softmax);
+                if (t + 1 + S < T) xs.load(t + 1 + S);
+            }
+            __syncthreads();
+            const float* __restrict__ zt = s_z[t & 1];
+
+            // ---- (B) addresses and gates of step t (every wave), y_t.
+            float* __restrict__ khw = s_kh[t & 1][wave];
+            float* __restrict__ ew = s_e[wave];
+            wave_addresses<D_IN>(zt + D_OUT, zt + D_OUT + D_IN, khw, ew, lane);
+            const float gl = sigmoid_f32(zt[MAIN + (NLR == 4 ? (lane & 3) : 0)]);
+            const float g0 = readlane(gl, 0), g1 = readlane(gl, 1), g2 = readlane(gl, 2), g3 = readlane(gl, 3);
+            if (wave == 1) store_y<D_OUT, BF16>(yv, y0 + (int64_t)t * y_step, zt, lane);
+
+            // ---- (D) of step t-1: W_{t-2} -> W_{t-1} (overlaps the chain above).
+            if (t > 0) {
+                const float* __restrict__ khp = s_kh[(t - 1) & 1][wave];
+                float kv[L];
+                load_f32<L>(khp + p * L, kv);
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int c = 0; c < L; ++c) w[r][c] = fmaf(a_prev[r], kv[c], w[r][c]);
+                if constexpr (BETA_SEP) {
+                    if (wave == 0) {
+                        float kb[LB];
+                        load_f32<LB>(khp + bcol, kb);
+#pragma unroll
+                        for (int c = 0; c < LB; ++c) wb[c] = fmaf(ab_prev, kb[c], wb[c]);
+                    }
+                }
+            }
+            wave_sync();
+
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                if constexpr (Gm::ALIGNED) {
+                    const int bk = Gm::rate_of_reg(r);
+                    gate_of[r] = bk == 0 ? g0 : bk == 1 ? g1 : bk == 2 ? g2 : g3;
+                } else {
+                    const int bk = rate_of_row<NLR>(rg + G * r, D_IN, D_OUT);
+                    gate_of[r] = bk == 0 ? g0 : bk == 1 ? g1 : bk == 2 ? g2 : g3;
+                }
+            }
+
+            // ---- fused pass over W_{t-1}: read (e_t) and next projection (u_{t+1}).
+            const int tn = has_next ? t + 1 : t;
+            const float* __restrict__ un = &s_x[(tn / S) & 1][tn % S][0];
+            float accr[R], accz[R];
+            float cpart = 0.f;  // kh_t . u_{t+1}, this lane's columns
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                accr[r] = 0.f;
+                accz[r] = 0.f;
+            }
+            {
+                float ev[L], uv[L], kv[L];
+                load_f32<L>(ew + p * L, ev);
+                load_f32<L>(un + p * L, uv);
+                load_f32<L>(khw + p * L, kv);
+#pragma unroll
+                for (int c = 0; c < L; ++c) {
+                    cpart = fmaf(kv[c], uv[c], cpart);
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        accr[r] = fmaf(w[r][c], ev[c], accr[r]);
+                        accz[r] = fmaf(w[r][c], uv[c], accz[r]);
+                    }
+                }
+            }
+            const float ct = group_sum<P>(cpart);
+            float* __restrict__ zn = s_z[(t + 1) & 1];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float a = gate_of[r] * group_sum<P>(accr[r]);
+                a_prev[r] = a;
+                if (has_next) {
+                    const float z = fmaf(a, ct, group_sum<P>(accz[r]));
+                    const int row = rg + G * r;
+                    if (p == 0 && (Gm::ALIGNED || row < ROWS)) zn[row] = z;
+                }
+            }
+            if constexpr (BETA_SEP) {
+                if (wave == 0) {
+                    float eb[LB], ub[LB];
+                    load_f32<LB>(ew + bcol, eb);
+                    load_f32<LB>(un + bcol, ub);
+                    float br = 0.f, bz = 0.f;
+#pragma unroll
+                    for (int c = 0; c < LB; ++c) {
+                        br = fmaf(wb[c], eb[c], br);
+                        bz = fmaf(wb[c], ub[c], bz);
+                    }
+                    ab_prev = g3 * group_sum<16>(br);
+                    if (has_next) {
+                        const float z = fmaf(ab_prev, ct, group_sum<16>(bz));
+                        if ((lane & 15) == 0 && brow < NLR) zn[MAIN + brow] = z;
+                    }
+                }
+            }
+        }
+
+        // ---- (D) of the last step.
+        {
+            const float* __restrict__ khp = s_kh[(T - 1) & 1][wave];
+            float kv[L];
+            load_f32<L>(khp + p * L, kv);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int c = 0; c < L; ++c) w[r][c] = fmaf(a_prev[r], kv[c], w[r][c]);
+            if constexpr (BETA_SEP) {
+                if (wave == 0) {
+                    float kb[LB];
+                    load_f32<LB>(khp + bcol, kb);
+#pragma unroll
+                    for (int c = 0; c < LB; ++c) wb[c] = fmaf(ab_prev, kb[c], wb[c]);
+                }
+            }
+        }
+    }
+
+    // ---- a7: W_T[b,h] <- W.
+    if (WT != nullptr) {
+        float* __restrict__ wdst = WT + (int64_t)unit * M * D_IN;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = rg + G * r;
+            if (row < ROWS) store_f32<L>(wdst + (int64_t)row * D_IN + p * L, w[r]);
+        }
+        if constexpr (BETA_SEP) {
+            if (wave == 0 && brow < NLR) store_f32<LB>(wdst + (int64_t)(MAIN + brow) * D_IN + bcol, wb);
+        }
+    }
+}
+
+
+}  // namespace srwm
