@@ -166,7 +166,10 @@ void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin
     __shared__ __attribute__((aligned(16))) float s_tape[3][TW];
     __shared__ __attribute__((aligned(16))) float s_u[3][D_IN];
     __shared__ __attribute__((aligned(16))) float s_gy[3][D_OUT];
-    __shared__ __attribute__((aligned(16))) float4 s_red[2][NW][D_IN];  // khh, eh, uh partials per wave
+    // khh, eh, uh column partials per wave, one float array per quantity so that
+    // the writers (8 column slices 32 floats apart) and the readers (lane j,
+    // column j) both meet at most two-way bank conflicts
+    __shared__ __attribute__((aligned(16))) float s_red[2][NW][3][D_IN];
     __shared__ __attribute__((aligned(16))) float4 s_bred[2][NW];       // betah partials per wave
     __shared__ __attribute__((aligned(16))) float s_zh[NW][M];          // each wave's own zh rows
 
@@ -183,6 +186,11 @@ void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin
     const int64_t x0 = ((int64_t)b * T * H + h) * D_IN;
     const int64_t y0 = ((int64_t)b * T * H + h) * D_OUT;
     const float* __restrict__ tp0 = tape + (int64_t)unit * T * TW;
+
+    // Register rows r with G*(r+1) <= M hold real rows in every lane; the last
+    // one may be partial: its reads clamp the address and select 0 (no branch).
+    auto row_ok = [](int r, int row) { return G * (r + 1) <= M || row < M; };
+    auto row_at = [](int r, int row) { return G * (r + 1) <= M ? row : (row < M ? row : M - 1); };
 
     // Learning-rate index of register r (the row block; 0 with one rate).
     auto rate = [](int r) constexpr {
@@ -255,7 +263,16 @@ void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin
         if (CX::writer(lane)) {
             const int c0 = CX::col0(lane);
 #pragma unroll
-            for (int c = 0; c < CX::LC; ++c) s_red[par][wave][c0 + c] = make_float4(part[0][c], part[1][c], part[2][c], 0.f);
+            for (int a = 0; a < 3; ++a) {
+                if constexpr (CX::LC % 2 == 0) {
+#pragma unroll
+                    for (int c = 0; c < CX::LC; c += 2)
+                        *reinterpret_cast<float2*>(&s_red[par][wave][a][c0 + c]) = make_float2(part[a][c], part[a][c + 1]);
+                } else {
+#pragma unroll
+                    for (int c = 0; c < CX::LC; ++c) s_red[par][wave][a][c0 + c] = part[a][c];
+                }
+            }
         }
 #pragma unroll
         for (int c = 0; c < NLR; ++c) {
@@ -277,10 +294,9 @@ void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin
         if (lane < D_IN) {
 #pragma unroll
             for (int wv = 0; wv < NW; ++wv) {
-                const float4 v = s_red[par][wv][lane];
-                khh_j += v.x;
-                eh_j += v.y;
-                uh_j += v.z;
+                khh_j += s_red[par][wv][0][lane];
+                eh_j += s_red[par][wv][1][lane];
+                uh_j += s_red[par][wv][2][lane];
             }
         }
     };
@@ -319,7 +335,8 @@ void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int row = rg + G * r;
-            a[r] = row < M ? tt[row] : 0.f;
+            const float av = tt[row_at(r, row)];
+            a[r] = row_ok(r, row) ? av : 0.f;
         }
         load_f32<L>(tt + TL::KH_OFF + p * L, kt);
         const float4 gv = *reinterpret_cast<const float4*>(tt + TL::G_OFF);
@@ -410,7 +427,10 @@ void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin
             const int row = rg + G * r;
             float zr;
             if (G * r < D_OUT) zr = gs[row];
-            else zr = row < M ? s_zh[wave][row] : 0.f;
+            else {
+                const float zv = s_zh[wave][row_at(r, row)];
+                zr = row_ok(r, row) ? zv : 0.f;
+            }
 #pragma unroll
             for (int c = 0; c < L; ++c) {
                 part[2][c] = fmaf(w[r][c], zr, part[2][c]);
