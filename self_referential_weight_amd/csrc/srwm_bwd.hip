@@ -26,8 +26,8 @@ struct BwdVariant {
     BwdVariant{DI, DO, SRWM_IO_F32, NLR, NW, &srwm_bwd_kernel<DI, DO, NW, P, NLR, false>},      \
         BwdVariant{DI, DO, SRWM_IO_BF16, NLR, NW, &srwm_bwd_kernel<DI, DO, NW, P, NLR, true>}
 const BwdVariant kBwdVariants[] = {
-    SRWM_BWD(8, 8, 1, 8, 4), SRWM_BWD(16, 16, 1, 4, 4), SRWM_BWD(64, 64, 4, 8, 4),
-    SRWM_BWD(8, 8, 1, 8, 1), SRWM_BWD(16, 16, 1, 4, 1), SRWM_BWD(64, 64, 4, 8, 1),
+    SRWM_BWD(8, 8, 1, 8, 4), SRWM_BWD(16, 16, 1, 4, 4), SRWM_BWD(64, 64, 4, 16, 4),
+    SRWM_BWD(8, 8, 1, 8, 1), SRWM_BWD(16, 16, 1, 4, 1), SRWM_BWD(64, 64, 4, 16, 1),
 };
 constexpr int kNumBwdVariants = sizeof(kBwdVariants) / sizeof(kBwdVariants[0]);
 

@@ -83,7 +83,7 @@ __device__ __forceinline__ float wave_total(float v)
 template <int P, int L>
 struct ColExchange {
     static constexpr int LOGP = P == 1 ? 0 : P == 2 ? 1 : P == 4 ? 2 : P == 8 ? 3 : 4;
-    static_assert(P == 4 || P == 8, "row-group bits must include bits 3..5");
+    static_assert(P == 4 || P == 8 || P == 16, "lanes per row");
     static constexpr bool H5 = L >= 2;
     static constexpr int L1 = H5 ? L / 2 : L;
     static constexpr bool H4 = L1 >= 2;
@@ -125,7 +125,7 @@ struct ColExchange {
         if constexpr (LOGP == 2) {
             x += dpp<0x128>(x);  // bit 3 (row_ror:8)
             x += dpp<0x124>(x);  // then bit 2 (row_ror:4): the four lanes i + 4k of a DPP row
-        } else {
+        } else if constexpr (LOGP == 3) {
             x = pair_sum<3>(x);
         }
         if constexpr (!H4) x = pair_sum<4>(x);
@@ -281,7 +281,7 @@ void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin
             if constexpr (P == 4) {
                 v += dpp<0x128>(v);
                 v += dpp<0x124>(v);
-            } else {
+            } else if constexpr (P == 8) {
                 v = pair_sum<3>(v);
             }
             bp[c] = pair_sum<5>(pair_sum<4>(v));
