@@ -216,17 +216,21 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
 
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    # one event between consecutive launches: per-launch durations, same stream
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for i in range(args.steps):
         step()
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gpu_ms = ev0.elapsed_time(ev1) / args.steps  # one kernel launch per step
+    per_launch = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
+    gpu_ms = evs[0].elapsed_time(evs[-1]) / args.steps  # one kernel launch per step
+    per_launch.sort()
+    med_ms = per_launch[len(per_launch) // 2] if len(per_launch) % 2 else \
+        0.5 * (per_launch[len(per_launch) // 2 - 1] + per_launch[len(per_launch) // 2])
     ms_per_step = wall * 1e3 / args.steps
     log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step wall, {gpu_ms:.3f} ms/launch (HIP events)")
 
@@ -258,6 +262,8 @@ def main() -> int:
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_TFLOPS, "traffic": traffic},
         "kernel": {k: kernel[k] for k in ("index", "waves", "lanes_per_row", "waves_per_simd", "schedule")},
         "kernel_ms": gpu_ms,
+        "kernel_ms_median": med_ms,
+        "kernel_ms_min": per_launch[0],
         "io_stream_GBps": io_bytes / (gpu_ms * 1e-3) / 1e9,
     }
     if not args.no_cpu:
