@@ -1,6 +1,8 @@
 /*
- * srwm.h -- C ABI of libsrwm: forward recurrence of the multi-head
- * self-referential weight matrix (SRWM) on AMD Instinct MI355X (gfx950).
+ * srwm.h -- C ABI of libsrwm on AMD Instinct MI355X (gfx950): the forward
+ * recurrence of the multi-head self-referential weight matrix (SRWM), its
+ * backward pass (memory-efficient BPTT), and the DeltaNet / SR-DeltaNet
+ * fast-weight programmers (declared further down).
  *
  * The operation (sources: "Metalearning Continual Learning Algorithms --
  * part 2/5", Sec. 2.3 Eq. (1)-(3) and the "4-learning-rate version"
@@ -49,7 +51,7 @@ extern "C" {
 #endif
 
 #define SRWM_VERSION_MAJOR 0
-#define SRWM_VERSION_MINOR 2
+#define SRWM_VERSION_MINOR 3
 #define SRWM_VERSION_PATCH 0
 
 typedef enum { SRWM_IO_F32 = 0, SRWM_IO_BF16 = 1 } srwm_io_dtype_t;
