@@ -40,42 +40,6 @@ namespace srwm {
 // reads column j.  uh of step t is reduced together with khh and eh of step
 // t-1, so each step has a single workgroup barrier: step inputs are staged in
 // a triple-buffered LDS ring and the exchange area is double-buffered.
-__device__ __forceinline__ void swap32(float& x, float& y)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-    x = __uint_as_float(r[0]);
-    y = __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ void swap16(float& x, float& y)
-{
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-    x = __uint_as_float(r[0]);
-    y = __uint_as_float(r[1]);
-}
-
-// Sum of v over the lane pair that differs in lane bit B (B = 3, 4 or 5).
-template <int B>
-__device__ __forceinline__ float pair_sum(float v)
-{
-    static_assert(B >= 3 && B <= 5, "lane bit");
-    if constexpr (B == 3) {
-        return v + dpp<0x128>(v);  // row_ror:8 -- lane i+8 mod 16, i.e. i ^ 8
-    } else {
-        float x = v, y = v;
-        if constexpr (B == 4) swap16(x, y);
-        else swap32(x, y);
-        return x + y;
-    }
-}
-
-// Sum over all 64 lanes, the same bits in every lane.
-__device__ __forceinline__ float wave_total(float v)
-{
-    v = group_sum<16>(v);
-    return pair_sum<5>(pair_sum<4>(v));
-}
-
 // How the column sums over the row-group lane bits are split: halving on
 // lane bit 5, then on bit 4, while the lane still carries >= 2 columns; the
 // remaining row-group bits are summed in place.  After the exchange a lane

@@ -99,6 +99,64 @@ __device__ __forceinline__ float wave_sum(float v)
     return (readlane(v, 0) + readlane(v, 16)) + (readlane(v, 32) + readlane(v, 48));
 }
 
+// Lane-row exchanges of gfx950: v_permlane32_swap swaps DPP rows 2-3 of its
+// first operand with rows 0-1 of its second; v_permlane16_swap swaps the odd
+// rows of the first with the even rows of the second (a row is 16 lanes).
+__device__ __forceinline__ void swap32(float& x, float& y)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    x = __uint_as_float(r[0]);
+    y = __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ void swap16(float& x, float& y)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    x = __uint_as_float(r[0]);
+    y = __uint_as_float(r[1]);
+}
+
+// Sum of v over the lane pair that differs in lane bit B (B = 3, 4 or 5).
+template <int B>
+__device__ __forceinline__ float pair_sum(float v)
+{
+    static_assert(B >= 3 && B <= 5, "lane bit");
+    if constexpr (B == 3) {
+        return v + dpp<0x128>(v);  // row_ror:8 -- lane i+8 mod 16, i.e. i ^ 8
+    } else {
+        float x = v, y = v;
+        if constexpr (B == 4) swap16(x, y);
+        else swap32(x, y);
+        return x + y;
+    }
+}
+
+// Sum over all 64 lanes, the same bits in every lane.
+__device__ __forceinline__ float wave_total(float v)
+{
+    v = group_sum<16>(v);
+    return pair_sum<5>(pair_sum<4>(v));
+}
+
+// Max / sum over each half-wave (lanes 0-31 and 32-63 separately): the DPP
+// tree inside 16-lane rows, then rows 0+1 and 2+3 joined by one lane-row
+// swap.  Every lane of a half ends with the same bits.
+__device__ __forceinline__ float half_max(float v)
+{
+    int k = order_key(v);
+    k = max(k, dpp_i<kDppXor1>(k));
+    k = max(k, dpp_i<kDppXor2>(k));
+    k = max(k, dpp_i<kDppHalfMirror>(k));
+    k = max(k, dpp_i<kDppMirror>(k));
+    const auto r = __builtin_amdgcn_permlane16_swap(static_cast<unsigned>(k), static_cast<unsigned>(k), false, false);
+    return from_order_key(max(static_cast<int>(r[0]), static_cast<int>(r[1])));
+}
+
+__device__ __forceinline__ float half_sum(float v)
+{
+    return pair_sum<4>(group_sum<16>(v));
+}
+
 // e^x as 2^(x log2 e) on the hardware exp2 (v_exp_f32).
 __device__ __forceinline__ float exp_f32(float x)
 {
