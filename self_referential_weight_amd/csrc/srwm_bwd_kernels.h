@@ -134,7 +134,7 @@ void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin
     // the writers (8 column slices 32 floats apart) and the readers (lane j,
     // column j) both meet at most two-way bank conflicts
     __shared__ __attribute__((aligned(16))) float s_red[2][NW][3][D_IN];
-    __shared__ __attribute__((aligned(16))) float4 s_bred[2][NW];       // betah partials per wave
+    __shared__ __attribute__((aligned(16))) float s_bred[2][NW][4];     // betah partials per wave
     __shared__ __attribute__((aligned(16))) float s_zh[NW][M];          // each wave's own zh rows
 
     const int tid = threadIdx.x;
@@ -238,19 +238,29 @@ void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin
                 }
             }
         }
+        // Only lanes with p == 0 hold betah partials; sum them over the
+        // row-group bits below 4 in place, then over bits 5 and 4:
+        // with four rates as a reduce-scatter (rate c ends in lane 16c).
 #pragma unroll
         for (int c = 0; c < NLR; ++c) {
-            // only lanes with p == 0 hold betah partials: sum over the row-group bits
-            float v = bp[c];
             if constexpr (P == 4) {
-                v += dpp<0x128>(v);
-                v += dpp<0x124>(v);
+                bp[c] += dpp<0x128>(bp[c]);
+                bp[c] += dpp<0x124>(bp[c]);
             } else if constexpr (P == 8) {
-                v = pair_sum<3>(v);
+                bp[c] = pair_sum<3>(bp[c]);
             }
-            bp[c] = pair_sum<5>(pair_sum<4>(v));
         }
-        if (lane == 0) s_bred[par][wave] = make_float4(bp[0], bp[1], bp[2], bp[3]);
+        if constexpr (NLR == 4) {
+            swap32(bp[0], bp[2]);
+            swap32(bp[1], bp[3]);
+            float lo = bp[0] + bp[2], hi = bp[1] + bp[3];  // rows 0-1: rates 0, 1; rows 2-3: 2, 3
+            swap16(lo, hi);
+            const float tot = lo + hi;  // row q of the wave holds rate q
+            if ((lane & 15) == 0) s_bred[par][wave][lane >> 4] = tot;
+        } else {
+            const float tot = pair_sum<5>(pair_sum<4>(bp[0]));
+            if (lane == 0) s_bred[par][wave][0] = tot;
+        }
     };
     // Column j's totals over the unit (lane j of every wave).
     auto gather = [&](int par, float& khh_j, float& eh_j, float& uh_j) {
@@ -353,27 +363,32 @@ void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin
         if (t + 1 < T && wave == ((t + 1) & (NW - 1))) store_dx(t + 1, uh1_j, u_next);
         u_next = lane < D_IN ? us[lane] : 0.f;
         {
-            float4 bt = s_bred[par][0];
+            float bt[4];
 #pragma unroll
-            for (int wv = 1; wv < NW; ++wv) {
-                const float4 v = s_bred[par][wv];
-                bt.x += v.x;
-                bt.y += v.y;
-                bt.z += v.z;
-                bt.w += v.w;
-            }
+            for (int c = 0; c < 4; ++c) bt[c] = c < NLR ? s_bred[par][0][c] : 0.f;
+#pragma unroll
+            for (int wv = 1; wv < NW; ++wv)
+#pragma unroll
+                for (int c = 0; c < NLR; ++c) bt[c] += s_bred[par][wv][c];
             const float kh_j = lane < D_IN ? tt[TL::KH_OFF + lane] : 0.f;
             const float e_j = lane < D_IN ? tt[TL::E_OFF + lane] : 0.f;
             const float qh_j = kh_j + e_j;
             const float kb = khh_j - eh_j;
-            const float dk = wave_total(kb * kh_j);
-            const float dq = wave_total(eh_j * qh_j);
+            // <kb, kh> and <eh, qh> over the 64 columns with one reduction: the
+            // lower half-wave sums the first, the upper the second (columns j
+            // and j +/- 32 joined by a lane-row swap), then a swap hands each
+            // half the other's total.
+            float pk = kb * kh_j, pq = eh_j * qh_j;
+            swap32(pk, pq);                       // lower: kb kh of j, j+32; upper: eh qh of j-32, j
+            float dk = half_sum(pk + pq);         // lower half: <kb, kh>; upper half: <eh, qh>
+            float dq = dk;
+            swap32(dk, dq);                       // every lane: dk = lower's total, dq = upper's
             if (lane < D_IN) {
                 s_zh[wave][D_OUT + lane] = kh_j * (kb - dk);
                 s_zh[wave][D_OUT + D_IN + lane] = qh_j * (eh_j - dq);
             }
             if (lane < NLR) {
-                const float bv = lane == 0 ? bt.x : lane == 1 ? bt.y : lane == 2 ? bt.z : bt.w;
+                const float bv = lane == 0 ? bt[0] : lane == 1 ? bt[1] : lane == 2 ? bt[2] : bt[3];
                 const float gl = lane == 0 ? gate[0] : lane == 1 ? gate[1] : lane == 2 ? gate[2] : gate[3];
                 s_zh[wave][MAIN + lane] = (1.f - gl) * bv;
             }
