@@ -337,10 +337,13 @@ void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             rh[r] = gate[rate(r)] * ah[r];
-            bp[rate(r)] += (p == 0) ? ah[r] * a[r] : 0.f;  // each row once
+            bp[rate(r)] = fmaf(ah[r], a[r], bp[rate(r)]);
 #pragma unroll
             for (int c = 0; c < L; ++c) eh[c] = fmaf(w[r][c], rh[r], eh[c]);
         }
+        // every lane of a row group holds the same ah: count each row once
+#pragma unroll
+        for (int c = 0; c < 4; ++c) bp[c] = p == 0 ? bp[c] : 0.f;
         // part[2] holds uh of step t+1 (zero before the first step)
 #pragma unroll
         for (int c = 0; c < L; ++c) {
