@@ -345,3 +345,16 @@ def test_deltanet_project_ignores_fast_buffers():
     a = _lib.DeltanetArgs(x=FAKE_X, W_slow=FAKE_W0, F0=None, z=FAKE_X + 16, y=None, F_T=None, B=2, T=3, H=2,
                           d_in=16, d_key=16, d_v=16, stream=None)
     assert lib.srwm_deltanet_project(ctypes.byref(a)) == E_ALIAS
+
+
+def test_size_limits():
+    # the kernels index units and steps with 32-bit grid coordinates: B*H and T
+    # must fit, else SRWM_ERR_SHAPE before any device call
+    assert call(B=2 ** 31, H=1, T=1) == E_SHAPE
+    assert call(B=1, H=1, T=2 ** 31) == E_SHAPE
+    assert call_ex(B=2 ** 16, H=2 ** 16, T=1) == E_SHAPE
+    assert call_bwd(B=2 ** 31, H=1, T=1) == E_SHAPE
+    assert call_bwd(T=2 ** 31, B=1, H=1) == E_SHAPE
+    assert call_dn(B=2 ** 31, H=1, T=1) == E_SHAPE
+    assert call_fast(B=1, H=1, T=2 ** 31) == E_SHAPE
+    assert _lib.load().srwm_tape_row(2 ** 40, 1, 4) > 0  # large but well-formed row lengths are computed

@@ -344,3 +344,20 @@ def test_reset_ablation(name):
     y_ref, WT_ref = oracle.forward(x, W0, w.apply_input_softmax, reset_interval=50)
     check_y(y, y_ref, w.io_dtype, name)
     check_state(WT, WT_ref, name)
+
+
+# ---------------------------------------------------------------------------
+# A long sequence: 65,537 steps (x staging over thousands of chunks, 64-bit
+# offsets), every step checked.  At this length float32 itself drifts from
+# float64 by ~2e-5 for d = 64 (tests the same gates); d = 16 drifts by 3e-4
+# (the float32 definition, not the kernel: see tests/test_oracle_drift.py).
+def test_long_sequence():
+    w = WORKLOADS["fewshot_d64"].with_(B=1, H=2, T=65537)
+    say(f"[parity] long sequence: {w}")
+    x = gen_x(w)
+    W0 = gen_W0(w)
+    y, WT = run_gpu(x, W0, w.io_dtype, w.apply_input_softmax)
+    y_ref, WT_ref = oracle.forward(x, W0, w.apply_input_softmax)
+    ry = check_y(y, y_ref, w.io_dtype, "long sequence")
+    rw = check_state(WT, WT_ref, "long sequence")
+    say(f"[parity] long sequence relL2 y={ry:.2e} W_T={rw:.2e}")
