@@ -42,6 +42,10 @@ TRAFFIC_FILE = ROOT / "profiles" / "srwm_fwd_rl_d64_bf16_hbm_traffic.json"
 # The backward kernel's device code and the device helpers it includes.
 BWD_SRCS = [ROOT / "self_referential_weight_amd" / "csrc" / f for f in ("srwm_bwd_kernels.h", "srwm_device.h")]
 BWD_TRAFFIC_FILE = ROOT / "profiles" / "srwm_bwd_rl_d64_bf16_hbm_traffic.json"
+LDS_FILE = ROOT / "profiles" / "srwm_lds_rl_d64_bf16.json"
+# LDS bandwidth the achieved figure is compared with: 128 bytes per clock per
+# CU (the CDNA3 compute unit's figure, assumed) x 256 CUs x 2.4 GHz.
+PEAK_LDS_TBPS = 128 * 256 * 2.4e9 / 1e12
 
 
 def log(msg: str) -> None:
@@ -68,6 +72,23 @@ def measured_traffic(workload: str, variant: int, path=TRAFFIC_FILE, srcs=None):
             or rec.get("workload") != workload or rec.get("variant", -1) != variant):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def measured_lds(which: str, workload: str, srcs, kernel_ms: float):
+    """LDS bytes per launch from the committed counter run, if taken on the
+    current kernel source and workload, turned into a rate over kernel_ms."""
+    if not LDS_FILE.exists():
+        return None
+    try:
+        rec = json.loads(LDS_FILE.read_text()).get(which, {})
+    except ValueError:
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash(srcs) or rec.get("workload") != workload:
+        return None
+    nbytes = rec["lds_load_bytes_per_launch"] + rec["lds_store_bytes_per_launch"]
+    tbps = nbytes / (kernel_ms * 1e-3) / 1e12
+    return {"bytes_per_launch": nbytes, "achieved": tbps, "unit": "TB/s", "assumed_peak": PEAK_LDS_TBPS,
+            "frac": tbps / PEAK_LDS_TBPS}
 
 
 def cpu_baseline(w, x_host, W0_host, budget_s: float):
@@ -261,6 +282,7 @@ def main() -> int:
         "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_TFLOPS, "traffic": traffic},
         "kernel": {k: kernel[k] for k in ("index", "waves", "lanes_per_row", "waves_per_simd", "schedule")},
+        "lds": measured_lds("forward", name, None, gpu_ms) if args.variant < 0 else None,
         "kernel_ms": gpu_ms,
         "kernel_ms_median": med_ms,
         "kernel_ms_min": per_launch[0],
@@ -339,6 +361,7 @@ def bench_backward(args, w, name, x, x_host, W0, W0_host, dev) -> int:
         "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_TFLOPS,
                      "traffic": measured_traffic(name + "+backward", -1, BWD_TRAFFIC_FILE, BWD_SRCS)},
+        "lds": measured_lds("backward", name + "+backward", BWD_SRCS, b_ms),
         "forward_ms": f_ms,
         "backward_ms": b_ms,
     }
