@@ -74,6 +74,31 @@ def measured_traffic(workload: str, variant: int, path=TRAFFIC_FILE, srcs=None):
     return rec.get("hbm_bytes_per_launch")
 
 
+def valu_calibration(dev, stream) -> dict:
+    """The chip's measured scalar FP32 FMA rate (srwm_valu_probe: independent
+    FMA chains over 8 waves per SIMD), outside the timed region."""
+    import torch
+
+    from self_referential_weight_amd import _lib
+
+    lib = _lib.load()
+    wgs, iters = 2048, 12000
+    out = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+    handle = stream.cuda_stream
+    rc = lib.srwm_valu_probe(out.data_ptr(), wgs, iters, handle)
+    if rc != 0:
+        raise RuntimeError(_lib.strerror(rc))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(3):
+        lib.srwm_valu_probe(out.data_ptr(), wgs, iters, handle)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 3
+    return {"fp32_scalar_fma_TFLOPs": lib.srwm_valu_probe_flop(wgs, iters) / (ms * 1e-3) / 1e12,
+            "probe": f"{wgs} workgroups x 256 threads x {iters * 16} x 8 independent v_fma_f32 chains"}
+
+
 def measured_lds(which: str, workload: str, srcs, kernel_ms: float):
     """LDS bytes per launch from the committed counter run, if taken on the
     current kernel source and workload, turned into a rate over kernel_ms."""
@@ -288,6 +313,14 @@ def main() -> int:
         "kernel_ms_min": per_launch[0],
         "io_stream_GBps": io_bytes / (gpu_ms * 1e-3) / 1e9,
     }
+    # Against the measured scalar FP32 rate: the kernel executes 6 m d_in FLOP
+    # per head-step (the two reads fused into one) of the algorithmic 8 m d_in.
+    cal = valu_calibration(dev, stream)
+    executed = achieved * 6.0 / 8.0
+    cal.update({"executed_TFLOPs": executed, "executed_frac": executed / cal["fp32_scalar_fma_TFLOPs"]})
+    rec["calibration"] = cal
+    log(f"[bench] measured scalar FP32 FMA rate {cal['fp32_scalar_fma_TFLOPs']:.1f} TFLOP/s; "
+        f"kernel executes {executed:.1f} TFLOP/s ({100 * cal['executed_frac']:.1f}%)")
     if not args.no_cpu:
         log("[bench] timing the float64 CPU oracle on a bounded sample")
         rec["cpu_baseline"] = cpu_baseline(w, x_host, W0_host, args.cpu_budget)

@@ -312,6 +312,17 @@ int srwm_fwp_supported(int64_t d_key, int64_t d_v);
 /* 1 if a kernel exists for (d_in, d_out, io_dtype, n_lr), else 0. */
 int srwm_supported(int64_t d_in, int64_t d_out, int io_dtype, int n_lr);
 
+/*
+ * Measurement aid (not part of the method): srwm_valu_probe launches
+ * `workgroups` workgroups of 256 threads that each run `iters` rounds of 16
+ * steps of 8 independent single-lane FP32 FMA chains and write one float per
+ * thread to out[workgroups*256] (device, 16-byte aligned).  Timing it gives the
+ * chip's scalar FP32 FMA rate, the ceiling of kernels built without packed
+ * FP32; srwm_valu_probe_flop returns the FLOP (2 per FMA) of one launch.
+ */
+int srwm_valu_probe(float* out, int64_t workgroups, int iters, void* stream);
+int64_t srwm_valu_probe_flop(int64_t workgroups, int iters);
+
 /* Static string naming an error code (never NULL). */
 const char* srwm_strerror(int code);
 

@@ -8,7 +8,7 @@ from pathlib import Path
 
 PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
-SRCS = [PKG / "csrc" / f for f in ("srwm_fwd.hip", "srwm_bwd.hip", "srwm_fwp.hip")]
+SRCS = [PKG / "csrc" / f for f in ("srwm_fwd.hip", "srwm_bwd.hip", "srwm_fwp.hip", "srwm_calib.hip")]
 LIB = PKG / "libsrwm.so"
 
 HIPCC_FLAGS = [

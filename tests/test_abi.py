@@ -358,3 +358,12 @@ def test_size_limits():
     assert call_dn(B=2 ** 31, H=1, T=1) == E_SHAPE
     assert call_fast(B=1, H=1, T=2 ** 31) == E_SHAPE
     assert _lib.load().srwm_tape_row(2 ** 40, 1, 4) > 0  # large but well-formed row lengths are computed
+
+
+def test_valu_probe_validation():
+    lib = _lib.load()
+    assert lib.srwm_valu_probe(None, 4, 1, None) == E_NULL
+    assert lib.srwm_valu_probe(FAKE_Y, 0, 1, None) == E_SHAPE
+    assert lib.srwm_valu_probe(FAKE_Y, 4, 0, None) == E_SHAPE
+    assert lib.srwm_valu_probe(FAKE_Y + 4, 4, 1, None) == E_ARG
+    assert lib.srwm_valu_probe_flop(2, 3) == 2 * 256 * 3 * 16 * 8 * 2
