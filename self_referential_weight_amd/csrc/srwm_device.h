@@ -39,8 +39,10 @@ __device__ __forceinline__ float group_sum(float v)
     return v;
 }
 
-// max(a, b) for finite or infinite operands (no NaN canonicalisation).
-__device__ __forceinline__ float fmax2(float a, float b) { return a > b ? a : b; }
+// max(a, b) for finite or infinite operands: the median of {a, b, +inf}, one
+// v_med3_f32 (a compare and select would need a VCC hazard wait between them;
+// a NaN operand is dropped here and still reaches the softmax through exp).
+__device__ __forceinline__ float fmax2(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
 
 // Order-preserving map of a float to a signed int (an involution): positive
 // floats keep their bits, negative ones flip their magnitude bits, so signed
@@ -136,6 +138,47 @@ __device__ __forceinline__ float wave_total(float v)
 {
     v = group_sum<16>(v);
     return pair_sum<5>(pair_sum<4>(v));
+}
+
+// Max over all 64 lanes of two values at once, the same bits in every lane:
+// the 16-lane DPP trees, then one lane-row swap pairs the two values' row
+// results (rows 0, 2 carry a's pairs, rows 1, 3 b's), a second joins the two
+// halves and a third hands every row both totals.  Seven instructions after
+// the trees instead of two readlane chains, and no scalar-register hazards.
+__device__ __forceinline__ void wave_max2(float& a, float& b)
+{
+    int ka = order_key(a), kb = order_key(b);
+    ka = max(ka, dpp_i<kDppXor1>(ka));
+    kb = max(kb, dpp_i<kDppXor1>(kb));
+    ka = max(ka, dpp_i<kDppXor2>(ka));
+    kb = max(kb, dpp_i<kDppXor2>(kb));
+    ka = max(ka, dpp_i<kDppHalfMirror>(ka));
+    kb = max(kb, dpp_i<kDppHalfMirror>(kb));
+    ka = max(ka, dpp_i<kDppMirror>(ka));
+    kb = max(kb, dpp_i<kDppMirror>(kb));
+    // rows (0,1) of a meet in row 0, of b in row 1; rows (2,3) in rows 2 / 3
+    auto r = __builtin_amdgcn_permlane16_swap(static_cast<unsigned>(ka), static_cast<unsigned>(kb), false, false);
+    const int t = max(static_cast<int>(r[0]), static_cast<int>(r[1]));
+    r = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(t), static_cast<unsigned>(t), false, false);
+    const int u = max(static_cast<int>(r[0]), static_cast<int>(r[1]));  // rows 0, 2: a; rows 1, 3: b
+    r = __builtin_amdgcn_permlane16_swap(static_cast<unsigned>(u), static_cast<unsigned>(u), false, false);
+    a = from_order_key(static_cast<int>(r[0]));
+    b = from_order_key(static_cast<int>(r[1]));
+}
+
+// Sum over all 64 lanes of two values at once (the same pairing as wave_max2).
+__device__ __forceinline__ void wave_sum2(float& a, float& b)
+{
+    a = group_sum<16>(a);
+    b = group_sum<16>(b);
+    float x = a, y = b;
+    swap16(x, y);
+    float t = x + y, t2 = t;
+    swap32(t, t2);
+    float u = t + t2, u2 = u;
+    swap16(u, u2);
+    a = u;
+    b = u2;
 }
 
 // Max / sum over each half-wave (lanes 0-31 and 32-63 separately): the DPP

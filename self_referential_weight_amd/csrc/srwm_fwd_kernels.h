@@ -75,14 +75,15 @@ __device__ __forceinline__ int rate_of_row(int row, int d_in, int d_out)
 // phi(k) and phi(q) by one wave: k and q are d-vectors in LDS.  The lower
 // half-wave takes k, the upper half q (lane hl of a half holds entries hl,
 // hl + 32, ...: consecutive lanes, consecutive LDS words), so both softmaxes
-// share every reduction step; one
-// lane-row swap then brings phi(q) next to phi(k) in the lower half, which
-// writes kh = softmax(k) and e = softmax(q) - kh, the difference the fused
-// read of Eq. (2) needs.
+// share every reduction step.  Then phi(k) and phi(q) entries meet in one
+// lane: a lane-row swap of two entries i, i+1 leaves the lower half with
+// (phi(k), phi(q)) of entry i and the upper half with those of entry i+1, so
+// every lane writes one kh = softmax(k) entry and e = softmax(q) - kh, the
+// difference the fused read of Eq. (2) needs (with one entry per lane, the
+// lower half alone writes).
 template <int D>
-__device__ __forceinline__ void wave_addresses_paired(const float* __restrict__ k, const float* __restrict__ q,
-                                               float* __restrict__ kh_out, float* __restrict__ e_out,
-                                               int lane)
+__device__ __forceinline__ void wave_addresses(const float* __restrict__ k, const float* __restrict__ q,
+                                               float* __restrict__ kh_out, float* __restrict__ e_out, int lane)
 {
     constexpr int EPH = (D + 31) / 32;
     const bool upper = lane >= 32;
@@ -105,78 +106,32 @@ __device__ __forceinline__ void wave_addresses_paired(const float* __restrict__ 
         s += v[i];
     }
     const float inv = rcp_f32(half_sum(s));
+    // Both probabilities are rounded before the difference (no fused
+    // multiply-subtract), so k_t == q_t gives e == 0 exactly: the two halves
+    // run the same instructions on the same values.
+    if constexpr (EPH % 2 == 0) {
 #pragma unroll
-    for (int i = 0; i < EPH; ++i) {
-        // Both probabilities are rounded before the difference (no fused
-        // multiply-subtract), so k_t == q_t gives e == 0 exactly: the two
-        // halves run the same instructions on the same values.
+        for (int i = 0; i < EPH; i += 2) {
 #pragma clang fp contract(off)
-        float p = v[i] * inv, pq = p;
-        swap32(p, pq);  // lower half: p = phi(k) entry, pq = the matching phi(q) entry
-        const int j = hl + 32 * i;
-        if (!upper && j < D) {
-            kh_out[j] = p;
-            e_out[j] = pq - p;
+            float pk = v[i] * inv, pq = v[i + 1] * inv;
+            swap32(pk, pq);  // lower: (phi(k), phi(q)) of entry i; upper: of entry i+1
+            const int j = hl + 32 * (upper ? i + 1 : i);
+            kh_out[j] = pk;
+            e_out[j] = pq - pk;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < EPH; ++i) {
+#pragma clang fp contract(off)
+            float p = v[i] * inv, pq = p;
+            swap32(p, pq);  // lower half: p = phi(k) entry, pq = the matching phi(q) entry
+            const int j = hl + 32 * i;
+            if (!upper && j < D) {
+                kh_out[j] = p;
+                e_out[j] = pq - p;
+            }
         }
     }
-}
-
-// phi(k) and phi(q) by one wave, as two independent reduction chains that
-// the scheduler interleaves: lanes take entries lane, lane+64, ... of both
-// vectors.  Fewer instructions are spent by the paired form above, but where
-// a unit is a single wave at two waves per SIMD (and for d = 128) the two
-// chains hide each other's latency and measure faster.
-template <int D>
-__device__ __forceinline__ void wave_addresses_two_chains(const float* __restrict__ k, const float* __restrict__ q,
-                                                          float* __restrict__ kh_out, float* __restrict__ e_out,
-                                                          int lane)
-{
-    constexpr int EPL = (D + 63) / 64;
-    float a[EPL], b[EPL];
-    float ma = -INFINITY, mb = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        const int j = lane + 64 * i;
-        a[i] = (j < D) ? k[j] : -INFINITY;
-        b[i] = (j < D) ? q[j] : -INFINITY;
-        ma = fmax2(ma, a[i]);
-        mb = fmax2(mb, b[i]);
-    }
-    ma = wave_max(ma);
-    mb = wave_max(mb);
-    float sa = 0.f, sb = 0.f;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        const int j = lane + 64 * i;
-        a[i] = (j < D) ? exp_f32(a[i] - ma) : 0.f;
-        b[i] = (j < D) ? exp_f32(b[i] - mb) : 0.f;
-        sa += a[i];
-        sb += b[i];
-    }
-    const float ia = rcp_f32(wave_sum(sa));
-    const float ib = rcp_f32(wave_sum(sb));
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        const int j = lane + 64 * i;
-        if (j < D) {
-            // rounded before the difference: k_t == q_t gives e == 0 exactly
-#pragma clang fp contract(off)
-            const float kh = a[i] * ia;
-            const float qh = b[i] * ib;
-            kh_out[j] = kh;
-            e_out[j] = qh - kh;
-        }
-    }
-}
-
-template <int D, bool PAIRED>
-__device__ __forceinline__ void wave_addresses(const float* __restrict__ k, const float* __restrict__ q,
-                                               float* __restrict__ kh_out, float* __restrict__ e_out, int lane)
-{
-    if constexpr (PAIRED)
-        wave_addresses_paired<D>(k, q, kh_out, e_out, lane);
-    else
-        wave_addresses_two_chains<D>(k, q, kh_out, e_out, lane);
 }
 
 // Width of the LDS vector pieces streamed through the FMA loops.
@@ -449,10 +404,7 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
 
                 // ---- (B) phi(k), phi(q), sigma(beta), computed by every wave for
                 // itself (identical bits in every wave); y_t from W_{t-1}.
-                // (measured: the paired softmax except for one-wave units with two
-                // lanes per row, the layout of the large-batch d = 64 kernel)
-                wave_addresses<D_IN, !(NW == 1 && P == 2)>(zt + D_OUT, zt + D_OUT + D_IN, s_kh[wave],
-                                                          s_e[wave], lane);
+                wave_addresses<D_IN>(zt + D_OUT, zt + D_OUT + D_IN, s_kh[wave], s_e[wave], lane);
                 const float gl = sigmoid_f32(zt[MAIN + (NLR == 4 ? (lane & 3) : 0)]);
                 const float g0 = readlane(gl, 0), g1 = readlane(gl, 1), g2 = readlane(gl, 2), g3 = readlane(gl, 3);
                 if (wave == WAVE_AUX) store_y<D_OUT, BF16>(yv, y0 + (int64_t)t * y_step, zt, lane);
@@ -670,7 +622,7 @@ void srwm_fwd_fused_kernel(const void* __restrict__ xv, const float* __restrict_
             // ---- (B) addresses and gates of step t (every wave), y_t.
             float* __restrict__ khw = s_kh[t & 1][wave];
             float* __restrict__ ew = s_e[wave];
-            wave_addresses<D_IN, (D_IN <= 64)>(zt + D_OUT, zt + D_OUT + D_IN, khw, ew, lane);
+            wave_addresses<D_IN>(zt + D_OUT, zt + D_OUT + D_IN, khw, ew, lane);
             const float gl = sigmoid_f32(zt[MAIN + (NLR == 4 ? (lane & 3) : 0)]);
             const float g0 = readlane(gl, 0), g1 = readlane(gl, 1), g2 = readlane(gl, 2), g3 = readlane(gl, 3);
             if (wave == 1) store_y<D_OUT, BF16>(yv, y0 + (int64_t)t * y_step, zt, lane);

@@ -204,8 +204,7 @@ __global__ __launch_bounds__(NW * 64) void srwm_fast_kernel(const float* __restr
                 if (e < V0) mk = fmax2(mk, zr[j][i]);
                 else if (e >= Q0 && e < BETA) mq = fmax2(mq, zr[j][i]);
             }
-            mk = wave_max(mk);
-            mq = wave_max(mq);
+            wave_max2(mk, mq);
             float ex[EZ];
             float sk = 0.f, sq = 0.f;
 #pragma unroll
@@ -216,7 +215,8 @@ __global__ __launch_bounds__(NW * 64) void srwm_fast_kernel(const float* __restr
                 if (isk) sk += ex[i];
                 if (isq) sq += ex[i];
             }
-            const float ik = rcp_f32(wave_sum(sk)), iq = rcp_f32(wave_sum(sq));
+            wave_sum2(sk, sq);
+            const float ik = rcp_f32(sk), iq = rcp_f32(sq);
 #pragma unroll
             for (int i = 0; i < EZ; ++i) {
                 const int e = lane + kWave * i;
