@@ -280,6 +280,12 @@ __device__ __forceinline__ void wave_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Keep v materialised in every lane at this point: a value that only some
+// lanes store afterwards would otherwise have its last reduction step sunk
+// into the store's branch, where the DPP add can no longer be fused (an extra
+// move and a separate add per value).  Emits no instruction.
+__device__ __forceinline__ void keep(float& v) { asm volatile("" : "+v"(v)); }
+
 __device__ __forceinline__ float uniform(float v)
 {
     return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));

@@ -105,14 +105,15 @@ const Variant kVariants[] = {
     SRWM_BOTH_IO_FUSED(64, 64, 4, 4, 1, 4, 0),
     SRWM_BOTH_IO_RESET(64, 64, 2, 8, 2, 4, 1),
     // d = 128
-    SRWM_BOTH_IO(128, 128, 8, 8, 1, 4, 1),
+    SRWM_BOTH_IO(128, 128, 8, 4, 1, 4, 1),
+    SRWM_BOTH_IO(128, 128, 8, 8, 1, 4, 0),
     SRWM_BOTH_IO_FUSED(128, 128, 8, 8, 1, 4, 0),
     SRWM_BOTH_IO_FUSED(128, 128, 8, 16, 1, 4, 0),
     SRWM_BOTH_IO_FUSED(128, 128, 16, 16, 1, 4, 0),
     SRWM_BOTH_IO(128, 128, 8, 16, 1, 4, 0),
     SRWM_BOTH_IO(128, 128, 16, 16, 1, 4, 0),
     SRWM_BOTH_IO(128, 128, 16, 8, 1, 4, 0),
-    SRWM_BOTH_IO_RESET(128, 128, 8, 8, 1, 4, 1),
+    SRWM_BOTH_IO_RESET(128, 128, 8, 4, 1, 4, 1),
     // one learning rate
     SRWM_BOTH_IO_RESET(2, 2, 1, 2, 1, 1, 1),
     SRWM_BOTH_IO_RESET(8, 8, 1, 8, 1, 1, 1),
@@ -121,9 +122,9 @@ const Variant kVariants[] = {
     SRWM_BOTH_IO_RESET(64, 64, 2, 8, 2, 1, 1),
     SRWM_BOTH_IO(64, 64, 8, 8, 1, 1, 1),
     SRWM_BOTH_IO_FUSED(64, 64, 8, 8, 1, 1, 0),
-    SRWM_BOTH_IO(128, 128, 8, 8, 1, 1, 1),
+    SRWM_BOTH_IO(128, 128, 8, 4, 1, 1, 1),
     SRWM_BOTH_IO_FUSED(128, 128, 8, 8, 1, 1, 0),
-    SRWM_BOTH_IO_RESET(128, 128, 8, 8, 1, 1, 1),
+    SRWM_BOTH_IO_RESET(128, 128, 8, 4, 1, 1, 1),
     // SR-DeltaNet's projection: d_out = d_v + 2*d_key + 1 (float32 I/O)
     make_variant<8, 25, 1, 8, 1, 4, 1, false>(1),
     make_variant<8, 25, 1, 8, 1, 1, 1, false>(1),

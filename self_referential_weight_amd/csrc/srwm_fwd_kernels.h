@@ -287,6 +287,10 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
     constexpr int L = Gm::L, G = Gm::G, R = Gm::R, LB = Gm::LB;
     constexpr int S = Gm::S;
     constexpr bool BETA_SEP = Gm::BETA_SEP;
+    // Row sums held complete in every lane before the stores that only some
+    // lanes make (keep()): measured faster for multi-wave d <= 64 units,
+    // slower at d = 128 and without the registers to spare in one-wave units.
+    constexpr bool KEEP_SUMS = NW > 1 && D_IN <= 64;
 
     __shared__ __attribute__((aligned(16))) float s_x[2][S][D_IN];
     // z_t, double-buffered by step parity so one barrier per step suffices.
@@ -382,6 +386,10 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
                 });
 #pragma unroll
                 for (int r = 0; r < R; ++r) acc[r] = group_sum<P>(acc[r]);
+                if constexpr (KEEP_SUMS) {
+#pragma unroll
+                    for (int r = 0; r < R; ++r) keep(acc[r]);
+                }
                 // All P lanes of a row group hold the same sums; lane p stores
                 // registers r = p, p+P, ... (one LDS store per P registers).
 #pragma unroll
@@ -397,6 +405,7 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
                         float accb = 0.f;
                         stream_lds<LB>(urow + bcol, [&](int c, float uc) { accb = fmaf(wb[c], uc, accb); });
                         accb = group_sum<16>(accb);
+                        if constexpr (KEEP_SUMS) keep(accb);
                         if ((lane & 15) == 0 && brow < NLR) zt[MAIN + brow] = accb;
                     }
                 }
@@ -430,6 +439,10 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
                         gate = bk == 0 ? g0 : bk == 1 ? g1 : bk == 2 ? g2 : g3;
                     }
                     acc[r] = gate * group_sum<P>(acc[r]);
+                }
+                if constexpr (KEEP_SUMS) {
+#pragma unroll
+                    for (int r = 0; r < R; ++r) keep(acc[r]);
                 }
                 float accb = 0.f;
                 if constexpr (BETA_SEP) {
@@ -690,7 +703,8 @@ void srwm_fwd_fused_kernel(const void* __restrict__ xv, const float* __restrict_
                 const float a = gate_of[r] * group_sum<P>(accr[r]);
                 a_prev[r] = a;
                 if (has_next) {
-                    const float z = fmaf(a, ct, group_sum<P>(accz[r]));
+                    float z = fmaf(a, ct, group_sum<P>(accz[r]));
+                    if constexpr (D_IN <= 64) keep(z);  // as KEEP_SUMS of the phased kernel
                     const int row = rg + G * r;
                     if (p == 0 && (Gm::ALIGNED || row < ROWS)) zn[row] = z;
                 }
@@ -708,7 +722,8 @@ void srwm_fwd_fused_kernel(const void* __restrict__ xv, const float* __restrict_
                     }
                     ab_prev = g3 * group_sum<16>(br);
                     if (has_next) {
-                        const float z = fmaf(ab_prev, ct, group_sum<16>(bz));
+                        float z = fmaf(ab_prev, ct, group_sum<16>(bz));
+                        if constexpr (D_IN <= 64) keep(z);
                         if ((lane & 15) == 0 && brow < NLR) zn[MAIN + brow] = z;
                     }
                 }
