@@ -93,14 +93,14 @@ const Variant kVariants[] = {
     SRWM_BOTH_IO_RESET(32, 32, 1, 4, 1, 4, 1),
     // d = 64: one wave per unit for many units, up to eight for few
     SRWM_BOTH_IO(64, 64, 1, 2, 2, 4, 1),
-    SRWM_BOTH_IO(64, 64, 2, 8, 2, 4, 1),
-    SRWM_BOTH_IO_FUSED(64, 64, 4, 8, 1, 4, 1),
+    SRWM_BOTH_IO(64, 64, 2, 8, 2, 4, 0),
+    SRWM_BOTH_IO_FUSED(64, 64, 4, 8, 1, 4, 0),
     SRWM_BOTH_IO_FUSED(64, 64, 8, 8, 1, 4, 0),
     SRWM_BOTH_IO(64, 64, 1, 4, 2, 4, 0),
     SRWM_BOTH_IO(64, 64, 1, 4, 1, 4, 0),
     SRWM_BOTH_IO(64, 64, 4, 8, 1, 4, 0),
     SRWM_BOTH_IO(64, 64, 4, 16, 1, 4, 0),
-    SRWM_BOTH_IO(64, 64, 4, 4, 1, 4, 0),
+    SRWM_BOTH_IO(64, 64, 4, 4, 1, 4, 1),
     SRWM_BOTH_IO(64, 64, 8, 8, 1, 4, 1),
     SRWM_BOTH_IO_FUSED(64, 64, 4, 4, 1, 4, 0),
     SRWM_BOTH_IO_RESET(64, 64, 2, 8, 2, 4, 1),
@@ -120,6 +120,7 @@ const Variant kVariants[] = {
     SRWM_BOTH_IO_RESET(16, 16, 1, 4, 1, 1, 1),
     SRWM_BOTH_IO(64, 64, 1, 2, 2, 1, 1),
     SRWM_BOTH_IO_RESET(64, 64, 2, 8, 2, 1, 1),
+    SRWM_BOTH_IO(64, 64, 4, 4, 1, 1, 1),
     SRWM_BOTH_IO(64, 64, 8, 8, 1, 1, 1),
     SRWM_BOTH_IO_FUSED(64, 64, 8, 8, 1, 1, 0),
     SRWM_BOTH_IO(128, 128, 8, 4, 1, 1, 1),
@@ -139,13 +140,17 @@ const Variant kVariants[] = {
     SRWM_BOTH_IO_TAPE(8, 8, 1, 8, 1, 4, 1),
     SRWM_BOTH_IO_TAPE(16, 16, 1, 4, 1, 4, 1),
     SRWM_BOTH_IO_TAPE(64, 64, 1, 4, 2, 4, 1),
-    SRWM_BOTH_IO_TAPE(64, 64, 2, 8, 2, 4, 1),
-    SRWM_BOTH_IO_TAPE(64, 64, 4, 8, 1, 4, 1),
+    SRWM_BOTH_IO_TAPE(64, 64, 2, 8, 2, 4, 0),
+    SRWM_BOTH_IO_TAPE(64, 64, 4, 8, 1, 4, 0),
+    SRWM_BOTH_IO_TAPE(64, 64, 4, 4, 1, 4, 1),
+    SRWM_BOTH_IO_TAPE(64, 64, 8, 8, 1, 4, 1),
     SRWM_BOTH_IO_TAPE(8, 8, 1, 8, 1, 1, 1),
     SRWM_BOTH_IO_TAPE(16, 16, 1, 4, 1, 1, 1),
     SRWM_BOTH_IO_TAPE(64, 64, 1, 4, 2, 1, 1),
-    SRWM_BOTH_IO_TAPE(64, 64, 2, 8, 2, 1, 1),
-    SRWM_BOTH_IO_TAPE(64, 64, 4, 8, 1, 1, 1),
+    SRWM_BOTH_IO_TAPE(64, 64, 2, 8, 2, 1, 0),
+    SRWM_BOTH_IO_TAPE(64, 64, 4, 8, 1, 1, 0),
+    SRWM_BOTH_IO_TAPE(64, 64, 4, 4, 1, 1, 1),
+    SRWM_BOTH_IO_TAPE(64, 64, 8, 8, 1, 1, 1),
 };
 
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
@@ -162,8 +167,9 @@ bool variant_matches(const Variant& v, int64_t d_in, int64_t d_out, int io, int 
 
 // Automatic choice among the eligible variants: the fewest waves per unit
 // that still give every SIMD of the chip two waves (units * waves >= 2048);
-// if none does, the most waves per unit.  With a reset interval only the
-// variants built with the reset ablation qualify.
+// if none does, the most waves per unit.  Variants whose reset support
+// matches the request come first: a variant built with the reset ablation
+// serves a plain request only for a shape that has no plain variant.
 int find_variant(int64_t d_in, int64_t d_out, int io, int nlr, bool reset, bool tape, int requested,
                  int64_t units)
 {
@@ -171,14 +177,17 @@ int find_variant(int64_t d_in, int64_t d_out, int io, int nlr, bool reset, bool 
         if (requested >= kNumVariants) return -1;
         return variant_matches(kVariants[requested], d_in, d_out, io, nlr, reset, tape) ? requested : -1;
     }
-    int best_fill = -1, best_any = -1;
-    for (int i = 0; i < kNumVariants; ++i) {
-        const Variant& v = kVariants[i];
-        if (!variant_matches(v, d_in, d_out, io, nlr, reset, tape) || !v.is_auto) continue;
-        if (units * v.nw >= kChipWaveSlots && (best_fill < 0 || v.nw < kVariants[best_fill].nw)) best_fill = i;
-        if (best_any < 0 || v.nw > kVariants[best_any].nw) best_any = i;
+    for (int pass = 0; pass < 2; ++pass) {
+        int best_fill = -1, best_any = -1;
+        for (int i = 0; i < kNumVariants; ++i) {
+            const Variant& v = kVariants[i];
+            if (!variant_matches(v, d_in, d_out, io, nlr, reset, tape) || !v.is_auto) continue;
+            if (pass == 0 && (v.reset != 0) != reset) continue;
+            if (units * v.nw >= kChipWaveSlots && (best_fill < 0 || v.nw < kVariants[best_fill].nw)) best_fill = i;
+            if (best_any < 0 || v.nw > kVariants[best_any].nw) best_any = i;
+        }
+        if (best_fill >= 0 || best_any >= 0) return best_fill >= 0 ? best_fill : best_any;
     }
-    if (best_fill >= 0 || best_any >= 0) return best_fill >= 0 ? best_fill : best_any;
     // a shape whose only variants are not marked eligible (or all fused, with reset)
     for (int i = 0; i < kNumVariants; ++i)
         if (variant_matches(kVariants[i], d_in, d_out, io, nlr, reset, tape)) return i;
