@@ -70,3 +70,35 @@ def test_gradient_of_frozen_dynamics_is_linear_map():
     np.testing.assert_allclose(dW[0, :d_out], np.einsum("to,ti->oi", gy[0, :, 0], x[0, :, 0]) + gW[0, 0, :d_out],
                                rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(dx[0, :, 0], gy[0, :, 0] @ W0[0, :d_out], rtol=1e-12, atol=1e-12)
+
+
+def test_reset_every_step_has_closed_form_gradient():
+    # With R = 1 every step starts from W0 (SRWM review page Sec. 4.5, read as
+    # a return to the initial state), so y_t = W0[Y] x_t and, without a cost
+    # on W_T, dL/dW0 = sum_t gy[t] x_t^T in the y rows and 0 elsewhere, and
+    # dL/dx_t = W0[Y]^T gy[t].
+    x, W0, gy, _ = _problem(5, 2, 7, 2, 4, 3)
+    d_out = 3
+    dx, dW = backward.grads(x, W0, False, gy, None, 4, 1)
+    np.testing.assert_allclose(dW[:, :d_out], np.einsum("btho,bthi->hoi", gy, x), rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(dW[:, d_out:], 0.0)
+    np.testing.assert_allclose(dx, np.einsum("btho,hoi->bthi", gy, W0[:, :d_out]), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("flag,n_lr", [(False, 4), (True, 1)])
+def test_reset_gradient_is_sum_over_independent_windows(flag, n_lr):
+    # Windows [0,R), [R,2R), ... each start from W0 and never see each other,
+    # so the reset run's gradient is the windows' gradients taken as separate
+    # runs: dx concatenated over t, dW0 summed; only the last window's final
+    # state is W_T.
+    R, T = 4, 11
+    x, W0, gy, gW = _problem(6, 2, T, 2, 4, 3, n_lr)
+    dx, dW = backward.grads(x, W0, flag, gy, gW, n_lr, R)
+    dx_w, dW_w = [], np.zeros_like(W0)
+    for t0 in range(0, T, R):
+        t1 = min(t0 + R, T)
+        a, b = backward.grads(x[:, t0:t1], W0, flag, gy[:, t0:t1], gW if t1 == T else None, n_lr)
+        dx_w.append(a)
+        dW_w += b
+    np.testing.assert_allclose(dx, np.concatenate(dx_w, axis=1), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dW, dW_w, rtol=1e-11, atol=1e-12)
