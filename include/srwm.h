@@ -51,7 +51,7 @@ extern "C" {
 #endif
 
 #define SRWM_VERSION_MAJOR 0
-#define SRWM_VERSION_MINOR 3
+#define SRWM_VERSION_MINOR 4
 #define SRWM_VERSION_PATCH 0
 
 typedef enum { SRWM_IO_F32 = 0, SRWM_IO_BF16 = 1 } srwm_io_dtype_t;
@@ -121,6 +121,15 @@ int srwm_forward_variant(const void* x, const float* W0, void* y, float* W_T,
  *                    INT32_MAX.
  *   variant          -1 for the automatic choice, else a srwm_variant_info
  *                    index.
+ *   tape             NULL, or the backward tape (see srwm_backward).
+ *   window_states    with a tape and R > 0: the state of each unit at the end
+ *                    of every window but the last (the last one's is W_T),
+ *                    [B][H][n_resets][m][d_in] float32 (out), n_resets =
+ *                    (T - 1) / R, the number of resets the run performs
+ *                    (0 when T <= R; then it may be NULL).  The backward pass
+ *                    restarts each earlier window from it: a window's start is
+ *                    the initial matrix, not the previous window's end, so
+ *                    undoing updates cannot cross a reset.  Ignored otherwise.
  */
 typedef struct srwm_forward_args {
     const void* x;
@@ -136,7 +145,8 @@ typedef struct srwm_forward_args {
     int variant;
     void* stream;
     float* tape;   /* NULL, or [B][H][T][srwm_tape_row()] float32 (out): the
-                      record srwm_backward needs (see there); not with resets */
+                      record srwm_backward needs (see there) */
+    float* window_states;
 } srwm_forward_args_t;
 
 /* srwm_forward_ex -- the forward pass with every option.  Same edge cases,
@@ -202,7 +212,14 @@ int srwm_select_variant(int64_t d_in, int64_t d_out, int io_dtype, int n_lr,
  * Inputs: x and W_T as the forward pass saw and wrote them, the tape, gy
  * [B][T][H][d_out] float32, gW_T [B][H][m][d_in] float32 or NULL (zero).
  * With B == 0 a given dW0 is filled with zeros (one kernel launch); with
- * H == 0 nothing is launched.  Not covered: the reset ablation.  Same
+ * H == 0 nothing is launched.
+ * The reset ablation: reset_interval R > 0 as in the forward pass, with the
+ * forward pass's window_states.  Walking back into window w-1 at the reset
+ * before step wR, the kernel adds the adjoint of the state entering step wR
+ * (window w's share of dL/d(initial state)) to dW_init, sets the adjoint to
+ * zero (the discarded end state of window w-1 affects nothing) and restarts
+ * from window w-1's recorded end state.  dW_init is the sum of the windows'
+ * shares, taken from the last window to the first.  Same
  * conventions as the forward: device pointers, 16-byte aligned, nothing
  * allocated, asynchronous on `stream`; errors as there (SRWM_ERR_UNSUPPORTED
  * when srwm_backward_supported() is 0).
@@ -221,6 +238,8 @@ typedef struct srwm_backward_args {
     int apply_input_softmax;
     int n_lr;
     void* stream;
+    int64_t reset_interval;       /* 0, or R > 0 as in the forward pass */
+    const float* window_states;   /* the forward pass's, with R > 0 and T > R */
 } srwm_backward_args_t;
 
 int srwm_backward(const srwm_backward_args_t* args);

@@ -9,10 +9,12 @@ call raises.
 """
 from __future__ import annotations
 
+from typing import NamedTuple, Optional
+
 from . import _lib
 from .workloads import HEADLINE, WORKLOADS, Workload
 
-__all__ = ["forward", "backward", "srwm", "tape_row", "deltanet_forward", "deltanet_project", "fast_forward", "srdeltanet_forward", "fwp_supported", "supported", "backward_supported", "variants", "select_variant", "m_rows", "WORKLOADS", "HEADLINE", "Workload"]
+__all__ = ["forward", "backward", "srwm", "Tape", "tape_row", "deltanet_forward", "deltanet_project", "fast_forward", "srdeltanet_forward", "fwp_supported", "supported", "backward_supported", "variants", "select_variant", "m_rows", "WORKLOADS", "HEADLINE", "Workload"]
 
 
 def m_rows(d_in: int, d_out: int, n_lr: int = 4) -> int:
@@ -45,6 +47,19 @@ def select_variant(d_in: int, d_out: int, io_dtype: str, units: int, n_lr: int =
     return _lib.variants()[i]
 
 
+class Tape(NamedTuple):
+    """What ``forward(..., save_tape=True)`` records for ``backward``.
+
+    rows: [B, H, T, tape_row] float32, one row per unit and step (a_t,
+    phi(k_t), phi(q_t) - phi(k_t), the learning rates).
+    window_states: with reset_interval R > 0, the end state of every window
+    but the last, [B, H, (T - 1) // R, m, d_in] float32; else None.
+    """
+    rows: object
+    window_states: Optional[object]
+    reset_interval: int
+
+
 def tape_row(d_in: int, d_out: int, n_lr: int = 4) -> int:
     """Floats per step and unit in the backward tape."""
     return int(_lib.load().srwm_tape_row(d_in, d_out, n_lr))
@@ -63,7 +78,7 @@ def forward(x, W0, apply_input_softmax: bool = False, return_state: bool = False
     reset_interval: 0, or R > 0 to return every state to W0 before each step
           t > 0 with t % R == 0 (the reset ablation)
     save_tape: also record what ``backward`` needs (implies return_state);
-          the return value is then (y, W_T, tape).
+          the return value is then (y, W_T, Tape).
     Returns (y [B, T, H, d_out] in x's dtype, W_T [B, H, m, d_in] float32 or None).
     ``y`` / ``W_T`` may be passed preallocated; the call is asynchronous on
     ``stream`` (default: torch's current stream).
@@ -115,9 +130,12 @@ def forward(x, W0, apply_input_softmax: bool = False, return_state: bool = False
             raise ValueError("preallocated W_T has the wrong shape/dtype/device/layout")
     else:
         W_T = None
-    tape = None
+    tape = wstates = None
     if save_tape:
         tape = torch.empty((B, H, T, tape_row(d_in, d_out, n_lr)), dtype=torch.float32, device=x.device)
+        if reset_interval > 0:
+            n_res = (T - 1) // reset_interval if T > 0 else 0
+            wstates = torch.empty((B, H, n_res, m, d_in), dtype=torch.float32, device=x.device)
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
@@ -128,13 +146,14 @@ def forward(x, W0, apply_input_softmax: bool = False, return_state: bool = False
         B=B, T=T, H=H, d_in=d_in, d_out=d_out, m=m, io_dtype=io,
         apply_input_softmax=int(bool(apply_input_softmax)), n_lr=int(n_lr),
         w0_per_sequence=int(per_seq), reset_interval=int(reset_interval), variant=int(variant),
-        stream=handle, tape=tape.data_ptr() if tape is not None and tape.numel() else None)
+        stream=handle, tape=tape.data_ptr() if tape is not None and tape.numel() else None,
+        window_states=wstates.data_ptr() if wstates is not None and wstates.numel() else None)
     with torch.cuda.device(x.device):
         rc = lib.srwm_forward_ex(a)
     if rc != 0:
         raise RuntimeError(_lib.strerror(rc))
     if save_tape:
-        return y, W_T, tape
+        return y, W_T, Tape(tape, wstates, int(reset_interval))
     return y, W_T
 
 
@@ -142,15 +161,19 @@ def backward(x, W_T, tape, gy, gW_T=None, apply_input_softmax: bool = False, n_l
              shared_W0: bool = True, stream=None):
     """Gradients of L = sum_t <gy[t], y_t> + <gW_T, W_T> through the recurrence.
 
-    x, W_T, tape: the forward pass's input, final state and tape
-    (``forward(..., save_tape=True)``); gy [B, T, H, d_out] and gW_T
-    [B, H, m, d_in] (or None) float32.  Returns (dx [B, T, H, d_in] float32,
-    dW0): dW0 is [H, m, d_in] (summed over the batch) when shared_W0, else the
-    per-unit gradient [B, H, m, d_in].
+    x, W_T, tape: the forward pass's input, final state and Tape
+    (``forward(..., save_tape=True)``, with or without a reset interval); gy
+    [B, T, H, d_out] and gW_T [B, H, m, d_in] (or None) float32.  Returns
+    (dx [B, T, H, d_in] float32, dW0): dW0 is [H, m, d_in] (summed over the
+    batch) when shared_W0, else the per-unit gradient [B, H, m, d_in].
     """
     import torch
 
     lib = _lib.load()
+    if not isinstance(tape, Tape):
+        raise TypeError("tape must be the Tape that forward(..., save_tape=True) returned")
+    wstates, reset_interval = tape.window_states, tape.reset_interval
+    tape = tape.rows
     B, T, H, d_in = x.shape
     m = W_T.shape[-2]
     d_out = m - 2 * d_in - n_lr
@@ -170,6 +193,11 @@ def backward(x, W_T, tape, gy, gW_T=None, apply_input_softmax: bool = False, n_l
         raise ValueError("gy / W_T shapes do not match x")
     if tuple(tape.shape) != (B, H, T, tape_row(d_in, d_out, n_lr)):
         raise ValueError("tape shape does not match x")
+    if reset_interval > 0:
+        n_res = (T - 1) // reset_interval if T > 0 else 0
+        if (wstates is None or tuple(wstates.shape) != (B, H, n_res, m, d_in) or wstates.dtype != torch.float32
+                or wstates.device != x.device or not wstates.is_contiguous()):
+            raise ValueError("the tape's window states do not match x")
     dx = torch.empty((B, T, H, d_in), dtype=torch.float32, device=x.device)
     dWi = torch.empty((B, H, m, d_in), dtype=torch.float32, device=x.device)
     dW0 = torch.empty((H, m, d_in), dtype=torch.float32, device=x.device) if shared_W0 else None
@@ -184,7 +212,7 @@ def backward(x, W_T, tape, gy, gW_T=None, apply_input_softmax: bool = False, n_l
                           dx=ptr(dx), dW_init=ptr(dWi), dW0=ptr(dW0), B=B, T=T, H=H, d_in=d_in,
                           d_out=d_out, m=m, io_dtype=io,
                           apply_input_softmax=int(bool(apply_input_softmax)), n_lr=int(n_lr),
-                          stream=handle)
+                          stream=handle, reset_interval=int(reset_interval), window_states=ptr(wstates))
     with torch.cuda.device(x.device):
         rc = lib.srwm_backward(a)
     if rc != 0:
@@ -199,18 +227,20 @@ def _autograd_function():
         """y, W_T = srwm(x, W0) with gradients for x and W0 from ``backward``."""
 
         @staticmethod
-        def forward(ctx, x, W0, apply_input_softmax, n_lr):
+        def forward(ctx, x, W0, apply_input_softmax, n_lr, reset_interval):
             y, W_T, tape = forward(x, W0, apply_input_softmax=apply_input_softmax, n_lr=n_lr,
-                                   save_tape=True)
-            ctx.save_for_backward(x, W_T, tape)
-            ctx.flags = (bool(apply_input_softmax), int(n_lr), W0.dim() == 3)
+                                   reset_interval=reset_interval, save_tape=True)
+            ws = tape.window_states if tape.window_states is not None else W_T.new_empty(0)
+            ctx.save_for_backward(x, W_T, tape.rows, ws)
+            ctx.flags = (bool(apply_input_softmax), int(n_lr), W0.dim() == 3, int(reset_interval))
             ctx.set_materialize_grads(False)
             return y, W_T
 
         @staticmethod
         def backward(ctx, gy, gW_T):
-            x, W_T, tape = ctx.saved_tensors
-            flag, n_lr, shared = ctx.flags
+            x, W_T, rows, ws = ctx.saved_tensors
+            flag, n_lr, shared, reset_interval = ctx.flags
+            tape = Tape(rows, ws if reset_interval > 0 else None, reset_interval)
             if gy is None:
                 d_out = W_T.shape[-2] - 2 * x.shape[-1] - n_lr
                 gy = torch.zeros((*x.shape[:3], d_out), dtype=torch.float32, device=x.device)
@@ -219,14 +249,14 @@ def _autograd_function():
             gW_T = None if gW_T is None else gW_T.contiguous()
             dx, dW0 = backward(x, W_T, tape, gy, gW_T, apply_input_softmax=flag, n_lr=n_lr,
                                shared_W0=shared)
-            return dx.to(x.dtype), dW0, None, None
+            return dx.to(x.dtype), dW0, None, None, None
 
     return SRWMFunction
 
 
-def srwm(x, W0, apply_input_softmax: bool = False, n_lr: int = 4):
+def srwm(x, W0, apply_input_softmax: bool = False, n_lr: int = 4, reset_interval: int = 0):
     """Differentiable forward: returns (y, W_T); gradients flow to x and W0."""
-    return _autograd_function().apply(x, W0, apply_input_softmax, n_lr)
+    return _autograd_function().apply(x, W0, apply_input_softmax, n_lr, reset_interval)
 
 
 def fwp_supported(d_key: int, d_v: int) -> bool:

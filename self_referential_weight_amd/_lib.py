@@ -31,6 +31,7 @@ class ForwardArgs(ctypes.Structure):
         ("variant", ctypes.c_int),
         ("stream", ctypes.c_void_p),
         ("tape", ctypes.c_void_p),
+        ("window_states", ctypes.c_void_p),
     ]
 
 
@@ -55,6 +56,8 @@ class BackwardArgs(ctypes.Structure):
         ("apply_input_softmax", ctypes.c_int),
         ("n_lr", ctypes.c_int),
         ("stream", ctypes.c_void_p),
+        ("reset_interval", ctypes.c_int64),
+        ("window_states", ctypes.c_void_p),
     ]
 
 

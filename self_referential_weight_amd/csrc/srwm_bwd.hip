@@ -17,14 +17,17 @@ using namespace srwm;
 // Backward kernels: (d_in, d_out, waves per unit, lanes per row, learning
 // rates), both I/O dtypes.
 using BwdFn = void (*)(const void*, const float*, const float*, const float*, const float*, float*,
-                       float*, int, int, int);
+                       float*, int, int, int, int, const float*);
 struct BwdVariant {
-    int d_in, d_out, io, nlr, nw;
+    int d_in, d_out, io, nlr, nw, reset;
     BwdFn fn;
 };
-#define SRWM_BWD(DI, DO, NW, P, NLR)                                                            \
-    BwdVariant{DI, DO, SRWM_IO_F32, NLR, NW, &srwm_bwd_kernel<DI, DO, NW, P, NLR, false>},      \
-        BwdVariant{DI, DO, SRWM_IO_BF16, NLR, NW, &srwm_bwd_kernel<DI, DO, NW, P, NLR, true>}
+// Both I/O dtypes, without and with the reset ablation's window restarts.
+#define SRWM_BWD(DI, DO, NW, P, NLR)                                                                  \
+    BwdVariant{DI, DO, SRWM_IO_F32, NLR, NW, 0, &srwm_bwd_kernel<DI, DO, NW, P, NLR, false, false>},  \
+        BwdVariant{DI, DO, SRWM_IO_BF16, NLR, NW, 0, &srwm_bwd_kernel<DI, DO, NW, P, NLR, true, false>}, \
+        BwdVariant{DI, DO, SRWM_IO_F32, NLR, NW, 1, &srwm_bwd_kernel<DI, DO, NW, P, NLR, false, true>},  \
+        BwdVariant{DI, DO, SRWM_IO_BF16, NLR, NW, 1, &srwm_bwd_kernel<DI, DO, NW, P, NLR, true, true>}
 const BwdVariant kBwdVariants[] = {
     SRWM_BWD(8, 8, 1, 8, 4), SRWM_BWD(16, 16, 1, 4, 4), SRWM_BWD(64, 64, 4, 16, 4),
     SRWM_BWD(8, 8, 1, 8, 1), SRWM_BWD(16, 16, 1, 4, 1), SRWM_BWD(64, 64, 4, 16, 1),
@@ -40,27 +43,34 @@ int backward_impl(const srwm_backward_args_t* a)
     if (m != d_out + 2 * d_in + a->n_lr) return SRWM_ERR_SHAPE;
     if (a->io_dtype != SRWM_IO_F32 && a->io_dtype != SRWM_IO_BF16) return SRWM_ERR_ARG;
     if (a->apply_input_softmax != 0 && a->apply_input_softmax != 1) return SRWM_ERR_ARG;
+    if (a->reset_interval < 0 || a->reset_interval > INT32_MAX) return SRWM_ERR_ARG;
     int vi = -1;
+    const int want_reset = a->reset_interval > 0 ? 1 : 0;
     for (int i = 0; i < kNumBwdVariants; ++i) {
         const BwdVariant& v = kBwdVariants[i];
-        if (v.d_in == d_in && v.d_out == d_out && v.io == a->io_dtype && v.nlr == a->n_lr) vi = i;
+        if (v.d_in == d_in && v.d_out == d_out && v.io == a->io_dtype && v.nlr == a->n_lr && v.reset == want_reset)
+            vi = i;
     }
     if (vi < 0) return SRWM_ERR_UNSUPPORTED;
     const int64_t es = a->io_dtype == SRWM_IO_BF16 ? 2 : 4;
-    int64_t units, steps, nx, ndx, ngy, nst, ntape, nw0;
+    int64_t units, steps, nx, ndx, ngy, nst, ntape, nw0, nws;
+    // the forward pass's end states of all windows but the last
+    const int64_t nres = (a->reset_interval > 0 && T > 0) ? (T - 1) / a->reset_interval : 0;
     if (!mul_ok(B, H, &units) || !mul_ok(units, T, &steps) || !mul_ok(steps, d_in * es, &nx) ||
         !mul_ok(steps, d_in * 4, &ndx) || !mul_ok(steps, d_out * 4, &ngy) ||
         !mul_ok(units, m * d_in * 4, &nst) || !mul_ok(steps, tape_row(d_in, d_out, a->n_lr) * 4, &ntape) ||
-        !mul_ok(H, m * d_in * 4, &nw0))
+        !mul_ok(H, m * d_in * 4, &nw0) || !mul_ok(nst, nres, &nws))
         return SRWM_ERR_SHAPE;
     if (units > INT32_MAX || T > INT32_MAX || H > INT32_MAX) return SRWM_ERR_SHAPE;
     if ((nst > 0 && (a->W_T == nullptr || a->dW_init == nullptr)) || (ntape > 0 && a->tape == nullptr) ||
-        (nx > 0 && (a->x == nullptr || a->dx == nullptr)) || (ngy > 0 && a->gy == nullptr))
+        (nx > 0 && (a->x == nullptr || a->dx == nullptr)) || (ngy > 0 && a->gy == nullptr) ||
+        (nws > 0 && a->window_states == nullptr))
         return SRWM_ERR_NULL;
     if ((reinterpret_cast<uintptr_t>(a->x) | reinterpret_cast<uintptr_t>(a->W_T) |
          reinterpret_cast<uintptr_t>(a->tape) | reinterpret_cast<uintptr_t>(a->gy) |
          reinterpret_cast<uintptr_t>(a->gW_T) | reinterpret_cast<uintptr_t>(a->dx) |
-         reinterpret_cast<uintptr_t>(a->dW_init) | reinterpret_cast<uintptr_t>(a->dW0)) & 15u)
+         reinterpret_cast<uintptr_t>(a->dW_init) | reinterpret_cast<uintptr_t>(a->dW0) |
+         reinterpret_cast<uintptr_t>(nws > 0 ? a->window_states : nullptr)) & 15u)
         return SRWM_ERR_ARG;
     hipStream_t st = static_cast<hipStream_t>(a->stream);
     auto sum_over_batch = [&]() -> int {
@@ -77,12 +87,13 @@ int backward_impl(const srwm_backward_args_t* a)
         return e == hipSuccess ? SRWM_OK : SRWM_ERR_HIP;
     };
     if (units == 0) return sum_over_batch();
-    const void* ins[] = {a->x, a->W_T, a->tape, a->gy, a->gW_T};
-    const int64_t nins[] = {nx, nst, ntape, ngy, a->gW_T ? nst : 0};
+    const float* wstates = nws > 0 ? a->window_states : nullptr;
+    const void* ins[] = {a->x, a->W_T, a->tape, a->gy, a->gW_T, wstates};
+    const int64_t nins[] = {nx, nst, ntape, ngy, a->gW_T ? nst : 0, nws};
     void* outs[] = {a->dx, a->dW_init, a->dW0};
     const int64_t nouts[] = {ndx, nst, a->dW0 ? nw0 : 0};
     for (int o = 0; o < 3; ++o) {
-        for (int i = 0; i < 5; ++i)
+        for (int i = 0; i < 6; ++i)
             if (ranges_overlap(outs[o], nouts[o], ins[i], nins[i])) return SRWM_ERR_ALIAS;
         for (int o2 = o + 1; o2 < 3; ++o2)
             if (ranges_overlap(outs[o], nouts[o], outs[o2], nouts[o2])) return SRWM_ERR_ALIAS;
@@ -96,8 +107,10 @@ int backward_impl(const srwm_backward_args_t* a)
     float* dx = a->dx;
     float* dWi = a->dW_init;
     int Ti = static_cast<int>(T), Hi = static_cast<int>(H), fl = a->apply_input_softmax;
+    int rst = static_cast<int>(a->reset_interval);
     void* args[] = {const_cast<void**>(&x), const_cast<float**>(&WTp), const_cast<float**>(&tape),
-                    const_cast<float**>(&gy), const_cast<float**>(&gWT), &dx, &dWi, &Ti, &Hi, &fl};
+                    const_cast<float**>(&gy), const_cast<float**>(&gWT), &dx, &dWi, &Ti, &Hi, &fl, &rst,
+                    const_cast<float**>(&wstates)};
     const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(v.fn),
                                            dim3(static_cast<unsigned>(units)), dim3(v.nw * kWave), args, 0, st);
     if (err != hipSuccess) return SRWM_ERR_HIP;

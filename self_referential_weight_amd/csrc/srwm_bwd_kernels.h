@@ -105,12 +105,13 @@ struct ColExchange {
     __device__ __forceinline__ static bool writer(int lane) { return (lane & KEEP_MASK) == 0; }
 };
 
-template <int D_IN, int D_OUT, int NW, int P, int NLR, bool BF16>
+template <int D_IN, int D_OUT, int NW, int P, int NLR, bool BF16, bool RESET>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * kWave, NW * kWave), amdgpu_waves_per_eu(2)))
 void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin,
                      const float* __restrict__ tape, const float* __restrict__ gy,
                      const float* __restrict__ gWT, float* __restrict__ dx,
-                     float* __restrict__ dWinit, int T, int H, int in_softmax)
+                     float* __restrict__ dWinit, int T, int H, int in_softmax, int reset_interval,
+                     const float* __restrict__ wstates)
 {
     constexpr int NT = NW * kWave;
     constexpr int M = D_OUT + 2 * D_IN + NLR;
@@ -290,6 +291,37 @@ void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin
         for (int c = 0; c < L; ++c) part[a][c] = 0.f;
     float u_next = 0.f;  // u_{t+1}[lane]
 
+    // Reset ablation (built only into the RESET variants): the windows' shares
+    // of dL/d(initial state) are summed into this unit's dWinit, from the last
+    // window to the first, onto zeros written first; each thread adds to its
+    // own elements, so each load follows the same thread's store.
+    const int n_resets = (RESET && reset_interval > 0 && T > 0) ? (T - 1) / reset_interval : 0;
+    int next_reset = n_resets * reset_interval;  // the latest step that starts a window, or 0
+    float* __restrict__ dwi_unit = dWinit + (int64_t)unit * M * D_IN;
+    auto add_share = [&]() {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = rg + G * r;
+            if (row < M) {
+                float prev[L];
+                load_f32<L>(dwi_unit + row * D_IN + p * L, prev);
+#pragma unroll
+                for (int c = 0; c < L; ++c) prev[c] += wh[r][c];
+                store_f32<L>(dwi_unit + row * D_IN + p * L, prev);
+            }
+        }
+    };
+    if (n_resets > 0) {
+        float zero[L];
+#pragma unroll
+        for (int c = 0; c < L; ++c) zero[c] = 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = rg + G * r;
+            if (row < M) store_f32<L>(dwi_unit + row * D_IN + p * L, zero);
+        }
+    }
+
     if (T > 0) {
         fetch(T - 1);
         stage((T - 1) % 3);
@@ -420,6 +452,26 @@ void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin
             }
         }
         slot = slot_prev;
+
+        // Reset ablation: step t = wR started window w from the initial state.
+        // The adjoint now held is window w's share of dL/d(initial state); the
+        // end state of window w-1, which the reset discarded, has a zero adjoint,
+        // and the walk continues from that end state as the forward pass
+        // recorded it (undoing updates cannot cross the reset).
+        if (RESET && t == next_reset && t > 0) {
+            add_share();
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int c = 0; c < L; ++c) wh[r][c] = 0.f;
+            const float* __restrict__ ws = wstates + ((int64_t)unit * n_resets + (t / reset_interval - 1)) * M * D_IN;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int row = rg + G * r;
+                if (row < M) load_f32<L>(ws + row * D_IN + p * L, w[r]);
+            }
+            next_reset -= reset_interval;
+        }
     }
 
     if (T > 0) {
@@ -434,11 +486,16 @@ void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin
         if (wave == 0) store_dx(0, uh0_j, u_next);
     }
 
-    // dL/d(initial state of this unit)
+    // dL/d(initial state of this unit): with resets, the first window's share
+    // added to the later windows' sum
+    if (n_resets > 0) {
+        add_share();
+    } else {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int row = rg + G * r;
-        if (row < M) store_f32<L>(dWinit + ((int64_t)unit * M + row) * D_IN + p * L, wh[r]);
+        for (int r = 0; r < R; ++r) {
+            const int row = rg + G * r;
+            if (row < M) store_f32<L>(dwi_unit + row * D_IN + p * L, wh[r]);
+        }
     }
 }
 

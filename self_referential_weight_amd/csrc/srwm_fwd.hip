@@ -44,7 +44,7 @@ using namespace srwm;
 
 // ----------------------------------------------------------------------------
 // Variant table.
-using KernelFn = void (*)(const void*, const float*, void*, float*, float*, int, int, int, int, int);
+using KernelFn = void (*)(const void*, const float*, void*, float*, float*, float*, int, int, int, int, int);
 
 struct Variant {
     int d_in, d_out, io, nw, p, wpe, nlr, fused, reset, tape, is_auto;
@@ -52,7 +52,8 @@ struct Variant {
 };
 
 // SCHED: 0 phased, 1 phased with the reset ablation, 2 fused, 3 phased
-// writing the backward tape.
+// writing the backward tape, 4 phased with the reset ablation writing the
+// backward tape (and the windows' end states).
 template <int D_IN, int D_OUT, int NW, int P, int WPE, int NLR, int SCHED, bool BF16>
 constexpr Variant make_variant(int is_auto)
 {
@@ -61,8 +62,10 @@ constexpr Variant make_variant(int is_auto)
         return Variant{D_IN, D_OUT, io, NW, P, WPE, NLR, 1, 0, 0, is_auto,
                        &srwm_fwd_fused_kernel<D_IN, D_OUT, NW, P, WPE, NLR, BF16>};
     else
-        return Variant{D_IN, D_OUT, io, NW, P, WPE, NLR, 0, SCHED == 1, SCHED == 3, is_auto,
-                       &srwm_fwd_kernel<D_IN, D_OUT, NW, P, WPE, NLR, SCHED == 1, SCHED == 3, BF16>};
+        return Variant{D_IN, D_OUT, io, NW, P, WPE, NLR, 0, SCHED == 1 || SCHED == 4, SCHED == 3 || SCHED == 4,
+                       is_auto,
+                       &srwm_fwd_kernel<D_IN, D_OUT, NW, P, WPE, NLR, SCHED == 1 || SCHED == 4,
+                                        SCHED == 3 || SCHED == 4, BF16>};
 }
 
 // Both I/O dtypes of one geometry: (d_in, d_out, waves per unit, lanes per
@@ -80,6 +83,9 @@ constexpr Variant make_variant(int is_auto)
 #define SRWM_BOTH_IO_TAPE(DI, DO, NW, P, WPE, NLR, AUTO)              \
     make_variant<DI, DO, NW, P, WPE, NLR, 3, false>(AUTO),             \
         make_variant<DI, DO, NW, P, WPE, NLR, 3, true>(AUTO)
+#define SRWM_BOTH_IO_TAPE_RESET(DI, DO, NW, P, WPE, NLR, AUTO)        \
+    make_variant<DI, DO, NW, P, WPE, NLR, 4, false>(AUTO),             \
+        make_variant<DI, DO, NW, P, WPE, NLR, 4, true>(AUTO)
 
 const Variant kVariants[] = {
     // small shapes (tests, latency-bound workloads)
@@ -151,6 +157,17 @@ const Variant kVariants[] = {
     SRWM_BOTH_IO_TAPE(64, 64, 4, 8, 1, 1, 0),
     SRWM_BOTH_IO_TAPE(64, 64, 4, 4, 1, 1, 1),
     SRWM_BOTH_IO_TAPE(64, 64, 8, 8, 1, 1, 1),
+    // ... with the reset ablation (they also record each window's end state)
+    SRWM_BOTH_IO_TAPE_RESET(8, 8, 1, 8, 1, 4, 1),
+    SRWM_BOTH_IO_TAPE_RESET(16, 16, 1, 4, 1, 4, 1),
+    SRWM_BOTH_IO_TAPE_RESET(64, 64, 1, 4, 2, 4, 1),
+    SRWM_BOTH_IO_TAPE_RESET(64, 64, 4, 4, 1, 4, 1),
+    SRWM_BOTH_IO_TAPE_RESET(64, 64, 8, 8, 1, 4, 1),
+    SRWM_BOTH_IO_TAPE_RESET(8, 8, 1, 8, 1, 1, 1),
+    SRWM_BOTH_IO_TAPE_RESET(16, 16, 1, 4, 1, 1, 1),
+    SRWM_BOTH_IO_TAPE_RESET(64, 64, 1, 4, 2, 1, 1),
+    SRWM_BOTH_IO_TAPE_RESET(64, 64, 4, 4, 1, 1, 1),
+    SRWM_BOTH_IO_TAPE_RESET(64, 64, 8, 8, 1, 1, 1),
 };
 
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
@@ -208,15 +225,17 @@ int forward_impl(const srwm_forward_args_t* a)
     if (a->variant < -1) return SRWM_ERR_ARG;
     const bool reset = a->reset_interval > 0;
     const bool want_tape = a->tape != nullptr;
-    if (reset && want_tape) return SRWM_ERR_ARG;  // the backward does not cover resets
     const int64_t units_hint = (B > 0 && H > INT64_MAX / B) ? INT64_MAX : B * H;
     const int vi = find_variant(d_in, d_out, a->io_dtype, a->n_lr, reset, want_tape, a->variant, units_hint);
     if (vi < 0) return a->variant >= 0 ? SRWM_ERR_ARG : SRWM_ERR_UNSUPPORTED;
     const int64_t es = a->io_dtype == SRWM_IO_BF16 ? 2 : 4;
-    int64_t units, steps, nx, ny, nw0, nwt, ntape;
+    int64_t units, steps, nx, ny, nw0, nwt, ntape, nws;
+    // with a tape and resets: the end states of all windows but the last
+    const int64_t nres = (reset && want_tape && T > 0) ? (T - 1) / a->reset_interval : 0;
     if (!mul_ok(B, H, &units) || !mul_ok(units, T, &steps) || !mul_ok(steps, d_in * es, &nx) ||
         !mul_ok(steps, d_out * es, &ny) || !mul_ok(a->w0_per_sequence ? units : H, m * d_in * 4, &nw0) ||
-        !mul_ok(units, m * d_in * 4, &nwt) || !mul_ok(steps, tape_row(d_in, d_out, a->n_lr) * 4, &ntape))
+        !mul_ok(units, m * d_in * 4, &nwt) || !mul_ok(steps, tape_row(d_in, d_out, a->n_lr) * 4, &ntape) ||
+        !mul_ok(nwt, nres, &nws))
         return SRWM_ERR_SHAPE;
     if (!want_tape) ntape = 0;
     if (units > INT32_MAX || T > INT32_MAX || H > INT32_MAX) return SRWM_ERR_SHAPE;
@@ -225,12 +244,14 @@ int forward_impl(const srwm_forward_args_t* a)
     void* y = a->y;
     float* W_T = a->W_T;
     float* tape = a->tape;
-    if ((nx > 0 && x == nullptr) || (ny > 0 && y == nullptr) || (nw0 > 0 && units > 0 && W0 == nullptr))
+    float* wstates = nws > 0 ? a->window_states : nullptr;
+    if ((nx > 0 && x == nullptr) || (ny > 0 && y == nullptr) || (nw0 > 0 && units > 0 && W0 == nullptr) ||
+        (nws > 0 && wstates == nullptr))
         return SRWM_ERR_NULL;
     // The kernels move 16-byte pieces: every buffer must be 16-byte aligned.
     if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(W0) |
          reinterpret_cast<uintptr_t>(y) | reinterpret_cast<uintptr_t>(W_T) |
-         reinterpret_cast<uintptr_t>(tape)) & 15u)
+         reinterpret_cast<uintptr_t>(tape) | reinterpret_cast<uintptr_t>(wstates)) & 15u)
         return SRWM_ERR_ARG;
     if (units == 0) return SRWM_OK;
     if (W_T == nullptr) nwt = 0;
@@ -238,14 +259,17 @@ int forward_impl(const srwm_forward_args_t* a)
         ranges_overlap(x, nx, W_T, nwt) || ranges_overlap(W0, nw0, y, ny) ||
         ranges_overlap(y, ny, W_T, nwt) || ranges_overlap(tape, ntape, x, nx) ||
         ranges_overlap(tape, ntape, W0, nw0) || ranges_overlap(tape, ntape, y, ny) ||
-        ranges_overlap(tape, ntape, W_T, nwt))
+        ranges_overlap(tape, ntape, W_T, nwt) || ranges_overlap(wstates, nws, x, nx) ||
+        ranges_overlap(wstates, nws, W0, nw0) || ranges_overlap(wstates, nws, y, ny) ||
+        ranges_overlap(wstates, nws, W_T, nwt) || ranges_overlap(wstates, nws, tape, ntape))
         return SRWM_ERR_ALIAS;
     if (T == 0 && W_T == nullptr) return SRWM_OK;
 
     const Variant& v = kVariants[vi];
     int Ti = static_cast<int>(T), Hi = static_cast<int>(H), fl = a->apply_input_softmax;
     int per_seq = a->w0_per_sequence, rst = static_cast<int>(a->reset_interval);
-    void* args[] = {const_cast<void**>(&x), const_cast<float**>(&W0), &y, &W_T, &tape, &Ti, &Hi, &fl, &per_seq, &rst};
+    void* args[] = {const_cast<void**>(&x), const_cast<float**>(&W0), &y, &W_T, &tape, &wstates, &Ti, &Hi, &fl,
+                    &per_seq, &rst};
     const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(v.fn),
                                            dim3(static_cast<unsigned>(units)), dim3(v.nw * kWave),
                                            args, 0, static_cast<hipStream_t>(a->stream));
@@ -275,6 +299,7 @@ srwm_forward_args_t basic_args(const void* x, const float* W0, void* y, float* W
     a.variant = variant;
     a.stream = stream;
     a.tape = nullptr;
+    a.window_states = nullptr;
     return a;
 }
 

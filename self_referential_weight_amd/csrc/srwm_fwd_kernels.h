@@ -280,7 +280,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * kWave, NW * kWave),
                           amdgpu_waves_per_eu(WPE)))
 void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
                      void* __restrict__ yv, float* __restrict__ WT, float* __restrict__ tape,
-                     int T, int H, int in_softmax, int w0_per_seq, int reset_interval)
+                     float* __restrict__ wstates, int T, int H, int in_softmax, int w0_per_seq,
+                     int reset_interval)
 {
     using Gm = Geom<D_IN, D_OUT, NW, P, NLR>;
     constexpr int M = Gm::M, MAIN = Gm::MAIN, ROWS = Gm::ROWS;
@@ -343,6 +344,17 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
         }
     };
     load_w0();
+    // W -> dst[m][d_in] (W_T, or with the tape and resets the end state of a window).
+    auto store_w = [&](float* __restrict__ wdst) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = rg + G * r;
+            if (row < ROWS) store_f32<L>(wdst + (int64_t)row * D_IN + p * L, w[r]);
+        }
+        if constexpr (BETA_SEP) {
+            if (wave == 0 && brow < NLR) store_f32<LB>(wdst + (int64_t)(MAIN + brow) * D_IN + bcol, wb);
+        }
+    };
 
     XStage<D_IN, D_OUT, NW, P, BF16> xs(tid, xv, x0, x_step, T);
 
@@ -369,6 +381,11 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
                     // step t > 0 with t % R == 0 the state returns to W0.
                     if (reset_interval > 0) {
                         if (until_reset == 0) {
+                            if constexpr (TAPE) {
+                                // the backward pass restarts window t/R - 1 from its end state
+                                const int nres = (T - 1) / reset_interval;
+                                store_w(wstates + ((int64_t)unit * nres + (t / reset_interval - 1)) * M * D_IN);
+                            }
                             load_w0();
                             until_reset = reset_interval;
                         }
@@ -498,17 +515,7 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
     }
 
     // ---- a7: W_T[b,h] <- W.
-    if (WT != nullptr) {
-        float* __restrict__ wdst = WT + (int64_t)unit * M * D_IN;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int row = rg + G * r;
-            if (row < ROWS) store_f32<L>(wdst + (int64_t)row * D_IN + p * L, w[r]);
-        }
-        if constexpr (BETA_SEP) {
-            if (wave == 0 && brow < NLR) store_f32<LB>(wdst + (int64_t)(MAIN + brow) * D_IN + bcol, wb);
-        }
-    }
+    if (WT != nullptr) store_w(WT + (int64_t)unit * M * D_IN);
 }
 
 // ----------------------------------------------------------------------------
@@ -526,7 +533,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * kWave, NW * kWave),
                           amdgpu_waves_per_eu(WPE)))
 void srwm_fwd_fused_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
                            void* __restrict__ yv, float* __restrict__ WT, float* /*tape: not written*/,
-                           int T, int H, int in_softmax, int w0_per_seq,
+                           float* /*window states: not written*/, int T, int H, int in_softmax, int w0_per_seq,
                            int /*reset_interval: not supported by this schedule*/)
 {
     using Gm = Geom<D_IN, D_OUT, NW, P, NLR>;

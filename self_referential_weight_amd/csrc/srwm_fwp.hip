@@ -482,6 +482,7 @@ int srdeltanet_impl(const srwm_srdeltanet_args_t* a)
     f.variant = -1;
     f.stream = a->stream;
     f.tape = nullptr;
+    f.window_states = nullptr;
     rc = srwm_forward_ex(&f);
     if (rc != SRWM_OK) return rc;
     if (a->T == 0) {

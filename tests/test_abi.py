@@ -29,7 +29,7 @@ def test_header_symbols_exported():
 
 def test_version_and_strerror():
     lib = _lib.load()
-    assert lib.srwm_version() == 300
+    assert lib.srwm_version() == 400
     for code in (OK, E_NULL, E_SHAPE, E_UNSUP, E_ALIAS, E_HIP, E_ARG):
         assert _lib.strerror(code).startswith("SRWM_")
     assert "unknown" in _lib.strerror(-99)
@@ -191,11 +191,21 @@ def test_tape_row_and_backward_support():
         for io in ("f32", "bf16"):
             for n_lr in (4, 1):
                 assert (d, d, io, n_lr) in tape
-    assert not any(v["writes_tape"] and v["supports_reset"] for v in vs)
+    # ... and, for the reset ablation, variants that write the tape and the windows' end states
+    tape_reset = {(v["d_in"], v["d_out"], v["io_dtype"], v["n_lr"]) for v in vs
+                  if v["writes_tape"] and v["supports_reset"]}
+    assert tape_reset == tape
+
+
+FAKE_WS = 0xB0000000
 
 
 def test_forward_tape_validation():
-    assert call_ex(tape=FAKE_TAPE, reset_interval=5) == E_ARG       # backward does not cover resets
+    # with resets the tape needs the windows' end states (T = 3, R = 1: two resets)
+    assert call_ex(tape=FAKE_TAPE, reset_interval=1) == E_NULL
+    assert call_ex(tape=FAKE_TAPE, reset_interval=1, window_states=FAKE_WS + 4) == E_ARG
+    assert call_ex(tape=FAKE_TAPE, reset_interval=1, window_states=FAKE_Y) == E_ALIAS
+    assert call_ex(tape=FAKE_TAPE, reset_interval=1, window_states=FAKE_TAPE + 64) == E_ALIAS
     assert call_ex(tape=FAKE_TAPE + 4) == E_ARG                     # misaligned
     assert call_ex(tape=FAKE_X + 16) == E_ALIAS                     # overlaps x
     assert call_ex(tape=FAKE_TAPE, d_in=128, d_out=128) == E_UNSUP  # no tape variant at d=128
@@ -236,6 +246,11 @@ def call_bwd(**kw):
     (dict(dW0=FAKE_DWI + 16), E_ALIAS),
     (dict(gW_T=FAKE_DWI), E_ALIAS),
     (dict(dW_init=FAKE_TAPE + 64), E_ALIAS),
+    (dict(reset_interval=-1), E_ARG),
+    (dict(reset_interval=2 ** 40), E_ARG),
+    (dict(reset_interval=1), E_NULL),                            # T = 3 > R: window states needed
+    (dict(reset_interval=1, window_states=FAKE_WS + 8), E_ARG),
+    (dict(reset_interval=1, window_states=FAKE_DWI), E_ALIAS),
 ])
 def test_backward_validation(kw, code):
     assert call_bwd(**kw) == code

@@ -34,11 +34,11 @@ def to_dev(a, io_dtype="f32"):
     return t.to(torch.bfloat16) if io_dtype == "bf16" else t
 
 
-def gpu_grads(w, x, W0, gy, gW, flag, shared=True, variant=-1):
+def gpu_grads(w, x, W0, gy, gW, flag, shared=True, variant=-1, reset_interval=0):
     srwm = _srwm()
     xd = to_dev(x, w.io_dtype)
     y, WT, tape = srwm.forward(xd, to_dev(W0), apply_input_softmax=flag, n_lr=w.n_lr, save_tape=True,
-                               variant=variant)
+                               variant=variant, reset_interval=reset_interval)
     dx, dW = srwm.backward(xd, WT, tape, to_dev(gy), None if gW is None else to_dev(gW),
                            apply_input_softmax=flag, n_lr=w.n_lr, shared_W0=shared)
     torch.cuda.synchronize()
@@ -200,3 +200,87 @@ def test_autograd_function(name):
         check_grad(xd.grad.cpu().numpy(), dx_ref2, "W_T-only dx")
     else:
         assert rel_l2(xd.grad.float().cpu().numpy(), dx_ref2) < 1e-2
+
+
+# ---------------------------------------------------------------------------
+# The reset ablation (review page Sec. 4.5): every R steps the state returns to
+# the initial matrix.  The taped forward records each window's end state; the
+# backward restarts every earlier window from it.
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("n_lr", [4, 1])
+@pytest.mark.parametrize("R", [1, 13])
+def test_backward_reset_parity(name, n_lr, R):
+    w = WORKLOADS[name].with_(n_lr=n_lr, **SMALL[name])
+    flag = w.apply_input_softmax
+    say(f"[bwd] reset R={R} {name} B={w.B} H={w.H} T={w.T} n_lr={n_lr}")
+    x, W0, gy, gW = gen_x(w), gen_W0(w), gen_gy(w), gen_gW(w)
+    y, WT, dx, dW0 = gpu_grads(w, x, W0, gy, gW, flag, reset_interval=R)
+    y_ref, WT_ref = oracle.forward(x, W0, flag, n_lr=n_lr, reset_interval=R)
+    check_y(y, y_ref, w.io_dtype, "taped forward with resets")
+    check_state(WT, WT_ref, "taped forward with resets")
+    dx_ref, dW0_ref = oracle_bwd.grads(x, W0, flag, gy, gW, n_lr=n_lr, reset_interval=R)
+    rx = check_grad(dx, dx_ref, "dx")
+    rw = check_grad(dW0, dW0_ref, "dW0")
+    say(f"[bwd] relL2 dx={rx:.2e} dW0={rw:.2e}")
+
+
+@pytest.mark.parametrize("name", ["fewshot_d64", "rl_d64_bf16"])
+def test_window_states_are_window_end_states(name):
+    # Window k covers steps [kR, (k+1)R) and starts from W0, so its end state
+    # is the final state of a separate run over those steps alone.
+    srwm = _srwm()
+    w = WORKLOADS[name].with_(B=2, H=2, T=50)
+    R = 13
+    flag = w.apply_input_softmax
+    x, W0 = gen_x(w), gen_W0(w)
+    _, _, tape = srwm.forward(to_dev(x, w.io_dtype), to_dev(W0), apply_input_softmax=flag, reset_interval=R,
+                              save_tape=True)
+    torch.cuda.synchronize()
+    ws = tape.window_states.cpu().numpy()
+    assert ws.shape == (2, 2, (50 - 1) // R, w.m, w.d_in)
+    for k in range(ws.shape[2]):
+        _, ref = oracle.forward(np.ascontiguousarray(x[:, k * R:(k + 1) * R]), W0, flag)
+        check_state(ws[:, :, k], ref, f"window {k} end state")
+
+
+def test_backward_reset_longer_than_sequence():
+    # R >= T: no reset happens and no window state is recorded; the gradient
+    # is the plain one.
+    w = WORKLOADS["fewshot_d64"].with_(B=2, H=2, T=30)
+    x, W0, gy, gW = gen_x(w), gen_W0(w), gen_gy(w), gen_gW(w)
+    _, _, dx, dW0 = gpu_grads(w, x, W0, gy, gW, False, reset_interval=30)
+    _, _, dx1, dW01 = gpu_grads(w, x, W0, gy, gW, False)
+    np.testing.assert_array_equal(dx, dx1)
+    np.testing.assert_array_equal(dW0, dW01)
+
+
+def test_backward_every_taped_reset_variant():
+    srwm = _srwm()
+    done = 0
+    for v in srwm.variants():
+        if not (v["writes_tape"] and v["supports_reset"]):
+            continue
+        w = Workload("taped_reset", B=2, H=2, d_in=v["d_in"], d_out=v["d_out"], T=45, io_dtype=v["io_dtype"],
+                     apply_input_softmax=True, return_state=True, w0_std=v["d_in"] ** -0.5, seed=v["index"],
+                     n_lr=v["n_lr"])
+        say(f"[bwd] taped reset variant {v}")
+        x, W0, gy, gW = gen_x(w), gen_W0(w), gen_gy(w), gen_gW(w)
+        _, _, dx, dW0 = gpu_grads(w, x, W0, gy, gW, True, variant=v["index"], reset_interval=10)
+        dx_ref, dW0_ref = oracle_bwd.grads(x, W0, True, gy, gW, n_lr=w.n_lr, reset_interval=10)
+        check_grad(dx, dx_ref, f"variant {v['index']} dx")
+        check_grad(dW0, dW0_ref, f"variant {v['index']} dW0")
+        done += 1
+    assert done >= 10
+
+
+def test_autograd_with_resets():
+    srwm = _srwm()
+    w = WORKLOADS["fewshot_d64"].with_(B=2, H=2, T=40)
+    x, W0, gy = gen_x(w), gen_W0(w), gen_gy(w)
+    xd = to_dev(x).requires_grad_()
+    W0d = to_dev(W0).requires_grad_()
+    y, _ = srwm.srwm(xd, W0d, reset_interval=9)
+    (y * to_dev(gy)).sum().backward()
+    dx_ref, dW0_ref = oracle_bwd.grads(x, W0, False, gy, None, reset_interval=9)
+    check_grad(xd.grad.cpu().numpy(), dx_ref, "autograd dx")
+    check_grad(W0d.grad.cpu().numpy(), dW0_ref, "autograd dW0")

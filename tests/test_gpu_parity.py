@@ -36,14 +36,15 @@ def run_gpu(x_np, W0_np, io_dtype, flag, return_state=True, variant=-1, n_lr=4, 
     y = out[0].float().cpu().numpy()
     WT = out[1].cpu().numpy() if out[1] is not None else None
     if save_tape:
-        return y, WT, out[2].cpu().numpy()
+        return y, WT, out[2].rows.cpu().numpy()
     return y, WT
 
 
-def check_tape(tape, x, W0, d_out, flag, n_lr, units):
+def check_tape(tape, x, W0, d_out, flag, n_lr, units, reset_interval=0):
     # The tape of unit (b, h) holds, per step, the update's row factor
     # a_t = g_rate(row) * (v_t - vbar_t), phi(k_t), phi(q_t) - phi(k_t) and the
-    # rates; all from the oracle's step-by-step quantities.
+    # rates; all from the oracle's step-by-step quantities (with resets, the
+    # steps restart from W0 every reset_interval steps).
     d_in = x.shape[-1]
     m = W0.shape[-2]
     kh_off = (m + 3) // 4 * 4
@@ -55,6 +56,8 @@ def check_tape(tape, x, W0, d_out, flag, n_lr, units):
         W = W0[h].astype(np.float64)
         a_ref, kh_ref, e_ref, g_ref = [], [], [], []
         for t in range(x.shape[1]):
+            if reset_interval > 0 and t > 0 and t % reset_interval == 0:
+                W = W0[h].astype(np.float64)
             s = oracle.step(W, x[b, t, h], d_out, flag, n_lr)
             a_ref.append(s["g"][rate] * (s["v"] - s["vb"]))
             kh_ref.append(s["kh"])
@@ -132,7 +135,7 @@ def test_variant_small(vi, T, flag):
     check_y(y, y_ref, w.io_dtype, f"variant {vi}")
     check_state(WT, WT_ref, f"variant {vi}")
     if v["writes_tape"]:
-        check_tape(out[2], x, W0, w.d_out, flag, w.n_lr, [(0, 0), (2, 1)])
+        check_tape(out[2], x, W0, w.d_out, flag, w.n_lr, [(0, 0), (2, 1)], reset)
 
 
 # ---------------------------------------------------------------------------
