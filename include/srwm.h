@@ -247,7 +247,10 @@ int srwm_backward(const srwm_backward_args_t* args);
 /* Floats per step in the tape: round_up(m, 4) + 2*d_in + 4, or SRWM_ERR_SHAPE. */
 int64_t srwm_tape_row(int64_t d_in, int64_t d_out, int n_lr);
 
-/* 1 if srwm_backward has a kernel for (d_in, d_out, io_dtype, n_lr), else 0. */
+/* 1 if srwm_backward has a kernel for (d_in, d_out, io_dtype, n_lr), else 0.
+ * (d_in = d_out = 128 has one without resets only: with reset_interval > 0
+ * srwm_backward returns SRWM_ERR_UNSUPPORTED there.  That kernel keeps the
+ * adjoint in dW_init while it runs.) */
 int srwm_backward_supported(int64_t d_in, int64_t d_out, int io_dtype, int n_lr);
 
 /*

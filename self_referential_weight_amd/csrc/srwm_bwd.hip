@@ -28,9 +28,14 @@ struct BwdVariant {
         BwdVariant{DI, DO, SRWM_IO_BF16, NLR, NW, 0, &srwm_bwd_kernel<DI, DO, NW, P, NLR, true, false>}, \
         BwdVariant{DI, DO, SRWM_IO_F32, NLR, NW, 1, &srwm_bwd_kernel<DI, DO, NW, P, NLR, false, true>},  \
         BwdVariant{DI, DO, SRWM_IO_BF16, NLR, NW, 1, &srwm_bwd_kernel<DI, DO, NW, P, NLR, true, true>}
+// d = 128: the wide kernel (W in registers, the adjoint in dW_init; no resets).
+#define SRWM_BWD_WIDE(DI, DO, NW, P, NLR)                                                                  \
+    BwdVariant{DI, DO, SRWM_IO_F32, NLR, NW, 0, &srwm_bwd_wide_kernel<DI, DO, NW, P, NLR, false, false>},  \
+        BwdVariant{DI, DO, SRWM_IO_BF16, NLR, NW, 0, &srwm_bwd_wide_kernel<DI, DO, NW, P, NLR, true, false>}
 const BwdVariant kBwdVariants[] = {
     SRWM_BWD(8, 8, 1, 8, 4), SRWM_BWD(16, 16, 1, 4, 4), SRWM_BWD(64, 64, 4, 16, 4),
     SRWM_BWD(8, 8, 1, 8, 1), SRWM_BWD(16, 16, 1, 4, 1), SRWM_BWD(64, 64, 4, 16, 1),
+    SRWM_BWD_WIDE(128, 128, 8, 16, 4), SRWM_BWD_WIDE(128, 128, 8, 16, 1),
 };
 constexpr int kNumBwdVariants = sizeof(kBwdVariants) / sizeof(kBwdVariants[0]);
 

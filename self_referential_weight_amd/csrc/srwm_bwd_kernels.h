@@ -499,6 +499,400 @@ void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin
     }
 }
 
+// ----------------------------------------------------------------------------
+// Backward pass for units whose W and adjoint Wh do not both fit in registers
+// (d = 128: 2 x 49,664 floats).  The same step as srwm_bwd_kernel, with three
+// differences:
+//   * W stays in registers (lane (rg, p): rows rg + G*r, columns [p*L, p*L+L));
+//     Wh lives in the unit's own rows of dWinit, each element read and written
+//     only by the lane that owns it (so every load follows that thread's own
+//     store), and holds dL/d(initial state) when the walk ends.  A unit's
+//     194 KB stay in its XCD's L2: the workloads of this shape have few units.
+//   * the per-column phase gives each lane CPL = D_IN / 64 columns
+//     (j = lane + 64 c);
+//   * the step inputs x_t and gy_t are staged CPL (resp. one per thread)
+//     entries per lane.
+// No reset ablation (Wh has no second buffer to gather the windows' shares).
+template <int D_IN, int D_OUT, int NW, int P, int NLR, bool BF16, bool RESET>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * kWave, NW * kWave), amdgpu_waves_per_eu(2)))
+void srwm_bwd_wide_kernel(const void* __restrict__ xv, const float* __restrict__ WTin,
+                          const float* __restrict__ tape, const float* __restrict__ gy,
+                          const float* __restrict__ gWT, float* __restrict__ dx,
+                          float* __restrict__ dWinit, int T, int H, int in_softmax, int /*reset_interval*/,
+                          const float* __restrict__ /*wstates*/)
+{
+    static_assert(!RESET, "the wide backward has no reset variant");
+    constexpr int NT = NW * kWave;
+    constexpr int M = D_OUT + 2 * D_IN + NLR;
+    constexpr int MAIN = D_OUT + 2 * D_IN;
+    constexpr int L = D_IN / P;
+    constexpr int G = NT / P;
+    constexpr int R = (M + G - 1) / G;
+    constexpr int CPL = D_IN / kWave;  // columns per lane in the per-column phase
+    using TL = TapeLayout<M, D_IN>;
+    using CX = ColExchange<P, L>;
+    constexpr int TW = TL::ROW;
+    constexpr int TPL = (TW + NT - 1) / NT;
+    static_assert(D_IN % kWave == 0 && D_OUT % kWave == 0, "whole columns per lane");
+    static_assert(D_IN % P == 0 && D_IN % G == 0 && D_OUT % G == 0, "row blocks must align with row groups");
+    static_assert(D_OUT <= NT, "one thread per output");
+    static_assert(L % 4 == 0, "16-byte pieces of Wh");
+    static_assert((NW & (NW - 1)) == 0, "power-of-two waves");
+
+    __shared__ __attribute__((aligned(16))) float s_tape[3][TW];
+    __shared__ __attribute__((aligned(16))) float s_u[3][D_IN];
+    __shared__ __attribute__((aligned(16))) float s_gy[3][D_OUT];
+    __shared__ __attribute__((aligned(16))) float s_red[2][NW][3][D_IN];
+    __shared__ __attribute__((aligned(16))) float s_bred[2][NW][4];
+    __shared__ __attribute__((aligned(16))) float s_zh[NW][M];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int p = tid % P;
+    const int rg = tid / P;
+    const int unit = blockIdx.x;
+    const int b = unit / H;
+    const int h = unit - b * H;
+    const int64_t x_step = (int64_t)H * D_IN;
+    const int64_t y_step = (int64_t)H * D_OUT;
+    const int64_t x0 = ((int64_t)b * T * H + h) * D_IN;
+    const int64_t y0 = ((int64_t)b * T * H + h) * D_OUT;
+    const float* __restrict__ tp0 = tape + (int64_t)unit * T * TW;
+    float* __restrict__ whu = dWinit + (int64_t)unit * M * D_IN;  // this unit's Wh
+    const float* __restrict__ wtu = WTin + (int64_t)unit * M * D_IN;
+    // One register row of Wh (zeros for padding rows); the passes over Wh load
+    // row r+1 before row r is processed (measured: 132 -> 118 ms on the wide
+    // workload against fencing each row with a scheduling barrier).
+    auto load_wh = [&](int r, float (&v)[L]) {
+        const int row = rg + G * r;
+        if (row < M) {
+            load_f32<L>(whu + row * D_IN + p * L, v);
+        } else {
+#pragma unroll
+            for (int c = 0; c < L; ++c) v[c] = 0.f;
+        }
+    };
+
+    auto rate = [](int r) constexpr {
+        const int row = G * r;
+        return NLR == 1 ? 0 : row < D_OUT ? 0 : row < D_OUT + D_IN ? 1 : row < MAIN ? 2 : 3;
+    };
+
+    // W <- W_T (rows >= M are zero padding); Wh <- dL/dW_T (or 0), in dWinit.
+    float w[R][L];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int row = rg + G * r;
+        if (row < M) {
+            load_f32<L>(wtu + row * D_IN + p * L, w[r]);
+            float v[L];
+            if (gWT != nullptr) {
+                load_f32<L>(gWT + (int64_t)unit * M * D_IN + row * D_IN + p * L, v);
+            } else {
+#pragma unroll
+                for (int c = 0; c < L; ++c) v[c] = 0.f;
+            }
+            store_f32<L>(whu + row * D_IN + p * L, v);
+        } else {
+#pragma unroll
+            for (int c = 0; c < L; ++c) w[r][c] = 0.f;
+        }
+    }
+
+    // Step inputs, fetched two steps ahead into registers, staged one step
+    // ahead into the LDS ring.
+    float tnext[TPL];
+    float xnext[CPL];
+    float gnext = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) xnext[c] = 0.f;
+    auto fetch = [&](int t) {
+        const float* __restrict__ tpp = tp0 + (int64_t)t * TW;
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) {
+            const int j = tid + NT * i;
+            tnext[i] = (j < TW) ? tpp[j] : 0.f;
+        }
+        if (wave == 0) {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                const int64_t o = x0 + (int64_t)t * x_step + lane + kWave * c;
+                if constexpr (BF16)
+                    xnext[c] = bf16_to_f32(reinterpret_cast<const uint16_t*>(xv)[o]);
+                else
+                    xnext[c] = reinterpret_cast<const float*>(xv)[o];
+            }
+        }
+        if (tid < D_OUT) gnext = gy[y0 + (int64_t)t * y_step + tid];
+    };
+    auto stage = [&](int slot) {
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) {
+            const int j = tid + NT * i;
+            if (j < TW) s_tape[slot][j] = tnext[i];
+        }
+        if (wave == 0) {
+            float uv[CPL];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) uv[c] = xnext[c];
+            if (in_softmax) {
+                float mx = uv[0];
+#pragma unroll
+                for (int c = 1; c < CPL; ++c) mx = fmax2(mx, uv[c]);
+                mx = wave_max(mx);
+                float sum = 0.f;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    uv[c] = exp_f32(uv[c] - mx);
+                    sum += uv[c];
+                }
+                const float inv = rcp_f32(wave_total(sum));
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) uv[c] *= inv;
+            }
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) s_u[slot][lane + kWave * c] = uv[c];
+        }
+        if (tid < D_OUT) s_gy[slot][tid] = gnext;
+    };
+
+    float part[3][L];
+    auto exchange = [&](int par, float (&bp)[4]) {
+        CX::run(part);
+        if (CX::writer(lane)) {
+            const int c0 = CX::col0(lane);
+#pragma unroll
+            for (int a = 0; a < 3; ++a) {
+                if constexpr (CX::LC % 2 == 0) {
+#pragma unroll
+                    for (int c = 0; c < CX::LC; c += 2)
+                        *reinterpret_cast<float2*>(&s_red[par][wave][a][c0 + c]) = make_float2(part[a][c], part[a][c + 1]);
+                } else {
+#pragma unroll
+                    for (int c = 0; c < CX::LC; ++c) s_red[par][wave][a][c0 + c] = part[a][c];
+                }
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < NLR; ++c) {
+            if constexpr (P == 4) {
+                bp[c] += dpp<0x128>(bp[c]);
+                bp[c] += dpp<0x124>(bp[c]);
+            } else if constexpr (P == 8) {
+                bp[c] = pair_sum<3>(bp[c]);
+            }
+        }
+        if constexpr (NLR == 4) {
+            swap32(bp[0], bp[2]);
+            swap32(bp[1], bp[3]);
+            float lo = bp[0] + bp[2], hi = bp[1] + bp[3];
+            swap16(lo, hi);
+            const float tot = lo + hi;
+            if ((lane & 15) == 0) s_bred[par][wave][lane >> 4] = tot;
+        } else {
+            const float tot = pair_sum<5>(pair_sum<4>(bp[0]));
+            if (lane == 0) s_bred[par][wave][0] = tot;
+        }
+    };
+    auto gather = [&](int par, float (&khh_j)[CPL], float (&eh_j)[CPL], float (&uh_j)[CPL]) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const int j = lane + kWave * c;
+            khh_j[c] = eh_j[c] = uh_j[c] = 0.f;
+#pragma unroll
+            for (int wv = 0; wv < NW; ++wv) {
+                khh_j[c] += s_red[par][wv][0][j];
+                eh_j[c] += s_red[par][wv][1][j];
+                uh_j[c] += s_red[par][wv][2][j];
+            }
+        }
+    };
+    auto store_dx = [&](int t, const float (&uh_j)[CPL], const float (&u_j)[CPL]) {
+        float d[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) d[c] = uh_j[c];
+        if (in_softmax) {
+            float s = 0.f;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) s = fmaf(uh_j[c], u_j[c], s);
+            const float du = wave_total(s);
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) d[c] = u_j[c] * (uh_j[c] - du);
+        }
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) dx[x0 + (int64_t)t * x_step + lane + kWave * c] = d[c];
+    };
+
+#pragma unroll
+    for (int a = 0; a < 3; ++a)
+#pragma unroll
+        for (int c = 0; c < L; ++c) part[a][c] = 0.f;
+    float u_next[CPL];  // u_{t+1}, columns lane + 64 c
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) u_next[c] = 0.f;
+
+    if (T > 0) {
+        fetch(T - 1);
+        stage((T - 1) % 3);
+        if (T > 1) fetch(T - 2);
+        __syncthreads();
+    }
+
+    int slot = (T - 1) % 3;
+    for (int t = T - 1; t >= 0; --t) {
+        const float* __restrict__ tt = s_tape[slot];
+        const float* __restrict__ us = s_u[slot];
+        const float* __restrict__ gs = s_gy[slot];
+        const int par = t & 1;
+
+        // ---- (A) undo the update of step t; ah (row sums of Wh kh), khh = Wh^T a,
+        // rh, eh = W^T rh.
+        float a[R], kt[L];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = rg + G * r;
+            const float av = tt[row < M ? row : M - 1];  // clamped: padding rows read a real row, then 0
+            a[r] = row < M ? av : 0.f;
+        }
+        load_f32<L>(tt + TL::KH_OFF + p * L, kt);
+        const float4 gv = *reinterpret_cast<const float4*>(tt + TL::G_OFF);
+        const float gate[4] = {gv.x, gv.y, gv.z, gv.w};
+
+        float khh[L], ah[R];
+#pragma unroll
+        for (int c = 0; c < L; ++c) khh[c] = 0.f;
+        float whn[L];
+        load_wh(0, whn);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float wh[L];
+#pragma unroll
+            for (int c = 0; c < L; ++c) wh[c] = whn[c];
+            if (r + 1 < R) load_wh(r + 1, whn);
+            float as = 0.f;
+#pragma unroll
+            for (int c = 0; c < L; ++c) {
+                w[r][c] = fmaf(-a[r], kt[c], w[r][c]);
+                as = fmaf(wh[c], kt[c], as);
+                khh[c] = fmaf(wh[c], a[r], khh[c]);
+            }
+            ah[r] = group_sum<P>(as);
+        }
+        float bp[4] = {0.f, 0.f, 0.f, 0.f};
+        float rh[R], eh[L];
+#pragma unroll
+        for (int c = 0; c < L; ++c) eh[c] = 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            rh[r] = gate[rate(r)] * ah[r];
+            bp[rate(r)] = fmaf(ah[r], a[r], bp[rate(r)]);
+#pragma unroll
+            for (int c = 0; c < L; ++c) eh[c] = fmaf(w[r][c], rh[r], eh[c]);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) bp[c] = p == 0 ? bp[c] : 0.f;
+#pragma unroll
+        for (int c = 0; c < L; ++c) {
+            part[0][c] = khh[c];
+            part[1][c] = eh[c];
+        }
+        exchange(par, bp);
+
+        const int slot_prev = slot == 0 ? 2 : slot - 1;
+        if (t > 0) {
+            stage(slot_prev);
+            if (t > 1) fetch(t - 2);
+        }
+        __syncthreads();
+
+        // ---- (B) per column (lane j = lane + 64 c): totals, dx of step t+1,
+        // kbar, qbar, betah.
+        float khh_j[CPL], eh_j[CPL], uh1_j[CPL];
+        gather(par, khh_j, eh_j, uh1_j);
+        if (t + 1 < T && wave == ((t + 1) & (NW - 1))) store_dx(t + 1, uh1_j, u_next);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) u_next[c] = us[lane + kWave * c];
+        {
+            float bt[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) bt[c] = c < NLR ? s_bred[par][0][c] : 0.f;
+#pragma unroll
+            for (int wv = 1; wv < NW; ++wv)
+#pragma unroll
+                for (int c = 0; c < NLR; ++c) bt[c] += s_bred[par][wv][c];
+            float kh_j[CPL], qh_j[CPL], kb[CPL];
+            float sk = 0.f, sq = 0.f;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                const int j = lane + kWave * c;
+                kh_j[c] = tt[TL::KH_OFF + j];
+                qh_j[c] = kh_j[c] + tt[TL::E_OFF + j];
+                kb[c] = khh_j[c] - eh_j[c];
+                sk = fmaf(kb[c], kh_j[c], sk);
+                sq = fmaf(eh_j[c], qh_j[c], sq);
+            }
+            wave_sum2(sk, sq);  // <kb, kh> and <eh, qh> over all D_IN columns
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                const int j = lane + kWave * c;
+                s_zh[wave][D_OUT + j] = kh_j[c] * (kb[c] - sk);
+                s_zh[wave][D_OUT + D_IN + j] = qh_j[c] * (eh_j[c] - sq);
+            }
+            if (lane < NLR) {
+                const float bv = lane == 0 ? bt[0] : lane == 1 ? bt[1] : lane == 2 ? bt[2] : bt[3];
+                const float gl = lane == 0 ? gate[0] : lane == 1 ? gate[1] : lane == 2 ? gate[2] : gate[3];
+                s_zh[wave][MAIN + lane] = (1.f - gl) * bv;
+            }
+        }
+        wave_sync();
+
+        // ---- (C) uh of step t (column partials, reduced with step t-1); Wh update.
+        float ev[L], uv[L];
+        load_f32<L>(tt + TL::E_OFF + p * L, ev);
+        load_f32<L>(us + p * L, uv);
+#pragma unroll
+        for (int c = 0; c < L; ++c) part[2][c] = 0.f;
+        load_wh(0, whn);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = rg + G * r;
+            float wh[L];
+#pragma unroll
+            for (int c = 0; c < L; ++c) wh[c] = whn[c];
+            if (r + 1 < R) load_wh(r + 1, whn);
+            float zr;
+            if (G * r < D_OUT) {
+                zr = gs[row];
+            } else {
+                const float zv = s_zh[wave][row < M ? row : M - 1];  // clamped as above
+                zr = row < M ? zv : 0.f;
+            }
+#pragma unroll
+            for (int c = 0; c < L; ++c) part[2][c] = fmaf(w[r][c], zr, part[2][c]);
+            if (row < M) {
+#pragma unroll
+                for (int c = 0; c < L; ++c) wh[c] = fmaf(rh[r], ev[c], fmaf(zr, uv[c], wh[c]));
+                store_f32<L>(whu + row * D_IN + p * L, wh);
+            }
+        }
+        slot = slot_prev;
+    }
+
+    if (T > 0) {
+        // uh of step 0: one more exchange (no khh, eh, betah)
+        float bp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < L; ++c) part[0][c] = part[1][c] = 0.f;
+        exchange(1, bp);
+        __syncthreads();
+        float khh_j[CPL], eh_j[CPL], uh0_j[CPL];
+        gather(1, khh_j, eh_j, uh0_j);
+        if (wave == 0) store_dx(0, uh0_j, u_next);
+    }
+    // dWinit already holds Wh = dL/d(initial state of this unit).
+}
+
 // dW0[h] = sum_b dWinit[b][h] (the gradient of the initial matrix shared over
 // the batch), summed in a fixed order b = 0, 1, ...
 __global__ __launch_bounds__(256) void srwm_sum_over_batch_kernel(const float* __restrict__ dWinit,

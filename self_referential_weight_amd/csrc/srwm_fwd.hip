@@ -157,6 +157,8 @@ const Variant kVariants[] = {
     SRWM_BOTH_IO_TAPE(64, 64, 4, 8, 1, 1, 0),
     SRWM_BOTH_IO_TAPE(64, 64, 4, 4, 1, 1, 1),
     SRWM_BOTH_IO_TAPE(64, 64, 8, 8, 1, 1, 1),
+    SRWM_BOTH_IO_TAPE(128, 128, 8, 4, 1, 4, 1),
+    SRWM_BOTH_IO_TAPE(128, 128, 8, 4, 1, 1, 1),
     // ... with the reset ablation (they also record each window's end state)
     SRWM_BOTH_IO_TAPE_RESET(8, 8, 1, 8, 1, 4, 1),
     SRWM_BOTH_IO_TAPE_RESET(16, 16, 1, 4, 1, 4, 1),

@@ -182,19 +182,21 @@ def test_tape_row_and_backward_support():
         for io in (0, 1):
             for n_lr in (4, 1):
                 assert lib.srwm_backward_supported(d, d, io, n_lr) == 1
-    assert lib.srwm_backward_supported(128, 128, 0, 4) == 0
+    assert lib.srwm_backward_supported(128, 128, 0, 4) == 1
+    assert lib.srwm_backward_supported(32, 32, 0, 4) == 0
     assert lib.srwm_backward_supported(64, 64, 2, 4) == 0
     # every shape with a backward kernel has forward variants that write the tape
     vs = _lib.variants()
     tape = {(v["d_in"], v["d_out"], v["io_dtype"], v["n_lr"]) for v in vs if v["writes_tape"]}
-    for d in (8, 16, 64):
+    for d in (8, 16, 64, 128):
         for io in ("f32", "bf16"):
             for n_lr in (4, 1):
                 assert (d, d, io, n_lr) in tape
     # ... and, for the reset ablation, variants that write the tape and the windows' end states
+    # (d = 128: no backward with resets)
     tape_reset = {(v["d_in"], v["d_out"], v["io_dtype"], v["n_lr"]) for v in vs
                   if v["writes_tape"] and v["supports_reset"]}
-    assert tape_reset == tape
+    assert tape_reset == {k for k in tape if k[0] != 128}
 
 
 FAKE_WS = 0xB0000000
@@ -208,7 +210,7 @@ def test_forward_tape_validation():
     assert call_ex(tape=FAKE_TAPE, reset_interval=1, window_states=FAKE_TAPE + 64) == E_ALIAS
     assert call_ex(tape=FAKE_TAPE + 4) == E_ARG                     # misaligned
     assert call_ex(tape=FAKE_X + 16) == E_ALIAS                     # overlaps x
-    assert call_ex(tape=FAKE_TAPE, d_in=128, d_out=128) == E_UNSUP  # no tape variant at d=128
+    assert call_ex(tape=FAKE_TAPE, d_in=32, d_out=32) == E_UNSUP    # no tape variant at d=32
     vs = _lib.variants()
     plain = next(v for v in vs if v["d_in"] == 16 and v["io_dtype"] == "f32" and v["n_lr"] == 4
                  and not v["writes_tape"])
@@ -235,7 +237,8 @@ def call_bwd(**kw):
     (dict(d_in=0), E_SHAPE),
     (dict(io_dtype=2), E_ARG),
     (dict(apply_input_softmax=3), E_ARG),
-    (dict(d_in=128, d_out=128), E_UNSUP),
+    (dict(d_in=32, d_out=32), E_UNSUP),
+    (dict(d_in=128, d_out=128, reset_interval=1), E_UNSUP),      # the wide kernel has no resets
     (dict(W_T=None), E_NULL),
     (dict(dW_init=None), E_NULL),
     (dict(tape=None), E_NULL),

@@ -50,6 +50,7 @@ SMALL = {
     "multitask_d16": dict(),                  # the workload as is: B=4, H=4, T=256
     "fewshot_d64": dict(B=3, H=3, T=200),
     "rl_d64_bf16": dict(B=2, H=3, T=157),
+    "wide_d128": dict(B=2, H=2, T=61),
 }
 
 
@@ -206,7 +207,7 @@ def test_autograd_function(name):
 # The reset ablation (review page Sec. 4.5): every R steps the state returns to
 # the initial matrix.  The taped forward records each window's end state; the
 # backward restarts every earlier window from it.
-@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("name", [n for n in SMALL if n != "wide_d128"])  # no resets at d = 128
 @pytest.mark.parametrize("n_lr", [4, 1])
 @pytest.mark.parametrize("R", [1, 13])
 def test_backward_reset_parity(name, n_lr, R):
@@ -284,3 +285,22 @@ def test_autograd_with_resets():
     dx_ref, dW0_ref = oracle_bwd.grads(x, W0, False, gy, None, reset_interval=9)
     check_grad(xd.grad.cpu().numpy(), dx_ref, "autograd dx")
     check_grad(W0d.grad.cpu().numpy(), dW0_ref, "autograd dW0")
+
+
+def test_backward_wide_full_size_sampled_unit():
+    # The full wide workload (d = 128, T = 8192) through the wide backward
+    # kernel; units are independent, so one sampled unit's gradients (its
+    # sequence's dx for that head, its dW_init) are checked against the oracle
+    # run on that unit alone.
+    w = WORKLOADS["wide_d128"]
+    flag = w.apply_input_softmax
+    say(f"[bwd] full size wide_d128: B={w.B} H={w.H} T={w.T} (oracle on unit b=0, h=1)")
+    x, W0, gy = gen_x(w), gen_W0(w), gen_gy(w)
+    _, _, dx, dWi = gpu_grads(w, x, W0, gy, None, flag, shared=False)
+    assert np.isfinite(dx).all() and np.isfinite(dWi).all()
+    b, h = 0, 1
+    dx_ref, dW_ref = oracle_bwd.grads(x[b:b + 1, :, h:h + 1], W0[h:h + 1], flag, gy[b:b + 1, :, h:h + 1], None,
+                                      n_lr=w.n_lr)
+    rx = check_grad(dx[b:b + 1, :, h:h + 1], dx_ref, "wide dx")
+    rw = check_grad(dWi[b, h:h + 1], dW_ref, "wide dW")
+    say(f"[bwd] wide_d128 unit ({b},{h}): relL2 dx={rx:.2e} dW={rw:.2e}")
