@@ -504,10 +504,11 @@ void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin
 // (d = 128: 2 x 49,664 floats).  The same step as srwm_bwd_kernel, with three
 // differences:
 //   * W stays in registers (lane (rg, p): rows rg + G*r, columns [p*L, p*L+L));
-//     Wh lives in the unit's own rows of dWinit, each element read and written
-//     only by the lane that owns it (so every load follows that thread's own
-//     store), and holds dL/d(initial state) when the walk ends.  A unit's
-//     194 KB stay in its XCD's L2: the workloads of this shape have few units.
+//     of Wh, register rows r < RL live in LDS and the rest in the unit's own
+//     rows of dWinit (L2-resident: the workloads of this shape have few
+//     units), each element read and written only by the lane that owns it, so
+//     every load follows that thread's own store.  The LDS rows are written to
+//     dWinit when the walk ends, which then holds dL/d(initial state).
 //   * the per-column phase gives each lane CPL = D_IN / 64 columns
 //     (j = lane + 64 c);
 //   * the step inputs x_t and gy_t are staged CPL (resp. one per thread)
@@ -538,6 +539,9 @@ void srwm_bwd_wide_kernel(const void* __restrict__ xv, const float* __restrict__
     static_assert(D_OUT <= NT, "one thread per output");
     static_assert(L % 4 == 0, "16-byte pieces of Wh");
     static_assert((NW & (NW - 1)) == 0, "power-of-two waves");
+    // register rows of Wh kept in LDS: as many as fit beside the staging buffers
+    constexpr int RL = 7;
+    static_assert(RL <= R, "LDS rows");
 
     __shared__ __attribute__((aligned(16))) float s_tape[3][TW];
     __shared__ __attribute__((aligned(16))) float s_u[3][D_IN];
@@ -545,6 +549,9 @@ void srwm_bwd_wide_kernel(const void* __restrict__ xv, const float* __restrict__
     __shared__ __attribute__((aligned(16))) float s_red[2][NW][3][D_IN];
     __shared__ __attribute__((aligned(16))) float s_bred[2][NW][4];
     __shared__ __attribute__((aligned(16))) float s_zh[NW][M];
+    __shared__ __attribute__((aligned(16))) float s_wh[RL][G][D_IN];
+    static_assert(sizeof(float) * (3 * TW + 3 * D_IN + 3 * D_OUT + 2 * NW * 3 * D_IN + 2 * NW * 4 + NW * M +
+                                   RL * G * D_IN) <= 160 * 1024, "LDS");
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -566,12 +573,19 @@ void srwm_bwd_wide_kernel(const void* __restrict__ xv, const float* __restrict__
     // workload against fencing each row with a scheduling barrier).
     auto load_wh = [&](int r, float (&v)[L]) {
         const int row = rg + G * r;
-        if (row < M) {
+        if (r < RL) {
+            load_f32<L>(&s_wh[r < RL ? r : 0][rg][p * L], v);
+        } else if (row < M) {
             load_f32<L>(whu + row * D_IN + p * L, v);
         } else {
 #pragma unroll
             for (int c = 0; c < L; ++c) v[c] = 0.f;
         }
+    };
+    auto store_wh = [&](int r, const float (&v)[L]) {
+        const int row = rg + G * r;
+        if (r < RL) store_f32<L>(&s_wh[r < RL ? r : 0][rg][p * L], v);
+        else if (row < M) store_f32<L>(whu + row * D_IN + p * L, v);
     };
 
     auto rate = [](int r) constexpr {
@@ -579,25 +593,19 @@ void srwm_bwd_wide_kernel(const void* __restrict__ xv, const float* __restrict__
         return NLR == 1 ? 0 : row < D_OUT ? 0 : row < D_OUT + D_IN ? 1 : row < MAIN ? 2 : 3;
     };
 
-    // W <- W_T (rows >= M are zero padding); Wh <- dL/dW_T (or 0), in dWinit.
+    // W <- W_T (rows >= M are zero padding); Wh <- dL/dW_T (or 0).
     float w[R][L];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int row = rg + G * r;
+        float v[L];
+#pragma unroll
+        for (int c = 0; c < L; ++c) w[r][c] = v[c] = 0.f;
         if (row < M) {
             load_f32<L>(wtu + row * D_IN + p * L, w[r]);
-            float v[L];
-            if (gWT != nullptr) {
-                load_f32<L>(gWT + (int64_t)unit * M * D_IN + row * D_IN + p * L, v);
-            } else {
-#pragma unroll
-                for (int c = 0; c < L; ++c) v[c] = 0.f;
-            }
-            store_f32<L>(whu + row * D_IN + p * L, v);
-        } else {
-#pragma unroll
-            for (int c = 0; c < L; ++c) w[r][c] = 0.f;
+            if (gWT != nullptr) load_f32<L>(gWT + (int64_t)unit * M * D_IN + row * D_IN + p * L, v);
         }
+        store_wh(r, v);
     }
 
     // Step inputs, fetched two steps ahead into registers, staged one step
@@ -870,11 +878,9 @@ void srwm_bwd_wide_kernel(const void* __restrict__ xv, const float* __restrict__
             }
 #pragma unroll
             for (int c = 0; c < L; ++c) part[2][c] = fmaf(w[r][c], zr, part[2][c]);
-            if (row < M) {
 #pragma unroll
-                for (int c = 0; c < L; ++c) wh[c] = fmaf(rh[r], ev[c], fmaf(zr, uv[c], wh[c]));
-                store_f32<L>(whu + row * D_IN + p * L, wh);
-            }
+            for (int c = 0; c < L; ++c) wh[c] = fmaf(rh[r], ev[c], fmaf(zr, uv[c], wh[c]));
+            store_wh(r, wh);  // padding rows stay zero: rh = zr = 0 there
         }
         slot = slot_prev;
     }
@@ -890,7 +896,17 @@ void srwm_bwd_wide_kernel(const void* __restrict__ xv, const float* __restrict__
         gather(1, khh_j, eh_j, uh0_j);
         if (wave == 0) store_dx(0, uh0_j, u_next);
     }
-    // dWinit already holds Wh = dL/d(initial state of this unit).
+    // dWinit <- Wh = dL/d(initial state of this unit): its LDS rows (the
+    // others are there already).
+#pragma unroll
+    for (int r = 0; r < RL; ++r) {
+        const int row = rg + G * r;
+        if (row < M) {
+            float v[L];
+            load_f32<L>(&s_wh[r][rg][p * L], v);
+            store_f32<L>(whu + row * D_IN + p * L, v);
+        }
+    }
 }
 
 // dW0[h] = sum_b dWinit[b][h] (the gradient of the initial matrix shared over
