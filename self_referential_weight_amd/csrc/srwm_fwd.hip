@@ -137,10 +137,11 @@ const Variant kVariants[] = {
     make_variant<8, 25, 1, 8, 1, 1, 1, false>(1),
     make_variant<16, 49, 1, 4, 1, 4, 1, false>(1),
     make_variant<16, 49, 1, 4, 1, 1, 1, false>(1),
-    make_variant<64, 193, 4, 8, 1, 4, 1, false>(1),
-    make_variant<64, 193, 4, 8, 1, 1, 1, false>(1),
-    make_variant<64, 193, 8, 8, 1, 4, 0, false>(1),
-    make_variant<64, 193, 8, 8, 1, 1, 0, false>(1),
+    make_variant<64, 193, 4, 4, 1, 4, 1, false>(1),
+    make_variant<64, 193, 4, 4, 1, 1, 1, false>(1),
+    make_variant<64, 193, 8, 4, 1, 4, 0, false>(1),
+    make_variant<64, 193, 8, 4, 1, 1, 0, false>(1),
+    make_variant<64, 193, 8, 8, 1, 4, 0, false>(0),
     make_variant<64, 193, 8, 8, 1, 4, 2, false>(0),
     // forward passes that also write the backward tape
     SRWM_BOTH_IO_TAPE(8, 8, 1, 8, 1, 4, 1),
