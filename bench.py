@@ -213,7 +213,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
+        print(f"bench.py: libsrwm measures one GPU only (--gpus {args.gpus} requested); "
               "the (sequence, head) units shard across GPUs with no communication, "
               "so one GPU's share is what is measured", file=sys.stderr)
         return 2

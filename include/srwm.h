@@ -51,7 +51,7 @@ extern "C" {
 #endif
 
 #define SRWM_VERSION_MAJOR 0
-#define SRWM_VERSION_MINOR 4
+#define SRWM_VERSION_MINOR 5
 #define SRWM_VERSION_PATCH 0
 
 typedef enum { SRWM_IO_F32 = 0, SRWM_IO_BF16 = 1 } srwm_io_dtype_t;
@@ -200,17 +200,25 @@ int srwm_select_variant(int64_t d_in, int64_t d_out, int io_dtype, int n_lr,
  *   [0, m)            a_t, the row factor of the step's rank-one update
  *   [K, K+d_in)       phi(k_t)
  *   [K+d_in, K+2d_in) phi(q_t) - phi(k_t), rounded as the forward pass used it
- *   [K+2d_in, +4)     the learning rates sigma(beta_t) (n_lr of them)
+ *   [K+2d_in, +4)     the learning rates sigma(beta_t) (n_lr of them, the
+ *                     rest zero)
+ *   [K+2d_in+4, +d_in) u_t, the step's input as the projection used it (x_t
+ *                     widened to float32, softmax-ed when the input softmax
+ *                     is on)
  * ([m, K) is padding and is not written).  From the final state W_T,
  * srwm_backward walks t = T-1..0, undoes each update (W_{t-1} = W_t -
- * a_t phi(k_t)^T) and accumulates the adjoint; no projection is recomputed.
+ * a_t phi(k_t)^T) and accumulates the adjoint; no projection and no input
+ * softmax is recomputed.
  * With L = sum_t <gy[t], y_t> + <gW_T, W_T> it writes
  *   dx       [B][T][H][d_in]   dL/dx, float32 (also for bf16 x)
  *   dW_init  [B][H][m][d_in]   dL/d(initial state of each unit)
  *   dW0      [H][m][d_in]      sum over b of dW_init (the gradient of an
  *                              initial matrix shared over the batch), or NULL
- * Inputs: x and W_T as the forward pass saw and wrote them, the tape, gy
- * [B][T][H][d_out] float32, gW_T [B][H][m][d_in] float32 or NULL (zero).
+ * Inputs: W_T as the forward pass wrote it, the tape, gy [B][T][H][d_out]
+ * float32, gW_T [B][H][m][d_in] float32 or NULL (zero).  x is not read (the
+ * tape holds u_t) and may be NULL; io_dtype must still name x's dtype, and
+ * apply_input_softmax must be the forward pass's flag (it selects the
+ * softmax's backward for dx).
  * With B == 0 a given dW0 is filled with zeros (one kernel launch); with
  * H == 0 nothing is launched.
  * The reset ablation: reset_interval R > 0 as in the forward pass, with the
@@ -225,7 +233,7 @@ int srwm_select_variant(int64_t d_in, int64_t d_out, int io_dtype, int n_lr,
  * when srwm_backward_supported() is 0).
  */
 typedef struct srwm_backward_args {
-    const void* x;
+    const void* x;                /* not read; kept for the layout of 0.4 */
     const float* W_T;
     const float* tape;
     const float* gy;
@@ -244,7 +252,7 @@ typedef struct srwm_backward_args {
 
 int srwm_backward(const srwm_backward_args_t* args);
 
-/* Floats per step in the tape: round_up(m, 4) + 2*d_in + 4, or SRWM_ERR_SHAPE. */
+/* Floats per step in the tape: round_up(m, 4) + 3*d_in + 4, or SRWM_ERR_SHAPE. */
 int64_t srwm_tape_row(int64_t d_in, int64_t d_out, int n_lr);
 
 /* 1 if srwm_backward has a kernel for (d_in, d_out, io_dtype, n_lr), else 0.

@@ -51,7 +51,7 @@ class Tape(NamedTuple):
     """What ``forward(..., save_tape=True)`` records for ``backward``.
 
     rows: [B, H, T, tape_row] float32, one row per unit and step (a_t,
-    phi(k_t), phi(q_t) - phi(k_t), the learning rates).
+    phi(k_t), phi(q_t) - phi(k_t), the learning rates, u_t).
     window_states: with reset_interval R > 0, the end state of every window
     but the last, [B, H, (T - 1) // R, m, d_in] float32; else None.
     """
@@ -208,7 +208,8 @@ def backward(x, W_T, tape, gy, gW_T=None, apply_input_softmax: bool = False, n_l
     def ptr(t_):
         return t_.data_ptr() if t_ is not None and t_.numel() else None
 
-    a = _lib.BackwardArgs(x=ptr(x), W_T=ptr(W_T), tape=ptr(tape), gy=ptr(gy), gW_T=ptr(gW_T),
+    # x gives the shapes, dtype and device; the kernels read u_t from the tape
+    a = _lib.BackwardArgs(x=None, W_T=ptr(W_T), tape=ptr(tape), gy=ptr(gy), gW_T=ptr(gW_T),
                           dx=ptr(dx), dW_init=ptr(dWi), dW0=ptr(dW0), B=B, T=T, H=H, d_in=d_in,
                           d_out=d_out, m=m, io_dtype=io,
                           apply_input_softmax=int(bool(apply_input_softmax)), n_lr=int(n_lr),

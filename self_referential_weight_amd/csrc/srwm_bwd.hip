@@ -15,23 +15,21 @@ namespace {
 using namespace srwm;
 
 // Backward kernels: (d_in, d_out, waves per unit, lanes per row, learning
-// rates), both I/O dtypes.
-using BwdFn = void (*)(const void*, const float*, const float*, const float*, const float*, float*,
-                       float*, int, int, int, int, const float*);
+// rates).  They read u_t from the tape, never x, so one kernel serves both
+// I/O dtypes of the forward pass.
+using BwdFn = void (*)(const float*, const float*, const float*, const float*, float*, float*, int, int,
+                       int, int, const float*);
 struct BwdVariant {
-    int d_in, d_out, io, nlr, nw, reset;
+    int d_in, d_out, nlr, nw, reset;
     BwdFn fn;
 };
-// Both I/O dtypes, without and with the reset ablation's window restarts.
-#define SRWM_BWD(DI, DO, NW, P, NLR)                                                                  \
-    BwdVariant{DI, DO, SRWM_IO_F32, NLR, NW, 0, &srwm_bwd_kernel<DI, DO, NW, P, NLR, false, false>},  \
-        BwdVariant{DI, DO, SRWM_IO_BF16, NLR, NW, 0, &srwm_bwd_kernel<DI, DO, NW, P, NLR, true, false>}, \
-        BwdVariant{DI, DO, SRWM_IO_F32, NLR, NW, 1, &srwm_bwd_kernel<DI, DO, NW, P, NLR, false, true>},  \
-        BwdVariant{DI, DO, SRWM_IO_BF16, NLR, NW, 1, &srwm_bwd_kernel<DI, DO, NW, P, NLR, true, true>}
+// Without and with the reset ablation's window restarts.
+#define SRWM_BWD(DI, DO, NW, P, NLR)                                                     \
+    BwdVariant{DI, DO, NLR, NW, 0, &srwm_bwd_kernel<DI, DO, NW, P, NLR, false>},        \
+        BwdVariant{DI, DO, NLR, NW, 1, &srwm_bwd_kernel<DI, DO, NW, P, NLR, true>}
 // d = 128: the wide kernel (W in registers, the adjoint in dW_init; no resets).
-#define SRWM_BWD_WIDE(DI, DO, NW, P, NLR)                                                                  \
-    BwdVariant{DI, DO, SRWM_IO_F32, NLR, NW, 0, &srwm_bwd_wide_kernel<DI, DO, NW, P, NLR, false, false>},  \
-        BwdVariant{DI, DO, SRWM_IO_BF16, NLR, NW, 0, &srwm_bwd_wide_kernel<DI, DO, NW, P, NLR, true, false>}
+#define SRWM_BWD_WIDE(DI, DO, NW, P, NLR) \
+    BwdVariant{DI, DO, NLR, NW, 0, &srwm_bwd_wide_kernel<DI, DO, NW, P, NLR, false>}
 const BwdVariant kBwdVariants[] = {
     SRWM_BWD(8, 8, 1, 8, 4), SRWM_BWD(16, 16, 1, 4, 4), SRWM_BWD(64, 64, 4, 16, 4),
     SRWM_BWD(8, 8, 1, 8, 1), SRWM_BWD(16, 16, 1, 4, 1), SRWM_BWD(64, 64, 4, 16, 1),
@@ -53,25 +51,22 @@ int backward_impl(const srwm_backward_args_t* a)
     const int want_reset = a->reset_interval > 0 ? 1 : 0;
     for (int i = 0; i < kNumBwdVariants; ++i) {
         const BwdVariant& v = kBwdVariants[i];
-        if (v.d_in == d_in && v.d_out == d_out && v.io == a->io_dtype && v.nlr == a->n_lr && v.reset == want_reset)
-            vi = i;
+        if (v.d_in == d_in && v.d_out == d_out && v.nlr == a->n_lr && v.reset == want_reset) vi = i;
     }
     if (vi < 0) return SRWM_ERR_UNSUPPORTED;
-    const int64_t es = a->io_dtype == SRWM_IO_BF16 ? 2 : 4;
-    int64_t units, steps, nx, ndx, ngy, nst, ntape, nw0, nws;
+    int64_t units, steps, ndx, ngy, nst, ntape, nw0, nws;
     // the forward pass's end states of all windows but the last
     const int64_t nres = (a->reset_interval > 0 && T > 0) ? (T - 1) / a->reset_interval : 0;
-    if (!mul_ok(B, H, &units) || !mul_ok(units, T, &steps) || !mul_ok(steps, d_in * es, &nx) ||
-        !mul_ok(steps, d_in * 4, &ndx) || !mul_ok(steps, d_out * 4, &ngy) ||
+    if (!mul_ok(B, H, &units) || !mul_ok(units, T, &steps) || !mul_ok(steps, d_in * 4, &ndx) || !mul_ok(steps, d_out * 4, &ngy) ||
         !mul_ok(units, m * d_in * 4, &nst) || !mul_ok(steps, tape_row(d_in, d_out, a->n_lr) * 4, &ntape) ||
         !mul_ok(H, m * d_in * 4, &nw0) || !mul_ok(nst, nres, &nws))
         return SRWM_ERR_SHAPE;
     if (units > INT32_MAX || T > INT32_MAX || H > INT32_MAX) return SRWM_ERR_SHAPE;
     if ((nst > 0 && (a->W_T == nullptr || a->dW_init == nullptr)) || (ntape > 0 && a->tape == nullptr) ||
-        (nx > 0 && (a->x == nullptr || a->dx == nullptr)) || (ngy > 0 && a->gy == nullptr) ||
+        (ndx > 0 && a->dx == nullptr) || (ngy > 0 && a->gy == nullptr) ||
         (nws > 0 && a->window_states == nullptr))
         return SRWM_ERR_NULL;
-    if ((reinterpret_cast<uintptr_t>(a->x) | reinterpret_cast<uintptr_t>(a->W_T) |
+    if ((reinterpret_cast<uintptr_t>(a->W_T) |
          reinterpret_cast<uintptr_t>(a->tape) | reinterpret_cast<uintptr_t>(a->gy) |
          reinterpret_cast<uintptr_t>(a->gW_T) | reinterpret_cast<uintptr_t>(a->dx) |
          reinterpret_cast<uintptr_t>(a->dW_init) | reinterpret_cast<uintptr_t>(a->dW0) |
@@ -93,18 +88,17 @@ int backward_impl(const srwm_backward_args_t* a)
     };
     if (units == 0) return sum_over_batch();
     const float* wstates = nws > 0 ? a->window_states : nullptr;
-    const void* ins[] = {a->x, a->W_T, a->tape, a->gy, a->gW_T, wstates};
-    const int64_t nins[] = {nx, nst, ntape, ngy, a->gW_T ? nst : 0, nws};
+    const void* ins[] = {a->W_T, a->tape, a->gy, a->gW_T, wstates};
+    const int64_t nins[] = {nst, ntape, ngy, a->gW_T ? nst : 0, nws};
     void* outs[] = {a->dx, a->dW_init, a->dW0};
     const int64_t nouts[] = {ndx, nst, a->dW0 ? nw0 : 0};
     for (int o = 0; o < 3; ++o) {
-        for (int i = 0; i < 6; ++i)
+        for (int i = 0; i < 5; ++i)
             if (ranges_overlap(outs[o], nouts[o], ins[i], nins[i])) return SRWM_ERR_ALIAS;
         for (int o2 = o + 1; o2 < 3; ++o2)
             if (ranges_overlap(outs[o], nouts[o], outs[o2], nouts[o2])) return SRWM_ERR_ALIAS;
     }
     const BwdVariant& v = kBwdVariants[vi];
-    const void* x = a->x;
     const float* WTp = a->W_T;
     const float* tape = a->tape;
     const float* gy = a->gy;
@@ -113,7 +107,7 @@ int backward_impl(const srwm_backward_args_t* a)
     float* dWi = a->dW_init;
     int Ti = static_cast<int>(T), Hi = static_cast<int>(H), fl = a->apply_input_softmax;
     int rst = static_cast<int>(a->reset_interval);
-    void* args[] = {const_cast<void**>(&x), const_cast<float**>(&WTp), const_cast<float**>(&tape),
+    void* args[] = {const_cast<float**>(&WTp), const_cast<float**>(&tape),
                     const_cast<float**>(&gy), const_cast<float**>(&gWT), &dx, &dWi, &Ti, &Hi, &fl, &rst,
                     const_cast<float**>(&wstates)};
     const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(v.fn),
@@ -130,9 +124,10 @@ int srwm_backward(const srwm_backward_args_t* args) { return backward_impl(args)
 
 int srwm_backward_supported(int64_t d_in, int64_t d_out, int io_dtype, int n_lr)
 {
+    if (io_dtype != SRWM_IO_F32 && io_dtype != SRWM_IO_BF16) return 0;
     for (int i = 0; i < kNumBwdVariants; ++i) {
         const BwdVariant& v = kBwdVariants[i];
-        if (v.d_in == d_in && v.d_out == d_out && v.io == io_dtype && v.nlr == n_lr) return 1;
+        if (v.d_in == d_in && v.d_out == d_out && v.nlr == n_lr) return 1;
     }
     return 0;
 }

@@ -105,9 +105,9 @@ struct ColExchange {
     __device__ __forceinline__ static bool writer(int lane) { return (lane & KEEP_MASK) == 0; }
 };
 
-template <int D_IN, int D_OUT, int NW, int P, int NLR, bool BF16, bool RESET>
+template <int D_IN, int D_OUT, int NW, int P, int NLR, bool RESET>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * kWave, NW * kWave), amdgpu_waves_per_eu(2)))
-void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin,
+void srwm_bwd_kernel(const float* __restrict__ WTin,
                      const float* __restrict__ tape, const float* __restrict__ gy,
                      const float* __restrict__ gWT, float* __restrict__ dx,
                      float* __restrict__ dWinit, int T, int H, int in_softmax, int reset_interval,
@@ -129,14 +129,22 @@ void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin
     static_assert((NW & (NW - 1)) == 0, "power-of-two waves");
 
     __shared__ __attribute__((aligned(16))) float s_tape[3][TW];
-    __shared__ __attribute__((aligned(16))) float s_u[3][D_IN];
     __shared__ __attribute__((aligned(16))) float s_gy[3][D_OUT];
     // khh, eh, uh column partials per wave, one float array per quantity so that
     // the writers (8 column slices 32 floats apart) and the readers (lane j,
     // column j) both meet at most two-way bank conflicts
     __shared__ __attribute__((aligned(16))) float s_red[2][NW][3][D_IN];
     __shared__ __attribute__((aligned(16))) float s_bred[2][NW][4];     // betah partials per wave
-    __shared__ __attribute__((aligned(16))) float s_zh[NW][M];          // each wave's own zh rows
+    // The per-column phase (lane <-> column jc).  With P = 16 and d_in = 64
+    // the columns are dealt so that the kbar and qbar entries of every K and Q
+    // row a lane holds sit in its own DPP row: lane 16q + k of wave w takes
+    // column q + 4((w + k / KR) mod NW) + G (k mod KR), and the lanes of row
+    // group rg = 4w + q hold rows rg + G r, i.e. columns q + 4w + G k of the K
+    // and Q blocks (k < KR), so one row_newbcast hands each of them over.
+    // Otherwise lane j takes column j and the zh rows go through LDS.
+    constexpr bool BCAST = P == 16 && D_IN == kWave && 16 % NW == 0;
+    constexpr int KR = D_IN / G;  // register rows per K or Q block
+    __shared__ __attribute__((aligned(16))) float s_zh[BCAST ? 1 : NW][BCAST ? 1 : M];  // each wave's own zh rows
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -146,6 +154,11 @@ void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin
     const int unit = blockIdx.x;
     const int b = unit / H;
     const int h = unit - b * H;
+    int jc = lane;
+    if constexpr (BCAST) {
+        const int kq = lane & 15;
+        jc = (lane >> 4) + 4 * ((wave + kq / KR) & (NW - 1)) + G * (kq % KR);
+    }
     const int64_t x_step = (int64_t)H * D_IN;
     const int64_t y_step = (int64_t)H * D_OUT;
     const int64_t x0 = ((int64_t)b * T * H + h) * D_IN;
@@ -183,22 +196,15 @@ void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin
     }
 
     // Step inputs are fetched two steps ahead into registers and staged one
-    // step ahead into the LDS ring: tape row, u_t (x_t widened, softmax-ed
-    // when the forward pass did), gy_t.
+    // step ahead into the LDS ring: the tape row (which holds u_t) and gy_t.
     float tnext[TPL];
-    float xnext = 0.f, gnext = 0.f;
+    float gnext = 0.f;
     auto fetch = [&](int t) {
         const float* __restrict__ tp = tp0 + (int64_t)t * TW;
 #pragma unroll
         for (int i = 0; i < TPL; ++i) {
             const int j = tid + NT * i;
             tnext[i] = (j < TW) ? tp[j] : 0.f;
-        }
-        if (wave == 0 && lane < D_IN) {
-            if constexpr (BF16)
-                xnext = bf16_to_f32(reinterpret_cast<const uint16_t*>(xv)[x0 + (int64_t)t * x_step + lane]);
-            else
-                xnext = reinterpret_cast<const float*>(xv)[x0 + (int64_t)t * x_step + lane];
         }
         if (tid < D_OUT) gnext = gy[y0 + (int64_t)t * y_step + tid];
     };
@@ -207,15 +213,6 @@ void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin
         for (int i = 0; i < TPL; ++i) {
             const int j = tid + NT * i;
             if (j < TW) s_tape[slot][j] = tnext[i];
-        }
-        if (wave == 0) {
-            float uv = xnext;
-            if (in_softmax) {
-                const float mx = wave_max(lane < D_IN ? xnext : -INFINITY);
-                const float ev = lane < D_IN ? exp_f32(xnext - mx) : 0.f;
-                uv = ev * rcp_f32(wave_total(ev));
-            }
-            if (lane < D_IN) s_u[slot][lane] = uv;
         }
         if (tid < D_OUT) s_gy[slot][tid] = gnext;
     };
@@ -269,9 +266,9 @@ void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin
         if (lane < D_IN) {
 #pragma unroll
             for (int wv = 0; wv < NW; ++wv) {
-                khh_j += s_red[par][wv][0][lane];
-                eh_j += s_red[par][wv][1][lane];
-                uh_j += s_red[par][wv][2][lane];
+                khh_j += s_red[par][wv][0][jc];
+                eh_j += s_red[par][wv][1][jc];
+                uh_j += s_red[par][wv][2][jc];
             }
         }
     };
@@ -282,7 +279,7 @@ void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin
             const float du = wave_total(lane < D_IN ? uh_j * u_j : 0.f);
             d = u_j * (uh_j - du);
         }
-        if (lane < D_IN) dx[x0 + (int64_t)t * x_step + lane] = d;
+        if (lane < D_IN) dx[x0 + (int64_t)t * x_step + jc] = d;
     };
 
 #pragma unroll
@@ -332,7 +329,7 @@ void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin
     int slot = (T - 1) % 3;
     for (int t = T - 1; t >= 0; --t) {
         const float* __restrict__ tt = s_tape[slot];
-        const float* __restrict__ us = s_u[slot];
+        const float* __restrict__ us = tt + TL::U_OFF;
         const float* __restrict__ gs = s_gy[slot];
         const int par = t & 1;
 
@@ -396,7 +393,8 @@ void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin
         float khh_j, eh_j, uh1_j;
         gather(par, khh_j, eh_j, uh1_j);
         if (t + 1 < T && wave == ((t + 1) & (NW - 1))) store_dx(t + 1, uh1_j, u_next);
-        u_next = lane < D_IN ? us[lane] : 0.f;
+        u_next = lane < D_IN ? us[jc] : 0.f;
+        float kbar_v = 0.f, qbar_v = 0.f, zb = 0.f;  // BCAST: this lane's column of kbar, qbar; its beta row
         {
             float bt[4];
 #pragma unroll
@@ -405,8 +403,8 @@ void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin
             for (int wv = 1; wv < NW; ++wv)
 #pragma unroll
                 for (int c = 0; c < NLR; ++c) bt[c] += s_bred[par][wv][c];
-            const float kh_j = lane < D_IN ? tt[TL::KH_OFF + lane] : 0.f;
-            const float e_j = lane < D_IN ? tt[TL::E_OFF + lane] : 0.f;
+            const float kh_j = lane < D_IN ? tt[TL::KH_OFF + jc] : 0.f;
+            const float e_j = lane < D_IN ? tt[TL::E_OFF + jc] : 0.f;
             const float qh_j = kh_j + e_j;
             const float kb = khh_j - eh_j;
             // <kb, kh> and <eh, qh> over the 64 columns with one reduction: the
@@ -418,17 +416,25 @@ void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin
             float dk = half_sum(pk + pq);         // lower half: <kb, kh>; upper half: <eh, qh>
             float dq = dk;
             swap32(dk, dq);                       // every lane: dk = lower's total, dq = upper's
-            if (lane < D_IN) {
-                s_zh[wave][D_OUT + lane] = kh_j * (kb - dk);
-                s_zh[wave][D_OUT + D_IN + lane] = qh_j * (eh_j - dq);
-            }
-            if (lane < NLR) {
-                const float bv = lane == 0 ? bt[0] : lane == 1 ? bt[1] : lane == 2 ? bt[2] : bt[3];
-                const float gl = lane == 0 ? gate[0] : lane == 1 ? gate[1] : lane == 2 ? gate[2] : gate[3];
-                s_zh[wave][MAIN + lane] = (1.f - gl) * bv;
+            if constexpr (BCAST) {
+                kbar_v = kh_j * (kb - dk);
+                qbar_v = qh_j * (eh_j - dq);
+#pragma unroll
+                for (int c = 0; c < NLR; ++c)
+                    if (rg == c) zb = (1.f - gate[c]) * bt[c];
+            } else {
+                if (lane < D_IN) {
+                    s_zh[wave][D_OUT + lane] = kh_j * (kb - dk);
+                    s_zh[wave][D_OUT + D_IN + lane] = qh_j * (eh_j - dq);
+                }
+                if (lane < NLR) {
+                    const float bv = lane == 0 ? bt[0] : lane == 1 ? bt[1] : lane == 2 ? bt[2] : bt[3];
+                    const float gl = lane == 0 ? gate[0] : lane == 1 ? gate[1] : lane == 2 ? gate[2] : gate[3];
+                    s_zh[wave][MAIN + lane] = (1.f - gl) * bv;
+                }
             }
         }
-        wave_sync();
+        if constexpr (!BCAST) wave_sync();
 
         // ---- (C) uh of step t (column partials, reduced with step t-1); Wh update.
         float ev[L], uv[L];
@@ -441,7 +447,12 @@ void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin
             const int row = rg + G * r;
             float zr;
             if (G * r < D_OUT) zr = gs[row];
-            else {
+            else if constexpr (BCAST) {
+                // rows of the beta block past M hold zb = 0
+                zr = G * r < D_OUT + D_IN ? row_bcast(kbar_v, r - D_OUT / G)
+                   : G * r < MAIN         ? row_bcast(qbar_v, r - (D_OUT + D_IN) / G)
+                                          : zb;
+            } else {
                 const float zv = s_zh[wave][row_at(r, row)];
                 zr = row_ok(r, row) ? zv : 0.f;
             }
@@ -511,12 +522,11 @@ void srwm_bwd_kernel(const void* __restrict__ xv, const float* __restrict__ WTin
 //     dWinit when the walk ends, which then holds dL/d(initial state).
 //   * the per-column phase gives each lane CPL = D_IN / 64 columns
 //     (j = lane + 64 c);
-//   * the step inputs x_t and gy_t are staged CPL (resp. one per thread)
-//     entries per lane.
+//   * gy_t is staged one entry per thread.
 // No reset ablation (Wh has no second buffer to gather the windows' shares).
-template <int D_IN, int D_OUT, int NW, int P, int NLR, bool BF16, bool RESET>
+template <int D_IN, int D_OUT, int NW, int P, int NLR, bool RESET>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * kWave, NW * kWave), amdgpu_waves_per_eu(2)))
-void srwm_bwd_wide_kernel(const void* __restrict__ xv, const float* __restrict__ WTin,
+void srwm_bwd_wide_kernel(const float* __restrict__ WTin,
                           const float* __restrict__ tape, const float* __restrict__ gy,
                           const float* __restrict__ gWT, float* __restrict__ dx,
                           float* __restrict__ dWinit, int T, int H, int in_softmax, int /*reset_interval*/,
@@ -544,13 +554,12 @@ void srwm_bwd_wide_kernel(const void* __restrict__ xv, const float* __restrict__
     static_assert(RL <= R, "LDS rows");
 
     __shared__ __attribute__((aligned(16))) float s_tape[3][TW];
-    __shared__ __attribute__((aligned(16))) float s_u[3][D_IN];
     __shared__ __attribute__((aligned(16))) float s_gy[3][D_OUT];
     __shared__ __attribute__((aligned(16))) float s_red[2][NW][3][D_IN];
     __shared__ __attribute__((aligned(16))) float s_bred[2][NW][4];
     __shared__ __attribute__((aligned(16))) float s_zh[NW][M];
     __shared__ __attribute__((aligned(16))) float s_wh[RL][G][D_IN];
-    static_assert(sizeof(float) * (3 * TW + 3 * D_IN + 3 * D_OUT + 2 * NW * 3 * D_IN + 2 * NW * 4 + NW * M +
+    static_assert(sizeof(float) * (3 * TW + 3 * D_OUT + 2 * NW * 3 * D_IN + 2 * NW * 4 + NW * M +
                                    RL * G * D_IN) <= 160 * 1024, "LDS");
 
     const int tid = threadIdx.x;
@@ -608,29 +617,16 @@ void srwm_bwd_wide_kernel(const void* __restrict__ xv, const float* __restrict__
         store_wh(r, v);
     }
 
-    // Step inputs, fetched two steps ahead into registers, staged one step
-    // ahead into the LDS ring.
+    // Step inputs (the tape row, which holds u_t, and gy_t), fetched two
+    // steps ahead into registers, staged one step ahead into the LDS ring.
     float tnext[TPL];
-    float xnext[CPL];
     float gnext = 0.f;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) xnext[c] = 0.f;
     auto fetch = [&](int t) {
         const float* __restrict__ tpp = tp0 + (int64_t)t * TW;
 #pragma unroll
         for (int i = 0; i < TPL; ++i) {
             const int j = tid + NT * i;
             tnext[i] = (j < TW) ? tpp[j] : 0.f;
-        }
-        if (wave == 0) {
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                const int64_t o = x0 + (int64_t)t * x_step + lane + kWave * c;
-                if constexpr (BF16)
-                    xnext[c] = bf16_to_f32(reinterpret_cast<const uint16_t*>(xv)[o]);
-                else
-                    xnext[c] = reinterpret_cast<const float*>(xv)[o];
-            }
         }
         if (tid < D_OUT) gnext = gy[y0 + (int64_t)t * y_step + tid];
     };
@@ -639,28 +635,6 @@ void srwm_bwd_wide_kernel(const void* __restrict__ xv, const float* __restrict__
         for (int i = 0; i < TPL; ++i) {
             const int j = tid + NT * i;
             if (j < TW) s_tape[slot][j] = tnext[i];
-        }
-        if (wave == 0) {
-            float uv[CPL];
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) uv[c] = xnext[c];
-            if (in_softmax) {
-                float mx = uv[0];
-#pragma unroll
-                for (int c = 1; c < CPL; ++c) mx = fmax2(mx, uv[c]);
-                mx = wave_max(mx);
-                float sum = 0.f;
-#pragma unroll
-                for (int c = 0; c < CPL; ++c) {
-                    uv[c] = exp_f32(uv[c] - mx);
-                    sum += uv[c];
-                }
-                const float inv = rcp_f32(wave_total(sum));
-#pragma unroll
-                for (int c = 0; c < CPL; ++c) uv[c] *= inv;
-            }
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) s_u[slot][lane + kWave * c] = uv[c];
         }
         if (tid < D_OUT) s_gy[slot][tid] = gnext;
     };
@@ -750,7 +724,7 @@ void srwm_bwd_wide_kernel(const void* __restrict__ xv, const float* __restrict__
     int slot = (T - 1) % 3;
     for (int t = T - 1; t >= 0; --t) {
         const float* __restrict__ tt = s_tape[slot];
-        const float* __restrict__ us = s_u[slot];
+        const float* __restrict__ us = tt + TL::U_OFF;
         const float* __restrict__ gs = s_gy[slot];
         const int par = t & 1;
 

@@ -39,6 +39,30 @@ __device__ __forceinline__ float group_sum(float v)
     return v;
 }
 
+// Lane c of this lane's 16-lane DPP row (row_newbcast:c); k must fold to a
+// constant.
+__device__ __forceinline__ float row_bcast(float v, int k)
+{
+    switch (k) {
+    case 0: return dpp<0x150>(v);
+    case 1: return dpp<0x151>(v);
+    case 2: return dpp<0x152>(v);
+    case 3: return dpp<0x153>(v);
+    case 4: return dpp<0x154>(v);
+    case 5: return dpp<0x155>(v);
+    case 6: return dpp<0x156>(v);
+    case 7: return dpp<0x157>(v);
+    case 8: return dpp<0x158>(v);
+    case 9: return dpp<0x159>(v);
+    case 10: return dpp<0x15A>(v);
+    case 11: return dpp<0x15B>(v);
+    case 12: return dpp<0x15C>(v);
+    case 13: return dpp<0x15D>(v);
+    case 14: return dpp<0x15E>(v);
+    default: return dpp<0x15F>(v);
+    }
+}
+
 // max(a, b) for finite or infinite operands: the median of {a, b, +inf}, one
 // v_med3_f32 (a compare and select would need a VCC hazard wait between them;
 // a NaN operand is dropped here and still reaches the softmax through exp).
@@ -298,18 +322,21 @@ __device__ __forceinline__ float uniform(float v)
 //   [m, KH_OFF)           padding to a 16-byte boundary (not written)
 //   [KH_OFF, E_OFF)       phi(k_t)
 //   [E_OFF, G_OFF)        phi(q_t) - phi(k_t), as the forward pass rounded it
-//   [G_OFF, G_OFF + 4)    the learning rates sigma(beta_t) (n_lr of them, rest zero)
+//   [G_OFF, U_OFF)        the learning rates sigma(beta_t) (n_lr of them, rest zero)
+//   [U_OFF, ROW)          u_t, the step's input as the projection used it (x_t
+//                         widened, softmax-ed when the input softmax is on)
 template <int M, int D_IN>
 struct TapeLayout {
     static constexpr int KH_OFF = (M + 3) & ~3;
     static constexpr int E_OFF = KH_OFF + D_IN;
     static constexpr int G_OFF = E_OFF + D_IN;
-    static constexpr int ROW = G_OFF + 4;
+    static constexpr int U_OFF = G_OFF + 4;
+    static constexpr int ROW = U_OFF + D_IN;
 };
 
 inline int64_t tape_row(int64_t d_in, int64_t d_out, int64_t n_lr)
 {
-    return ((d_out + 2 * d_in + n_lr + 3) & ~int64_t(3)) + 2 * d_in + 4;
+    return ((d_out + 2 * d_in + n_lr + 3) & ~int64_t(3)) + 3 * d_in + 4;
 }
 
 // ----------------------------------------------------------------------------

@@ -470,8 +470,9 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
                 }
                 if constexpr (TAPE) {
                     // Tape for the backward pass: a_t, phi(k_t) (enough to undo the
-                    // update, W_{t-1} = W_t - a_t phi(k_t)^T), phi(q_t) - phi(k_t) and
-                    // the learning rates (so the backward needs no projection).
+                    // update, W_{t-1} = W_t - a_t phi(k_t)^T), phi(q_t) - phi(k_t), the
+                    // learning rates and u_t (so the backward needs no projection and
+                    // no input softmax).
                     using TL = TapeLayout<M, D_IN>;
                     float* __restrict__ tp = tape + ((int64_t)unit * T + t) * TL::ROW;
 #pragma unroll
@@ -491,6 +492,7 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
                             if (j0 + lane < D_IN) {
                                 tp[TL::KH_OFF + j0 + lane] = khw[j0 + lane];
                                 tp[TL::E_OFF + j0 + lane] = ew[j0 + lane];
+                                tp[TL::U_OFF + j0 + lane] = urow[j0 + lane];
                             }
                         }
                         if (lane < 4) tp[TL::G_OFF + lane] = lane < NLR ? gl : 0.f;

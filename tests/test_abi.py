@@ -29,7 +29,7 @@ def test_header_symbols_exported():
 
 def test_version_and_strerror():
     lib = _lib.load()
-    assert lib.srwm_version() == 400
+    assert lib.srwm_version() == 500
     for code in (OK, E_NULL, E_SHAPE, E_UNSUP, E_ALIAS, E_HIP, E_ARG):
         assert _lib.strerror(code).startswith("SRWM_")
     assert "unknown" in _lib.strerror(-99)
@@ -175,7 +175,7 @@ def test_tape_row_and_backward_support():
     lib = _lib.load()
     for d_in, d_out, n_lr in [(8, 8, 4), (16, 16, 1), (64, 64, 4), (64, 64, 1), (3, 5, 1)]:
         m = d_out + 2 * d_in + n_lr
-        assert lib.srwm_tape_row(d_in, d_out, n_lr) == (m + 3) // 4 * 4 + 2 * d_in + 4
+        assert lib.srwm_tape_row(d_in, d_out, n_lr) == (m + 3) // 4 * 4 + 3 * d_in + 4
     assert lib.srwm_tape_row(0, 8, 4) == E_SHAPE
     assert lib.srwm_tape_row(8, 8, 2) == E_SHAPE
     for d in (8, 16, 64):
@@ -245,7 +245,7 @@ def call_bwd(**kw):
     (dict(gy=None), E_NULL),
     (dict(dx=None), E_NULL),
     (dict(dx=FAKE_DX + 8), E_ARG),
-    (dict(dx=FAKE_X), E_ALIAS),
+    (dict(dx=FAKE_GY), E_ALIAS),
     (dict(dW0=FAKE_DWI + 16), E_ALIAS),
     (dict(gW_T=FAKE_DWI), E_ALIAS),
     (dict(dW_init=FAKE_TAPE + 64), E_ALIAS),

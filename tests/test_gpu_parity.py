@@ -42,9 +42,9 @@ def run_gpu(x_np, W0_np, io_dtype, flag, return_state=True, variant=-1, n_lr=4, 
 
 def check_tape(tape, x, W0, d_out, flag, n_lr, units, reset_interval=0):
     # The tape of unit (b, h) holds, per step, the update's row factor
-    # a_t = g_rate(row) * (v_t - vbar_t), phi(k_t), phi(q_t) - phi(k_t) and the
-    # rates; all from the oracle's step-by-step quantities (with resets, the
-    # steps restart from W0 every reset_interval steps).
+    # a_t = g_rate(row) * (v_t - vbar_t), phi(k_t), phi(q_t) - phi(k_t), the
+    # rates and the input u_t; all from the oracle's step-by-step quantities
+    # (with resets, the steps restart from W0 every reset_interval steps).
     d_in = x.shape[-1]
     m = W0.shape[-2]
     kh_off = (m + 3) // 4 * 4
@@ -54,7 +54,7 @@ def check_tape(tape, x, W0, d_out, flag, n_lr, units, reset_interval=0):
         rate = np.zeros(m, dtype=int)
     for b, h in units:
         W = W0[h].astype(np.float64)
-        a_ref, kh_ref, e_ref, g_ref = [], [], [], []
+        a_ref, kh_ref, e_ref, g_ref, u_ref = [], [], [], [], []
         for t in range(x.shape[1]):
             if reset_interval > 0 and t > 0 and t % reset_interval == 0:
                 W = W0[h].astype(np.float64)
@@ -63,15 +63,17 @@ def check_tape(tape, x, W0, d_out, flag, n_lr, units, reset_interval=0):
             kh_ref.append(s["kh"])
             e_ref.append(s["qh"] - s["kh"])
             g_ref.append(s["g"])
+            u_ref.append(s["u"])
             W = s["W"]
         tp = tape[b, h]
-        assert tp.shape[-1] == kh_off + 2 * d_in + 4
+        assert tp.shape[-1] == kh_off + 3 * d_in + 4
         assert rel_l2(tp[:, :m], np.array(a_ref)) <= 2e-4
         assert rel_l2(tp[:, kh_off:kh_off + d_in], np.array(kh_ref)) <= 2e-4
         assert rel_l2(tp[:, kh_off + d_in:kh_off + 2 * d_in], np.array(e_ref)) <= 2e-4
         g_off = kh_off + 2 * d_in
         assert rel_l2(tp[:, g_off:g_off + n_lr], np.array(g_ref)) <= 2e-4
         assert not tp[:, g_off + n_lr:g_off + 4].any()
+        assert rel_l2(tp[:, g_off + 4:], np.array(u_ref)) <= 2e-4
 
 
 def say(msg):
