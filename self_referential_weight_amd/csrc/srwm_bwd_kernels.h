@@ -159,6 +159,15 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
         const int kq = lane & 15;
         jc = (lane >> 4) + 4 * ((wave + kq / KR) & (NW - 1)) + G * (kq % KR);
     }
+    // Where the exchange puts column c in every wave's array.  With the
+    // columns dealt, slot 16 (c mod 4) + c / 4: the 32 lanes of a half-wave
+    // then write (column 4p + 2 b5 + b4 from lane (b5, b4, p)) and read
+    // (column jc) 32 distinct consecutive slots, with no bank conflict.
+    auto col_slot = [](int c) {
+        if constexpr (BCAST) return 16 * (c & 3) + (c >> 2);
+        else return c;
+    };
+    const int jslot = col_slot(jc);
     const int64_t x_step = (int64_t)H * D_IN;
     const int64_t y_step = (int64_t)H * D_OUT;
     const int64_t x0 = ((int64_t)b * T * H + h) * D_IN;
@@ -224,9 +233,12 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
         CX::run(part);
         if (CX::writer(lane)) {
             const int c0 = CX::col0(lane);
+            static_assert(!BCAST || CX::LC == 1, "one column per writer when the columns are dealt");
 #pragma unroll
             for (int a = 0; a < 3; ++a) {
-                if constexpr (CX::LC % 2 == 0) {
+                if constexpr (BCAST) {
+                    s_red[par][wave][a][col_slot(c0)] = part[a][0];
+                } else if constexpr (CX::LC % 2 == 0) {
 #pragma unroll
                     for (int c = 0; c < CX::LC; c += 2)
                         *reinterpret_cast<float2*>(&s_red[par][wave][a][c0 + c]) = make_float2(part[a][c], part[a][c + 1]);
@@ -266,9 +278,9 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
         if (lane < D_IN) {
 #pragma unroll
             for (int wv = 0; wv < NW; ++wv) {
-                khh_j += s_red[par][wv][0][jc];
-                eh_j += s_red[par][wv][1][jc];
-                uh_j += s_red[par][wv][2][jc];
+                khh_j += s_red[par][wv][0][jslot];
+                eh_j += s_red[par][wv][1][jslot];
+                uh_j += s_red[par][wv][2][jslot];
             }
         }
     };
