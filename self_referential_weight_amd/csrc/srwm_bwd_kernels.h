@@ -148,9 +148,13 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = NW == 1 ? 0 : tid / kWave;
+    const int wave = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid / kWave);
     const int p = tid % P;
     const int rg = tid / P;
+    // The last register row holds rows G(R-1) + rg; in a wave whose row groups
+    // all land past M (the beta block is short) it is only padding, and the
+    // wave skips it (W and Wh stay zero there).
+    const bool last_empty = NW > 1 && wave * (kWave / P) + G * (R - 1) >= M;
     const int unit = blockIdx.x;
     const int b = unit / H;
     const int h = unit - b * H;
@@ -362,6 +366,10 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
         for (int c = 0; c < L; ++c) khh[c] = 0.f;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
+            if (r == R - 1 && last_empty) {
+                ah[r] = 0.f;
+                continue;
+            }
             float as = 0.f;
 #pragma unroll
             for (int c = 0; c < L; ++c) {
@@ -377,6 +385,10 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
         for (int c = 0; c < L; ++c) eh[c] = 0.f;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
+            if (r == R - 1 && last_empty) {
+                rh[r] = 0.f;
+                continue;
+            }
             rh[r] = gate[rate(r)] * ah[r];
             bp[rate(r)] = fmaf(ah[r], a[r], bp[rate(r)]);
 #pragma unroll
@@ -408,13 +420,17 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
         u_next = lane < D_IN ? us[jc] : 0.f;
         float kbar_v = 0.f, qbar_v = 0.f, zb = 0.f;  // BCAST: this lane's column of kbar, qbar; its beta row
         {
-            float bt[4];
+            // betah totals (with dealt columns only the wave that holds the
+            // beta rows needs them)
+            float bt[4] = {0.f, 0.f, 0.f, 0.f};
+            if (!(BCAST && last_empty)) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) bt[c] = c < NLR ? s_bred[par][0][c] : 0.f;
+                for (int c = 0; c < NLR; ++c) bt[c] = s_bred[par][0][c];
 #pragma unroll
-            for (int wv = 1; wv < NW; ++wv)
+                for (int wv = 1; wv < NW; ++wv)
 #pragma unroll
-                for (int c = 0; c < NLR; ++c) bt[c] += s_bred[par][wv][c];
+                    for (int c = 0; c < NLR; ++c) bt[c] += s_bred[par][wv][c];
+            }
             const float kh_j = lane < D_IN ? tt[TL::KH_OFF + jc] : 0.f;
             const float e_j = lane < D_IN ? tt[TL::E_OFF + jc] : 0.f;
             const float qh_j = kh_j + e_j;
@@ -431,9 +447,11 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
             if constexpr (BCAST) {
                 kbar_v = kh_j * (kb - dk);
                 qbar_v = qh_j * (eh_j - dq);
+                if (!last_empty) {
 #pragma unroll
-                for (int c = 0; c < NLR; ++c)
-                    if (rg == c) zb = (1.f - gate[c]) * bt[c];
+                    for (int c = 0; c < NLR; ++c)
+                        if (rg == c) zb = (1.f - gate[c]) * bt[c];
+                }
             } else {
                 if (lane < D_IN) {
                     s_zh[wave][D_OUT + lane] = kh_j * (kb - dk);
@@ -456,6 +474,7 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
         for (int c = 0; c < L; ++c) part[2][c] = 0.f;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
+            if (r == R - 1 && last_empty) continue;
             const int row = rg + G * r;
             float zr;
             if (G * r < D_OUT) zr = gs[row];
