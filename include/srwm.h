@@ -205,7 +205,7 @@ int srwm_select_variant(int64_t d_in, int64_t d_out, int io_dtype, int n_lr,
  *   [K+2d_in+4, +d_in) u_t, the step's input as the projection used it (x_t
  *                     widened to float32, softmax-ed when the input softmax
  *                     is on)
- * ([m, K) is padding and is not written).  From the final state W_T,
+ * ([m, K) is padding: written as zeros or left as it was).  From the final state W_T,
  * srwm_backward walks t = T-1..0, undoes each update (W_{t-1} = W_t -
  * a_t phi(k_t)^T) and accumulates the adjoint; no projection and no input
  * softmax is recomputed.

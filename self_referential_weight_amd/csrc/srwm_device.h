@@ -319,7 +319,7 @@ __device__ __forceinline__ float uniform(float v)
 // The backward tape: one float32 row per (unit, step), written by the forward
 // pass and read by the backward pass.
 //   [0, m)                a_t, the row factor of the step's rank-one update
-//   [m, KH_OFF)           padding to a 16-byte boundary (not written)
+//   [m, KH_OFF)           padding to a 16-byte boundary (zeros, or not written)
 //   [KH_OFF, E_OFF)       phi(k_t)
 //   [E_OFF, G_OFF)        phi(q_t) - phi(k_t), as the forward pass rounded it
 //   [G_OFF, U_OFF)        the learning rates sigma(beta_t) (n_lr of them, rest zero)

@@ -296,9 +296,16 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
     __shared__ __attribute__((aligned(16))) float s_x[2][S][D_IN];
     // z_t, double-buffered by step parity so one barrier per step suffices.
     __shared__ __attribute__((aligned(16))) float s_z[2][R * G + 4];
-    // Each wave forms phi(k_t) and phi(q_t) - phi(k_t) itself, in its own slice.
-    __shared__ __attribute__((aligned(16))) float s_kh[NW][D_IN];
-    __shared__ __attribute__((aligned(16))) float s_e[NW][D_IN];
+    // One-wave units that write the tape assemble each step's row in s_tr and
+    // write it with 16-byte stores: phi(k_t) and phi(q_t) - phi(k_t) are
+    // formed in place there, a_t, the rates and u_t are copied in.
+    using TL = TapeLayout<M, D_IN>;
+    constexpr bool TAPE_LDS = TAPE && NW == 1;
+    static_assert(!TAPE_LDS || (TL::ROW % 4 == 0 && D_IN <= kWave), "16-byte pieces of the tape row");
+    __shared__ __attribute__((aligned(16))) float s_tr[TAPE_LDS ? TL::ROW : 4];
+    // Otherwise each wave forms phi(k_t) and phi(q_t) - phi(k_t) itself, in its own slice.
+    __shared__ __attribute__((aligned(16))) float s_kh[TAPE_LDS ? 1 : NW][TAPE_LDS ? 4 : D_IN];
+    __shared__ __attribute__((aligned(16))) float s_e[TAPE_LDS ? 1 : NW][TAPE_LDS ? 4 : D_IN];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -357,6 +364,12 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
     };
 
     XStage<D_IN, D_OUT, NW, P, BF16> xs(tid, xv, x0, x_step, T);
+    if constexpr (TAPE_LDS) {
+        // the row's padding [m, KH_OFF) is written as zeros
+        for (int o = M + lane; o < TL::KH_OFF; o += kWave) s_tr[o] = 0.f;
+    }
+    float* const khs = TAPE_LDS ? s_tr + TL::KH_OFF : s_kh[wave];
+    float* const es = TAPE_LDS ? s_tr + TL::E_OFF : s_e[wave];
 
     // The wave that stores y_t.
     constexpr int WAVE_AUX = NW >= 2 ? 1 : 0;
@@ -430,13 +443,13 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
 
                 // ---- (B) phi(k), phi(q), sigma(beta), computed by every wave for
                 // itself (identical bits in every wave); y_t from W_{t-1}.
-                wave_addresses<D_IN>(zt + D_OUT, zt + D_OUT + D_IN, s_kh[wave], s_e[wave], lane);
+                wave_addresses<D_IN>(zt + D_OUT, zt + D_OUT + D_IN, khs, es, lane);
                 const float gl = sigmoid_f32(zt[MAIN + (NLR == 4 ? (lane & 3) : 0)]);
                 const float g0 = readlane(gl, 0), g1 = readlane(gl, 1), g2 = readlane(gl, 2), g3 = readlane(gl, 3);
                 if (wave == WAVE_AUX) store_y<D_OUT, BF16>(yv, y0 + (int64_t)t * y_step, zt, lane);
                 wave_sync();
-                const float* __restrict__ khw = s_kh[wave];
-                const float* __restrict__ ew = s_e[wave];
+                const float* __restrict__ khw = khs;
+                const float* __restrict__ ew = es;
 
                 // ---- (C) Eq. (2)/(4) fused: W (qh - kh) = v - vb, times the gate.
 #pragma unroll
@@ -473,20 +486,28 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
                     // update, W_{t-1} = W_t - a_t phi(k_t)^T), phi(q_t) - phi(k_t), the
                     // learning rates and u_t (so the backward needs no projection and
                     // no input softmax).
-                    using TL = TapeLayout<M, D_IN>;
                     float* __restrict__ tp = tape + ((int64_t)unit * T + t) * TL::ROW;
+                    // a_t: the tape row buffer (one wave) or the tape itself
+                    float* __restrict__ ta = TAPE_LDS ? s_tr : tp;
 #pragma unroll
                     for (int r0 = 0; r0 < R; r0 += P) {
                         float v = acc[r0];
 #pragma unroll
                         for (int q = 1; q < P && r0 + q < R; ++q) v = (p == q) ? acc[r0 + q] : v;
                         const int row = rg + G * (r0 + p);
-                        if ((r0 + P <= R || r0 + p < R) && row < ROWS) tp[row] = v;
+                        if ((r0 + P <= R || r0 + p < R) && row < ROWS) ta[row] = v;
                     }
                     if constexpr (BETA_SEP) {
-                        if (wave == 0 && (lane & 15) == 0 && brow < NLR) tp[MAIN + brow] = accb;
+                        if (wave == 0 && (lane & 15) == 0 && brow < NLR) ta[MAIN + brow] = accb;
                     }
-                    if (wave == 0) {
+                    if constexpr (TAPE_LDS) {
+                        if (lane < 4) s_tr[TL::G_OFF + lane] = lane < NLR ? gl : 0.f;
+                        if (lane < D_IN) s_tr[TL::U_OFF + lane] = urow[lane];
+                        wave_sync();
+#pragma unroll
+                        for (int o = 4 * lane; o < TL::ROW; o += 4 * kWave)
+                            *reinterpret_cast<float4*>(tp + o) = *reinterpret_cast<const float4*>(s_tr + o);
+                    } else if (wave == 0) {
 #pragma unroll
                         for (int j0 = 0; j0 < D_IN; j0 += kWave) {
                             if (j0 + lane < D_IN) {
