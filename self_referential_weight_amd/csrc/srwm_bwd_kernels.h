@@ -252,9 +252,10 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
                 }
             }
         }
-        // Only lanes with p == 0 hold betah partials; sum them over the
-        // row-group bits below 4 in place, then over bits 5 and 4:
-        // with four rates as a reduce-scatter (rate c ends in lane 16c).
+        // The P lanes of a row group hold the same betah partials; sum them
+        // over the row-group bits below 4 in place, then over bits 5 and 4
+        // (one copy per row group): with four rates as a reduce-scatter (rate
+        // c ends in lane 16c).
 #pragma unroll
         for (int c = 0; c < NLR; ++c) {
             if constexpr (P == 4) {
@@ -280,8 +281,11 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
     auto gather = [&](int par, float& khh_j, float& eh_j, float& uh_j) {
         khh_j = eh_j = uh_j = 0.f;
         if (lane < D_IN) {
+            khh_j = s_red[par][0][0][jslot];
+            eh_j = s_red[par][0][1][jslot];
+            uh_j = s_red[par][0][2][jslot];
 #pragma unroll
-            for (int wv = 0; wv < NW; ++wv) {
+            for (int wv = 1; wv < NW; ++wv) {
                 khh_j += s_red[par][wv][0][jslot];
                 eh_j += s_red[par][wv][1][jslot];
                 uh_j += s_red[par][wv][2][jslot];
@@ -385,18 +389,14 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
         for (int c = 0; c < L; ++c) eh[c] = 0.f;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            if (r == R - 1 && last_empty) {
-                rh[r] = 0.f;
-                continue;
-            }
+            // (a skipped last row has ah = 0 and W = 0: no branch here)
             rh[r] = gate[rate(r)] * ah[r];
             bp[rate(r)] = fmaf(ah[r], a[r], bp[rate(r)]);
 #pragma unroll
             for (int c = 0; c < L; ++c) eh[c] = fmaf(w[r][c], rh[r], eh[c]);
         }
-        // every lane of a row group holds the same ah: count each row once
-#pragma unroll
-        for (int c = 0; c < 4; ++c) bp[c] = p == 0 ? bp[c] : 0.f;
+        // (every lane of a row group holds the same bp: the exchange sums them
+        // over the row-group lane bits only, and one lane per DPP row writes)
         // part[2] holds uh of step t+1 (zero before the first step)
 #pragma unroll
         for (int c = 0; c < L; ++c) {
