@@ -146,14 +146,14 @@ const Variant kVariants[] = {
     // forward passes that also write the backward tape
     SRWM_BOTH_IO_TAPE(8, 8, 1, 8, 1, 4, 1),
     SRWM_BOTH_IO_TAPE(16, 16, 1, 4, 1, 4, 1),
-    SRWM_BOTH_IO_TAPE(64, 64, 1, 4, 2, 4, 1),
+    SRWM_BOTH_IO_TAPE(64, 64, 1, 2, 2, 4, 1),
     SRWM_BOTH_IO_TAPE(64, 64, 2, 8, 2, 4, 0),
     SRWM_BOTH_IO_TAPE(64, 64, 4, 8, 1, 4, 0),
     SRWM_BOTH_IO_TAPE(64, 64, 4, 4, 1, 4, 1),
     SRWM_BOTH_IO_TAPE(64, 64, 8, 8, 1, 4, 1),
     SRWM_BOTH_IO_TAPE(8, 8, 1, 8, 1, 1, 1),
     SRWM_BOTH_IO_TAPE(16, 16, 1, 4, 1, 1, 1),
-    SRWM_BOTH_IO_TAPE(64, 64, 1, 4, 2, 1, 1),
+    SRWM_BOTH_IO_TAPE(64, 64, 1, 2, 2, 1, 1),
     SRWM_BOTH_IO_TAPE(64, 64, 2, 8, 2, 1, 0),
     SRWM_BOTH_IO_TAPE(64, 64, 4, 8, 1, 1, 0),
     SRWM_BOTH_IO_TAPE(64, 64, 4, 4, 1, 1, 1),
