@@ -42,10 +42,11 @@ struct Geom {
     static constexpr bool ALIGNED = (D_IN % G == 0) && (D_OUT % G == 0);
     static constexpr int LB = BETA_SEP ? D_IN / 16 : 0; // beta columns per lane
     // x staging: E consecutive elements per lane, LR lanes per step row.
-    // Aim for 32 step rows per chunk (8 for one-wave units, whose registers
-    // are scarcer) with every lane loading, at most 16 and at least d_in/16
-    // elements per lane (so a row spans <= 16 lanes).
-    static constexpr int E_TARGET = ((NW == 1 ? 8 : 32) * D_IN) / NT;
+    // Aim for 32 step rows per chunk (16 for one-wave units, whose registers
+    // are scarcer: at d_in = 64, 16 steps measured 0.6% (plain) and 2.4%
+    // (tape-writing) faster than 8) with every lane loading, at most 16 and
+    // at least d_in/16 elements per lane (so a row spans <= 16 lanes).
+    static constexpr int E_TARGET = ((NW == 1 ? 16 : 32) * D_IN) / NT;
     static constexpr int E_LO = D_IN / 16 > E_TARGET ? D_IN / 16 : E_TARGET;
     static constexpr int E = D_IN < 16 ? D_IN : (E_LO < 16 ? (E_LO < 1 ? 1 : E_LO) : 16);
     static constexpr int LR = D_IN / E;
