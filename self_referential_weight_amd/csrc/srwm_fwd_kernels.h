@@ -28,7 +28,7 @@ namespace srwm {
 //     With one rate, DPP rows 1-3 hold zeros and store nothing.
 //   otherwise: they are appended to the main rows (one extra register row,
 //     zero padded), which only the small test shapes use.
-template <int D_IN, int D_OUT, int NW, int P, int NLR = 4>
+template <int D_IN, int D_OUT, int NW, int P, int NLR = 4, bool LONG = false>
 struct Geom {
     static_assert(NLR == 1 || NLR == 4, "one or four learning rates");
     static constexpr int NT = NW * kWave;            // threads per unit
@@ -42,11 +42,13 @@ struct Geom {
     static constexpr bool ALIGNED = (D_IN % G == 0) && (D_OUT % G == 0);
     static constexpr int LB = BETA_SEP ? D_IN / 16 : 0; // beta columns per lane
     // x staging: E consecutive elements per lane, LR lanes per step row.
-    // Aim for 32 step rows per chunk (16 for one-wave units, whose registers
-    // are scarcer: at d_in = 64, 16 steps measured 0.6% (plain) and 2.4%
-    // (tape-writing) faster than 8) with every lane loading, at most 16 and
-    // at least d_in/16 elements per lane (so a row spans <= 16 lanes).
-    static constexpr int E_TARGET = ((NW == 1 ? 16 : 32) * D_IN) / NT;
+    // Aim for 32 step rows per chunk with every lane loading, at most 16 and
+    // at least d_in/16 elements per lane (so a row spans <= 16 lanes).  One-wave
+    // units have scarcer registers: 8 rows, or 16 with LONG (the tape-writing
+    // forward at d_in = 64: 2.4% faster than 8; the plain forward would gain
+    // 0.6% but spill 14 more registers, whose write-backs add 7.7% to its HBM
+    // traffic).
+    static constexpr int E_TARGET = ((NW == 1 ? (LONG ? 16 : 8) : 32) * D_IN) / NT;
     static constexpr int E_LO = D_IN / 16 > E_TARGET ? D_IN / 16 : E_TARGET;
     static constexpr int E = D_IN < 16 ? D_IN : (E_LO < 16 ? (E_LO < 1 ? 1 : E_LO) : 16);
     static constexpr int LR = D_IN / E;
@@ -170,9 +172,9 @@ __device__ __forceinline__ void stream_lds(const float* __restrict__ src, F&& bo
 // registers (lane tid < S*LR takes E consecutive elements of row tid/LR), then
 // widened (bf16 -> f32 is exact), optionally softmax-ed per row, and written
 // to an LDS tile.
-template <int D_IN, int D_OUT, int NW, int P, bool BF16>
+template <int D_IN, int D_OUT, int NW, int P, bool BF16, bool LONG = false>
 struct XStage {
-    using Gm = Geom<D_IN, D_OUT, NW, P>;
+    using Gm = Geom<D_IN, D_OUT, NW, P, 4, LONG>;
     static constexpr int E = Gm::E, LR = Gm::LR, S = Gm::S;
     static constexpr int XR = BF16 ? (E + 1) / 2 : E; // registers held per lane
     using XT = typename std::conditional<BF16, uint16_t, float>::type;
@@ -284,7 +286,7 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
                      float* __restrict__ wstates, int T, int H, int in_softmax, int w0_per_seq,
                      int reset_interval)
 {
-    using Gm = Geom<D_IN, D_OUT, NW, P, NLR>;
+    using Gm = Geom<D_IN, D_OUT, NW, P, NLR, TAPE>;
     constexpr int M = Gm::M, MAIN = Gm::MAIN, ROWS = Gm::ROWS;
     constexpr int L = Gm::L, G = Gm::G, R = Gm::R, LB = Gm::LB;
     constexpr int S = Gm::S;
@@ -364,7 +366,7 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
         }
     };
 
-    XStage<D_IN, D_OUT, NW, P, BF16> xs(tid, xv, x0, x_step, T);
+    XStage<D_IN, D_OUT, NW, P, BF16, TAPE> xs(tid, xv, x0, x_step, T);
     if constexpr (TAPE_LDS) {
         // the row's padding [m, KH_OFF) is written as zeros
         for (int o = M + lane; o < TL::KH_OFF; o += kWave) s_tr[o] = 0.f;
