@@ -116,6 +116,18 @@ def measured_lds(which: str, workload: str, srcs, kernel_ms: float):
             "frac": tbps / PEAK_LDS_TBPS}
 
 
+def cpu_model() -> str:
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, x_host, W0_host, budget_s: float):
     """Time the float64 oracle on the first n sequences (all heads, all T
     steps) of the workload, n sized so the run takes about budget_s."""
@@ -145,6 +157,7 @@ def cpu_baseline(w, x_host, W0_host, budget_s: float):
         "unit": "head-steps/s",
         "cores": cores,
         "kind": "oracle",
+        "cpu_model": cpu_model(),
         "sample": (f"first {n} of {w.B} sequences x {w.H} heads ({units} units) x T={w.T} "
                    f"of {w.name}, float64, {dt:.1f} s wall"),
     }
@@ -192,6 +205,7 @@ def cpu_baseline_backward(w, x_host, W0_host, gy_host, budget_s: float):
         "unit": "head-steps/s",
         "cores": cores,
         "kind": "oracle",
+        "cpu_model": cpu_model(),
         "sample": (f"forward+backward of the first {n} of {w.B} sequences x {w.H} heads ({units} units) "
                    f"x T={T} of {w.name}, float64 autograd, {dt:.1f} s wall"),
     }
@@ -306,7 +320,8 @@ def main() -> int:
                    "return_state": w.return_state, "variant": args.variant},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_TFLOPS, "traffic": traffic},
-        "kernel": {k: kernel[k] for k in ("index", "waves", "lanes_per_row", "waves_per_simd", "schedule")},
+        "kernel": dict({k: kernel[k] for k in ("index", "waves", "lanes_per_row", "waves_per_simd", "schedule")},
+                       resources=srwm.kernel_resources(kernel["index"])),
         "lds": measured_lds("forward", name, None, gpu_ms) if args.variant < 0 else None,
         "kernel_ms": gpu_ms,
         "kernel_ms_median": med_ms,
@@ -397,6 +412,7 @@ def bench_backward(args, w, name, x, x_host, W0, W0_host, dev) -> int:
         "lds": measured_lds("backward", name + "+backward", BWD_SRCS, b_ms),
         "forward_ms": f_ms,
         "backward_ms": b_ms,
+        "backward_kernel_resources": srwm.backward_resources(w.d_in, w.d_out, w.n_lr, False),
     }
     if not args.no_cpu:
         log("[bench] timing the float64 gradient oracle on a bounded sample")

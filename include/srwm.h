@@ -51,7 +51,7 @@ extern "C" {
 #endif
 
 #define SRWM_VERSION_MAJOR 0
-#define SRWM_VERSION_MINOR 5
+#define SRWM_VERSION_MINOR 6
 #define SRWM_VERSION_PATCH 0
 
 typedef enum { SRWM_IO_F32 = 0, SRWM_IO_BF16 = 1 } srwm_io_dtype_t;
@@ -187,6 +187,28 @@ int srwm_variant_info(int i, srwm_variant_info_t* info);
  */
 int srwm_select_variant(int64_t d_in, int64_t d_out, int io_dtype, int n_lr,
                         int64_t reset_interval, int64_t units);
+
+/* Resources of one compiled kernel, as the HIP runtime reports them on the
+ * current device (hipFuncGetAttributes, and
+ * hipOccupancyMaxActiveBlocksPerMultiprocessor for its launch size). */
+typedef struct srwm_kernel_resources {
+    int vgprs;             /* vector registers per lane                        */
+    int lds_bytes;         /* static LDS per workgroup                         */
+    int scratch_bytes;     /* private (spill) memory per lane                  */
+    int threads;           /* threads per workgroup of its launches            */
+    int workgroups_per_cu; /* workgroups one CU holds at once                  */
+    int waves_per_simd;    /* workgroups_per_cu * threads / 64 / 4 SIMDs       */
+} srwm_kernel_resources_t;
+
+/* srwm_variant_resources -- *out for forward variant `i`.  SRWM_ERR_ARG (bad
+ * index) and SRWM_ERR_NULL (out == NULL) come before any HIP call;
+ * SRWM_ERR_HIP if a runtime query fails (no GPU, say). */
+int srwm_variant_resources(int i, srwm_kernel_resources_t* out);
+
+/* srwm_backward_resources -- *out for the kernel srwm_backward launches for
+ * (d_in, d_out, n_lr) without (reset == 0) or with resets; errors as
+ * srwm_variant_resources, and SRWM_ERR_UNSUPPORTED when there is none. */
+int srwm_backward_resources(int64_t d_in, int64_t d_out, int n_lr, int reset, srwm_kernel_resources_t* out);
 
 /*
  * Backward pass (memory-efficient backpropagation through time: the pages

@@ -14,7 +14,7 @@ from typing import NamedTuple, Optional
 from . import _lib
 from .workloads import HEADLINE, WORKLOADS, Workload
 
-__all__ = ["forward", "backward", "srwm", "Tape", "tape_row", "deltanet_forward", "deltanet_project", "fast_forward", "srdeltanet_forward", "fwp_supported", "supported", "backward_supported", "variants", "select_variant", "m_rows", "WORKLOADS", "HEADLINE", "Workload"]
+__all__ = ["forward", "backward", "srwm", "Tape", "tape_row", "deltanet_forward", "deltanet_project", "fast_forward", "srdeltanet_forward", "fwp_supported", "supported", "backward_supported", "variants", "select_variant", "kernel_resources", "backward_resources", "m_rows", "WORKLOADS", "HEADLINE", "Workload"]
 
 
 def m_rows(d_in: int, d_out: int, n_lr: int = 4) -> int:
@@ -36,6 +36,18 @@ def backward_supported(d_in: int, d_out: int, io_dtype: str = "f32", n_lr: int =
 
 def variants() -> list[dict]:
     return _lib.variants()
+
+
+def kernel_resources(variant: int) -> dict:
+    """Registers, LDS, scratch and occupancy of forward variant `variant` on the
+    current device (vgprs, lds_bytes, scratch_bytes, threads, workgroups_per_cu,
+    waves_per_simd)."""
+    return _lib.variant_resources(variant)
+
+
+def backward_resources(d_in: int, d_out: int, n_lr: int = 4, reset: bool = False) -> dict:
+    """The same for the kernel srwm_backward launches for this shape."""
+    return _lib.backward_resources(d_in, d_out, n_lr, reset)
 
 
 def select_variant(d_in: int, d_out: int, io_dtype: str, units: int, n_lr: int = 4,

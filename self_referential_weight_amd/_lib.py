@@ -125,6 +125,12 @@ class VariantInfo(ctypes.Structure):
         "schedule", "supports_reset", "writes_tape", "is_auto")]
 
 
+class KernelResources(ctypes.Structure):
+    """srwm_kernel_resources_t."""
+    _fields_ = [(name, ctypes.c_int) for name in (
+        "vgprs", "lds_bytes", "scratch_bytes", "threads", "workgroups_per_cu", "waves_per_simd")]
+
+
 _lib = None
 
 
@@ -170,6 +176,10 @@ def load() -> ctypes.CDLL:
     lib.srwm_variant_count.restype = ci
     lib.srwm_variant_info.argtypes = [ci, ctypes.POINTER(VariantInfo)]
     lib.srwm_variant_info.restype = ci
+    lib.srwm_variant_resources.argtypes = [ci, ctypes.POINTER(KernelResources)]
+    lib.srwm_variant_resources.restype = ci
+    lib.srwm_backward_resources.argtypes = [i64, i64, ci, ci, ctypes.POINTER(KernelResources)]
+    lib.srwm_backward_resources.restype = ci
     lib.srwm_select_variant.argtypes = [i64, i64, ci, ci, i64, i64]
     lib.srwm_select_variant.restype = ci
     lib.srwm_supported.argtypes = [i64, i64, ci, ci]
@@ -184,6 +194,23 @@ def load() -> ctypes.CDLL:
 
 def strerror(code: int) -> str:
     return load().srwm_strerror(int(code)).decode()
+
+
+def _resources(rc: int, r: KernelResources) -> dict:
+    if rc != 0:
+        raise RuntimeError(strerror(rc))
+    return {name: getattr(r, name) for name, _ in KernelResources._fields_}
+
+
+def variant_resources(i: int) -> dict:
+    r = KernelResources()
+    return _resources(load().srwm_variant_resources(int(i), ctypes.byref(r)), r)
+
+
+def backward_resources(d_in: int, d_out: int, n_lr: int = 4, reset: bool = False) -> dict:
+    r = KernelResources()
+    return _resources(load().srwm_backward_resources(int(d_in), int(d_out), int(n_lr), int(bool(reset)),
+                                                     ctypes.byref(r)), r)
 
 
 def variants() -> list[dict]:

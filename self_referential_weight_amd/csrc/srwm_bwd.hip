@@ -122,6 +122,18 @@ extern "C" {
 
 int srwm_backward(const srwm_backward_args_t* args) { return backward_impl(args); }
 
+int srwm_backward_resources(int64_t d_in, int64_t d_out, int n_lr, int reset, srwm_kernel_resources_t* out)
+{
+    if (n_lr != 1 && n_lr != 4) return SRWM_ERR_ARG;
+    if (out == nullptr) return SRWM_ERR_NULL;
+    for (int i = 0; i < kNumBwdVariants; ++i) {
+        const BwdVariant& v = kBwdVariants[i];
+        if (v.d_in == d_in && v.d_out == d_out && v.nlr == n_lr && v.reset == (reset ? 1 : 0))
+            return kernel_resources(reinterpret_cast<const void*>(v.fn), v.nw * kWave, out);
+    }
+    return SRWM_ERR_UNSUPPORTED;
+}
+
 int srwm_backward_supported(int64_t d_in, int64_t d_out, int io_dtype, int n_lr)
 {
     if (io_dtype != SRWM_IO_F32 && io_dtype != SRWM_IO_BF16) return 0;

@@ -9,6 +9,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "srwm.h"
+
 namespace srwm {
 
 constexpr int kWave = 64;
@@ -341,6 +343,23 @@ inline int64_t tape_row(int64_t d_in, int64_t d_out, int64_t n_lr)
 
 // ----------------------------------------------------------------------------
 // Host-side helpers.
+
+// A kernel's registers, LDS, scratch and occupancy for `threads` threads per
+// workgroup, from the runtime's view of the loaded code object.
+inline int kernel_resources(const void* fn, int threads, srwm_kernel_resources_t* out)
+{
+    hipFuncAttributes fa;
+    if (hipFuncGetAttributes(&fa, fn) != hipSuccess) return SRWM_ERR_HIP;
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, threads, 0) != hipSuccess) return SRWM_ERR_HIP;
+    out->vgprs = fa.numRegs;
+    out->lds_bytes = static_cast<int>(fa.sharedSizeBytes);
+    out->scratch_bytes = static_cast<int>(fa.localSizeBytes);
+    out->threads = threads;
+    out->workgroups_per_cu = blocks;
+    out->waves_per_simd = blocks * (threads / kWave) / 4;
+    return SRWM_OK;
+}
 
 inline bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb)
 {

@@ -357,6 +357,13 @@ int srwm_variant_info(int i, srwm_variant_info_t* info)
     return SRWM_OK;
 }
 
+int srwm_variant_resources(int i, srwm_kernel_resources_t* out)
+{
+    if (i < 0 || i >= kNumVariants) return SRWM_ERR_ARG;
+    if (out == nullptr) return SRWM_ERR_NULL;
+    return kernel_resources(reinterpret_cast<const void*>(kVariants[i].fn), kVariants[i].nw * kWave, out);
+}
+
 int srwm_select_variant(int64_t d_in, int64_t d_out, int io_dtype, int n_lr, int64_t reset_interval,
                         int64_t units)
 {

@@ -29,7 +29,7 @@ def test_header_symbols_exported():
 
 def test_version_and_strerror():
     lib = _lib.load()
-    assert lib.srwm_version() == 500
+    assert lib.srwm_version() == 600
     for code in (OK, E_NULL, E_SHAPE, E_UNSUP, E_ALIAS, E_HIP, E_ARG):
         assert _lib.strerror(code).startswith("SRWM_")
     assert "unknown" in _lib.strerror(-99)
@@ -385,3 +385,18 @@ def test_valu_probe_validation():
     assert lib.srwm_valu_probe(FAKE_Y, 4, 0, None) == E_SHAPE
     assert lib.srwm_valu_probe(FAKE_Y + 4, 4, 1, None) == E_ARG
     assert lib.srwm_valu_probe_flop(2, 3) == 2 * 256 * 3 * 16 * 8 * 2
+
+
+# ---------------------------------------------------------------------------
+# Kernel resource queries: validation before any HIP call.
+def test_resource_query_validation():
+    lib = _lib.load()
+    r = _lib.KernelResources()
+    n = lib.srwm_variant_count()
+    assert lib.srwm_variant_resources(-1, ctypes.byref(r)) == E_ARG
+    assert lib.srwm_variant_resources(n, ctypes.byref(r)) == E_ARG
+    assert lib.srwm_variant_resources(0, None) == E_NULL
+    assert lib.srwm_backward_resources(64, 64, 2, 0, ctypes.byref(r)) == E_ARG
+    assert lib.srwm_backward_resources(64, 64, 4, 0, None) == E_NULL
+    assert lib.srwm_backward_resources(32, 32, 4, 0, ctypes.byref(r)) == E_UNSUP
+    assert lib.srwm_backward_resources(128, 128, 4, 1, ctypes.byref(r)) == E_UNSUP  # no wide reset kernel
