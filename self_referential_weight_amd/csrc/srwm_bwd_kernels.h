@@ -420,10 +420,10 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
         u_next = lane < D_IN ? us[jc] : 0.f;
         float kbar_v = 0.f, qbar_v = 0.f, zb = 0.f;  // BCAST: this lane's column of kbar, qbar; its beta row
         {
-            // betah totals (with dealt columns only the wave that holds the
-            // beta rows needs them)
+            // betah totals (with dealt columns each lane of the wave that
+            // holds the beta rows sums its own row's, below)
             float bt[4] = {0.f, 0.f, 0.f, 0.f};
-            if (!(BCAST && last_empty)) {
+            if constexpr (!BCAST) {
 #pragma unroll
                 for (int c = 0; c < NLR; ++c) bt[c] = s_bred[par][0][c];
 #pragma unroll
@@ -448,9 +448,12 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
                 kbar_v = kh_j * (kb - dk);
                 qbar_v = qh_j * (eh_j - dq);
                 if (!last_empty) {
+                    // this lane's beta row rg (rows past M hold zb = 0)
+                    const int c = rg < NLR ? rg : 0;
+                    float bsum = s_bred[par][0][c];
 #pragma unroll
-                    for (int c = 0; c < NLR; ++c)
-                        if (rg == c) zb = (1.f - gate[c]) * bt[c];
+                    for (int wv = 1; wv < NW; ++wv) bsum += s_bred[par][wv][c];
+                    zb = rg < NLR ? (1.f - tt[TL::G_OFF + c]) * bsum : 0.f;
                 }
             } else {
                 if (lane < D_IN) {
