@@ -209,7 +209,12 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
     }
 
     // Step inputs are fetched two steps ahead into registers and staged one
-    // step ahead into the LDS ring: the tape row (which holds u_t) and gy_t.
+    // step ahead into the LDS ring: the tape row (which holds u_t) and gy_t,
+    // whose entries every GS-th thread takes (spread over all waves).
+    constexpr int GS = NT / D_OUT;
+    static_assert(NT % D_OUT == 0, "gy entries spread over the threads");
+    const bool g_mine = tid % GS == 0;
+    const int g_idx = tid / GS;
     float tnext[TPL];
     float gnext = 0.f;
     auto fetch = [&](int t) {
@@ -219,7 +224,7 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
             const int j = tid + NT * i;
             tnext[i] = (j < TW) ? tp[j] : 0.f;
         }
-        if (tid < D_OUT) gnext = gy[y0 + (int64_t)t * y_step + tid];
+        if (g_mine) gnext = gy[y0 + (int64_t)t * y_step + g_idx];
     };
     auto stage = [&](int slot) {
 #pragma unroll
@@ -227,7 +232,7 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
             const int j = tid + NT * i;
             if (j < TW) s_tape[slot][j] = tnext[i];
         }
-        if (tid < D_OUT) s_gy[slot][tid] = gnext;
+        if (g_mine) s_gy[slot][g_idx] = gnext;
     };
 
     // The exchange: this lane's column partials of khh, eh and uh (and the
