@@ -101,13 +101,14 @@ __device__ __forceinline__ void wave_addresses(const float* __restrict__ k, cons
         mx = fmax2(mx, v[i]);
     }
     mx = half_max(mx);
-    float s = 0.f;
 #pragma unroll
     for (int i = 0; i < EPH; ++i) {
         const int j = hl + 32 * i;
         v[i] = (j < D) ? exp_f32(v[i] - mx) : 0.f;
-        s += v[i];
     }
+    float s = v[0];  // (not 0 + v[0]: the compiler keeps that add, as -0 + 0 = +0)
+#pragma unroll
+    for (int i = 1; i < EPH; ++i) s += v[i];
     const float inv = rcp_f32(half_sum(s));
     // Both probabilities are rounded before the difference (no fused
     // multiply-subtract), so k_t == q_t gives e == 0 exactly: the two halves
