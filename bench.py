@@ -412,7 +412,7 @@ def bench_backward(args, w, name, x, x_host, W0, W0_host, dev) -> int:
         "lds": measured_lds("backward", name + "+backward", BWD_SRCS, b_ms),
         "forward_ms": f_ms,
         "backward_ms": b_ms,
-        "backward_kernel_resources": srwm.backward_resources(w.d_in, w.d_out, w.n_lr, False),
+        "backward_kernel_resources": srwm.backward_resources(w.d_in, w.d_out, w.n_lr, False, w.units),
     }
     if not args.no_cpu:
         log("[bench] timing the float64 gradient oracle on a bounded sample")

@@ -206,9 +206,13 @@ typedef struct srwm_kernel_resources {
 int srwm_variant_resources(int i, srwm_kernel_resources_t* out);
 
 /* srwm_backward_resources -- *out for the kernel srwm_backward launches for
- * (d_in, d_out, n_lr) without (reset == 0) or with resets; errors as
- * srwm_variant_resources, and SRWM_ERR_UNSUPPORTED when there is none. */
-int srwm_backward_resources(int64_t d_in, int64_t d_out, int n_lr, int reset, srwm_kernel_resources_t* out);
+ * (d_in, d_out, n_lr), without (reset == 0) or with resets, and units = B*H
+ * (it takes, among the kernels for the shape, the fewest waves per unit that
+ * still give every SIMD two waves, else the most); errors as
+ * srwm_variant_resources, SRWM_ERR_SHAPE for units < 0, and
+ * SRWM_ERR_UNSUPPORTED when there is none. */
+int srwm_backward_resources(int64_t d_in, int64_t d_out, int n_lr, int reset, int64_t units,
+                            srwm_kernel_resources_t* out);
 
 /*
  * Backward pass (memory-efficient backpropagation through time: the pages

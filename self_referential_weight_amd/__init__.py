@@ -45,9 +45,9 @@ def kernel_resources(variant: int) -> dict:
     return _lib.variant_resources(variant)
 
 
-def backward_resources(d_in: int, d_out: int, n_lr: int = 4, reset: bool = False) -> dict:
-    """The same for the kernel srwm_backward launches for this shape."""
-    return _lib.backward_resources(d_in, d_out, n_lr, reset)
+def backward_resources(d_in: int, d_out: int, n_lr: int = 4, reset: bool = False, units: int = 2048) -> dict:
+    """The same for the kernel srwm_backward launches for this shape and B*H = units."""
+    return _lib.backward_resources(d_in, d_out, n_lr, reset, units)
 
 
 def select_variant(d_in: int, d_out: int, io_dtype: str, units: int, n_lr: int = 4,

@@ -178,7 +178,7 @@ def load() -> ctypes.CDLL:
     lib.srwm_variant_info.restype = ci
     lib.srwm_variant_resources.argtypes = [ci, ctypes.POINTER(KernelResources)]
     lib.srwm_variant_resources.restype = ci
-    lib.srwm_backward_resources.argtypes = [i64, i64, ci, ci, ctypes.POINTER(KernelResources)]
+    lib.srwm_backward_resources.argtypes = [i64, i64, ci, ci, i64, ctypes.POINTER(KernelResources)]
     lib.srwm_backward_resources.restype = ci
     lib.srwm_select_variant.argtypes = [i64, i64, ci, ci, i64, i64]
     lib.srwm_select_variant.restype = ci
@@ -207,10 +207,10 @@ def variant_resources(i: int) -> dict:
     return _resources(load().srwm_variant_resources(int(i), ctypes.byref(r)), r)
 
 
-def backward_resources(d_in: int, d_out: int, n_lr: int = 4, reset: bool = False) -> dict:
+def backward_resources(d_in: int, d_out: int, n_lr: int = 4, reset: bool = False, units: int = 2048) -> dict:
     r = KernelResources()
     return _resources(load().srwm_backward_resources(int(d_in), int(d_out), int(n_lr), int(bool(reset)),
-                                                     ctypes.byref(r)), r)
+                                                     int(units), ctypes.byref(r)), r)
 
 
 def variants() -> list[dict]:

@@ -31,11 +31,26 @@ struct BwdVariant {
 #define SRWM_BWD_WIDE(DI, DO, NW, P, NLR) \
     BwdVariant{DI, DO, NLR, NW, 0, &srwm_bwd_wide_kernel<DI, DO, NW, P, NLR, false>}
 const BwdVariant kBwdVariants[] = {
-    SRWM_BWD(8, 8, 1, 8, 4), SRWM_BWD(16, 16, 1, 4, 4), SRWM_BWD(64, 64, 4, 16, 4),
-    SRWM_BWD(8, 8, 1, 8, 1), SRWM_BWD(16, 16, 1, 4, 1), SRWM_BWD(64, 64, 4, 16, 1),
+    SRWM_BWD(8, 8, 1, 8, 4), SRWM_BWD(16, 16, 1, 4, 4), SRWM_BWD(64, 64, 4, 16, 4), SRWM_BWD(64, 64, 8, 16, 4),
+    SRWM_BWD(8, 8, 1, 8, 1), SRWM_BWD(16, 16, 1, 4, 1), SRWM_BWD(64, 64, 4, 16, 1), SRWM_BWD(64, 64, 8, 16, 1),
     SRWM_BWD_WIDE(128, 128, 8, 16, 4), SRWM_BWD_WIDE(128, 128, 8, 16, 1),
 };
 constexpr int kNumBwdVariants = sizeof(kBwdVariants) / sizeof(kBwdVariants[0]);
+
+// Among the kernels for (d_in, d_out, n_lr, reset): the fewest waves per unit
+// for which units * waves gives every SIMD of the chip two waves (>= 2048), or
+// else the most waves per unit (as the forward pass chooses); -1 if none.
+int find_bwd(int64_t d_in, int64_t d_out, int nlr, int reset, int64_t units)
+{
+    int enough = -1, most = -1;
+    for (int i = 0; i < kNumBwdVariants; ++i) {
+        const BwdVariant& v = kBwdVariants[i];
+        if (v.d_in != d_in || v.d_out != d_out || v.nlr != nlr || v.reset != reset) continue;
+        if (units >= (2048 + v.nw - 1) / v.nw && (enough < 0 || v.nw < kBwdVariants[enough].nw)) enough = i;
+        if (most < 0 || v.nw > kBwdVariants[most].nw) most = i;
+    }
+    return enough >= 0 ? enough : most;
+}
 
 int backward_impl(const srwm_backward_args_t* a)
 {
@@ -47,17 +62,14 @@ int backward_impl(const srwm_backward_args_t* a)
     if (a->io_dtype != SRWM_IO_F32 && a->io_dtype != SRWM_IO_BF16) return SRWM_ERR_ARG;
     if (a->apply_input_softmax != 0 && a->apply_input_softmax != 1) return SRWM_ERR_ARG;
     if (a->reset_interval < 0 || a->reset_interval > INT32_MAX) return SRWM_ERR_ARG;
-    int vi = -1;
     const int want_reset = a->reset_interval > 0 ? 1 : 0;
-    for (int i = 0; i < kNumBwdVariants; ++i) {
-        const BwdVariant& v = kBwdVariants[i];
-        if (v.d_in == d_in && v.d_out == d_out && v.nlr == a->n_lr && v.reset == want_reset) vi = i;
-    }
-    if (vi < 0) return SRWM_ERR_UNSUPPORTED;
     int64_t units, steps, ndx, ngy, nst, ntape, nw0, nws;
+    if (!mul_ok(B, H, &units)) return SRWM_ERR_SHAPE;
+    const int vi = find_bwd(d_in, d_out, a->n_lr, want_reset, units);
+    if (vi < 0) return SRWM_ERR_UNSUPPORTED;
     // the forward pass's end states of all windows but the last
     const int64_t nres = (a->reset_interval > 0 && T > 0) ? (T - 1) / a->reset_interval : 0;
-    if (!mul_ok(B, H, &units) || !mul_ok(units, T, &steps) || !mul_ok(steps, d_in * 4, &ndx) || !mul_ok(steps, d_out * 4, &ngy) ||
+    if (!mul_ok(units, T, &steps) || !mul_ok(steps, d_in * 4, &ndx) || !mul_ok(steps, d_out * 4, &ngy) ||
         !mul_ok(units, m * d_in * 4, &nst) || !mul_ok(steps, tape_row(d_in, d_out, a->n_lr) * 4, &ntape) ||
         !mul_ok(H, m * d_in * 4, &nw0) || !mul_ok(nst, nres, &nws))
         return SRWM_ERR_SHAPE;
@@ -122,16 +134,15 @@ extern "C" {
 
 int srwm_backward(const srwm_backward_args_t* args) { return backward_impl(args); }
 
-int srwm_backward_resources(int64_t d_in, int64_t d_out, int n_lr, int reset, srwm_kernel_resources_t* out)
+int srwm_backward_resources(int64_t d_in, int64_t d_out, int n_lr, int reset, int64_t units,
+                            srwm_kernel_resources_t* out)
 {
     if (n_lr != 1 && n_lr != 4) return SRWM_ERR_ARG;
+    if (units < 0) return SRWM_ERR_SHAPE;
     if (out == nullptr) return SRWM_ERR_NULL;
-    for (int i = 0; i < kNumBwdVariants; ++i) {
-        const BwdVariant& v = kBwdVariants[i];
-        if (v.d_in == d_in && v.d_out == d_out && v.nlr == n_lr && v.reset == (reset ? 1 : 0))
-            return kernel_resources(reinterpret_cast<const void*>(v.fn), v.nw * kWave, out);
-    }
-    return SRWM_ERR_UNSUPPORTED;
+    const int vi = find_bwd(d_in, d_out, n_lr, reset ? 1 : 0, units);
+    if (vi < 0) return SRWM_ERR_UNSUPPORTED;
+    return kernel_resources(reinterpret_cast<const void*>(kBwdVariants[vi].fn), kBwdVariants[vi].nw * kWave, out);
 }
 
 int srwm_backward_supported(int64_t d_in, int64_t d_out, int io_dtype, int n_lr)

@@ -396,7 +396,8 @@ def test_resource_query_validation():
     assert lib.srwm_variant_resources(-1, ctypes.byref(r)) == E_ARG
     assert lib.srwm_variant_resources(n, ctypes.byref(r)) == E_ARG
     assert lib.srwm_variant_resources(0, None) == E_NULL
-    assert lib.srwm_backward_resources(64, 64, 2, 0, ctypes.byref(r)) == E_ARG
-    assert lib.srwm_backward_resources(64, 64, 4, 0, None) == E_NULL
-    assert lib.srwm_backward_resources(32, 32, 4, 0, ctypes.byref(r)) == E_UNSUP
-    assert lib.srwm_backward_resources(128, 128, 4, 1, ctypes.byref(r)) == E_UNSUP  # no wide reset kernel
+    assert lib.srwm_backward_resources(64, 64, 2, 0, 1, ctypes.byref(r)) == E_ARG
+    assert lib.srwm_backward_resources(64, 64, 4, 0, -1, ctypes.byref(r)) == E_SHAPE
+    assert lib.srwm_backward_resources(64, 64, 4, 0, 1, None) == E_NULL
+    assert lib.srwm_backward_resources(32, 32, 4, 0, 1, ctypes.byref(r)) == E_UNSUP
+    assert lib.srwm_backward_resources(128, 128, 4, 1, 1, ctypes.byref(r)) == E_UNSUP  # no wide reset kernel

@@ -109,6 +109,26 @@ def test_backward_every_taped_variant():
     assert done >= 6
 
 
+@pytest.mark.parametrize("n_lr", [4, 1])
+@pytest.mark.parametrize("R", [0, 7])
+def test_backward_kernel_by_unit_count(n_lr, R):
+    # d = 64 has a 4-wave and an 8-wave backward kernel; B*H = 512 units take
+    # the 4-wave one (the small shapes above take the 8-wave one).  Whole
+    # sampled sequences against the oracle, with and without resets.
+    srwm = _srwm()
+    w = WORKLOADS["rl_d64_bf16"].with_(B=32, H=16, T=23, n_lr=n_lr)
+    assert srwm.backward_resources(64, 64, n_lr, R > 0, w.units)["threads"] == 256
+    assert srwm.backward_resources(64, 64, n_lr, R > 0, 4)["threads"] == 512
+    flag = w.apply_input_softmax
+    say(f"[bwd] 512 units n_lr={n_lr} R={R}")
+    x, W0, gy = gen_x(w), gen_W0(w), gen_gy(w)
+    _, _, dx, dWi = gpu_grads(w, x, W0, gy, None, flag, shared=False, reset_interval=R)
+    for b in (0, 17, 31):
+        dx_ref, dW_ref = oracle_bwd.grads(x[b:b + 1], W0, flag, gy[b:b + 1], None, n_lr=n_lr, reset_interval=R)
+        check_grad(dx[b:b + 1], dx_ref, f"b={b} dx")
+        check_grad(dWi[b], dW_ref, f"b={b} dW")
+
+
 @pytest.mark.parametrize("name,bs", [("fewshot_d64", [0, 31]), ("rl_d64_bf16", [0, 127])])
 def test_backward_full_size_sampled(name, bs):
     # The full workload on the GPU; whole sampled sequences (all heads, all T

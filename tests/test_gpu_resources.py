@@ -38,5 +38,7 @@ def test_backward_resources():
             assert 0 < r["vgprs"] <= 512 and r["workgroups_per_cu"] >= 1
             if d != 128:
                 assert srwm.backward_resources(d, d, n_lr, True)["threads"] == r["threads"]
-    r = srwm.backward_resources(64, 64, 4, False)
+    # d = 64: four waves per unit when there are enough units, eight below
+    r = srwm.backward_resources(64, 64, 4, False, 2048)
     assert r["threads"] == 256 and r["waves_per_simd"] == 2
+    assert srwm.backward_resources(64, 64, 4, False, 256)["threads"] == 512
