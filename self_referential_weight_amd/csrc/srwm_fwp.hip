@@ -49,6 +49,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 // MFMA 16x16x4 f32 operand layout: lane l supplies A[l % 16][l / 16] and
 // B[l / 16][l % 16]; accumulator register r of lane l is D[4 (l / 16) + r][l % 16].
 constexpr int kGM = 64, kGN = 64, kGK = 32, kGPad = 4;
+static_assert(kGK == 32, "one chunk of K: eight MFMA steps of four lane groups");
 
 // Workgroups are dispatched to the 8 XCDs round-robin (workgroup i on XCD
 // i % 8), each XCD with its own L2.  The 1-D grid is renumbered so that the
@@ -94,17 +95,31 @@ __global__ __launch_bounds__(256) void srwm_proj_gemm_kernel(const float* __rest
             *reinterpret_cast<float4*>(&sW[r][lc]) = vw;
         }
         __syncthreads();
+        // The sum over k is order-free, so in MFMA step s of the chunk lane
+        // group j = lane / 16 supplies k = 8 j + s: its operands for all eight
+        // steps are 8 consecutive floats of one row, two 16-byte LDS reads.
+        {
+            const int kb = 8 * (lane >> 4);
+            const int ra = wm + (lane & 15), rb = wn + (lane & 15);
+            const float4 a0l = *reinterpret_cast<const float4*>(&sX[ra][kb]);
+            const float4 a0h = *reinterpret_cast<const float4*>(&sX[ra][kb + 4]);
+            const float4 a1l = *reinterpret_cast<const float4*>(&sX[ra + 16][kb]);
+            const float4 a1h = *reinterpret_cast<const float4*>(&sX[ra + 16][kb + 4]);
+            const float4 b0l = *reinterpret_cast<const float4*>(&sW[rb][kb]);
+            const float4 b0h = *reinterpret_cast<const float4*>(&sW[rb][kb + 4]);
+            const float4 b1l = *reinterpret_cast<const float4*>(&sW[rb + 16][kb]);
+            const float4 b1h = *reinterpret_cast<const float4*>(&sW[rb + 16][kb + 4]);
+            const float a0[8] = {a0l.x, a0l.y, a0l.z, a0l.w, a0h.x, a0h.y, a0h.z, a0h.w};
+            const float a1[8] = {a1l.x, a1l.y, a1l.z, a1l.w, a1h.x, a1h.y, a1h.z, a1h.w};
+            const float b0[8] = {b0l.x, b0l.y, b0l.z, b0l.w, b0h.x, b0h.y, b0h.z, b0h.w};
+            const float b1[8] = {b1l.x, b1l.y, b1l.z, b1l.w, b1h.x, b1h.y, b1h.z, b1h.w};
 #pragma unroll
-        for (int kk = 0; kk < kGK; kk += 4) {
-            const int kr = kk + (lane >> 4);
-            const float a0 = sX[wm + (lane & 15)][kr];
-            const float a1 = sX[wm + 16 + (lane & 15)][kr];
-            const float b0 = sW[wn + (lane & 15)][kr];
-            const float b1 = sW[wn + 16 + (lane & 15)][kr];
-            acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc[0][0], 0, 0, 0);
-            acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, acc[0][1], 0, 0, 0);
-            acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b0, acc[1][0], 0, 0, 0);
-            acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc[1][1], 0, 0, 0);
+            for (int st = 0; st < 8; ++st) {
+                acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[st], b0[st], acc[0][0], 0, 0, 0);
+                acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[st], b1[st], acc[0][1], 0, 0, 0);
+                acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[st], b0[st], acc[1][0], 0, 0, 0);
+                acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[st], b1[st], acc[1][1], 0, 0, 0);
+            }
         }
         __syncthreads();
     }
