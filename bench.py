@@ -433,6 +433,8 @@ def bench_fwp(args, w) -> int:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        copy_calibration(int(args.copy_calibration), dev)
     log(f"[bench] generating {w.name}: {w.kind} B={w.B} H={w.H} d_in={w.d_in} d_key={w.d_key} d_v={w.d_v} T={w.T}")
     x_host = gen_x(w)
     x = torch.from_numpy(x_host).to(dev)
