@@ -32,9 +32,10 @@
  *     bf16 with round-to-nearest-even.
  *   - Memory: every pointer is a device pointer (hipMalloc'd or equivalent),
  *     16-byte aligned (SRWM_ERR_ARG otherwise) and owned by the caller.  The
- *     library allocates nothing, frees nothing, keeps no pointer after the
+ *     library allocates no memory, frees nothing, keeps no pointer after the
  *     call returns and holds no mutable global state: concurrent calls on
- *     different streams are safe.
+ *     different streams are safe.  (An SR-DeltaNet call given a second stream
+ *     creates and destroys HIP events; see there.)
  *   - Execution: asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream).  The return code covers argument validation and the launch
  *     only; a fault during execution surfaces at the next synchronisation.
@@ -51,7 +52,7 @@ extern "C" {
 #endif
 
 #define SRWM_VERSION_MAJOR 0
-#define SRWM_VERSION_MINOR 6
+#define SRWM_VERSION_MINOR 7
 #define SRWM_VERSION_PATCH 0
 
 typedef enum { SRWM_IO_F32 = 0, SRWM_IO_BF16 = 1 } srwm_io_dtype_t;
@@ -130,6 +131,12 @@ int srwm_forward_variant(const void* x, const float* W0, void* y, float* W_T,
  *                    restarts each earlier window from it: a window's start is
  *                    the initial matrix, not the previous window's end, so
  *                    undoing updates cannot cross a reset.  Ignored otherwise.
+ *   t_stride         0: x and y are [B][T][H][*]; S >= T: they are the steps
+ *                    [t0, t0+T) of longer sequences laid out [B][S][H][*]
+ *                    (x and y point at step t0 of sequence 0), so a run can
+ *                    continue over time slices of one buffer without copies.
+ *                    0 < S < T gives SRWM_ERR_SHAPE.  The tape and the window
+ *                    states keep their own [B][H][T] layout.
  */
 typedef struct srwm_forward_args {
     const void* x;
@@ -147,6 +154,7 @@ typedef struct srwm_forward_args {
     float* tape;   /* NULL, or [B][H][T][srwm_tape_row()] float32 (out): the
                       record srwm_backward needs (see there) */
     float* window_states;
+    int64_t t_stride;
 } srwm_forward_args_t;
 
 /* srwm_forward_ex -- the forward pass with every option.  Same edge cases,
@@ -334,7 +342,9 @@ int srwm_deltanet_project(const srwm_deltanet_args_t* args);
 /* The fast-matrix recurrence alone, from given projections z[B][T][H][P]
  * (P = d_v + 2*d_key + 1, rows [k; v; q; beta]): y[B][T][H][d_v] and F_T
  * (NULL allowed), starting from F0 (NULL: zero).  The second half of both
- * srwm_deltanet_forward and srwm_srdeltanet_forward. */
+ * srwm_deltanet_forward and srwm_srdeltanet_forward.  t_stride as in
+ * srwm_forward_args_t: 0, or S >= T when z and y are the steps [t0, t0+T) of
+ * [B][S][H][*] buffers. */
 typedef struct srwm_fast_args {
     const float* z;
     const float* F0;
@@ -342,10 +352,26 @@ typedef struct srwm_fast_args {
     float* F_T;
     int64_t B, T, H, d_key, d_v;
     void* stream;
+    int64_t t_stride;
 } srwm_fast_args_t;
 
 int srwm_fast_forward(const srwm_fast_args_t* args);
 
+/*
+ * SR-DeltaNet's two halves can overlap in time: the projection of steps
+ * [t0+C, t0+2C) needs nothing from the fast matrix, so it runs on `stream`
+ * while the fast-matrix recurrence of steps [t0, t0+C) runs on `aux_stream`.
+ *   aux_stream   a second hipStream_t of the caller's, or NULL.
+ *   chunk_steps  C: 0 picks a length for the shape; C >= T runs unchunked.
+ * The overlap needs aux_stream, W_T and F_T (the carried states of both
+ * halves live there between chunks); without any of them, or with C >= T, the
+ * call runs the two halves one after the other on `stream`.  The results are
+ * the same bits either way.  An overlapped call creates and destroys HIP
+ * events, makes aux_stream wait for `stream`'s earlier work and makes
+ * `stream` wait for all of it, so work queued on `stream` afterwards sees
+ * every output.  Overlapping calls that share an aux_stream are serialised
+ * on it, not wrong.
+ */
 typedef struct srwm_srdeltanet_args {
     const float* x;
     const float* W0;
@@ -358,9 +384,19 @@ typedef struct srwm_srdeltanet_args {
     int n_lr;
     int apply_input_softmax;
     void* stream;
+    void* aux_stream;
+    int64_t chunk_steps;
 } srwm_srdeltanet_args_t;
 
 int srwm_srdeltanet_forward(const srwm_srdeltanet_args_t* args);
+
+/* The chunk length srwm_srdeltanet_forward takes for chunk_steps == 0 with
+ * these sizes: about T/8 in whole 32-step pieces, at least 256, when the
+ * projection's waves over all units leave room beside it (at most two per
+ * SIMD of the chip), else T (no overlap).  Negative error code for sizes or
+ * an n_lr that srwm_srdeltanet_forward would reject. */
+int64_t srwm_srdeltanet_chunk_steps(int64_t B, int64_t T, int64_t H, int64_t d_in, int64_t d_key, int64_t d_v,
+                                    int n_lr);
 
 /* 1 if the fast-matrix kernel exists for (d_key, d_v), else 0. */
 int srwm_fwp_supported(int64_t d_key, int64_t d_v);

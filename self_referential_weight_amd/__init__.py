@@ -14,7 +14,7 @@ from typing import NamedTuple, Optional
 from . import _lib
 from .workloads import HEADLINE, WORKLOADS, Workload
 
-__all__ = ["forward", "backward", "srwm", "Tape", "tape_row", "deltanet_forward", "deltanet_project", "fast_forward", "srdeltanet_forward", "fwp_supported", "supported", "backward_supported", "variants", "select_variant", "kernel_resources", "backward_resources", "m_rows", "WORKLOADS", "HEADLINE", "Workload"]
+__all__ = ["forward", "backward", "srwm", "Tape", "tape_row", "deltanet_forward", "deltanet_project", "fast_forward", "srdeltanet_forward", "srdeltanet_chunk_steps", "fwp_supported", "supported", "backward_supported", "variants", "select_variant", "kernel_resources", "backward_resources", "m_rows", "WORKLOADS", "HEADLINE", "Workload"]
 
 
 def m_rows(d_in: int, d_out: int, n_lr: int = 4) -> int:
@@ -112,8 +112,9 @@ def forward(x, W0, apply_input_softmax: bool = False, return_state: bool = False
         raise TypeError("W0 must be float32")
     if x.dim() != 4 or W0.dim() not in (3, 4):
         raise ValueError("x must be [B,T,H,d_in] and W0 [H,m,d_in] or [B,H,m,d_in]")
-    if not (x.is_contiguous() and W0.is_contiguous()):
-        raise ValueError("x and W0 must be contiguous")
+    t_stride = _time_stride(x, "x")
+    if not W0.is_contiguous():
+        raise ValueError("W0 must be contiguous")
     B, T, H, d_in = x.shape
     per_seq = W0.dim() == 4
     if per_seq:
@@ -128,9 +129,11 @@ def forward(x, W0, apply_input_softmax: bool = False, return_state: bool = False
     if d_out < 1:
         raise ValueError(f"W0 has {m} rows; need d_out + 2*d_in + {n_lr} with d_out >= 1")
     if y is None:
+        if t_stride:
+            raise ValueError("x is a time slice of longer sequences: pass y, a slice of the same steps")
         y = torch.empty((B, T, H, d_out), dtype=x.dtype, device=x.device)
     elif (tuple(y.shape) != (B, T, H, d_out) or y.dtype != x.dtype or y.device != x.device
-          or not y.is_contiguous()):
+          or _time_stride(y, "y") != t_stride):
         raise ValueError("preallocated y has the wrong shape/dtype/device/layout")
     if save_tape:
         return_state = True
@@ -159,7 +162,8 @@ def forward(x, W0, apply_input_softmax: bool = False, return_state: bool = False
         apply_input_softmax=int(bool(apply_input_softmax)), n_lr=int(n_lr),
         w0_per_sequence=int(per_seq), reset_interval=int(reset_interval), variant=int(variant),
         stream=handle, tape=tape.data_ptr() if tape is not None and tape.numel() else None,
-        window_states=wstates.data_ptr() if wstates is not None and wstates.numel() else None)
+        window_states=wstates.data_ptr() if wstates is not None and wstates.numel() else None,
+        t_stride=t_stride)
     with torch.cuda.device(x.device):
         rc = lib.srwm_forward_ex(a)
     if rc != 0:
@@ -301,6 +305,18 @@ def _fwp_common(x, F0, d_key, d_v, return_state, z, y):
     return B, T, H, d_in, P, z, y, F_T
 
 
+def _time_stride(t, name: str) -> int:
+    """0 for a contiguous [B, T, H, D] tensor; S for the steps [t0, t0+T) of a
+    contiguous [B, S, H, D] buffer (a slice along dim 1); ValueError else."""
+    if t.is_contiguous():
+        return 0
+    B, T, H, D = t.shape
+    st = t.stride()
+    if st[3] == 1 and st[2] == D and st[1] == H * D and st[0] % max(H * D, 1) == 0 and st[0] // (H * D) >= T:
+        return st[0] // (H * D)
+    raise ValueError(f"{name} must be contiguous or a time slice [:, t0:t1] of a contiguous [B, S, H, D] tensor")
+
+
 def _ptr(t):
     return t.data_ptr() if t is not None and t.numel() else None
 
@@ -339,31 +355,58 @@ def deltanet_forward(x, W_slow, d_key: int, d_v: int, F0=None, return_state: boo
     return y, F_T, z
 
 
+_aux_streams: dict = {}
+
+
+def _aux_stream(device):
+    """The binding's second stream on `device` (default priority), made once."""
+    import torch
+
+    key = torch.device(device).index
+    if key not in _aux_streams:
+        _aux_streams[key] = torch.cuda.Stream(device)
+    return _aux_streams[key]
+
+
 def srdeltanet_forward(x, W0, d_key: int, d_v: int, F0=None, apply_input_softmax: bool = False,
-                       n_lr: int = 4, return_state: bool = False, z=None, y=None, stream=None):
+                       n_lr: int = 4, return_state: bool = False, z=None, y=None, stream=None,
+                       overlap: bool = True, aux_stream=None, chunk_steps: int = 0):
     """SR-DeltaNet forward on the GPU: a per-head SRWM (d_out = P) produces
     each step's [k; v; q; beta] for a fast matrix queried after its write.
 
     W0 [H, m, d_in] float32, m = P + 2*d_in + n_lr.  Returns (y, W_T (the
     SRWM's final state [B, H, m, d_in]) or None, F_T or None, z).
+    overlap: run the projection of later steps beside the fast matrix of
+    earlier ones on a second stream (``aux_stream``, default the binding's
+    own), in chunks of ``chunk_steps`` (0: the library's choice).  Same
+    results either way; the states of both halves are then carried in
+    W_T and F_T, allocated here when not returned.
     """
     import torch
 
     lib = _lib.load()
-    B, T, H, d_in, P, z, y, F_T = _fwp_common(x, F0, d_key, d_v, return_state, z, y)
+    B, T, H, d_in, P, z, y, F_T = _fwp_common(x, F0, d_key, d_v, return_state or overlap, z, y)
     m = P + 2 * d_in + n_lr
     if (tuple(W0.shape) != (H, m, d_in) or W0.dtype != torch.float32 or W0.device != x.device
             or not W0.is_contiguous()):
         raise ValueError(f"W0 must be a contiguous float32 [H, {m}, d_in] tensor on x's device")
-    W_T = torch.empty((B, H, m, d_in), dtype=torch.float32, device=x.device) if return_state else None
+    if chunk_steps < 0:
+        raise ValueError("chunk_steps must be >= 0")
+    W_T = (torch.empty((B, H, m, d_in), dtype=torch.float32, device=x.device)
+           if return_state or overlap else None)
+    aux = None
+    if overlap:
+        aux = _stream_handle(x, aux_stream if aux_stream is not None else _aux_stream(x.device))
     a = _lib.SrdeltanetArgs(x=_ptr(x), W0=_ptr(W0), F0=_ptr(F0), z=_ptr(z), y=_ptr(y), W_T=_ptr(W_T),
                             F_T=_ptr(F_T), B=B, T=T, H=H, d_in=d_in, d_key=d_key, d_v=d_v, n_lr=int(n_lr),
                             apply_input_softmax=int(bool(apply_input_softmax)),
-                            stream=_stream_handle(x, stream))
+                            stream=_stream_handle(x, stream), aux_stream=aux, chunk_steps=int(chunk_steps))
     with torch.cuda.device(x.device):
         rc = lib.srwm_srdeltanet_forward(a)
     if rc != 0:
         raise RuntimeError(_lib.strerror(rc))
+    if not return_state:
+        W_T = F_T = None
     return y, W_T, F_T, z
 
 
@@ -385,24 +428,46 @@ def deltanet_project(x, W_slow, d_key: int, d_v: int, z=None, stream=None):
     return z
 
 
-def fast_forward(z, d_key: int, d_v: int, F0=None, return_state: bool = False, y=None, stream=None):
+def srdeltanet_chunk_steps(B: int, T: int, H: int, d_in: int, d_key: int, d_v: int, n_lr: int = 4) -> int:
+    """Steps per chunk of srdeltanet_forward's overlapped schedule for these
+    sizes (T: the halves run one after the other)."""
+    c = _lib.load().srwm_srdeltanet_chunk_steps(B, T, H, d_in, d_key, d_v, n_lr)
+    if c < 0:
+        raise ValueError(_lib.strerror(int(c)))
+    return int(c)
+
+
+def fast_forward(z, d_key: int, d_v: int, F0=None, return_state: bool = False, y=None, stream=None, F_T=None):
     """The fast-matrix recurrence alone from given projections z [B, T, H, P]:
-    returns (y [B, T, H, d_v], F_T or None)."""
+    returns (y [B, T, H, d_v], F_T or None).  ``z`` and ``y`` may be the same
+    time slice [:, t0:t1] of longer [B, S, H, *] buffers; ``F_T`` may be
+    passed preallocated (then it is returned)."""
     import torch
 
     lib = _lib.load()
     if not isinstance(z, torch.Tensor) or z.device.type != "cuda" or z.dtype != torch.float32 \
-            or z.dim() != 4 or not z.is_contiguous() or z.shape[-1] != d_v + 2 * d_key + 1:
-        raise ValueError("z must be a contiguous float32 [B, T, H, d_v + 2*d_key + 1] tensor on a ROCm GPU")
+            or z.dim() != 4 or z.shape[-1] != d_v + 2 * d_key + 1:
+        raise ValueError("z must be a float32 [B, T, H, d_v + 2*d_key + 1] tensor on a ROCm GPU")
+    t_stride = _time_stride(z, "z")
     B, T, H, _ = z.shape
     if F0 is not None and (tuple(F0.shape) != (B, H, d_v, d_key) or F0.dtype != torch.float32
                            or F0.device != z.device or not F0.is_contiguous()):
         raise ValueError("F0 must be a contiguous float32 [B, H, d_v, d_key] tensor on z's device")
     if y is None:
+        if t_stride:
+            raise ValueError("z is a time slice of longer sequences: pass y, a slice of the same steps")
         y = torch.empty((B, T, H, d_v), dtype=torch.float32, device=z.device)
-    F_T = torch.empty((B, H, d_v, d_key), dtype=torch.float32, device=z.device) if return_state else None
+    elif (tuple(y.shape) != (B, T, H, d_v) or y.dtype != torch.float32 or y.device != z.device
+          or _time_stride(y, "y") != t_stride):
+        raise ValueError("y must be a float32 [B, T, H, d_v] tensor laid out like z")
+    if F_T is not None:
+        if (tuple(F_T.shape) != (B, H, d_v, d_key) or F_T.dtype != torch.float32 or F_T.device != z.device
+                or not F_T.is_contiguous()):
+            raise ValueError("F_T must be a contiguous float32 [B, H, d_v, d_key] tensor on z's device")
+    elif return_state:
+        F_T = torch.empty((B, H, d_v, d_key), dtype=torch.float32, device=z.device)
     a = _lib.FastArgs(z=_ptr(z), F0=_ptr(F0), y=_ptr(y), F_T=_ptr(F_T), B=B, T=T, H=H, d_key=d_key, d_v=d_v,
-                      stream=_stream_handle(z, stream))
+                      stream=_stream_handle(z, stream), t_stride=t_stride)
     with torch.cuda.device(z.device):
         rc = lib.srwm_fast_forward(a)
     if rc != 0:

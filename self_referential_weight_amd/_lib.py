@@ -32,6 +32,7 @@ class ForwardArgs(ctypes.Structure):
         ("stream", ctypes.c_void_p),
         ("tape", ctypes.c_void_p),
         ("window_states", ctypes.c_void_p),
+        ("t_stride", ctypes.c_int64),
     ]
 
 
@@ -99,6 +100,8 @@ class SrdeltanetArgs(ctypes.Structure):
         ("n_lr", ctypes.c_int),
         ("apply_input_softmax", ctypes.c_int),
         ("stream", ctypes.c_void_p),
+        ("aux_stream", ctypes.c_void_p),
+        ("chunk_steps", ctypes.c_int64),
     ]
 
 
@@ -115,6 +118,7 @@ class FastArgs(ctypes.Structure):
         ("d_key", ctypes.c_int64),
         ("d_v", ctypes.c_int64),
         ("stream", ctypes.c_void_p),
+        ("t_stride", ctypes.c_int64),
     ]
 
 
@@ -168,6 +172,8 @@ def load() -> ctypes.CDLL:
     lib.srwm_fast_forward.restype = ci
     lib.srwm_fwp_supported.argtypes = [i64, i64]
     lib.srwm_fwp_supported.restype = ci
+    lib.srwm_srdeltanet_chunk_steps.argtypes = [i64, i64, i64, i64, i64, i64, ci]
+    lib.srwm_srdeltanet_chunk_steps.restype = i64
     lib.srwm_valu_probe.argtypes = [ctypes.c_void_p, i64, ci, ctypes.c_void_p]
     lib.srwm_valu_probe.restype = ci
     lib.srwm_valu_probe_flop.argtypes = [i64, ci]

@@ -376,4 +376,20 @@ inline bool mul_ok(int64_t a, int64_t b, int64_t* out)
     return true;
 }
 
+// A validated forward call: the variant, the units and the window-state
+// buffer its kernel gets, and whether any kernel runs.  forward_check
+// validates exactly as srwm_forward_ex; forward_launch launches the kernel of
+// a plan with the buffers, T and t_stride of `a` and checks nothing (the
+// chunks of a validated call may read their initial state from W_T in place:
+// every lane loads its own state elements before it writes them back).
+struct FwdPlan {
+    int vi;
+    int waves;  // of the variant's workgroup
+    int64_t units;
+    float* wstates;
+    bool run;
+};
+int forward_check(const srwm_forward_args_t* a, FwdPlan* plan);
+int forward_launch(const FwdPlan& plan, const srwm_forward_args_t* a);
+
 }  // namespace srwm

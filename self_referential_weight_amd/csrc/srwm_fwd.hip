@@ -44,7 +44,7 @@ using namespace srwm;
 
 // ----------------------------------------------------------------------------
 // Variant table.
-using KernelFn = void (*)(const void*, const float*, void*, float*, float*, float*, int, int, int, int, int);
+using KernelFn = void (*)(const void*, const float*, void*, float*, float*, float*, int, int, int, int, int, int);
 
 struct Variant {
     int d_in, d_out, io, nw, p, wpe, nlr, fused, reset, tape, is_auto;
@@ -214,11 +214,17 @@ int find_variant(int64_t d_in, int64_t d_out, int io, int nlr, bool reset, bool 
     return -1;
 }
 
-int forward_impl(const srwm_forward_args_t* a)
+}  // namespace
+
+namespace srwm {
+
+int forward_check(const srwm_forward_args_t* a, FwdPlan* plan)
 {
     if (a == nullptr) return SRWM_ERR_NULL;
     const int64_t B = a->B, T = a->T, H = a->H, d_in = a->d_in, d_out = a->d_out, m = a->m;
     if (B < 0 || T < 0 || H < 0 || d_in < 1 || d_out < 1) return SRWM_ERR_SHAPE;
+    if (a->t_stride < 0 || (a->t_stride > 0 && a->t_stride < T)) return SRWM_ERR_SHAPE;
+    const int64_t S = a->t_stride > 0 ? a->t_stride : T;
     if (a->n_lr != 1 && a->n_lr != 4) return SRWM_ERR_ARG;
     if (m != d_out + 2 * d_in + a->n_lr) return SRWM_ERR_SHAPE;
     if (a->io_dtype != SRWM_IO_F32 && a->io_dtype != SRWM_IO_BF16) return SRWM_ERR_ARG;
@@ -232,16 +238,19 @@ int forward_impl(const srwm_forward_args_t* a)
     const int vi = find_variant(d_in, d_out, a->io_dtype, a->n_lr, reset, want_tape, a->variant, units_hint);
     if (vi < 0) return a->variant >= 0 ? SRWM_ERR_ARG : SRWM_ERR_UNSUPPORTED;
     const int64_t es = a->io_dtype == SRWM_IO_BF16 ? 2 : 4;
-    int64_t units, steps, nx, ny, nw0, nwt, ntape, nws;
+    int64_t units, steps, span, nx, ny, nw0, nwt, ntape, nws;
     // with a tape and resets: the end states of all windows but the last
     const int64_t nres = (reset && want_tape && T > 0) ? (T - 1) / a->reset_interval : 0;
-    if (!mul_ok(B, H, &units) || !mul_ok(units, T, &steps) || !mul_ok(steps, d_in * es, &nx) ||
-        !mul_ok(steps, d_out * es, &ny) || !mul_ok(a->w0_per_sequence ? units : H, m * d_in * 4, &nw0) ||
+    // x and y cover (B-1)*S + T steps of each head (all of them when S == T)
+    if (!mul_ok(B > 0 ? B - 1 : 0, S, &span) || span > INT64_MAX - T) return SRWM_ERR_SHAPE;
+    span = (B > 0 && T > 0) ? span + T : 0;
+    if (!mul_ok(B, H, &units) || !mul_ok(units, T, &steps) || !mul_ok(span, H * d_in * es, &nx) ||
+        !mul_ok(span, H * d_out * es, &ny) || !mul_ok(a->w0_per_sequence ? units : H, m * d_in * 4, &nw0) ||
         !mul_ok(units, m * d_in * 4, &nwt) || !mul_ok(steps, tape_row(d_in, d_out, a->n_lr) * 4, &ntape) ||
         !mul_ok(nwt, nres, &nws))
         return SRWM_ERR_SHAPE;
     if (!want_tape) ntape = 0;
-    if (units > INT32_MAX || T > INT32_MAX || H > INT32_MAX) return SRWM_ERR_SHAPE;
+    if (units > INT32_MAX || S > INT32_MAX || H > INT32_MAX) return SRWM_ERR_SHAPE;
     const void* x = a->x;
     const float* W0 = a->W0;
     void* y = a->y;
@@ -256,6 +265,11 @@ int forward_impl(const srwm_forward_args_t* a)
          reinterpret_cast<uintptr_t>(y) | reinterpret_cast<uintptr_t>(W_T) |
          reinterpret_cast<uintptr_t>(tape) | reinterpret_cast<uintptr_t>(wstates)) & 15u)
         return SRWM_ERR_ARG;
+    plan->vi = vi;
+    plan->waves = kVariants[vi].nw;
+    plan->units = units;
+    plan->wstates = wstates;
+    plan->run = false;
     if (units == 0) return SRWM_OK;
     if (W_T == nullptr) nwt = 0;
     if (ranges_overlap(x, nx, y, ny) || ranges_overlap(W0, nw0, W_T, nwt) ||
@@ -266,17 +280,40 @@ int forward_impl(const srwm_forward_args_t* a)
         ranges_overlap(wstates, nws, W0, nw0) || ranges_overlap(wstates, nws, y, ny) ||
         ranges_overlap(wstates, nws, W_T, nwt) || ranges_overlap(wstates, nws, tape, ntape))
         return SRWM_ERR_ALIAS;
-    if (T == 0 && W_T == nullptr) return SRWM_OK;
+    plan->run = !(T == 0 && W_T == nullptr);
+    return SRWM_OK;
+}
 
-    const Variant& v = kVariants[vi];
-    int Ti = static_cast<int>(T), Hi = static_cast<int>(H), fl = a->apply_input_softmax;
+int forward_launch(const FwdPlan& plan, const srwm_forward_args_t* a)
+{
+    const Variant& v = kVariants[plan.vi];
+    const void* x = a->x;
+    const float* W0 = a->W0;
+    void* y = a->y;
+    float* W_T = a->W_T;
+    float* tape = a->tape;
+    float* wstates = plan.wstates;
+    int Ti = static_cast<int>(a->T), Si = static_cast<int>(a->t_stride > 0 ? a->t_stride : a->T);
+    int Hi = static_cast<int>(a->H), fl = a->apply_input_softmax;
     int per_seq = a->w0_per_sequence, rst = static_cast<int>(a->reset_interval);
-    void* args[] = {const_cast<void**>(&x), const_cast<float**>(&W0), &y, &W_T, &tape, &wstates, &Ti, &Hi, &fl,
+    void* args[] = {const_cast<void**>(&x), const_cast<float**>(&W0), &y, &W_T, &tape, &wstates, &Ti, &Si, &Hi, &fl,
                     &per_seq, &rst};
     const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(v.fn),
-                                           dim3(static_cast<unsigned>(units)), dim3(v.nw * kWave),
+                                           dim3(static_cast<unsigned>(plan.units)), dim3(v.nw * kWave),
                                            args, 0, static_cast<hipStream_t>(a->stream));
     return err == hipSuccess ? SRWM_OK : SRWM_ERR_HIP;
+}
+
+}  // namespace srwm
+
+namespace {
+
+int forward_impl(const srwm_forward_args_t* a)
+{
+    FwdPlan plan;
+    const int rc = forward_check(a, &plan);
+    if (rc != SRWM_OK || !plan.run) return rc;
+    return forward_launch(plan, a);
 }
 
 srwm_forward_args_t basic_args(const void* x, const float* W0, void* y, float* W_T, int64_t B, int64_t T,
@@ -303,6 +340,7 @@ srwm_forward_args_t basic_args(const void* x, const float* W0, void* y, float* W
     a.stream = stream;
     a.tape = nullptr;
     a.window_states = nullptr;
+    a.t_stride = 0;
     return a;
 }
 

@@ -284,8 +284,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * kWave, NW * kWave),
                           amdgpu_waves_per_eu(WPE)))
 void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
                      void* __restrict__ yv, float* __restrict__ WT, float* __restrict__ tape,
-                     float* __restrict__ wstates, int T, int H, int in_softmax, int w0_per_seq,
-                     int reset_interval)
+                     float* __restrict__ wstates, int T, int t_stride, int H, int in_softmax,
+                     int w0_per_seq, int reset_interval)
 {
     using Gm = Geom<D_IN, D_OUT, NW, P, NLR, TAPE>;
     constexpr int M = Gm::M, MAIN = Gm::MAIN, ROWS = Gm::ROWS;
@@ -320,11 +320,12 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
     const int b = unit / H;
     const int h = unit - b * H;
 
-    // Element offsets.  x[b][t][h][:] = x0 + t*x_step.
+    // Element offsets.  x[b][t][h][:] = x0 + t*x_step; sequences lie t_stride
+    // (>= T) steps apart, so x and y may be time slices of longer sequences.
     const int64_t x_step = (int64_t)H * D_IN;
     const int64_t y_step = (int64_t)H * D_OUT;
-    const int64_t x0 = ((int64_t)b * T * H + h) * D_IN;
-    const int64_t y0 = ((int64_t)b * T * H + h) * D_OUT;
+    const int64_t x0 = ((int64_t)b * t_stride * H + h) * D_IN;
+    const int64_t y0 = ((int64_t)b * t_stride * H + h) * D_OUT;
     const float* __restrict__ w0h = W0 + (int64_t)(w0_per_seq ? unit : h) * M * D_IN;
 
     // ---- a0: W <- W0 into registers (again at each reset of the ablation).
@@ -560,8 +561,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * kWave, NW * kWave),
                           amdgpu_waves_per_eu(WPE)))
 void srwm_fwd_fused_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
                            void* __restrict__ yv, float* __restrict__ WT, float* /*tape: not written*/,
-                           float* /*window states: not written*/, int T, int H, int in_softmax, int w0_per_seq,
-                           int /*reset_interval: not supported by this schedule*/)
+                           float* /*window states: not written*/, int T, int t_stride, int H, int in_softmax,
+                           int w0_per_seq, int /*reset_interval: not supported by this schedule*/)
 {
     using Gm = Geom<D_IN, D_OUT, NW, P, NLR>;
     constexpr int M = Gm::M, MAIN = Gm::MAIN, ROWS = Gm::ROWS;
@@ -587,8 +588,8 @@ void srwm_fwd_fused_kernel(const void* __restrict__ xv, const float* __restrict_
     const int h = unit - b * H;
     const int64_t x_step = (int64_t)H * D_IN;
     const int64_t y_step = (int64_t)H * D_OUT;
-    const int64_t x0 = ((int64_t)b * T * H + h) * D_IN;
-    const int64_t y0 = ((int64_t)b * T * H + h) * D_OUT;
+    const int64_t x0 = ((int64_t)b * t_stride * H + h) * D_IN;
+    const int64_t y0 = ((int64_t)b * t_stride * H + h) * D_OUT;
     const float* __restrict__ w0h = W0 + (int64_t)(w0_per_seq ? unit : h) * M * D_IN;
 
     // ---- a0: W <- W0[h].

@@ -151,7 +151,7 @@ template <int D_KEY, int D_V, int NW, int P, int S>
 __global__ __launch_bounds__(NW * 64) void srwm_fast_kernel(const float* __restrict__ Z,
                                                             const float* __restrict__ F0,
                                                             float* __restrict__ y, float* __restrict__ FT,
-                                                            int T, int H)
+                                                            int T, int t_stride, int H)
 {
     constexpr int PR = D_V + 2 * D_KEY + 1;
     constexpr int L = D_KEY / P;
@@ -178,9 +178,9 @@ __global__ __launch_bounds__(NW * 64) void srwm_fast_kernel(const float* __restr
     const int b = unit / H;
     const int h = unit - b * H;
     const int64_t z_step = (int64_t)H * PR;
-    const int64_t z0 = ((int64_t)b * T * H + h) * PR;
+    const int64_t z0 = ((int64_t)b * t_stride * H + h) * PR;  // sequences t_stride (>= T) steps apart
     const int64_t y_step = (int64_t)H * D_V;
-    const int64_t y0 = ((int64_t)b * T * H + h) * D_V;
+    const int64_t y0 = ((int64_t)b * t_stride * H + h) * D_V;
 
     float F[R][L];
 #pragma unroll
@@ -299,7 +299,7 @@ __global__ __launch_bounds__(NW * 64) void srwm_fast_kernel(const float* __restr
 
 // ----------------------------------------------------------------------------
 // Variants: (d_key, d_v, lanes per row).
-using FastFn = void (*)(const float*, const float*, float*, float*, int, int);
+using FastFn = void (*)(const float*, const float*, float*, float*, int, int, int);
 struct FastVariant {
     int d_key, d_v, nw;
     FastFn fn;
@@ -344,11 +344,22 @@ int fwp_sizes(int64_t B, int64_t T, int64_t H, int64_t d_in, int64_t d_key, int6
     return SRWM_OK;
 }
 
-int launch_fast(int vi, const float* z, const float* F0, float* y, float* FT, int64_t units, int64_t T,
-                int64_t H, void* stream)
+// Steps of each head that buffers of T steps per sequence, sequences
+// t_stride (0: T) apart, cover: (B-1)*t_stride + T, or 0 when empty.
+int time_span(int64_t B, int64_t T, int64_t t_stride, int64_t* span)
 {
-    int Ti = static_cast<int>(T), Hi = static_cast<int>(H);
-    void* args[] = {const_cast<float**>(&z), const_cast<float**>(&F0), &y, &FT, &Ti, &Hi};
+    if (t_stride < 0 || (t_stride > 0 && t_stride < T)) return SRWM_ERR_SHAPE;
+    const int64_t S = t_stride > 0 ? t_stride : T;
+    if (S > INT32_MAX || !mul_ok(B > 0 ? B - 1 : 0, S, span) || *span > INT64_MAX - T) return SRWM_ERR_SHAPE;
+    *span = (B > 0 && T > 0) ? *span + T : 0;
+    return SRWM_OK;
+}
+
+int launch_fast(int vi, const float* z, const float* F0, float* y, float* FT, int64_t units, int64_t T,
+                int64_t t_stride, int64_t H, void* stream)
+{
+    int Ti = static_cast<int>(T), Si = static_cast<int>(t_stride > 0 ? t_stride : T), Hi = static_cast<int>(H);
+    void* args[] = {const_cast<float**>(&z), const_cast<float**>(&F0), &y, &FT, &Ti, &Si, &Hi};
     const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(kFastVariants[vi].fn),
                                            dim3(static_cast<unsigned>(units)), dim3(kFastVariants[vi].nw * kWave), args, 0,
                                            static_cast<hipStream_t>(stream));
@@ -420,7 +431,7 @@ int deltanet_impl(const srwm_deltanet_args_t* a, bool project_only)
     if (a->B * a->H == 0) return SRWM_OK;
     const int rp = launch_projection(a, K, C);
     if (rp != SRWM_OK || project_only) return rp;
-    return launch_fast(vi, a->z, a->F0, a->y, a->F_T, a->B * a->H, a->T, a->H, a->stream);
+    return launch_fast(vi, a->z, a->F0, a->y, a->F_T, a->B * a->H, a->T, 0, a->H, a->stream);
 }
 
 int fast_impl(const srwm_fast_args_t* a)
@@ -431,6 +442,11 @@ int fast_impl(const srwm_fast_args_t* a)
     if (rc != SRWM_OK) return rc;
     const int vi = find_fast(a->d_key, a->d_v, s.units);
     if (vi < 0) return SRWM_ERR_UNSUPPORTED;
+    int64_t span;
+    rc = time_span(a->B, a->T, a->t_stride, &span);
+    if (rc != SRWM_OK) return rc;
+    const int64_t P = a->d_v + 2 * a->d_key + 1;
+    if (!mul_ok(span * a->H, P * 4, &s.nz) || !mul_ok(span * a->H, a->d_v * 4, &s.ny)) return SRWM_ERR_SHAPE;
     if (s.units == 0) return SRWM_OK;
     if (s.steps > 0 && (a->z == nullptr || a->y == nullptr)) return SRWM_ERR_NULL;
     if ((reinterpret_cast<uintptr_t>(a->F0) | reinterpret_cast<uintptr_t>(a->y) |
@@ -444,7 +460,56 @@ int fast_impl(const srwm_fast_args_t* a)
         for (int i = 0; i < 2; ++i)
             if (ranges_overlap(outs[o], nouts[o], ins[i], nins[i])) return SRWM_ERR_ALIAS;
     if (ranges_overlap(a->y, s.ny, a->F_T, a->F_T ? s.nf : 0)) return SRWM_ERR_ALIAS;
-    return launch_fast(vi, a->z, a->F0, a->y, a->F_T, s.units, a->T, a->H, a->stream);
+    return launch_fast(vi, a->z, a->F0, a->y, a->F_T, s.units, a->T, a->t_stride, a->H, a->stream);
+}
+
+// Steps per chunk when SR-DeltaNet's halves overlap: about an eighth of the
+// sequence, whole 32-step pieces, at least 256 steps (the fast matrix's last
+// chunk is the part that cannot overlap; each chunk adds a state store and
+// reload and a launch).  Only when the projection leaves room on the chip (at
+// most two of its waves per SIMD over all units); else unchunked.
+int64_t auto_chunk_steps(int64_t T, int64_t units, int proj_waves)
+{
+    if (units * proj_waves > 2048) return T;
+    int64_t C = (T + 7) / 8;
+    C = (C + 31) / 32 * 32;
+    return C < 256 ? 256 : C;
+}
+
+// The two halves over chunks of C steps: the projection of chunk c on
+// `stream`, then (after an event) the fast matrix of chunk c on aux.  The
+// states carried between chunks live in W_T and F_T, read and rewritten in
+// place by each chunk's kernel.
+int srdeltanet_overlapped(const srwm_srdeltanet_args_t* a, const FwdPlan& plan, const srwm_forward_args_t& f,
+                          int vi, int64_t units, int64_t C)
+{
+    const hipStream_t main_s = static_cast<hipStream_t>(a->stream);
+    const hipStream_t aux_s = static_cast<hipStream_t>(a->aux_stream);
+    const int64_t P = a->d_v + 2 * a->d_key + 1;
+    hipEvent_t ev;
+    for (int64_t t0 = 0; t0 < a->T; t0 += C) {
+        const int64_t n = (a->T - t0) < C ? (a->T - t0) : C;
+        srwm_forward_args_t fc = f;
+        fc.x = a->x + t0 * a->H * a->d_in;
+        fc.y = a->z + t0 * a->H * P;
+        fc.T = n;
+        fc.t_stride = a->T;
+        fc.W0 = t0 == 0 ? a->W0 : a->W_T;
+        fc.w0_per_sequence = t0 == 0 ? 0 : 1;
+        int rc = forward_launch(plan, &fc);
+        if (rc != SRWM_OK) return rc;
+        if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) return SRWM_ERR_HIP;
+        const bool ok = hipEventRecord(ev, main_s) == hipSuccess && hipStreamWaitEvent(aux_s, ev, 0) == hipSuccess;
+        (void)hipEventDestroy(ev);
+        if (!ok) return SRWM_ERR_HIP;
+        rc = launch_fast(vi, a->z + t0 * a->H * P, t0 == 0 ? a->F0 : a->F_T, a->y + t0 * a->H * a->d_v, a->F_T,
+                         units, n, a->T, a->H, a->aux_stream);
+        if (rc != SRWM_OK) return rc;
+    }
+    if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) return SRWM_ERR_HIP;
+    const bool ok = hipEventRecord(ev, aux_s) == hipSuccess && hipStreamWaitEvent(main_s, ev, 0) == hipSuccess;
+    (void)hipEventDestroy(ev);
+    return ok ? SRWM_OK : SRWM_ERR_HIP;
 }
 
 int srdeltanet_impl(const srwm_srdeltanet_args_t* a)
@@ -457,6 +522,7 @@ int srdeltanet_impl(const srwm_srdeltanet_args_t* a)
     if (vi < 0) return SRWM_ERR_UNSUPPORTED;
     const int64_t P = a->d_v + 2 * a->d_key + 1;
     if (a->n_lr != 1 && a->n_lr != 4) return SRWM_ERR_ARG;
+    if (a->chunk_steps < 0) return SRWM_ERR_ARG;
     const int64_t m = P + 2 * a->d_in + a->n_lr;
     int64_t nst, nw0;
     if (!mul_ok(s.units, m * a->d_in * 4, &nst) || !mul_ok(a->H, m * a->d_in * 4, &nw0)) return SRWM_ERR_SHAPE;
@@ -498,12 +564,20 @@ int srdeltanet_impl(const srwm_srdeltanet_args_t* a)
     f.stream = a->stream;
     f.tape = nullptr;
     f.window_states = nullptr;
-    rc = srwm_forward_ex(&f);
+    f.t_stride = 0;
+    FwdPlan plan;
+    rc = forward_check(&f, &plan);
     if (rc != SRWM_OK) return rc;
-    if (a->T == 0) {
-        if (a->F_T == nullptr) return SRWM_OK;
+    const int64_t C = a->chunk_steps > 0 ? a->chunk_steps : auto_chunk_steps(a->T, s.units, plan.waves);
+    if (C < a->T && a->aux_stream != nullptr && a->aux_stream != a->stream && a->W_T != nullptr &&
+        a->F_T != nullptr)
+        return srdeltanet_overlapped(a, plan, f, vi, s.units, C);
+    if (plan.run) {
+        rc = forward_launch(plan, &f);
+        if (rc != SRWM_OK) return rc;
     }
-    return launch_fast(vi, a->z, a->F0, a->y, a->F_T, s.units, a->T, a->H, a->stream);
+    if (a->T == 0 && a->F_T == nullptr) return SRWM_OK;
+    return launch_fast(vi, a->z, a->F0, a->y, a->F_T, s.units, a->T, 0, a->H, a->stream);
 }
 
 }  // namespace
@@ -519,5 +593,20 @@ int srwm_fast_forward(const srwm_fast_args_t* args) { return fast_impl(args); }
 int srwm_srdeltanet_forward(const srwm_srdeltanet_args_t* args) { return srdeltanet_impl(args); }
 
 int srwm_fwp_supported(int64_t d_key, int64_t d_v) { return find_fast(d_key, d_v) >= 0 ? 1 : 0; }
+
+int64_t srwm_srdeltanet_chunk_steps(int64_t B, int64_t T, int64_t H, int64_t d_in, int64_t d_key, int64_t d_v,
+                                    int n_lr)
+{
+    FwpSizes s;
+    const int rc = fwp_sizes(B, T, H, d_in, d_key, d_v, &s);
+    if (rc != SRWM_OK) return rc;
+    if (n_lr != 1 && n_lr != 4) return SRWM_ERR_ARG;
+    if (find_fast(d_key, d_v, s.units) < 0) return SRWM_ERR_UNSUPPORTED;
+    const int vi = srwm_select_variant(d_in, d_v + 2 * d_key + 1, SRWM_IO_F32, n_lr, 0, s.units);
+    if (vi < 0) return vi;
+    srwm_variant_info_t info;
+    if (srwm_variant_info(vi, &info) != SRWM_OK) return SRWM_ERR_UNSUPPORTED;
+    return auto_chunk_steps(T, s.units, info.waves);
+}
 
 }  // extern "C"

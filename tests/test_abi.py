@@ -29,7 +29,7 @@ def test_header_symbols_exported():
 
 def test_version_and_strerror():
     lib = _lib.load()
-    assert lib.srwm_version() == 600
+    assert lib.srwm_version() == 700
     for code in (OK, E_NULL, E_SHAPE, E_UNSUP, E_ALIAS, E_HIP, E_ARG):
         assert _lib.strerror(code).startswith("SRWM_")
     assert "unknown" in _lib.strerror(-99)
@@ -132,6 +132,9 @@ def call_ex(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
+    (dict(t_stride=2), E_SHAPE),                    # sequences closer than T steps
+    (dict(t_stride=-1), E_SHAPE),
+    (dict(t_stride=1000, y=FAKE_X + 65536), E_ALIAS),  # y inside x's strided span
     (dict(n_lr=2), E_ARG),
     (dict(n_lr=1, m=52), E_SHAPE),
     (dict(n_lr=4, m=49), E_SHAPE),
@@ -321,6 +324,7 @@ def test_deltanet_validation(kw, code):
     (dict(y=FAKE_Z + 64), E_ALIAS),
     (dict(F_T=FAKE_W0 + 16), E_ALIAS),
     (dict(y=None), E_NULL),
+    (dict(chunk_steps=-1), E_ARG),
 ])
 def test_srdeltanet_validation(kw, code):
     assert call_sdn(**kw) == code
@@ -332,6 +336,48 @@ def test_fwp_empty_problems_are_noops():
     assert lib.srwm_srdeltanet_forward(None) == E_NULL
     assert call_dn(B=0, x=None, z=None, y=None) == OK
     assert call_sdn(H=0, x=None, z=None, y=None, W0=None) == OK
+
+
+def test_srdeltanet_chunk_steps():
+    lib = _lib.load()
+    # 256 units of an 8-wave projection leave room: about T/8 in 32-step pieces
+    assert lib.srwm_srdeltanet_chunk_steps(128, 4096, 2, 64, 64, 64, 4) == 512
+    assert lib.srwm_srdeltanet_chunk_steps(128, 1000, 2, 64, 64, 64, 1) == 256   # at least 256
+    assert lib.srwm_srdeltanet_chunk_steps(128, 3000, 2, 64, 64, 64, 4) == 384   # ceil(375 / 32) * 32
+    # a projection that fills the chip: no chunks (T)
+    assert lib.srwm_srdeltanet_chunk_steps(1024, 4096, 16, 64, 64, 64, 4) == 4096
+    assert lib.srwm_srdeltanet_chunk_steps(2, 3, 2, 16, 16, 16, 2) == E_ARG
+    assert lib.srwm_srdeltanet_chunk_steps(2, 3, 2, 16, 7, 7, 4) == E_UNSUP
+    assert lib.srwm_srdeltanet_chunk_steps(-1, 3, 2, 16, 16, 16, 4) == E_SHAPE
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    # The ctypes mirrors of the argument structs against the C compiler's
+    # layout of include/srwm.h: every field's offset, and the size.
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no C compiler")
+    structs = {"srwm_forward_args_t": _lib.ForwardArgs, "srwm_backward_args_t": _lib.BackwardArgs,
+               "srwm_deltanet_args_t": _lib.DeltanetArgs, "srwm_srdeltanet_args_t": _lib.SrdeltanetArgs,
+               "srwm_fast_args_t": _lib.FastArgs, "srwm_variant_info_t": _lib.VariantInfo,
+               "srwm_kernel_resources_t": _lib.KernelResources}
+    lines = ["#include <stddef.h>", "#include <stdio.h>", '#include "srwm.h"', "int main(void) {"]
+    for cname, cls in structs.items():
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f in cls._fields_:
+            lines.append(f'printf("{cname} {f[0]} %zu\\n", offsetof({cname}, {f[0]}));')
+    lines += ["return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    inc = Path(__file__).resolve().parents[1] / "include"
+    subprocess.check_call(["gcc", "-std=c11", "-I", str(inc), str(src), "-o", str(tmp_path / "layout")])
+    got = dict(line.rsplit(" ", 1) for line in
+               subprocess.check_output([str(tmp_path / "layout")], text=True).splitlines())
+    for cname, cls in structs.items():
+        assert int(got[f"{cname} size"]) == ctypes.sizeof(cls), cname
+        for f in cls._fields_:
+            assert int(got[f"{cname} {f[0]}"]) == getattr(cls, f[0]).offset, (cname, f[0])
 
 
 def call_fast(**kw):
@@ -348,6 +394,8 @@ def call_fast(**kw):
     (dict(F_T=FAKE_Y + 4), E_ARG),
     (dict(y=FAKE_Z + 32), E_ALIAS),
     (dict(F_T=FAKE_Y + 64), E_ALIAS),
+    (dict(t_stride=2), E_SHAPE),
+    (dict(t_stride=1000, y=FAKE_Z + 65536), E_ALIAS),
 ])
 def test_fast_forward_validation(kw, code):
     assert call_fast(**kw) == code

@@ -190,3 +190,84 @@ def test_split_entry_points_equal_the_composites():
     np.testing.assert_array_equal(zs.cpu().numpy(), z)
     np.testing.assert_array_equal(y3.cpu().numpy(), y)
     np.testing.assert_array_equal(F3.cpu().numpy(), FT)
+
+
+def _srdeltanet_t(w, x, W0, F0, **kw):
+    return _srwm().srdeltanet_forward(x, W0, w.d_key, w.d_v, F0=F0, apply_input_softmax=w.apply_input_softmax,
+                                      n_lr=w.n_lr, return_state=True, **kw)
+
+
+@pytest.mark.parametrize("w", SDN_CASES[1:], ids=lambda w: w.name)
+@pytest.mark.parametrize("chunk", [1, 7, 32, 69])
+def test_srdeltanet_overlap_same_bits(w, chunk):
+    # The projection of later steps on the caller's stream beside the fast
+    # matrix of earlier ones on a second stream, states carried in W_T and F_T
+    # between chunks: the one-stream call's bits, ragged last chunks included.
+    say(f"[fwp] srdeltanet overlapped, chunks of {chunk}: {w}")
+    x, W0 = td(gen_x(w)), td(gen_W0(w))
+    for F0 in (None, td(fast0(w, 21))):
+        ref = _srdeltanet_t(w, x, W0, F0, overlap=False)
+        got = _srdeltanet_t(w, x, W0, F0, chunk_steps=chunk)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("y", "W_T", "F_T", "z"), ref, got):
+            assert torch.equal(a, b), f"{name} differs, chunks of {chunk}"
+
+
+def test_srdeltanet_overlap_full_size_and_stream_order():
+    # The RL-sized workload chunked automatically, on a caller stream that is
+    # not torch's current one: work queued on that stream right after the call
+    # (a copy of y and F_T) sees the fast matrix's last chunk, which ran on the
+    # second stream.
+    w = FWP_WORKLOADS["srdeltanet_rl"]
+    say(f"[fwp] srdeltanet full size overlapped: {w}")
+    x, W0 = td(gen_x(w)), td(gen_W0(w))
+    ref = _srdeltanet_t(w, x, W0, None, overlap=False)
+    torch.cuda.synchronize()
+    s, aux = torch.cuda.Stream(dev()), torch.cuda.Stream(dev())
+    s.wait_stream(torch.cuda.current_stream(dev()))
+    with torch.cuda.stream(s):
+        got = _srdeltanet_t(w, x, W0, None, stream=s, aux_stream=aux)
+        y_copy, F_copy = got[0].clone(), got[2].clone()
+    torch.cuda.synchronize()
+    for name, a, b in zip(("y", "W_T", "F_T", "z"), ref, got):
+        assert torch.equal(a, b), f"{name} differs"
+    assert torch.equal(y_copy, ref[0]) and torch.equal(F_copy, ref[2])
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [16, 64])
+def test_forward_over_time_slices(io, d):
+    # Steps [0, t1) and then [t1, T) of one x and one y buffer (views along
+    # time, no copies), the second call starting from the first's W_T, give
+    # the bits of one call over all T steps.
+    srwm = _srwm()
+    from self_referential_weight_amd.workloads import Workload, gen_W0 as gen_W0_srwm, gen_x as gen_x_srwm
+    w = Workload(f"slices_d{d}", B=3, H=2, d_in=d, d_out=d, T=75, io_dtype=io, apply_input_softmax=d == 64,
+                 return_state=True, w0_std=d ** -0.5)
+    say(f"[fwp] forward over time slices: {w}")
+    dt = torch.bfloat16 if io == "bf16" else torch.float32
+    x = torch.from_numpy(gen_x_srwm(w)).to(dev()).to(dt)
+    W0 = td(gen_W0_srwm(w))
+    y_ref, W_ref = srwm.forward(x, W0, apply_input_softmax=w.apply_input_softmax, return_state=True)
+    y = torch.full_like(y_ref, float("nan"))
+    for t1 in (1, 30, 74):
+        _, Wa = srwm.forward(x[:, :t1], W0, apply_input_softmax=w.apply_input_softmax, y=y[:, :t1],
+                             return_state=True)
+        _, Wb = srwm.forward(x[:, t1:], Wa, apply_input_softmax=w.apply_input_softmax, y=y[:, t1:],
+                             return_state=True)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref) and torch.equal(Wb, W_ref), f"split at {t1}"
+    with pytest.raises(ValueError):
+        srwm.forward(x[:, 5:9], W0)  # a time slice needs its y slice
+
+
+def test_fast_forward_over_time_slices():
+    srwm = _srwm()
+    w = SDN_CASES[2]
+    z = torch.randn((w.B, w.T, w.H, w.P), generator=torch.Generator().manual_seed(5)).to(dev()) * 0.5
+    y_ref, F_ref = srwm.fast_forward(z, w.d_key, w.d_v, return_state=True)
+    y = torch.full_like(y_ref, float("nan"))
+    _, Fa = srwm.fast_forward(z[:, :33], w.d_key, w.d_v, y=y[:, :33], return_state=True)
+    _, Fb = srwm.fast_forward(z[:, 33:], w.d_key, w.d_v, F0=Fa, y=y[:, 33:], return_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref) and torch.equal(Fb, F_ref)
