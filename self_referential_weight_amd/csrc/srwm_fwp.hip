@@ -146,9 +146,12 @@ __global__ __launch_bounds__(256) void srwm_proj_gemm_kernel(const float* __rest
 // are formed (wave w takes steps w, w+NW, ... of the chunk, from registers
 // loaded a chunk earlier) into one half of a double-buffered LDS area while
 // the matrix work of chunk c runs from the other half; one workgroup barrier
-// per chunk.
-template <int D_KEY, int D_V, int NW, int P, int S>
-__global__ __launch_bounds__(NW * 64) void srwm_fast_kernel(const float* __restrict__ Z,
+// per chunk.  With NPW > 0 the preparation is left to NPW extra waves, which
+// form chunk c+1 while the NW row-holding waves work through chunk c (the
+// recurrence is bound by its per-step dependency chain, so the preparation
+// fills issue slots the recurrence leaves idle).
+template <int D_KEY, int D_V, int NW, int P, int S, int NPW = 0>
+__global__ __launch_bounds__((NW + NPW) * 64) void srwm_fast_kernel(const float* __restrict__ Z,
                                                             const float* __restrict__ F0,
                                                             float* __restrict__ y, float* __restrict__ FT,
                                                             int T, int t_stride, int H)
@@ -160,17 +163,25 @@ __global__ __launch_bounds__(NW * 64) void srwm_fast_kernel(const float* __restr
     constexpr int R = (RW + G - 1) / G;      // rows per lane
     constexpr int EZ = (PR + kWave - 1) / kWave;
     constexpr int V0 = D_KEY, Q0 = D_KEY + D_V, BETA = PR - 1;
-    constexpr int SW = S / NW;               // steps each wave prepares per chunk
+    constexpr int NPREP = NPW > 0 ? NPW : NW;  // waves that prepare a chunk
+    constexpr int SW = S / NPREP;              // steps each of them prepares per chunk
     // prepared step: kh [0, D_KEY), qh [D_KEY, 2 D_KEY), v [2 D_KEY, +D_V), g
-    constexpr int KQ = 2 * D_KEY, GO = KQ + D_V, KP = (GO + 1 + 3) & ~3;
-    static_assert(D_KEY % P == 0 && D_V % NW == 0 && S % NW == 0, "shapes");
+    constexpr int KQ = 2 * D_KEY, GO = KQ + D_V, KP = (GO + 2 + 3) & ~3;
+    // <kh, qh> of a step is formed once, by the wave that prepares the step,
+    // when lane j holds key column j and query column j of the raw projection
+    // (stored at GO + 1); otherwise every wave forms it per step.
+    constexpr bool KQ_PREP = D_KEY <= kWave && Q0 % kWave == 0;
+    static_assert(D_KEY % P == 0 && D_V % NW == 0 && S % NPREP == 0, "shapes");
     static_assert(D_KEY % 4 == 0 && D_V % 4 == 0, "16-byte sections");
 
     __shared__ __attribute__((aligned(16))) float s_p[2][S][KP];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = NW == 1 ? 0 : tid / kWave;
+    const int wave = NW + NPW == 1 ? 0 : tid / kWave;
+    const bool rec = NPW == 0 || wave < NW;      // holds rows of F
+    const bool preps = NPW == 0 || wave >= NW;   // prepares steps
+    const int pw = NPW > 0 ? wave - NW : wave;   // index among the preparing waves
     const int p = lane % P;
     const int rg = lane / P;
     const int row0 = wave * RW;
@@ -186,7 +197,7 @@ __global__ __launch_bounds__(NW * 64) void srwm_fast_kernel(const float* __restr
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int lr = rg + G * r;
-        if (F0 != nullptr && lr < RW) {
+        if (F0 != nullptr && lr < RW && rec) {
             load_f32<L>(F0 + ((int64_t)unit * D_V + row0 + lr) * D_KEY + p * L, F[r]);
         } else {
 #pragma unroll
@@ -194,12 +205,12 @@ __global__ __launch_bounds__(NW * 64) void srwm_fast_kernel(const float* __restr
         }
     }
 
-    // This wave's share of a chunk's raw projections: steps c0 + wave + NW*j.
+    // This wave's share of a chunk's raw projections: steps c0 + pw + NPREP*j.
     float zr[SW][EZ];
     auto load_chunk = [&](int c0) {
 #pragma unroll
         for (int j = 0; j < SW; ++j) {
-            const int t = c0 + wave + NW * j;
+            const int t = c0 + pw + NPREP * j;
 #pragma unroll
             for (int i = 0; i < EZ; ++i) {
                 const int e = lane + kWave * i;
@@ -211,7 +222,7 @@ __global__ __launch_bounds__(NW * 64) void srwm_fast_kernel(const float* __restr
     auto prep_chunk = [&](int buf) {
 #pragma unroll
         for (int j = 0; j < SW; ++j) {
-            const int s = wave + NW * j;
+            const int s = pw + NPREP * j;
             float mk = -INFINITY, mq = -INFINITY;
 #pragma unroll
             for (int i = 0; i < EZ; ++i) {
@@ -232,6 +243,10 @@ __global__ __launch_bounds__(NW * 64) void srwm_fast_kernel(const float* __restr
             }
             wave_sum2(sk, sq);
             const float ik = rcp_f32(sk), iq = rcp_f32(sq);
+            if constexpr (KQ_PREP) {
+                const float kq = wave_total(lane < D_KEY ? ex[0] * ex[Q0 / kWave] : 0.f) * (ik * iq);
+                if (lane == 0) s_p[buf][s][GO + 1] = kq;
+            }
 #pragma unroll
             for (int i = 0; i < EZ; ++i) {
                 const int e = lane + kWave * i;
@@ -244,18 +259,20 @@ __global__ __launch_bounds__(NW * 64) void srwm_fast_kernel(const float* __restr
     };
 
     if (T > 0) {
-        load_chunk(0);
-        prep_chunk(0);
-        if (T > S) load_chunk(S);
+        if (preps) {
+            load_chunk(0);
+            prep_chunk(0);
+            if (T > S) load_chunk(S);
+        }
         __syncthreads();
     }
     for (int c0 = 0, chunk = 0; c0 < T; c0 += S, ++chunk) {
         const int buf = chunk & 1;
-        if (c0 + S < T) {
+        if (preps && c0 + S < T) {
             prep_chunk(buf ^ 1);
             if (c0 + 2 * S < T) load_chunk(c0 + 2 * S);
         }
-        const int n = (T - c0) < S ? (T - c0) : S;
+        const int n = !rec ? 0 : (T - c0) < S ? (T - c0) : S;
         for (int s = 0; s < n; ++s) {
             const float* __restrict__ ps = s_p[buf][s];
             float kh[L], qh[L];
@@ -263,9 +280,13 @@ __global__ __launch_bounds__(NW * 64) void srwm_fast_kernel(const float* __restr
             load_f32<L>(ps + D_KEY + p * L, qh);
             const float g = ps[GO];
             float kq = 0.f;
+            if constexpr (KQ_PREP) {
+                kq = ps[GO + 1];
+            } else {
 #pragma unroll
-            for (int c = 0; c < L; ++c) kq = fmaf(kh[c], qh[c], kq);
-            kq = group_sum<P>(kq);
+                for (int c = 0; c < L; ++c) kq = fmaf(kh[c], qh[c], kq);
+                kq = group_sum<P>(kq);
+            }
             const int64_t yt = y0 + (int64_t)(c0 + s) * y_step + row0;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
@@ -288,7 +309,7 @@ __global__ __launch_bounds__(NW * 64) void srwm_fast_kernel(const float* __restr
         __syncthreads();
     }
 
-    if (FT != nullptr) {
+    if (FT != nullptr && rec) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int lr = rg + G * r;
@@ -301,15 +322,15 @@ __global__ __launch_bounds__(NW * 64) void srwm_fast_kernel(const float* __restr
 // Variants: (d_key, d_v, lanes per row).
 using FastFn = void (*)(const float*, const float*, float*, float*, int, int, int);
 struct FastVariant {
-    int d_key, d_v, nw;
+    int d_key, d_v, nw, npw;  // row-holding waves, preparing waves
     FastFn fn;
 };
-// (d_key, d_v, waves per unit, lanes per row, steps per chunk)
+// (d_key, d_v, waves per unit, lanes per row, steps per chunk, preparing waves)
 const FastVariant kFastVariants[] = {
-    {8, 8, 1, &srwm_fast_kernel<8, 8, 1, 8, 16>},
-    {16, 16, 1, &srwm_fast_kernel<16, 16, 1, 4, 16>},
-    {64, 64, 4, &srwm_fast_kernel<64, 64, 4, 4, 16>},
-    {64, 64, 8, &srwm_fast_kernel<64, 64, 8, 8, 16>},
+    {8, 8, 1, 0, &srwm_fast_kernel<8, 8, 1, 8, 16>},
+    {16, 16, 1, 0, &srwm_fast_kernel<16, 16, 1, 4, 16>},
+    {64, 64, 4, 0, &srwm_fast_kernel<64, 64, 4, 4, 16>},
+    {64, 64, 8, 4, &srwm_fast_kernel<64, 64, 8, 8, 16, 4>},
 };
 constexpr int kNumFastVariants = sizeof(kFastVariants) / sizeof(kFastVariants[0]);
 
@@ -361,7 +382,7 @@ int launch_fast(int vi, const float* z, const float* F0, float* y, float* FT, in
     int Ti = static_cast<int>(T), Si = static_cast<int>(t_stride > 0 ? t_stride : T), Hi = static_cast<int>(H);
     void* args[] = {const_cast<float**>(&z), const_cast<float**>(&F0), &y, &FT, &Ti, &Si, &Hi};
     const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(kFastVariants[vi].fn),
-                                           dim3(static_cast<unsigned>(units)), dim3(kFastVariants[vi].nw * kWave), args, 0,
+                                           dim3(static_cast<unsigned>(units)), dim3((kFastVariants[vi].nw + kFastVariants[vi].npw) * kWave), args, 0,
                                            static_cast<hipStream_t>(stream));
     return err == hipSuccess ? SRWM_OK : SRWM_ERR_HIP;
 }
