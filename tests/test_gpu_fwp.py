@@ -271,3 +271,21 @@ def test_fast_forward_over_time_slices():
     _, Fb = srwm.fast_forward(z[:, 33:], w.d_key, w.d_v, F0=Fa, y=y[:, 33:], return_state=True)
     torch.cuda.synchronize()
     assert torch.equal(y, y_ref) and torch.equal(Fb, F_ref)
+
+
+@pytest.mark.parametrize("B", [260])
+def test_fast_kernel_for_many_units(B):
+    # Above 512 units the fast matrix runs on 4 waves per unit (two rows per
+    # lane, every wave preparing its share of a chunk) instead of 8 row-holding
+    # waves beside 4 preparing ones: the same results, checked against the
+    # oracle on sampled sequences, with a ragged last chunk (T = 37).
+    w = FwpWorkload("dn_units", "deltanet", B=B, H=2, d_in=16, d_key=64, d_v=64, T=37, apply_input_softmax=False,
+                    w0_std=32 ** -0.5, seed=7)
+    say(f"[fwp] fast kernel, {w.B * w.H} units: {w}")
+    x, Wslow = gen_x(w), gen_W_slow(w)
+    F0 = fast0(w, 17)
+    y, FT, _ = run_deltanet(w, x, Wslow, F0)
+    for b in (0, 131, B - 1):
+        y_ref, FT_ref = oracle.deltanet_forward(x[b:b + 1], Wslow, w.d_key, w.d_v, F0=F0[b:b + 1])
+        check_y(y[b:b + 1], y_ref, "f32", f"{w.name} b={b}")
+        check_state(FT[b:b + 1], FT_ref, f"{w.name} b={b}")
