@@ -378,13 +378,17 @@ def srdeltanet_forward(x, W0, d_key: int, d_v: int, F0=None, apply_input_softmax
     SRWM's final state [B, H, m, d_in]) or None, F_T or None, z).
     overlap: run the projection of later steps beside the fast matrix of
     earlier ones on a second stream (``aux_stream``, default the binding's
-    own), in chunks of ``chunk_steps`` (0: the library's choice).  Same
-    results either way; the states of both halves are then carried in
-    W_T and F_T, allocated here when not returned.
+    own), in chunks of ``chunk_steps`` (0: the library's choice; T or more:
+    no overlap).  Same results either way; the states of both halves are
+    then carried in W_T and F_T, allocated here when not returned.
     """
     import torch
 
     lib = _lib.load()
+    if overlap:
+        B_, T_, H_, d_in_ = x.shape
+        C = chunk_steps or lib.srwm_srdeltanet_chunk_steps(B_, T_, H_, d_in_, d_key, d_v, n_lr)
+        overlap = 0 < C < T_  # else one stream (errors are reported by the call below)
     B, T, H, d_in, P, z, y, F_T = _fwp_common(x, F0, d_key, d_v, return_state or overlap, z, y)
     m = P + 2 * d_in + n_lr
     if (tuple(W0.shape) != (H, m, d_in) or W0.dtype != torch.float32 or W0.device != x.device
