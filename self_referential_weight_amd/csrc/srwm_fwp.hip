@@ -303,7 +303,11 @@ __global__ __launch_bounds__((NW + NPW) * 64) void srwm_fast_kernel(const float*
                 const float a = g * (v - s1);
 #pragma unroll
                 for (int c = 0; c < L; ++c) F[r][c] = fmaf(a, kh[c], F[r][c]);
-                if (p == 0 && lr < RW) y[yt + lr] = fmaf(a, kq, s2);
+                // y formed in every lane before the store's branch: otherwise the
+                // last DPP level of s2 sinks into the branch as a move and an add
+                float yv = fmaf(a, kq, s2);
+                asm volatile("" : "+v"(yv));
+                if (p == 0 && lr < RW) y[yt + lr] = yv;
             }
         }
         __syncthreads();
