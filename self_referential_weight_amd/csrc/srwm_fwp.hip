@@ -211,10 +211,12 @@ __global__ __launch_bounds__((NW + NPW) * 64) void srwm_fast_kernel(const float*
 #pragma unroll
         for (int j = 0; j < SW; ++j) {
             const int t = c0 + pw + NPREP * j;
+            // one row address per step; its EZ pieces are constant offsets from it
+            const float* __restrict__ zrow = Z + z0 + (int64_t)t * z_step + lane;
 #pragma unroll
             for (int i = 0; i < EZ; ++i) {
                 const int e = lane + kWave * i;
-                zr[j][i] = (t < T && e < PR) ? Z[z0 + (int64_t)t * z_step + e] : 0.f;
+                zr[j][i] = (t < T && e < PR) ? zrow[kWave * i] : 0.f;
             }
         }
     };
