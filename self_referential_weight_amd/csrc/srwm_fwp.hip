@@ -335,7 +335,7 @@ struct FastVariant {
 const FastVariant kFastVariants[] = {
     {8, 8, 1, 0, &srwm_fast_kernel<8, 8, 1, 8, 16>},
     {16, 16, 1, 0, &srwm_fast_kernel<16, 16, 1, 4, 16>},
-    {64, 64, 4, 0, &srwm_fast_kernel<64, 64, 4, 4, 16>},
+    {64, 64, 4, 4, &srwm_fast_kernel<64, 64, 4, 4, 16, 4>},
     {64, 64, 8, 4, &srwm_fast_kernel<64, 64, 8, 8, 16, 4>},
 };
 constexpr int kNumFastVariants = sizeof(kFastVariants) / sizeof(kFastVariants[0]);

@@ -275,10 +275,10 @@ def test_fast_forward_over_time_slices():
 
 @pytest.mark.parametrize("B", [260])
 def test_fast_kernel_for_many_units(B):
-    # Above 512 units the fast matrix runs on 4 waves per unit (two rows per
-    # lane, every wave preparing its share of a chunk) instead of 8 row-holding
-    # waves beside 4 preparing ones: the same results, checked against the
-    # oracle on sampled sequences, with a ragged last chunk (T = 37).
+    # Above 512 units the fast matrix runs on 4 row-holding waves per unit (two
+    # rows per lane) beside 4 preparing ones instead of 8 beside 4: the same
+    # results, checked against the oracle on sampled sequences, with a ragged
+    # last chunk (T = 37).
     w = FwpWorkload("dn_units", "deltanet", B=B, H=2, d_in=16, d_key=64, d_v=64, T=37, apply_input_softmax=False,
                     w0_std=32 ** -0.5, seed=7)
     say(f"[fwp] fast kernel, {w.B * w.H} units: {w}")
