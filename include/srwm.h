@@ -370,7 +370,9 @@ int srwm_fast_forward(const srwm_fast_args_t* args);
  * events, makes aux_stream wait for `stream`'s earlier work and makes
  * `stream` wait for all of it, so work queued on `stream` afterwards sees
  * every output.  Overlapping calls that share an aux_stream are serialised
- * on it, not wrong.
+ * on it, not wrong.  The overlapped form has not been tested under HIP graph
+ * capture; a caller that captures `stream` should pass aux_stream = NULL
+ * (or chunk_steps >= T), which keeps every launch on `stream`.
  */
 typedef struct srwm_srdeltanet_args {
     const float* x;
