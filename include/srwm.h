@@ -370,9 +370,10 @@ int srwm_fast_forward(const srwm_fast_args_t* args);
  * events, makes aux_stream wait for `stream`'s earlier work and makes
  * `stream` wait for all of it, so work queued on `stream` afterwards sees
  * every output.  Overlapping calls that share an aux_stream are serialised
- * on it, not wrong.  The overlapped form has not been tested under HIP graph
- * capture; a caller that captures `stream` should pass aux_stream = NULL
- * (or chunk_steps >= T), which keeps every launch on `stream`.
+ * on it, not wrong.  Under HIP graph capture of `stream`, aux_stream joins
+ * the capture through the first event and is joined back by the last, so
+ * the captured graph holds both halves (aux_stream must not be capturing
+ * anything else).
  */
 typedef struct srwm_srdeltanet_args {
     const float* x;

@@ -83,3 +83,23 @@ def test_deltanet_in_graph():
     def capture():
         return srwm.deltanet_forward(x, Ws, f.d_key, f.d_v, return_state=True)
     replay_and_check(capture, (y_e, FT_e, z_e))
+
+
+def test_srdeltanet_overlapped_in_graph():
+    # The two-stream chunk schedule captured from the caller's stream: the
+    # second stream joins the capture through the schedule's events and is
+    # joined back at its end, so the graph replays to the one-stream result.
+    srwm = _srwm()
+    w = FWP_WORKLOADS["srdeltanet_small"].with_(d_in=64, d_key=64, d_v=64, T=100, B=2)
+    x, W0 = td(gen_x(w)), td(gen_W0(w))
+    kw = dict(apply_input_softmax=w.apply_input_softmax, n_lr=w.n_lr, return_state=True)
+    y_e, WT_e, FT_e, z_e = srwm.srdeltanet_forward(x, W0, w.d_key, w.d_v, overlap=False, **kw)
+    torch.cuda.synchronize()
+    aux = torch.cuda.Stream()
+    z, y = torch.empty_like(z_e), torch.empty_like(y_e)
+
+    def capture():
+        y_, WT, FT, z_ = srwm.srdeltanet_forward(x, W0, w.d_key, w.d_v, z=z, y=y, aux_stream=aux, chunk_steps=23,
+                                                 **kw)
+        return (y_, WT, FT, z_)
+    replay_and_check(capture, (y_e, WT_e, FT_e, z_e))
