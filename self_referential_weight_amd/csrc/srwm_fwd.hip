@@ -1,4 +1,5 @@
-// srwm_fwd.hip -- gfx950 kernels and C ABI of libsrwm.
+// srwm_fwd.hip -- C ABI of libsrwm's forward pass (the kernels are in
+// srwm_fwd_kernels.h, instantiated by the variant table's parts).
 //
 // Forward recurrence of the multi-head, 4-learning-rate self-referential
 // weight matrix ("Metalearning Continual Learning Algorithms -- part 2/5",
@@ -36,144 +37,34 @@
 
 #include "srwm.h"
 #include "srwm_device.h"
-#include "srwm_fwd_kernels.h"
+#include "srwm_fwd_table.h"
 
 namespace {
 
 using namespace srwm;
 
 // ----------------------------------------------------------------------------
-// Variant table.
-using KernelFn = void (*)(const void*, const float*, void*, float*, float*, float*, int, int, int, int, int, int);
+// The variant table: its parts (each instantiated in its own translation
+// unit) indexed as one table, in this order.
+VariantPart (*const kFwdParts[])() = {fwd_variants_small, fwd_variants_d64, fwd_variants_misc, fwd_variants_tape};
 
-struct Variant {
-    int d_in, d_out, io, nw, p, wpe, nlr, fused, reset, tape, is_auto;
-    KernelFn fn;
+struct Table {
+    const Variant* v[512];
+    int n = 0;
+    Table()
+    {
+        for (auto part : kFwdParts) {
+            const VariantPart p = part();
+            for (int i = 0; i < p.n && n < 512; ++i) v[n++] = &p.v[i];
+        }
+    }
 };
 
-// SCHED: 0 phased, 1 phased with the reset ablation, 2 fused, 3 phased
-// writing the backward tape, 4 phased with the reset ablation writing the
-// backward tape (and the windows' end states).
-template <int D_IN, int D_OUT, int NW, int P, int WPE, int NLR, int SCHED, bool BF16>
-constexpr Variant make_variant(int is_auto)
+const Table& table()
 {
-    constexpr int io = BF16 ? SRWM_IO_BF16 : SRWM_IO_F32;
-    if constexpr (SCHED == 2)
-        return Variant{D_IN, D_OUT, io, NW, P, WPE, NLR, 1, 0, 0, is_auto,
-                       &srwm_fwd_fused_kernel<D_IN, D_OUT, NW, P, WPE, NLR, BF16>};
-    else
-        return Variant{D_IN, D_OUT, io, NW, P, WPE, NLR, 0, SCHED == 1 || SCHED == 4, SCHED == 3 || SCHED == 4,
-                       is_auto,
-                       &srwm_fwd_kernel<D_IN, D_OUT, NW, P, WPE, NLR, SCHED == 1 || SCHED == 4,
-                                        SCHED == 3 || SCHED == 4, BF16>};
+    static const Table t;
+    return t;
 }
-
-// Both I/O dtypes of one geometry: (d_in, d_out, waves per unit, lanes per
-// row, waves per SIMD the registers allow, learning rates, eligible for the
-// automatic choice).  _RESET variants also implement the reset ablation.
-#define SRWM_BOTH_IO(DI, DO, NW, P, WPE, NLR, AUTO)                   \
-    make_variant<DI, DO, NW, P, WPE, NLR, 0, false>(AUTO),             \
-        make_variant<DI, DO, NW, P, WPE, NLR, 0, true>(AUTO)
-#define SRWM_BOTH_IO_RESET(DI, DO, NW, P, WPE, NLR, AUTO)             \
-    make_variant<DI, DO, NW, P, WPE, NLR, 1, false>(AUTO),             \
-        make_variant<DI, DO, NW, P, WPE, NLR, 1, true>(AUTO)
-#define SRWM_BOTH_IO_FUSED(DI, DO, NW, P, WPE, NLR, AUTO)             \
-    make_variant<DI, DO, NW, P, WPE, NLR, 2, false>(AUTO),             \
-        make_variant<DI, DO, NW, P, WPE, NLR, 2, true>(AUTO)
-#define SRWM_BOTH_IO_TAPE(DI, DO, NW, P, WPE, NLR, AUTO)              \
-    make_variant<DI, DO, NW, P, WPE, NLR, 3, false>(AUTO),             \
-        make_variant<DI, DO, NW, P, WPE, NLR, 3, true>(AUTO)
-#define SRWM_BOTH_IO_TAPE_RESET(DI, DO, NW, P, WPE, NLR, AUTO)        \
-    make_variant<DI, DO, NW, P, WPE, NLR, 4, false>(AUTO),             \
-        make_variant<DI, DO, NW, P, WPE, NLR, 4, true>(AUTO)
-
-const Variant kVariants[] = {
-    // small shapes (tests, latency-bound workloads)
-    SRWM_BOTH_IO_RESET(2, 2, 1, 2, 1, 4, 1),
-    SRWM_BOTH_IO_RESET(3, 5, 1, 1, 1, 4, 1),
-    SRWM_BOTH_IO_RESET(8, 8, 1, 8, 1, 4, 1),
-    SRWM_BOTH_IO_RESET(8, 16, 1, 8, 1, 4, 1),
-    SRWM_BOTH_IO_RESET(16, 8, 1, 8, 1, 4, 1),
-    SRWM_BOTH_IO_RESET(16, 16, 1, 4, 1, 4, 1),
-    SRWM_BOTH_IO_FUSED(16, 16, 2, 4, 1, 4, 0),
-    SRWM_BOTH_IO_RESET(32, 32, 1, 4, 1, 4, 1),
-    // d = 64: one wave per unit for many units, up to eight for few
-    SRWM_BOTH_IO(64, 64, 1, 2, 2, 4, 1),
-    SRWM_BOTH_IO(64, 64, 2, 8, 2, 4, 0),
-    SRWM_BOTH_IO_FUSED(64, 64, 4, 8, 1, 4, 0),
-    SRWM_BOTH_IO_FUSED(64, 64, 8, 8, 1, 4, 0),
-    SRWM_BOTH_IO(64, 64, 1, 4, 2, 4, 0),
-    SRWM_BOTH_IO(64, 64, 1, 4, 1, 4, 0),
-    SRWM_BOTH_IO(64, 64, 4, 8, 1, 4, 0),
-    SRWM_BOTH_IO(64, 64, 4, 16, 1, 4, 0),
-    SRWM_BOTH_IO(64, 64, 4, 4, 1, 4, 1),
-    SRWM_BOTH_IO(64, 64, 8, 8, 1, 4, 1),
-    SRWM_BOTH_IO_FUSED(64, 64, 4, 4, 1, 4, 0),
-    SRWM_BOTH_IO_RESET(64, 64, 2, 8, 2, 4, 1),
-    // d = 128
-    SRWM_BOTH_IO(128, 128, 8, 4, 1, 4, 1),
-    SRWM_BOTH_IO(128, 128, 8, 8, 1, 4, 0),
-    SRWM_BOTH_IO_FUSED(128, 128, 8, 8, 1, 4, 0),
-    SRWM_BOTH_IO_FUSED(128, 128, 8, 16, 1, 4, 0),
-    SRWM_BOTH_IO_FUSED(128, 128, 16, 16, 1, 4, 0),
-    SRWM_BOTH_IO(128, 128, 8, 16, 1, 4, 0),
-    SRWM_BOTH_IO(128, 128, 16, 16, 1, 4, 0),
-    SRWM_BOTH_IO(128, 128, 16, 8, 1, 4, 0),
-    SRWM_BOTH_IO_RESET(128, 128, 8, 4, 1, 4, 1),
-    // one learning rate
-    SRWM_BOTH_IO_RESET(2, 2, 1, 2, 1, 1, 1),
-    SRWM_BOTH_IO_RESET(8, 8, 1, 8, 1, 1, 1),
-    SRWM_BOTH_IO_RESET(16, 16, 1, 4, 1, 1, 1),
-    SRWM_BOTH_IO(64, 64, 1, 2, 2, 1, 1),
-    SRWM_BOTH_IO_RESET(64, 64, 2, 8, 2, 1, 1),
-    SRWM_BOTH_IO(64, 64, 4, 4, 1, 1, 1),
-    SRWM_BOTH_IO(64, 64, 8, 8, 1, 1, 1),
-    SRWM_BOTH_IO_FUSED(64, 64, 8, 8, 1, 1, 0),
-    SRWM_BOTH_IO(128, 128, 8, 4, 1, 1, 1),
-    SRWM_BOTH_IO_FUSED(128, 128, 8, 8, 1, 1, 0),
-    SRWM_BOTH_IO_RESET(128, 128, 8, 4, 1, 1, 1),
-    // SR-DeltaNet's projection: d_out = d_v + 2*d_key + 1 (float32 I/O)
-    make_variant<8, 25, 1, 8, 1, 4, 1, false>(1),
-    make_variant<8, 25, 1, 8, 1, 1, 1, false>(1),
-    make_variant<16, 49, 1, 4, 1, 4, 1, false>(1),
-    make_variant<16, 49, 1, 4, 1, 1, 1, false>(1),
-    make_variant<64, 193, 4, 4, 1, 4, 1, false>(1),
-    make_variant<64, 193, 4, 4, 1, 1, 1, false>(1),
-    make_variant<64, 193, 8, 4, 1, 4, 0, false>(1),
-    make_variant<64, 193, 8, 4, 1, 1, 0, false>(1),
-    make_variant<64, 193, 8, 8, 1, 4, 0, false>(0),
-    make_variant<64, 193, 8, 8, 1, 4, 2, false>(0),
-    // forward passes that also write the backward tape
-    SRWM_BOTH_IO_TAPE(8, 8, 1, 8, 1, 4, 1),
-    SRWM_BOTH_IO_TAPE(16, 16, 1, 4, 1, 4, 1),
-    SRWM_BOTH_IO_TAPE(64, 64, 1, 2, 2, 4, 1),
-    SRWM_BOTH_IO_TAPE(64, 64, 2, 8, 2, 4, 0),
-    SRWM_BOTH_IO_TAPE(64, 64, 4, 8, 1, 4, 0),
-    SRWM_BOTH_IO_TAPE(64, 64, 4, 4, 1, 4, 1),
-    SRWM_BOTH_IO_TAPE(64, 64, 8, 8, 1, 4, 1),
-    SRWM_BOTH_IO_TAPE(8, 8, 1, 8, 1, 1, 1),
-    SRWM_BOTH_IO_TAPE(16, 16, 1, 4, 1, 1, 1),
-    SRWM_BOTH_IO_TAPE(64, 64, 1, 2, 2, 1, 1),
-    SRWM_BOTH_IO_TAPE(64, 64, 2, 8, 2, 1, 0),
-    SRWM_BOTH_IO_TAPE(64, 64, 4, 8, 1, 1, 0),
-    SRWM_BOTH_IO_TAPE(64, 64, 4, 4, 1, 1, 1),
-    SRWM_BOTH_IO_TAPE(64, 64, 8, 8, 1, 1, 1),
-    SRWM_BOTH_IO_TAPE(128, 128, 8, 4, 1, 4, 1),
-    SRWM_BOTH_IO_TAPE(128, 128, 8, 4, 1, 1, 1),
-    // ... with the reset ablation (they also record each window's end state)
-    SRWM_BOTH_IO_TAPE_RESET(8, 8, 1, 8, 1, 4, 1),
-    SRWM_BOTH_IO_TAPE_RESET(16, 16, 1, 4, 1, 4, 1),
-    SRWM_BOTH_IO_TAPE_RESET(64, 64, 1, 4, 2, 4, 1),
-    SRWM_BOTH_IO_TAPE_RESET(64, 64, 4, 4, 1, 4, 1),
-    SRWM_BOTH_IO_TAPE_RESET(64, 64, 8, 8, 1, 4, 1),
-    SRWM_BOTH_IO_TAPE_RESET(8, 8, 1, 8, 1, 1, 1),
-    SRWM_BOTH_IO_TAPE_RESET(16, 16, 1, 4, 1, 1, 1),
-    SRWM_BOTH_IO_TAPE_RESET(64, 64, 1, 4, 2, 1, 1),
-    SRWM_BOTH_IO_TAPE_RESET(64, 64, 4, 4, 1, 1, 1),
-    SRWM_BOTH_IO_TAPE_RESET(64, 64, 8, 8, 1, 1, 1),
-};
-
-constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 // Two waves per SIMD of the chip (256 CUs x 4 SIMDs x 2): enough waves to
 // hide one wave's latency behind another's arithmetic.
@@ -194,23 +85,23 @@ int find_variant(int64_t d_in, int64_t d_out, int io, int nlr, bool reset, bool 
                  int64_t units)
 {
     if (requested >= 0) {
-        if (requested >= kNumVariants) return -1;
-        return variant_matches(kVariants[requested], d_in, d_out, io, nlr, reset, tape) ? requested : -1;
+        if (requested >= table().n) return -1;
+        return variant_matches(*table().v[requested], d_in, d_out, io, nlr, reset, tape) ? requested : -1;
     }
     for (int pass = 0; pass < 2; ++pass) {
         int best_fill = -1, best_any = -1;
-        for (int i = 0; i < kNumVariants; ++i) {
-            const Variant& v = kVariants[i];
+        for (int i = 0; i < table().n; ++i) {
+            const Variant& v = *table().v[i];
             if (!variant_matches(v, d_in, d_out, io, nlr, reset, tape) || !v.is_auto) continue;
             if (pass == 0 && (v.reset != 0) != reset) continue;
-            if (units * v.nw >= kChipWaveSlots && (best_fill < 0 || v.nw < kVariants[best_fill].nw)) best_fill = i;
-            if (best_any < 0 || v.nw > kVariants[best_any].nw) best_any = i;
+            if (units * v.nw >= kChipWaveSlots && (best_fill < 0 || v.nw < table().v[best_fill]->nw)) best_fill = i;
+            if (best_any < 0 || v.nw > table().v[best_any]->nw) best_any = i;
         }
         if (best_fill >= 0 || best_any >= 0) return best_fill >= 0 ? best_fill : best_any;
     }
     // a shape whose only variants are not marked eligible (or all fused, with reset)
-    for (int i = 0; i < kNumVariants; ++i)
-        if (variant_matches(kVariants[i], d_in, d_out, io, nlr, reset, tape)) return i;
+    for (int i = 0; i < table().n; ++i)
+        if (variant_matches(*table().v[i], d_in, d_out, io, nlr, reset, tape)) return i;
     return -1;
 }
 
@@ -266,7 +157,7 @@ int forward_check(const srwm_forward_args_t* a, FwdPlan* plan)
          reinterpret_cast<uintptr_t>(tape) | reinterpret_cast<uintptr_t>(wstates)) & 15u)
         return SRWM_ERR_ARG;
     plan->vi = vi;
-    plan->waves = kVariants[vi].nw;
+    plan->waves = table().v[vi]->nw;
     plan->units = units;
     plan->wstates = wstates;
     plan->run = false;
@@ -286,7 +177,7 @@ int forward_check(const srwm_forward_args_t* a, FwdPlan* plan)
 
 int forward_launch(const FwdPlan& plan, const srwm_forward_args_t* a)
 {
-    const Variant& v = kVariants[plan.vi];
+    const Variant& v = *table().v[plan.vi];
     const void* x = a->x;
     const float* W0 = a->W0;
     void* y = a->y;
@@ -374,13 +265,13 @@ int64_t srwm_tape_row(int64_t d_in, int64_t d_out, int n_lr)
     return tape_row(d_in, d_out, n_lr);
 }
 
-int srwm_variant_count(void) { return kNumVariants; }
+int srwm_variant_count(void) { return table().n; }
 
 int srwm_variant_info(int i, srwm_variant_info_t* info)
 {
-    if (i < 0 || i >= kNumVariants) return SRWM_ERR_ARG;
+    if (i < 0 || i >= table().n) return SRWM_ERR_ARG;
     if (info == nullptr) return SRWM_ERR_NULL;
-    const Variant& v = kVariants[i];
+    const Variant& v = *table().v[i];
     info->d_in = v.d_in;
     info->d_out = v.d_out;
     info->io_dtype = v.io;
@@ -397,9 +288,9 @@ int srwm_variant_info(int i, srwm_variant_info_t* info)
 
 int srwm_variant_resources(int i, srwm_kernel_resources_t* out)
 {
-    if (i < 0 || i >= kNumVariants) return SRWM_ERR_ARG;
+    if (i < 0 || i >= table().n) return SRWM_ERR_ARG;
     if (out == nullptr) return SRWM_ERR_NULL;
-    return kernel_resources(reinterpret_cast<const void*>(kVariants[i].fn), kVariants[i].nw * kWave, out);
+    return kernel_resources(reinterpret_cast<const void*>(table().v[i]->fn), table().v[i]->nw * kWave, out);
 }
 
 int srwm_select_variant(int64_t d_in, int64_t d_out, int io_dtype, int n_lr, int64_t reset_interval,
