@@ -9,7 +9,11 @@ in HBM before timing starts.
 Prints ONE JSON line with the headline metric (head-steps/s = B*H*T/s), the
 roofline of the kernel (algorithmic FP32 FLOP per launch / average launch time
 from HIP events on the launch stream, against the FP32 vector peak) and the
-float64 CPU oracle timed on a bounded sample of the same workload.
+float64 CPU oracle timed on a bounded sample of the same workload.  After the
+timed headline steps, the `configs` block times every SRWM workload the same
+way (median and minimum launch time, head-steps/s, fraction of the FP32 peak)
+beside the oracle on a bounded sample of each, and `calibration` holds the
+chip's measured scalar FMA rate and LDS read bandwidth.
 
 With --backward a step is one training pass instead: the forward pass that
 records the tape, then the backward pass (dx and the batch-summed dW0 for a
@@ -18,6 +22,7 @@ the CPU baseline is the float64 gradient oracle.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--variant I] [--no-cpu] [--copy-calibration BYTES] [--backward]
+                  [--no-configs] [--config-cpu-budget S]
 """
 from __future__ import annotations
 
@@ -99,9 +104,38 @@ def valu_calibration(dev, stream) -> dict:
             "probe": f"{wgs} workgroups x 256 threads x {iters * 16} x 8 independent v_fma_f32 chains"}
 
 
-def measured_lds(which: str, workload: str, srcs, kernel_ms: float):
+def lds_calibration(dev, stream) -> dict:
+    """The chip's measured LDS read bandwidth (srwm_lds_probe: conflict-free
+    16-byte LDS reads by every lane, 8 workgroups of 4 waves per CU), outside
+    the timed region."""
+    import torch
+
+    from self_referential_weight_amd import _lib
+
+    lib = _lib.load()
+    wgs, iters = 2048, 4096
+    out = torch.empty(wgs * 256, dtype=torch.int32, device=dev)
+    handle = stream.cuda_stream
+    rc = lib.srwm_lds_probe(out.data_ptr(), wgs, iters, handle)
+    if rc != 0:
+        raise RuntimeError(_lib.strerror(rc))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(3):
+        lib.srwm_lds_probe(out.data_ptr(), wgs, iters, handle)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 3
+    tbps = lib.srwm_lds_probe_bytes(wgs, iters) / (ms * 1e-3) / 1e12
+    return {"lds_read_TBps": tbps, "bytes_per_clk_per_cu_at_2.4GHz": tbps * 1e12 / (256 * 2.4e9),
+            "probe": f"{wgs} workgroups x 256 threads x {iters * 16} ds_read_b128, conflict-free"}
+
+
+def measured_lds(which: str, workload: str, srcs, kernel_ms: float, peak_tbps=None):
     """LDS bytes per launch from the committed counter run, if taken on the
-    current kernel source and workload, turned into a rate over kernel_ms."""
+    current kernel source and workload, turned into a rate over kernel_ms and
+    compared with the measured LDS read bandwidth (peak_tbps) when given, else
+    with the assumed CDNA3 figure."""
     if not LDS_FILE.exists():
         return None
     try:
@@ -112,8 +146,10 @@ def measured_lds(which: str, workload: str, srcs, kernel_ms: float):
         return None
     nbytes = rec["lds_load_bytes_per_launch"] + rec["lds_store_bytes_per_launch"]
     tbps = nbytes / (kernel_ms * 1e-3) / 1e12
-    return {"bytes_per_launch": nbytes, "achieved": tbps, "unit": "TB/s", "assumed_peak": PEAK_LDS_TBPS,
-            "frac": tbps / PEAK_LDS_TBPS}
+    peak = peak_tbps if peak_tbps else PEAK_LDS_TBPS
+    return {"bytes_per_launch": nbytes, "achieved": tbps, "unit": "TB/s", "peak": peak,
+            "peak_kind": "measured (srwm_lds_probe)" if peak_tbps else "assumed (128 B/clk/CU)",
+            "frac": tbps / peak}
 
 
 def cpu_model() -> str:
@@ -136,9 +172,6 @@ def cpu_baseline(w, x_host, W0_host, budget_s: float):
     from oracle import oracle
 
     cores = oracle.default_threads()
-    env_cap = os.environ.get("OMP_NUM_THREADS")
-    if env_cap and env_cap.isdigit():
-        cores = max(1, min(cores, int(env_cap)))
     # calibration: one sequence
     t0 = time.perf_counter()
     oracle.forward(np.ascontiguousarray(x_host[:1], dtype=np.float64), W0_host,
@@ -148,19 +181,85 @@ def cpu_baseline(w, x_host, W0_host, budget_s: float):
     tau = t1 * min(w.H, cores) / w.H
     n = max(1, min(w.B, int(budget_s * cores / (max(tau, 1e-9) * w.H))))
     xs = np.ascontiguousarray(x_host[:n], dtype=np.float64)
-    t0 = time.perf_counter()
-    oracle.forward(xs, W0_host, w.apply_input_softmax, return_state=False, nthreads=cores)
-    dt = time.perf_counter() - t0
+    # very small workloads: repeat the call until the wall time is measurable
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(xs, W0_host, w.apply_input_softmax, return_state=False, nthreads=cores)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min(0.5, budget_s) or reps >= 100000:
+            break
     units = n * w.H
+    rep_note = f", {reps} repetitions" if reps > 1 else ""
     return {
-        "value": units * w.T / dt,
+        "value": reps * units * w.T / dt,
         "unit": "head-steps/s",
         "cores": cores,
         "kind": "oracle",
         "cpu_model": cpu_model(),
         "sample": (f"first {n} of {w.B} sequences x {w.H} heads ({units} units) x T={w.T} "
-                   f"of {w.name}, float64, {dt:.1f} s wall"),
+                   f"of {w.name}, float64, {dt:.1f} s wall{rep_note}"),
     }
+
+
+def oracle_cores_note() -> dict:
+    """How many host CPUs the oracle's thread pool uses and why."""
+    from oracle import oracle
+
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        aff = os.cpu_count() or 1
+    return {"affinity_cpus": aff, "threads": oracle.default_threads(),
+            "cap": "at most 16 threads (and OMP_NUM_THREADS): the host share one GPU is allotted"}
+
+
+def time_launches(step, stream, steps: int, warmup: int) -> list:
+    """Per-launch durations (ms) of `step` from HIP events on `stream`, one
+    event between consecutive launches, after `warmup` untimed calls."""
+    import torch
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record(stream)
+    for i in range(steps):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+
+
+def median(v: list) -> float:
+    v = sorted(v)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+
+def config_entry(w, per_launch: list, fma_rate, cpu) -> dict:
+    """One workload's line of the `configs` block."""
+    import self_referential_weight_amd as srwm
+
+    med, mn = median(per_launch), min(per_launch)
+    flop = w.flop_per_head_step * w.head_steps
+    kernel = srwm.select_variant(w.d_in, w.d_out, w.io_dtype, w.units)
+    ent = {
+        "B": w.B, "H": w.H, "d_in": w.d_in, "d_out": w.d_out, "T": w.T, "io_dtype": w.io_dtype,
+        "apply_input_softmax": w.apply_input_softmax, "return_state": w.return_state,
+        "units": w.units, "launches": len(per_launch),
+        "ms_median": med, "ms_min": mn, "ms_mean": sum(per_launch) / len(per_launch),
+        "head_steps_per_s": w.head_steps / (med * 1e-3),
+        "frac": flop / (med * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
+        "executed_frac": 0.75 * flop / (med * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
+        "kernel": f"srwm_fwd_kernel<{w.d_in},{w.d_out},{kernel['waves']},{kernel['lanes_per_row']},"
+                  f"{kernel['waves_per_simd']},...> ({kernel['schedule']}, variant {kernel['index']})",
+    }
+    if fma_rate:
+        ent["executed_frac_of_measured_fma_rate"] = 0.75 * flop / (med * 1e-3) / 1e12 / fma_rate
+    if cpu is not None:
+        ent["cpu_baseline"] = cpu
+    return ent
 
 
 def copy_calibration(nbytes: int, dev) -> None:
@@ -224,6 +323,10 @@ def main() -> int:
                     help="also run a plain device copy of this many bytes (counter calibration)")
     ap.add_argument("--backward", action="store_true",
                     help="time the training step (taped forward + backward) instead of the forward")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the `configs` block (every SRWM workload timed after the headline)")
+    ap.add_argument("--config-cpu-budget", type=float, default=3.0,
+                    help="seconds of oracle wall time per workload in the `configs` block")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -288,9 +391,7 @@ def main() -> int:
     wall = time.perf_counter() - t0
     per_launch = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
     gpu_ms = evs[0].elapsed_time(evs[-1]) / args.steps  # one kernel launch per step
-    per_launch.sort()
-    med_ms = per_launch[len(per_launch) // 2] if len(per_launch) % 2 else \
-        0.5 * (per_launch[len(per_launch) // 2 - 1] + per_launch[len(per_launch) // 2])
+    med_ms = median(per_launch)
     ms_per_step = wall * 1e3 / args.steps
     log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step wall, {gpu_ms:.3f} ms/launch (HIP events)")
 
@@ -302,6 +403,10 @@ def main() -> int:
     kernel = (srwm.variants()[args.variant] if args.variant >= 0
               else srwm.select_variant(w.d_in, w.d_out, w.io_dtype, w.units))
 
+    # Chip calibrations, outside the timed region: the scalar FP32 FMA rate and
+    # the LDS read bandwidth.
+    cal = valu_calibration(dev, stream)
+    lds_cal = lds_calibration(dev, stream)
     rec = {
         "metric": METRIC,
         "value": head_steps / (ms_per_step * 1e-3),
@@ -322,25 +427,66 @@ def main() -> int:
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_TFLOPS, "traffic": traffic},
         "kernel": dict({k: kernel[k] for k in ("index", "waves", "lanes_per_row", "waves_per_simd", "schedule")},
                        resources=srwm.kernel_resources(kernel["index"])),
-        "lds": measured_lds("forward", name, None, gpu_ms) if args.variant < 0 else None,
+        "lds": (measured_lds("forward", name, None, gpu_ms, lds_cal["lds_read_TBps"])
+                if args.variant < 0 else None),
         "kernel_ms": gpu_ms,
         "kernel_ms_median": med_ms,
-        "kernel_ms_min": per_launch[0],
+        "kernel_ms_min": min(per_launch),
         "io_stream_GBps": io_bytes / (gpu_ms * 1e-3) / 1e9,
     }
     # Against the measured scalar FP32 rate: the kernel executes 6 m d_in FLOP
     # per head-step (the two reads fused into one) of the algorithmic 8 m d_in.
-    cal = valu_calibration(dev, stream)
     executed = achieved * 6.0 / 8.0
     cal.update({"executed_TFLOPs": executed, "executed_frac": executed / cal["fp32_scalar_fma_TFLOPs"]})
-    rec["calibration"] = cal
+    rec["calibration"] = dict(cal, lds=lds_cal)
     log(f"[bench] measured scalar FP32 FMA rate {cal['fp32_scalar_fma_TFLOPs']:.1f} TFLOP/s; "
-        f"kernel executes {executed:.1f} TFLOP/s ({100 * cal['executed_frac']:.1f}%)")
+        f"kernel executes {executed:.1f} TFLOP/s ({100 * cal['executed_frac']:.1f}%); "
+        f"LDS read {lds_cal['lds_read_TBps']:.1f} TB/s")
     if not args.no_cpu:
         log("[bench] timing the float64 CPU oracle on a bounded sample")
-        rec["cpu_baseline"] = cpu_baseline(w, x_host, W0_host, args.cpu_budget)
+        rec["cpu_baseline"] = dict(cpu_baseline(w, x_host, W0_host, args.cpu_budget), **oracle_cores_note())
+    if not args.no_configs and args.variant < 0:
+        rec["configs"] = all_configs(args, name, w, per_launch, rec.get("cpu_baseline"), dev, stream,
+                                     cal["fp32_scalar_fma_TFLOPs"])
     print(json.dumps(rec), flush=True)
     return 0
+
+
+def all_configs(args, headline, hw, headline_launches, headline_cpu, dev, stream, fma_rate) -> dict:
+    """Every SRWM workload, timed like the headline (HIP events around each
+    launch of the automatically chosen kernel on `stream`, after warm-up),
+    with the float64 oracle timed on a bounded sample of each.  The headline
+    workload reuses the timed launches above."""
+    import torch
+
+    import self_referential_weight_amd as srwm
+    from self_referential_weight_amd.workloads import WORKLOADS, gen_W0, gen_x
+
+    out = {}
+    for name, w in WORKLOADS.items():
+        if name == headline:
+            out[name] = config_entry(hw, headline_launches, fma_rate, headline_cpu)
+            continue
+        x_host, W0_host = gen_x(w), gen_W0(w)
+        x = torch.from_numpy(x_host).to(dev)
+        if w.io_dtype == "bf16":
+            x = x.to(torch.bfloat16)
+        W0 = torch.from_numpy(W0_host).to(dev)
+        y = torch.empty((w.B, w.T, w.H, w.d_out), dtype=x.dtype, device=dev)
+        W_T = torch.empty((w.B, w.H, w.m, w.d_in), dtype=torch.float32, device=dev) if w.return_state else None
+
+        def step():
+            srwm.forward(x, W0, apply_input_softmax=w.apply_input_softmax, return_state=w.return_state,
+                         y=y, W_T=W_T, stream=stream)
+        launches = time_launches(step, stream, max(args.steps, 20), max(args.warmup, 3))
+        log(f"[bench] {name}: median {median(launches):.4f} ms, min {min(launches):.4f} ms "
+            f"over {len(launches)} launches")
+        cpu = None
+        if not args.no_cpu:
+            cpu = dict(cpu_baseline(w, x_host, W0_host, args.config_cpu_budget), **oracle_cores_note())
+        out[name] = config_entry(w, launches, fma_rate, cpu)
+        del x, W0, y, W_T
+    return out
 
 
 def bench_backward(args, w, name, x, x_host, W0, W0_host, dev) -> int:
@@ -391,6 +537,7 @@ def bench_backward(args, w, name, x, x_host, W0, W0_host, dev) -> int:
     # FLOP), the rank-one update two more (Wh kh and Wh^T a, 4 m d_in): 16 m d_in.
     flop_bwd = 16 * w.m * w.d_in * head_steps
     achieved = flop_bwd / (b_ms * 1e-3) / 1e12
+    lds_cal = lds_calibration(dev, stream)
     rec = {
         "metric": "SRWM training head-steps/sec (taped forward + backward), 1×MI355X",
         "value": head_steps / (ms_per_step * 1e-3),
@@ -409,7 +556,8 @@ def bench_backward(args, w, name, x, x_host, W0, W0_host, dev) -> int:
         "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_TFLOPS,
                      "traffic": measured_traffic(name + "+backward", -1, BWD_TRAFFIC_FILE, BWD_SRCS)},
-        "lds": measured_lds("backward", name + "+backward", BWD_SRCS, b_ms),
+        "lds": measured_lds("backward", name + "+backward", BWD_SRCS, b_ms, lds_cal["lds_read_TBps"]),
+        "calibration": {"lds": lds_cal},
         "forward_ms": f_ms,
         "backward_ms": b_ms,
         "backward_kernel_resources": srwm.backward_resources(w.d_in, w.d_out, w.n_lr, False, w.units),

@@ -39,6 +39,15 @@
  *   - Execution: asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream).  The return code covers argument validation and the launch
  *     only; a fault during execution surfaces at the next synchronisation.
+ *   - Plain C types at the boundary: every `int io_dtype` holds a
+ *     srwm_io_dtype_t value and every `void* stream` (and `aux_stream`) is a
+ *     hipStream_t passed as a pointer, so this header needs no HIP header and
+ *     a caller that has none (ctypes, another language's FFI) can still call
+ *     it.  The ABI is the same as with the enum and hipStream_t spelled out.
+ *   - Alignment: the kernels move 16-byte pieces, so every buffer must start
+ *     on a 16-byte boundary.  A hipMalloc'd pointer always does; a view at an
+ *     odd offset into a larger buffer may not, and is refused with
+ *     SRWM_ERR_ARG (the Python binding names the offending tensor).
  *   - Errors: negative codes below; srwm_strerror() names them.  Validation
  *     happens before any HIP call, so an invalid call touches no device.
  */
@@ -417,6 +426,20 @@ int srwm_supported(int64_t d_in, int64_t d_out, int io_dtype, int n_lr);
  */
 int srwm_valu_probe(float* out, int64_t workgroups, int iters, void* stream);
 int64_t srwm_valu_probe_flop(int64_t workgroups, int iters);
+
+/*
+ * Measurement aid (not part of the method): srwm_lds_probe launches
+ * `workgroups` workgroups of 256 threads that each fill a 16 KB LDS array and
+ * then run `iters` rounds of 16 conflict-free 16-byte LDS reads per lane
+ * (ds_read_b128; a wave's lanes read one contiguous 1 KB span), folding the
+ * values into one word per thread written to out[workgroups*256] (device,
+ * 16-byte aligned).  Timing it gives the chip's LDS read bandwidth, the roof
+ * the kernels' LDS traffic is compared with; srwm_lds_probe_bytes returns the
+ * LDS bytes one launch reads.  Errors: SRWM_ERR_NULL (out), SRWM_ERR_SHAPE
+ * (workgroups or iters < 1), SRWM_ERR_ARG (alignment), SRWM_ERR_HIP (launch).
+ */
+int srwm_lds_probe(unsigned* out, int64_t workgroups, int iters, void* stream);
+int64_t srwm_lds_probe_bytes(int64_t workgroups, int iters);
 
 /* Static string naming an error code (never NULL). */
 const char* srwm_strerror(int code);

@@ -151,6 +151,7 @@ def forward(x, W0, apply_input_softmax: bool = False, return_state: bool = False
         if reset_interval > 0:
             n_res = (T - 1) // reset_interval if T > 0 else 0
             wstates = torch.empty((B, H, n_res, m, d_in), dtype=torch.float32, device=x.device)
+    _check_aligned(x=x, W0=W0, y=y, W_T=W_T)
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
@@ -214,6 +215,7 @@ def backward(x, W_T, tape, gy, gW_T=None, apply_input_softmax: bool = False, n_l
         if (wstates is None or tuple(wstates.shape) != (B, H, n_res, m, d_in) or wstates.dtype != torch.float32
                 or wstates.device != x.device or not wstates.is_contiguous()):
             raise ValueError("the tape's window states do not match x")
+    _check_aligned(W_T=W_T, tape=tape, gy=gy, gW_T=gW_T, window_states=wstates)
     dx = torch.empty((B, T, H, d_in), dtype=torch.float32, device=x.device)
     dWi = torch.empty((B, H, m, d_in), dtype=torch.float32, device=x.device)
     dW0 = torch.empty((H, m, d_in), dtype=torch.float32, device=x.device) if shared_W0 else None
@@ -234,6 +236,8 @@ def backward(x, W_T, tape, gy, gW_T=None, apply_input_softmax: bool = False, n_l
         rc = lib.srwm_backward(a)
     if rc != 0:
         raise RuntimeError(_lib.strerror(rc))
+    if shared_W0:
+        _hold_for(dWi, x.device, stream)  # per-unit gradients, summed into dW0 on `stream`
     return dx, (dW0 if shared_W0 else dWi)
 
 
@@ -321,12 +325,41 @@ def _ptr(t):
     return t.data_ptr() if t is not None and t.numel() else None
 
 
+def _check_aligned(**tensors):
+    """The kernels move 16-byte pieces, so the library takes only buffers that
+    start on a 16-byte boundary (a misaligned pointer is SRWM_ERR_ARG); name
+    the offending tensor here instead."""
+    for name, t in tensors.items():
+        if t is not None and t.numel() and t.data_ptr() % 16:
+            raise ValueError(f"{name} must start on a 16-byte boundary (libsrwm's kernels move 16-byte pieces); "
+                             f"its data pointer is {t.data_ptr() % 16} bytes past one, as a view at an odd "
+                             f"offset into a larger buffer can be: pass a fresh allocation or .clone() it")
+
+
 def _stream_handle(x, stream):
     import torch
 
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _hold_for(t, device, *streams):
+    """Keep the caching allocator from handing `t`'s memory to other work
+    until what is queued now on each of `streams` (torch streams or raw HIP
+    handles) has run: for library temporaries that are dropped when the call
+    returns while kernels that use them may still be queued on a stream other
+    than torch's current one."""
+    import torch
+
+    if t is None or not t.numel():
+        return
+    for s in streams:
+        if s is None:
+            continue
+        if not hasattr(s, "cuda_stream"):
+            s = torch.cuda.ExternalStream(int(s), device=device)
+        t.record_stream(s)
 
 
 def deltanet_forward(x, W_slow, d_key: int, d_v: int, F0=None, return_state: bool = False, z=None, y=None,
@@ -346,6 +379,7 @@ def deltanet_forward(x, W_slow, d_key: int, d_v: int, F0=None, return_state: boo
     if (tuple(W_slow.shape) != (H * P, H * d_in) or W_slow.dtype != torch.float32
             or W_slow.device != x.device or not W_slow.is_contiguous()):
         raise ValueError("W_slow must be a contiguous float32 [H*P, H*d_in] tensor on x's device")
+    _check_aligned(x=x, W_slow=W_slow, F0=F0, z=z, y=y)
     a = _lib.DeltanetArgs(x=_ptr(x), W_slow=_ptr(W_slow), F0=_ptr(F0), z=_ptr(z), y=_ptr(y), F_T=_ptr(F_T),
                           B=B, T=T, H=H, d_in=d_in, d_key=d_key, d_v=d_v, stream=_stream_handle(x, stream))
     with torch.cuda.device(x.device):
@@ -398,9 +432,12 @@ def srdeltanet_forward(x, W0, d_key: int, d_v: int, F0=None, apply_input_softmax
         raise ValueError("chunk_steps must be >= 0")
     W_T = (torch.empty((B, H, m, d_in), dtype=torch.float32, device=x.device)
            if return_state or overlap else None)
-    aux = None
+    aux = aux_obj = None
     if overlap:
-        aux = _stream_handle(x, aux_stream if aux_stream is not None else _aux_stream(x.device))
+        aux_obj = aux_stream if aux_stream is not None else _aux_stream(x.device)
+        aux = _stream_handle(x, aux_obj)
+    main = stream if stream is not None else torch.cuda.current_stream(x.device)
+    _check_aligned(x=x, W0=W0, F0=F0, z=z, y=y)
     a = _lib.SrdeltanetArgs(x=_ptr(x), W0=_ptr(W0), F0=_ptr(F0), z=_ptr(z), y=_ptr(y), W_T=_ptr(W_T),
                             F_T=_ptr(F_T), B=B, T=T, H=H, d_in=d_in, d_key=d_key, d_v=d_v, n_lr=int(n_lr),
                             apply_input_softmax=int(bool(apply_input_softmax)),
@@ -410,6 +447,9 @@ def srdeltanet_forward(x, W0, d_key: int, d_v: int, F0=None, apply_input_softmax
     if rc != 0:
         raise RuntimeError(_lib.strerror(rc))
     if not return_state:
+        # the chunks' carried states, read and rewritten by kernels on both streams
+        _hold_for(W_T, x.device, main, aux_obj)
+        _hold_for(F_T, x.device, main, aux_obj)
         W_T = F_T = None
     return y, W_T, F_T, z
 
@@ -423,6 +463,7 @@ def deltanet_project(x, W_slow, d_key: int, d_v: int, z=None, stream=None):
     if (tuple(W_slow.shape) != (H * P, H * d_in) or W_slow.dtype != torch.float32
             or W_slow.device != x.device or not W_slow.is_contiguous()):
         raise ValueError("W_slow must be a contiguous float32 [H*P, H*d_in] tensor on x's device")
+    _check_aligned(x=x, W_slow=W_slow, z=z)
     a = _lib.DeltanetArgs(x=_ptr(x), W_slow=_ptr(W_slow), F0=None, z=_ptr(z), y=None, F_T=None,
                           B=B, T=T, H=H, d_in=d_in, d_key=d_key, d_v=d_v, stream=_stream_handle(x, stream))
     with torch.cuda.device(x.device):
@@ -470,6 +511,7 @@ def fast_forward(z, d_key: int, d_v: int, F0=None, return_state: bool = False, y
             raise ValueError("F_T must be a contiguous float32 [B, H, d_v, d_key] tensor on z's device")
     elif return_state:
         F_T = torch.empty((B, H, d_v, d_key), dtype=torch.float32, device=z.device)
+    _check_aligned(F0=F0, y=y, F_T=F_T)  # z's rows are read at any offset
     a = _lib.FastArgs(z=_ptr(z), F0=_ptr(F0), y=_ptr(y), F_T=_ptr(F_T), B=B, T=T, H=H, d_key=d_key, d_v=d_v,
                       stream=_stream_handle(z, stream), t_stride=t_stride)
     with torch.cuda.device(z.device):

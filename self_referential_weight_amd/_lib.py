@@ -178,6 +178,10 @@ def load() -> ctypes.CDLL:
     lib.srwm_valu_probe.restype = ci
     lib.srwm_valu_probe_flop.argtypes = [i64, ci]
     lib.srwm_valu_probe_flop.restype = i64
+    lib.srwm_lds_probe.argtypes = [ctypes.c_void_p, i64, ci, ctypes.c_void_p]
+    lib.srwm_lds_probe.restype = ci
+    lib.srwm_lds_probe_bytes.argtypes = [i64, ci]
+    lib.srwm_lds_probe_bytes.restype = i64
     lib.srwm_variant_count.argtypes = []
     lib.srwm_variant_count.restype = ci
     lib.srwm_variant_info.argtypes = [ci, ctypes.POINTER(VariantInfo)]

@@ -1,7 +1,8 @@
-// srwm_calib.hip -- measurement aid: the chip's scalar FP32 FMA rate, against
+// srwm_calib.hip -- measurement aids: the chip's scalar FP32 FMA rate, against
 // which the kernels' executed arithmetic is compared (the peak the product
 // kernels can reach: packed FP32 instructions are disabled at build time, so
-// every FMA is a single-lane v_fma_f32 / v_fmac_f32).
+// every FMA is a single-lane v_fma_f32 / v_fmac_f32), and its LDS read
+// bandwidth, against which the kernels' LDS traffic is compared.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -30,6 +31,35 @@ __global__ __launch_bounds__(256) void srwm_valu_probe_kernel(float* __restrict_
     out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// LDS read bandwidth: every lane reads 16-byte pieces (ds_read_b128) from a
+// 16 KB LDS array, a wave's 64 lanes one contiguous 1 KB span (no bank
+// conflicts), at an address that moves by 13 entries per iteration (not a
+// divisor of the array, so the addresses of one iteration never repeat those
+// of the last and no load can be hoisted out of the loop or merged).  The values are folded with three-input XORs (two VALU
+// instructions per 16-byte load), far below the VALU's rate, so the loads set
+// the pace.  Four waves per workgroup, several workgroups per CU.
+constexpr int kLdsVec = 1024;  // float4 entries of the array (16 KB)
+constexpr int kLdsUnroll = 16;
+
+__global__ __launch_bounds__(256) void srwm_lds_probe_kernel(unsigned* __restrict__ out, int iters)
+{
+    __shared__ uint4 buf[kLdsVec];
+    const int t = threadIdx.x;
+    for (int i = t; i < kLdsVec; i += 256)
+        buf[i] = make_uint4(i * 2654435761u, i ^ 0x9e3779b9u, i + 7u, ~i);
+    __syncthreads();
+    unsigned a = t, b = t * 3u;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int u = 0; u < kLdsUnroll; ++u) {
+            const uint4 v = buf[(t + 64 * u + 13 * it) & (kLdsVec - 1)];
+            a = a ^ v.x ^ v.y;
+            b = b ^ v.z ^ v.w;
+        }
+    }
+    out[blockIdx.x * blockDim.x + t] = a + b;
+}
+
 }  // namespace
 
 extern "C" {
@@ -51,6 +81,24 @@ int srwm_valu_probe(float* out, int64_t workgroups, int iters, void* stream)
 int64_t srwm_valu_probe_flop(int64_t workgroups, int iters)
 {
     return workgroups * 256 * static_cast<int64_t>(iters) * 16 * kChains * 2;
+}
+
+int srwm_lds_probe(unsigned* out, int64_t workgroups, int iters, void* stream)
+{
+    if (out == nullptr) return SRWM_ERR_NULL;
+    if (workgroups < 1 || workgroups > INT32_MAX || iters < 1) return SRWM_ERR_SHAPE;
+    if (reinterpret_cast<uintptr_t>(out) & 15u) return SRWM_ERR_ARG;
+    int it = iters;
+    void* args[] = {&out, &it};
+    const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(&srwm_lds_probe_kernel),
+                                           dim3(static_cast<unsigned>(workgroups)), dim3(256), args, 0,
+                                           static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? SRWM_OK : SRWM_ERR_HIP;
+}
+
+int64_t srwm_lds_probe_bytes(int64_t workgroups, int iters)
+{
+    return workgroups * 256 * static_cast<int64_t>(iters) * kLdsUnroll * 16;
 }
 
 }  // extern "C"

@@ -340,8 +340,11 @@ const FastVariant kFastVariants[] = {
 };
 constexpr int kNumFastVariants = sizeof(kFastVariants) / sizeof(kFastVariants[0]);
 
-// The most waves per unit that keep units * waves within four waves per SIMD
-// of the chip (4096); else the fewest.
+// The most row-holding waves per unit that keep units * nw within four waves
+// per SIMD of the chip (4096); else the fewest.  The bound counts the
+// row-holding waves only: the preparing waves sit beside them (512 units of
+// the 8 + 4 variant launch 6144 waves), which measured faster than the
+// 4 + 4 variant at 512 units.
 int find_fast(int64_t d_key, int64_t d_v, int64_t units = 1)
 {
     int best = -1, fewest = -1;
@@ -513,8 +516,13 @@ int srdeltanet_overlapped(const srwm_srdeltanet_args_t* a, const FwdPlan& plan, 
     const hipStream_t main_s = static_cast<hipStream_t>(a->stream);
     const hipStream_t aux_s = static_cast<hipStream_t>(a->aux_stream);
     const int64_t P = a->d_v + 2 * a->d_key + 1;
+    // One event, recorded once per chunk on the caller's stream (a wait takes
+    // the record made before it) and once at the end on aux.
     hipEvent_t ev;
-    for (int64_t t0 = 0; t0 < a->T; t0 += C) {
+    if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) return SRWM_ERR_HIP;
+    int rc = SRWM_OK;
+    bool aux_used = false;
+    for (int64_t t0 = 0; t0 < a->T && rc == SRWM_OK; t0 += C) {
         const int64_t n = (a->T - t0) < C ? (a->T - t0) : C;
         srwm_forward_args_t fc = f;
         fc.x = a->x + t0 * a->H * a->d_in;
@@ -523,20 +531,25 @@ int srdeltanet_overlapped(const srwm_srdeltanet_args_t* a, const FwdPlan& plan, 
         fc.t_stride = a->T;
         fc.W0 = t0 == 0 ? a->W0 : a->W_T;
         fc.w0_per_sequence = t0 == 0 ? 0 : 1;
-        int rc = forward_launch(plan, &fc);
-        if (rc != SRWM_OK) return rc;
-        if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) return SRWM_ERR_HIP;
-        const bool ok = hipEventRecord(ev, main_s) == hipSuccess && hipStreamWaitEvent(aux_s, ev, 0) == hipSuccess;
-        (void)hipEventDestroy(ev);
-        if (!ok) return SRWM_ERR_HIP;
+        rc = forward_launch(plan, &fc);
+        if (rc != SRWM_OK) break;
+        if (hipEventRecord(ev, main_s) != hipSuccess || hipStreamWaitEvent(aux_s, ev, 0) != hipSuccess) {
+            rc = SRWM_ERR_HIP;
+            break;
+        }
+        aux_used = true;
         rc = launch_fast(vi, a->z + t0 * a->H * P, t0 == 0 ? a->F0 : a->F_T, a->y + t0 * a->H * a->d_v, a->F_T,
                          units, n, a->T, a->H, a->aux_stream);
-        if (rc != SRWM_OK) return rc;
     }
-    if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) return SRWM_ERR_HIP;
-    const bool ok = hipEventRecord(ev, aux_s) == hipSuccess && hipStreamWaitEvent(main_s, ev, 0) == hipSuccess;
+    // The caller's stream waits for everything queued on aux, also after an
+    // error (best effort), so no fast-matrix chunk outlives the call's stream
+    // order and a captured aux stream is always joined back.
+    if (aux_used) {
+        const bool ok = hipEventRecord(ev, aux_s) == hipSuccess && hipStreamWaitEvent(main_s, ev, 0) == hipSuccess;
+        if (!ok && rc == SRWM_OK) rc = SRWM_ERR_HIP;
+    }
     (void)hipEventDestroy(ev);
-    return ok ? SRWM_OK : SRWM_ERR_HIP;
+    return rc;
 }
 
 int srdeltanet_impl(const srwm_srdeltanet_args_t* a)
@@ -570,6 +583,10 @@ int srdeltanet_impl(const srwm_srdeltanet_args_t* a)
         if (ranges_overlap(outs[o], nouts[o], a->F0, a->F0 ? s.nf : 0)) return SRWM_ERR_ALIAS;
     }
     if (ranges_overlap(a->y, s.ny, a->F_T, a->F_T ? s.nf : 0)) return SRWM_ERR_ALIAS;
+    // the SRWM half writes z and W_T before the fast matrix reads F0
+    if (ranges_overlap(a->F0, a->F0 ? s.nf : 0, a->z, s.nz) ||
+        ranges_overlap(a->F0, a->F0 ? s.nf : 0, a->W_T, a->W_T ? nst : 0))
+        return SRWM_ERR_ALIAS;
     // the projection: the SRWM with d_out = P writes its outputs into z
     srwm_forward_args_t f;
     f.x = a->x;

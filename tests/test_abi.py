@@ -323,6 +323,10 @@ def test_deltanet_validation(kw, code):
     (dict(y=FAKE_Y + 4), E_ARG),
     (dict(y=FAKE_Z + 64), E_ALIAS),
     (dict(F_T=FAKE_W0 + 16), E_ALIAS),
+    # the SRWM half writes z and W_T before the fast matrix reads F0
+    (dict(F0=FAKE_Z + 16), E_ALIAS),
+    (dict(F0=FAKE_WT, W_T=FAKE_WT), E_ALIAS),
+    (dict(F0=FAKE_WT + 64, W_T=FAKE_WT, F_T=FAKE_Y + 65536), E_ALIAS),
     (dict(y=None), E_NULL),
     (dict(chunk_steps=-1), E_ARG),
 ])
@@ -433,6 +437,16 @@ def test_valu_probe_validation():
     assert lib.srwm_valu_probe(FAKE_Y, 4, 0, None) == E_SHAPE
     assert lib.srwm_valu_probe(FAKE_Y + 4, 4, 1, None) == E_ARG
     assert lib.srwm_valu_probe_flop(2, 3) == 2 * 256 * 3 * 16 * 8 * 2
+
+
+def test_lds_probe_validation():
+    lib = _lib.load()
+    assert lib.srwm_lds_probe(None, 4, 1, None) == E_NULL
+    assert lib.srwm_lds_probe(FAKE_Y, 0, 1, None) == E_SHAPE
+    assert lib.srwm_lds_probe(FAKE_Y, 4, 0, None) == E_SHAPE
+    assert lib.srwm_lds_probe(FAKE_Y + 4, 4, 1, None) == E_ARG
+    # 16 reads of 16 bytes per lane and iteration
+    assert lib.srwm_lds_probe_bytes(2, 3) == 2 * 256 * 3 * 16 * 16
 
 
 # ---------------------------------------------------------------------------

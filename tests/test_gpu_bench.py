@@ -34,7 +34,7 @@ def check_common(d, metric_word):
 
 
 def test_forward_line():
-    d = bench(["--steps", "3", "--warmup", "1", "--cpu-budget", "2"])
+    d = bench(["--steps", "3", "--warmup", "1", "--cpu-budget", "2", "--config-cpu-budget", "1"])
     check_common(d, "head-steps/sec")
     # B*H*T / time per step
     assert d["value"] == pytest.approx(128 * 16 * 4096 / (d["ms_per_step"] * 1e-3), rel=1e-6)
@@ -42,6 +42,18 @@ def test_forward_line():
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["unit"] == "head-steps/s"
     assert cb["sample"] and cb["cpu_model"]
+    assert cb["threads"] == cb["cores"] and cb["affinity_cpus"] >= 1
+    # the chip's measured LDS read bandwidth, and the five workloads
+    assert d["calibration"]["lds"]["lds_read_TBps"] > 0
+    from self_referential_weight_amd.workloads import WORKLOADS
+    assert set(d["configs"]) == set(WORKLOADS)
+    for name, c in d["configs"].items():
+        w = WORKLOADS[name]
+        assert c["launches"] >= 3 and 0 < c["ms_min"] <= c["ms_median"]
+        assert c["head_steps_per_s"] == pytest.approx(w.head_steps / (c["ms_median"] * 1e-3))
+        assert c["executed_frac"] == pytest.approx(0.75 * c["frac"]) and 0 < c["frac"] < 1
+        assert c["cpu_baseline"]["kind"] == "oracle" and c["cpu_baseline"]["value"] > 0
+    assert d["configs"]["rl_d64_bf16"]["cpu_baseline"] == cb
 
 
 def test_training_line():

@@ -275,8 +275,8 @@ def test_fast_forward_over_time_slices():
 
 @pytest.mark.parametrize("B", [260])
 def test_fast_kernel_for_many_units(B):
-    # Above 512 units the fast matrix runs on 4 row-holding waves per unit (two
-    # rows per lane) beside 4 preparing ones instead of 8 beside 4: the same
+    # Above 512 units the fast matrix runs on 4 row-holding waves per unit (one
+    # row of 16 columns per lane) beside 4 preparing ones instead of 8 beside 4: the same
     # results, checked against the oracle on sampled sequences, with a ragged
     # last chunk (T = 37).
     w = FwpWorkload("dn_units", "deltanet", B=B, H=2, d_in=16, d_key=64, d_v=64, T=37, apply_input_softmax=False,
