@@ -429,7 +429,7 @@ int64_t srwm_valu_probe_flop(int64_t workgroups, int iters);
 
 /*
  * Measurement aid (not part of the method): srwm_lds_probe launches
- * `workgroups` workgroups of 256 threads that each fill a 16 KB LDS array and
+ * `workgroups` workgroups of 256 threads that each fill a 32 KB LDS array and
  * then run `iters` rounds of 16 conflict-free 16-byte LDS reads per lane
  * (ds_read_b128; a wave's lanes read one contiguous 1 KB span), folding the
  * values into one word per thread written to out[workgroups*256] (device,

@@ -32,13 +32,16 @@ __global__ __launch_bounds__(256) void srwm_valu_probe_kernel(float* __restrict_
 }
 
 // LDS read bandwidth: every lane reads 16-byte pieces (ds_read_b128) from a
-// 16 KB LDS array, a wave's 64 lanes one contiguous 1 KB span (no bank
-// conflicts), at an address that moves by 13 entries per iteration (not a
-// divisor of the array, so the addresses of one iteration never repeat those
-// of the last and no load can be hoisted out of the loop or merged).  The values are folded with three-input XORs (two VALU
-// instructions per 16-byte load), far below the VALU's rate, so the loads set
-// the pace.  Four waves per workgroup, several workgroups per CU.
-constexpr int kLdsVec = 1024;  // float4 entries of the array (16 KB)
+// 32 KB LDS array, a wave's 64 lanes one contiguous 1 KB span (no bank
+// conflicts).  Per iteration the 16 reads of a lane sit 1 KB apart from one
+// base (immediate offsets: no address arithmetic per read), and the base moves
+// by 13 entries per iteration, so no read can be hoisted out of the loop or
+// merged with the last iteration's.  The values are folded with three-input
+// integer adds (two VALU instructions per 16-byte read: a wave's 1 KB read
+// costs 8 SIMD cycles of issue, so the VALU could keep up with 512 B per
+// clock per CU), and the reads set the pace.  Four waves per workgroup, several workgroups
+// per CU.
+constexpr int kLdsVec = 2048;  // float4 entries of the array (32 KB)
 constexpr int kLdsUnroll = 16;
 
 __global__ __launch_bounds__(256) void srwm_lds_probe_kernel(unsigned* __restrict__ out, int iters)
@@ -50,11 +53,12 @@ __global__ __launch_bounds__(256) void srwm_lds_probe_kernel(unsigned* __restric
     __syncthreads();
     unsigned a = t, b = t * 3u;
     for (int it = 0; it < iters; ++it) {
+        const uint4* __restrict__ base = buf + ((t + 13 * it) & 1023);  // + 15 KB stays inside the array
 #pragma unroll
         for (int u = 0; u < kLdsUnroll; ++u) {
-            const uint4 v = buf[(t + 64 * u + 13 * it) & (kLdsVec - 1)];
-            a = a ^ v.x ^ v.y;
-            b = b ^ v.z ^ v.w;
+            const uint4 v = base[64 * u];
+            a = a + v.x + v.y;  // v_add3_u32
+            b = b + v.z + v.w;
         }
     }
     out[blockIdx.x * blockDim.x + t] = a + b;
