@@ -35,7 +35,8 @@
  *     library allocates no memory, frees nothing, keeps no pointer after the
  *     call returns and holds no mutable global state: concurrent calls on
  *     different streams are safe.  (An SR-DeltaNet call given a second stream
- *     creates and destroys HIP events; see there.)
+ *     creates and destroys a HIP event; see there.  srwm_backward_noalloc
+ *     uses a scratch array the library holds per GPU; see there.)
  *   - Execution: asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream).  The return code covers argument validation and the launch
  *     only; a fault during execution surfaces at the next synchronisation.
@@ -61,7 +62,7 @@ extern "C" {
 #endif
 
 #define SRWM_VERSION_MAJOR 0
-#define SRWM_VERSION_MINOR 7
+#define SRWM_VERSION_MINOR 8
 #define SRWM_VERSION_PATCH 0
 
 typedef enum { SRWM_IO_F32 = 0, SRWM_IO_BF16 = 1 } srwm_io_dtype_t;
@@ -73,9 +74,11 @@ enum {
     SRWM_ERR_UNSUPPORTED = -3, /* no kernel built for (d_in, d_out, io_dtype, n_lr) */
     SRWM_ERR_ALIAS = -4,       /* an output overlaps an input or the other output  */
     SRWM_ERR_HIP = -5,         /* the HIP runtime rejected the launch               */
-    SRWM_ERR_ARG = -6          /* other invalid argument (io_dtype, flag, n_lr,
+    SRWM_ERR_ARG = -6,         /* other invalid argument (io_dtype, flag, n_lr,
                                   reset interval, variant, a pointer not 16-byte
                                   aligned)                                          */
+    SRWM_ERR_SCRATCH = -7      /* srwm_backward_noalloc: one sequence's per-unit
+                                  gradients exceed the library's scratch array   */
 };
 
 /*
@@ -294,6 +297,36 @@ typedef struct srwm_backward_args {
 } srwm_backward_args_t;
 
 int srwm_backward(const srwm_backward_args_t* args);
+
+/*
+ * srwm_backward_noalloc -- srwm_backward for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving or training
+ * loops, harnesses that forbid hipMalloc) and want only the gradient of a
+ * shared initial matrix: the per-unit gradients srwm_backward writes to the
+ * caller's dW_init live instead in a scratch array the library holds on each
+ * GPU (a file-scope device array of srwm_backward_noalloc_scratch_bytes()
+ * bytes, 32 MiB, one copy per GPU, held until the process ends).
+ *
+ *   args->dW_init must be NULL (SRWM_ERR_ARG otherwise); args->dW0 [H][m][d_in]
+ *   is required when H*m*d_in > 0 (SRWM_ERR_NULL); everything else as in
+ *   srwm_backward, whose kernels it runs.  dx and dW0 are bit-identical to
+ *   srwm_backward's for the same arguments.
+ *   The batch runs in slices of whole sequences that fit the scratch, each
+ *   slice's gradients summed into dW0 in order; a call whose single sequence
+ *   needs more (H*m*d_in*4 bytes > the scratch) returns SRWM_ERR_SCRATCH.
+ *   The scratch used is the current device's: `stream` (if not NULL) must
+ *   belong to the current device (SRWM_ERR_ARG otherwise).  The first call on
+ *   a device looks the array's address up (a HIP call, no allocation); no
+ *   call allocates or frees memory.
+ *   Calls on one GPU share its scratch and it keeps the last call's
+ *   contents (every element a call reads it has written first): two calls
+ *   that overlap in time on one GPU, on any streams, race and give wrong
+ *   results; serialise them.
+ */
+int srwm_backward_noalloc(const srwm_backward_args_t* args);
+
+/* Size in bytes of srwm_backward_noalloc's scratch array (per GPU). */
+int64_t srwm_backward_noalloc_scratch_bytes(void);
 
 /* Floats per step in the tape: round_up(m, 4) + 3*d_in + 4, or SRWM_ERR_SHAPE. */
 int64_t srwm_tape_row(int64_t d_in, int64_t d_out, int n_lr);

@@ -175,7 +175,7 @@ def forward(x, W0, apply_input_softmax: bool = False, return_state: bool = False
 
 
 def backward(x, W_T, tape, gy, gW_T=None, apply_input_softmax: bool = False, n_lr: int = 4,
-             shared_W0: bool = True, stream=None):
+             shared_W0: bool = True, stream=None, no_alloc: bool = False):
     """Gradients of L = sum_t <gy[t], y_t> + <gW_T, W_T> through the recurrence.
 
     x, W_T, tape: the forward pass's input, final state and Tape
@@ -183,6 +183,9 @@ def backward(x, W_T, tape, gy, gW_T=None, apply_input_softmax: bool = False, n_l
     [B, T, H, d_out] and gW_T [B, H, m, d_in] (or None) float32.  Returns
     (dx [B, T, H, d_in] float32, dW0): dW0 is [H, m, d_in] (summed over the
     batch) when shared_W0, else the per-unit gradient [B, H, m, d_in].
+    no_alloc (with shared_W0): call srwm_backward_noalloc, whose per-unit
+    gradients live in the library's scratch array instead of a temporary
+    (calls that overlap in time on one GPU must not both use it).
     """
     import torch
 
@@ -216,8 +219,10 @@ def backward(x, W_T, tape, gy, gW_T=None, apply_input_softmax: bool = False, n_l
                 or wstates.device != x.device or not wstates.is_contiguous()):
             raise ValueError("the tape's window states do not match x")
     _check_aligned(W_T=W_T, tape=tape, gy=gy, gW_T=gW_T, window_states=wstates)
+    if no_alloc and not shared_W0:
+        raise ValueError("no_alloc returns only the batch-summed gradient: it needs shared_W0=True")
     dx = torch.empty((B, T, H, d_in), dtype=torch.float32, device=x.device)
-    dWi = torch.empty((B, H, m, d_in), dtype=torch.float32, device=x.device)
+    dWi = None if no_alloc else torch.empty((B, H, m, d_in), dtype=torch.float32, device=x.device)
     dW0 = torch.empty((H, m, d_in), dtype=torch.float32, device=x.device) if shared_W0 else None
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
@@ -233,7 +238,7 @@ def backward(x, W_T, tape, gy, gW_T=None, apply_input_softmax: bool = False, n_l
                           apply_input_softmax=int(bool(apply_input_softmax)), n_lr=int(n_lr),
                           stream=handle, reset_interval=int(reset_interval), window_states=ptr(wstates))
     with torch.cuda.device(x.device):
-        rc = lib.srwm_backward(a)
+        rc = lib.srwm_backward_noalloc(a) if no_alloc else lib.srwm_backward(a)
     if rc != 0:
         raise RuntimeError(_lib.strerror(rc))
     if shared_W0:

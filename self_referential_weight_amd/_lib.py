@@ -158,6 +158,10 @@ def load() -> ctypes.CDLL:
     lib.srwm_forward_ex.restype = ci
     lib.srwm_backward.argtypes = [ctypes.POINTER(BackwardArgs)]
     lib.srwm_backward.restype = ci
+    lib.srwm_backward_noalloc.argtypes = [ctypes.POINTER(BackwardArgs)]
+    lib.srwm_backward_noalloc.restype = ci
+    lib.srwm_backward_noalloc_scratch_bytes.argtypes = []
+    lib.srwm_backward_noalloc_scratch_bytes.restype = i64
     lib.srwm_tape_row.argtypes = [i64, i64, ci]
     lib.srwm_tape_row.restype = i64
     lib.srwm_backward_supported.argtypes = [i64, i64, ci, ci]

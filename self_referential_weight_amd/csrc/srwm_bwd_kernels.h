@@ -923,14 +923,15 @@ void srwm_bwd_wide_kernel(const float* __restrict__ WTin,
 }
 
 // dW0[h] = sum_b dWinit[b][h] (the gradient of the initial matrix shared over
-// the batch), summed in a fixed order b = 0, 1, ...
+// the batch), summed in a fixed order b = 0, 1, ...; with `accumulate` the sum
+// continues from dW0's value (a batch summed in slices, in order).
 __global__ __launch_bounds__(256) void srwm_sum_over_batch_kernel(const float* __restrict__ dWinit,
                                                                   float* __restrict__ dW0, int64_t B,
-                                                                  int64_t per_b)
+                                                                  int64_t per_b, int accumulate)
 {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= per_b) return;
-    float s = 0.f;
+    float s = accumulate ? dW0[i] : 0.f;
     for (int64_t b = 0; b < B; ++b) s += dWinit[b * per_b + i];
     dW0[i] = s;
 }

@@ -318,6 +318,9 @@ const char* srwm_strerror(int code)
     case SRWM_ERR_ALIAS: return "SRWM_ERR_ALIAS: an output buffer overlaps another buffer";
     case SRWM_ERR_HIP: return "SRWM_ERR_HIP: the HIP runtime rejected the launch";
     case SRWM_ERR_ARG: return "SRWM_ERR_ARG: invalid io_dtype, flag, n_lr, reset interval, variant or alignment";
+    case SRWM_ERR_SCRATCH:
+        return "SRWM_ERR_SCRATCH: one sequence's per-unit gradients (H*m*d_in floats) exceed the no-allocation "
+               "backward's scratch array";
     default: return "unknown srwm error code";
     }
 }

@@ -164,6 +164,24 @@ int main(void)
         EXPECT(srwm_backward(&a), SRWM_OK);
     }
 
+    /* srwm_backward_noalloc: validation before any HIP call */
+    {
+        srwm_backward_args_t a = bwd_args();
+        a.dW_init = NULL;
+        EXPECT(srwm_backward_noalloc(NULL), SRWM_ERR_NULL);
+        a.dW_init = F(DWI);
+        EXPECT(srwm_backward_noalloc(&a), SRWM_ERR_ARG);
+        a.dW_init = NULL, a.dW0 = NULL;
+        EXPECT(srwm_backward_noalloc(&a), SRWM_ERR_NULL);
+        a = bwd_args(), a.dW_init = NULL, a.H = 170, a.d_in = 128, a.d_out = 128, a.m = 388;
+        EXPECT(srwm_backward_noalloc(&a), SRWM_ERR_SCRATCH);
+        a = bwd_args(), a.dW_init = NULL, a.B = INT64_MAX / 2;
+        EXPECT(srwm_backward_noalloc(&a), SRWM_ERR_SHAPE);
+        a = bwd_args(), a.dW_init = NULL, a.H = 0;
+        EXPECT(srwm_backward_noalloc(&a), SRWM_OK);
+        EXPECT(srwm_backward_noalloc_scratch_bytes(), (int64_t)32 << 20);
+    }
+
     /* DeltaNet, SR-DeltaNet, the fast matrix alone */
     {
         srwm_deltanet_args_t a = dn_args();
@@ -245,7 +263,7 @@ int main(void)
         EXPECT(srwm_valu_probe(NULL, 4, 1, NULL), SRWM_ERR_NULL);
         EXPECT(srwm_lds_probe(NULL, 4, 1, NULL), SRWM_ERR_NULL);
         EXPECT(srwm_lds_probe((unsigned*)(uintptr_t)(Y + 4), 4, 1, NULL), SRWM_ERR_ARG);
-        for (int c = 0; c >= -8; --c)
+        for (int c = 0; c >= -9; --c)
             if (srwm_strerror(c) == NULL) ++failures;
         if (srwm_version() <= 0) ++failures;
     }

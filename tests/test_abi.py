@@ -10,7 +10,7 @@ from self_referential_weight_amd import _lib
 
 HEADER = Path(__file__).resolve().parents[1] / "include" / "srwm.h"
 
-OK, E_NULL, E_SHAPE, E_UNSUP, E_ALIAS, E_HIP, E_ARG = 0, -1, -2, -3, -4, -5, -6
+OK, E_NULL, E_SHAPE, E_UNSUP, E_ALIAS, E_HIP, E_ARG, E_SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7
 
 
 def declared_functions():
@@ -29,8 +29,8 @@ def test_header_symbols_exported():
 
 def test_version_and_strerror():
     lib = _lib.load()
-    assert lib.srwm_version() == 700
-    for code in (OK, E_NULL, E_SHAPE, E_UNSUP, E_ALIAS, E_HIP, E_ARG):
+    assert lib.srwm_version() == 800
+    for code in (OK, E_NULL, E_SHAPE, E_UNSUP, E_ALIAS, E_HIP, E_ARG, E_SCRATCH):
         assert _lib.strerror(code).startswith("SRWM_")
     assert "unknown" in _lib.strerror(-99)
 
@@ -260,6 +260,40 @@ def call_bwd(**kw):
 ])
 def test_backward_validation(kw, code):
     assert call_bwd(**kw) == code
+
+
+def call_bwd_noalloc(**kw):
+    base = dict(x=FAKE_X, W_T=FAKE_WT, tape=FAKE_TAPE, gy=FAKE_GY, gW_T=None, dx=FAKE_DX,
+                dW_init=None, dW0=FAKE_DW0, B=2, T=3, H=2, d_in=16, d_out=16, m=None,
+                io_dtype=0, apply_input_softmax=0, n_lr=4, stream=None)
+    base.update(kw)
+    if base["m"] is None:
+        base["m"] = base["d_out"] + 2 * base["d_in"] + base["n_lr"]
+    return _lib.load().srwm_backward_noalloc(ctypes.byref(_lib.BackwardArgs(**base)))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dW_init=FAKE_DWI), E_ARG),          # the per-unit gradients live in the library's scratch
+    (dict(dW0=None), E_NULL),                 # the one gradient this entry point returns
+    (dict(dx=None), E_NULL),
+    (dict(m=51), E_SHAPE),
+    (dict(d_in=32, d_out=32), E_UNSUP),
+    (dict(dx=FAKE_GY), E_ALIAS),
+    (dict(dW0=FAKE_TAPE + 16), E_ALIAS),
+    (dict(dW0=FAKE_DW0 + 4), E_ARG),
+    # one sequence's per-unit gradients (H*m*d_in floats) larger than the 32 MiB scratch
+    (dict(H=200, d_in=128, d_out=128), E_SCRATCH),
+    (dict(H=0, x=None, W_T=None, tape=None, gy=None, dx=None, dW0=None), OK),
+])
+def test_backward_noalloc_validation(kw, code):
+    assert call_bwd_noalloc(**kw) == code
+
+
+def test_backward_noalloc_scratch_size():
+    assert _lib.load().srwm_backward_noalloc_scratch_bytes() == 32 << 20
+    # the limit is one sequence's H*m*d_in floats: 168 heads of d = 128 fit, 169 do not
+    assert 168 * 388 * 128 * 4 <= 32 << 20 < 169 * 388 * 128 * 4
+    assert call_bwd_noalloc(H=169, d_in=128, d_out=128) == E_SCRATCH
 
 
 def test_backward_null_and_empty():
