@@ -550,15 +550,17 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
 }
 
 // ----------------------------------------------------------------------------
-// Backward pass for units whose W and adjoint Wh do not both fit in registers
-// (d = 128: 2 x 49,664 floats).  The same step as srwm_bwd_kernel, with three
+// Backward pass for units whose W and adjoint Wh do not both fit in the
+// registers of one workgroup with room for the step's vectors (d = 128:
+// 2 x 49,664 floats).  The same step as srwm_bwd_kernel, with these
 // differences:
 //   * W stays in registers (lane (rg, p): rows rg + G*r, columns [p*L, p*L+L));
-//     of Wh, register rows r < RL live in LDS and the rest in the unit's own
-//     rows of dWinit (L2-resident: the workloads of this shape have few
-//     units), each element read and written only by the lane that owns it, so
-//     every load follows that thread's own store.  The LDS rows are written to
-//     dWinit when the walk ends, which then holds dL/d(initial state).
+//     of Wh, register rows r < RL live in LDS (each element read and written
+//     only by the lane that owns it, so every load follows that thread's own
+//     store) and the rest in registers beside W.  Nothing of the state leaves
+//     the chip during the walk; dWinit is written once at the end.
+//   * each pass over the rows takes a row's inputs (a_t entry, zh entry, Wh
+//     row) as it reaches the row, so the step's vectors stay few;
 //   * the per-column phase gives each lane CPL = D_IN / 64 columns
 //     (j = lane + 64 c);
 //   * gy_t is staged one entry per thread.
@@ -588,8 +590,10 @@ void srwm_bwd_wide_kernel(const float* __restrict__ WTin,
     static_assert(D_OUT <= NT, "one thread per output");
     static_assert(L % 4 == 0, "16-byte pieces of Wh");
     static_assert((NW & (NW - 1)) == 0, "power-of-two waves");
-    // register rows of Wh kept in LDS: as many as fit beside the staging buffers
+    // register rows of Wh kept in LDS: as many as fit beside the staging
+    // buffers; the other R - RL rows are registers
     constexpr int RL = 7;
+    constexpr int RR = R - RL;
     static_assert(RL <= R, "LDS rows");
 
     __shared__ __attribute__((aligned(16))) float s_tape[3][TW];
@@ -614,26 +618,26 @@ void srwm_bwd_wide_kernel(const float* __restrict__ WTin,
     const int64_t x0 = ((int64_t)b * T * H + h) * D_IN;
     const int64_t y0 = ((int64_t)b * T * H + h) * D_OUT;
     const float* __restrict__ tp0 = tape + (int64_t)unit * T * TW;
-    float* __restrict__ whu = dWinit + (int64_t)unit * M * D_IN;  // this unit's Wh
+    float* __restrict__ whu = dWinit + (int64_t)unit * M * D_IN;  // this unit's Wh at the end
     const float* __restrict__ wtu = WTin + (int64_t)unit * M * D_IN;
-    // One register row of Wh (zeros for padding rows); the passes over Wh load
-    // row r+1 before row r is processed (measured: 132 -> 118 ms on the wide
-    // workload against fencing each row with a scheduling barrier).
+
+    // Wh register rows RL..R-1 (rows >= M are zero padding)
+    float whr[RR > 0 ? RR : 1][L];
     auto load_wh = [&](int r, float (&v)[L]) {
-        const int row = rg + G * r;
         if (r < RL) {
             load_f32<L>(&s_wh[r < RL ? r : 0][rg][p * L], v);
-        } else if (row < M) {
-            load_f32<L>(whu + row * D_IN + p * L, v);
         } else {
 #pragma unroll
-            for (int c = 0; c < L; ++c) v[c] = 0.f;
+            for (int c = 0; c < L; ++c) v[c] = whr[r < RL ? 0 : r - RL][c];
         }
     };
     auto store_wh = [&](int r, const float (&v)[L]) {
-        const int row = rg + G * r;
-        if (r < RL) store_f32<L>(&s_wh[r < RL ? r : 0][rg][p * L], v);
-        else if (row < M) store_f32<L>(whu + row * D_IN + p * L, v);
+        if (r < RL) {
+            store_f32<L>(&s_wh[r < RL ? r : 0][rg][p * L], v);
+        } else {
+#pragma unroll
+            for (int c = 0; c < L; ++c) whr[r < RL ? 0 : r - RL][c] = v[c];
+        }
     };
 
     auto rate = [](int r) constexpr {
@@ -767,47 +771,33 @@ void srwm_bwd_wide_kernel(const float* __restrict__ WTin,
         const float* __restrict__ gs = s_gy[slot];
         const int par = t & 1;
 
-        // ---- (A) undo the update of step t; ah (row sums of Wh kh), khh = Wh^T a,
-        // rh, eh = W^T rh.
-        float a[R], kt[L];
+        // ---- (A) row by row: undo the update of step t; ah (row sums of
+        // Wh kh) and rh = g ah; khh = Wh^T a, eh = W^T rh (column partials).
+        float kt[L];
+        load_f32<L>(tt + TL::KH_OFF + p * L, kt);
+        const float4 gv = *reinterpret_cast<const float4*>(tt + TL::G_OFF);
+        const float gate[4] = {gv.x, gv.y, gv.z, gv.w};
+        float khh[L], eh[L], rh[R];
+        float bp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < L; ++c) khh[c] = eh[c] = 0.f;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int row = rg + G * r;
             const float av = tt[row < M ? row : M - 1];  // clamped: padding rows read a real row, then 0
-            a[r] = row < M ? av : 0.f;
-        }
-        load_f32<L>(tt + TL::KH_OFF + p * L, kt);
-        const float4 gv = *reinterpret_cast<const float4*>(tt + TL::G_OFF);
-        const float gate[4] = {gv.x, gv.y, gv.z, gv.w};
-
-        float khh[L], ah[R];
-#pragma unroll
-        for (int c = 0; c < L; ++c) khh[c] = 0.f;
-        float whn[L];
-        load_wh(0, whn);
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
+            const float ar = row < M ? av : 0.f;
             float wh[L];
-#pragma unroll
-            for (int c = 0; c < L; ++c) wh[c] = whn[c];
-            if (r + 1 < R) load_wh(r + 1, whn);
+            load_wh(r, wh);
             float as = 0.f;
 #pragma unroll
             for (int c = 0; c < L; ++c) {
-                w[r][c] = fmaf(-a[r], kt[c], w[r][c]);
+                w[r][c] = fmaf(-ar, kt[c], w[r][c]);
                 as = fmaf(wh[c], kt[c], as);
-                khh[c] = fmaf(wh[c], a[r], khh[c]);
+                khh[c] = fmaf(wh[c], ar, khh[c]);
             }
-            ah[r] = group_sum<P>(as);
-        }
-        float bp[4] = {0.f, 0.f, 0.f, 0.f};
-        float rh[R], eh[L];
-#pragma unroll
-        for (int c = 0; c < L; ++c) eh[c] = 0.f;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            rh[r] = gate[rate(r)] * ah[r];
-            bp[rate(r)] = fmaf(ah[r], a[r], bp[rate(r)]);
+            const float ah = group_sum<P>(as);
+            rh[r] = gate[rate(r)] * ah;
+            bp[rate(r)] = fmaf(ah, ar, bp[rate(r)]);
 #pragma unroll
             for (int c = 0; c < L; ++c) eh[c] = fmaf(w[r][c], rh[r], eh[c]);
         }
@@ -829,12 +819,12 @@ void srwm_bwd_wide_kernel(const float* __restrict__ WTin,
 
         // ---- (B) per column (lane j = lane + 64 c): totals, dx of step t+1,
         // kbar, qbar, betah.
-        float khh_j[CPL], eh_j[CPL], uh1_j[CPL];
-        gather(par, khh_j, eh_j, uh1_j);
-        if (t + 1 < T && wave == ((t + 1) & (NW - 1))) store_dx(t + 1, uh1_j, u_next);
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) u_next[c] = us[lane + kWave * c];
         {
+            float khh_j[CPL], eh_j[CPL], uh1_j[CPL];
+            gather(par, khh_j, eh_j, uh1_j);
+            if (t + 1 < T && wave == ((t + 1) & (NW - 1))) store_dx(t + 1, uh1_j, u_next);
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) u_next[c] = us[lane + kWave * c];
             float bt[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) bt[c] = c < NLR ? s_bred[par][0][c] : 0.f;
@@ -868,20 +858,16 @@ void srwm_bwd_wide_kernel(const float* __restrict__ WTin,
         }
         wave_sync();
 
-        // ---- (C) uh of step t (column partials, reduced with step t-1); Wh update.
+        // ---- (C) row by row: uh of step t (column partials, reduced with
+        // step t-1); Wh += rh e^T + zh u^T.
         float ev[L], uv[L];
         load_f32<L>(tt + TL::E_OFF + p * L, ev);
         load_f32<L>(us + p * L, uv);
 #pragma unroll
         for (int c = 0; c < L; ++c) part[2][c] = 0.f;
-        load_wh(0, whn);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int row = rg + G * r;
-            float wh[L];
-#pragma unroll
-            for (int c = 0; c < L; ++c) wh[c] = whn[c];
-            if (r + 1 < R) load_wh(r + 1, whn);
             float zr;
             if (G * r < D_OUT) {
                 zr = gs[row];
@@ -889,6 +875,8 @@ void srwm_bwd_wide_kernel(const float* __restrict__ WTin,
                 const float zv = s_zh[wave][row < M ? row : M - 1];  // clamped as above
                 zr = row < M ? zv : 0.f;
             }
+            float wh[L];
+            load_wh(r, wh);
 #pragma unroll
             for (int c = 0; c < L; ++c) part[2][c] = fmaf(w[r][c], zr, part[2][c]);
 #pragma unroll
@@ -909,14 +897,13 @@ void srwm_bwd_wide_kernel(const float* __restrict__ WTin,
         gather(1, khh_j, eh_j, uh0_j);
         if (wave == 0) store_dx(0, uh0_j, u_next);
     }
-    // dWinit <- Wh = dL/d(initial state of this unit): its LDS rows (the
-    // others are there already).
+    // dWinit <- Wh = dL/d(initial state of this unit).
 #pragma unroll
-    for (int r = 0; r < RL; ++r) {
+    for (int r = 0; r < R; ++r) {
         const int row = rg + G * r;
         if (row < M) {
             float v[L];
-            load_f32<L>(&s_wh[r][rg][p * L], v);
+            load_wh(r, v);
             store_f32<L>(whu + row * D_IN + p * L, v);
         }
     }
