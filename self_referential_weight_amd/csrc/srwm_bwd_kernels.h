@@ -554,15 +554,20 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
 // registers of one workgroup with room for the step's vectors (d = 128:
 // 2 x 49,664 floats).  The same step as srwm_bwd_kernel, with these
 // differences:
-//   * W stays in registers (lane (rg, p): rows rg + G*r, columns [p*L, p*L+L));
-//     of Wh, register rows r < RL live in LDS (each element read and written
-//     only by the lane that owns it, so every load follows that thread's own
-//     store) and the rest in registers beside W.  Nothing of the state leaves
-//     the chip during the walk; dWinit is written once at the end.
+//   * the main rows (y, k, q: MAIN = d_out + 2 d_in of them, RM register rows
+//     of G) are spread as in srwm_bwd_kernel: lane (rg, p) holds rows
+//     rg + G*r, columns [p*L, p*L+L).  W stays in registers; of Wh, register
+//     rows r < RL live in LDS and the rest in registers beside W.  The rate
+//     rows (n_lr of them) sit in LDS, W and Wh, and are processed by wave 0,
+//     whose lanes rg < n_lr take them as a last row (rows MAIN + rg): no
+//     wave carries padding rows.  Every LDS element of the state is read and
+//     written only by the lane that owns it, so every load follows that
+//     thread's own store.  Nothing of the state leaves the chip during the
+//     walk; dWinit is written once at the end.
 //   * each pass over the rows takes a row's inputs (a_t entry, zh entry, Wh
 //     row) as it reaches the row, so the step's vectors stay few;
 //   * the per-column phase gives each lane CPL = D_IN / 64 columns
-//     (j = lane + 64 c);
+//     (j = lane + 64 c); each wave keeps only the zh entries of its own rows;
 //   * gy_t is staged one entry per thread.
 // No reset ablation (Wh has no second buffer to gather the windows' shares).
 template <int D_IN, int D_OUT, int NW, int P, int NLR, bool RESET>
@@ -579,31 +584,38 @@ void srwm_bwd_wide_kernel(const float* __restrict__ WTin,
     constexpr int MAIN = D_OUT + 2 * D_IN;
     constexpr int L = D_IN / P;
     constexpr int G = NT / P;
-    constexpr int R = (M + G - 1) / G;
+    constexpr int RM = MAIN / G;       // register rows of the main rows
+    constexpr int RG = kWave / P;      // row groups per wave
     constexpr int CPL = D_IN / kWave;  // columns per lane in the per-column phase
     using TL = TapeLayout<M, D_IN>;
     using CX = ColExchange<P, L>;
     constexpr int TW = TL::ROW;
-    constexpr int TPL = (TW + NT - 1) / NT;
     static_assert(D_IN % kWave == 0 && D_OUT % kWave == 0, "whole columns per lane");
-    static_assert(D_IN % P == 0 && D_IN % G == 0 && D_OUT % G == 0, "row blocks must align with row groups");
+    static_assert(D_IN % P == 0 && D_IN % G == 0 && D_OUT % G == 0 && MAIN % G == 0,
+                  "row blocks must align with row groups");
     static_assert(D_OUT <= NT, "one thread per output");
     static_assert(L % 4 == 0, "16-byte pieces of Wh");
     static_assert((NW & (NW - 1)) == 0, "power-of-two waves");
+    static_assert(RG >= 4, "wave 0 holds the rate rows as its row groups 0..n_lr-1");
     // register rows of Wh kept in LDS: as many as fit beside the staging
-    // buffers; the other R - RL rows are registers
+    // buffers; the other RM - RL rows are registers
     constexpr int RL = 7;
-    constexpr int RR = R - RL;
-    static_assert(RL <= R, "LDS rows");
+    constexpr int RR = RM - RL;
+    static_assert(RL <= RM, "LDS rows");
+    // zh entries a wave reads: its rows rg + G r for r >= D_OUT / G (the k, q
+    // rows), RG per register row, and for wave 0 the n_lr rate rows
+    constexpr int RZ0 = D_OUT / G;
+    constexpr int NZ = (RM - RZ0) * RG + 4;
 
     __shared__ __attribute__((aligned(16))) float s_tape[3][TW];
     __shared__ __attribute__((aligned(16))) float s_gy[3][D_OUT];
     __shared__ __attribute__((aligned(16))) float s_red[2][NW][3][D_IN];
     __shared__ __attribute__((aligned(16))) float s_bred[2][NW][4];
-    __shared__ __attribute__((aligned(16))) float s_zh[NW][M];
+    __shared__ __attribute__((aligned(16))) float s_zh[NW][NZ];
     __shared__ __attribute__((aligned(16))) float s_wh[RL][G][D_IN];
-    static_assert(sizeof(float) * (3 * TW + 3 * D_OUT + 2 * NW * 3 * D_IN + 2 * NW * 4 + NW * M +
-                                   RL * G * D_IN) <= 160 * 1024, "LDS");
+    __shared__ __attribute__((aligned(16))) float s_wb[2][4][D_IN];  // rate rows: [0] W, [1] Wh
+    static_assert(sizeof(float) * (3 * TW + 3 * D_OUT + 2 * NW * 3 * D_IN + 2 * NW * 4 + NW * NZ +
+                                   RL * G * D_IN + 8 * D_IN) <= 160 * 1024, "LDS");
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -620,12 +632,35 @@ void srwm_bwd_wide_kernel(const float* __restrict__ WTin,
     const float* __restrict__ tp0 = tape + (int64_t)unit * T * TW;
     float* __restrict__ whu = dWinit + (int64_t)unit * M * D_IN;  // this unit's Wh at the end
     const float* __restrict__ wtu = WTin + (int64_t)unit * M * D_IN;
+    const int rgw = rg - RG * wave;  // row group within the wave
+    // the rate row of this lane when wave == 0 (rows >= n_lr: zero rows)
+    const bool brow = wave == 0 && rg < NLR;
 
-    // Wh register rows RL..R-1 (rows >= M are zero padding)
+    // Wh register rows RL..RM-1
     float whr[RR > 0 ? RR : 1][L];
+    // A lane's L floats of an LDS row are stored as L/4 16-byte pieces, piece
+    // q of lane p at 16-byte slot q*P + p of the row group's D_IN floats: the
+    // P lanes of a row group read or write one contiguous span per piece (no
+    // bank conflicts), not pieces 4*L bytes apart.
+    static_assert(L % 4 == 0 && D_IN == P * L, "16-byte pieces");
+    auto lds_get = [&](const float* __restrict__ seg, float (&v)[L]) {
+#pragma unroll
+        for (int q = 0; q < L / 4; ++q) {
+            const float4 f = *reinterpret_cast<const float4*>(seg + 4 * (q * P + p));
+            v[4 * q] = f.x;
+            v[4 * q + 1] = f.y;
+            v[4 * q + 2] = f.z;
+            v[4 * q + 3] = f.w;
+        }
+    };
+    auto lds_put = [&](float* __restrict__ seg, const float (&v)[L]) {
+#pragma unroll
+        for (int q = 0; q < L / 4; ++q)
+            *reinterpret_cast<float4*>(seg + 4 * (q * P + p)) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    };
     auto load_wh = [&](int r, float (&v)[L]) {
         if (r < RL) {
-            load_f32<L>(&s_wh[r < RL ? r : 0][rg][p * L], v);
+            lds_get(&s_wh[r < RL ? r : 0][rg][0], v);
         } else {
 #pragma unroll
             for (int c = 0; c < L; ++c) v[c] = whr[r < RL ? 0 : r - RL][c];
@@ -633,7 +668,7 @@ void srwm_bwd_wide_kernel(const float* __restrict__ WTin,
     };
     auto store_wh = [&](int r, const float (&v)[L]) {
         if (r < RL) {
-            store_f32<L>(&s_wh[r < RL ? r : 0][rg][p * L], v);
+            lds_put(&s_wh[r < RL ? r : 0][rg][0], v);
         } else {
 #pragma unroll
             for (int c = 0; c < L; ++c) whr[r < RL ? 0 : r - RL][c] = v[c];
@@ -642,44 +677,55 @@ void srwm_bwd_wide_kernel(const float* __restrict__ WTin,
 
     auto rate = [](int r) constexpr {
         const int row = G * r;
-        return NLR == 1 ? 0 : row < D_OUT ? 0 : row < D_OUT + D_IN ? 1 : row < MAIN ? 2 : 3;
+        return NLR == 1 ? 0 : row < D_OUT ? 0 : row < D_OUT + D_IN ? 1 : 2;
     };
+    constexpr int RATE_B = NLR == 1 ? 0 : 3;
 
-    // W <- W_T (rows >= M are zero padding); Wh <- dL/dW_T (or 0).
-    float w[R][L];
+    // W <- W_T; Wh <- dL/dW_T (or 0).
+    float w[RM][L];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
+    for (int r = 0; r < RM; ++r) {
         const int row = rg + G * r;
         float v[L];
+        load_f32<L>(wtu + row * D_IN + p * L, w[r]);
+        if (gWT != nullptr) {
+            load_f32<L>(gWT + (int64_t)unit * M * D_IN + row * D_IN + p * L, v);
+        } else {
 #pragma unroll
-        for (int c = 0; c < L; ++c) w[r][c] = v[c] = 0.f;
-        if (row < M) {
-            load_f32<L>(wtu + row * D_IN + p * L, w[r]);
-            if (gWT != nullptr) load_f32<L>(gWT + (int64_t)unit * M * D_IN + row * D_IN + p * L, v);
+            for (int c = 0; c < L; ++c) v[c] = 0.f;
         }
         store_wh(r, v);
     }
+    if (wave == 0) {
+        float wv[L], hv[L];
+#pragma unroll
+        for (int c = 0; c < L; ++c) wv[c] = hv[c] = 0.f;
+        if (rg < NLR) {
+            load_f32<L>(wtu + (MAIN + rg) * D_IN + p * L, wv);
+            if (gWT != nullptr) load_f32<L>(gWT + (int64_t)unit * M * D_IN + (MAIN + rg) * D_IN + p * L, hv);
+        }
+        lds_put(&s_wb[0][rg][0], wv);
+        lds_put(&s_wb[1][rg][0], hv);
+    }
 
-    // Step inputs (the tape row, which holds u_t, and gy_t), fetched two
-    // steps ahead into registers, staged one step ahead into the LDS ring.
-    float tnext[TPL];
-    float gnext = 0.f;
-    auto fetch = [&](int t) {
+    // Step inputs (the tape row, which holds u_t, and gy_t) are copied two
+    // steps ahead straight from global memory into the LDS ring (no
+    // registers): the rows in 64-dword pieces, piece k by wave k mod NW (gy's
+    // two pieces by the waves with fewest tape pieces), each lane one dword.
+    constexpr int NPC = (TW + kWave - 1) / kWave;  // pieces of a tape row
+    constexpr int NGC = D_OUT / kWave;             // pieces of a gy row
+    static_assert(NPC <= 2 * NW && NPC % NW + NGC <= NW, "one or two tape pieces and at most one gy piece per wave");
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
+    auto fetch = [&](int t, int slot) {
         const float* __restrict__ tpp = tp0 + (int64_t)t * TW;
 #pragma unroll
-        for (int i = 0; i < TPL; ++i) {
-            const int j = tid + NT * i;
-            tnext[i] = (j < TW) ? tpp[j] : 0.f;
+        for (int i = 0; i < 2; ++i) {
+            const int k = wu + NW * i;
+            if (k < NPC && kWave * k + lane < TW) copy_dword_to_lds(tpp + kWave * k + lane, &s_tape[slot][kWave * k]);
         }
-        if (tid < D_OUT) gnext = gy[y0 + (int64_t)t * y_step + tid];
-    };
-    auto stage = [&](int slot) {
-#pragma unroll
-        for (int i = 0; i < TPL; ++i) {
-            const int j = tid + NT * i;
-            if (j < TW) s_tape[slot][j] = tnext[i];
-        }
-        if (tid < D_OUT) s_gy[slot][tid] = gnext;
+        const int kg = wu - NPC % NW;  // gy piece of the waves after those with two tape pieces
+        if (kg >= 0 && kg < NGC)
+            copy_dword_to_lds(gy + y0 + (int64_t)t * y_step + kWave * kg + lane, &s_gy[slot][kWave * kg]);
     };
 
     float part[3][L];
@@ -758,9 +804,9 @@ void srwm_bwd_wide_kernel(const float* __restrict__ WTin,
     for (int c = 0; c < CPL; ++c) u_next[c] = 0.f;
 
     if (T > 0) {
-        fetch(T - 1);
-        stage((T - 1) % 3);
-        if (T > 1) fetch(T - 2);
+        fetch(T - 1, (T - 1) % 3);
+        if (T > 1) fetch(T - 2, (T - 2) % 3);
+        wait_vmem();
         __syncthreads();
     }
 
@@ -777,29 +823,73 @@ void srwm_bwd_wide_kernel(const float* __restrict__ WTin,
         load_f32<L>(tt + TL::KH_OFF + p * L, kt);
         const float4 gv = *reinterpret_cast<const float4*>(tt + TL::G_OFF);
         const float gate[4] = {gv.x, gv.y, gv.z, gv.w};
-        float khh[L], eh[L], rh[R];
+        float khh[L], eh[L], rh[RM];
+        float rhb = 0.f;  // the rate row's rh (wave 0)
         float bp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < L; ++c) khh[c] = eh[c] = 0.f;
+        // (A1) per row: undo, the row's partial of ah, khh; the next row's
+        // Wh and a_t entry are requested before this row is processed, and a
+        // scheduling fence per row keeps the loads from running further ahead
+        // (each would hold a row of registers).
+        {
+            float whn[L];
+            load_wh(0, whn);
+            float an = tt[rg];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int row = rg + G * r;
-            const float av = tt[row < M ? row : M - 1];  // clamped: padding rows read a real row, then 0
-            const float ar = row < M ? av : 0.f;
-            float wh[L];
-            load_wh(r, wh);
+            for (int r = 0; r < RM; ++r) {
+                float wh[L];
+#pragma unroll
+                for (int c = 0; c < L; ++c) wh[c] = whn[c];
+                const float ar = an;
+                if (r + 1 < RM) {
+                    load_wh(r + 1, whn);
+                    an = tt[rg + G * (r + 1)];
+                }
+                float as = 0.f;
+#pragma unroll
+                for (int c = 0; c < L; ++c) {
+                    w[r][c] = fmaf(-ar, kt[c], w[r][c]);
+                    as = fmaf(wh[c], kt[c], as);
+                    khh[c] = fmaf(wh[c], ar, khh[c]);
+                }
+                rh[r] = as;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        // (A2) the row sums, all rows' DPP chains side by side; rh = g ah
+        // (a_t entries read again from LDS rather than held in registers)
+#pragma unroll
+        for (int r = 0; r < RM; ++r) {
+            const float ah = group_sum<P>(rh[r]);
+            rh[r] = gate[rate(r)] * ah;
+            bp[rate(r)] = fmaf(ah, tt[rg + G * r], bp[rate(r)]);
+        }
+        // (A3) eh = W^T rh (W after the undo)
+#pragma unroll
+        for (int r = 0; r < RM; ++r)
+#pragma unroll
+            for (int c = 0; c < L; ++c) eh[c] = fmaf(w[r][c], rh[r], eh[c]);
+        if (wave == 0) {
+            // the rate rows (zero rows for rg >= n_lr)
+            const float av = tt[MAIN + (rg < NLR ? rg : 0)];
+            const float ar = rg < NLR ? av : 0.f;
+            float wv[L], wh[L];
+            lds_get(&s_wb[0][rg][0], wv);
+            lds_get(&s_wb[1][rg][0], wh);
             float as = 0.f;
 #pragma unroll
             for (int c = 0; c < L; ++c) {
-                w[r][c] = fmaf(-ar, kt[c], w[r][c]);
+                wv[c] = fmaf(-ar, kt[c], wv[c]);
                 as = fmaf(wh[c], kt[c], as);
                 khh[c] = fmaf(wh[c], ar, khh[c]);
             }
+            lds_put(&s_wb[0][rg][0], wv);
             const float ah = group_sum<P>(as);
-            rh[r] = gate[rate(r)] * ah;
-            bp[rate(r)] = fmaf(ah, ar, bp[rate(r)]);
+            rhb = gate[RATE_B] * ah;
+            bp[RATE_B] = fmaf(ah, ar, bp[RATE_B]);
 #pragma unroll
-            for (int c = 0; c < L; ++c) eh[c] = fmaf(w[r][c], rh[r], eh[c]);
+            for (int c = 0; c < L; ++c) eh[c] = fmaf(wv[c], rhb, eh[c]);
         }
 #pragma unroll
         for (int c = 0; c < 4; ++c) bp[c] = p == 0 ? bp[c] : 0.f;
@@ -811,14 +901,15 @@ void srwm_bwd_wide_kernel(const float* __restrict__ WTin,
         exchange(par, bp);
 
         const int slot_prev = slot == 0 ? 2 : slot - 1;
-        if (t > 0) {
-            stage(slot_prev);
-            if (t > 1) fetch(t - 2);
-        }
+        // step t-1's inputs (copied during step t+1) are in LDS for every wave
+        // after this barrier; then step t-2's are requested into the slot step
+        // t+1 used
+        wait_vmem();
         __syncthreads();
+        if (t > 1) fetch(t - 2, slot_prev == 0 ? 2 : slot_prev - 1);
 
         // ---- (B) per column (lane j = lane + 64 c): totals, dx of step t+1,
-        // kbar, qbar, betah.
+        // kbar, qbar, betah; each wave keeps the zh entries of its own rows.
         {
             float khh_j[CPL], eh_j[CPL], uh1_j[CPL];
             gather(par, khh_j, eh_j, uh1_j);
@@ -847,13 +938,18 @@ void srwm_bwd_wide_kernel(const float* __restrict__ WTin,
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
                 const int j = lane + kWave * c;
-                s_zh[wave][D_OUT + j] = kh_j[c] * (kb[c] - sk);
-                s_zh[wave][D_OUT + D_IN + j] = qh_j[c] * (eh_j[c] - sq);
+                // rows D_OUT + j (kbar) and D_OUT + D_IN + j (qbar): row group
+                // j mod G, register rows RZ0 + j / G and RZ0 + (D_IN + j) / G
+                const int jg = j % G;
+                if (jg / RG == wave) {
+                    s_zh[wave][(j / G) * RG + jg % RG] = kh_j[c] * (kb[c] - sk);
+                    s_zh[wave][((D_IN + j) / G) * RG + jg % RG] = qh_j[c] * (eh_j[c] - sq);
+                }
             }
-            if (lane < NLR) {
+            if (wave == 0 && lane < NLR) {
                 const float bv = lane == 0 ? bt[0] : lane == 1 ? bt[1] : lane == 2 ? bt[2] : bt[3];
                 const float gl = lane == 0 ? gate[0] : lane == 1 ? gate[1] : lane == 2 ? gate[2] : gate[3];
-                s_zh[wave][MAIN + lane] = (1.f - gl) * bv;
+                s_zh[0][NZ - 4 + lane] = (1.f - gl) * bv;
             }
         }
         wave_sync();
@@ -865,23 +961,37 @@ void srwm_bwd_wide_kernel(const float* __restrict__ WTin,
         load_f32<L>(us + p * L, uv);
 #pragma unroll
         for (int c = 0; c < L; ++c) part[2][c] = 0.f;
+        {
+            // per row, with the next row's Wh requested first (fenced as in A1)
+            float whn[L];
+            load_wh(0, whn);
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int row = rg + G * r;
-            float zr;
-            if (G * r < D_OUT) {
-                zr = gs[row];
-            } else {
-                const float zv = s_zh[wave][row < M ? row : M - 1];  // clamped as above
-                zr = row < M ? zv : 0.f;
+            for (int r = 0; r < RM; ++r) {
+                const int row = rg + G * r;
+                const float zr = r < RZ0 ? gs[row] : s_zh[wave][(r < RZ0 ? 0 : r - RZ0) * RG + rgw];
+                float wh[L];
+#pragma unroll
+                for (int c = 0; c < L; ++c) wh[c] = whn[c];
+                if (r + 1 < RM) load_wh(r + 1, whn);
+#pragma unroll
+                for (int c = 0; c < L; ++c) part[2][c] = fmaf(w[r][c], zr, part[2][c]);
+#pragma unroll
+                for (int c = 0; c < L; ++c) wh[c] = fmaf(rh[r], ev[c], fmaf(zr, uv[c], wh[c]));
+                store_wh(r, wh);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            float wh[L];
-            load_wh(r, wh);
+        }
+        if (wave == 0) {
+            const float zv = s_zh[0][NZ - 4 + (rg < NLR ? rg : 0)];
+            const float zr = rg < NLR ? zv : 0.f;
+            float wv[L], wh[L];
+            lds_get(&s_wb[0][rg][0], wv);
+            lds_get(&s_wb[1][rg][0], wh);
 #pragma unroll
-            for (int c = 0; c < L; ++c) part[2][c] = fmaf(w[r][c], zr, part[2][c]);
+            for (int c = 0; c < L; ++c) part[2][c] = fmaf(wv[c], zr, part[2][c]);
 #pragma unroll
-            for (int c = 0; c < L; ++c) wh[c] = fmaf(rh[r], ev[c], fmaf(zr, uv[c], wh[c]));
-            store_wh(r, wh);  // padding rows stay zero: rh = zr = 0 there
+            for (int c = 0; c < L; ++c) wh[c] = fmaf(rhb, ev[c], fmaf(zr, uv[c], wh[c]));
+            lds_put(&s_wb[1][rg][0], wh);
         }
         slot = slot_prev;
     }
@@ -899,13 +1009,16 @@ void srwm_bwd_wide_kernel(const float* __restrict__ WTin,
     }
     // dWinit <- Wh = dL/d(initial state of this unit).
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
+    for (int r = 0; r < RM; ++r) {
         const int row = rg + G * r;
-        if (row < M) {
-            float v[L];
-            load_wh(r, v);
-            store_f32<L>(whu + row * D_IN + p * L, v);
-        }
+        float v[L];
+        load_wh(r, v);
+        store_f32<L>(whu + row * D_IN + p * L, v);
+    }
+    if (brow) {
+        float v[L];
+        lds_get(&s_wb[1][rg][0], v);
+        store_f32<L>(whu + (MAIN + rg) * D_IN + p * L, v);
     }
 }
 

@@ -306,6 +306,21 @@ __device__ __forceinline__ void wave_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Asynchronous copy of one dword per active lane from global memory straight
+// into LDS (gfx950 global_load_lds_dword): lane i of the wave writes
+// lds_base[i], lds_base uniform over the wave.  The copy is tracked by vmcnt:
+// wait_vmem() before the workgroup barrier after which the LDS words are read.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void global_void_t;
+__device__ __forceinline__ void copy_dword_to_lds(const float* src_lane, float* lds_base)
+{
+    __builtin_amdgcn_global_load_lds((global_void_t*)(src_lane), (lds_void_t*)(lds_base), 4, 0, 0);
+}
+
+// s_waitcnt vmcnt(0): every vector memory operation of this wave has completed
+// (expcnt and lgkmcnt left at their maxima).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Keep v materialised in every lane at this point: a value that only some
 // lanes store afterwards would otherwise have its last reduction step sunk
 // into the store's branch, where the DPP add can no longer be fused (an extra
