@@ -232,6 +232,15 @@ __device__ __forceinline__ float exp_f32(float x)
     return __builtin_amdgcn_exp2f(x * 1.44269504088896340736f);
 }
 
+// e^(x - m) given ms = m log2(e): 2^(x log2 e - ms), the shift and the scale
+// in one multiply-add.
+__device__ __forceinline__ float exp_shifted(float x, float ms)
+{
+    return __builtin_amdgcn_exp2f(fmaf(x, 1.44269504088896340736f, -ms));
+}
+
+__device__ __forceinline__ float log2e_scaled(float m) { return m * 1.44269504088896340736f; }
+
 // 1/x on the hardware reciprocal (v_rcp_f32, 1 ulp).
 __device__ __forceinline__ float rcp_f32(float x) { return __builtin_amdgcn_rcpf(x); }
 

@@ -100,11 +100,11 @@ __device__ __forceinline__ void wave_addresses(const float* __restrict__ k, cons
         v[i] = (j < D) ? src[j] : -INFINITY;
         mx = fmax2(mx, v[i]);
     }
-    mx = half_max(mx);
+    const float ms = log2e_scaled(half_max(mx));
 #pragma unroll
     for (int i = 0; i < EPH; ++i) {
         const int j = hl + 32 * i;
-        v[i] = (j < D) ? exp_f32(v[i] - mx) : 0.f;
+        v[i] = (j < D) ? exp_shifted(v[i], ms) : 0.f;
     }
     float s = v[0];  // (not 0 + v[0]: the compiler keeps that add, as -0 + 0 = +0)
 #pragma unroll
@@ -245,11 +245,11 @@ struct XStage {
             float mx = v[0];
 #pragma unroll
             for (int i = 1; i < E; ++i) mx = fmax2(mx, v[i]);
-            mx = group_max<LR>(mx);
+            const float ms = log2e_scaled(group_max<LR>(mx));
             float sum = 0.f;
 #pragma unroll
             for (int i = 0; i < E; ++i) {
-                v[i] = exp_f32(v[i] - mx);
+                v[i] = exp_shifted(v[i], ms);
                 sum += v[i];
             }
             const float inv = rcp_f32(group_sum<LR>(sum));
@@ -425,15 +425,13 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
 #pragma unroll
                     for (int r = 0; r < R; ++r) keep(acc[r]);
                 }
-                // All P lanes of a row group hold the same sums; lane p stores
-                // registers r = p, p+P, ... (one LDS store per P registers).
+                // All P lanes of a row group hold the same sums and every one
+                // stores them (the same word from P lanes): stores at constant
+                // offsets from one address, no per-lane selection of a register.
 #pragma unroll
-                for (int r0 = 0; r0 < R; r0 += P) {
-                    float v = acc[r0];
-#pragma unroll
-                    for (int q = 1; q < P && r0 + q < R; ++q) v = (p == q) ? acc[r0 + q] : v;
-                    const int row = rg + G * (r0 + p);
-                    if ((r0 + P <= R || r0 + p < R) && (Gm::ALIGNED || row < ROWS)) zt[row] = v;
+                for (int r = 0; r < R; ++r) {
+                    const int row = rg + G * r;
+                    if (Gm::ALIGNED || row < ROWS) zt[row] = acc[r];
                 }
                 if constexpr (BETA_SEP) {
                     if (wave == 0) {
@@ -495,12 +493,9 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
                     // a_t: the tape row buffer (one wave) or the tape itself
                     float* __restrict__ ta = TAPE_LDS ? s_tr : tp;
 #pragma unroll
-                    for (int r0 = 0; r0 < R; r0 += P) {
-                        float v = acc[r0];
-#pragma unroll
-                        for (int q = 1; q < P && r0 + q < R; ++q) v = (p == q) ? acc[r0 + q] : v;
-                        const int row = rg + G * (r0 + p);
-                        if ((r0 + P <= R || r0 + p < R) && row < ROWS) ta[row] = v;
+                    for (int r = 0; r < R; ++r) {
+                        const int row = rg + G * r;
+                        if (row < ROWS) ta[row] = acc[r];  // the same word from all P lanes of the row
                     }
                     if constexpr (BETA_SEP) {
                         if (wave == 0 && (lane & 15) == 0 && brow < NLR) ta[MAIN + brow] = accb;
