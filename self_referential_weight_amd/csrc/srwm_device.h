@@ -22,10 +22,14 @@ constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within 8
 constexpr int kDppMirror = 0x140;     // lane i <- lane 15-i within 16
 
+// bound_ctrl is set: every source lane the DPP patterns used here read
+// (quad_perm, row mirrors and rotations, row_newbcast) is valid, so the old
+// value is never used, and the compiler need not write it to the
+// destination before each move.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v)
 {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
 // Sum over aligned groups of P adjacent lanes (P | 16); every lane of the
@@ -88,7 +92,7 @@ __device__ __forceinline__ float from_order_key(int k)
 template <int CTRL>
 __device__ __forceinline__ int dpp_i(int v)
 {
-    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
 }
 
 template <int P>
