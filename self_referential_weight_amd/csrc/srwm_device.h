@@ -264,6 +264,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f)
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// Two floats to bf16 in one conversion (round to nearest even, as
+// f32_to_bf16): a in the low half, b in the high half.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b)
+{
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
 // Load N consecutive floats (16-byte aligned when N % 4 == 0).
 template <int N>
 __device__ __forceinline__ void load_f32(const float* __restrict__ src, float (&dst)[N])

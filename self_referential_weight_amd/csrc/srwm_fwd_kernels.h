@@ -378,6 +378,201 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
 
     // The wave that stores y_t.
     constexpr int WAVE_AUX = NW >= 2 ? 1 : 0;
+    // One-wave units take y_t and the learning rates straight from the
+    // registers of the projection: every lane holds whole row sums of the y
+    // rows (registers r < D_OUT / G) and DPP row i of the rate rows holds rate
+    // row i's sum, so neither goes through LDS.
+    constexpr bool Y_REG = NW == 1 && Gm::ALIGNED;
+    constexpr bool G_REG = NW == 1 && BETA_SEP;
+    constexpr int RY = D_OUT / G;  // y registers (Y_REG)
+
+    int until_reset = reset_interval;  // steps left before the next reset
+    (void)until_reset;
+
+    // One step t, reading u_t at urow; PAR = t & 1 picks the z buffer (the
+    // chunk length is even, so it is the parity of the step within its chunk).
+    auto step = [&](const int t, const float* __restrict__ urow, auto par) {
+        constexpr int PAR = decltype(par)::value;
+        if constexpr (RESET) {
+            // Reset ablation of the review page (Sec. 4.5): before every
+            // step t > 0 with t % R == 0 the state returns to W0.
+            if (reset_interval > 0) {
+                if (until_reset == 0) {
+                    if constexpr (TAPE) {
+                        // the backward pass restarts window t/R - 1 from its end state
+                        const int nres = (T - 1) / reset_interval;
+                        store_w(wstates + ((int64_t)unit * nres + (t / reset_interval - 1)) * M * D_IN);
+                    }
+                    load_w0();
+                    until_reset = reset_interval;
+                }
+                --until_reset;
+            }
+        }
+        // ---- (A) Eq. (1): z = W u.
+        float* __restrict__ zt = s_z[PAR];
+        float acc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = 0.f;
+        stream_lds<L>(urow + p * L, [&](int c, float uc) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[r] = fmaf(w[r][c], uc, acc[r]);
+        });
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = group_sum<P>(acc[r]);
+        if constexpr (KEEP_SUMS) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) keep(acc[r]);
+        }
+        // All P lanes of a row group hold the same sums and every one
+        // stores them (the same word from P lanes): stores at constant
+        // offsets from one address, no per-lane selection of a register.
+#pragma unroll
+        for (int r = (Y_REG ? RY : 0); r < R; ++r) {
+            const int row = rg + G * r;
+            if (Gm::ALIGNED || row < ROWS) zt[row] = acc[r];
+        }
+        if constexpr (Y_REG) {
+            // y_t rows rg + G*r, r < RY, from every lane of the row group
+            const int64_t yo = y0 + (int64_t)t * y_step + rg;
+            if constexpr (BF16) {
+                uint16_t* __restrict__ yb = reinterpret_cast<uint16_t*>(yv) + yo;
+#pragma unroll
+                for (int r = 0; r + 1 < RY; r += 2) {
+                    const uint32_t pk = f32x2_to_bf16x2(acc[r], acc[r + 1]);
+                    yb[G * r] = static_cast<uint16_t>(pk);
+                    yb[G * (r + 1)] = static_cast<uint16_t>(pk >> 16);
+                }
+                if constexpr (RY % 2 == 1) yb[G * (RY - 1)] = f32_to_bf16(acc[RY - 1]);
+            } else {
+                float* __restrict__ yf = reinterpret_cast<float*>(yv) + yo;
+#pragma unroll
+                for (int r = 0; r < RY; ++r) yf[G * r] = acc[r];
+            }
+        }
+        float gb = 0.f;  // G_REG: the gate of rate row brow, in DPP row brow
+        if constexpr (BETA_SEP) {
+            if (wave == 0) {
+                float accb = 0.f;
+                stream_lds<LB>(urow + bcol, [&](int c, float uc) { accb = fmaf(wb[c], uc, accb); });
+                accb = group_sum<16>(accb);
+                if constexpr (G_REG) {
+                    gb = sigmoid_f32(accb);
+                    if constexpr (TAPE_LDS) {
+                        if ((lane & 15) == 0) s_tr[TL::G_OFF + brow] = brow < NLR ? gb : 0.f;
+                    }
+                } else {
+                    if constexpr (KEEP_SUMS) keep(accb);
+                    if ((lane & 15) == 0 && brow < NLR) zt[MAIN + brow] = accb;
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- (B) phi(k), phi(q), sigma(beta), computed by every wave for
+        // itself (identical bits in every wave); y_t from W_{t-1}.
+        wave_addresses<D_IN>(zt + D_OUT, zt + D_OUT + D_IN, khs, es, lane);
+        float gl = 0.f, g0, g1, g2, g3;
+        if constexpr (G_REG) {
+            g0 = readlane(gb, 0);
+            if constexpr (NLR == 4) {
+                g1 = readlane(gb, 16);
+                g2 = readlane(gb, 32);
+                g3 = readlane(gb, 48);
+            } else {
+                g1 = g2 = g3 = g0;
+            }
+        } else {
+            gl = sigmoid_f32(zt[MAIN + (NLR == 4 ? (lane & 3) : 0)]);
+            g0 = readlane(gl, 0);
+            g1 = readlane(gl, 1);
+            g2 = readlane(gl, 2);
+            g3 = readlane(gl, 3);
+        }
+        if constexpr (!Y_REG) {
+            if (wave == WAVE_AUX) store_y<D_OUT, BF16>(yv, y0 + (int64_t)t * y_step, zt, lane);
+        }
+        wave_sync();
+        const float* __restrict__ khw = khs;
+        const float* __restrict__ ew = es;
+
+        // ---- (C) Eq. (2)/(4) fused: W (qh - kh) = v - vb, times the gate.
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = 0.f;
+        stream_lds<L>(ew + p * L, [&](int c, float ec) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[r] = fmaf(w[r][c], ec, acc[r]);
+        });
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float gate;
+            if constexpr (Gm::ALIGNED) {
+                const int bk = Gm::rate_of_reg(r);
+                gate = bk == 0 ? g0 : bk == 1 ? g1 : bk == 2 ? g2 : g3;
+            } else {
+                const int bk = rate_of_row<NLR>(rg + G * r, D_IN, D_OUT);
+                gate = bk == 0 ? g0 : bk == 1 ? g1 : bk == 2 ? g2 : g3;
+            }
+            acc[r] = gate * group_sum<P>(acc[r]);
+        }
+        if constexpr (KEEP_SUMS) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) keep(acc[r]);
+        }
+        float accb = 0.f;
+        if constexpr (BETA_SEP) {
+            if (wave == 0) {
+                stream_lds<LB>(ew + bcol, [&](int c, float ec) { accb = fmaf(wb[c], ec, accb); });
+                accb = g3 * group_sum<16>(accb);
+            }
+        }
+        if constexpr (TAPE) {
+            // Tape for the backward pass: a_t, phi(k_t) (enough to undo the
+            // update, W_{t-1} = W_t - a_t phi(k_t)^T), phi(q_t) - phi(k_t), the
+            // learning rates and u_t (so the backward needs no projection and
+            // no input softmax).
+            float* __restrict__ tp = tape + ((int64_t)unit * T + t) * TL::ROW;
+            // a_t: the tape row buffer (one wave) or the tape itself
+            float* __restrict__ ta = TAPE_LDS ? s_tr : tp;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int row = rg + G * r;
+                if (row < ROWS) ta[row] = acc[r];  // the same word from all P lanes of the row
+            }
+            if constexpr (BETA_SEP) {
+                if (wave == 0 && (lane & 15) == 0 && brow < NLR) ta[MAIN + brow] = accb;
+            }
+            if constexpr (TAPE_LDS) {
+                if constexpr (!G_REG) {
+                    if (lane < 4) s_tr[TL::G_OFF + lane] = lane < NLR ? gl : 0.f;
+                }
+                if (lane < D_IN) s_tr[TL::U_OFF + lane] = urow[lane];
+                wave_sync();
+#pragma unroll
+                for (int o = 4 * lane; o < TL::ROW; o += 4 * kWave)
+                    *reinterpret_cast<float4*>(tp + o) = *reinterpret_cast<const float4*>(s_tr + o);
+            } else if (wave == 0) {
+#pragma unroll
+                for (int j0 = 0; j0 < D_IN; j0 += kWave) {
+                    if (j0 + lane < D_IN) {
+                        tp[TL::KH_OFF + j0 + lane] = khw[j0 + lane];
+                        tp[TL::E_OFF + j0 + lane] = ew[j0 + lane];
+                        tp[TL::U_OFF + j0 + lane] = urow[j0 + lane];
+                    }
+                }
+                if (lane < 4) tp[TL::G_OFF + lane] = lane < NLR ? gl : 0.f;
+            }
+        }
+        // ---- (D) Eq. (3)/(5): W += a kh^T, in place.
+        stream_lds<L>(khw + p * L, [&](int c, float kc) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) w[r][c] = fmaf(acc[r], kc, w[r][c]);
+        });
+        if constexpr (BETA_SEP) {
+            if (wave == 0)
+                stream_lds<LB>(khw + bcol, [&](int c, float kc) { wb[c] = fmaf(accb, kc, wb[c]); });
+        }
+    };
 
     if (T > 0) {
         xs.load(0);
@@ -385,149 +580,15 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
         if (T > S) xs.load(S);
         __syncthreads();
 
+        static_assert(S % 2 == 0, "chunks start at even steps");
         int chunk = 0;
-        int until_reset = reset_interval;  // steps left before the next reset
-        (void)until_reset;
         for (int c0 = 0; c0 < T; c0 += S, ++chunk) {
             const int n = (T - c0) < S ? (T - c0) : S;
             const float* sxc = &s_x[chunk & 1][0][0];
-            for (int s = 0; s < n; ++s) {
-                const int t = c0 + s;
-                const float* __restrict__ urow = sxc + s * D_IN;
-                if constexpr (RESET) {
-                    // Reset ablation of the review page (Sec. 4.5): before every
-                    // step t > 0 with t % R == 0 the state returns to W0.
-                    if (reset_interval > 0) {
-                        if (until_reset == 0) {
-                            if constexpr (TAPE) {
-                                // the backward pass restarts window t/R - 1 from its end state
-                                const int nres = (T - 1) / reset_interval;
-                                store_w(wstates + ((int64_t)unit * nres + (t / reset_interval - 1)) * M * D_IN);
-                            }
-                            load_w0();
-                            until_reset = reset_interval;
-                        }
-                        --until_reset;
-                    }
-                }
-                // ---- (A) Eq. (1): z = W u.
-                float* __restrict__ zt = s_z[t & 1];
-                float acc[R];
-#pragma unroll
-                for (int r = 0; r < R; ++r) acc[r] = 0.f;
-                stream_lds<L>(urow + p * L, [&](int c, float uc) {
-#pragma unroll
-                    for (int r = 0; r < R; ++r) acc[r] = fmaf(w[r][c], uc, acc[r]);
-                });
-#pragma unroll
-                for (int r = 0; r < R; ++r) acc[r] = group_sum<P>(acc[r]);
-                if constexpr (KEEP_SUMS) {
-#pragma unroll
-                    for (int r = 0; r < R; ++r) keep(acc[r]);
-                }
-                // All P lanes of a row group hold the same sums and every one
-                // stores them (the same word from P lanes): stores at constant
-                // offsets from one address, no per-lane selection of a register.
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const int row = rg + G * r;
-                    if (Gm::ALIGNED || row < ROWS) zt[row] = acc[r];
-                }
-                if constexpr (BETA_SEP) {
-                    if (wave == 0) {
-                        float accb = 0.f;
-                        stream_lds<LB>(urow + bcol, [&](int c, float uc) { accb = fmaf(wb[c], uc, accb); });
-                        accb = group_sum<16>(accb);
-                        if constexpr (KEEP_SUMS) keep(accb);
-                        if ((lane & 15) == 0 && brow < NLR) zt[MAIN + brow] = accb;
-                    }
-                }
-                __syncthreads();
-
-                // ---- (B) phi(k), phi(q), sigma(beta), computed by every wave for
-                // itself (identical bits in every wave); y_t from W_{t-1}.
-                wave_addresses<D_IN>(zt + D_OUT, zt + D_OUT + D_IN, khs, es, lane);
-                const float gl = sigmoid_f32(zt[MAIN + (NLR == 4 ? (lane & 3) : 0)]);
-                const float g0 = readlane(gl, 0), g1 = readlane(gl, 1), g2 = readlane(gl, 2), g3 = readlane(gl, 3);
-                if (wave == WAVE_AUX) store_y<D_OUT, BF16>(yv, y0 + (int64_t)t * y_step, zt, lane);
-                wave_sync();
-                const float* __restrict__ khw = khs;
-                const float* __restrict__ ew = es;
-
-                // ---- (C) Eq. (2)/(4) fused: W (qh - kh) = v - vb, times the gate.
-#pragma unroll
-                for (int r = 0; r < R; ++r) acc[r] = 0.f;
-                stream_lds<L>(ew + p * L, [&](int c, float ec) {
-#pragma unroll
-                    for (int r = 0; r < R; ++r) acc[r] = fmaf(w[r][c], ec, acc[r]);
-                });
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    float gate;
-                    if constexpr (Gm::ALIGNED) {
-                        const int bk = Gm::rate_of_reg(r);
-                        gate = bk == 0 ? g0 : bk == 1 ? g1 : bk == 2 ? g2 : g3;
-                    } else {
-                        const int bk = rate_of_row<NLR>(rg + G * r, D_IN, D_OUT);
-                        gate = bk == 0 ? g0 : bk == 1 ? g1 : bk == 2 ? g2 : g3;
-                    }
-                    acc[r] = gate * group_sum<P>(acc[r]);
-                }
-                if constexpr (KEEP_SUMS) {
-#pragma unroll
-                    for (int r = 0; r < R; ++r) keep(acc[r]);
-                }
-                float accb = 0.f;
-                if constexpr (BETA_SEP) {
-                    if (wave == 0) {
-                        stream_lds<LB>(ew + bcol, [&](int c, float ec) { accb = fmaf(wb[c], ec, accb); });
-                        accb = g3 * group_sum<16>(accb);
-                    }
-                }
-                if constexpr (TAPE) {
-                    // Tape for the backward pass: a_t, phi(k_t) (enough to undo the
-                    // update, W_{t-1} = W_t - a_t phi(k_t)^T), phi(q_t) - phi(k_t), the
-                    // learning rates and u_t (so the backward needs no projection and
-                    // no input softmax).
-                    float* __restrict__ tp = tape + ((int64_t)unit * T + t) * TL::ROW;
-                    // a_t: the tape row buffer (one wave) or the tape itself
-                    float* __restrict__ ta = TAPE_LDS ? s_tr : tp;
-#pragma unroll
-                    for (int r = 0; r < R; ++r) {
-                        const int row = rg + G * r;
-                        if (row < ROWS) ta[row] = acc[r];  // the same word from all P lanes of the row
-                    }
-                    if constexpr (BETA_SEP) {
-                        if (wave == 0 && (lane & 15) == 0 && brow < NLR) ta[MAIN + brow] = accb;
-                    }
-                    if constexpr (TAPE_LDS) {
-                        if (lane < 4) s_tr[TL::G_OFF + lane] = lane < NLR ? gl : 0.f;
-                        if (lane < D_IN) s_tr[TL::U_OFF + lane] = urow[lane];
-                        wave_sync();
-#pragma unroll
-                        for (int o = 4 * lane; o < TL::ROW; o += 4 * kWave)
-                            *reinterpret_cast<float4*>(tp + o) = *reinterpret_cast<const float4*>(s_tr + o);
-                    } else if (wave == 0) {
-#pragma unroll
-                        for (int j0 = 0; j0 < D_IN; j0 += kWave) {
-                            if (j0 + lane < D_IN) {
-                                tp[TL::KH_OFF + j0 + lane] = khw[j0 + lane];
-                                tp[TL::E_OFF + j0 + lane] = ew[j0 + lane];
-                                tp[TL::U_OFF + j0 + lane] = urow[j0 + lane];
-                            }
-                        }
-                        if (lane < 4) tp[TL::G_OFF + lane] = lane < NLR ? gl : 0.f;
-                    }
-                }
-                // ---- (D) Eq. (3)/(5): W += a kh^T, in place.
-                stream_lds<L>(khw + p * L, [&](int c, float kc) {
-#pragma unroll
-                    for (int r = 0; r < R; ++r) w[r][c] = fmaf(acc[r], kc, w[r][c]);
-                });
-                if constexpr (BETA_SEP) {
-                    if (wave == 0)
-                        stream_lds<LB>(khw + bcol, [&](int c, float kc) { wb[c] = fmaf(accb, kc, wb[c]); });
-                }
+            // two steps per iteration, so the z buffer of each is a constant
+            for (int s = 0; s < n; s += 2) {
+                step(c0 + s, sxc + s * D_IN, std::integral_constant<int, 0>{});
+                if (s + 1 < n) step(c0 + s + 1, sxc + (s + 1) * D_IN, std::integral_constant<int, 1>{});
             }
             if (c0 + S < T) {
                 xs.stage(s_x[(chunk + 1) & 1], in_softmax);
