@@ -95,6 +95,7 @@ __device__ __forceinline__ int dpp_i(int v)
     return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
 }
 
+
 template <int P>
 __device__ __forceinline__ float group_max(float v)
 {
@@ -223,6 +224,35 @@ __device__ __forceinline__ float half_max(float v)
     k = max(k, dpp_i<kDppMirror>(k));
     const auto r = __builtin_amdgcn_permlane16_swap(static_cast<unsigned>(k), static_cast<unsigned>(k), false, false);
     return from_order_key(max(static_cast<int>(r[0]), static_cast<int>(r[1])));
+}
+
+// half_max as float max with DPP operands, written out: the compiler cannot
+// fuse a DPP move into v_max_f32 itself (IEEE mode makes it canonicalise both
+// operands first), so the order-preserving integer form above costs six
+// conversions that this form does not.  Each DPP read follows its operand's
+// write by two wait states (s_nop 1), and a trailing s_nop 1 covers a
+// consumer placed right after the block.  NaN operands are dropped, as by
+// fmax2.  Faster where several waves share a SIMD; one-wave units, which
+// interleave the integer form with other work, keep that.
+__device__ __forceinline__ float half_max_f(float v)
+{
+    float r = v, t;
+    asm("s_nop 1\n\t"
+        "v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "s_nop 1\n\t"
+        "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "s_nop 1\n\t"
+        "v_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "s_nop 1\n\t"
+        "v_max_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_mov_b32 %1, %0\n\t"
+        "s_nop 1\n\t"
+        "v_permlane16_swap_b32 %0, %1\n\t"
+        "s_nop 1\n\t"
+        "v_max_f32 %0, %0, %1\n\t"
+        "s_nop 1"
+        : "+v"(r), "=&v"(t));
+    return r;
 }
 
 __device__ __forceinline__ float half_sum(float v)

@@ -77,8 +77,11 @@ bool variant_matches(const Variant& v, int64_t d_in, int64_t d_out, int io, int 
 }
 
 // Automatic choice among the eligible variants: the fewest waves per unit
-// that still give every SIMD of the chip two waves (units * waves >= 2048);
-// if none does, the most waves per unit.  Variants whose reset support
+// that still fill the chip -- two waves per SIMD for one-wave units (units >=
+// 2048), four for multi-wave units (units * waves >= 4096: they spend part of
+// each step in barriers and LDS round trips that a second pair of waves
+// hides; at d = 64 and 512 units eight waves per unit take 0.49 ms against
+// 0.51 ms for four); if none does, the most waves per unit.  Variants whose reset support
 // matches the request come first: a variant built with the reset ablation
 // serves a plain request only for a shape that has no plain variant.
 int find_variant(int64_t d_in, int64_t d_out, int io, int nlr, bool reset, bool tape, int requested,
@@ -94,7 +97,8 @@ int find_variant(int64_t d_in, int64_t d_out, int io, int nlr, bool reset, bool 
             const Variant& v = *table().v[i];
             if (!variant_matches(v, d_in, d_out, io, nlr, reset, tape) || !v.is_auto) continue;
             if (pass == 0 && (v.reset != 0) != reset) continue;
-            if (units * v.nw >= kChipWaveSlots && (best_fill < 0 || v.nw < table().v[best_fill]->nw)) best_fill = i;
+            const int64_t fill = v.nw == 1 ? kChipWaveSlots : 2 * kChipWaveSlots;
+            if (units * v.nw >= fill && (best_fill < 0 || v.nw < table().v[best_fill]->nw)) best_fill = i;
             if (best_any < 0 || v.nw > table().v[best_any]->nw) best_any = i;
         }
         if (best_fill >= 0 || best_any >= 0) return best_fill >= 0 ? best_fill : best_any;

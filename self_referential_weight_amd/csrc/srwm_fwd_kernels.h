@@ -83,8 +83,9 @@ __device__ __forceinline__ int rate_of_row(int row, int d_in, int d_out)
 // (phi(k), phi(q)) of entry i and the upper half with those of entry i+1, so
 // every lane writes one kh = softmax(k) entry and e = softmax(q) - kh, the
 // difference the fused read of Eq. (2) needs (with one entry per lane, the
-// lower half alone writes).
-template <int D>
+// lower half alone writes).  FMAX picks the float form of the half-wave max
+// (multi-wave units) over the integer one.
+template <int D, bool FMAX = false>
 __device__ __forceinline__ void wave_addresses(const float* __restrict__ k, const float* __restrict__ q,
                                                float* __restrict__ kh_out, float* __restrict__ e_out, int lane)
 {
@@ -100,7 +101,7 @@ __device__ __forceinline__ void wave_addresses(const float* __restrict__ k, cons
         v[i] = (j < D) ? src[j] : -INFINITY;
         mx = fmax2(mx, v[i]);
     }
-    const float ms = log2e_scaled(half_max(mx));
+    const float ms = log2e_scaled(FMAX ? half_max_f(mx) : half_max(mx));
 #pragma unroll
     for (int i = 0; i < EPH; ++i) {
         const int j = hl + 32 * i;
@@ -314,6 +315,7 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = NW == 1 ? 0 : tid / kWave;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // the same, known uniform
     const int p = tid % P;
     const int rg = tid / P;
     const int unit = blockIdx.x;
@@ -391,8 +393,24 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
 
     // One step t, reading u_t at urow; PAR = t & 1 picks the z buffer (the
     // chunk length is even, so it is the parity of the step within its chunk).
-    auto step = [&](const int t, const float* __restrict__ urow, auto par) {
+    // Multi-wave units have registers to spare: they read a lane's columns of
+    // a vector at once rather than in pieces, read q^ - k^ and k^ together (so
+    // the update does not wait for its own LDS read), and the first step of
+    // each pair also reads the second step's u (its row is in the same tile).
+    // (Units holding more than 48 state floats per lane keep the piecewise
+    // reads and the single copy of the step below: with them the two-wave
+    // d = 64 units spill.)
+    constexpr bool SPARE = NW > 1 && R * L <= 48;
+    constexpr bool PREF = SPARE && L <= 8;
+    float u_next[PREF ? L : 1];
+
+    auto step = [&](const int t, const float* __restrict__ urow, auto par, auto role) {
         constexpr int PAR = decltype(par)::value;
+        // role 0: wave 0 (the rate rows, the tape's vectors); 1: the wave that
+        // stores y_t; 2: the others; 3: any wave (decided at run time)
+        constexpr int ROLE = decltype(role)::value;
+        const bool W0 = ROLE == 3 ? wave == 0 : ROLE == 0;
+        const bool AUX = NW == 1 || (ROLE == 3 ? wave == WAVE_AUX : ROLE == 1);
         if constexpr (RESET) {
             // Reset ablation of the review page (Sec. 4.5): before every
             // step t > 0 with t % R == 0 the state returns to W0.
@@ -414,10 +432,25 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
         float acc[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = 0.f;
-        stream_lds<L>(urow + p * L, [&](int c, float uc) {
+        if constexpr (PREF) {
+            float uv[L];
+            if constexpr (PAR == 0) {
+                load_f32<L>(urow + p * L, uv);
+                load_f32<L>(urow + D_IN + p * L, u_next);  // row s + 1 <= S - 1 of the tile
+            } else {
 #pragma unroll
-            for (int r = 0; r < R; ++r) acc[r] = fmaf(w[r][c], uc, acc[r]);
-        });
+                for (int c = 0; c < L; ++c) uv[c] = u_next[c];
+            }
+#pragma unroll
+            for (int c = 0; c < L; ++c)
+#pragma unroll
+                for (int r = 0; r < R; ++r) acc[r] = fmaf(w[r][c], uv[c], acc[r]);
+        } else {
+            stream_lds<L>(urow + p * L, [&](int c, float uc) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) acc[r] = fmaf(w[r][c], uc, acc[r]);
+            });
+        }
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = group_sum<P>(acc[r]);
         if constexpr (KEEP_SUMS) {
@@ -452,7 +485,7 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
         }
         float gb = 0.f;  // G_REG: the gate of rate row brow, in DPP row brow
         if constexpr (BETA_SEP) {
-            if (wave == 0) {
+            if (W0) {
                 float accb = 0.f;
                 stream_lds<LB>(urow + bcol, [&](int c, float uc) { accb = fmaf(wb[c], uc, accb); });
                 accb = group_sum<16>(accb);
@@ -462,6 +495,8 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
                         if ((lane & 15) == 0) s_tr[TL::G_OFF + brow] = brow < NLR ? gb : 0.f;
                     }
                 } else {
+                    // the other waves read the gates themselves
+                    accb = sigmoid_f32(accb);
                     if constexpr (KEEP_SUMS) keep(accb);
                     if ((lane & 15) == 0 && brow < NLR) zt[MAIN + brow] = accb;
                 }
@@ -471,7 +506,7 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
 
         // ---- (B) phi(k), phi(q), sigma(beta), computed by every wave for
         // itself (identical bits in every wave); y_t from W_{t-1}.
-        wave_addresses<D_IN>(zt + D_OUT, zt + D_OUT + D_IN, khs, es, lane);
+        wave_addresses<D_IN, (NW > 1)>(zt + D_OUT, zt + D_OUT + D_IN, khs, es, lane);
         float gl = 0.f, g0, g1, g2, g3;
         if constexpr (G_REG) {
             g0 = readlane(gb, 0);
@@ -482,6 +517,17 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
             } else {
                 g1 = g2 = g3 = g0;
             }
+        } else if constexpr (BETA_SEP) {
+            // wave 0 stored the gates (one sigmoid per unit instead of one per wave)
+            g0 = zt[MAIN];
+            if constexpr (NLR == 4) {
+                g1 = zt[MAIN + 1];
+                g2 = zt[MAIN + 2];
+                g3 = zt[MAIN + 3];
+            } else {
+                g1 = g2 = g3 = g0;
+            }
+            if constexpr (TAPE) gl = zt[MAIN + (NLR == 4 ? (lane & 3) : 0)];
         } else {
             gl = sigmoid_f32(zt[MAIN + (NLR == 4 ? (lane & 3) : 0)]);
             g0 = readlane(gl, 0);
@@ -490,19 +536,30 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
             g3 = readlane(gl, 3);
         }
         if constexpr (!Y_REG) {
-            if (wave == WAVE_AUX) store_y<D_OUT, BF16>(yv, y0 + (int64_t)t * y_step, zt, lane);
+            if (AUX) store_y<D_OUT, BF16>(yv, y0 + (int64_t)t * y_step, zt, lane);
         }
         wave_sync();
         const float* __restrict__ khw = khs;
         const float* __restrict__ ew = es;
 
         // ---- (C) Eq. (2)/(4) fused: W (qh - kh) = v - vb, times the gate.
+        float kv[PREF ? L : 1];
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = 0.f;
-        stream_lds<L>(ew + p * L, [&](int c, float ec) {
+        if constexpr (PREF) {
+            float ev[L];
+            load_f32<L>(ew + p * L, ev);
+            load_f32<L>(khw + p * L, kv);
 #pragma unroll
-            for (int r = 0; r < R; ++r) acc[r] = fmaf(w[r][c], ec, acc[r]);
-        });
+            for (int c = 0; c < L; ++c)
+#pragma unroll
+                for (int r = 0; r < R; ++r) acc[r] = fmaf(w[r][c], ev[c], acc[r]);
+        } else {
+            stream_lds<L>(ew + p * L, [&](int c, float ec) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) acc[r] = fmaf(w[r][c], ec, acc[r]);
+            });
+        }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             float gate;
@@ -521,7 +578,7 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
         }
         float accb = 0.f;
         if constexpr (BETA_SEP) {
-            if (wave == 0) {
+            if (W0) {
                 stream_lds<LB>(ew + bcol, [&](int c, float ec) { accb = fmaf(wb[c], ec, accb); });
                 accb = g3 * group_sum<16>(accb);
             }
@@ -540,7 +597,7 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
                 if (row < ROWS) ta[row] = acc[r];  // the same word from all P lanes of the row
             }
             if constexpr (BETA_SEP) {
-                if (wave == 0 && (lane & 15) == 0 && brow < NLR) ta[MAIN + brow] = accb;
+                if (W0 && (lane & 15) == 0 && brow < NLR) ta[MAIN + brow] = accb;
             }
             if constexpr (TAPE_LDS) {
                 if constexpr (!G_REG) {
@@ -551,7 +608,7 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
 #pragma unroll
                 for (int o = 4 * lane; o < TL::ROW; o += 4 * kWave)
                     *reinterpret_cast<float4*>(tp + o) = *reinterpret_cast<const float4*>(s_tr + o);
-            } else if (wave == 0) {
+            } else if (W0) {
 #pragma unroll
                 for (int j0 = 0; j0 < D_IN; j0 += kWave) {
                     if (j0 + lane < D_IN) {
@@ -564,12 +621,19 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
             }
         }
         // ---- (D) Eq. (3)/(5): W += a kh^T, in place.
-        stream_lds<L>(khw + p * L, [&](int c, float kc) {
+        if constexpr (PREF) {
 #pragma unroll
-            for (int r = 0; r < R; ++r) w[r][c] = fmaf(acc[r], kc, w[r][c]);
-        });
+            for (int c = 0; c < L; ++c)
+#pragma unroll
+                for (int r = 0; r < R; ++r) w[r][c] = fmaf(acc[r], kv[c], w[r][c]);
+        } else {
+            stream_lds<L>(khw + p * L, [&](int c, float kc) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) w[r][c] = fmaf(acc[r], kc, w[r][c]);
+            });
+        }
         if constexpr (BETA_SEP) {
-            if (wave == 0)
+            if (W0)
                 stream_lds<LB>(khw + bcol, [&](int c, float kc) { wb[c] = fmaf(accb, kc, wb[c]); });
         }
     };
@@ -586,9 +650,35 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
             const int n = (T - c0) < S ? (T - c0) : S;
             const float* sxc = &s_x[chunk & 1][0][0];
             // two steps per iteration, so the z buffer of each is a constant
-            for (int s = 0; s < n; s += 2) {
-                step(c0 + s, sxc + s * D_IN, std::integral_constant<int, 0>{});
-                if (s + 1 < n) step(c0 + s + 1, sxc + (s + 1) * D_IN, std::integral_constant<int, 1>{});
+            auto run = [&](auto role) {
+                for (int s = 0; s < n; s += 2) {
+                    step(c0 + s, sxc + s * D_IN, std::integral_constant<int, 0>{}, role);
+                    if (s + 1 < n) step(c0 + s + 1, sxc + (s + 1) * D_IN, std::integral_constant<int, 1>{}, role);
+                }
+            };
+            // Each wave role runs its own straight-line copy of the step (a
+            // scalar branch per chunk), so wave 0's rate-row work interleaves
+            // with its main rows instead of sitting behind exec-mask branches.
+            // At d = 128 the three copies cost registers (spills around the
+            // chunk loop) and time (11.2 vs 11.0 ms on the wide workload), and
+            // in SR-DeltaNet's projection (d_out = 193) they take registers
+            // that the fast-matrix kernel running beside it needs (4.54 vs
+            // 4.38 ms per step), so one copy decides at run time there.
+            if constexpr (NW > 1 && (D_IN > 64 || !Gm::ALIGNED || !SPARE)) {
+                run(std::integral_constant<int, 3>{});
+            } else if constexpr (NW == 1) {
+                for (int s = 0; s < n; s += 2) {
+                    step(c0 + s, sxc + s * D_IN, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+                    if (s + 1 < n)
+                        step(c0 + s + 1, sxc + (s + 1) * D_IN, std::integral_constant<int, 1>{},
+                             std::integral_constant<int, 0>{});
+                }
+            } else if (wave_u == 0) {
+                run(std::integral_constant<int, 0>{});
+            } else if (wave_u == WAVE_AUX) {
+                run(std::integral_constant<int, 1>{});
+            } else {
+                run(std::integral_constant<int, 2>{});
             }
             if (c0 + S < T) {
                 xs.stage(s_x[(chunk + 1) & 1], in_softmax);
@@ -726,7 +816,7 @@ void srwm_fwd_fused_kernel(const void* __restrict__ xv, const float* __restrict_
             // ---- (B) addresses and gates of step t (every wave), y_t.
             float* __restrict__ khw = s_kh[t & 1][wave];
             float* __restrict__ ew = s_e[wave];
-            wave_addresses<D_IN>(zt + D_OUT, zt + D_OUT + D_IN, khw, ew, lane);
+            wave_addresses<D_IN, true>(zt + D_OUT, zt + D_OUT + D_IN, khw, ew, lane);
             const float gl = sigmoid_f32(zt[MAIN + (NLR == 4 ? (lane & 3) : 0)]);
             const float g0 = readlane(gl, 0), g1 = readlane(gl, 1), g2 = readlane(gl, 2), g3 = readlane(gl, 3);
             if (wave == 1) store_y<D_OUT, BF16>(yv, y0 + (int64_t)t * y_step, zt, lane);

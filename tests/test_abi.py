@@ -109,6 +109,9 @@ def test_select_variant():
     # many units: the fewest waves per unit; few units: more waves per unit
     assert vs[lib.srwm_select_variant(64, 64, 1, 4, 0, 2048)]["waves"] == 1
     assert vs[lib.srwm_select_variant(64, 64, 0, 4, 0, 256)]["waves"] > 1
+    # one-wave units from two waves per SIMD on; multi-wave units fill four
+    assert [vs[lib.srwm_select_variant(64, 64, 0, 4, 0, u)]["waves"] for u in (256, 512, 1024, 2048, 4096)] == \
+        [8, 8, 4, 1, 1]
     assert lib.srwm_select_variant(7, 7, 0, 4, 0, 4) == E_UNSUP
     assert lib.srwm_select_variant(64, 64, 3, 4, 0, 4) == E_ARG
     assert lib.srwm_select_variant(64, 64, 0, 2, 0, 4) == E_ARG
