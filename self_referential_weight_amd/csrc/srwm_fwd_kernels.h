@@ -402,6 +402,8 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
     // d = 64 units spill.)
     constexpr bool SPARE = NW > 1 && R * L <= 48;
     constexpr bool PREF = SPARE && L <= 8;
+    // a straight-line copy of the step per wave role (the chunk loop below)
+    constexpr bool ROLES = NW > 1 && D_IN <= 64 && Gm::ALIGNED && SPARE;
     float u_next[PREF ? L : 1];
 
     auto step = [&](const int t, const float* __restrict__ urow, auto par, auto role) {
@@ -429,6 +431,18 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
         }
         // ---- (A) Eq. (1): z = W u.
         float* __restrict__ zt = s_z[PAR];
+        // Multi-wave units with a copy of the step per role: wave 0 reads its
+        // rate-row columns of u, q^ - k^ and k^ together with the other
+        // vectors, not right before use -- the rate rows are its extra work,
+        // and every other wave waits for it at the barrier (few-shot taped
+        // forward 0.79 -> 0.745 ms).  Where the role is decided at run time
+        // (d = 128, d_out = 193) the loads sit behind a branch and cost more
+        // than they save (wide 11.06 -> 11.79 ms).
+        constexpr bool BPREF = BETA_SEP && ROLES;
+        float ubv[BPREF ? LB : 1];
+        if constexpr (BPREF) {
+            if (W0) load_f32<LB>(urow + bcol, ubv);
+        }
         float acc[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = 0.f;
@@ -487,7 +501,12 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
         if constexpr (BETA_SEP) {
             if (W0) {
                 float accb = 0.f;
-                stream_lds<LB>(urow + bcol, [&](int c, float uc) { accb = fmaf(wb[c], uc, accb); });
+                if constexpr (BPREF) {
+#pragma unroll
+                    for (int c = 0; c < LB; ++c) accb = fmaf(wb[c], ubv[c], accb);
+                } else {
+                    stream_lds<LB>(urow + bcol, [&](int c, float uc) { accb = fmaf(wb[c], uc, accb); });
+                }
                 accb = group_sum<16>(accb);
                 if constexpr (G_REG) {
                     gb = sigmoid_f32(accb);
@@ -543,6 +562,13 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
         const float* __restrict__ ew = es;
 
         // ---- (C) Eq. (2)/(4) fused: W (qh - kh) = v - vb, times the gate.
+        float ebv[BPREF ? LB : 1], kbv[BPREF ? LB : 1];
+        if constexpr (BPREF) {
+            if (W0) {
+                load_f32<LB>(ew + bcol, ebv);
+                load_f32<LB>(khw + bcol, kbv);
+            }
+        }
         float kv[PREF ? L : 1];
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = 0.f;
@@ -579,7 +605,12 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
         float accb = 0.f;
         if constexpr (BETA_SEP) {
             if (W0) {
-                stream_lds<LB>(ew + bcol, [&](int c, float ec) { accb = fmaf(wb[c], ec, accb); });
+                if constexpr (BPREF) {
+#pragma unroll
+                    for (int c = 0; c < LB; ++c) accb = fmaf(wb[c], ebv[c], accb);
+                } else {
+                    stream_lds<LB>(ew + bcol, [&](int c, float ec) { accb = fmaf(wb[c], ec, accb); });
+                }
                 accb = g3 * group_sum<16>(accb);
             }
         }
@@ -633,8 +664,14 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
             });
         }
         if constexpr (BETA_SEP) {
-            if (W0)
-                stream_lds<LB>(khw + bcol, [&](int c, float kc) { wb[c] = fmaf(accb, kc, wb[c]); });
+            if (W0) {
+                if constexpr (BPREF) {
+#pragma unroll
+                    for (int c = 0; c < LB; ++c) wb[c] = fmaf(accb, kbv[c], wb[c]);
+                } else {
+                    stream_lds<LB>(khw + bcol, [&](int c, float kc) { wb[c] = fmaf(accb, kc, wb[c]); });
+                }
+            }
         }
     };
 
@@ -664,7 +701,7 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
             // in SR-DeltaNet's projection (d_out = 193) they take registers
             // that the fast-matrix kernel running beside it needs (4.54 vs
             // 4.38 ms per step), so one copy decides at run time there.
-            if constexpr (NW > 1 && (D_IN > 64 || !Gm::ALIGNED || !SPARE)) {
+            if constexpr (NW > 1 && !ROLES) {
                 run(std::integral_constant<int, 3>{});
             } else if constexpr (NW == 1) {
                 for (int s = 0; s < n; s += 2) {
