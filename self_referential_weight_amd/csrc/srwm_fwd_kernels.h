@@ -443,6 +443,18 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
         if constexpr (BPREF) {
             if (W0) load_f32<LB>(urow + bcol, ubv);
         }
+        // With the prefetch, wave 0 forms its rate rows' sums and gates first:
+        // the chain (row sum over 16 lanes, exp, reciprocal) then overlaps
+        // its main rows instead of ending its pass before the barrier.
+        float gz = 0.f;
+        if constexpr (BPREF) {
+            if (W0) {
+                float accb = 0.f;
+#pragma unroll
+                for (int c = 0; c < LB; ++c) accb = fmaf(wb[c], ubv[c], accb);
+                gz = sigmoid_f32(group_sum<16>(accb));
+            }
+        }
         float acc[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = 0.f;
@@ -499,14 +511,12 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
         }
         float gb = 0.f;  // G_REG: the gate of rate row brow, in DPP row brow
         if constexpr (BETA_SEP) {
-            if (W0) {
+            if (BPREF && W0) {
+                if constexpr (KEEP_SUMS) keep(gz);
+                if ((lane & 15) == 0 && brow < NLR) zt[MAIN + brow] = gz;
+            } else if (W0) {
                 float accb = 0.f;
-                if constexpr (BPREF) {
-#pragma unroll
-                    for (int c = 0; c < LB; ++c) accb = fmaf(wb[c], ubv[c], accb);
-                } else {
-                    stream_lds<LB>(urow + bcol, [&](int c, float uc) { accb = fmaf(wb[c], uc, accb); });
-                }
+                stream_lds<LB>(urow + bcol, [&](int c, float uc) { accb = fmaf(wb[c], uc, accb); });
                 accb = group_sum<16>(accb);
                 if constexpr (G_REG) {
                     gb = sigmoid_f32(accb);
