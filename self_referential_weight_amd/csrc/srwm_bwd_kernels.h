@@ -387,6 +387,10 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
                 khh[c] = fmaf(wh[r][c], a[r], khh[c]);
             }
             ah[r] = group_sum<P>(as);
+            // complete in every lane here: otherwise the last DPP level of
+            // each sum is split into a move before the last row's branch and
+            // an add after it (12 extra instructions per step)
+            keep(ah[r]);
         }
         float bp[4] = {0.f, 0.f, 0.f, 0.f};
         float rh[R], eh[L];
