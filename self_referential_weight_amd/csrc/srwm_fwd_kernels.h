@@ -632,12 +632,21 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
             float* __restrict__ tp = tape + ((int64_t)unit * T + t) * TL::ROW;
             // a_t: the tape row buffer (one wave) or the tape itself
             float* __restrict__ ta = TAPE_LDS ? s_tr : tp;
+            // (in multi-wave units, where every register row is a real row, no
+            // branch: it would split the last DPP level of each row sum into a
+            // move before it and an add after it -- few-shot taped forward
+            // 0.749 -> 0.728 ms; one-wave units keep it: without it they hold
+            // more values across the step and spill more, 10.89 -> 11.09 ms)
+            constexpr bool ALL_REAL = NW > 1 && R * G == ROWS;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const int row = rg + G * r;
-                if (row < ROWS) ta[row] = acc[r];  // the same word from all P lanes of the row
+                if (ALL_REAL || row < ROWS) ta[row] = acc[r];  // the same word from all P lanes of the row
             }
             if constexpr (BETA_SEP) {
+                if constexpr (NW > 1) {
+                    if (W0) keep(accb);
+                }
                 if (W0 && (lane & 15) == 0 && brow < NLR) ta[MAIN + brow] = accb;
             }
             if constexpr (TAPE_LDS) {
