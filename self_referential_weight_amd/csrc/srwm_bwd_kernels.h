@@ -30,9 +30,10 @@ namespace srwm {
 //     Wh   += rh e^T + zh u^T
 // after which Wh = dL/dW_{t-1}.
 //
-// Layout: lane (rg, p), rg = tid / P, p = tid % P, holds rows rg + G*r and
-// columns [p*L, p*L + L) of both W and Wh in registers.  Row sums (ah) are P
-// lanes joined by DPP.  Column sums (khh, eh, uh) are over all G row groups:
+// Layout: lane (rg, p), rg = tid / P, p = tid % P, holds G-th rows (rows
+// rg + G*r, or with P = 16 runs of consecutive rows in a lane-dependent slot
+// order, below) and columns [p*L, p*L + L) of both W and Wh in registers.
+// Row sums (ah) are P lanes joined by DPP.  Column sums (khh, eh, uh) are over all G row groups:
 // inside a wave they are reduce-scattered over the row-group lane bits (the
 // lane-row swaps v_permlane32_swap / v_permlane16_swap halve the columns a
 // lane carries, 1 swap + 1 add per pair; a DPP rotation adds the remaining
@@ -105,6 +106,51 @@ struct ColExchange {
     __device__ __forceinline__ static bool writer(int lane) { return (lane & KEEP_MASK) == 0; }
 };
 
+// Row sums over the 16 lanes of a DPP row for a run of SW register rows held
+// swizzled: slot s of lane p holds the run's row s ^ (p mod SW).  Lane p and
+// lane p ^ 1 hold each row in opposite slots of a pair, so one DPP add per
+// pair joins two lanes of two rows at once; after log2(SW) such levels lane p
+// holds row p mod SW summed over its SW-lane group, and two rotations finish
+// the 16 lanes.
+template <int SW>
+struct RunSum {
+    static_assert(SW == 1 || SW == 2 || SW == 4, "run length");
+    __device__ __forceinline__ static float total(const float* v)
+    {
+        if constexpr (SW == 1) return group_sum<16>(v[0]);
+        float u = v[0] + dpp<kDppXor1>(v[1]);
+        if constexpr (SW == 4) {
+            const float x = v[2] + dpp<kDppXor1>(v[3]);
+            u += dpp<kDppXor2>(x);
+        } else {
+            u += dpp<kDppXor2>(u);
+        }
+        u += dpp<0x124>(u);  // row_ror:4
+        u += dpp<0x128>(u);  // row_ror:8
+        return u;
+    }
+    // Slot s of the run from the per-lane value of row p mod SW (slot 0):
+    // slot s holds row s ^ (p mod SW), which lane p ^ s of the quad has.
+    __device__ __forceinline__ static float slot(int s, float v)
+    {
+        if constexpr (SW == 1) return v;
+        switch (s) {
+        case 0: return v;
+        case 1: return dpp<kDppXor1>(v);
+        case 2: return dpp<kDppXor2>(v);
+        default: return dpp<0x1B>(v);  // quad_perm [3,2,1,0]
+        }
+    }
+    // Sum over the SW lanes that hold the run's SW different rows.
+    __device__ __forceinline__ static float quad_sum(float v)
+    {
+        if constexpr (SW == 1) return v;
+        v += dpp<kDppXor1>(v);
+        if constexpr (SW == 4) v += dpp<kDppXor2>(v);
+        return v;
+    }
+};
+
 template <int D_IN, int D_OUT, int NW, int P, int NLR, bool RESET>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * kWave, NW * kWave), amdgpu_waves_per_eu(2)))
 void srwm_bwd_kernel(const float* __restrict__ WTin,
@@ -128,8 +174,11 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
     static_assert(D_IN % 4 == 0, "16-byte tape pieces");
     static_assert((NW & (NW - 1)) == 0, "power-of-two waves");
 
-    __shared__ __attribute__((aligned(16))) float s_tape[3][TW];
-    __shared__ __attribute__((aligned(16))) float s_gy[3][D_OUT];
+    // the step-input ring: a slot holds the tape row, then gy_t (one slot
+    // offset serves both)
+    constexpr int RW = TW + D_OUT;
+    static_assert(TW % 4 == 0, "16-byte ring slots");
+    __shared__ __attribute__((aligned(16))) float s_ring[3][RW];
     // khh, eh, uh column partials per wave, one float array per quantity so that
     // the writers (8 column slices 32 floats apart) and the readers (lane j,
     // column j) both meet at most two-way bank conflicts
@@ -144,7 +193,19 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
     // Otherwise lane j takes column j and the zh rows go through LDS.
     constexpr bool BCAST = P == 16 && D_IN == kWave && 16 % NW == 0;
     constexpr int KR = D_IN / G;  // register rows per K or Q block
-    __shared__ __attribute__((aligned(16))) float s_zh[BCAST ? 1 : NW][BCAST ? 1 : M];  // each wave's own zh rows
+    // Rows of the main blocks are held swizzled (with P = 16): in each run of
+    // SW register rows of one block, slot s of lane p holds the run's row
+    // s ^ (p mod SW).  A run's row sums then take a butterfly (RunSum below):
+    // 5 DPP adds for 4 rows instead of 16, ending with the total of row
+    // p mod SW in lane p, from which the run's other slots come back by
+    // quad_perm.  The kbar and qbar entries of the K and Q rows then go
+    // through LDS (the dealt columns sit one per lane, not one per slot).
+    constexpr int YR = D_OUT / G;  // register rows of the y block
+    constexpr int SW = P != 16 ? 1 : (KR % 4 == 0 && YR % 4 == 0) ? 4 : (KR % 2 == 0 && YR % 2 == 0) ? 2 : 1;
+    constexpr int RS = MAIN / G;   // register rows of the main blocks
+    constexpr bool ZLDS = !BCAST || SW > 1;
+    static_assert(SW == 1 || BCAST, "swizzled rows take the per-lane beta row");
+    __shared__ __attribute__((aligned(16))) float s_zh[ZLDS ? NW : 1][ZLDS ? M : 1];  // each wave's own zh rows
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -182,6 +243,22 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
     // one may be partial: its reads clamp the address and select 0 (no branch).
     auto row_ok = [](int r, int row) { return G * (r + 1) <= M || row < M; };
     auto row_at = [](int r, int row) { return G * (r + 1) <= M ? row : (row < M ? row : M - 1); };
+    // The row register r of this lane holds (see the swizzle above).  With
+    // SW > 1 the rows of run j of a block are SW consecutive rows,
+    // SW (G j + rg) + (0 .. SW-1) past the block's first row, so that the
+    // lanes of a half-wave read the tape and zh entries of their slots from
+    // consecutive LDS words (no bank conflict).
+    const int sw_e = lane & (SW - 1);
+    int so[SW];
+#pragma unroll
+    for (int s = 0; s < SW; ++s) so[s] = SW == 1 ? rg : SW * rg + (s ^ sw_e);
+    auto srow = [&](int r) {
+        if (r >= RS) return rg + G * r;
+        if constexpr (SW == 1) return rg + G * r;
+        const int rb = r < YR ? 0 : r < YR + KR ? YR : YR + KR;            // the block's first register
+        const int b0 = r < YR ? 0 : r < YR + KR ? D_OUT : D_OUT + D_IN;    // and its first row
+        return b0 + SW * G * ((r - rb) / SW) + so[r % SW];
+    };
 
     // Learning-rate index of register r (the row block; 0 with one rate).
     auto rate = [](int r) constexpr {
@@ -193,7 +270,7 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
     float w[R][L], wh[R][L];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const int row = rg + G * r;
+        const int row = srow(r);
         if (row < M) {
             load_f32<L>(WTin + ((int64_t)unit * M + row) * D_IN + p * L, w[r]);
             if (gWT != nullptr) {
@@ -230,9 +307,9 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
 #pragma unroll
         for (int i = 0; i < TPL; ++i) {
             const int j = tid + NT * i;
-            if (j < TW) s_tape[slot][j] = tnext[i];
+            if (j < TW) s_ring[slot][j] = tnext[i];
         }
-        if (g_mine) s_gy[slot][g_idx] = gnext;
+        if (g_mine) s_ring[slot][TW + g_idx] = gnext;
     };
 
     // The exchange: this lane's column partials of khh, eh and uh (and the
@@ -323,7 +400,7 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
     auto add_share = [&]() {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int row = rg + G * r;
+            const int row = srow(r);
             if (row < M) {
                 float prev[L];
                 load_f32<L>(dwi_unit + row * D_IN + p * L, prev);
@@ -339,7 +416,7 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
         for (int c = 0; c < L; ++c) zero[c] = 0.f;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int row = rg + G * r;
+            const int row = srow(r);
             if (row < M) store_f32<L>(dwi_unit + row * D_IN + p * L, zero);
         }
     }
@@ -353,16 +430,16 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
 
     int slot = (T - 1) % 3;
     for (int t = T - 1; t >= 0; --t) {
-        const float* __restrict__ tt = s_tape[slot];
+        const float* __restrict__ tt = s_ring[slot];
         const float* __restrict__ us = tt + TL::U_OFF;
-        const float* __restrict__ gs = s_gy[slot];
+        const float* __restrict__ gs = tt + TW;
         const int par = t & 1;
 
         // ---- (A) undo the update of step t; ah, khh, rh, eh.
         float a[R], kt[L];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int row = rg + G * r;
+            const int row = srow(r);
             const float av = tt[row_at(r, row)];
             a[r] = row_ok(r, row) ? av : 0.f;
         }
@@ -370,7 +447,9 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
         const float4 gv = *reinterpret_cast<const float4*>(tt + TL::G_OFF);
         const float gate[4] = {gv.x, gv.y, gv.z, gv.w};
 
-        float khh[L], ah[R];
+        // ah of the rows: per register row with SW = 1 (and for the beta
+        // row); with swizzled runs, ar[j] is the total of row p mod SW of run j
+        float khh[L], ah[R], pr[R], ar[RS / SW];
 #pragma unroll
         for (int c = 0; c < L; ++c) khh[c] = 0.f;
 #pragma unroll
@@ -386,11 +465,19 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
                 as = fmaf(wh[r][c], kt[c], as);
                 khh[c] = fmaf(wh[r][c], a[r], khh[c]);
             }
-            ah[r] = group_sum<P>(as);
-            // complete in every lane here: otherwise the last DPP level of
-            // each sum is split into a move before the last row's branch and
-            // an add after it (12 extra instructions per step)
-            keep(ah[r]);
+            if (SW > 1 && r < RS) {
+                pr[r] = as;
+                if (r % SW == SW - 1) {
+                    ar[r / SW] = RunSum<SW>::total(&pr[r + 1 - SW]);
+                    keep(ar[r / SW]);  // (as below: no DPP level split over the branch)
+                }
+            } else {
+                ah[r] = group_sum<P>(as);
+                // complete in every lane here: otherwise the last DPP level of
+                // each sum is split into a move before the last row's branch and
+                // an add after it (12 extra instructions per step)
+                keep(ah[r]);
+            }
         }
         float bp[4] = {0.f, 0.f, 0.f, 0.f};
         float rh[R], eh[L];
@@ -398,9 +485,24 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
         for (int c = 0; c < L; ++c) eh[c] = 0.f;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            // (a skipped last row has ah = 0 and W = 0: no branch here)
-            rh[r] = gate[rate(r)] * ah[r];
-            bp[rate(r)] = fmaf(ah[r], a[r], bp[rate(r)]);
+            if (SW > 1 && r < RS) {
+                // the run's rates from its one total: rh by quad_perm; the
+                // betah partial sum_i ah_i a_i over the run's rows by a quad sum
+                // (slot 0 holds row p mod SW, the one whose total this lane has)
+                const int s = r % SW, j = r / SW;
+                rh[r] = RunSum<SW>::slot(s, gate[rate(r)] * ar[j]);
+                if (s == 0) {
+                    float pb = ar[j] * a[r];
+                    keep(pb);  // (a multiply, not folded into the first add: that add takes the DPP)
+                    pb = RunSum<SW>::quad_sum(pb);
+                    keep(pb);
+                    bp[rate(r)] += pb;
+                }
+            } else {
+                // (a skipped last row has ah = 0 and W = 0: no branch here)
+                rh[r] = gate[rate(r)] * ah[r];
+                bp[rate(r)] = fmaf(ah[r], a[r], bp[rate(r)]);
+            }
 #pragma unroll
             for (int c = 0; c < L; ++c) eh[c] = fmaf(w[r][c], rh[r], eh[c]);
         }
@@ -456,6 +558,11 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
             if constexpr (BCAST) {
                 kbar_v = kh_j * (kb - dk);
                 qbar_v = qh_j * (eh_j - dq);
+                if constexpr (ZLDS) {
+                    // column jc of this wave's dealt columns (all 64 in every wave)
+                    s_zh[wave][D_OUT + jc] = kbar_v;
+                    s_zh[wave][D_OUT + D_IN + jc] = qbar_v;
+                }
                 if (!last_empty) {
                     // this lane's beta row rg (rows past M hold zb = 0)
                     const int c = rg < NLR ? rg : 0;
@@ -476,7 +583,7 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
                 }
             }
         }
-        if constexpr (!BCAST) wave_sync();
+        if constexpr (ZLDS) wave_sync();
 
         // ---- (C) uh of step t (column partials, reduced with step t-1); Wh update.
         float ev[L], uv[L];
@@ -487,14 +594,15 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             if (r == R - 1 && last_empty) continue;
-            const int row = rg + G * r;
+            const int row = srow(r);
             float zr;
             if (G * r < D_OUT) zr = gs[row];
             else if constexpr (BCAST) {
                 // rows of the beta block past M hold zb = 0
-                zr = G * r < D_OUT + D_IN ? row_bcast(kbar_v, r - D_OUT / G)
-                   : G * r < MAIN         ? row_bcast(qbar_v, r - (D_OUT + D_IN) / G)
-                                          : zb;
+                if (r >= RS) zr = zb;
+                else if constexpr (ZLDS) zr = s_zh[wave][row];
+                else zr = G * r < D_OUT + D_IN ? row_bcast(kbar_v, r - D_OUT / G)
+                                               : row_bcast(qbar_v, r - (D_OUT + D_IN) / G);
             } else {
                 const float zv = s_zh[wave][row_at(r, row)];
                 zr = row_ok(r, row) ? zv : 0.f;
@@ -521,7 +629,7 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
             const float* __restrict__ ws = wstates + ((int64_t)unit * n_resets + (t / reset_interval - 1)) * M * D_IN;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const int row = rg + G * r;
+                const int row = srow(r);
                 if (row < M) load_f32<L>(ws + row * D_IN + p * L, w[r]);
             }
             next_reset -= reset_interval;
@@ -547,7 +655,7 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
     } else {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int row = rg + G * r;
+            const int row = srow(r);
             if (row < M) store_f32<L>(dwi_unit + row * D_IN + p * L, wh[r]);
         }
     }
