@@ -185,12 +185,14 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
     __shared__ __attribute__((aligned(16))) float s_red[2][NW][3][D_IN];
     __shared__ __attribute__((aligned(16))) float s_bred[2][NW][4];     // betah partials per wave
     // The per-column phase (lane <-> column jc).  With P = 16 and d_in = 64
-    // the columns are dealt so that the kbar and qbar entries of every K and Q
-    // row a lane holds sit in its own DPP row: lane 16q + k of wave w takes
-    // column q + 4((w + k / KR) mod NW) + G (k mod KR), and the lanes of row
-    // group rg = 4w + q hold rows rg + G r, i.e. columns q + 4w + G k of the K
-    // and Q blocks (k < KR), so one row_newbcast hands each of them over.
-    // Otherwise lane j takes column j and the zh rows go through LDS.
+    // the columns are dealt: lane 16q + k of wave w takes column
+    // q + 4((w + k / KR) mod NW) + G (k mod KR).  The exchange's LDS slots
+    // follow the dealing (col_slot below).  Unswizzled rows (SW = 1) would
+    // then find the kbar and qbar entries of every K and Q row they hold in
+    // their own DPP row (the lanes of row group rg = 4w + q hold columns
+    // q + 4w + G k of those blocks, one row_newbcast each); the swizzled runs
+    // take them through LDS (ZLDS).  Otherwise lane j takes column j and the
+    // zh rows go through LDS.
     constexpr bool BCAST = P == 16 && D_IN == kWave && 16 % NW == 0;
     constexpr int KR = D_IN / G;  // register rows per K or Q block
     // Rows of the main blocks are held swizzled (with P = 16): in each run of
