@@ -33,6 +33,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "srwm.h"
 #include "srwm_device.h"
 
@@ -76,64 +78,89 @@ __global__ __launch_bounds__(256) void srwm_proj_gemm_kernel(const float* __rest
     const int c0 = static_cast<int>(g % ctiles) * kGN;
     const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
     const int lr = tid >> 3, lc = (tid & 7) * 4;  // loader: rows lr, lr + 32; columns lc..lc+3
+    // The tile's corner in X, W and Z (uniform): inside a tile every element
+    // is a 32-bit offset from it.
+    const float* __restrict__ Xt = X + n0 * K;
+    const float* __restrict__ Wt = W + (int64_t)c0 * K;
+    float* __restrict__ Zt = Z + n0 * C + c0;
 
-    v4f acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    for (int k0 = 0; k0 < K; k0 += kGK) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int r = lr + 32 * i;
-            const int gk = k0 + lc;
-            float4 vx = make_float4(0.f, 0.f, 0.f, 0.f), vw = vx;
-            if (n0 + r < N && gk < K) vx = *reinterpret_cast<const float4*>(X + (n0 + r) * K + gk);
-            if (c0 + r < C && gk < K) vw = *reinterpret_cast<const float4*>(W + (int64_t)(c0 + r) * K + gk);
-            *reinterpret_cast<float4*>(&sX[r][lc]) = vx;
-            *reinterpret_cast<float4*>(&sW[r][lc]) = vw;
-        }
-        __syncthreads();
-        // The sum over k is order-free, so in MFMA step s of the chunk lane
-        // group j = lane / 16 supplies k = 8 j + s: its operands for all eight
-        // steps are 8 consecutive floats of one row, two 16-byte LDS reads.
-        {
-            const int kb = 8 * (lane >> 4);
-            const int ra = wm + (lane & 15), rb = wn + (lane & 15);
-            const float4 a0l = *reinterpret_cast<const float4*>(&sX[ra][kb]);
-            const float4 a0h = *reinterpret_cast<const float4*>(&sX[ra][kb + 4]);
-            const float4 a1l = *reinterpret_cast<const float4*>(&sX[ra + 16][kb]);
-            const float4 a1h = *reinterpret_cast<const float4*>(&sX[ra + 16][kb + 4]);
-            const float4 b0l = *reinterpret_cast<const float4*>(&sW[rb][kb]);
-            const float4 b0h = *reinterpret_cast<const float4*>(&sW[rb][kb + 4]);
-            const float4 b1l = *reinterpret_cast<const float4*>(&sW[rb + 16][kb]);
-            const float4 b1h = *reinterpret_cast<const float4*>(&sW[rb + 16][kb + 4]);
-            const float a0[8] = {a0l.x, a0l.y, a0l.z, a0l.w, a0h.x, a0h.y, a0h.z, a0h.w};
-            const float a1[8] = {a1l.x, a1l.y, a1l.z, a1l.w, a1h.x, a1h.y, a1h.z, a1h.w};
-            const float b0[8] = {b0l.x, b0l.y, b0l.z, b0l.w, b0h.x, b0h.y, b0h.z, b0h.w};
-            const float b1[8] = {b1l.x, b1l.y, b1l.z, b1l.w, b1h.x, b1h.y, b1h.z, b1h.w};
-#pragma unroll
-            for (int st = 0; st < 8; ++st) {
-                acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[st], b0[st], acc[0][0], 0, 0, 0);
-                acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[st], b1[st], acc[0][1], 0, 0, 0);
-                acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[st], b0[st], acc[1][0], 0, 0, 0);
-                acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[st], b1[st], acc[1][1], 0, 0, 0);
+    // FULL: every row, column and K chunk of the tile exists (all but the
+    // edge tiles), so loads and stores need no bounds checks.
+    auto run = [&](auto full) {
+        constexpr bool FULL = decltype(full)::value;
+        v4f c00 = {0.f, 0.f, 0.f, 0.f}, c01 = c00, c10 = c00, c11 = c00;
+        // K chunk k0's X and W pieces of this thread (rows lr, lr + 32)
+        float4 px0, px1, pw0, pw1;
+        auto piece = [&](const float* __restrict__ base, int row0, int lim, int r, int gk) {
+            if constexpr (FULL) {
+                return *reinterpret_cast<const float4*>(base + static_cast<uint32_t>(r * K + gk));
+            } else {
+                float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (row0 + r < lim && gk < K) v = *reinterpret_cast<const float4*>(base + static_cast<int64_t>(r) * K + gk);
+                return v;
             }
-        }
-        __syncthreads();
-    }
+        };
+        const int nl = N - n0 < kGM ? static_cast<int>(N - n0) : kGM;  // rows of the tile that exist
+        auto fetch = [&](int k0) {
+            px0 = piece(Xt, 0, nl, lr, k0 + lc);
+            px1 = piece(Xt, 0, nl, lr + 32, k0 + lc);
+            pw0 = piece(Wt, c0, C, lr, k0 + lc);
+            pw1 = piece(Wt, c0, C, lr + 32, k0 + lc);
+        };
+        fetch(0);
+        for (int k0 = 0; k0 < K; k0 += kGK) {
+            *reinterpret_cast<float4*>(&sX[lr][lc]) = px0;
+            *reinterpret_cast<float4*>(&sX[lr + 32][lc]) = px1;
+            *reinterpret_cast<float4*>(&sW[lr][lc]) = pw0;
+            *reinterpret_cast<float4*>(&sW[lr + 32][lc]) = pw1;
+            __syncthreads();
+            // the next chunk's loads are in flight while this one's MFMAs run
+            if (k0 + kGK < K) fetch(k0 + kGK);
+            // The sum over k is order-free, so in MFMA step s of the chunk lane
+            // group j = lane / 16 supplies k = 8 j + s: its operands for all eight
+            // steps are 8 consecutive floats of one row, one 16-byte LDS read per
+            // half of four steps (16 operand registers live at a time).
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+            for (int hf = 0; hf < 2; ++hf) {
+                const int kb = 8 * (lane >> 4) + 4 * hf;
+                const int ra = wm + (lane & 15), rb = wn + (lane & 15);
+                const float4 a0 = *reinterpret_cast<const float4*>(&sX[ra][kb]);
+                const float4 a1 = *reinterpret_cast<const float4*>(&sX[ra + 16][kb]);
+                const float4 b0 = *reinterpret_cast<const float4*>(&sW[rb][kb]);
+                const float4 b1 = *reinterpret_cast<const float4*>(&sW[rb + 16][kb]);
+                const float av0[4] = {a0.x, a0.y, a0.z, a0.w}, av1[4] = {a1.x, a1.y, a1.z, a1.w};
+                const float bv0[4] = {b0.x, b0.y, b0.z, b0.w}, bv1[4] = {b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int col = c0 + wn + 16 * j + (lane & 15);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t row = n0 + wm + 16 * i + 4 * (lane >> 4) + r;
-                if (row < N && col < C) Z[row * C + col] = acc[i][j][r];
+                for (int st = 0; st < 4; ++st) {
+                    c00 = __builtin_amdgcn_mfma_f32_16x16x4f32(av0[st], bv0[st], c00, 0, 0, 0);
+                    c01 = __builtin_amdgcn_mfma_f32_16x16x4f32(av0[st], bv1[st], c01, 0, 0, 0);
+                    c10 = __builtin_amdgcn_mfma_f32_16x16x4f32(av1[st], bv0[st], c10, 0, 0, 0);
+                    c11 = __builtin_amdgcn_mfma_f32_16x16x4f32(av1[st], bv1[st], c11, 0, 0, 0);
+                }
             }
+            __syncthreads();
         }
+        const v4f acc[2][2] = {{c00, c01}, {c10, c11}};
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int col = wn + 16 * j + (lane & 15);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = wm + 16 * i + 4 * (lane >> 4) + r;
+                    if constexpr (FULL) {
+                        Zt[static_cast<uint32_t>(row * C + col)] = acc[i][j][r];
+                    } else {
+                        if (n0 + row < N && c0 + col < C) Zt[static_cast<int64_t>(row) * C + col] = acc[i][j][r];
+                    }
+                }
+            }
+    };
+    // (the 32-bit offsets: rows * K and rows * C within a tile stay below 2^31)
+    if (n0 + kGM <= N && c0 + kGN <= C && K % kGK == 0 && K <= INT32_MAX / kGM && C <= INT32_MAX / kGM)
+        run(std::true_type{});
+    else run(std::false_type{});
 }
 
 // ----------------------------------------------------------------------------
