@@ -87,7 +87,8 @@ __device__ __forceinline__ int rate_of_row(int row, int d_in, int d_out)
 // (multi-wave units) over the integer one.
 template <int D, bool FMAX = false>
 __device__ __forceinline__ void wave_addresses(const float* __restrict__ k, const float* __restrict__ q,
-                                               float* __restrict__ kh_out, float* __restrict__ e_out, int lane)
+                                               float* __restrict__ kh_out, float* __restrict__ e_out, int lane,
+                                               float* kh_lane = nullptr, float* e_lane = nullptr)
 {
     constexpr int EPH = (D + 31) / 32;
     const bool upper = lane >= 32;
@@ -123,6 +124,11 @@ __device__ __forceinline__ void wave_addresses(const float* __restrict__ k, cons
             const int j = hl + 32 * (upper ? i + 1 : i);
             kh_out[j] = pk;
             e_out[j] = pq - pk;
+            if (kh_lane != nullptr && i == (EPH == 2 ? 0 : -1)) {
+                // with two entries per lane (D = 64) entry j is this lane's own: j == lane
+                *kh_lane = pk;
+                *e_lane = pq - pk;
+            }
         }
     } else {
 #pragma unroll
@@ -134,6 +140,11 @@ __device__ __forceinline__ void wave_addresses(const float* __restrict__ k, cons
             if (!upper && j < D) {
                 kh_out[j] = p;
                 e_out[j] = pq - p;
+            }
+            if (kh_lane != nullptr && i == 0) {
+                // one entry per lane (D <= 32): lane j < D holds entry j
+                *kh_lane = p;
+                *e_lane = pq - p;
             }
         }
     }
@@ -301,16 +312,20 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
     __shared__ __attribute__((aligned(16))) float s_x[2][S][D_IN];
     // z_t, double-buffered by step parity so one barrier per step suffices.
     __shared__ __attribute__((aligned(16))) float s_z[2][R * G + 4];
-    // One-wave units that write the tape assemble each step's row in s_tr and
-    // write it with 16-byte stores: phi(k_t) and phi(q_t) - phi(k_t) are
-    // formed in place there, a_t, the rates and u_t are copied in.
     using TL = TapeLayout<M, D_IN>;
-    constexpr bool TAPE_LDS = TAPE && NW == 1;
-    static_assert(!TAPE_LDS || (TL::ROW % 4 == 0 && D_IN <= kWave), "16-byte pieces of the tape row");
-    __shared__ __attribute__((aligned(16))) float s_tr[TAPE_LDS ? TL::ROW : 4];
-    // Otherwise each wave forms phi(k_t) and phi(q_t) - phi(k_t) itself, in its own slice.
-    __shared__ __attribute__((aligned(16))) float s_kh[TAPE_LDS ? 1 : NW][TAPE_LDS ? 4 : D_IN];
-    __shared__ __attribute__((aligned(16))) float s_e[TAPE_LDS ? 1 : NW][TAPE_LDS ? 4 : D_IN];
+    // One-wave units write the tape with buffer stores straight from the
+    // registers that hold each entry: the row's address is a uniform
+    // descriptor per step (SGPRs; its record count is one tape row, so no
+    // store leaves the row), each lane's offset a constant.  (Assembling the
+    // row in LDS and copying it out with 16-byte stores measured 2.3% slower:
+    // with every register in use, the copy's two pieces per lane each waited
+    // for its LDS read before its store.)  Multi-wave units: wave 0 copies
+    // the vectors from LDS, every wave its a_t rows.
+    constexpr bool TAPE_BUF = TAPE && NW == 1;
+    static_assert(!TAPE_BUF || D_IN <= kWave, "one tape entry per lane of phi(k_t), e_t and u_t");
+    // Each wave forms phi(k_t) and phi(q_t) - phi(k_t) itself, in its own slice.
+    __shared__ __attribute__((aligned(16))) float s_kh[NW][D_IN];
+    __shared__ __attribute__((aligned(16))) float s_e[NW][D_IN];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -371,12 +386,8 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
     };
 
     XStage<D_IN, D_OUT, NW, P, BF16, TAPE> xs(tid, xv, x0, x_step, T);
-    if constexpr (TAPE_LDS) {
-        // the row's padding [m, KH_OFF) is written as zeros
-        for (int o = M + lane; o < TL::KH_OFF; o += kWave) s_tr[o] = 0.f;
-    }
-    float* const khs = TAPE_LDS ? s_tr + TL::KH_OFF : s_kh[wave];
-    float* const es = TAPE_LDS ? s_tr + TL::E_OFF : s_e[wave];
+    float* const khs = s_kh[wave];
+    float* const es = s_e[wave];
 
     // The wave that stores y_t.
     constexpr int WAVE_AUX = NW >= 2 ? 1 : 0;
@@ -431,6 +442,15 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
         }
         // ---- (A) Eq. (1): z = W u.
         float* __restrict__ zt = s_z[PAR];
+        // TAPE_BUF: one word of this step's tape row, through the row as a
+        // buffer resource (uniform, the same for every store of the step), at
+        // a lane-constant byte offset vb (VGPR) plus a compile-time one cb
+        // (the store's scalar offset)
+        auto tstore = [&](float v, int vb, int cb) {
+            const __amdgpu_buffer_rsrc_t row = __builtin_amdgcn_make_buffer_rsrc(
+                tape + ((int64_t)unit * T + t) * TL::ROW, (short)0, TL::ROW * 4, 0x00020000);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), row, vb, cb, 0);
+        };
         // Multi-wave units with a copy of the step per role: wave 0 reads its
         // rate-row columns of u, q^ - k^ and k^ together with the other
         // vectors, not right before use -- the rate rows are its extra work,
@@ -520,8 +540,8 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
                 accb = group_sum<16>(accb);
                 if constexpr (G_REG) {
                     gb = sigmoid_f32(accb);
-                    if constexpr (TAPE_LDS) {
-                        if ((lane & 15) == 0) s_tr[TL::G_OFF + brow] = brow < NLR ? gb : 0.f;
+                    if constexpr (TAPE_BUF) {
+                        tstore(brow < NLR ? gb : 0.f, 4 * brow, 4 * TL::G_OFF);  // the same word from the 16 lanes
                     }
                 } else {
                     // the other waves read the gates themselves
@@ -535,7 +555,16 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
 
         // ---- (B) phi(k), phi(q), sigma(beta), computed by every wave for
         // itself (identical bits in every wave); y_t from W_{t-1}.
-        wave_addresses<D_IN, (NW > 1)>(zt + D_OUT, zt + D_OUT + D_IN, khs, es, lane);
+        if constexpr (TAPE_BUF) {
+            float khl = 0.f, el = 0.f;
+            wave_addresses<D_IN, (NW > 1)>(zt + D_OUT, zt + D_OUT + D_IN, khs, es, lane, &khl, &el);
+            if (lane < D_IN) {
+                tstore(khl, 4 * lane, 4 * TL::KH_OFF);
+                tstore(el, 4 * lane, 4 * TL::E_OFF);
+            }
+        } else {
+            wave_addresses<D_IN, (NW > 1)>(zt + D_OUT, zt + D_OUT + D_IN, khs, es, lane);
+        }
         float gl = 0.f, g0, g1, g2, g3;
         if constexpr (G_REG) {
             g0 = readlane(gb, 0);
@@ -630,44 +659,46 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
             // learning rates and u_t (so the backward needs no projection and
             // no input softmax).
             float* __restrict__ tp = tape + ((int64_t)unit * T + t) * TL::ROW;
-            // a_t: the tape row buffer (one wave) or the tape itself
-            float* __restrict__ ta = TAPE_LDS ? s_tr : tp;
-            // (in multi-wave units, where every register row is a real row, no
-            // branch: it would split the last DPP level of each row sum into a
-            // move before it and an add after it -- few-shot taped forward
-            // 0.749 -> 0.728 ms; one-wave units keep it: without it they hold
-            // more values across the step and spill more, 10.89 -> 11.09 ms)
-            constexpr bool ALL_REAL = NW > 1 && R * G == ROWS;
+            if constexpr (TAPE_BUF) {
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const int row = rg + G * r;
-                if (ALL_REAL || row < ROWS) ta[row] = acc[r];  // the same word from all P lanes of the row
-            }
-            if constexpr (BETA_SEP) {
-                if constexpr (NW > 1) {
+                for (int r = 0; r < R; ++r) {
+                    const int row = rg + G * r;
+                    // (rows past ROWS are padding: their words would land on phi(k_t))
+                    if (R * G == ROWS || row < ROWS) tstore(acc[r], 4 * rg, 4 * G * r);  // the same word from all P lanes of the row
+                }
+                if constexpr (BETA_SEP) {
+                    // every lane of DPP row brow holds rate row brow's a (zero past n_lr: the row padding)
+                    tstore(brow < NLR ? accb : 0.f, 4 * brow, 4 * MAIN);
+                } else {
+                    if (lane < 4) tstore(lane < NLR ? gl : 0.f, 4 * lane, 4 * TL::G_OFF);
+                }
+                if (lane < D_IN) tstore(urow[lane], 4 * lane, 4 * TL::U_OFF);
+            } else {
+                // (where every register row is a real row, no branch: it would
+                // split the last DPP level of each row sum into a move before
+                // it and an add after it -- few-shot taped forward 0.749 ->
+                // 0.728 ms)
+                constexpr bool ALL_REAL = R * G == ROWS;
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int row = rg + G * r;
+                    if (ALL_REAL || row < ROWS) tp[row] = acc[r];  // the same word from all P lanes of the row
+                }
+                if constexpr (BETA_SEP) {
                     if (W0) keep(accb);
+                    if (W0 && (lane & 15) == 0 && brow < NLR) tp[MAIN + brow] = accb;
                 }
-                if (W0 && (lane & 15) == 0 && brow < NLR) ta[MAIN + brow] = accb;
-            }
-            if constexpr (TAPE_LDS) {
-                if constexpr (!G_REG) {
-                    if (lane < 4) s_tr[TL::G_OFF + lane] = lane < NLR ? gl : 0.f;
-                }
-                if (lane < D_IN) s_tr[TL::U_OFF + lane] = urow[lane];
-                wave_sync();
+                if (W0) {
 #pragma unroll
-                for (int o = 4 * lane; o < TL::ROW; o += 4 * kWave)
-                    *reinterpret_cast<float4*>(tp + o) = *reinterpret_cast<const float4*>(s_tr + o);
-            } else if (W0) {
-#pragma unroll
-                for (int j0 = 0; j0 < D_IN; j0 += kWave) {
-                    if (j0 + lane < D_IN) {
-                        tp[TL::KH_OFF + j0 + lane] = khw[j0 + lane];
-                        tp[TL::E_OFF + j0 + lane] = ew[j0 + lane];
-                        tp[TL::U_OFF + j0 + lane] = urow[j0 + lane];
+                    for (int j0 = 0; j0 < D_IN; j0 += kWave) {
+                        if (j0 + lane < D_IN) {
+                            tp[TL::KH_OFF + j0 + lane] = khw[j0 + lane];
+                            tp[TL::E_OFF + j0 + lane] = ew[j0 + lane];
+                            tp[TL::U_OFF + j0 + lane] = urow[j0 + lane];
+                        }
                     }
+                    if (lane < 4) tp[TL::G_OFF + lane] = lane < NLR ? gl : 0.f;
                 }
-                if (lane < 4) tp[TL::G_OFF + lane] = lane < NLR ? gl : 0.f;
             }
         }
         // ---- (D) Eq. (3)/(5): W += a kh^T, in place.
