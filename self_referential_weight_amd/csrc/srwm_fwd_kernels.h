@@ -313,16 +313,19 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
     // z_t, double-buffered by step parity so one barrier per step suffices.
     __shared__ __attribute__((aligned(16))) float s_z[2][R * G + 4];
     using TL = TapeLayout<M, D_IN>;
-    // One-wave units write the tape with buffer stores straight from the
-    // registers that hold each entry: the row's address is a uniform
-    // descriptor per step (SGPRs; its record count is one tape row, so no
-    // store leaves the row), each lane's offset a constant.  (Assembling the
-    // row in LDS and copying it out with 16-byte stores measured 2.3% slower:
-    // with every register in use, the copy's two pieces per lane each waited
-    // for its LDS read before its store.)  Multi-wave units: wave 0 copies
-    // the vectors from LDS, every wave its a_t rows.
-    constexpr bool TAPE_BUF = TAPE && NW == 1;
-    static_assert(!TAPE_BUF || D_IN <= kWave, "one tape entry per lane of phi(k_t), e_t and u_t");
+    // The tape is written with buffer stores straight from the registers that
+    // hold each entry (d_in <= 64: one entry of phi(k_t), e_t and u_t per
+    // lane): the row's address is a uniform descriptor per step (SGPRs; its
+    // record count is one tape row, so no store leaves the row), each lane's
+    // offset a constant.  Every wave stores its a_t rows, wave 0 the rest.
+    // (One-wave units used to assemble the row in LDS and copy it out with
+    // 16-byte stores, 2.3% slower: with every register in use, the copy's two
+    // pieces per lane each waited for its LDS read before its store; wave 0 of
+    // multi-wave units read the vectors back from LDS, 2.3% slower on the
+    // few-shot taped forward.)  At d_in = 128 wave 0 copies the vectors from
+    // LDS and every wave stores its a_t rows through plain pointers.
+    constexpr bool TAPE_BUF = TAPE && D_IN <= kWave;
+    static_assert(!(TAPE && NW == 1) || D_IN <= kWave, "one tape entry per lane of phi(k_t), e_t and u_t");
     // Each wave forms phi(k_t) and phi(q_t) - phi(k_t) itself, in its own slice.
     __shared__ __attribute__((aligned(16))) float s_kh[NW][D_IN];
     __shared__ __attribute__((aligned(16))) float s_e[NW][D_IN];
@@ -558,7 +561,7 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
         if constexpr (TAPE_BUF) {
             float khl = 0.f, el = 0.f;
             wave_addresses<D_IN, (NW > 1)>(zt + D_OUT, zt + D_OUT + D_IN, khs, es, lane, &khl, &el);
-            if (lane < D_IN) {
+            if (W0 && lane < D_IN) {  // (every wave forms them; wave 0 stores them)
                 tstore(khl, 4 * lane, 4 * TL::KH_OFF);
                 tstore(el, 4 * lane, 4 * TL::E_OFF);
             }
@@ -666,13 +669,20 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
                     // (rows past ROWS are padding: their words would land on phi(k_t))
                     if (R * G == ROWS || row < ROWS) tstore(acc[r], 4 * rg, 4 * G * r);  // the same word from all P lanes of the row
                 }
-                if constexpr (BETA_SEP) {
-                    // every lane of DPP row brow holds rate row brow's a (zero past n_lr: the row padding)
-                    tstore(brow < NLR ? accb : 0.f, 4 * brow, 4 * MAIN);
-                } else {
-                    if (lane < 4) tstore(lane < NLR ? gl : 0.f, 4 * lane, 4 * TL::G_OFF);
+                if constexpr (BETA_SEP && NW > 1) {
+                    if (W0) keep(accb);  // (its last DPP level not sunk into the branch below)
                 }
-                if (lane < D_IN) tstore(urow[lane], 4 * lane, 4 * TL::U_OFF);
+                if (W0) {
+                    if constexpr (BETA_SEP) {
+                        // every lane of DPP row brow holds rate row brow's a (zero past n_lr: the row padding)
+                        tstore(brow < NLR ? accb : 0.f, 4 * brow, 4 * MAIN);
+                    }
+                    // the rates: from the gate registers (one wave), else lanes 0..3 hold them
+                    if (NW > 1 || !BETA_SEP) {
+                        if (lane < 4) tstore(lane < NLR ? gl : 0.f, 4 * lane, 4 * TL::G_OFF);
+                    }
+                    if (lane < D_IN) tstore(urow[lane], 4 * lane, 4 * TL::U_OFF);
+                }
             } else {
                 // (where every register row is a real row, no branch: it would
                 // split the last DPP level of each row sum into a move before
