@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "srwm_device.h"
 
 namespace srwm {
@@ -430,212 +432,227 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
         __syncthreads();
     }
 
-    int slot = (T - 1) % 3;
-    for (int t = T - 1; t >= 0; --t) {
-        const float* __restrict__ tt = s_ring[slot];
-        const float* __restrict__ us = tt + TL::U_OFF;
-        const float* __restrict__ gs = tt + TW;
-        const int par = t & 1;
+    // One step t of the walk.  The input ring slot is t mod 3 and the
+    // exchange area t mod 2: in the loop six steps at a time both are
+    // constants, so every LDS address is a lane-constant base plus an
+    // immediate offset (no per-step slot arithmetic).
+    auto bstep = [&](const int t, auto slot_v, auto par_v) {
+            const int slot = slot_v, par = par_v;  // (compile-time constants in the unrolled loop below)
+            const float* __restrict__ tt = s_ring[slot];
+            const float* __restrict__ us = tt + TL::U_OFF;
+            const float* __restrict__ gs = tt + TW;
 
-        // ---- (A) undo the update of step t; ah, khh, rh, eh.
-        float a[R], kt[L];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int row = srow(r);
-            const float av = tt[row_at(r, row)];
-            a[r] = row_ok(r, row) ? av : 0.f;
-        }
-        load_f32<L>(tt + TL::KH_OFF + p * L, kt);
-        const float4 gv = *reinterpret_cast<const float4*>(tt + TL::G_OFF);
-        const float gate[4] = {gv.x, gv.y, gv.z, gv.w};
-
-        // ah of the rows: per register row with SW = 1 (and for the beta
-        // row); with swizzled runs, ar[j] is the total of row p mod SW of run j
-        float khh[L], ah[R], pr[R], ar[RS / SW];
-#pragma unroll
-        for (int c = 0; c < L; ++c) khh[c] = 0.f;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            if (r == R - 1 && last_empty) {
-                ah[r] = 0.f;
-                continue;
-            }
-            float as = 0.f;
-#pragma unroll
-            for (int c = 0; c < L; ++c) {
-                w[r][c] = fmaf(-a[r], kt[c], w[r][c]);
-                as = fmaf(wh[r][c], kt[c], as);
-                khh[c] = fmaf(wh[r][c], a[r], khh[c]);
-            }
-            if (SW > 1 && r < RS) {
-                pr[r] = as;
-                if (r % SW == SW - 1) {
-                    ar[r / SW] = RunSum<SW>::total(&pr[r + 1 - SW]);
-                    keep(ar[r / SW]);  // (as below: no DPP level split over the branch)
-                }
-            } else {
-                ah[r] = group_sum<P>(as);
-                // complete in every lane here: otherwise the last DPP level of
-                // each sum is split into a move before the last row's branch and
-                // an add after it (12 extra instructions per step)
-                keep(ah[r]);
-            }
-        }
-        float bp[4] = {0.f, 0.f, 0.f, 0.f};
-        float rh[R], eh[L];
-#pragma unroll
-        for (int c = 0; c < L; ++c) eh[c] = 0.f;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            if (SW > 1 && r < RS) {
-                // the run's rates from its one total: rh by quad_perm; the
-                // betah partial sum_i ah_i a_i over the run's rows by a quad sum
-                // (slot 0 holds row p mod SW, the one whose total this lane has)
-                const int s = r % SW, j = r / SW;
-                rh[r] = RunSum<SW>::slot(s, gate[rate(r)] * ar[j]);
-                if (s == 0) {
-                    float pb = ar[j] * a[r];
-                    keep(pb);  // (a multiply, not folded into the first add: that add takes the DPP)
-                    pb = RunSum<SW>::quad_sum(pb);
-                    keep(pb);
-                    bp[rate(r)] += pb;
-                }
-            } else {
-                // (a skipped last row has ah = 0 and W = 0: no branch here)
-                rh[r] = gate[rate(r)] * ah[r];
-                bp[rate(r)] = fmaf(ah[r], a[r], bp[rate(r)]);
-            }
-#pragma unroll
-            for (int c = 0; c < L; ++c) eh[c] = fmaf(w[r][c], rh[r], eh[c]);
-        }
-        // (every lane of a row group holds the same bp: the exchange sums them
-        // over the row-group lane bits only, and one lane per DPP row writes)
-        // part[2] holds uh of step t+1 (zero before the first step)
-#pragma unroll
-        for (int c = 0; c < L; ++c) {
-            part[0][c] = khh[c];
-            part[1][c] = eh[c];
-        }
-        exchange(par, bp);
-
-        // stage the inputs of step t-1 (two slots away from anything in use)
-        const int slot_prev = slot == 0 ? 2 : slot - 1;
-        if (t > 0) {
-            stage(slot_prev);
-            if (t > 1) fetch(t - 2);
-        }
-        __syncthreads();
-
-        // ---- (B) per column (lane j): totals, dx of step t+1, kbar, qbar, betah.
-        float khh_j, eh_j, uh1_j;
-        gather(par, khh_j, eh_j, uh1_j);
-        if (t + 1 < T && wave == ((t + 1) & (NW - 1))) store_dx(t + 1, uh1_j, u_next);
-        u_next = lane < D_IN ? us[jc] : 0.f;
-        float kbar_v = 0.f, qbar_v = 0.f, zb = 0.f;  // BCAST: this lane's column of kbar, qbar; its beta row
-        {
-            // betah totals (with dealt columns each lane of the wave that
-            // holds the beta rows sums its own row's, below)
-            float bt[4] = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (!BCAST) {
-#pragma unroll
-                for (int c = 0; c < NLR; ++c) bt[c] = s_bred[par][0][c];
-#pragma unroll
-                for (int wv = 1; wv < NW; ++wv)
-#pragma unroll
-                    for (int c = 0; c < NLR; ++c) bt[c] += s_bred[par][wv][c];
-            }
-            const float kh_j = lane < D_IN ? tt[TL::KH_OFF + jc] : 0.f;
-            const float e_j = lane < D_IN ? tt[TL::E_OFF + jc] : 0.f;
-            const float qh_j = kh_j + e_j;
-            const float kb = khh_j - eh_j;
-            // <kb, kh> and <eh, qh> over the 64 columns with one reduction: the
-            // lower half-wave sums the first, the upper the second (columns j
-            // and j +/- 32 joined by a lane-row swap), then a swap hands each
-            // half the other's total.
-            float pk = kb * kh_j, pq = eh_j * qh_j;
-            swap32(pk, pq);                       // lower: kb kh of j, j+32; upper: eh qh of j-32, j
-            float dk = half_sum(pk + pq);         // lower half: <kb, kh>; upper half: <eh, qh>
-            float dq = dk;
-            swap32(dk, dq);                       // every lane: dk = lower's total, dq = upper's
-            if constexpr (BCAST) {
-                kbar_v = kh_j * (kb - dk);
-                qbar_v = qh_j * (eh_j - dq);
-                if constexpr (ZLDS) {
-                    // column jc of this wave's dealt columns (all 64 in every wave)
-                    s_zh[wave][D_OUT + jc] = kbar_v;
-                    s_zh[wave][D_OUT + D_IN + jc] = qbar_v;
-                }
-                if (!last_empty) {
-                    // this lane's beta row rg (rows past M hold zb = 0)
-                    const int c = rg < NLR ? rg : 0;
-                    float bsum = s_bred[par][0][c];
-#pragma unroll
-                    for (int wv = 1; wv < NW; ++wv) bsum += s_bred[par][wv][c];
-                    zb = rg < NLR ? (1.f - tt[TL::G_OFF + c]) * bsum : 0.f;
-                }
-            } else {
-                if (lane < D_IN) {
-                    s_zh[wave][D_OUT + lane] = kh_j * (kb - dk);
-                    s_zh[wave][D_OUT + D_IN + lane] = qh_j * (eh_j - dq);
-                }
-                if (lane < NLR) {
-                    const float bv = lane == 0 ? bt[0] : lane == 1 ? bt[1] : lane == 2 ? bt[2] : bt[3];
-                    const float gl = lane == 0 ? gate[0] : lane == 1 ? gate[1] : lane == 2 ? gate[2] : gate[3];
-                    s_zh[wave][MAIN + lane] = (1.f - gl) * bv;
-                }
-            }
-        }
-        if constexpr (ZLDS) wave_sync();
-
-        // ---- (C) uh of step t (column partials, reduced with step t-1); Wh update.
-        float ev[L], uv[L];
-        load_f32<L>(tt + TL::E_OFF + p * L, ev);
-        load_f32<L>(us + p * L, uv);
-#pragma unroll
-        for (int c = 0; c < L; ++c) part[2][c] = 0.f;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            if (r == R - 1 && last_empty) continue;
-            const int row = srow(r);
-            float zr;
-            if (G * r < D_OUT) zr = gs[row];
-            else if constexpr (BCAST) {
-                // rows of the beta block past M hold zb = 0
-                if (r >= RS) zr = zb;
-                else if constexpr (ZLDS) zr = s_zh[wave][row];
-                else zr = G * r < D_OUT + D_IN ? row_bcast(kbar_v, r - D_OUT / G)
-                                               : row_bcast(qbar_v, r - (D_OUT + D_IN) / G);
-            } else {
-                const float zv = s_zh[wave][row_at(r, row)];
-                zr = row_ok(r, row) ? zv : 0.f;
-            }
-#pragma unroll
-            for (int c = 0; c < L; ++c) {
-                part[2][c] = fmaf(w[r][c], zr, part[2][c]);
-                wh[r][c] = fmaf(rh[r], ev[c], fmaf(zr, uv[c], wh[r][c]));
-            }
-        }
-        slot = slot_prev;
-
-        // Reset ablation: step t = wR started window w from the initial state.
-        // The adjoint now held is window w's share of dL/d(initial state); the
-        // end state of window w-1, which the reset discarded, has a zero adjoint,
-        // and the walk continues from that end state as the forward pass
-        // recorded it (undoing updates cannot cross the reset).
-        if (RESET && t == next_reset && t > 0) {
-            add_share();
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-#pragma unroll
-                for (int c = 0; c < L; ++c) wh[r][c] = 0.f;
-            const float* __restrict__ ws = wstates + ((int64_t)unit * n_resets + (t / reset_interval - 1)) * M * D_IN;
-#pragma unroll
+            // ---- (A) undo the update of step t; ah, khh, rh, eh.
+            float a[R], kt[L];
+    #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const int row = srow(r);
-                if (row < M) load_f32<L>(ws + row * D_IN + p * L, w[r]);
+                const float av = tt[row_at(r, row)];
+                a[r] = row_ok(r, row) ? av : 0.f;
             }
-            next_reset -= reset_interval;
-        }
+            load_f32<L>(tt + TL::KH_OFF + p * L, kt);
+            const float4 gv = *reinterpret_cast<const float4*>(tt + TL::G_OFF);
+            const float gate[4] = {gv.x, gv.y, gv.z, gv.w};
+
+            // ah of the rows: per register row with SW = 1 (and for the beta
+            // row); with swizzled runs, ar[j] is the total of row p mod SW of run j
+            float khh[L], ah[R], pr[R], ar[RS / SW];
+    #pragma unroll
+            for (int c = 0; c < L; ++c) khh[c] = 0.f;
+    #pragma unroll
+            for (int r = 0; r < R; ++r) {
+                if (r == R - 1 && last_empty) {
+                    ah[r] = 0.f;
+                    continue;
+                }
+                float as = 0.f;
+    #pragma unroll
+                for (int c = 0; c < L; ++c) {
+                    w[r][c] = fmaf(-a[r], kt[c], w[r][c]);
+                    as = fmaf(wh[r][c], kt[c], as);
+                    khh[c] = fmaf(wh[r][c], a[r], khh[c]);
+                }
+                if (SW > 1 && r < RS) {
+                    pr[r] = as;
+                    if (r % SW == SW - 1) {
+                        ar[r / SW] = RunSum<SW>::total(&pr[r + 1 - SW]);
+                        keep(ar[r / SW]);  // (as below: no DPP level split over the branch)
+                    }
+                } else {
+                    ah[r] = group_sum<P>(as);
+                    // complete in every lane here: otherwise the last DPP level of
+                    // each sum is split into a move before the last row's branch and
+                    // an add after it (12 extra instructions per step)
+                    keep(ah[r]);
+                }
+            }
+            float bp[4] = {0.f, 0.f, 0.f, 0.f};
+            float rh[R], eh[L];
+    #pragma unroll
+            for (int c = 0; c < L; ++c) eh[c] = 0.f;
+    #pragma unroll
+            for (int r = 0; r < R; ++r) {
+                if (SW > 1 && r < RS) {
+                    // the run's rates from its one total: rh by quad_perm; the
+                    // betah partial sum_i ah_i a_i over the run's rows by a quad sum
+                    // (slot 0 holds row p mod SW, the one whose total this lane has)
+                    const int s = r % SW, j = r / SW;
+                    rh[r] = RunSum<SW>::slot(s, gate[rate(r)] * ar[j]);
+                    if (s == 0) {
+                        float pb = ar[j] * a[r];
+                        keep(pb);  // (a multiply, not folded into the first add: that add takes the DPP)
+                        pb = RunSum<SW>::quad_sum(pb);
+                        keep(pb);
+                        bp[rate(r)] += pb;
+                    }
+                } else {
+                    // (a skipped last row has ah = 0 and W = 0: no branch here)
+                    rh[r] = gate[rate(r)] * ah[r];
+                    bp[rate(r)] = fmaf(ah[r], a[r], bp[rate(r)]);
+                }
+    #pragma unroll
+                for (int c = 0; c < L; ++c) eh[c] = fmaf(w[r][c], rh[r], eh[c]);
+            }
+            // (every lane of a row group holds the same bp: the exchange sums them
+            // over the row-group lane bits only, and one lane per DPP row writes)
+            // part[2] holds uh of step t+1 (zero before the first step)
+    #pragma unroll
+            for (int c = 0; c < L; ++c) {
+                part[0][c] = khh[c];
+                part[1][c] = eh[c];
+            }
+            exchange(par, bp);
+
+            // stage the inputs of step t-1 (two slots away from anything in use)
+            const int slot_prev = slot == 0 ? 2 : slot - 1;
+            if (t > 0) {
+                stage(slot_prev);
+                if (t > 1) fetch(t - 2);
+            }
+            __syncthreads();
+
+            // ---- (B) per column (lane j): totals, dx of step t+1, kbar, qbar, betah.
+            float khh_j, eh_j, uh1_j;
+            gather(par, khh_j, eh_j, uh1_j);
+            if (t + 1 < T && wave == ((t + 1) & (NW - 1))) store_dx(t + 1, uh1_j, u_next);
+            u_next = lane < D_IN ? us[jc] : 0.f;
+            float kbar_v = 0.f, qbar_v = 0.f, zb = 0.f;  // BCAST: this lane's column of kbar, qbar; its beta row
+            {
+                // betah totals (with dealt columns each lane of the wave that
+                // holds the beta rows sums its own row's, below)
+                float bt[4] = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (!BCAST) {
+    #pragma unroll
+                    for (int c = 0; c < NLR; ++c) bt[c] = s_bred[par][0][c];
+    #pragma unroll
+                    for (int wv = 1; wv < NW; ++wv)
+    #pragma unroll
+                        for (int c = 0; c < NLR; ++c) bt[c] += s_bred[par][wv][c];
+                }
+                const float kh_j = lane < D_IN ? tt[TL::KH_OFF + jc] : 0.f;
+                const float e_j = lane < D_IN ? tt[TL::E_OFF + jc] : 0.f;
+                const float qh_j = kh_j + e_j;
+                const float kb = khh_j - eh_j;
+                // <kb, kh> and <eh, qh> over the 64 columns with one reduction: the
+                // lower half-wave sums the first, the upper the second (columns j
+                // and j +/- 32 joined by a lane-row swap), then a swap hands each
+                // half the other's total.
+                float pk = kb * kh_j, pq = eh_j * qh_j;
+                swap32(pk, pq);                       // lower: kb kh of j, j+32; upper: eh qh of j-32, j
+                float dk = half_sum(pk + pq);         // lower half: <kb, kh>; upper half: <eh, qh>
+                float dq = dk;
+                swap32(dk, dq);                       // every lane: dk = lower's total, dq = upper's
+                if constexpr (BCAST) {
+                    kbar_v = kh_j * (kb - dk);
+                    qbar_v = qh_j * (eh_j - dq);
+                    if constexpr (ZLDS) {
+                        // column jc of this wave's dealt columns (all 64 in every wave)
+                        s_zh[wave][D_OUT + jc] = kbar_v;
+                        s_zh[wave][D_OUT + D_IN + jc] = qbar_v;
+                    }
+                    if (!last_empty) {
+                        // this lane's beta row rg (rows past M hold zb = 0)
+                        const int c = rg < NLR ? rg : 0;
+                        float bsum = s_bred[par][0][c];
+    #pragma unroll
+                        for (int wv = 1; wv < NW; ++wv) bsum += s_bred[par][wv][c];
+                        zb = rg < NLR ? (1.f - tt[TL::G_OFF + c]) * bsum : 0.f;
+                    }
+                } else {
+                    if (lane < D_IN) {
+                        s_zh[wave][D_OUT + lane] = kh_j * (kb - dk);
+                        s_zh[wave][D_OUT + D_IN + lane] = qh_j * (eh_j - dq);
+                    }
+                    if (lane < NLR) {
+                        const float bv = lane == 0 ? bt[0] : lane == 1 ? bt[1] : lane == 2 ? bt[2] : bt[3];
+                        const float gl = lane == 0 ? gate[0] : lane == 1 ? gate[1] : lane == 2 ? gate[2] : gate[3];
+                        s_zh[wave][MAIN + lane] = (1.f - gl) * bv;
+                    }
+                }
+            }
+            if constexpr (ZLDS) wave_sync();
+
+            // ---- (C) uh of step t (column partials, reduced with step t-1); Wh update.
+            float ev[L], uv[L];
+            load_f32<L>(tt + TL::E_OFF + p * L, ev);
+            load_f32<L>(us + p * L, uv);
+    #pragma unroll
+            for (int c = 0; c < L; ++c) part[2][c] = 0.f;
+    #pragma unroll
+            for (int r = 0; r < R; ++r) {
+                if (r == R - 1 && last_empty) continue;
+                const int row = srow(r);
+                float zr;
+                if (G * r < D_OUT) zr = gs[row];
+                else if constexpr (BCAST) {
+                    // rows of the beta block past M hold zb = 0
+                    if (r >= RS) zr = zb;
+                    else if constexpr (ZLDS) zr = s_zh[wave][row];
+                    else zr = G * r < D_OUT + D_IN ? row_bcast(kbar_v, r - D_OUT / G)
+                                                   : row_bcast(qbar_v, r - (D_OUT + D_IN) / G);
+                } else {
+                    const float zv = s_zh[wave][row_at(r, row)];
+                    zr = row_ok(r, row) ? zv : 0.f;
+                }
+    #pragma unroll
+                for (int c = 0; c < L; ++c) {
+                    part[2][c] = fmaf(w[r][c], zr, part[2][c]);
+                    wh[r][c] = fmaf(rh[r], ev[c], fmaf(zr, uv[c], wh[r][c]));
+                }
+            }
+
+            // Reset ablation: step t = wR started window w from the initial state.
+            // The adjoint now held is window w's share of dL/d(initial state); the
+            // end state of window w-1, which the reset discarded, has a zero adjoint,
+            // and the walk continues from that end state as the forward pass
+            // recorded it (undoing updates cannot cross the reset).
+            if (RESET && t == next_reset && t > 0) {
+                add_share();
+    #pragma unroll
+                for (int r = 0; r < R; ++r)
+    #pragma unroll
+                    for (int c = 0; c < L; ++c) wh[r][c] = 0.f;
+                const float* __restrict__ ws = wstates + ((int64_t)unit * n_resets + (t / reset_interval - 1)) * M * D_IN;
+    #pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int row = srow(r);
+                    if (row < M) load_f32<L>(ws + row * D_IN + p * L, w[r]);
+                }
+                next_reset -= reset_interval;
+            }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    int t = T - 1;
+    for (; t >= 0 && t % 6 != 5; --t) bstep(t, t % 3, t & 1);  // down to a step t = 5 (mod 6)
+    for (; t >= 5; t -= 6) {
+        bstep(t, I2{}, I1{});
+        bstep(t - 1, I1{}, I0{});
+        bstep(t - 2, I0{}, I1{});
+        bstep(t - 3, I2{}, I0{});
+        bstep(t - 4, I1{}, I1{});
+        bstep(t - 5, I0{}, I0{});
     }
 
     if (T > 0) {
