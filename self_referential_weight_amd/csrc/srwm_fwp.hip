@@ -302,7 +302,9 @@ __global__ __launch_bounds__((NW + NPW) * 64) void srwm_fast_kernel(const float*
             if (c0 + 2 * S < T) load_chunk(c0 + 2 * S);
         }
         const int n = !rec ? 0 : (T - c0) < S ? (T - c0) : S;
-        for (int s = 0; s < n; ++s) {
+        // step c0 + s of the chunk (in a full chunk every s is a constant:
+        // the prepared vectors' LDS addresses and y's offset are immediates)
+        auto fstep = [&](const int s) {
             const float* __restrict__ ps = s_p[buf][s];
             float kh[L], qh[L];
             load_f32<L>(ps + p * L, kh);
@@ -338,6 +340,12 @@ __global__ __launch_bounds__((NW + NPW) * 64) void srwm_fast_kernel(const float*
                 asm volatile("" : "+v"(yv));
                 if (p == 0 && lr < RW) y[yt + lr] = yv;
             }
+        };
+        if (n == S) {
+#pragma unroll
+            for (int s = 0; s < S; ++s) fstep(s);
+        } else {
+            for (int s = 0; s < n; ++s) fstep(s);
         }
         __syncthreads();
     }
