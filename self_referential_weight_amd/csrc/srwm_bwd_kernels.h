@@ -847,16 +847,19 @@ void srwm_bwd_wide_kernel(const float* __restrict__ WTin,
     constexpr int NGC = D_OUT / kWave;             // pieces of a gy row
     static_assert(NPC <= 2 * NW && NPC % NW + NGC <= NW, "one or two tape pieces and at most one gy piece per wave");
     const int wu = __builtin_amdgcn_readfirstlane(wave);
+    // one buffer resource per row (wave-uniform, SGPRs) and the lane's byte
+    // offset as the only per-lane operand: no 64-bit lane addresses held
+    const int lane4 = 4 * lane;
     auto fetch = [&](int t, int slot) {
-        const float* __restrict__ tpp = tp0 + (int64_t)t * TW;
+        const __amdgpu_buffer_rsrc_t trow = float_rsrc(tp0 + (int64_t)t * TW, TW);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int k = wu + NW * i;
-            if (k < NPC && kWave * k + lane < TW) copy_dword_to_lds(tpp + kWave * k + lane, &s_tape[slot][kWave * k]);
+            if (k < NPC && kWave * k + lane < TW) copy_dword_to_lds(trow, lane4, 4 * kWave * k, &s_tape[slot][kWave * k]);
         }
         const int kg = wu - NPC % NW;  // gy piece of the waves after those with two tape pieces
         if (kg >= 0 && kg < NGC)
-            copy_dword_to_lds(gy + y0 + (int64_t)t * y_step + kWave * kg + lane, &s_gy[slot][kWave * kg]);
+            copy_dword_to_lds(float_rsrc(gy + y0 + (int64_t)t * y_step, D_OUT), lane4, 4 * kWave * kg, &s_gy[slot][kWave * kg]);
     };
 
     float part[3][L];
@@ -891,7 +894,7 @@ void srwm_bwd_wide_kernel(const float* __restrict__ WTin,
             float lo = bp[0] + bp[2], hi = bp[1] + bp[3];
             swap16(lo, hi);
             const float tot = lo + hi;
-            if ((lane & 15) == 0) s_bred[par][wave][lane >> 4] = tot;
+            if ((lane & 15) == 0) s_bred[par][wave][lane_now() >> 4] = tot;
         } else {
             const float tot = pair_sum<5>(pair_sum<4>(bp[0]));
             if (lane == 0) s_bred[par][wave][0] = tot;
@@ -922,8 +925,9 @@ void srwm_bwd_wide_kernel(const float* __restrict__ WTin,
 #pragma unroll
             for (int c = 0; c < CPL; ++c) d[c] = u_j[c] * (uh_j[c] - du);
         }
+        const __amdgpu_buffer_rsrc_t xrow = float_rsrc(dx + x0 + (int64_t)t * x_step, D_IN);
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) dx[x0 + (int64_t)t * x_step + lane + kWave * c] = d[c];
+        for (int c = 0; c < CPL; ++c) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(d[c]), xrow, lane4, 4 * kWave * c, 0);
     };
 
 #pragma unroll
@@ -1080,7 +1084,7 @@ void srwm_bwd_wide_kernel(const float* __restrict__ WTin,
             if (wave == 0 && lane < NLR) {
                 const float bv = lane == 0 ? bt[0] : lane == 1 ? bt[1] : lane == 2 ? bt[2] : bt[3];
                 const float gl = lane == 0 ? gate[0] : lane == 1 ? gate[1] : lane == 2 ? gate[2] : gate[3];
-                s_zh[0][NZ - 4 + lane] = (1.f - gl) * bv;
+                s_zh[0][NZ - 4 + lane_now()] = (1.f - gl) * bv;
             }
         }
         wave_sync();
@@ -1113,7 +1117,8 @@ void srwm_bwd_wide_kernel(const float* __restrict__ WTin,
             }
         }
         if (wave == 0) {
-            const float zv = s_zh[0][NZ - 4 + (rg < NLR ? rg : 0)];
+            const int rg0 = lane_now() / P;  // rg of wave 0's lanes
+            const float zv = s_zh[0][NZ - 4 + (rg0 < NLR ? rg0 : 0)];
             const float zr = rg < NLR ? zv : 0.f;
             float wv[L], wh[L];
             lds_get(&s_wb[0][rg][0], wv);

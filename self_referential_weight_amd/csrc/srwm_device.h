@@ -359,15 +359,37 @@ __device__ __forceinline__ void wave_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Asynchronous copy of one dword per active lane from global memory straight
-// into LDS (gfx950 global_load_lds_dword): lane i of the wave writes
-// lds_base[i], lds_base uniform over the wave.  The copy is tracked by vmcnt:
-// wait_vmem() before the workgroup barrier after which the LDS words are read.
+// Asynchronous copy of one dword per active lane from a buffer straight into
+// LDS (gfx950 buffer_load_dword ... lds): lane i of the wave reads the dword
+// at byte voff + soff of the buffer described by rsrc and writes lds_base[i],
+// lds_base uniform over the wave.  voff is the lane's own byte offset, soff a
+// wave-uniform one; a read past the resource's num_records yields zero.  The
+// copy is tracked by vmcnt: wait_vmem() before the workgroup barrier after
+// which the LDS words are read.
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void global_void_t;
-__device__ __forceinline__ void copy_dword_to_lds(const float* src_lane, float* lds_base)
+__device__ __forceinline__ void copy_dword_to_lds(__amdgpu_buffer_rsrc_t rsrc, int voff, int soff, float* lds_base)
 {
-    __builtin_amdgcn_global_load_lds((global_void_t*)(src_lane), (lds_void_t*)(lds_base), 4, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds_base), 4, voff, soff, 0, 0);
+}
+
+// Buffer resource over n floats at base (raw buffer, bounds-checked against
+// n * 4 bytes): its four dwords are wave-uniform, so they live in SGPRs.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t float_rsrc(const float* base, int n)
+{
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, n * 4, 0x00020000);
+}
+
+// The lane's index in its wave, computed afresh at each call (two VALU
+// instructions with no register inputs; volatile, so never hoisted): for a
+// lane-constant LDS address used once per loop iteration in a kernel whose
+// registers are full, cheaper than holding the address live across the loop,
+// which there means a spill and a scratch reload with a wait on every
+// outstanding vector-memory operation.
+__device__ __forceinline__ int lane_now()
+{
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
 }
 
 // s_waitcnt vmcnt(0): every vector memory operation of this wave has completed
