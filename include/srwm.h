@@ -98,7 +98,8 @@ enum {
  * untouched and writes W_T[b,h] = W0[h].  NaN/Inf in x or W0 propagate; they
  * are not checked.  Outputs must not overlap inputs or each other
  * (SRWM_ERR_ALIAS).  Pointers may be NULL only when the tensor they address
- * is empty.  Returns SRWM_OK or a negative error code.
+ * is empty.  One step's row of x, H*d_in elements, may span at most 64 MiB
+ * (SRWM_ERR_SHAPE beyond).  Returns SRWM_OK or a negative error code.
  */
 int srwm_forward(const void* x, const float* W0, void* y, float* W_T,
                  int64_t B, int64_t T, int64_t H, int64_t d_in, int64_t d_out,

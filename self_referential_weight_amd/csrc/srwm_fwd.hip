@@ -146,6 +146,10 @@ int forward_check(const srwm_forward_args_t* a, FwdPlan* plan)
         return SRWM_ERR_SHAPE;
     if (!want_tape) ntape = 0;
     if (units > INT32_MAX || S > INT32_MAX || H > INT32_MAX) return SRWM_ERR_SHAPE;
+    // the kernels address a chunk of up to 32 steps of x with a lane's 32-bit
+    // offset from the chunk's first row: one step's row (H*d_in elements) may
+    // span at most 64 MiB
+    if (H * d_in * es > (INT64_C(1) << 26)) return SRWM_ERR_SHAPE;
     const void* x = a->x;
     const float* W0 = a->W0;
     void* y = a->y;

@@ -460,6 +460,10 @@ def test_size_limits():
     assert call(B=2 ** 31, H=1, T=1) == E_SHAPE
     assert call(B=1, H=1, T=2 ** 31) == E_SHAPE
     assert call_ex(B=2 ** 16, H=2 ** 16, T=1) == E_SHAPE
+    # a chunk of x is addressed with 32-bit lane offsets: a step's row of x
+    # (H*d_in elements) may span at most 64 MiB
+    assert call(B=1, H=2 ** 20 + 1, T=1) == E_SHAPE  # fp32, d_in = 16
+    assert call(B=1, H=2 ** 21 + 1, T=1, io=1) == E_SHAPE  # bf16
     assert call_bwd(B=2 ** 31, H=1, T=1) == E_SHAPE
     assert call_bwd(T=2 ** 31, B=1, H=1) == E_SHAPE
     assert call_dn(B=2 ** 31, H=1, T=1) == E_SHAPE
