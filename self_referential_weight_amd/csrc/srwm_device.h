@@ -372,6 +372,13 @@ __device__ __forceinline__ void copy_dword_to_lds(__amdgpu_buffer_rsrc_t rsrc, i
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds_base), 4, voff, soff, 0, 0);
 }
 
+// The same copy, 16 bytes per active lane (gfx950 buffer_load_dwordx4 ...
+// lds): lane i writes the 16 bytes at lds_base + 16 i.
+__device__ __forceinline__ void copy_x4_to_lds(__amdgpu_buffer_rsrc_t rsrc, int voff, int soff, void* lds_base)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds_base), 16, voff, soff, 0, 0);
+}
+
 // Buffer resource over n floats at base (raw buffer, bounds-checked against
 // n * 4 bytes): its four dwords are wave-uniform, so they live in SGPRs.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t float_rsrc(const float* base, int n)

@@ -185,12 +185,27 @@ __device__ __forceinline__ void stream_lds(const float* __restrict__ src, F&& bo
 // registers (lane tid < S*LR takes E consecutive elements of row tid/LR), then
 // widened (bf16 -> f32 is exact), optionally softmax-ed per row, and written
 // to an LDS tile.
+//
+// One-wave tape-writing units whose x rows are whole 16-byte pieces (DMA)
+// fetch the raw chunk straight into a second LDS buffer instead (buffer_load_dwordx4 ...
+// lds, 1 KB per instruction: lane i takes piece i mod LPR of row i / LPR of
+// the instruction's rows), and stage() reads each lane's E elements from
+// there.  No register then holds x across the chunk: in the registers of a
+// one-wave unit such a prefetch was spilled, its loads waited for at once.
+// The lane's offsets are recomputed from the lane index at each use.
 template <int D_IN, int D_OUT, int NW, int P, bool BF16, bool LONG = false>
 struct XStage {
     using Gm = Geom<D_IN, D_OUT, NW, P, 4, LONG>;
     static constexpr int E = Gm::E, LR = Gm::LR, S = Gm::S;
     static constexpr int XR = BF16 ? (E + 1) / 2 : E; // registers held per lane
     using XT = typename std::conditional<BF16, uint16_t, float>::type;
+    static constexpr int RB = D_IN * (int)sizeof(XT);  // bytes per step row
+    static constexpr int LPR = RB / 16;                 // DMA lanes per row
+    static constexpr bool DMA = LONG && NW == 1 && RB % 16 == 0 && LPR <= kWave && kWave % LPR == 0 &&
+                                (E * (int)sizeof(XT)) % 4 == 0;
+    static constexpr int RPI = DMA ? kWave / LPR : 1;  // rows per DMA instruction
+    static constexpr int NI = (S + RPI - 1) / RPI;      // DMA instructions per chunk
+    static constexpr int RAW_WORDS = DMA ? NI * kWave * 4 : 4;  // the raw chunk buffer (uint32)
     uint32_t xr[XR];
     int row, col;
     uint32_t lane_off;  // element offset of this lane's piece within a chunk
@@ -198,10 +213,12 @@ struct XStage {
     const XT* __restrict__ xu;  // x[b][0][h][0] (wave-uniform)
     int64_t x_step;
     int T;
+    uint32_t* raw;  // DMA: the raw chunk in LDS, RAW_WORDS words
 
-    __device__ __forceinline__ XStage(int tid, const void* __restrict__ xv_, int64_t x0_, int64_t x_step_, int T_)
+    __device__ __forceinline__ XStage(int tid, const void* __restrict__ xv_, int64_t x0_, int64_t x_step_, int T_,
+                                      uint32_t* raw_ = nullptr)
         : row(tid / LR), col((tid % LR) * E), active(tid < S * LR),
-          xu(reinterpret_cast<const XT*>(xv_) + x0_), x_step(x_step_), T(T_)
+          xu(reinterpret_cast<const XT*>(xv_) + x0_), x_step(x_step_), T(T_), raw(raw_)
     {
         lane_off = static_cast<uint32_t>(row * x_step + col);
     }
@@ -209,6 +226,25 @@ struct XStage {
     // Issue the global loads of the chunk that starts at step c0.
     __device__ __forceinline__ void load(int c0)
     {
+        if constexpr (DMA) {
+            // The resource ends with the unit's last step row in the chunk, and
+            // lanes of rows past it copy nothing.  The host bounds a step's row
+            // to 64 MiB, so every offset here is below 2^31.
+            const int l = lane_now();
+            const int r0 = l / LPR;
+            const int xsb = static_cast<int>(x_step * (int64_t)sizeof(XT));
+            const int last = (T - 1 - c0) < (S - 1) ? (T - 1 - c0) : (S - 1);
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(xu + (int64_t)c0 * x_step), (short)0, last * xsb + RB, 0x00020000);
+            const int voff = r0 * xsb + (l % LPR) * 16;
+#pragma unroll
+            for (int k = 0; k < NI; ++k) {
+                const int rk = k * RPI + r0;
+                if ((NI * RPI == S || rk < S) && c0 + rk < T)
+                    copy_x4_to_lds(rs, voff, k * RPI * xsb, raw + k * kWave * 4);
+            }
+            return;
+        }
         const int t = c0 + row;
         if (active && t < T) {
             const XT* src = xu + (int64_t)c0 * x_step + lane_off;
@@ -245,6 +281,18 @@ struct XStage {
     // Widen, apply the optional input softmax per step row, write to LDS.
     __device__ __forceinline__ void stage(float (*dst)[D_IN], int in_softmax)
     {
+        if constexpr (DMA) {
+            wait_vmem();  // the chunk's copies (and every earlier store) have landed
+            const int l = lane_now();
+            // lanes past the chunk's S rows (l >= S*LR) read nothing
+            const int lr = l < S * LR ? l : 0;
+            const uint32_t* src = raw + ((lr / LR) * RB + (lr % LR) * E * (int)sizeof(XT)) / 4;
+#pragma unroll
+            for (int i = 0; i < XR; ++i) xr[i] = src[i];
+        }
+        const int srow = DMA ? lane_now() / LR : row;
+        const int scol = DMA ? (lane_now() % LR) * E : col;
+        const bool sact = DMA ? lane_now() < S * LR : active;
         float v[E];
 #pragma unroll
         for (int i = 0; i < E; ++i) {
@@ -268,7 +316,7 @@ struct XStage {
 #pragma unroll
             for (int i = 0; i < E; ++i) v[i] *= inv;
         }
-        if (active) store_f32<E>(&dst[row][col], v);
+        if (sact) store_f32<E>(&dst[srow][scol], v);
     }
 };
 
@@ -310,6 +358,8 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
     constexpr bool KEEP_SUMS = NW > 1 && D_IN <= 64;
 
     __shared__ __attribute__((aligned(16))) float s_x[2][S][D_IN];
+    using XS = XStage<D_IN, D_OUT, NW, P, BF16, TAPE>;
+    __shared__ __attribute__((aligned(16))) uint32_t s_xraw[XS::RAW_WORDS];
     // z_t, double-buffered by step parity so one barrier per step suffices.
     __shared__ __attribute__((aligned(16))) float s_z[2][R * G + 4];
     using TL = TapeLayout<M, D_IN>;
@@ -388,7 +438,18 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
         }
     };
 
-    XStage<D_IN, D_OUT, NW, P, BF16, TAPE> xs(tid, xv, x0, x_step, T);
+    XS xs(tid, xv, x0, x_step, T, s_xraw);
+    // The unit's barrier.  With the x chunk copied straight into LDS (one
+    // wave) a wave-scope fence suffices, and a workgroup-scope one would also
+    // wait for those copies in flight (they are LDS writes), which stage()
+    // waits for when it needs them.  (For the other one-wave units the
+    // wave-scope fence measured 0.3% slower.)
+    auto unit_sync = [] {
+        if constexpr (XS::DMA)
+            wave_sync();
+        else
+            __syncthreads();
+    };
     float* const khs = s_kh[wave];
     float* const es = s_e[wave];
 
@@ -554,7 +615,7 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
                 }
             }
         }
-        __syncthreads();
+        unit_sync();
 
         // ---- (B) phi(k), phi(q), sigma(beta), computed by every wave for
         // itself (identical bits in every wave); y_t from W_{t-1}.
@@ -739,7 +800,7 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
         xs.load(0);
         xs.stage(s_x[0], in_softmax);
         if (T > S) xs.load(S);
-        __syncthreads();
+        unit_sync();
 
         static_assert(S % 2 == 0, "chunks start at even steps");
         int chunk = 0;
@@ -780,7 +841,7 @@ void srwm_fwd_kernel(const void* __restrict__ xv, const float* __restrict__ W0,
             if (c0 + S < T) {
                 xs.stage(s_x[(chunk + 1) & 1], in_softmax);
                 if (c0 + 2 * S < T) xs.load(c0 + 2 * S);
-                __syncthreads();
+                unit_sync();
             }
         }
     }
