@@ -296,16 +296,20 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
     static_assert(NT % D_OUT == 0, "gy entries spread over the threads");
     const bool g_mine = tid % GS == 0;
     const int g_idx = tid / GS;
+    // Each row is read through a buffer resource made per step (SGPRs; its
+    // record count is the row, so the entries past it read as zero) with the
+    // thread's byte offset as the only per-lane operand.
     float tnext[TPL];
     float gnext = 0.f;
+    const int tid4 = 4 * tid;
     auto fetch = [&](int t) {
-        const float* __restrict__ tp = tp0 + (int64_t)t * TW;
+        const __amdgpu_buffer_rsrc_t trow = float_rsrc(tp0 + (int64_t)t * TW, TW);
 #pragma unroll
-        for (int i = 0; i < TPL; ++i) {
-            const int j = tid + NT * i;
-            tnext[i] = (j < TW) ? tp[j] : 0.f;
-        }
-        if (g_mine) gnext = gy[y0 + (int64_t)t * y_step + g_idx];
+        for (int i = 0; i < TPL; ++i)
+            tnext[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(trow, tid4, 4 * NT * i, 0));
+        if (g_mine)
+            gnext = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(float_rsrc(gy + y0 + (int64_t)t * y_step, D_OUT),
+                                                                        4 * g_idx, 0, 0));
     };
     auto stage = [&](int slot) {
 #pragma unroll
@@ -385,7 +389,9 @@ void srwm_bwd_kernel(const float* __restrict__ WTin,
             const float du = wave_total(lane < D_IN ? uh_j * u_j : 0.f);
             d = u_j * (uh_j - du);
         }
-        if (lane < D_IN) dx[x0 + (int64_t)t * x_step + jc] = d;
+        if (lane < D_IN)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(d), float_rsrc(dx + x0 + (int64_t)t * x_step, D_IN),
+                                                  4 * jc, 0, 0);
     };
 
 #pragma unroll
