@@ -52,6 +52,16 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 // B[l / 16][l % 16]; accumulator register r of lane l is D[4 (l / 16) + r][l % 16].
 constexpr int kGM = 64, kGN = 64, kGK = 32, kGPad = 4;
 static_assert(kGK == 32, "one chunk of K: eight MFMA steps of four lane groups");
+// A remainder of at most kGX columns past the last whole 64-column tile is
+// taken by that tile as one more 16-column MFMA block (each wave computes one
+// 16 x 16 piece of it), instead of a tile of its own that would be nearly all
+// padding: DeltaNet's C = 2 x 193 = 386 would otherwise spend a seventh of
+// its MFMAs on a tile with 2 real columns.
+constexpr int kGX = 16;
+__host__ __device__ constexpr int64_t gemm_col_tiles(int64_t C)
+{
+    return (C > kGN && C % kGN != 0 && C % kGN <= kGX) ? C / kGN : (C + kGN - 1) / kGN;
+}
 
 // Workgroups are dispatched to the 8 XCDs round-robin (workgroup i on XCD
 // i % 8), each XCD with its own L2.  The 1-D grid is renumbered so that the
@@ -65,11 +75,11 @@ __global__ __launch_bounds__(256) void srwm_proj_gemm_kernel(const float* __rest
                                                              int K)
 {
     __shared__ __attribute__((aligned(16))) float sX[kGM][kGK + kGPad];
-    __shared__ __attribute__((aligned(16))) float sW[kGN][kGK + kGPad];
+    __shared__ __attribute__((aligned(16))) float sW[kGN + kGX][kGK + kGPad];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int64_t ctiles = (C + kGN - 1) / kGN;
+    const int64_t ctiles = gemm_col_tiles(C);
     const int64_t tiles = ((N + kGM - 1) / kGM) * ctiles;
     const int64_t per_xcd = (int64_t)gridDim.x / kXcds;  // grid is a multiple of kXcds
     const int64_t g = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
@@ -77,6 +87,7 @@ __global__ __launch_bounds__(256) void srwm_proj_gemm_kernel(const float* __rest
     const int64_t n0 = (g / ctiles) * kGM;
     const int c0 = static_cast<int>(g % ctiles) * kGN;
     const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
+    const bool wodd = __builtin_amdgcn_readfirstlane(wave) & 1;  // uniform
     const int lr = tid >> 3, lc = (tid & 7) * 4;  // loader: rows lr, lr + 32; columns lc..lc+3
     // The tile's corner in X, W and Z (uniform): inside a tile every element
     // is a 32-bit offset from it.
@@ -85,12 +96,16 @@ __global__ __launch_bounds__(256) void srwm_proj_gemm_kernel(const float* __rest
     float* __restrict__ Zt = Z + n0 * C + c0;
 
     // FULL: every row, column and K chunk of the tile exists (all but the
-    // edge tiles), so loads and stores need no bounds checks.
-    auto run = [&](auto full) {
+    // edge tiles), so loads and stores need no bounds checks.  EXTRA: the
+    // last column tile with the remainder columns (checked: only C - c0 - 64
+    // of its 16 are real).
+    auto run = [&](auto full, auto extra) {
         constexpr bool FULL = decltype(full)::value;
-        v4f c00 = {0.f, 0.f, 0.f, 0.f}, c01 = c00, c10 = c00, c11 = c00;
-        // K chunk k0's X and W pieces of this thread (rows lr, lr + 32)
-        float4 px0, px1, pw0, pw1;
+        constexpr bool EXTRA = decltype(extra)::value;
+        v4f c00 = {0.f, 0.f, 0.f, 0.f}, c01 = c00, c10 = c00, c11 = c00, cx = c00;
+        // K chunk k0's X and W pieces of this thread (rows lr, lr + 32; with
+        // EXTRA, threads < 128 also row kGN + lr of W)
+        float4 px0, px1, pw0, pw1, pwx = make_float4(0.f, 0.f, 0.f, 0.f);
         auto piece = [&](const float* __restrict__ base, int row0, int lim, int r, int gk) {
             if constexpr (FULL) {
                 return *reinterpret_cast<const float4*>(base + static_cast<uint32_t>(r * K + gk));
@@ -106,6 +121,12 @@ __global__ __launch_bounds__(256) void srwm_proj_gemm_kernel(const float* __rest
             px1 = piece(Xt, 0, nl, lr + 32, k0 + lc);
             pw0 = piece(Wt, c0, C, lr, k0 + lc);
             pw1 = piece(Wt, c0, C, lr + 32, k0 + lc);
+            if constexpr (EXTRA) {
+                // rows kGN .. kGN + 15 of the tile, bounds-checked against C
+                pwx = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (tid < 8 * kGX && c0 + kGN + lr < C && k0 + lc < K)
+                    pwx = *reinterpret_cast<const float4*>(Wt + static_cast<int64_t>(kGN + lr) * K + k0 + lc);
+            }
         };
         fetch(0);
         for (int k0 = 0; k0 < K; k0 += kGK) {
@@ -113,6 +134,9 @@ __global__ __launch_bounds__(256) void srwm_proj_gemm_kernel(const float* __rest
             *reinterpret_cast<float4*>(&sX[lr + 32][lc]) = px1;
             *reinterpret_cast<float4*>(&sW[lr][lc]) = pw0;
             *reinterpret_cast<float4*>(&sW[lr + 32][lc]) = pw1;
+            if constexpr (EXTRA) {
+                if (tid < 8 * kGX) *reinterpret_cast<float4*>(&sW[kGN + lr][lc]) = pwx;
+            }
             __syncthreads();
             // the next chunk's loads are in flight while this one's MFMAs run
             if (k0 + kGK < K) fetch(k0 + kGK);
@@ -137,6 +161,16 @@ __global__ __launch_bounds__(256) void srwm_proj_gemm_kernel(const float* __rest
                     c10 = __builtin_amdgcn_mfma_f32_16x16x4f32(av1[st], bv0[st], c10, 0, 0, 0);
                     c11 = __builtin_amdgcn_mfma_f32_16x16x4f32(av1[st], bv1[st], c11, 0, 0, 0);
                 }
+                if constexpr (EXTRA) {
+                    // this wave's piece of the extra block: rows 16 wave .. +15,
+                    // which are the rows of its A operand av0 (even waves) or
+                    // av1 (odd waves), already in registers
+                    const float4 bx = *reinterpret_cast<const float4*>(&sW[kGN + (lane & 15)][kb]);
+                    const float bxv[4] = {bx.x, bx.y, bx.z, bx.w};
+#pragma unroll
+                    for (int st = 0; st < 4; ++st)
+                        cx = __builtin_amdgcn_mfma_f32_16x16x4f32(wodd ? av1[st] : av0[st], bxv[st], cx, 0, 0, 0);
+                }
             }
             __syncthreads();
         }
@@ -156,11 +190,26 @@ __global__ __launch_bounds__(256) void srwm_proj_gemm_kernel(const float* __rest
                     }
                 }
             }
+        if constexpr (EXTRA) {
+            const int col = kGN + (lane & 15);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * wave + 4 * (lane >> 4) + r;
+                if ((FULL || n0 + row < N) && c0 + col < C) Zt[static_cast<int64_t>(row) * C + col] = cx[r];
+            }
+        }
     };
     // (the 32-bit offsets: rows * K and rows * C within a tile stay below 2^31)
-    if (n0 + kGM <= N && c0 + kGN <= C && K % kGK == 0 && K <= INT32_MAX / kGM && C <= INT32_MAX / kGM)
-        run(std::true_type{});
-    else run(std::false_type{});
+    const bool full = n0 + kGM <= N && c0 + kGN <= C && K % kGK == 0 && K <= INT32_MAX / (kGN + kGX) &&
+                      C <= INT32_MAX / kGM;
+    const bool extra = c0 + kGN < C && g % ctiles == ctiles - 1;  // the last tile, with the remainder
+    if (full) {
+        if (extra) run(std::true_type{}, std::true_type{});
+        else run(std::true_type{}, std::false_type{});
+    } else {
+        if (extra) run(std::false_type{}, std::true_type{});
+        else run(std::false_type{}, std::false_type{});
+    }
 }
 
 // ----------------------------------------------------------------------------
@@ -478,7 +527,7 @@ int launch_projection(const srwm_deltanet_args_t* a, int64_t K, int64_t C)
     int Ci = static_cast<int>(C), Ki = static_cast<int>(K);
     int64_t Nv = N;
     void* args[] = {const_cast<float**>(&X), const_cast<float**>(&Wp), &Zp, &Nv, &Ci, &Ki};
-    const int64_t tiles = ((N + kGM - 1) / kGM) * ((C + kGN - 1) / kGN);
+    const int64_t tiles = ((N + kGM - 1) / kGM) * gemm_col_tiles(C);
     const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
     if (grid > INT32_MAX) return SRWM_ERR_SHAPE;
     const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(&srwm_proj_gemm_kernel),
