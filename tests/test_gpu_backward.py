@@ -109,6 +109,29 @@ def test_backward_every_taped_variant():
     assert done >= 6
 
 
+def test_backward_one_wave_taped_shorter_than_a_chunk():
+    # One-wave taped units stage x a chunk of 16 or 32 steps at a time; a run
+    # shorter than one chunk leaves the chunk's later rows unfetched and unused.
+    srwm = _srwm()
+    done = 0
+    for v in srwm.variants():
+        if v["waves"] != 1 or not v["writes_tape"] or not srwm.backward_supported(v["d_in"], v["d_out"],
+                                                                                   v["io_dtype"], v["n_lr"]):
+            continue
+        for T in (1, 3):
+            w = Workload("taped_short", B=2, H=2, d_in=v["d_in"], d_out=v["d_out"], T=T, io_dtype=v["io_dtype"],
+                         apply_input_softmax=True, return_state=True, w0_std=v["d_in"] ** -0.5,
+                         seed=100 + v["index"], n_lr=v["n_lr"])
+            say(f"[bwd] one-wave taped variant {v['index']} T={T}")
+            x, W0, gy, gW = gen_x(w), gen_W0(w), gen_gy(w), gen_gW(w)
+            _, _, dx, dW0 = gpu_grads(w, x, W0, gy, gW, True, variant=v["index"])
+            dx_ref, dW0_ref = oracle_bwd.grads(x, W0, True, gy, gW, n_lr=w.n_lr)
+            check_grad(dx, dx_ref, f"variant {v['index']} T={T} dx")
+            check_grad(dW0, dW0_ref, f"variant {v['index']} T={T} dW0")
+            done += 1
+    assert done >= 4
+
+
 @pytest.mark.parametrize("n_lr", [4, 1])
 @pytest.mark.parametrize("R", [0, 7])
 def test_backward_kernel_by_unit_count(n_lr, R):
