@@ -46,16 +46,16 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 // ----------------------------------------------------------------------------
 // Z[n][c] = sum_k X[n][k] W[c][k]: n < N (= B*T rows of x), c < C (= H*P),
-// k < K (= H*d_in, K % 4 == 0).  Workgroup tile 64 x 64, four waves of 32 x 32
-// (2 x 2 MFMA tiles of 16 x 16), K staged through LDS 32 at a time.
+// k < K (= H*d_in, K % 4 == 0).  Workgroup tile 64 x 128, four waves of
+// 32 x 64 (2 x 4 MFMA tiles of 16 x 16), K staged through LDS 32 at a time.
 // MFMA 16x16x4 f32 operand layout: lane l supplies A[l % 16][l / 16] and
 // B[l / 16][l % 16]; accumulator register r of lane l is D[4 (l / 16) + r][l % 16].
-constexpr int kGM = 64, kGN = 64, kGK = 32, kGPad = 4;
+constexpr int kGM = 64, kGN = 128, kGK = 32, kGPad = 4;
 static_assert(kGK == 32, "one chunk of K: eight MFMA steps of four lane groups");
-// A remainder of at most kGX columns past the last whole 64-column tile is
+// A remainder of at most kGX columns past the last whole column tile is
 // taken by that tile as one more 16-column MFMA block (each wave computes one
 // 16 x 16 piece of it), instead of a tile of its own that would be nearly all
-// padding: DeltaNet's C = 2 x 193 = 386 would otherwise spend a seventh of
+// padding: DeltaNet's C = 2 x 193 = 386 would otherwise spend a quarter of
 // its MFMAs on a tile with 2 real columns.
 constexpr int kGX = 16;
 __host__ __device__ constexpr int64_t gemm_col_tiles(int64_t C)
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void srwm_proj_gemm_kernel(const float* __rest
     if (g >= tiles) return;  // padding workgroups (whole workgroup, before any barrier)
     const int64_t n0 = (g / ctiles) * kGM;
     const int c0 = static_cast<int>(g % ctiles) * kGN;
-    const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
+    const int wm = (wave >> 1) * 32, wn = (wave & 1) * 64;
     const bool wodd = __builtin_amdgcn_readfirstlane(wave) & 1;  // uniform
     const int lr = tid >> 3, lc = (tid & 7) * 4;  // loader: rows lr, lr + 32; columns lc..lc+3
     // The tile's corner in X, W and Z (uniform): inside a tile every element
@@ -97,15 +97,16 @@ __global__ __launch_bounds__(256) void srwm_proj_gemm_kernel(const float* __rest
 
     // FULL: every row, column and K chunk of the tile exists (all but the
     // edge tiles), so loads and stores need no bounds checks.  EXTRA: the
-    // last column tile with the remainder columns (checked: only C - c0 - 64
+    // last column tile with the remainder columns (checked: only C - c0 - kGN
     // of its 16 are real).
     auto run = [&](auto full, auto extra) {
         constexpr bool FULL = decltype(full)::value;
         constexpr bool EXTRA = decltype(extra)::value;
-        v4f c00 = {0.f, 0.f, 0.f, 0.f}, c01 = c00, c10 = c00, c11 = c00, cx = c00;
-        // K chunk k0's X and W pieces of this thread (rows lr, lr + 32; with
-        // EXTRA, threads < 128 also row kGN + lr of W)
-        float4 px0, px1, pw0, pw1, pwx = make_float4(0.f, 0.f, 0.f, 0.f);
+        v4f c00 = {0.f, 0.f, 0.f, 0.f}, c01 = c00, c02 = c00, c03 = c00;
+        v4f c10 = c00, c11 = c00, c12 = c00, c13 = c00, cx = c00;
+        // K chunk k0's X pieces (rows lr, lr + 32) and W pieces (rows lr +
+        // 32 i) of this thread; with EXTRA, threads < 128 also row kGN + lr of W
+        float4 px0, px1, pw0, pw1, pw2, pw3, pwx = make_float4(0.f, 0.f, 0.f, 0.f);
         auto piece = [&](const float* __restrict__ base, int row0, int lim, int r, int gk) {
             if constexpr (FULL) {
                 return *reinterpret_cast<const float4*>(base + static_cast<uint32_t>(r * K + gk));
@@ -121,6 +122,8 @@ __global__ __launch_bounds__(256) void srwm_proj_gemm_kernel(const float* __rest
             px1 = piece(Xt, 0, nl, lr + 32, k0 + lc);
             pw0 = piece(Wt, c0, C, lr, k0 + lc);
             pw1 = piece(Wt, c0, C, lr + 32, k0 + lc);
+            pw2 = piece(Wt, c0, C, lr + 64, k0 + lc);
+            pw3 = piece(Wt, c0, C, lr + 96, k0 + lc);
             if constexpr (EXTRA) {
                 // rows kGN .. kGN + 15 of the tile, bounds-checked against C
                 pwx = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -134,6 +137,8 @@ __global__ __launch_bounds__(256) void srwm_proj_gemm_kernel(const float* __rest
             *reinterpret_cast<float4*>(&sX[lr + 32][lc]) = px1;
             *reinterpret_cast<float4*>(&sW[lr][lc]) = pw0;
             *reinterpret_cast<float4*>(&sW[lr + 32][lc]) = pw1;
+            *reinterpret_cast<float4*>(&sW[lr + 64][lc]) = pw2;
+            *reinterpret_cast<float4*>(&sW[lr + 96][lc]) = pw3;
             if constexpr (EXTRA) {
                 if (tid < 8 * kGX) *reinterpret_cast<float4*>(&sW[kGN + lr][lc]) = pwx;
             }
@@ -143,7 +148,7 @@ __global__ __launch_bounds__(256) void srwm_proj_gemm_kernel(const float* __rest
             // The sum over k is order-free, so in MFMA step s of the chunk lane
             // group j = lane / 16 supplies k = 8 j + s: its operands for all eight
             // steps are 8 consecutive floats of one row, one 16-byte LDS read per
-            // half of four steps (16 operand registers live at a time).
+            // half of four steps.
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
                 const int kb = 8 * (lane >> 4) + 4 * hf;
@@ -152,14 +157,21 @@ __global__ __launch_bounds__(256) void srwm_proj_gemm_kernel(const float* __rest
                 const float4 a1 = *reinterpret_cast<const float4*>(&sX[ra + 16][kb]);
                 const float4 b0 = *reinterpret_cast<const float4*>(&sW[rb][kb]);
                 const float4 b1 = *reinterpret_cast<const float4*>(&sW[rb + 16][kb]);
+                const float4 b2 = *reinterpret_cast<const float4*>(&sW[rb + 32][kb]);
+                const float4 b3 = *reinterpret_cast<const float4*>(&sW[rb + 48][kb]);
                 const float av0[4] = {a0.x, a0.y, a0.z, a0.w}, av1[4] = {a1.x, a1.y, a1.z, a1.w};
                 const float bv0[4] = {b0.x, b0.y, b0.z, b0.w}, bv1[4] = {b1.x, b1.y, b1.z, b1.w};
+                const float bv2[4] = {b2.x, b2.y, b2.z, b2.w}, bv3[4] = {b3.x, b3.y, b3.z, b3.w};
 #pragma unroll
                 for (int st = 0; st < 4; ++st) {
                     c00 = __builtin_amdgcn_mfma_f32_16x16x4f32(av0[st], bv0[st], c00, 0, 0, 0);
                     c01 = __builtin_amdgcn_mfma_f32_16x16x4f32(av0[st], bv1[st], c01, 0, 0, 0);
+                    c02 = __builtin_amdgcn_mfma_f32_16x16x4f32(av0[st], bv2[st], c02, 0, 0, 0);
+                    c03 = __builtin_amdgcn_mfma_f32_16x16x4f32(av0[st], bv3[st], c03, 0, 0, 0);
                     c10 = __builtin_amdgcn_mfma_f32_16x16x4f32(av1[st], bv0[st], c10, 0, 0, 0);
                     c11 = __builtin_amdgcn_mfma_f32_16x16x4f32(av1[st], bv1[st], c11, 0, 0, 0);
+                    c12 = __builtin_amdgcn_mfma_f32_16x16x4f32(av1[st], bv2[st], c12, 0, 0, 0);
+                    c13 = __builtin_amdgcn_mfma_f32_16x16x4f32(av1[st], bv3[st], c13, 0, 0, 0);
                 }
                 if constexpr (EXTRA) {
                     // this wave's piece of the extra block: rows 16 wave .. +15,
@@ -174,11 +186,11 @@ __global__ __launch_bounds__(256) void srwm_proj_gemm_kernel(const float* __rest
             }
             __syncthreads();
         }
-        const v4f acc[2][2] = {{c00, c01}, {c10, c11}};
+        const v4f acc[2][4] = {{c00, c01, c02, c03}, {c10, c11, c12, c13}};
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < 4; ++j) {
                 const int col = wn + 16 * j + (lane & 15);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
